@@ -1,0 +1,175 @@
+"""Exact rational brute force of the three state representations, for tiny heads.
+
+TEST INFRASTRUCTURE (same rules as the rest of ``oracle/``). Everything is
+``fractions.Fraction``, so the algebraic identities the pages state -- window
+unrolling (LeapQuant eq. 4 and App. B.2) and the base+log invariant (DeltaLog
+eq. 7 and its closure argument) -- must hold with equality, not to a tolerance.
+Decays are kept as exact products of the gates; the exponential of a sum of
+log-decays in DeltaLog is the same product, which rationals can hold exactly.
+
+Matrices are lists of rows; vectors are lists.
+"""
+from __future__ import annotations
+
+from fractions import Fraction as F
+from typing import List, Sequence
+
+Mat = List[List[F]]
+Vec = List[F]
+
+
+def frac_vec(x: Sequence[float]) -> Vec:
+    return [F(float(t)) for t in x]
+
+
+def frac_mat(x) -> Mat:
+    return [frac_vec(row) for row in x]
+
+
+def dense_step(S: Mat, q: Vec, k: Vec, v: Vec, g: Vec, beta: F):
+    """Decay, read along k from the decayed state, delta write, post-update readout
+    (LeapQuant App. A). Returns (S_new, y); S is not modified."""
+    dk, dv = len(S), len(S[0])
+    Sd = [[g[i] * S[i][j] for j in range(dv)] for i in range(dk)]
+    u = [beta * (v[j] - sum(Sd[i][j] * k[i] for i in range(dk))) for j in range(dv)]
+    Sn = [[Sd[i][j] + k[i] * u[j] for j in range(dv)] for i in range(dk)]
+    y = [sum(Sn[i][j] * q[i] for i in range(dk)) for j in range(dv)]
+    return Sn, y
+
+
+def householder_step(S: Mat, k: Vec, v: Vec, g: Vec, beta: F) -> Mat:
+    """(I - beta k k^T) Diag(g) S + beta k v^T: the left-hand side of the GDN and
+    KDA expansions in LeapQuant App. A (for a scalar gate Diag(g) = alpha I commutes)."""
+    dk, dv = len(S), len(S[0])
+    Sd = [[g[i] * S[i][j] for j in range(dv)] for i in range(dk)]
+    A = [[(1 if i == m else 0) - beta * k[i] * k[m] for m in range(dk)] for i in range(dk)]
+    return [[sum(A[i][m] * Sd[m][j] for m in range(dk)) + beta * k[i] * v[j]
+             for j in range(dv)] for i in range(dk)]
+
+
+def _rne(x: F) -> int:
+    """Round to nearest integer, ties to even."""
+    fl = x.numerator // x.denominator
+    rem = x - fl
+    if rem > F(1, 2) or (rem == F(1, 2) and fl % 2 == 1):
+        return fl + 1
+    return fl
+
+
+def quantize(S: Mat):
+    """Per-row symmetric int8: a_i = max_j |S_ij|, z = clamp(rne(S*127/a), -127, 127)."""
+    Z, a = [], []
+    for row in S:
+        ai = max(abs(x) for x in row)
+        a.append(ai)
+        Z.append([0 if ai == 0 else max(-127, min(127, _rne(x * 127 / ai))) for x in row])
+    return Z, a
+
+
+def dequant(Z, a) -> Mat:
+    return [[F(z) * a[i] / 127 for z in Z[i]] for i in range(len(Z))]
+
+
+def window_run(S0: Mat, inputs, W: int):
+    """Per-window quantization by eq. 4: S_l = Gamma_{1:l} S^_0 + sum Gamma_{j+1:l} k_j u_j^T,
+    u_l from S_{l-1} read along the decayed key, y_l = S_l^T q_l, requantize at l = W.
+    inputs: list of (q, k, v, g, beta). Returns (ys, [(Z, a) at each boundary])."""
+    dk, dv = len(S0), len(S0[0])
+    Z, a = quantize(S0)
+    base = dequant(Z, a)
+    recs = []
+    ys, bounds = [], []
+
+    def mat(l):
+        out = []
+        for i in range(dk):
+            gam0 = F(1)
+            for (g, _, _) in recs[:l]:
+                gam0 *= g[i]
+            row = [gam0 * base[i][j] for j in range(dv)]
+            for m in range(l):
+                c = recs[m][1][i]
+                for (g, _, _) in recs[m + 1:l]:
+                    c *= g[i]
+                for j in range(dv):
+                    row[j] += c * recs[m][2][j]
+            out.append(row)
+        return out
+
+    for (q, k, v, g, beta) in inputs:
+        l = len(recs) + 1
+        Sp = mat(l - 1)
+        u = [beta * (v[j] - sum(g[i] * Sp[i][j] * k[i] for i in range(dk))) for j in range(dv)]
+        recs.append((g, k, u))
+        Sl = mat(l)
+        ys.append([sum(Sl[i][j] * q[i] for i in range(dk)) for j in range(dv)])
+        if l == W:
+            Z, a = quantize(Sl)
+            bounds.append((Z, a))
+            base = dequant(Z, a)
+            recs = []
+    return ys, bounds
+
+
+def explicit_schedule_run(S0: Mat, inputs, W: int):
+    """Dequantize, W eager dense steps, requantize -- the schedule eq. 4 unrolls."""
+    Z, a = quantize(S0)
+    S = dequant(Z, a)
+    ys, bounds = [], []
+    for t, (q, k, v, g, beta) in enumerate(inputs):
+        S, y = dense_step(S, q, k, v, g, beta)
+        ys.append(y)
+        if (t + 1) % W == 0:
+            Z, a = quantize(S)
+            bounds.append((Z, a))
+            S = dequant(Z, a)
+    return ys, bounds
+
+
+def log_run(S0: Mat, inputs, M: int):
+    """Base + log (DeltaLog Alg. 1, eqs. 4-7) with decays as exact gate products:
+    D(lbar) is the product of the gates since the last merge and D(lbar - Lam_m) the
+    product of the gates after entry m. Returns (ys, logical states after each step)."""
+    dk, dv = len(S0), len(S0[0])
+    C = M - 1
+    Sbar = [row[:] for row in S0]
+    dec = [F(1)] * dk                   # exp(lbar)
+    log_entries = []                    # (K, U, exp(Lam))
+    ys, states = [], []
+
+    def logical(decay, entries):
+        out = []
+        for i in range(dk):
+            row = [decay[i] * Sbar[i][j] for j in range(dv)]
+            for (Km, Um, Em) in entries:
+                c = decay[i] / Em[i] * Km[i]
+                for j in range(dv):
+                    row[j] += c * Um[j]
+            out.append(row)
+        return out
+
+    for (q, k, v, g, beta) in inputs:
+        Sold = logical(dec, log_entries)
+        b = [beta * (v[j] - sum(g[i] * Sold[i][j] * k[i] for i in range(dk))) for j in range(dv)]
+        dec = [dec[i] * g[i] for i in range(dk)]
+        Snew = logical(dec, log_entries)
+        Snew = [[Snew[i][j] + k[i] * b[j] for j in range(dv)] for i in range(dk)]
+        ys.append([sum(Snew[i][j] * q[i] for i in range(dk)) for j in range(dv)])
+        if len(log_entries) < C:
+            log_entries.append((k, b, dec[:]))
+        else:
+            Sbar = Snew
+            dec = [F(1)] * dk
+            log_entries = []
+        states.append(logical(dec, log_entries))
+    return ys, states
+
+
+def eager_run(S0: Mat, inputs):
+    S = [row[:] for row in S0]
+    ys, states = [], []
+    for (q, k, v, g, beta) in inputs:
+        S, y = dense_step(S, q, k, v, g, beta)
+        ys.append(y)
+        states.append(S)
+    return ys, states

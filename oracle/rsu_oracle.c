@@ -1,0 +1,324 @@
+/*
+ * rsu_oracle.c -- plain, slow, fp64 CPU reference of the delta-rule decode step.
+ *
+ * TEST INFRASTRUCTURE. Only the tests, the smoke check and the benchmark's CPU
+ * baseline use this file. It shares no code, header or constant with the HIP
+ * library and includes none of it. Loops are written out plainly, one head at a
+ * time (OpenMP only spreads independent heads over cores).
+ *
+ * Notation (LeapQuant, sec. 3.1 and App. A; STEPQuant notes, "from linear
+ * attention to the delta rule"): per head the state S is d_k x d_v, row i is a
+ * key channel, column j a value channel. g is the retention gate: a scalar alpha
+ * repeated over the key channels (Gated DeltaNet) or a per-key vector d (Kimi
+ * Delta Attention). beta in [0,1] is the scalar write strength.
+ *
+ * All arrays are row-major and contiguous:
+ *   S[nh][dk][dv], q,k[nh][dk], v,y[nh][dv], gate[nh] or [nh][dk], beta[nh].
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define IDX2(i, j, n2) ((size_t)(i) * (size_t)(n2) + (size_t)(j))
+
+static double gate_at(const double *gate_h, int per_key, int i)
+{
+    return per_key ? gate_h[i] : gate_h[0];
+}
+
+/*
+ * One decode step, eager dense form (LeapQuant, App. A, the GDN and KDA
+ * expansions, right-hand sides; STEPQuant notes: the step output is read after
+ * the update):
+ *   S' = Diag(g) S                 decay
+ *   p  = S'^T k                    old value read along k, from the decayed state
+ *   u  = beta (v - p)              correction, beta carried by u (App. A)
+ *   S  = S' + k u^T                rank-one delta write
+ *   y  = S^T q                     readout from the post-update state
+ */
+void oracle_dense_step(int64_t nh, int dk, int dv, int per_key, double *S,
+                       const double *q, const double *k, const double *v,
+                       const double *gate, const double *beta, double *y)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t h = 0; h < nh; ++h) {
+        double *Sh = S + (size_t)h * dk * dv;
+        const double *qh = q + (size_t)h * dk, *kh = k + (size_t)h * dk;
+        const double *vh = v + (size_t)h * dv;
+        const double *gh = gate + (per_key ? (size_t)h * dk : (size_t)h);
+        double *yh = y + (size_t)h * dv;
+        double *u = (double *)malloc(sizeof(double) * dv);
+
+        for (int i = 0; i < dk; ++i)
+            for (int j = 0; j < dv; ++j)
+                Sh[IDX2(i, j, dv)] *= gate_at(gh, per_key, i);
+        for (int j = 0; j < dv; ++j) {
+            double p = 0.0;
+            for (int i = 0; i < dk; ++i)
+                p += Sh[IDX2(i, j, dv)] * kh[i];
+            u[j] = beta[h] * (vh[j] - p);
+        }
+        for (int i = 0; i < dk; ++i)
+            for (int j = 0; j < dv; ++j)
+                Sh[IDX2(i, j, dv)] += kh[i] * u[j];
+        for (int j = 0; j < dv; ++j) {
+            double acc = 0.0;
+            for (int i = 0; i < dk; ++i)
+                acc += Sh[IDX2(i, j, dv)] * qh[i];
+            yh[j] = acc;
+        }
+        free(u);
+    }
+}
+
+/*
+ * Symmetric per-key-row int8 quantizer (STEPQuant notes, the uniform per-row
+ * absmax baseline; LeapQuant, App. B.3, the /127 convention).
+ *   a_i = max_j |S_ij|          stored as fp32
+ *   z_ij = clamp(rne(S_ij * (127 / a_i)), -127, 127)   and z = 0 when a_i = 0
+ *   dequant(z, a)_ij = z_ij * a_i / 127
+ * The code is an integer decided by floating point, so the decision is taken in
+ * fp32 exactly as the device does it: the value is first rounded to fp32, the
+ * reciprocal scale 127/a_i is one correctly rounded fp32 division, the product
+ * one fp32 multiplication, the rounding to nearest with ties to even.
+ * If w_out is not NULL it receives the exact pre-rounding code S_ij*127/a_i in
+ * fp64 (used to find elements near a rounding tie).
+ */
+void oracle_q8_quantize(int64_t nrows, int ncols, const double *X, int8_t *Z, float *a,
+                        double *w_out)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < nrows; ++r) {
+        const double *x = X + (size_t)r * ncols;
+        float amax = 0.0f;
+        for (int j = 0; j < ncols; ++j) {
+            float xf = fabsf((float)x[j]);
+            if (xf > amax)
+                amax = xf;
+        }
+        volatile float num = 127.0f;
+        float scale = amax > 0.0f ? num / amax : 0.0f;
+        a[r] = amax;
+        for (int j = 0; j < ncols; ++j) {
+            float w = (float)x[j] * scale;
+            float zr = rintf(w);
+            if (zr > 127.0f)
+                zr = 127.0f;
+            if (zr < -127.0f)
+                zr = -127.0f;
+            Z[(size_t)r * ncols + j] = (int8_t)zr;
+            if (w_out)
+                w_out[(size_t)r * ncols + j] = amax > 0.0f ? x[j] * 127.0 / (double)amax : 0.0;
+        }
+    }
+}
+
+/* dequant of one head's int8 state (App. B.3 with per-row scales) */
+static void dequant_head(int dk, int dv, const int8_t *Z, const float *a, double *out)
+{
+    for (int i = 0; i < dk; ++i)
+        for (int j = 0; j < dv; ++j)
+            out[IDX2(i, j, dv)] = (double)Z[IDX2(i, j, dv)] * (double)a[i] / 127.0;
+}
+
+/*
+ * Gamma_{from:to} for key channel i, with 0-based record indices: the product of
+ * the gates of records from..to (inclusive); the empty product is 1 (LeapQuant,
+ * sec. 3.2, the cumulative decay).
+ */
+static double window_gamma(const double *G, int per_key, int dk, int from, int to, int i)
+{
+    double g = 1.0;
+    for (int m = from; m <= to; ++m)
+        g *= per_key ? G[IDX2(m, i, dk)] : G[m];
+    return g;
+}
+
+/*
+ * S_l of eq. 4 (LeapQuant, sec. 3.2) for one head, from the fixed window-start
+ * state and the first l records (0-based records 0..l-1):
+ *   S_l = Gamma_{1:l} S0 + sum_{j=1..l} Gamma_{j+1:l} k_j u_j^T
+ */
+static void window_materialize(int dk, int dv, int per_key, int l, const double *S0,
+                               const double *G, const double *K, const double *U, double *out)
+{
+    for (int i = 0; i < dk; ++i) {
+        double g0 = window_gamma(G, per_key, dk, 0, l - 1, i);
+        for (int j = 0; j < dv; ++j)
+            out[IDX2(i, j, dv)] = g0 * S0[IDX2(i, j, dv)];
+        for (int m = 0; m < l; ++m) {
+            double c = window_gamma(G, per_key, dk, m + 1, l - 1, i) * K[IDX2(m, i, dk)];
+            for (int j = 0; j < dv; ++j)
+                out[IDX2(i, j, dv)] += c * U[IDX2(m, j, dv)];
+        }
+    }
+}
+
+/*
+ * One step of per-window quantization (LeapQuant, sec. 3.2, eqs. 3-4; App. B.2).
+ * The int8 state (Z, a) is the window-start state S^_0 and stays fixed inside
+ * the window. Step pos (0-based; the page's l = pos + 1) buffers the record
+ * (g_l, k_l, u_l) in higher precision:
+ *   S_{l-1} from eq. 4,  u_l = beta (v - (Diag(g_l) S_{l-1})^T k_l)   (eq. 3, App. A)
+ *   S_l     from eq. 4,  y = S_l^T q
+ * and at the end of the window (l = W) S_W is quantized into the next window's
+ * (Z, a) and the records are dropped (eq. 4, second line). The output of the
+ * last step is read from the unquantized S_W (STEPQuant notes: the readout comes
+ * before the quantization of the step).
+ * Records: G[nh][W] (scalar gate) or G[nh][W][dk], K[nh][W][dk], U[nh][W][dv].
+ * Sw_out, w_out (optional, boundary step only): S_W in fp64 and the pre-rounding codes.
+ */
+void oracle_q8_window_step(int64_t nh, int dk, int dv, int per_key, int W, int pos,
+                           int8_t *Z, float *a, double *G, double *K, double *U,
+                           const double *q, const double *k, const double *v,
+                           const double *gate, const double *beta, double *y,
+                           double *Sw_out, double *w_out)
+{
+    const int gdim = per_key ? dk : 1;
+#pragma omp parallel for schedule(static)
+    for (int64_t h = 0; h < nh; ++h) {
+        int8_t *Zh = Z + (size_t)h * dk * dv;
+        float *ah = a + (size_t)h * dk;
+        double *Gh = G + (size_t)h * W * gdim;
+        double *Kh = K + (size_t)h * W * dk;
+        double *Uh = U + (size_t)h * W * dv;
+        const double *qh = q + (size_t)h * dk, *kh = k + (size_t)h * dk;
+        const double *vh = v + (size_t)h * dv;
+        const double *gh = gate + (size_t)h * gdim;
+        double *yh = y + (size_t)h * dv;
+        const int l = pos + 1;
+
+        double *S0 = (double *)malloc(sizeof(double) * dk * dv);
+        double *St = (double *)malloc(sizeof(double) * dk * dv);
+        dequant_head(dk, dv, Zh, ah, S0);
+
+        /* the record's gate and key are known before its correction */
+        for (int i = 0; i < gdim; ++i)
+            Gh[IDX2(pos, i, gdim)] = gh[i];
+        for (int i = 0; i < dk; ++i)
+            Kh[IDX2(pos, i, dk)] = kh[i];
+
+        /* correction from S_{l-1}, read along the decayed key */
+        window_materialize(dk, dv, per_key, l - 1, S0, Gh, Kh, Uh, St);
+        for (int j = 0; j < dv; ++j) {
+            double p = 0.0;
+            for (int i = 0; i < dk; ++i)
+                p += St[IDX2(i, j, dv)] * gate_at(gh, per_key, i) * kh[i];
+            Uh[IDX2(pos, j, dv)] = beta[h] * (vh[j] - p);
+        }
+
+        /* readout from S_l */
+        window_materialize(dk, dv, per_key, l, S0, Gh, Kh, Uh, St);
+        for (int j = 0; j < dv; ++j) {
+            double acc = 0.0;
+            for (int i = 0; i < dk; ++i)
+                acc += St[IDX2(i, j, dv)] * qh[i];
+            yh[j] = acc;
+        }
+
+        if (l == W) {
+            if (Sw_out)
+                memcpy(Sw_out + (size_t)h * dk * dv, St, sizeof(double) * dk * dv);
+            oracle_q8_quantize(dk, dv, St, Zh, ah, w_out ? w_out + (size_t)h * dk * dv : NULL);
+        }
+        free(S0);
+        free(St);
+    }
+}
+
+/*
+ * One step of the base + log representation (DeltaLog, sec. 3.1, Algorithm 1,
+ * eqs. 2-7). The physical state of a head is the dense base Sbar, the cumulative
+ * log-decay lbar (one value, or one per key channel) and L live log entries
+ * (K_log[m], U_log[m], Lam_log[m]), m < L <= C. D(l) = diag(exp(l)).
+ * The logical state (eq. 7) is
+ *   S = D(lbar) Sbar + sum_{m<L} D(lbar - Lam_m) K_m U_m^T.
+ * With lambda_t = ln g_t (eq. 3) the step follows Algorithm 1:
+ *   1. read the old state: p = (D(lambda_t) S_{t-1})^T k    (the delta correction)
+ *   2. lbar += lambda_t                                      (eq. 4)
+ *   3. a = k, b = beta (v - p); y = S_t^T q with S_t of eq. 7 plus a b^T
+ *   4. L <  C: append (a, b, lbar) into slot L               (eq. 5); the caller sets L += 1
+ *   5. L == C: Sbar = S_t (eq. 6), lbar = 0; the caller sets L = 0.
+ * Log arrays: K[nh][C][dk], U[nh][C][dv], Lam[nh][C] or [nh][C][dk];
+ * lbar[nh] or [nh][dk].
+ */
+void oracle_log_step(int64_t nh, int dk, int dv, int per_key, int C, int L,
+                     double *Sbar, double *lbar, double *Klog, double *Ulog, double *Lam,
+                     const double *q, const double *k, const double *v,
+                     const double *gate, const double *beta, double *y)
+{
+    const int gdim = per_key ? dk : 1;
+#pragma omp parallel for schedule(static)
+    for (int64_t h = 0; h < nh; ++h) {
+        double *Sh = Sbar + (size_t)h * dk * dv;
+        double *lb = lbar + (size_t)h * gdim;
+        double *Kh = Klog + (size_t)h * C * dk;
+        double *Uh = Ulog + (size_t)h * C * dv;
+        double *Lh = Lam + (size_t)h * C * gdim;
+        const double *qh = q + (size_t)h * dk, *kh = k + (size_t)h * dk;
+        const double *vh = v + (size_t)h * dv;
+        const double *gh = gate + (size_t)h * gdim;
+        double *yh = y + (size_t)h * dv;
+        double *St = (double *)malloc(sizeof(double) * dk * dv);
+        double *b = (double *)malloc(sizeof(double) * dv);
+
+        /* eq. 7: the pre-update logical state */
+        for (int i = 0; i < dk; ++i) {
+            double li = lb[per_key ? i : 0];
+            for (int j = 0; j < dv; ++j) {
+                double s = exp(li) * Sh[IDX2(i, j, dv)];
+                for (int m = 0; m < L; ++m)
+                    s += exp(li - Lh[IDX2(m, per_key ? i : 0, gdim)]) * Kh[IDX2(m, i, dk)] *
+                         Uh[IDX2(m, j, dv)];
+                St[IDX2(i, j, dv)] = s;
+            }
+        }
+        /* 1. the old-state read of the delta rule, along the decayed key:
+              p = (D(lambda_t) S_{t-1})^T k with lambda_t = ln g_t */
+        for (int j = 0; j < dv; ++j) {
+            double p = 0.0;
+            for (int i = 0; i < dk; ++i) {
+                double lam = log(gate_at(gh, per_key, i));
+                p += exp(lam) * St[IDX2(i, j, dv)] * kh[i];
+            }
+            b[j] = beta[h] * (vh[j] - p);
+        }
+        /* 2. cumulative log-decay */
+        for (int i = 0; i < gdim; ++i)
+            lb[i] += log(gh[i]);
+        /* 3. post-update logical state (eq. 7 with the current pair a b^T) and output */
+        for (int i = 0; i < dk; ++i) {
+            double li = lb[per_key ? i : 0];
+            for (int j = 0; j < dv; ++j) {
+                double s = exp(li) * Sh[IDX2(i, j, dv)];
+                for (int m = 0; m < L; ++m)
+                    s += exp(li - Lh[IDX2(m, per_key ? i : 0, gdim)]) * Kh[IDX2(m, i, dk)] *
+                         Uh[IDX2(m, j, dv)];
+                St[IDX2(i, j, dv)] = s + kh[i] * b[j];
+            }
+        }
+        for (int j = 0; j < dv; ++j) {
+            double acc = 0.0;
+            for (int i = 0; i < dk; ++i)
+                acc += St[IDX2(i, j, dv)] * qh[i];
+            yh[j] = acc;
+        }
+        if (L < C) {
+            /* 4. append, eq. 5 */
+            for (int i = 0; i < dk; ++i)
+                Kh[IDX2(L, i, dk)] = kh[i];
+            for (int j = 0; j < dv; ++j)
+                Uh[IDX2(L, j, dv)] = b[j];
+            for (int i = 0; i < gdim; ++i)
+                Lh[IDX2(L, i, gdim)] = lb[i];
+        } else {
+            /* 5. merge, eq. 6, and reset */
+            memcpy(Sh, St, sizeof(double) * dk * dv);
+            for (int i = 0; i < gdim; ++i)
+                lb[i] = 0.0;
+        }
+        free(St);
+        free(b);
+    }
+}

@@ -1,0 +1,151 @@
+"""Seeded synthetic inputs for the delta-rule decode step.
+
+This module is shared by the HIP path's tests and benchmark and by the fp64
+oracle's tests. It holds random draws, the L2-normalisation of q and k that the
+workloads prescribe, and dtype casts of inputs -- and none of the recurrence's
+arithmetic.
+
+Workload shapes follow the decode-kernel experiments of the three pages:
+128x128 states per head (LeapQuant, sec. 4.3 "Kernel speedup"; DeltaLog, Table 3),
+32-48 heads per layer and batches of 4-512 requests, a window of 16 tokens
+(LeapQuant, sec. 4.1 "Implementation") and a merge interval of 8 for GDN
+(DeltaLog, Table 3).
+
+Every tensor of every step has its own substream:
+``numpy.random.SeedSequence([1000 + config_id, tensor_tag, step])`` feeding a
+PCG64 generator, so any step can be regenerated on its own.
+"""
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+
+DK = 128
+DV = 128
+
+# tensor tags of the substreams
+_TAG_S0, _TAG_Q, _TAG_K, _TAG_V, _TAG_GATE, _TAG_BETA, _TAG_OUTLIER = range(7)
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    cid: int
+    name: str
+    variant: str          # "gdn" (scalar gate alpha) or "kda" (per-key gate d)
+    path: str             # "dense", "q8_window" or "log"
+    B: int
+    H: int
+    steps: int
+    qkv: str              # "f32" or "bf16"
+    gate_lo: float
+    gate_hi: float
+    state_std: float = 0.02
+    W: int = 0            # window length of the int8 path
+    M: int = 0            # merge interval of the base+log path (capacity C = M - 1)
+    outliers: bool = False
+
+    @property
+    def heads(self) -> int:
+        return self.B * self.H
+
+    @property
+    def seed(self) -> int:
+        return 1000 + self.cid
+
+    @property
+    def per_key_gate(self) -> bool:
+        return self.variant == "kda"
+
+
+WORKLOADS = {
+    1: Workload(1, "gdn_dense_b4_h8_f32", "gdn", "dense", 4, 8, 64, "f32", 0.90, 0.999),
+    2: Workload(2, "gdn_dense_b256_h48_bf16", "gdn", "dense", 256, 48, 16, "bf16", 0.90, 0.999),
+    3: Workload(3, "kda_dense_b128_h32_bf16", "kda", "dense", 128, 32, 32, "bf16", 0.80, 1.0),
+    4: Workload(4, "gdn_q8_window_b256_h48_w16", "gdn", "q8_window", 256, 48, 256, "bf16",
+                0.90, 0.999, W=16, outliers=True),
+    5: Workload(5, "gdn_log_b256_h48_m8", "gdn", "log", 256, 48, 128, "bf16", 0.90, 0.999, M=8),
+}
+
+
+def custom(base: Workload, **changes) -> Workload:
+    """A workload with some fields replaced (smaller batches for fast parity runs)."""
+    return dataclasses.replace(base, **changes)
+
+
+def _rng(wl: Workload, tag: int, step: int = 0) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([wl.seed, tag, step])))
+
+
+def round_to_bf16(x: np.ndarray) -> np.ndarray:
+    """fp32 values rounded to the nearest bfloat16 (ties to even), returned as fp32.
+
+    Every returned value is exactly representable in bfloat16, so casting it to
+    bfloat16 on the device is exact and widening it to fp64 for the oracle is exact.
+    """
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    bits = x.view(np.uint32).astype(np.uint64)
+    bits = (bits + 0x7FFF + ((bits >> 16) & 1)) & 0xFFFF0000
+    return bits.astype(np.uint32).view(np.float32)
+
+
+def _cast(wl: Workload, x64: np.ndarray) -> np.ndarray:
+    x32 = x64.astype(np.float32)
+    return round_to_bf16(x32) if wl.qkv == "bf16" else x32
+
+
+def _unit_rows(x: np.ndarray) -> np.ndarray:
+    return x / np.linalg.norm(x, axis=-1, keepdims=True)
+
+
+def initial_state(wl: Workload) -> np.ndarray:
+    """S_0 of every head: fp32 [B*H, 128, 128], entries N(0, std^2).
+
+    For the int8 workload, 2 distinct key rows and 2 distinct value columns of
+    every head are multiplied by 50 (union of the row and column masks, so the
+    4 crossings are x50 too). Large rows and columns in real states are
+    described by LeapQuant (sec. 1; Figure 6) and by the STEPQuant notes
+    (row/column max-to-median ratios).
+    """
+    n = wl.heads
+    S = (_rng(wl, _TAG_S0).standard_normal((n, DK, DV)) * wl.state_std).astype(np.float32)
+    if wl.outliers:
+        r = _rng(wl, _TAG_OUTLIER)
+        for h in range(n):
+            rows = r.choice(DK, size=2, replace=False)
+            cols = r.choice(DV, size=2, replace=False)
+            mask = np.zeros((DK, DV), dtype=bool)
+            mask[rows, :] = True
+            mask[:, cols] = True
+            S[h][mask] *= np.float32(50.0)
+    return S
+
+
+def step_inputs(wl: Workload, t: int) -> dict:
+    """Inputs of decode step t (0-based) for all heads.
+
+    q, k: N(0,1) then L2-normalised over d_k in fp64, then cast to the
+    workload's input dtype (fp32 values, bf16-representable when qkv == bf16).
+    v: N(0,1) in the input dtype. gate: alpha ~ U(lo, hi) per head [B*H] for
+    GDN, d ~ U(lo, hi) per key channel [B*H, 128] for KDA. beta ~ U(0, 1) [B*H].
+    All arrays are fp32.
+    """
+    n = wl.heads
+    q = _cast(wl, _unit_rows(_rng(wl, _TAG_Q, t).standard_normal((n, DK))))
+    k = _cast(wl, _unit_rows(_rng(wl, _TAG_K, t).standard_normal((n, DK))))
+    v = _cast(wl, _rng(wl, _TAG_V, t).standard_normal((n, DV)))
+    gshape = (n, DK) if wl.per_key_gate else (n,)
+    gate = _rng(wl, _TAG_GATE, t).uniform(wl.gate_lo, wl.gate_hi, gshape).astype(np.float32)
+    beta = _rng(wl, _TAG_BETA, t).uniform(0.0, 1.0, (n,)).astype(np.float32)
+    return {"q": q, "k": k, "v": v, "gate": gate, "beta": beta}
+
+
+def sample_heads(wl: Workload, count: int, seed: int = 7) -> np.ndarray:
+    """Sorted distinct head indices for sampled full-size comparisons (always
+    includes the first and the last head)."""
+    n = wl.heads
+    if count >= n:
+        return np.arange(n)
+    r = np.random.default_rng(seed)
+    pick = set(r.choice(n, size=count - 2, replace=False).tolist()) | {0, n - 1}
+    return np.array(sorted(pick))
