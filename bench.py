@@ -1,0 +1,310 @@
+#!/usr/bin/env python3
+"""Benchmark of the batched decode-step update + readout of delta-rule states on one GPU.
+
+Default workload: Gated DeltaNet dense fp32 state, B=256 requests x H=48 heads,
+128x128 state per head (805 MB), bf16 q/k/v, 16 distinct steps of seeded
+synthetic inputs resident in HBM (cycled when more steps are timed).
+
+One "step" is one decode step of the whole batch: one launch of the dense step
+kernel (gate, k-read, correction, rank-one update, readout) over all B*H heads.
+
+Prints ONE JSON line on stdout:
+  value = state head-updates per second (B*H*K / timed seconds),
+  roofline = algorithmic HBM bytes per launch / average launch time vs 8 TB/s,
+  cpu_baseline = the fp64 oracle timed on the host cores on a bounded sample.
+Other workloads (--workload kda|q8|log|gdn_small) report the same fields for
+their own kernels; they are measurements, not the headline line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads as wl  # noqa: E402
+
+METRIC = "state head-updates/sec and achieved HBM GB/s (% of peak), B=256 H=48 decode"
+PEAK_HBM_GBS = 8000.0
+PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "counters_gdn_dense_b256_h48.txt")
+KERNEL_SOURCES = {
+    "dense": ["recurrent_state_update_head_amd/csrc/dense.hip",
+              "recurrent_state_update_head_amd/csrc/rsu_device.hpp"],
+}
+
+WORKLOAD_BY_FLAG = {"gdn": 2, "gdn_small": 1, "kda": 3, "q8": 4, "log": 5}
+
+
+# ----------------------------------------------------------------- byte accounting
+
+def _in_bytes(w: wl.Workload) -> int:
+    return 2 if w.qkv == "bf16" else 4
+
+
+def dense_bytes_per_head(w: wl.Workload) -> int:
+    """State read + write (fp32), q/k/v in their dtype, gate, beta, y (fp32)."""
+    d = wl.DK
+    gate = 4 * d if w.per_key_gate else 4
+    return 2 * 4 * d * d + 3 * d * _in_bytes(w) + gate + 4 + 4 * d
+
+
+def window_step_bytes_per_head(w: wl.Workload, pos: int) -> int:
+    """Int8 window step at position pos: codes + row scales, the pos records read,
+    the step inputs, y, and either the record write or (at the boundary) the
+    requantized codes and scales."""
+    d = wl.DK
+    gdim = d if w.per_key_gate else 1
+    rec = d * _in_bytes(w) + 4 * d + 4 * gdim
+    inputs = 3 * d * _in_bytes(w) + 4 * gdim + 4
+    rd = d * d + 4 * d + pos * rec + inputs
+    wr = 4 * d + ((d * d + 4 * d) if pos == w.W - 1 else rec)
+    return rd + wr
+
+
+def log_step_bytes_per_head(w: wl.Workload, L: int) -> int:
+    """Base+log step with L live entries: base read, L entries read, lbar, inputs,
+    y, and either the entry + lbar write (append) or the base + lbar write (merge)."""
+    d = wl.DK
+    C = w.M - 1
+    gdim = d if w.per_key_gate else 1
+    ent = d * _in_bytes(w) + 4 * d + 4 * gdim
+    inputs = 3 * d * _in_bytes(w) + 4 * gdim + 4
+    rd = 4 * d * d + L * ent + 4 * gdim + inputs
+    wr = 4 * d + (4 * d * d + 4 * gdim if L == C else ent + 4 * gdim)
+    return rd + wr
+
+
+def cycle_bytes_per_head(w: wl.Workload) -> float:
+    """Average algorithmic bytes per head-update over one window / merge cycle."""
+    if w.path == "dense":
+        return float(dense_bytes_per_head(w))
+    if w.path == "q8_window":
+        return sum(window_step_bytes_per_head(w, p) for p in range(w.W)) / w.W
+    return sum(log_step_bytes_per_head(w, L) for L in range(w.M)) / w.M
+
+
+# ----------------------------------------------------------------- counters on file
+
+def kernel_hash(kind: str) -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES[kind]:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def counter_traffic(bytes_per_launch: float):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was
+    taken on the current kernel source; else None."""
+    if not os.path.exists(PROFILE_COUNTERS):
+        return None
+    kv = {}
+    for line in open(PROFILE_COUNTERS):
+        if "=" in line and not line.lstrip().startswith("#"):
+            key, val = line.split("=", 1)
+            kv[key.strip()] = val.strip()
+    if kv.get("kernel_hash") != kernel_hash("dense"):
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+# ----------------------------------------------------------------- GPU runs
+
+def _dev_inputs(w, steps, torch, dev):
+    """All steps' inputs stacked on the device: dict of [steps, B, H, ...] tensors."""
+    dt = torch.bfloat16 if w.qkv == "bf16" else torch.float32
+    B, H = w.B, w.H
+    out = {n: [] for n in ("q", "k", "v", "gate", "beta")}
+    for t in range(steps):
+        x = wl.step_inputs(w, t)
+        for n in ("q", "k", "v"):
+            out[n].append(torch.from_numpy(x[n]).to(dev).to(dt).view(B, H, 128))
+        out["gate"].append(torch.from_numpy(x["gate"]).to(dev).view((B, H, 128) if w.per_key_gate else (B, H)))
+        out["beta"].append(torch.from_numpy(x["beta"]).to(dev).view(B, H))
+    return {n: torch.stack(v) for n, v in out.items()}
+
+
+def copy_ceiling(torch, rsu, nbytes: int, reps: int = 10) -> float:
+    """Read+write GB/s of the copy probe over a buffer of nbytes (counting both directions)."""
+    n = nbytes // 4 // 16384 * 16384
+    src = torch.empty(n, device="cuda").uniform_()
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        rsu.copy_f32(src, dst)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        rsu.copy_f32(src, dst)
+    e1.record()
+    torch.cuda.synchronize()
+    sec = e0.elapsed_time(e1) / 1e3 / reps
+    del src, dst
+    return 2 * n * 4 / sec / 1e9
+
+
+def run_gpu(w: wl.Workload, steps: int, warmup: int):
+    import torch
+    import recurrent_state_update_head_amd as rsu
+    dev = "cuda"
+    B, H = w.B, w.H
+    n_inputs = {"dense": w.steps, "q8_window": w.W, "log": w.M}[w.path]
+    n_inputs = min(n_inputs, max(1, w.steps))
+    x = _dev_inputs(w, n_inputs, torch, dev)
+    y = torch.empty(B, H, 128, device=dev)
+    S0 = torch.from_numpy(wl.initial_state(w)).to(dev).view(B, H, 128, 128)
+    kda = w.per_key_gate
+    state = {"t": 0}
+
+    if w.path == "dense":
+        fn = rsu.kda_decode_step if kda else rsu.gdn_decode_step
+        S = S0
+
+        def step():
+            i = state["t"] % n_inputs
+            fn(S, x["q"][i], x["k"][i], x["v"][i], x["gate"][i], x["beta"][i], y)
+            state["t"] += 1
+    elif w.path == "q8_window":
+        W = w.W
+        Z = torch.empty(B, H, 128, 128, device=dev, dtype=torch.int8)
+        A = torch.empty(B, H, 128, device=dev)
+        rsu.q8_quantize(S0, Z, A)
+        del S0
+        Kb = torch.zeros(B, H, W, 128, device=dev, dtype=x["q"].dtype)
+        Ub = torch.zeros(B, H, W, 128, device=dev)
+        Gb = torch.zeros((B, H, W, 128) if kda else (B, H, W), device=dev)
+        fn = rsu.kda_q8_window if kda else rsu.gdn_q8_window
+
+        def step():
+            t = state["t"]
+            i = t % n_inputs
+            fn(W, t % W, Z, A, Kb, Ub, Gb, x["q"][i], x["k"][i], x["v"][i], x["gate"][i], x["beta"][i], y)
+            state["t"] += 1
+    else:
+        C = w.M - 1
+        Sb = S0
+        lbar = torch.zeros((B, H, 128) if kda else (B, H), device=dev)
+        cap = max(C, 1)
+        Kl = torch.zeros(B, H, cap, 128, device=dev, dtype=x["q"].dtype)
+        Ul = torch.zeros(B, H, cap, 128, device=dev)
+        Lm = torch.zeros((B, H, cap, 128) if kda else (B, H, cap), device=dev)
+        app = rsu.kda_log_append if kda else rsu.gdn_log_append
+        mrg = rsu.kda_log_merge if kda else rsu.gdn_log_merge
+        state["L"] = 0
+
+        def step():
+            i = state["t"] % n_inputs
+            L = state["L"]
+            f = app if L < C else mrg
+            f(C, L, Sb, lbar, Kl, Ul, Lm, x["q"][i], x["k"][i], x["v"][i], x["gate"][i], x["beta"][i], y)
+            state["L"] = L + 1 if L < C else 0
+            state["t"] += 1
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_sec = e0.elapsed_time(e1) / 1e3
+    ceiling = copy_ceiling(torch, rsu, 4 * B * H * 128 * 128) if w.path == "dense" else None
+    return gpu_sec, wall, ceiling
+
+
+# ----------------------------------------------------------------- CPU baseline (oracle)
+
+def run_cpu_baseline(w: wl.Workload, budget_s: float = 12.0, max_steps: int = 16):
+    """The fp64 oracle (as it stands) on the host cores: every head of the workload,
+    consecutive steps until the time budget or max_steps is reached."""
+    import oracle
+    oracle.build(force=False)
+    S = wl.initial_state(w).astype(np.float64)
+    n_steps, t_total = 0, 0.0
+    for t in range(max_steps):
+        x = wl.step_inputs(w, t)
+        t0 = time.perf_counter()
+        oracle.dense_step(S, x["q"], x["k"], x["v"], x["gate"], x["beta"])
+        t_total += time.perf_counter() - t0
+        n_steps += 1
+        if t_total >= budget_s:
+            break
+    return {"value": w.heads * n_steps / t_total, "unit": "head-updates/s",
+            "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"all {w.heads} heads x {n_steps} consecutive steps of the same workload "
+                      f"(fp64 oracle, {t_total:.1f} s)"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None, help="timed steps (default: 256 for gdn)")
+    ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--workload", choices=sorted(WORKLOAD_BY_FLAG), default="gdn")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(this build has no multi-GPU path).", file=sys.stderr)
+        sys.exit(2)
+
+    w = wl.WORKLOADS[WORKLOAD_BY_FLAG[args.workload]]
+    cycle = {"dense": 1, "q8_window": w.W, "log": w.M}[w.path]
+    steps = args.steps if args.steps is not None else 256
+    steps = max(cycle, (steps + cycle - 1) // cycle * cycle)   # whole windows / cycles
+    warmup = args.warmup if args.warmup is not None else 2 * cycle
+    warmup = (warmup + cycle - 1) // cycle * cycle
+
+    gpu_sec, wall, ceiling = run_gpu(w, steps, warmup)
+    heads = w.heads
+    per_head = cycle_bytes_per_head(w)
+    launch_sec = gpu_sec / steps
+    achieved = per_head * heads / launch_sec / 1e9
+    traffic = counter_traffic(per_head * heads) if args.workload == "gdn" else None
+
+    out = {
+        "metric": METRIC,
+        "value": heads * steps / gpu_sec,
+        "unit": "head-updates/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": launch_sec * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded; shapes and distributions of the workload)",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "dk": 128, "dv": 128,
+                   "qkv": w.qkv, "state": "int8+f32 scales" if w.path == "q8_window" else "f32",
+                   "W": w.W or None, "M": w.M or None},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
+                     "algorithmic_bytes_per_launch": per_head * heads},
+        "hbm_copy_ceiling": ({"achieved": ceiling, "unit": "GB/s", "frac": ceiling / PEAK_HBM_GBS}
+                             if ceiling else None),
+        "wall_s_timed_region": wall,
+    }
+    if not args.no_cpu_baseline and w.path == "dense":
+        out["cpu_baseline"] = run_cpu_baseline(w)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,171 @@
+/*
+ * rsu.h -- C ABI of the MI355X (gfx950) decode-step library for delta-rule
+ * recurrent states (Gated DeltaNet and Kimi Delta Attention).
+ *
+ * Per head the state S is d_k x d_v = 128 x 128; row i is a key channel and
+ * column j a value channel. One decode step applies the retention gate g
+ * (a scalar alpha for GDN, a per-key vector d for KDA), reads the old value
+ * along the key from the decayed state, writes the beta-weighted correction
+ * and returns y = S^T q from the updated state:
+ *
+ *     u = beta (v - (Diag(g) S)^T k),   S <- Diag(g) S + k u^T,   y = S^T q
+ *
+ * (LeapQuant, sec. 3.1 eq. 1 and App. A, the GDN and KDA expansions with beta
+ * carried by the correction; STEPQuant reading notes, the unified recurrence
+ * with the step output read after the update.)
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Memory.   Every array pointer is a DEVICE pointer owned by the caller,
+ *           contiguous, row-major and 16-byte aligned. The library never
+ *           allocates, frees or synchronises; each call enqueues its kernels on
+ *           `stream` (NULL = the null stream) and returns without waiting.
+ * Shapes.   B requests x H heads. d_k and d_v must both be 128. B*H == 0 is a
+ *           valid empty batch: nothing is launched and 0 is returned.
+ * Inputs.   q, k [B,H,d_k] and v [B,H,d_v] are fp32 or bf16 (dims->qkv_dtype).
+ *           Gates and beta are fp32: alpha [B,H] (GDN) or d [B,H,d_k] (KDA),
+ *           beta [B,H]. Gates must be > 0 for the log path (it takes ln g).
+ * Outputs.  y [B,H,d_v] fp32.
+ * Errors.   The return value is RSU_OK or a negative RSU_E_* code. On error
+ *           nothing is launched and no buffer is written; rsu_last_error()
+ *           returns a message (per calling thread). RSU_E_HIP reports a failed
+ *           launch: the kernel did not run.
+ * Overlap.  Calls that write the same buffers must be ordered by the caller
+ *           (same stream, or events). Input and output arrays must not alias,
+ *           except where a buffer is documented as updated in place.
+ */
+#ifndef RSU_H
+#define RSU_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ABI-compatible with hipStream_t */
+typedef struct ihipStream_t *rsu_stream_t;
+
+enum rsu_dtype { RSU_F32 = 0, RSU_BF16 = 1 };
+
+enum rsu_status {
+    RSU_OK = 0,
+    RSU_E_NULL = -1,      /* a required pointer is NULL */
+    RSU_E_DIMS = -2,      /* B or H negative, d_k or d_v not 128, or B*H too large */
+    RSU_E_DTYPE = -3,     /* qkv_dtype not RSU_F32 / RSU_BF16 */
+    RSU_E_ALIGN = -4,     /* a pointer is not 16-byte aligned */
+    RSU_E_RANGE = -5,     /* W / pos / C / L out of range */
+    RSU_E_HIP = -6        /* the kernel launch failed */
+};
+
+typedef struct rsu_dims {
+    int32_t B, H;         /* requests, heads per request */
+    int32_t dk, dv;       /* must be 128, 128 */
+    int32_t qkv_dtype;    /* enum rsu_dtype: element type of q, k, v and of the stored keys */
+} rsu_dims;
+
+/* Version of this ABI (incremented on any signature or semantic change). */
+int rsu_abi_version(void);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char *rsu_last_error(void);
+
+/* ------------------------------------------------------------------------
+ * Dense fp32 state, one eager decode step.
+ * GDN (LeapQuant App. A, GDN expansion): the gate is alpha [B,H].
+ * KDA (LeapQuant App. A, KDA expansion): the gate is d [B,H,d_k].
+ * S [B,H,d_k,d_v] fp32 is read once and written once, updated in place.
+ * ---------------------------------------------------------------------- */
+int gdn_decode_step(const rsu_dims *dims, float *S, const void *q, const void *k,
+                    const void *v, const float *alpha, const float *beta, float *y,
+                    rsu_stream_t stream);
+int kda_decode_step(const rsu_dims *dims, float *S, const void *q, const void *k,
+                    const void *v, const float *d, const float *beta, float *y,
+                    rsu_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Int8 state with per-key-row scales (STEPQuant notes, the per-row absmax
+ * baseline; LeapQuant App. B.3, the /127 convention):
+ *   a_i = max_j |S_ij| (fp32),  z_ij = clamp(rne(S_ij * (127 / a_i)), -127, 127),
+ *   dequant = z_ij * a_i / 127;  a row of zeros gets a_i = 0 and z = 0.
+ * The reciprocal 127/a_i is one correctly rounded fp32 division, the product
+ * one fp32 multiplication, rounding is to nearest with ties to even.
+ *
+ * q8_quantize: quantize S [B,H,d_k,d_v] fp32 into Z [B,H,d_k,d_v] int8 and
+ * row_absmax [B,H,d_k] fp32 (the state at the start of the first window).
+ * ---------------------------------------------------------------------- */
+int q8_quantize(const rsu_dims *dims, const float *S, int8_t *Z, float *row_absmax,
+                rsu_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Per-window quantization (LeapQuant sec. 3.2, eqs. 3-4; readout App. B.2
+ * eq. 9). (Z, row_absmax) is the quantized window-start state and stays fixed
+ * inside the window; step pos (0 <= pos < W, the same for the whole batch)
+ * computes the correction u and the output from it and the pos earlier
+ * records, and stores its own record (g, k, u) in slot pos:
+ *   Kbuf [B,H,W,d_k] in qkv_dtype, Ubuf [B,H,W,d_v] fp32,
+ *   Gbuf [B,H,W] fp32 (GDN) or [B,H,W,d_k] fp32 (KDA).
+ * At pos == W-1 the step output is read from the unquantized state S_W, then
+ * S_W is requantized into Z and row_absmax in place (records of slot W-1 are
+ * not stored; the caller's next call uses pos = 0). 1 <= W <= 32.
+ * ---------------------------------------------------------------------- */
+int gdn_q8_window(const rsu_dims *dims, int W, int pos, int8_t *Z, float *row_absmax,
+                  void *Kbuf, float *Ubuf, float *Gbuf, const void *q, const void *k,
+                  const void *v, const float *alpha, const float *beta, float *y,
+                  rsu_stream_t stream);
+int kda_q8_window(const rsu_dims *dims, int W, int pos, int8_t *Z, float *row_absmax,
+                  void *Kbuf, float *Ubuf, float *Gbuf, const void *q, const void *k,
+                  const void *v, const float *d, const float *beta, float *y,
+                  rsu_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Dense base + bounded log (DeltaLog sec. 3.1, Algorithm 1, eqs. 4-7).
+ * Physical state: base Sbase [B,H,d_k,d_v] fp32; cumulative log-decay lbar
+ * [B,H] (GDN) or [B,H,d_k] (KDA) fp32; log of capacity C = M - 1 entries:
+ *   Klog [B,H,C,d_k] in qkv_dtype (the key factor a = k, stored losslessly),
+ *   Ulog [B,H,C,d_v] fp32 (the value factor b = u),
+ *   Lam  [B,H,C] (GDN) or [B,H,C,d_k] (KDA) fp32 (lbar after the entry's decay).
+ * L (0 <= L <= C, the same for the whole batch) is the live log length, kept
+ * by the caller. The represented state is eq. 7:
+ *   S = D(lbar) Sbase + sum_{m<L} D(lbar - Lam_m) K_m U_m^T,  D(l) = diag(exp l).
+ *
+ * *_log_append (requires 0 <= L < C): computes the correction and the output
+ * from the represented state, adds ln g to lbar, and writes entry L
+ * (Klog[L] = k, Ulog[L] = u, Lam[L] = lbar). Sbase is only read.
+ * The caller then sets L = L + 1.
+ *
+ * *_log_merge (requires L == C >= 0): the same step, but instead of appending
+ * it writes the represented state plus the current pair into Sbase (eq. 6)
+ * and resets lbar to 0. The caller then sets L = 0.
+ * C <= 16.
+ * ---------------------------------------------------------------------- */
+int gdn_log_append(const rsu_dims *dims, int C, int L, const float *Sbase, float *lbar,
+                   void *Klog, float *Ulog, float *Lam, const void *q, const void *k,
+                   const void *v, const float *alpha, const float *beta, float *y,
+                   rsu_stream_t stream);
+int kda_log_append(const rsu_dims *dims, int C, int L, const float *Sbase, float *lbar,
+                   void *Klog, float *Ulog, float *Lam, const void *q, const void *k,
+                   const void *v, const float *d, const float *beta, float *y,
+                   rsu_stream_t stream);
+int gdn_log_merge(const rsu_dims *dims, int C, int L, float *Sbase, float *lbar,
+                  const void *Klog, const float *Ulog, const float *Lam, const void *q,
+                  const void *k, const void *v, const float *alpha, const float *beta,
+                  float *y, rsu_stream_t stream);
+int kda_log_merge(const rsu_dims *dims, int C, int L, float *Sbase, float *lbar,
+                  const void *Klog, const float *Ulog, const float *Lam, const void *q,
+                  const void *k, const void *v, const float *d, const float *beta,
+                  float *y, rsu_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Measurement helper (not part of the recurrence): dst[i] = src[i] for
+ * n fp32 elements, with the same 128-bit non-temporal access pattern and grid
+ * shape (64 KiB per workgroup) as the dense step. n must be a multiple of 4.
+ * Used to find the practical read+write HBM ceiling and to calibrate counters.
+ * ---------------------------------------------------------------------- */
+int rsu_copy_f32(const float *src, float *dst, int64_t n, rsu_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RSU_H */

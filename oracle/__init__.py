@@ -49,11 +49,18 @@ def _load():
         lib.oracle_q8_window_step.argtypes = [I64, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P,
                                               P, P, P]
         lib.oracle_log_step.argtypes = [I64, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P, P]
+        lib.oracle_num_threads.argtypes = []
+        lib.oracle_num_threads.restype = ctypes.c_int
         for f in (lib.oracle_dense_step, lib.oracle_q8_quantize, lib.oracle_q8_window_step,
                   lib.oracle_log_step):
             f.restype = None
         _lib = lib
     return _lib
+
+
+def num_threads() -> int:
+    """OpenMP threads the oracle uses (one head per thread at a time)."""
+    return _load().oracle_num_threads()
 
 
 def _f64(x) -> np.ndarray:

@@ -16,11 +16,15 @@
  *   S[nh][dk][dv], q,k[nh][dk], v,y[nh][dv], gate[nh] or [nh][dk], beta[nh].
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
 
 #define IDX2(i, j, n2) ((size_t)(i) * (size_t)(n2) + (size_t)(j))
+
+/* threads the oracle spreads heads over */
+int oracle_num_threads(void) { return omp_get_max_threads(); }
 
 static double gate_at(const double *gate_h, int per_key, int i)
 {

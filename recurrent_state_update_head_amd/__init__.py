@@ -1,0 +1,221 @@
+"""Python binding of librsu.so, the gfx950 decode-step library for delta-rule
+recurrent states (Gated DeltaNet / Kimi Delta Attention).
+
+Argument marshalling only: every function checks torch tensors (device,
+dtype, contiguity, shape), derives the ``rsu_dims`` and calls the C entry point
+of the same name (include/rsu.h) on torch's current HIP stream. All the work
+runs in the HIP kernels; there is no fallback. Importing this package raises
+if the library has not been built (``python -m recurrent_state_update_head_amd._build``).
+
+Shapes (B requests, H heads, d = 128):
+  S, Sbase [B,H,d,d] fp32          q, k, v [B,H,d] fp32 or bf16 (all the same dtype)
+  alpha, beta [B,H] fp32           d (KDA gate) [B,H,d] fp32           y [B,H,d] fp32
+  Z [B,H,d,d] int8, row_absmax [B,H,d] fp32
+  Kbuf [B,H,W,d] (q dtype), Ubuf [B,H,W,d] fp32, Gbuf [B,H,W] or [B,H,W,d] fp32
+  Klog [B,H,C,d] (q dtype), Ulog [B,H,C,d] fp32, Lam [B,H,C] or [B,H,C,d] fp32,
+  lbar [B,H] or [B,H,d] fp32
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+from ._build import LIB as LIB_PATH
+
+D = 128
+RSU_F32, RSU_BF16 = 0, 1
+
+
+class RsuError(RuntimeError):
+    pass
+
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built; run `python -m recurrent_state_update_head_amd._build`")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+
+class _Dims(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("dk", ctypes.c_int32),
+                ("dv", ctypes.c_int32), ("qkv_dtype", ctypes.c_int32)]
+
+
+_P, _I = ctypes.c_void_p, ctypes.c_int
+_DP = ctypes.POINTER(_Dims)
+_SIGS = {
+    "gdn_decode_step": [_DP, _P, _P, _P, _P, _P, _P, _P, _P],
+    "kda_decode_step": [_DP, _P, _P, _P, _P, _P, _P, _P, _P],
+    "q8_quantize": [_DP, _P, _P, _P, _P],
+    "gdn_q8_window": [_DP, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
+    "kda_q8_window": [_DP, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
+    "gdn_log_append": [_DP, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
+    "kda_log_append": [_DP, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
+    "gdn_log_merge": [_DP, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
+    "kda_log_merge": [_DP, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
+    "rsu_copy_f32": [_P, _P, ctypes.c_int64, _P],
+}
+for _name, _args in _SIGS.items():
+    getattr(_lib, _name).argtypes = _args
+    getattr(_lib, _name).restype = ctypes.c_int
+_lib.rsu_abi_version.restype = ctypes.c_int
+_lib.rsu_last_error.restype = ctypes.c_char_p
+
+
+def abi_version() -> int:
+    return _lib.rsu_abi_version()
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t: torch.Tensor | None):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _call(name: str, *args):
+    rc = getattr(_lib, name)(*args)
+    if rc != 0:
+        raise RsuError(f"{name} returned {rc}: {_lib.rsu_last_error().decode()}")
+
+
+def _need(t: torch.Tensor, name: str, dtype, shape):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a HIP device, got {t.device}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _dims(q: torch.Tensor, k, v) -> _Dims:
+    if q.dim() != 3 or q.shape[-1] != D:
+        raise ValueError(f"q must be [B, H, {D}], got {tuple(q.shape)}")
+    if q.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError(f"q, k, v must be float32 or bfloat16, got {q.dtype}")
+    B, H = int(q.shape[0]), int(q.shape[1])
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, q.dtype, (B, H, D))
+    return _Dims(B, H, D, D, RSU_BF16 if q.dtype == torch.bfloat16 else RSU_F32)
+
+
+def _gate_shape(B, H, per_key):
+    return (B, H, D) if per_key else (B, H)
+
+
+def _step_common(dims, gate, beta, y, per_key, gname):
+    B, H = dims.B, dims.H
+    _need(gate, gname, torch.float32, _gate_shape(B, H, per_key))
+    _need(beta, "beta", torch.float32, (B, H))
+    _need(y, "y", torch.float32, (B, H, D))
+
+
+def _dense(name, per_key, S, q, k, v, gate, beta, y):
+    dims = _dims(q, k, v)
+    _need(S, "S", torch.float32, (dims.B, dims.H, D, D))
+    _step_common(dims, gate, beta, y, per_key, "d" if per_key else "alpha")
+    _call(name, ctypes.byref(dims), _ptr(S), _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(beta),
+          _ptr(y), _stream())
+    return y
+
+
+def gdn_decode_step(S, q, k, v, alpha, beta, y):
+    """One GDN decode step: S updated in place, y written. Returns y."""
+    return _dense("gdn_decode_step", False, S, q, k, v, alpha, beta, y)
+
+
+def kda_decode_step(S, q, k, v, d, beta, y):
+    """One KDA decode step (per-key gate d): S updated in place, y written. Returns y."""
+    return _dense("kda_decode_step", True, S, q, k, v, d, beta, y)
+
+
+def q8_quantize(S, Z, row_absmax):
+    """Per-key-row int8 quantization of S into (Z, row_absmax)."""
+    if S.dim() != 4:
+        raise ValueError("S must be [B, H, 128, 128]")
+    B, H = int(S.shape[0]), int(S.shape[1])
+    _need(S, "S", torch.float32, (B, H, D, D))
+    _need(Z, "Z", torch.int8, (B, H, D, D))
+    _need(row_absmax, "row_absmax", torch.float32, (B, H, D))
+    dims = _Dims(B, H, D, D, RSU_F32)
+    _call("q8_quantize", ctypes.byref(dims), _ptr(S), _ptr(Z), _ptr(row_absmax), _stream())
+
+
+def _window(name, per_key, W, pos, Z, row_absmax, Kbuf, Ubuf, Gbuf, q, k, v, gate, beta, y):
+    dims = _dims(q, k, v)
+    B, H = dims.B, dims.H
+    _need(Z, "Z", torch.int8, (B, H, D, D))
+    _need(row_absmax, "row_absmax", torch.float32, (B, H, D))
+    _need(Kbuf, "Kbuf", q.dtype, (B, H, W, D))
+    _need(Ubuf, "Ubuf", torch.float32, (B, H, W, D))
+    _need(Gbuf, "Gbuf", torch.float32, (B, H, W, D) if per_key else (B, H, W))
+    _step_common(dims, gate, beta, y, per_key, "d" if per_key else "alpha")
+    _call(name, ctypes.byref(dims), int(W), int(pos), _ptr(Z), _ptr(row_absmax), _ptr(Kbuf),
+          _ptr(Ubuf), _ptr(Gbuf), _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(beta), _ptr(y),
+          _stream())
+    return y
+
+
+def gdn_q8_window(W, pos, Z, row_absmax, Kbuf, Ubuf, Gbuf, q, k, v, alpha, beta, y):
+    """Step pos of a window of W on the int8 state (requantizes at pos == W - 1)."""
+    return _window("gdn_q8_window", False, W, pos, Z, row_absmax, Kbuf, Ubuf, Gbuf, q, k, v,
+                   alpha, beta, y)
+
+
+def kda_q8_window(W, pos, Z, row_absmax, Kbuf, Ubuf, Gbuf, q, k, v, d, beta, y):
+    return _window("kda_q8_window", True, W, pos, Z, row_absmax, Kbuf, Ubuf, Gbuf, q, k, v, d,
+                   beta, y)
+
+
+def _log(name, per_key, C, L, Sbase, lbar, Klog, Ulog, Lam, q, k, v, gate, beta, y):
+    dims = _dims(q, k, v)
+    B, H = dims.B, dims.H
+    _need(Sbase, "Sbase", torch.float32, (B, H, D, D))
+    _need(lbar, "lbar", torch.float32, _gate_shape(B, H, per_key))
+    if C > 0:
+        _need(Klog, "Klog", q.dtype, (B, H, C, D))
+        _need(Ulog, "Ulog", torch.float32, (B, H, C, D))
+        _need(Lam, "Lam", torch.float32, (B, H, C, D) if per_key else (B, H, C))
+    _step_common(dims, gate, beta, y, per_key, "d" if per_key else "alpha")
+    _call(name, ctypes.byref(dims), int(C), int(L), _ptr(Sbase), _ptr(lbar),
+          _ptr(Klog if C > 0 else None), _ptr(Ulog if C > 0 else None),
+          _ptr(Lam if C > 0 else None), _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(beta), _ptr(y),
+          _stream())
+    return y
+
+
+def gdn_log_append(C, L, Sbase, lbar, Klog, Ulog, Lam, q, k, v, alpha, beta, y):
+    """Decode step that appends entry L (requires L < C); the caller then sets L += 1."""
+    return _log("gdn_log_append", False, C, L, Sbase, lbar, Klog, Ulog, Lam, q, k, v, alpha, beta, y)
+
+
+def kda_log_append(C, L, Sbase, lbar, Klog, Ulog, Lam, q, k, v, d, beta, y):
+    return _log("kda_log_append", True, C, L, Sbase, lbar, Klog, Ulog, Lam, q, k, v, d, beta, y)
+
+
+def gdn_log_merge(C, L, Sbase, lbar, Klog, Ulog, Lam, q, k, v, alpha, beta, y):
+    """Decode step that folds the log into Sbase (requires L == C); the caller then sets L = 0."""
+    return _log("gdn_log_merge", False, C, L, Sbase, lbar, Klog, Ulog, Lam, q, k, v, alpha, beta, y)
+
+
+def kda_log_merge(C, L, Sbase, lbar, Klog, Ulog, Lam, q, k, v, d, beta, y):
+    return _log("kda_log_merge", True, C, L, Sbase, lbar, Klog, Ulog, Lam, q, k, v, d, beta, y)
+
+
+def copy_f32(src: torch.Tensor, dst: torch.Tensor):
+    """dst <- src with the dense step's access pattern (HBM ceiling probe)."""
+    _need(src, "src", torch.float32, src.shape)
+    _need(dst, "dst", torch.float32, src.shape)
+    _call("rsu_copy_f32", _ptr(src), _ptr(dst), src.numel(), _stream())
+
+
+def raw_library() -> ctypes.CDLL:
+    """The loaded librsu.so (for ABI-level tests)."""
+    return _lib

@@ -1,0 +1,219 @@
+// api.hip -- the extern "C" entry points declared in include/rsu.h: argument
+// validation, error reporting, kernel dispatch. Nothing here allocates memory
+// or synchronises the device.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <initializer_list>
+
+#include "../../include/rsu.h"
+#include "kernels.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+// dims, dtype; on success *heads = B * H
+int check_dims(const rsu_dims* d, int* heads, const char* fn) {
+    g_err[0] = '\0';
+    if (!d) return fail(RSU_E_NULL, "%s: dims is NULL", fn);
+    if (d->B < 0 || d->H < 0) return fail(RSU_E_DIMS, "%s: B=%d H=%d must be >= 0", fn, d->B, d->H);
+    if (d->dk != 128 || d->dv != 128)
+        return fail(RSU_E_DIMS, "%s: dk=%d dv=%d, only 128 x 128 states are supported", fn, d->dk, d->dv);
+    const long long n = static_cast<long long>(d->B) * d->H;
+    if (n > 0x7fffffffLL) return fail(RSU_E_DIMS, "%s: B*H=%lld exceeds the grid limit", fn, n);
+    if (d->qkv_dtype != RSU_F32 && d->qkv_dtype != RSU_BF16)
+        return fail(RSU_E_DTYPE, "%s: qkv_dtype=%d is neither RSU_F32 nor RSU_BF16", fn, d->qkv_dtype);
+    *heads = static_cast<int>(n);
+    return RSU_OK;
+}
+
+struct Ptr {
+    const void* p;
+    const char* name;
+};
+
+int check_ptrs(std::initializer_list<Ptr> ptrs, const char* fn) {
+    for (const Ptr& x : ptrs)
+        if (!x.p) return fail(RSU_E_NULL, "%s: %s is NULL", fn, x.name);
+    for (const Ptr& x : ptrs)
+        if (reinterpret_cast<uintptr_t>(x.p) % 16 != 0)
+            return fail(RSU_E_ALIGN, "%s: %s is not 16-byte aligned", fn, x.name);
+    return RSU_OK;
+}
+
+int launched(hipError_t e, const char* fn) {
+    if (e != hipSuccess) return fail(RSU_E_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+    return RSU_OK;
+}
+
+rsu::StepArgs step_args(int heads, float* S, const void* q, const void* k, const void* v,
+                        const float* gate, const float* beta, float* y) {
+    rsu::StepArgs a;
+    a.heads = heads;
+    a.S = S;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.gate = gate;
+    a.beta = beta;
+    a.y = y;
+    return a;
+}
+
+int dense_common(const char* fn, bool per_key, const rsu_dims* dims, float* S, const void* q,
+                 const void* k, const void* v, const float* gate, const float* beta, float* y,
+                 rsu_stream_t stream) {
+    int heads = 0;
+    if (int rc = check_dims(dims, &heads, fn)) return rc;
+    if (heads == 0) return RSU_OK;
+    if (int rc = check_ptrs({{S, "S"}, {q, "q"}, {k, "k"}, {v, "v"}, {gate, per_key ? "d" : "alpha"},
+                             {beta, "beta"}, {y, "y"}}, fn))
+        return rc;
+    return launched(rsu::launch_dense(step_args(heads, S, q, k, v, gate, beta, y), per_key,
+                                      dims->qkv_dtype == RSU_BF16, stream),
+                    fn);
+}
+
+int window_common(const char* fn, bool per_key, const rsu_dims* dims, int W, int pos, int8_t* Z,
+                  float* A, void* Kbuf, float* Ubuf, float* Gbuf, const void* q, const void* k,
+                  const void* v, const float* gate, const float* beta, float* y,
+                  rsu_stream_t stream) {
+    int heads = 0;
+    if (int rc = check_dims(dims, &heads, fn)) return rc;
+    if (W < 1 || W > rsu::kMaxW) return fail(RSU_E_RANGE, "%s: W=%d outside [1, %d]", fn, W, rsu::kMaxW);
+    if (pos < 0 || pos >= W) return fail(RSU_E_RANGE, "%s: pos=%d outside [0, W=%d)", fn, pos, W);
+    if (heads == 0) return RSU_OK;
+    if (int rc = check_ptrs({{Z, "Z"}, {A, "row_absmax"}, {Kbuf, "Kbuf"}, {Ubuf, "Ubuf"},
+                             {Gbuf, "Gbuf"}, {q, "q"}, {k, "k"}, {v, "v"},
+                             {gate, per_key ? "d" : "alpha"}, {beta, "beta"}, {y, "y"}}, fn))
+        return rc;
+    rsu::WindowArgs w;
+    w.W = W;
+    w.pos = pos;
+    w.Z = Z;
+    w.A = A;
+    w.Kbuf = Kbuf;
+    w.Ubuf = Ubuf;
+    w.Gbuf = Gbuf;
+    return launched(rsu::launch_q8_window(step_args(heads, nullptr, q, k, v, gate, beta, y), w,
+                                          per_key, dims->qkv_dtype == RSU_BF16, stream),
+                    fn);
+}
+
+int log_common(const char* fn, bool per_key, bool merge, const rsu_dims* dims, int C, int L,
+               float* Sbase, float* lbar, void* Klog, float* Ulog, float* Lam, const void* q,
+               const void* k, const void* v, const float* gate, const float* beta, float* y,
+               rsu_stream_t stream) {
+    int heads = 0;
+    if (int rc = check_dims(dims, &heads, fn)) return rc;
+    if (C < 0 || C > rsu::kMaxC) return fail(RSU_E_RANGE, "%s: C=%d outside [0, %d]", fn, C, rsu::kMaxC);
+    if (merge && L != C) return fail(RSU_E_RANGE, "%s: merge needs L == C, got L=%d C=%d", fn, L, C);
+    if (!merge && (L < 0 || L >= C))
+        return fail(RSU_E_RANGE, "%s: append needs 0 <= L < C, got L=%d C=%d", fn, L, C);
+    if (heads == 0) return RSU_OK;
+    if (int rc = check_ptrs({{Sbase, "Sbase"}, {lbar, "lbar"}, {q, "q"}, {k, "k"}, {v, "v"},
+                             {gate, per_key ? "d" : "alpha"}, {beta, "beta"}, {y, "y"}}, fn))
+        return rc;
+    if (C > 0)
+        if (int rc = check_ptrs({{Klog, "Klog"}, {Ulog, "Ulog"}, {Lam, "Lam"}}, fn)) return rc;
+    rsu::LogArgs l;
+    l.C = C;
+    l.L = L;
+    l.lbar = lbar;
+    l.Klog = Klog;
+    l.Ulog = Ulog;
+    l.Lam = Lam;
+    return launched(rsu::launch_log(step_args(heads, Sbase, q, k, v, gate, beta, y), l, merge, per_key,
+                                    dims->qkv_dtype == RSU_BF16, stream),
+                    fn);
+}
+
+}  // namespace
+
+extern "C" {
+
+int rsu_abi_version(void) { return 1; }
+
+const char* rsu_last_error(void) { return g_err; }
+
+int gdn_decode_step(const rsu_dims* dims, float* S, const void* q, const void* k, const void* v,
+                    const float* alpha, const float* beta, float* y, rsu_stream_t stream) {
+    return dense_common("gdn_decode_step", false, dims, S, q, k, v, alpha, beta, y, stream);
+}
+
+int kda_decode_step(const rsu_dims* dims, float* S, const void* q, const void* k, const void* v,
+                    const float* d, const float* beta, float* y, rsu_stream_t stream) {
+    return dense_common("kda_decode_step", true, dims, S, q, k, v, d, beta, y, stream);
+}
+
+int q8_quantize(const rsu_dims* dims, const float* S, int8_t* Z, float* row_absmax,
+                rsu_stream_t stream) {
+    int heads = 0;
+    if (int rc = check_dims(dims, &heads, "q8_quantize")) return rc;
+    if (heads == 0) return RSU_OK;
+    if (int rc = check_ptrs({{S, "S"}, {Z, "Z"}, {row_absmax, "row_absmax"}}, "q8_quantize")) return rc;
+    return launched(rsu::launch_q8_quantize(heads, S, Z, row_absmax, stream), "q8_quantize");
+}
+
+int gdn_q8_window(const rsu_dims* dims, int W, int pos, int8_t* Z, float* row_absmax, void* Kbuf,
+                  float* Ubuf, float* Gbuf, const void* q, const void* k, const void* v,
+                  const float* alpha, const float* beta, float* y, rsu_stream_t stream) {
+    return window_common("gdn_q8_window", false, dims, W, pos, Z, row_absmax, Kbuf, Ubuf, Gbuf, q, k,
+                         v, alpha, beta, y, stream);
+}
+
+int kda_q8_window(const rsu_dims* dims, int W, int pos, int8_t* Z, float* row_absmax, void* Kbuf,
+                  float* Ubuf, float* Gbuf, const void* q, const void* k, const void* v,
+                  const float* d, const float* beta, float* y, rsu_stream_t stream) {
+    return window_common("kda_q8_window", true, dims, W, pos, Z, row_absmax, Kbuf, Ubuf, Gbuf, q, k,
+                         v, d, beta, y, stream);
+}
+
+int gdn_log_append(const rsu_dims* dims, int C, int L, const float* Sbase, float* lbar, void* Klog,
+                   float* Ulog, float* Lam, const void* q, const void* k, const void* v,
+                   const float* alpha, const float* beta, float* y, rsu_stream_t stream) {
+    return log_common("gdn_log_append", false, false, dims, C, L, const_cast<float*>(Sbase), lbar,
+                      Klog, Ulog, Lam, q, k, v, alpha, beta, y, stream);
+}
+
+int kda_log_append(const rsu_dims* dims, int C, int L, const float* Sbase, float* lbar, void* Klog,
+                   float* Ulog, float* Lam, const void* q, const void* k, const void* v,
+                   const float* d, const float* beta, float* y, rsu_stream_t stream) {
+    return log_common("kda_log_append", true, false, dims, C, L, const_cast<float*>(Sbase), lbar,
+                      Klog, Ulog, Lam, q, k, v, d, beta, y, stream);
+}
+
+int gdn_log_merge(const rsu_dims* dims, int C, int L, float* Sbase, float* lbar, const void* Klog,
+                  const float* Ulog, const float* Lam, const void* q, const void* k, const void* v,
+                  const float* alpha, const float* beta, float* y, rsu_stream_t stream) {
+    return log_common("gdn_log_merge", false, true, dims, C, L, Sbase, lbar, const_cast<void*>(Klog),
+                      const_cast<float*>(Ulog), const_cast<float*>(Lam), q, k, v, alpha, beta, y,
+                      stream);
+}
+
+int kda_log_merge(const rsu_dims* dims, int C, int L, float* Sbase, float* lbar, const void* Klog,
+                  const float* Ulog, const float* Lam, const void* q, const void* k, const void* v,
+                  const float* d, const float* beta, float* y, rsu_stream_t stream) {
+    return log_common("kda_log_merge", true, true, dims, C, L, Sbase, lbar, const_cast<void*>(Klog),
+                      const_cast<float*>(Ulog), const_cast<float*>(Lam), q, k, v, d, beta, y, stream);
+}
+
+int rsu_copy_f32(const float* src, float* dst, int64_t n, rsu_stream_t stream) {
+    g_err[0] = '\0';
+    if (n < 0 || n % 4 != 0) return fail(RSU_E_DIMS, "rsu_copy_f32: n=%lld must be a multiple of 4", (long long)n);
+    if (n / (128 * 128) >= 0x7fffffffLL) return fail(RSU_E_DIMS, "rsu_copy_f32: n too large");
+    if (n == 0) return RSU_OK;
+    if (int rc = check_ptrs({{src, "src"}, {dst, "dst"}}, "rsu_copy_f32")) return rc;
+    return launched(rsu::launch_copy(src, dst, n, stream), "rsu_copy_f32");
+}
+
+}  // extern "C"

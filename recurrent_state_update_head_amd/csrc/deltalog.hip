@@ -1,0 +1,163 @@
+// deltalog.hip -- dense fp32 base plus a bounded log of (a, b) factor pairs.
+//
+// DeltaLog, sec. 3.1 (Algorithm 1, eqs. 4-7): the state of a head is
+//   S = D(lbar) Sbar + sum_{m<L} D(lbar - Lam_m) K_m U_m^T,   D(l) = diag(exp l),
+// with lbar the log-decay accumulated since the last merge and Lam_m the value
+// of lbar when entry m was appended. One decode step with gate g (lambda = ln g):
+//   lbar' = lbar + lambda
+//   p = (D(lambda) S)^T k = Sbar^T (e^{lbar'} k) + sum_m U_m (K_m . e^{lbar'-Lam_m} k)
+//   b = beta (v - p),  a = k
+//   y = S'^T q = Sbar^T (e^{lbar'} q) + sum_m U_m (K_m . e^{lbar'-Lam_m} q) + b (k . q)
+// then either the pair is appended (eq. 5: K_L = a, U_L = b, Lam_L = lbar')
+// or, when the log is full, the represented state plus a b^T is written back
+// into Sbar (eq. 6) and lbar is reset.
+//
+// The base is swept once per step for both read vectors (same fp32 layout as
+// the dense step); the key-side replay coefficients K_m . (...) are computed
+// once per head in the preparation phase and shared by all value columns.
+// Append steps only read the 64 KiB base; merge steps also write it.
+#include "kernels.hpp"
+#include "rsu_device.hpp"
+
+namespace rsu {
+
+template <bool kPerKey, bool kMerge, typename T>
+__global__ __launch_bounds__(kThreads) void log_step_kernel(
+    int C, int L, float* __restrict__ Sbase, float* __restrict__ lbar, T* __restrict__ Klog,
+    float* __restrict__ Ulog, float* __restrict__ Lam, const T* __restrict__ q,
+    const T* __restrict__ k, const T* __restrict__ v, const float* __restrict__ gate,
+    const float* __restrict__ beta, float* __restrict__ y) {
+    constexpr int kCp = kMaxC;                 // row stride of the merge coefficients
+    __shared__ f32x4 row_vec[kD];              // (E k, E q, k, E), E = exp(lbar') per key row
+    __shared__ f32x2 coefp[2][kMaxC];          // per entry (K_m . Dk, K_m . Dq), per half of the rows
+    __shared__ float kq_part[2];
+    __shared__ float kd[kMerge ? kD * kCp : 1];  // merge: exp(lbar' - Lam_m) K_m at row r
+
+    const int h = blockIdx.x, tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
+    const int ro = lane >> 3;
+    const int col = wave * 32 + (lane & 7) * 4;
+    const size_t vec_off = static_cast<size_t>(h) * kD;
+    const int gdim = kPerKey ? kD : 1;
+
+    float* Sh = Sbase + static_cast<size_t>(h) * kD * kD;
+    f32x4 s[kRowsPerThread];
+#pragma unroll
+    for (int it = 0; it < kRowsPerThread; ++it) s[it] = stream_load(Sh + (it * 8 + ro) * kD + col);
+    const f32x4 vv = load4_in(v, vec_off + col);
+    const float bt = beta[h];
+
+    // ---- key-side preparation: thread -> key row r, entry parity par
+    const int r = tid & (kD - 1), par = tid >> 7;
+    const float kr = load_in(k, vec_off + r), qr = load_in(q, vec_off + r);
+    const float gr = kPerKey ? gate[vec_off + r] : gate[h];
+    const float lb_new = (kPerKey ? lbar[vec_off + r] : lbar[h]) + logf(gr);
+    {
+        const T* Kh = Klog + static_cast<size_t>(h) * C * kD;
+        const float* Lh = Lam + static_cast<size_t>(h) * C * gdim;
+        for (int m = 0; m < L; ++m) {
+            const float lam = kPerKey ? Lh[static_cast<size_t>(m) * kD + r] : Lh[m];
+            const float e = expf(lb_new - lam) * load_in(Kh, static_cast<size_t>(m) * kD + r);
+            if ((m & 1) == par) {
+                const f32x2 c = wave_sum2(f32x2{e * kr, e * qr});
+                if (lane == 0) coefp[wave & 1][m] = c;
+            }
+            if (kMerge && par == 0) kd[r * kCp + m] = e;
+        }
+        if (par == 0) {
+            const float E = expf(lb_new);
+            row_vec[r] = f32x4{E * kr, E * qr, kr, E};
+            const float kq = wave_sum(kr * qr);
+            if (lane == 0) kq_part[wave] = kq;
+            if (kMerge)
+                for (int m = L; m < ((C + 3) & ~3); ++m) kd[r * kCp + m] = 0.f;
+        }
+    }
+    __syncthreads();
+
+    // metadata: one writer per element (all reads of lbar / Lam are done)
+    if (par == 0) {
+        if (kMerge) {
+            if (kPerKey) lbar[vec_off + r] = 0.f;
+            else if (r == 0) lbar[h] = 0.f;
+        } else {
+            const size_t ent = static_cast<size_t>(h) * C + L;
+            store_in(Klog, ent * kD + r, kr);
+            if (kPerKey) {
+                Lam[ent * kD + r] = lb_new;
+                lbar[vec_off + r] = lb_new;
+            } else if (r == 0) {
+                Lam[ent] = lb_new;
+                lbar[h] = lb_new;
+            }
+        }
+    }
+
+    // ---- sweep of the base for both read vectors, plus the log entries
+    f32x4 p1 = {0.f, 0.f, 0.f, 0.f}, p2 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int it = 0; it < kRowsPerThread; ++it) {
+        const f32x4 rv = row_vec[it * 8 + ro];
+        p1 += s[it] * rv.x;
+        p2 += s[it] * rv.y;
+    }
+    const float* Uh = Ulog + static_cast<size_t>(h) * C * kD;
+    for (int m = ro; m < L; m += 8) {
+        const f32x2 c = coefp[0][m] + coefp[1][m];
+        const f32x4 u = *reinterpret_cast<const f32x4*>(Uh + static_cast<size_t>(m) * kD + col);
+        p1 += u * c.x;
+        p2 += u * c.y;
+    }
+    p1 = sum_row_lanes(p1);
+    p2 = sum_row_lanes(p2);
+    const float kq = kq_part[0] + kq_part[1];
+    const f32x4 b = bt * (vv - p1);
+    if (ro == 0) {
+        *reinterpret_cast<f32x4*>(y + vec_off + col) = p2 + b * kq;
+        if (!kMerge) *reinterpret_cast<f32x4*>(Ulog + (static_cast<size_t>(h) * C + L) * kD + col) = b;
+    }
+    if (!kMerge) return;
+
+    // ---- merge (eq. 6): Sbar <- D(lbar') Sbar + sum_m D(lbar'-Lam_m) K_m U_m^T + k b^T
+#pragma unroll
+    for (int it = 0; it < kRowsPerThread; ++it) {
+        const f32x4 rv = row_vec[it * 8 + ro];
+        s[it] = s[it] * rv.w + rv.z * b;
+    }
+    for (int m0 = 0; m0 < L; m0 += 4) {
+        f32x4 u[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            u[i] = (m0 + i < L) ? *reinterpret_cast<const f32x4*>(Uh + static_cast<size_t>(m0 + i) * kD + col)
+                                : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int it = 0; it < kRowsPerThread; ++it) {
+            const f32x4 e = *reinterpret_cast<const f32x4*>(kd + (it * 8 + ro) * kCp + m0);
+            s[it] += u[0] * e.x + u[1] * e.y + u[2] * e.z + u[3] * e.w;
+        }
+    }
+#pragma unroll
+    for (int it = 0; it < kRowsPerThread; ++it) stream_store(Sh + (it * 8 + ro) * kD + col, s[it]);
+}
+
+template <bool kPerKey, bool kMerge, typename T>
+static hipError_t launch_log_t(const StepArgs& a, const LogArgs& l, hipStream_t stream) {
+    hipLaunchKernelGGL((log_step_kernel<kPerKey, kMerge, T>), dim3(a.heads), dim3(kThreads), 0, stream,
+                       l.C, l.L, a.S, l.lbar, static_cast<T*>(l.Klog), l.Ulog, l.Lam,
+                       static_cast<const T*>(a.q), static_cast<const T*>(a.k),
+                       static_cast<const T*>(a.v), a.gate, a.beta, a.y);
+    return hipGetLastError();
+}
+
+template <bool kPerKey, typename T>
+static hipError_t launch_log_m(const StepArgs& a, const LogArgs& l, bool merge, hipStream_t stream) {
+    return merge ? launch_log_t<kPerKey, true, T>(a, l, stream) : launch_log_t<kPerKey, false, T>(a, l, stream);
+}
+
+hipError_t launch_log(const StepArgs& a, const LogArgs& l, bool merge, bool per_key, bool bf16,
+                      hipStream_t stream) {
+    if (per_key) return bf16 ? launch_log_m<true, bf16_t>(a, l, merge, stream) : launch_log_m<true, float>(a, l, merge, stream);
+    return bf16 ? launch_log_m<false, bf16_t>(a, l, merge, stream) : launch_log_m<false, float>(a, l, merge, stream);
+}
+
+}  // namespace rsu

@@ -1,0 +1,47 @@
+// kernels.hpp -- host-side launchers of the gfx950 kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rsu {
+
+constexpr int kMaxW = 32;  // window length limit of the int8 path (LDS of the boundary step)
+constexpr int kMaxC = 16;  // log capacity limit of the base + log path
+
+// Per-step inputs shared by every representation; pointers are device pointers.
+struct StepArgs {
+    int heads;                    // B * H (one workgroup per head)
+    float* S;                     // dense fp32 state, or the base of the log path
+    const void *q, *k, *v;        // [heads, 128] in fp32 or bf16
+    const float* gate;            // [heads] or [heads, 128]
+    const float* beta;            // [heads]
+    float* y;                     // [heads, 128]
+};
+
+struct WindowArgs {
+    int W, pos;
+    int8_t* Z;                    // [heads, 128, 128]
+    float* A;                     // [heads, 128] row absmax
+    void* Kbuf;                   // [heads, W, 128] in the input dtype
+    float* Ubuf;                  // [heads, W, 128]
+    float* Gbuf;                  // [heads, W] or [heads, W, 128]
+};
+
+struct LogArgs {
+    int C, L;
+    float* lbar;                  // [heads] or [heads, 128]
+    void* Klog;                   // [heads, C, 128] in the input dtype
+    float* Ulog;                  // [heads, C, 128]
+    float* Lam;                   // [heads, C] or [heads, C, 128]
+};
+
+hipError_t launch_dense(const StepArgs& a, bool per_key, bool bf16, hipStream_t stream);
+hipError_t launch_copy(const float* src, float* dst, int64_t n, hipStream_t stream);
+hipError_t launch_q8_quantize(int heads, const float* S, int8_t* Z, float* A, hipStream_t stream);
+hipError_t launch_q8_window(const StepArgs& a, const WindowArgs& w, bool per_key, bool bf16,
+                            hipStream_t stream);
+hipError_t launch_log(const StepArgs& a, const LogArgs& l, bool merge, bool per_key, bool bf16,
+                      hipStream_t stream);
+
+}  // namespace rsu

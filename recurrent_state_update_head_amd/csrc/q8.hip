@@ -1,0 +1,249 @@
+// q8.hip -- int8 state with per-key-row absmax scales, quantized once per window.
+//
+// Per-window quantization (LeapQuant, sec. 3.2, eqs. 3-4; App. B.2, eq. 9):
+// the quantized window-start state S^_0 = (Z, a) stays fixed while the window's
+// records (g_j, k_j, u_j) are buffered in higher precision. Step l of the
+// window (0-based pos = l - 1) reads, for x = g_l * k_l (the delta read from
+// the decayed state) and for x = q (the readout of the updated state),
+//   S_{l-1}^T x = S^_0^T Gamma_{1:l-1} x + sum_{j<l} u_j (k_j . Gamma_{j+1:l-1} x)
+// and S_l^T q = S_{l-1}^T (g_l q) + u_l (k_l . q). The int8 tile is swept once
+// for both read vectors, with the row scale a_i / 127 and the cumulative decay
+// folded into the read vectors, so dequantization costs one conversion per code.
+// At l = W the full state S_W of eq. 4 is formed in registers, its per-row
+// absmax taken and the tile requantized in place.
+//
+// Thread layout of the int8 tile (one 256-thread workgroup per head): lane l
+// of wave w owns columns 4(l & 31) .. +3 and rows 8*it + 2w + (l >> 5),
+// it = 0..15, i.e. one 32-bit word of codes per row; one wave-wide load covers
+// two full rows (256 contiguous bytes).
+#include "kernels.hpp"
+#include "rsu_device.hpp"
+
+namespace rsu {
+
+__device__ __forceinline__ f32x4 unpack_i8x4(uint32_t w) {
+    return f32x4{static_cast<float>(static_cast<int8_t>(w & 0xffu)),
+                 static_cast<float>(static_cast<int8_t>((w >> 8) & 0xffu)),
+                 static_cast<float>(static_cast<int8_t>((w >> 16) & 0xffu)),
+                 static_cast<float>(static_cast<int8_t>(w >> 24))};
+}
+
+__device__ __forceinline__ uint32_t quant_code(float x, float scale) {
+    float z = __builtin_rintf(x * scale);  // round to nearest, ties to even
+    z = fminf(fmaxf(z, -127.f), 127.f);
+    return static_cast<uint32_t>(static_cast<int32_t>(z)) & 0xffu;
+}
+
+__device__ __forceinline__ int q8_row(int it, int wave, int ro) { return 8 * it + 2 * wave + ro; }
+
+// Requantize a head's fp32 tile held in registers (int8 layout) into Zh / Ah:
+// a_i = max_j |S_ij|, scale = 127 / a_i (one correctly rounded fp32 division),
+// z = clamp(rne(S * scale), -127, 127); a zero row gets a_i = 0 and z = 0.
+// Every thread of the workgroup must call it (it contains a barrier).
+__device__ __forceinline__ void requantize_tile(const f32x4 (&s)[kRowsPerThread], uint32_t* Zh,
+                                                float* Ah, float* scale_s, int wave, int lane) {
+    const int c4 = lane & 31, ro = lane >> 5;
+    float amax[kRowsPerThread];
+#pragma unroll
+    for (int it = 0; it < kRowsPerThread; ++it) {
+        float m = fmaxf(fmaxf(fabsf(s[it].x), fabsf(s[it].y)), fmaxf(fabsf(s[it].z), fabsf(s[it].w)));
+#pragma unroll
+        for (int sh = 1; sh <= 16; sh <<= 1) m = fmaxf(m, xor_shfl(m, sh));
+        amax[it] = m;
+    }
+    // lane c4 (< 16) of each half-wave publishes the scale of row (c4, wave, ro)
+    float mine = 0.f;
+#pragma unroll
+    for (int it = 0; it < kRowsPerThread; ++it) mine = (c4 == it) ? amax[it] : mine;
+    if (c4 < kRowsPerThread) {
+        const int r = q8_row(c4, wave, ro);
+        scale_s[r] = mine > 0.f ? __fdiv_rn(127.f, mine) : 0.f;
+        Ah[r] = mine;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int it = 0; it < kRowsPerThread; ++it) {
+        const int r = q8_row(it, wave, ro);
+        const float sc = scale_s[r];
+        const uint32_t w = quant_code(s[it].x, sc) | (quant_code(s[it].y, sc) << 8) |
+                           (quant_code(s[it].z, sc) << 16) | (quant_code(s[it].w, sc) << 24);
+        __builtin_nontemporal_store(w, Zh + r * (kD / 4) + c4);
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void q8_quantize_kernel(const float* __restrict__ S,
+                                                               int8_t* __restrict__ Z,
+                                                               float* __restrict__ A) {
+    __shared__ float scale_s[kD];
+    const int h = blockIdx.x, tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
+    const int c4 = lane & 31, ro = lane >> 5;
+    const float* Sh = S + static_cast<size_t>(h) * kD * kD;
+    f32x4 s[kRowsPerThread];
+#pragma unroll
+    for (int it = 0; it < kRowsPerThread; ++it)
+        s[it] = stream_load(Sh + q8_row(it, wave, ro) * kD + 4 * c4);
+    requantize_tile(s, reinterpret_cast<uint32_t*>(Z + static_cast<size_t>(h) * kD * kD),
+                    A + static_cast<size_t>(h) * kD, scale_s, wave, lane);
+}
+
+template <bool kPerKey, bool kBoundary, typename T>
+__global__ __launch_bounds__(kThreads) void q8_window_kernel(
+    int W, int pos, int8_t* __restrict__ Z, float* __restrict__ A, T* __restrict__ Kbuf,
+    float* __restrict__ Ubuf, float* __restrict__ Gbuf, const T* __restrict__ q,
+    const T* __restrict__ k, const T* __restrict__ v, const float* __restrict__ gate,
+    const float* __restrict__ beta, float* __restrict__ y) {
+    // boundary only: eT[r][Wp] = Gamma_{j+1:W} k_j at row r, Us[Wp][128] = u_j
+    extern __shared__ float dyn_lds[];
+    __shared__ f32x2 rowv[kD];            // a_r/127 Gamma_{1:l} (k_r, q_r)
+    __shared__ f32x2 coefp[2][kMaxW];     // per record (k_j.Gx, k_j.Gq), per half of the rows
+    __shared__ f32x2 red[4][kD];          // per-wave column partials
+    __shared__ float kq_part[2];
+    __shared__ float zcoef[kBoundary ? kD : 1];
+    __shared__ float scale_s[kBoundary ? kD : 1];
+
+    const int h = blockIdx.x, tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
+    const int c4 = lane & 31, ro = lane >> 5;
+    const size_t vec_off = static_cast<size_t>(h) * kD;
+    const int gdim = kPerKey ? kD : 1;
+    const int Wp = (W + 3) & ~3;
+    float* eT = dyn_lds;
+    float* Us = dyn_lds + kD * Wp;
+
+    uint32_t* Zh = reinterpret_cast<uint32_t*>(Z + static_cast<size_t>(h) * kD * kD);
+    uint32_t zw[kRowsPerThread];
+#pragma unroll
+    for (int it = 0; it < kRowsPerThread; ++it)
+        zw[it] = __builtin_nontemporal_load(Zh + q8_row(it, wave, ro) * (kD / 4) + c4);
+
+    // ---- key-side preparation: thread -> key row r, record parity par
+    const int r = tid & (kD - 1), par = tid >> 7;
+    const float kr = load_in(k, vec_off + r), qr = load_in(q, vec_off + r);
+    const float gr = kPerKey ? gate[vec_off + r] : gate[h];
+    {
+        const T* Kh = Kbuf + static_cast<size_t>(h) * W * kD;
+        const float* Gh = Gbuf + static_cast<size_t>(h) * W * gdim;
+        float G = 1.f;  // product of the gates of the records after j (and before l)
+        for (int j = pos - 1; j >= 0; --j) {
+            const float e = load_in(Kh, static_cast<size_t>(j) * kD + r) * G * gr;
+            if ((j & 1) == par) {
+                const f32x2 c = wave_sum2(f32x2{e * kr, e * qr});
+                if (lane == 0) coefp[wave & 1][j] = c;
+            }
+            if (kBoundary && par == 0) eT[r * Wp + j] = e;
+            G *= kPerKey ? Gh[static_cast<size_t>(j) * kD + r] : Gh[j];
+        }
+        if (par == 0) {
+            const float c0 = A[vec_off + r] / 127.f * G * gr;  // a_r/127 Gamma_{1:l} at row r
+            rowv[r] = f32x2{c0 * kr, c0 * qr};
+            const float kq = wave_sum(kr * qr);
+            if (lane == 0) kq_part[wave] = kq;
+            if (kBoundary) {
+                zcoef[r] = c0;
+                eT[r * Wp + pos] = kr;
+                for (int j = pos + 1; j < Wp; ++j) eT[r * Wp + j] = 0.f;
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- one sweep of the int8 tile for both read vectors, plus the records
+    f32x4 p1 = {0.f, 0.f, 0.f, 0.f}, p2 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int it = 0; it < kRowsPerThread; ++it) {
+        const f32x2 rv = rowv[q8_row(it, wave, ro)];
+        const f32x4 zf = unpack_i8x4(zw[it]);
+        p1 += zf * rv.x;
+        p2 += zf * rv.y;
+    }
+    const float* Uh = Ubuf + static_cast<size_t>(h) * W * kD;
+    for (int j = 2 * wave + ro; j < pos; j += 8) {
+        const f32x2 c = coefp[0][j] + coefp[1][j];
+        const f32x4 u = *reinterpret_cast<const f32x4*>(Uh + static_cast<size_t>(j) * kD + 4 * c4);
+        p1 += u * c.x;
+        p2 += u * c.y;
+    }
+    p1.x += xor_shfl(p1.x, 32); p1.y += xor_shfl(p1.y, 32);
+    p1.z += xor_shfl(p1.z, 32); p1.w += xor_shfl(p1.w, 32);
+    p2.x += xor_shfl(p2.x, 32); p2.y += xor_shfl(p2.y, 32);
+    p2.z += xor_shfl(p2.z, 32); p2.w += xor_shfl(p2.w, 32);
+    if (ro == 0) {
+        red[wave][4 * c4 + 0] = f32x2{p1.x, p2.x};
+        red[wave][4 * c4 + 1] = f32x2{p1.y, p2.y};
+        red[wave][4 * c4 + 2] = f32x2{p1.z, p2.z};
+        red[wave][4 * c4 + 3] = f32x2{p1.w, p2.w};
+    }
+    __syncthreads();
+
+    // ---- correction, output, and the record of this step (thread -> value column)
+    if (tid < kD) {
+        const int c = tid;
+        const f32x2 acc = red[0][c] + red[1][c] + red[2][c] + red[3][c];
+        const float kq = kq_part[0] + kq_part[1];
+        const float u = beta[h] * (load_in(v, vec_off + c) - acc.x);
+        y[vec_off + c] = acc.y + u * kq;
+        if (kBoundary) {
+            Us[pos * kD + c] = u;
+        } else {
+            const size_t rec = (static_cast<size_t>(h) * W + pos) * kD;
+            Ubuf[rec + c] = u;
+            store_in(Kbuf, rec + c, kr);  // thread c < 128 holds k at row r == c
+            if (kPerKey) Gbuf[rec + c] = gr;
+            else if (c == 0) Gbuf[static_cast<size_t>(h) * W + pos] = gr;
+        }
+    }
+    if (!kBoundary) return;
+
+    // ---- window boundary: S_W = Gamma_{1:W} S^_0 + sum_j Gamma_{j+1:W} k_j u_j^T, requantize
+    for (int i = tid; i < pos * kD; i += kThreads) Us[i] = Uh[i];
+    for (int i = (pos + 1) * kD + tid; i < Wp * kD; i += kThreads) Us[i] = 0.f;
+    __syncthreads();
+    f32x4 s[kRowsPerThread];
+#pragma unroll
+    for (int it = 0; it < kRowsPerThread; ++it) s[it] = unpack_i8x4(zw[it]) * zcoef[q8_row(it, wave, ro)];
+    for (int j0 = 0; j0 < Wp; j0 += 4) {
+        const f32x4 u0 = *reinterpret_cast<const f32x4*>(Us + (j0 + 0) * kD + 4 * c4);
+        const f32x4 u1 = *reinterpret_cast<const f32x4*>(Us + (j0 + 1) * kD + 4 * c4);
+        const f32x4 u2 = *reinterpret_cast<const f32x4*>(Us + (j0 + 2) * kD + 4 * c4);
+        const f32x4 u3 = *reinterpret_cast<const f32x4*>(Us + (j0 + 3) * kD + 4 * c4);
+#pragma unroll
+        for (int it = 0; it < kRowsPerThread; ++it) {
+            const f32x4 e = *reinterpret_cast<const f32x4*>(eT + q8_row(it, wave, ro) * Wp + j0);
+            s[it] += u0 * e.x + u1 * e.y + u2 * e.z + u3 * e.w;
+        }
+    }
+    requantize_tile(s, Zh, A + vec_off, scale_s, wave, lane);
+}
+
+hipError_t launch_q8_quantize(int heads, const float* S, int8_t* Z, float* A, hipStream_t stream) {
+    hipLaunchKernelGGL(q8_quantize_kernel, dim3(heads), dim3(kThreads), 0, stream, S, Z, A);
+    return hipGetLastError();
+}
+
+template <bool kPerKey, typename T>
+static hipError_t launch_window_t(const StepArgs& a, const WindowArgs& w, hipStream_t stream) {
+    const bool boundary = w.pos == w.W - 1;
+    const int Wp = (w.W + 3) & ~3;
+    if (boundary) {
+        const size_t lds = sizeof(float) * 2 * kD * Wp;
+        hipLaunchKernelGGL((q8_window_kernel<kPerKey, true, T>), dim3(a.heads), dim3(kThreads), lds,
+                           stream, w.W, w.pos, w.Z, w.A, static_cast<T*>(w.Kbuf), w.Ubuf, w.Gbuf,
+                           static_cast<const T*>(a.q), static_cast<const T*>(a.k),
+                           static_cast<const T*>(a.v), a.gate, a.beta, a.y);
+    } else {
+        hipLaunchKernelGGL((q8_window_kernel<kPerKey, false, T>), dim3(a.heads), dim3(kThreads), 0,
+                           stream, w.W, w.pos, w.Z, w.A, static_cast<T*>(w.Kbuf), w.Ubuf, w.Gbuf,
+                           static_cast<const T*>(a.q), static_cast<const T*>(a.k),
+                           static_cast<const T*>(a.v), a.gate, a.beta, a.y);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_q8_window(const StepArgs& a, const WindowArgs& w, bool per_key, bool bf16,
+                            hipStream_t stream) {
+    if (per_key) return bf16 ? launch_window_t<true, bf16_t>(a, w, stream) : launch_window_t<true, float>(a, w, stream);
+    return bf16 ? launch_window_t<false, bf16_t>(a, w, stream) : launch_window_t<false, float>(a, w, stream);
+}
+
+}  // namespace rsu

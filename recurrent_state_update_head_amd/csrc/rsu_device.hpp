@@ -1,0 +1,90 @@
+// rsu_device.hpp -- device-side helpers shared by the gfx950 decode-step kernels.
+//
+// Thread layout used by every fp32-state kernel (one 256-thread workgroup per
+// head, four wave64s):
+//   wave w owns value columns [32w, 32w+32); lane l owns the 4 columns
+//   32w + 4(l & 7) .. +3 and the key rows 8*it + (l >> 3), it = 0..15.
+//   One wave-wide 128-bit load therefore covers 8 rows x 128 contiguous bytes,
+//   and every column sum over the 128 key rows stays inside one wave: a thread
+//   sums its 16 rows, then lanes l, l^8, l^16, l^32 combine (3 butterfly steps).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kernels.hpp"
+
+namespace rsu {
+
+constexpr int kD = 128;            // d_k = d_v
+constexpr int kThreads = 256;      // 4 x wave64 per head
+constexpr int kRowsPerThread = 16; // fp32-state layout: 16 rows x 4 columns per thread
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+using bf16_t = uint16_t;  // raw bfloat16 bits
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t b) {
+    return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// Element loads of q / k / v in their storage type.
+__device__ __forceinline__ float load_in(const float* p, size_t i) { return p[i]; }
+__device__ __forceinline__ float load_in(const bf16_t* p, size_t i) { return bf16_to_f32(p[i]); }
+
+// Four consecutive elements starting at a 4-element-aligned index.
+__device__ __forceinline__ f32x4 load4_in(const float* p, size_t i) {
+    return *reinterpret_cast<const f32x4*>(p + i);
+}
+__device__ __forceinline__ f32x4 load4_in(const bf16_t* p, size_t i) {
+    const uint2 w = *reinterpret_cast<const uint2*>(p + i);
+    return f32x4{__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u),
+                 __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xffff0000u)};
+}
+
+// Store of one element in the stored-key type (bf16 keys are copied bit-exactly).
+__device__ __forceinline__ void store_in(float* p, size_t i, float x) { p[i] = x; }
+__device__ __forceinline__ void store_in(bf16_t* p, size_t i, float x) {
+    p[i] = static_cast<bf16_t>(__float_as_uint(x) >> 16);
+}
+
+// State streaming: the state is touched once per step, so bypass cache retention.
+__device__ __forceinline__ f32x4 stream_load(const float* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+}
+__device__ __forceinline__ void stream_store(float* p, f32x4 x) {
+    __builtin_nontemporal_store(x, reinterpret_cast<f32x4*>(p));
+}
+
+__device__ __forceinline__ float xor_shfl(float x, int mask) { return __shfl_xor(x, mask, 64); }
+
+// Sum over the lanes that differ only in lane bits 3..5 (the 8 row lanes of a
+// column group in the fp32-state layout).
+__device__ __forceinline__ f32x4 sum_row_lanes(f32x4 x) {
+#pragma unroll
+    for (int m = 8; m <= 32; m <<= 1) {
+        x.x += xor_shfl(x.x, m);
+        x.y += xor_shfl(x.y, m);
+        x.z += xor_shfl(x.z, m);
+        x.w += xor_shfl(x.w, m);
+    }
+    return x;
+}
+
+// Sum over all 64 lanes of a wave (result in every lane).
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+    for (int m = 1; m <= 32; m <<= 1) x += xor_shfl(x, m);
+    return x;
+}
+__device__ __forceinline__ f32x2 wave_sum2(f32x2 x) {
+#pragma unroll
+    for (int m = 1; m <= 32; m <<= 1) {
+        x.x += xor_shfl(x.x, m);
+        x.y += xor_shfl(x.y, m);
+    }
+    return x;
+}
+
+}  // namespace rsu

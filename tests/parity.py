@@ -1,0 +1,216 @@
+"""Helpers of the GPU parity tests: upload seeded inputs, run the HIP path through
+the C ABI, run the fp64 oracle on the same inputs (all heads, or sampled heads
+at full size), and measure the error as the pages' tolerances define it.
+
+Error metric: for every (head, step), the norm-wise relative error
+||x_gpu - x_ref||_2 / ||x_ref||_2 over the head's output vector (or state
+matrix); the maximum over heads and steps is compared with the tolerance.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+import workloads as wl
+
+DEV = "cuda"
+TOL_F32 = 1e-5      # fp32 state and outputs
+TOL_Q8 = 1e-4       # outputs of the int8 path against the oracle's same schedule
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def rsu():
+    import recurrent_state_update_head_amd as m
+    return m
+
+
+def qkv_dtype(w: wl.Workload):
+    return torch.bfloat16 if w.qkv == "bf16" else torch.float32
+
+
+def dev_inputs(w: wl.Workload, t: int):
+    """Host inputs of step t (fp32 numpy) and their device tensors in the workload dtype."""
+    x = wl.step_inputs(w, t)
+    B, H, dt = w.B, w.H, qkv_dtype(w)
+    d = {n: torch.from_numpy(x[n]).to(DEV).to(dt).view(B, H, 128) for n in ("q", "k", "v")}
+    d["gate"] = torch.from_numpy(x["gate"]).to(DEV).view((B, H, 128) if w.per_key_gate else (B, H))
+    d["beta"] = torch.from_numpy(x["beta"]).to(DEV).view(B, H)
+    return x, d
+
+
+def host_slice(x: dict, heads: np.ndarray):
+    return tuple(x[n][heads] for n in ("q", "k", "v", "gate", "beta"))
+
+
+def rel_err(gpu: np.ndarray, ref: np.ndarray) -> float:
+    """max over leading index of ||gpu - ref|| / ||ref|| over the trailing axes."""
+    g = gpu.reshape(gpu.shape[0], -1).astype(np.float64)
+    r = ref.reshape(ref.shape[0], -1).astype(np.float64)
+    num = np.linalg.norm(g - r, axis=1)
+    den = np.linalg.norm(r, axis=1)
+    return float(np.max(num / np.maximum(den, 1e-300)))
+
+
+def take(t: torch.Tensor, heads_dev: torch.Tensor, inner) -> np.ndarray:
+    return t.reshape((-1,) + tuple(inner))[heads_dev].cpu().numpy()
+
+
+def run_dense(w: wl.Workload, sample: int | None = None):
+    """Dense GDN/KDA steps on the GPU against the eager oracle; returns (max y err, final S err)."""
+    m = rsu()
+    B, H = w.B, w.H
+    S0 = wl.initial_state(w)
+    heads = np.arange(w.heads) if sample is None else wl.sample_heads(w, sample)
+    hd = torch.from_numpy(heads).to(DEV)
+    S = torch.from_numpy(S0).to(DEV).view(B, H, 128, 128)
+    S_ref = S0[heads].astype(np.float64)
+    del S0
+    y = torch.empty(B, H, 128, device=DEV)
+    fn = m.kda_decode_step if w.per_key_gate else m.gdn_decode_step
+    worst_y = 0.0
+    for t in range(w.steps):
+        x, d = dev_inputs(w, t)
+        fn(S, d["q"], d["k"], d["v"], d["gate"], d["beta"], y)
+        y_ref = oracle.dense_step(S_ref, *host_slice(x, heads))
+        worst_y = max(worst_y, rel_err(take(y, hd, (128,)), y_ref))
+    worst_S = rel_err(take(S, hd, (128, 128)), S_ref)
+    return worst_y, worst_S
+
+
+def new_log_buffers(w: wl.Workload, C: int):
+    B, H = w.B, w.H
+    per_key = w.per_key_gate
+    cap = max(C, 1)
+    return {
+        "lbar": torch.zeros((B, H, 128) if per_key else (B, H), device=DEV),
+        "Klog": torch.zeros(B, H, cap, 128, device=DEV, dtype=qkv_dtype(w)),
+        "Ulog": torch.zeros(B, H, cap, 128, device=DEV),
+        "Lam": torch.zeros((B, H, cap, 128) if per_key else (B, H, cap), device=DEV),
+    }
+
+
+def log_step(w: wl.Workload, C: int, L: int, Sbase, buf, d, y):
+    """One base+log step through the C ABI; returns the next L."""
+    m = rsu()
+    kda = w.per_key_gate
+    Klog, Ulog, Lam = (buf["Klog"], buf["Ulog"], buf["Lam"]) if C > 0 else (None, None, None)
+    if L < C:
+        (m.kda_log_append if kda else m.gdn_log_append)(
+            C, L, Sbase, buf["lbar"], Klog, Ulog, Lam, d["q"], d["k"], d["v"], d["gate"], d["beta"], y)
+        return L + 1
+    (m.kda_log_merge if kda else m.gdn_log_merge)(
+        C, L, Sbase, buf["lbar"], Klog, Ulog, Lam, d["q"], d["k"], d["v"], d["gate"], d["beta"], y)
+    return 0
+
+
+def run_log(w: wl.Workload, sample: int | None = None, steps: int | None = None):
+    """Base+log steps on the GPU against the oracle's base+log steps (which equal eager
+    decoding, a pinned property). Returns a dict of max errors."""
+    B, H = w.B, w.H
+    C = w.M - 1
+    steps = w.steps if steps is None else steps
+    S0 = wl.initial_state(w)
+    heads = np.arange(w.heads) if sample is None else wl.sample_heads(w, sample)
+    hd = torch.from_numpy(heads).to(DEV)
+    Sbase = torch.from_numpy(S0).to(DEV).view(B, H, 128, 128)
+    ref = oracle.LogState(S0[heads].astype(np.float64), C, w.per_key_gate)
+    del S0
+    buf = new_log_buffers(w, C)
+    y = torch.empty(B, H, 128, device=DEV)
+    err = {"y": 0.0, "Sbase": 0.0, "lbar": 0.0, "Ulog": 0.0, "Klog": 0.0, "Lam": 0.0}
+    L = 0
+    for t in range(steps):
+        x, d = dev_inputs(w, t)
+        L = log_step(w, C, L, Sbase, buf, d, y)
+        y_ref = ref.step(*host_slice(x, heads))
+        assert L == ref.L
+        err["y"] = max(err["y"], rel_err(take(y, hd, (128,)), y_ref))
+        if L == 0:
+            err["Sbase"] = max(err["Sbase"], rel_err(take(Sbase, hd, (128, 128)), ref.Sbar))
+        else:
+            m = L - 1
+            gd = (128,) if w.per_key_gate else ()
+            Ug = take(buf["Ulog"][:, :, m], hd, (128,))
+            err["Ulog"] = max(err["Ulog"], rel_err(Ug, ref.U[:, m]))
+            Kg = take(buf["Klog"][:, :, m].float(), hd, (128,))
+            err["Klog"] = max(err["Klog"], float(np.abs(Kg - ref.K[:, m]).max()))
+            lam_g = take(buf["Lam"][:, :, m], hd, gd)
+            err["Lam"] = max(err["Lam"], float(np.abs(lam_g - ref.Lam[:, m]).max()))
+        lb_g = take(buf["lbar"], hd, (128,) if w.per_key_gate else ())
+        err["lbar"] = max(err["lbar"], float(np.abs(lb_g - ref.lbar).max()))
+    return err
+
+
+def new_window_buffers(w: wl.Workload):
+    B, H, W = w.B, w.H, w.W
+    return {
+        "Z": torch.zeros(B, H, 128, 128, device=DEV, dtype=torch.int8),
+        "A": torch.zeros(B, H, 128, device=DEV),
+        "Kbuf": torch.zeros(B, H, W, 128, device=DEV, dtype=qkv_dtype(w)),
+        "Ubuf": torch.zeros(B, H, W, 128, device=DEV),
+        "Gbuf": torch.zeros((B, H, W, 128) if w.per_key_gate else (B, H, W), device=DEV),
+    }
+
+
+def window_step(w: wl.Workload, pos: int, buf, d, y):
+    m = rsu()
+    fn = m.kda_q8_window if w.per_key_gate else m.gdn_q8_window
+    fn(w.W, pos, buf["Z"], buf["A"], buf["Kbuf"], buf["Ubuf"], buf["Gbuf"], d["q"], d["k"], d["v"],
+       d["gate"], d["beta"], y)
+
+
+def run_window(w: wl.Workload, sample: int | None = None, steps: int | None = None,
+               tie_band: float = 1e-3):
+    """Int8 per-window path on the GPU against the oracle, teacher-forced per window:
+    at every window start the oracle restarts from the GPU's (Z, a), so a 1-LSB
+    rounding-tie flip at one boundary is not carried into later windows.
+    Returns a dict: max y error, max row-scale relative error, and code statistics
+    at the boundaries (max |dZ|, flips, flips outside the tie band)."""
+    m = rsu()
+    B, H, W = w.B, w.H, w.W
+    steps = w.steps if steps is None else steps
+    S0 = wl.initial_state(w)
+    heads = np.arange(w.heads) if sample is None else wl.sample_heads(w, sample)
+    hd = torch.from_numpy(heads).to(DEV)
+    buf = new_window_buffers(w)
+    S0_dev = torch.from_numpy(S0).to(DEV).view(B, H, 128, 128)
+    m.q8_quantize(S0_dev, buf["Z"], buf["A"])
+    Zr, ar = oracle.q8_quantize(S0[heads].astype(np.float64))
+    del S0, S0_dev
+    st = {"init_codes_equal": bool(np.array_equal(take(buf["Z"], hd, (128, 128)), Zr)),
+          "init_scales_equal": bool(np.array_equal(take(buf["A"], hd, (128,)), ar)),
+          "y": 0.0, "a": 0.0, "z_maxdiff": 0, "z_flips": 0, "z_flips_outside_band": 0,
+          "boundaries": 0}
+    y = torch.empty(B, H, 128, device=DEV)
+    ref = None
+    for t in range(steps):
+        pos = t % W
+        if pos == 0:
+            ref = oracle.WindowState(take(buf["Z"], hd, (128, 128)), take(buf["A"], hd, (128,)),
+                                     W, w.per_key_gate)
+        x, d = dev_inputs(w, t)
+        window_step(w, pos, buf, d, y)
+        if pos == W - 1:
+            y_ref, _, wcode = ref.step(*host_slice(x, heads), want_boundary=True)
+            Zg = take(buf["Z"], hd, (128, 128)).astype(np.int32)
+            ag = take(buf["A"], hd, (128,)).astype(np.float64)
+            aref = ref.a.astype(np.float64)
+            st["a"] = max(st["a"], float(np.max(np.abs(ag - aref) / np.maximum(aref, 1e-30))))
+            diff = Zg - ref.Z.astype(np.int32)
+            flips = diff != 0
+            near_tie = np.abs(np.abs(wcode - np.floor(wcode)) - 0.5) < tie_band
+            st["z_maxdiff"] = max(st["z_maxdiff"], int(np.abs(diff).max()))
+            st["z_flips"] += int(flips.sum())
+            st["z_flips_outside_band"] += int((flips & ~near_tie).sum())
+            st["boundaries"] += 1
+        else:
+            y_ref = ref.step(*host_slice(x, heads))
+        st["y"] = max(st["y"], rel_err(take(y, hd, (128,)), y_ref))
+    return st

@@ -1,0 +1,113 @@
+"""The C ABI without a GPU: librsu.so loads, exports every function include/rsu.h
+declares, and rejects invalid arguments before any launch (those paths make no
+HIP call, so they run on a host without a device)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rsu.h")
+LIB = os.path.join(ROOT, "recurrent_state_update_head_amd", "librsu.so")
+
+RSU_OK, E_NULL, E_DIMS, E_DTYPE, E_ALIGN, E_RANGE = 0, -1, -2, -3, -4, -5
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        from recurrent_state_update_head_amd import _build
+        _build.build()
+    return ctypes.CDLL(LIB)
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("dk", ctypes.c_int32),
+                ("dv", ctypes.c_int32), ("qkv_dtype", ctypes.c_int32)]
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("gdn_decode_step", "kda_decode_step", "q8_quantize", "gdn_q8_window",
+              "kda_q8_window", "gdn_log_append", "kda_log_append", "gdn_log_merge",
+              "kda_log_merge", "rsu_last_error", "rsu_abi_version", "rsu_copy_f32"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+    lib.rsu_abi_version.restype = ctypes.c_int
+    assert lib.rsu_abi_version() == 1
+
+
+P = ctypes.c_void_p
+GOOD = P(0x1000)        # aligned, never dereferenced (every call below fails validation)
+ODD = P(0x1004)
+
+
+def _dense(lib, dims, S=GOOD, q=GOOD, k=GOOD, v=GOOD, g=GOOD, b=GOOD, y=GOOD):
+    f = lib.gdn_decode_step
+    f.restype = ctypes.c_int
+    return f(ctypes.byref(dims) if dims is not None else None, S, q, k, v, g, b, y, None)
+
+
+def _last(lib):
+    lib.rsu_last_error.restype = ctypes.c_char_p
+    return lib.rsu_last_error().decode()
+
+
+def test_dense_validation(lib):
+    assert _dense(lib, None) == E_NULL
+    assert _dense(lib, Dims(2, 3, 64, 128, 0)) == E_DIMS
+    assert "128" in _last(lib)
+    assert _dense(lib, Dims(-1, 3, 128, 128, 0)) == E_DIMS
+    assert _dense(lib, Dims(2, 3, 128, 128, 7)) == E_DTYPE
+    assert _dense(lib, Dims(2, 3, 128, 128, 0), S=None) == E_NULL
+    assert "S is NULL" in _last(lib)
+    assert _dense(lib, Dims(2, 3, 128, 128, 1), y=ODD) == E_ALIGN
+    assert _dense(lib, Dims(70000, 70000, 128, 128, 0)) == E_DIMS
+
+
+def test_empty_batch_is_a_no_op(lib):
+    assert _dense(lib, Dims(0, 48, 128, 128, 1), S=None, q=None, k=None, v=None) == RSU_OK
+    assert _last(lib) == ""
+
+
+def test_window_and_log_ranges(lib):
+    w = lib.gdn_q8_window
+    w.restype = ctypes.c_int
+    d = Dims(2, 3, 128, 128, 1)
+    args = [GOOD] * 11
+    assert w(ctypes.byref(d), 16, 16, *args, None) == E_RANGE
+    assert w(ctypes.byref(d), 0, 0, *args, None) == E_RANGE
+    assert w(ctypes.byref(d), 33, 0, *args, None) == E_RANGE
+    assert w(ctypes.byref(d), 16, -1, *args, None) == E_RANGE
+    a = lib.gdn_log_append
+    a.restype = ctypes.c_int
+    m = lib.gdn_log_merge
+    m.restype = ctypes.c_int
+    largs = [GOOD] * 12
+    assert a(ctypes.byref(d), 7, 7, *largs, None) == E_RANGE   # append needs L < C
+    assert m(ctypes.byref(d), 7, 6, *largs, None) == E_RANGE   # merge needs L == C
+    assert a(ctypes.byref(d), 17, 0, *largs, None) == E_RANGE  # C above the limit
+    assert a(ctypes.byref(d), 0, 0, *largs, None) == E_RANGE   # no append with C == 0
+    # C == 0 merge may pass NULL log buffers; the NULL base is still caught
+    assert m(ctypes.byref(d), 0, 0, None, GOOD, None, None, None, *([GOOD] * 6), None) == E_NULL
+    assert "Sbase" in _last(lib)
+
+
+def test_copy_validation(lib):
+    c = lib.rsu_copy_f32
+    c.restype = ctypes.c_int
+    c.argtypes = [P, P, ctypes.c_int64, P]
+    assert c(GOOD, GOOD, 6, None) == E_DIMS
+    assert c(GOOD, ODD, 8, None) == E_ALIGN
+    assert c(None, None, 0, None) == RSU_OK

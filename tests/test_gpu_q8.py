@@ -1,0 +1,67 @@
+"""GPU parity of the int8 per-window path against the fp64 oracle's same schedule.
+
+Bars: the initial quantization of an fp32 state is bit-exact (both sides take the
+code decision in fp32 from identical inputs); inside a window the outputs are
+within 1e-4 norm-wise relative error of the oracle teacher-forced from the GPU's
+window-start state; at each boundary the requantized codes differ by at most
+1 LSB, and only where the exact code lies within 1e-3 LSB of a rounding tie;
+row scales within 1e-5 relative."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as wl
+from parity import DEV, TOL_Q8, rsu, run_window, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _check(st, name):
+    say(f"[q8] {name}: {st}")
+    assert st["init_codes_equal"] and st["init_scales_equal"]
+    assert st["y"] < TOL_Q8
+    assert st["a"] < 1e-5
+    assert st["z_maxdiff"] <= 1
+    assert st["z_flips_outside_band"] == 0
+
+
+def test_quantize_bit_exact_with_ties_and_zero_rows():
+    m = rsu()
+    B, H = 3, 5
+    g = torch.Generator().manual_seed(9)
+    S = torch.randn(B, H, 128, 128, generator=g) * 0.02
+    S[0, 0, 3] = 0.0                                  # a zero row
+    S[1, 2, 7, :] = torch.arange(128) - 63.5          # halves on a 127/63.5 grid
+    S[1, 2, 7, 0] = 127.0                             # absmax 127: scale 1, codes = rint(values)
+    S[1, 2, 7, 1:] = (torch.arange(127) - 63) + 0.5   # exact ties
+    Sd = S.to(DEV)
+    Z = torch.empty(B, H, 128, 128, dtype=torch.int8, device=DEV)
+    A = torch.empty(B, H, 128, device=DEV)
+    m.q8_quantize(Sd, Z, A)
+    Zr, ar = oracle.q8_quantize(S.double().numpy().reshape(-1, 128, 128))
+    np.testing.assert_array_equal(Z.cpu().numpy().reshape(-1, 128, 128), Zr)
+    np.testing.assert_array_equal(A.cpu().numpy().reshape(-1, 128), ar)
+    assert not Z[0, 0, 3].any() and A[0, 0, 3] == 0
+
+
+@pytest.mark.parametrize("variant,W,B,H", [("gdn", 16, 3, 7), ("gdn", 5, 2, 3), ("gdn", 1, 2, 2),
+                                           ("kda", 16, 2, 5), ("kda", 3, 1, 3)])
+def test_window_small_all_heads(variant, W, B, H):
+    base = wl.WORKLOADS[4]
+    w = wl.custom(base, B=B, H=H, W=W, steps=3 * W + 2,
+                  variant=variant, gate_lo=0.8 if variant == "kda" else 0.9,
+                  gate_hi=1.0 if variant == "kda" else 0.999)
+    _check(run_window(w), f"{variant} W={W} B={B} H={H}")
+
+
+def test_window_f32_inputs():
+    w = wl.custom(wl.WORKLOADS[4], B=2, H=4, qkv="f32", steps=40)
+    _check(run_window(w), "gdn W=16 f32 inputs")
+
+
+def test_window_b256_h48_full_size_sampled():
+    """The int8 workload at full size (B=256, H=48, W=16, 256 steps), 64 sampled heads."""
+    w = wl.WORKLOADS[4]
+    say(f"[q8] {w.name}: full size, 64 sampled heads, {w.steps} steps")
+    _check(run_window(w, sample=64), w.name)

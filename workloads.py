@@ -12,12 +12,16 @@ Workload shapes follow the decode-kernel experiments of the three pages:
 (DeltaLog, Table 3).
 
 Every tensor of every step has its own substream:
-``numpy.random.SeedSequence([1000 + config_id, tensor_tag, step])`` feeding a
-PCG64 generator, so any step can be regenerated on its own.
+``numpy.random.SeedSequence([1000 + config_id, tensor_tag, step])`` feeding an
+SFC64 generator (float32 normals and uniforms), so any step can be regenerated
+on its own. The initial state is drawn in chunks of 256 heads, each with its
+own substream ``[1000 + config_id, 0, chunk]``, on a few threads.
 """
 from __future__ import annotations
 
+import concurrent.futures
 import dataclasses
+import os
 
 import numpy as np
 
@@ -74,7 +78,11 @@ def custom(base: Workload, **changes) -> Workload:
 
 
 def _rng(wl: Workload, tag: int, step: int = 0) -> np.random.Generator:
-    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([wl.seed, tag, step])))
+    return np.random.Generator(np.random.SFC64(np.random.SeedSequence([wl.seed, tag, step])))
+
+
+_CHUNK = 256
+_THREADS = max(1, min(16, os.cpu_count() or 1))
 
 
 def round_to_bf16(x: np.ndarray) -> np.ndarray:
@@ -83,10 +91,12 @@ def round_to_bf16(x: np.ndarray) -> np.ndarray:
     Every returned value is exactly representable in bfloat16, so casting it to
     bfloat16 on the device is exact and widening it to fp64 for the oracle is exact.
     """
-    x = np.ascontiguousarray(x, dtype=np.float32)
-    bits = x.view(np.uint32).astype(np.uint64)
-    bits = (bits + 0x7FFF + ((bits >> 16) & 1)) & 0xFFFF0000
-    return bits.astype(np.uint32).view(np.float32)
+    bits = np.array(x, dtype=np.float32).view(np.uint32)
+    lsb = (bits >> 16) & np.uint32(1)
+    bits += np.uint32(0x7FFF)
+    bits += lsb
+    bits &= np.uint32(0xFFFF0000)
+    return bits.view(np.float32)
 
 
 def _cast(wl: Workload, x64: np.ndarray) -> np.ndarray:
@@ -108,16 +118,28 @@ def initial_state(wl: Workload) -> np.ndarray:
     (row/column max-to-median ratios).
     """
     n = wl.heads
-    S = (_rng(wl, _TAG_S0).standard_normal((n, DK, DV)) * wl.state_std).astype(np.float32)
-    if wl.outliers:
-        r = _rng(wl, _TAG_OUTLIER)
-        for h in range(n):
-            rows = r.choice(DK, size=2, replace=False)
-            cols = r.choice(DV, size=2, replace=False)
-            mask = np.zeros((DK, DV), dtype=bool)
-            mask[rows, :] = True
-            mask[:, cols] = True
-            S[h][mask] *= np.float32(50.0)
+    S = np.empty((n, DK, DV), dtype=np.float32)
+    std = np.float32(wl.state_std)
+
+    def fill(c):
+        lo, hi = c * _CHUNK, min(n, (c + 1) * _CHUNK)
+        r = _rng(wl, _TAG_S0, c)
+        r.standard_normal((hi - lo, DK, DV), dtype=np.float32, out=S[lo:hi])
+        S[lo:hi] *= std
+        if wl.outliers:
+            ro = _rng(wl, _TAG_OUTLIER, c)
+            rows = np.argsort(ro.random((hi - lo, DK)), axis=1)[:, :2]
+            cols = np.argsort(ro.random((hi - lo, DV)), axis=1)[:, :2]
+            rm = np.zeros((hi - lo, DK), dtype=bool)
+            cm = np.zeros((hi - lo, DV), dtype=bool)
+            np.put_along_axis(rm, rows, True, axis=1)
+            np.put_along_axis(cm, cols, True, axis=1)
+            blk = S[lo:hi]
+            blk[rm[:, :, None] | cm[:, None, :]] *= np.float32(50.0)
+
+    nchunks = (n + _CHUNK - 1) // _CHUNK
+    with concurrent.futures.ThreadPoolExecutor(_THREADS) as ex:
+        list(ex.map(fill, range(nchunks)))
     return S
 
 
@@ -131,12 +153,15 @@ def step_inputs(wl: Workload, t: int) -> dict:
     All arrays are fp32.
     """
     n = wl.heads
-    q = _cast(wl, _unit_rows(_rng(wl, _TAG_Q, t).standard_normal((n, DK))))
-    k = _cast(wl, _unit_rows(_rng(wl, _TAG_K, t).standard_normal((n, DK))))
-    v = _cast(wl, _rng(wl, _TAG_V, t).standard_normal((n, DV)))
+    f32 = np.float32
+    q = _cast(wl, _unit_rows(_rng(wl, _TAG_Q, t).standard_normal((n, DK), dtype=f32).astype(np.float64)))
+    k = _cast(wl, _unit_rows(_rng(wl, _TAG_K, t).standard_normal((n, DK), dtype=f32).astype(np.float64)))
+    v = _cast(wl, _rng(wl, _TAG_V, t).standard_normal((n, DV), dtype=f32))
     gshape = (n, DK) if wl.per_key_gate else (n,)
-    gate = _rng(wl, _TAG_GATE, t).uniform(wl.gate_lo, wl.gate_hi, gshape).astype(np.float32)
-    beta = _rng(wl, _TAG_BETA, t).uniform(0.0, 1.0, (n,)).astype(np.float32)
+    lo, hi = wl.gate_lo, wl.gate_hi
+    gate = (lo + (hi - lo) * _rng(wl, _TAG_GATE, t).random(gshape)).astype(f32)
+    gate = np.clip(gate, f32(lo), f32(hi))
+    beta = _rng(wl, _TAG_BETA, t).random((n,), dtype=f32)
     return {"q": q, "k": k, "v": v, "gate": gate, "beta": beta}
 
 
