@@ -33,7 +33,7 @@ __global__ __launch_bounds__(kThreads) void log_step_kernel(
     __shared__ float kq_part[2];
     __shared__ float kd[kMerge ? kD * kCp : 1];  // merge: exp(lbar' - Lam_m) K_m at row r
 
-    const int h = blockIdx.x, tid = threadIdx.x;
+    const int h = head_of_block(blockIdx.x, gridDim.x), tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
     const int ro = lane >> 3;
     const int col = wave * 32 + (lane & 7) * 4;

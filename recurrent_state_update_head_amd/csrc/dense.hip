@@ -8,6 +8,8 @@
 // as p through the identity S_new^T q = S^T (g * q) + u (k . q), so the state
 // is loaded once, reduced once (two column sums at the same time), updated in
 // registers and stored once: 64 KiB in and 64 KiB out per head per step.
+// Non-temporal 128-bit loads and stores and the XCD-grouped head order
+// (head_of_block) were chosen by measurement on MI355X.
 #include "kernels.hpp"
 #include "rsu_device.hpp"
 
@@ -18,27 +20,24 @@ __global__ __launch_bounds__(kThreads) void dense_step_kernel(
     float* __restrict__ S, const T* __restrict__ q, const T* __restrict__ k,
     const T* __restrict__ v, const float* __restrict__ gate, const float* __restrict__ beta,
     float* __restrict__ y) {
-    // per key row: (g*k, g*q, k, g)
-    __shared__ f32x4 row_vec[kD];
-    __shared__ float kq_part[2];
+    // per wave, per key row: (g*k, g*q, k, g); each wave stages its own copy, so the
+    // four waves of a head run without a workgroup barrier
+    __shared__ f32x4 row_vec[kThreads / 64][kD];
 
-    const int h = blockIdx.x;
+    const int h = head_of_block(blockIdx.x, gridDim.x);
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
     const int ro = lane >> 3;
     const int col = wave * 32 + (lane & 7) * 4;
     const size_t vec_off = static_cast<size_t>(h) * kD;
 
-    // key-side inputs (small) first, then the whole state tile
-    float kr = 0.f, qr = 0.f, gr = 0.f;
-    if (tid < kD) {
-        kr = load_in(k, vec_off + tid);
-        qr = load_in(q, vec_off + tid);
-        gr = kPerKey ? gate[vec_off + tid] : gate[h];
-    }
+    // key-side inputs (lane -> key rows 2*lane, 2*lane + 1), then the whole state tile
+    const f32x2 k2 = load2_in(k, vec_off + 2 * lane);
+    const f32x2 q2 = load2_in(q, vec_off + 2 * lane);
+    const float alpha = kPerKey ? 1.f : gate[h];
+    const f32x2 g2 = kPerKey ? *reinterpret_cast<const f32x2*>(gate + vec_off + 2 * lane) : f32x2{alpha, alpha};
     const f32x4 vv = load4_in(v, vec_off + col);
     const float b = beta[h];
-    const float alpha = kPerKey ? 1.f : gate[h];
 
     float* Sh = S + static_cast<size_t>(h) * kD * kD;
     f32x4 s[kRowsPerThread];
@@ -46,19 +45,16 @@ __global__ __launch_bounds__(kThreads) void dense_step_kernel(
     for (int it = 0; it < kRowsPerThread; ++it)
         s[it] = stream_load(Sh + (it * 8 + ro) * kD + col);
 
-    if (tid < kD) {
-        row_vec[tid] = f32x4{gr * kr, gr * qr, kr, gr};
-        const float kq = wave_sum(kr * qr);
-        if (lane == 0) kq_part[wave] = kq;
-    }
-    __syncthreads();
-    const float kq = kq_part[0] + kq_part[1];
+    row_vec[wave][2 * lane] = f32x4{g2.x * k2.x, g2.x * q2.x, k2.x, g2.x};
+    row_vec[wave][2 * lane + 1] = f32x4{g2.y * k2.y, g2.y * q2.y, k2.y, g2.y};
+    const float kq = wave_sum(k2.x * q2.x + k2.y * q2.y);
+    wave_lds_sync();
 
     // column sums over this thread's 16 rows, then over the 8 row lanes
     f32x4 p = {0.f, 0.f, 0.f, 0.f}, r = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int it = 0; it < kRowsPerThread; ++it) {
-        const f32x4 rv = row_vec[it * 8 + ro];
+        const f32x4 rv = row_vec[wave][it * 8 + ro];
         p += s[it] * rv.x;
         r += s[it] * rv.y;
     }
@@ -70,7 +66,7 @@ __global__ __launch_bounds__(kThreads) void dense_step_kernel(
 
 #pragma unroll
     for (int it = 0; it < kRowsPerThread; ++it) {
-        const f32x4 rv = row_vec[it * 8 + ro];
+        const f32x4 rv = row_vec[wave][it * 8 + ro];
         const float g = kPerKey ? rv.w : alpha;
         stream_store(Sh + (it * 8 + ro) * kD + col, s[it] * g + rv.z * u);
     }
@@ -79,7 +75,7 @@ __global__ __launch_bounds__(kThreads) void dense_step_kernel(
 // Read+write copy with the same access pattern, for the practical HBM ceiling.
 __global__ __launch_bounds__(kThreads) void copy_kernel(const float* __restrict__ src,
                                                         float* __restrict__ dst, int64_t n) {
-    const int64_t base = static_cast<int64_t>(blockIdx.x) * kD * kD;
+    const int64_t base = static_cast<int64_t>(head_of_block(blockIdx.x, gridDim.x)) * kD * kD;
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
     const int off = (lane >> 3) * kD + wave * 32 + (lane & 7) * 4;

@@ -75,7 +75,7 @@ __global__ __launch_bounds__(kThreads) void q8_quantize_kernel(const float* __re
                                                                int8_t* __restrict__ Z,
                                                                float* __restrict__ A) {
     __shared__ float scale_s[kD];
-    const int h = blockIdx.x, tid = threadIdx.x;
+    const int h = head_of_block(blockIdx.x, gridDim.x), tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
     const int c4 = lane & 31, ro = lane >> 5;
     const float* Sh = S + static_cast<size_t>(h) * kD * kD;
@@ -102,7 +102,7 @@ __global__ __launch_bounds__(kThreads) void q8_window_kernel(
     __shared__ float zcoef[kBoundary ? kD : 1];
     __shared__ float scale_s[kBoundary ? kD : 1];
 
-    const int h = blockIdx.x, tid = threadIdx.x;
+    const int h = head_of_block(blockIdx.x, gridDim.x), tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
     const int c4 = lane & 31, ro = lane >> 5;
     const size_t vec_off = static_cast<size_t>(h) * kD;

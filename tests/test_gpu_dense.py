@@ -21,7 +21,7 @@ def test_gdn_b4_h8_f32_all_heads_64_steps():
     assert ey < TOL_F32 and eS < TOL_F32
 
 
-@pytest.mark.parametrize("variant,qkv,B,H", [("gdn", "bf16", 3, 7), ("kda", "f32", 5, 3),
+@pytest.mark.parametrize("variant,qkv,B,H", [("gdn", "bf16", 3, 7), ("kda", "f32", 5, 3), ("gdn", "bf16", 10, 10),
                                              ("kda", "bf16", 1, 1), ("gdn", "f32", 2, 1)])
 def test_ragged_small_batches(variant, qkv, B, H):
     base = wl.WORKLOADS[3] if variant == "kda" else wl.WORKLOADS[2]

@@ -24,7 +24,8 @@ def _check(err, name):
 
 @pytest.mark.parametrize("variant,M,B,H,qkv", [("gdn", 8, 3, 7, "bf16"), ("gdn", 1, 2, 3, "bf16"),
                                                ("gdn", 2, 2, 2, "f32"), ("kda", 4, 2, 5, "bf16"),
-                                               ("kda", 8, 1, 3, "f32"), ("gdn", 17, 1, 2, "bf16")])
+                                               ("kda", 8, 1, 3, "f32"), ("gdn", 17, 1, 2, "bf16"),
+                                               ("gdn", 8, 10, 10, "bf16")])
 def test_log_small_all_heads(variant, M, B, H, qkv):
     w = wl.custom(wl.WORKLOADS[5], B=B, H=H, M=M, qkv=qkv, steps=2 * M + 3, variant=variant,
                   gate_lo=0.8 if variant == "kda" else 0.9, gate_hi=1.0 if variant == "kda" else 0.999)

@@ -46,7 +46,8 @@ def test_quantize_bit_exact_with_ties_and_zero_rows():
 
 
 @pytest.mark.parametrize("variant,W,B,H", [("gdn", 16, 3, 7), ("gdn", 5, 2, 3), ("gdn", 1, 2, 2),
-                                           ("kda", 16, 2, 5), ("kda", 3, 1, 3)])
+                                           ("kda", 16, 2, 5), ("kda", 3, 1, 3),
+                                           ("gdn", 16, 10, 10)])
 def test_window_small_all_heads(variant, W, B, H):
     base = wl.WORKLOADS[4]
     w = wl.custom(base, B=B, H=H, W=W, steps=3 * W + 2,
