@@ -214,6 +214,23 @@ def run_gpu(w: wl.Workload, steps: int, warmup: int):
         step()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
+    phases = None
+    if w.path != "dense":
+        # one untimed pass over whole cycles with an event pair around every launch:
+        # average launch time per window position / per live log length
+        cyc = w.W if w.path == "q8_window" else w.M
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(4 * cyc)]
+        for a, b in evs:
+            a.record(stream)
+            step()
+            b.record(stream)
+        torch.cuda.synchronize()
+        per = [0.0] * cyc
+        for i, (a, b) in enumerate(evs):
+            per[i % cyc] += a.elapsed_time(b) * 1e3 / 4
+        key = "pos" if w.path == "q8_window" else "L"
+        phases = {f"{key}{i}_us": round(t, 2) for i, t in enumerate(per)}
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     e0.record(stream)
@@ -224,7 +241,7 @@ def run_gpu(w: wl.Workload, steps: int, warmup: int):
     wall = time.perf_counter() - t0
     gpu_sec = e0.elapsed_time(e1) / 1e3
     ceiling = copy_ceiling(torch, rsu, 4 * B * H * 128 * 128) if w.path == "dense" else None
-    return gpu_sec, wall, ceiling
+    return gpu_sec, wall, ceiling, phases
 
 
 # ----------------------------------------------------------------- CPU baseline (oracle)
@@ -271,7 +288,7 @@ def main():
     warmup = args.warmup if args.warmup is not None else 2 * cycle
     warmup = (warmup + cycle - 1) // cycle * cycle
 
-    gpu_sec, wall, ceiling = run_gpu(w, steps, warmup)
+    gpu_sec, wall, ceiling, phases = run_gpu(w, steps, warmup)
     heads = w.heads
     per_head = cycle_bytes_per_head(w)
     launch_sec = gpu_sec / steps
@@ -301,6 +318,8 @@ def main():
                              if ceiling else None),
         "wall_s_timed_region": wall,
     }
+    if phases:
+        out["phases"] = phases
     if not args.no_cpu_baseline and w.path == "dense":
         out["cpu_baseline"] = run_cpu_baseline(w)
     print(json.dumps(out), flush=True)

@@ -29,9 +29,11 @@ __global__ __launch_bounds__(kThreads) void log_step_kernel(
     const float* __restrict__ beta, float* __restrict__ y) {
     constexpr int kCp = kMaxC;                 // row stride of the merge coefficients
     __shared__ f32x4 row_vec[kD];              // (E k, E q, k, E), E = exp(lbar') per key row
-    __shared__ f32x2 coefp[2][kMaxC];          // per entry (K_m . Dk, K_m . Dq), per half of the rows
+    __shared__ f32x2 kq_row[kD];               // (k_r, q_r)
+    __shared__ float Ek[kMaxC * kD];           // Ek[m][r] = exp(lbar' - Lam_m) K_m at row r
+    __shared__ f32x2 coef[kMaxC];              // per entry (Ek_m . k, Ek_m . q)
     __shared__ float kq_part[2];
-    __shared__ float kd[kMerge ? kD * kCp : 1];  // merge: exp(lbar' - Lam_m) K_m at row r
+    __shared__ float kd[kMerge ? kD * kCp : 1];  // merge: the transpose kd[r][m] of Ek
 
     const int h = head_of_block(blockIdx.x, gridDim.x), tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
@@ -47,36 +49,53 @@ __global__ __launch_bounds__(kThreads) void log_step_kernel(
     const f32x4 vv = load4_in(v, vec_off + col);
     const float bt = beta[h];
 
-    // ---- key-side preparation: thread -> key row r, entry parity par
-    const int r = tid & (kD - 1), par = tid >> 7;
+    // ---- key-side preparation: thread -> key row r; the first half writes Ek, the
+    // second half (merge only) its transpose
+    const int r = tid & (kD - 1);
+    const bool first = tid < kD;
     const float kr = load_in(k, vec_off + r), qr = load_in(q, vec_off + r);
     const float gr = kPerKey ? gate[vec_off + r] : gate[h];
     const float lb_new = (kPerKey ? lbar[vec_off + r] : lbar[h]) + logf(gr);
-    {
+    if (first || kMerge) {
         const T* Kh = Klog + static_cast<size_t>(h) * C * kD;
         const float* Lh = Lam + static_cast<size_t>(h) * C * gdim;
         for (int m = 0; m < L; ++m) {
             const float lam = kPerKey ? Lh[static_cast<size_t>(m) * kD + r] : Lh[m];
             const float e = expf(lb_new - lam) * load_in(Kh, static_cast<size_t>(m) * kD + r);
-            if ((m & 1) == par) {
-                const f32x2 c = wave_sum2(f32x2{e * kr, e * qr});
-                if (lane == 0) coefp[wave & 1][m] = c;
-            }
-            if (kMerge && par == 0) kd[r * kCp + m] = e;
+            if (first) Ek[m * kD + r] = e;
+            else kd[r * kCp + m] = e;
         }
-        if (par == 0) {
+        if (first) {
             const float E = expf(lb_new);
             row_vec[r] = f32x4{E * kr, E * qr, kr, E};
+            kq_row[r] = f32x2{kr, qr};
             const float kq = wave_sum(kr * qr);
             if (lane == 0) kq_part[wave] = kq;
-            if (kMerge)
-                for (int m = L; m < ((C + 3) & ~3); ++m) kd[r * kCp + m] = 0.f;
+        } else if (kMerge) {
+            for (int m = L; m < ((C + 3) & ~3); ++m) kd[r * kCp + m] = 0.f;
         }
     }
     __syncthreads();
 
+    // ---- replay coefficients: the 16 lanes of a DPP row reduce one entry (8 rows each)
+    {
+        const int chunk = tid & 15, m = tid >> 4;
+        f32x2 c = {0.f, 0.f};
+        if (m < L) {
+            const f32x4 e0 = *reinterpret_cast<const f32x4*>(Ek + m * kD + 8 * chunk);
+            const f32x4 e1 = *reinterpret_cast<const f32x4*>(Ek + m * kD + 8 * chunk + 4);
+            const f32x2* kqr = kq_row + 8 * chunk;
+            c = e0.x * kqr[0] + e0.y * kqr[1] + e0.z * kqr[2] + e0.w * kqr[3] +
+                e1.x * kqr[4] + e1.y * kqr[5] + e1.z * kqr[6] + e1.w * kqr[7];
+        }
+        c.x = row16_sum(c.x);
+        c.y = row16_sum(c.y);
+        if (chunk == 0 && m < L) coef[m] = c;
+    }
+    __syncthreads();
+
     // metadata: one writer per element (all reads of lbar / Lam are done)
-    if (par == 0) {
+    if (first) {
         if (kMerge) {
             if (kPerKey) lbar[vec_off + r] = 0.f;
             else if (r == 0) lbar[h] = 0.f;
@@ -103,7 +122,7 @@ __global__ __launch_bounds__(kThreads) void log_step_kernel(
     }
     const float* Uh = Ulog + static_cast<size_t>(h) * C * kD;
     for (int m = ro; m < L; m += 8) {
-        const f32x2 c = coefp[0][m] + coefp[1][m];
+        const f32x2 c = coef[m];
         const f32x4 u = *reinterpret_cast<const f32x4*>(Uh + static_cast<size_t>(m) * kD + col);
         p1 += u * c.x;
         p2 += u * c.y;

@@ -46,10 +46,8 @@ __device__ __forceinline__ void requantize_tile(const f32x4 (&s)[kRowsPerThread]
     float amax[kRowsPerThread];
 #pragma unroll
     for (int it = 0; it < kRowsPerThread; ++it) {
-        float m = fmaxf(fmaxf(fabsf(s[it].x), fabsf(s[it].y)), fmaxf(fabsf(s[it].z), fabsf(s[it].w)));
-#pragma unroll
-        for (int sh = 1; sh <= 16; sh <<= 1) m = fmaxf(m, xor_shfl(m, sh));
-        amax[it] = m;
+        const float m = fmaxf(fmaxf(fabsf(s[it].x), fabsf(s[it].y)), fmaxf(fabsf(s[it].z), fabsf(s[it].w)));
+        amax[it] = half_wave_max(m);  // the 32 lanes of a half-wave hold one row
     }
     // lane c4 (< 16) of each half-wave publishes the scale of row (c4, wave, ro)
     float mine = 0.f;
@@ -93,10 +91,13 @@ __global__ __launch_bounds__(kThreads) void q8_window_kernel(
     float* __restrict__ Ubuf, float* __restrict__ Gbuf, const T* __restrict__ q,
     const T* __restrict__ k, const T* __restrict__ v, const float* __restrict__ gate,
     const float* __restrict__ beta, float* __restrict__ y) {
-    // boundary only: eT[r][Wp] = Gamma_{j+1:W} k_j at row r, Us[Wp][128] = u_j
+    // dynamic LDS: E[Wp][128], E[j][r] = Gamma_{j+1:l} k_j at key row r (the record's key
+    // decayed to this step, times this step's gate); boundary only: its transpose
+    // Et[128][Wp] and the records' corrections Us[Wp][128]
     extern __shared__ float dyn_lds[];
     __shared__ f32x2 rowv[kD];            // a_r/127 Gamma_{1:l} (k_r, q_r)
-    __shared__ f32x2 coefp[2][kMaxW];     // per record (k_j.Gx, k_j.Gq), per half of the rows
+    __shared__ f32x2 kq_row[kD];          // (k_r, q_r)
+    __shared__ f32x2 coef[kMaxW];         // per record (E_j . k, E_j . q)
     __shared__ f32x2 red[4][kD];          // per-wave column partials
     __shared__ float kq_part[2];
     __shared__ float zcoef[kBoundary ? kD : 1];
@@ -108,8 +109,9 @@ __global__ __launch_bounds__(kThreads) void q8_window_kernel(
     const size_t vec_off = static_cast<size_t>(h) * kD;
     const int gdim = kPerKey ? kD : 1;
     const int Wp = (W + 3) & ~3;
-    float* eT = dyn_lds;
-    float* Us = dyn_lds + kD * Wp;
+    float* E = dyn_lds;
+    float* Et = dyn_lds + kD * Wp;
+    float* Us = dyn_lds + 2 * kD * Wp;
 
     uint32_t* Zh = reinterpret_cast<uint32_t*>(Z + static_cast<size_t>(h) * kD * kD);
     uint32_t zw[kRowsPerThread];
@@ -117,33 +119,53 @@ __global__ __launch_bounds__(kThreads) void q8_window_kernel(
     for (int it = 0; it < kRowsPerThread; ++it)
         zw[it] = __builtin_nontemporal_load(Zh + q8_row(it, wave, ro) * (kD / 4) + c4);
 
-    // ---- key-side preparation: thread -> key row r, record parity par
-    const int r = tid & (kD - 1), par = tid >> 7;
+    // ---- key-side preparation: thread -> key row r; the first half writes E, the
+    // second half (boundary only) its transpose
+    const int r = tid & (kD - 1);
+    const bool first = tid < kD;
     const float kr = load_in(k, vec_off + r), qr = load_in(q, vec_off + r);
     const float gr = kPerKey ? gate[vec_off + r] : gate[h];
-    {
+    if (first || kBoundary) {
         const T* Kh = Kbuf + static_cast<size_t>(h) * W * kD;
         const float* Gh = Gbuf + static_cast<size_t>(h) * W * gdim;
         float G = 1.f;  // product of the gates of the records after j (and before l)
+#pragma unroll 4
         for (int j = pos - 1; j >= 0; --j) {
             const float e = load_in(Kh, static_cast<size_t>(j) * kD + r) * G * gr;
-            if ((j & 1) == par) {
-                const f32x2 c = wave_sum2(f32x2{e * kr, e * qr});
-                if (lane == 0) coefp[wave & 1][j] = c;
-            }
-            if (kBoundary && par == 0) eT[r * Wp + j] = e;
+            if (first) E[j * kD + r] = e;
+            else Et[r * Wp + j] = e;
             G *= kPerKey ? Gh[static_cast<size_t>(j) * kD + r] : Gh[j];
         }
-        if (par == 0) {
+        if (first) {
             const float c0 = A[vec_off + r] / 127.f * G * gr;  // a_r/127 Gamma_{1:l} at row r
             rowv[r] = f32x2{c0 * kr, c0 * qr};
+            kq_row[r] = f32x2{kr, qr};
             const float kq = wave_sum(kr * qr);
             if (lane == 0) kq_part[wave] = kq;
-            if (kBoundary) {
-                zcoef[r] = c0;
-                eT[r * Wp + pos] = kr;
-                for (int j = pos + 1; j < Wp; ++j) eT[r * Wp + j] = 0.f;
+            if (kBoundary) zcoef[r] = c0;
+        } else if (kBoundary) {
+            Et[r * Wp + pos] = kr;
+            for (int j = pos + 1; j < Wp; ++j) Et[r * Wp + j] = 0.f;
+        }
+    }
+    __syncthreads();
+
+    // ---- record coefficients: the 16 lanes of a DPP row reduce one record (8 rows each)
+    {
+        const int chunk = tid & 15;
+        for (int j0 = 0; j0 < pos; j0 += kThreads / 16) {
+            const int j = j0 + (tid >> 4);
+            f32x2 c = {0.f, 0.f};
+            if (j < pos) {
+                const f32x4 e0 = *reinterpret_cast<const f32x4*>(E + j * kD + 8 * chunk);
+                const f32x4 e1 = *reinterpret_cast<const f32x4*>(E + j * kD + 8 * chunk + 4);
+                const f32x2* kqr = kq_row + 8 * chunk;
+                c = e0.x * kqr[0] + e0.y * kqr[1] + e0.z * kqr[2] + e0.w * kqr[3] +
+                    e1.x * kqr[4] + e1.y * kqr[5] + e1.z * kqr[6] + e1.w * kqr[7];
             }
+            c.x = row16_sum(c.x);
+            c.y = row16_sum(c.y);
+            if (chunk == 0 && j < pos) coef[j] = c;
         }
     }
     __syncthreads();
@@ -159,15 +181,13 @@ __global__ __launch_bounds__(kThreads) void q8_window_kernel(
     }
     const float* Uh = Ubuf + static_cast<size_t>(h) * W * kD;
     for (int j = 2 * wave + ro; j < pos; j += 8) {
-        const f32x2 c = coefp[0][j] + coefp[1][j];
+        const f32x2 c = coef[j];
         const f32x4 u = *reinterpret_cast<const f32x4*>(Uh + static_cast<size_t>(j) * kD + 4 * c4);
         p1 += u * c.x;
         p2 += u * c.y;
     }
-    p1.x += xor_shfl(p1.x, 32); p1.y += xor_shfl(p1.y, 32);
-    p1.z += xor_shfl(p1.z, 32); p1.w += xor_shfl(p1.w, 32);
-    p2.x += xor_shfl(p2.x, 32); p2.y += xor_shfl(p2.y, 32);
-    p2.z += xor_shfl(p2.z, 32); p2.w += xor_shfl(p2.w, 32);
+    p1 = f32x4{add_xor32(p1.x), add_xor32(p1.y), add_xor32(p1.z), add_xor32(p1.w)};
+    p2 = f32x4{add_xor32(p2.x), add_xor32(p2.y), add_xor32(p2.z), add_xor32(p2.w)};
     if (ro == 0) {
         red[wave][4 * c4 + 0] = f32x2{p1.x, p2.x};
         red[wave][4 * c4 + 1] = f32x2{p1.y, p2.y};
@@ -177,7 +197,7 @@ __global__ __launch_bounds__(kThreads) void q8_window_kernel(
     __syncthreads();
 
     // ---- correction, output, and the record of this step (thread -> value column)
-    if (tid < kD) {
+    if (first) {
         const int c = tid;
         const f32x2 acc = red[0][c] + red[1][c] + red[2][c] + red[3][c];
         const float kq = kq_part[0] + kq_part[1];
@@ -209,7 +229,7 @@ __global__ __launch_bounds__(kThreads) void q8_window_kernel(
         const f32x4 u3 = *reinterpret_cast<const f32x4*>(Us + (j0 + 3) * kD + 4 * c4);
 #pragma unroll
         for (int it = 0; it < kRowsPerThread; ++it) {
-            const f32x4 e = *reinterpret_cast<const f32x4*>(eT + q8_row(it, wave, ro) * Wp + j0);
+            const f32x4 e = *reinterpret_cast<const f32x4*>(Et + q8_row(it, wave, ro) * Wp + j0);
             s[it] += u0 * e.x + u1 * e.y + u2 * e.z + u3 * e.w;
         }
     }
@@ -226,13 +246,14 @@ static hipError_t launch_window_t(const StepArgs& a, const WindowArgs& w, hipStr
     const bool boundary = w.pos == w.W - 1;
     const int Wp = (w.W + 3) & ~3;
     if (boundary) {
-        const size_t lds = sizeof(float) * 2 * kD * Wp;
+        const size_t lds = sizeof(float) * 3 * kD * Wp;
         hipLaunchKernelGGL((q8_window_kernel<kPerKey, true, T>), dim3(a.heads), dim3(kThreads), lds,
                            stream, w.W, w.pos, w.Z, w.A, static_cast<T*>(w.Kbuf), w.Ubuf, w.Gbuf,
                            static_cast<const T*>(a.q), static_cast<const T*>(a.k),
                            static_cast<const T*>(a.v), a.gate, a.beta, a.y);
     } else {
-        hipLaunchKernelGGL((q8_window_kernel<kPerKey, false, T>), dim3(a.heads), dim3(kThreads), 0,
+        const size_t lds = sizeof(float) * kD * Wp;
+        hipLaunchKernelGGL((q8_window_kernel<kPerKey, false, T>), dim3(a.heads), dim3(kThreads), lds,
                            stream, w.W, w.pos, w.Z, w.A, static_cast<T*>(w.Kbuf), w.Ubuf, w.Gbuf,
                            static_cast<const T*>(a.q), static_cast<const T*>(a.k),
                            static_cast<const T*>(a.v), a.gate, a.beta, a.y);

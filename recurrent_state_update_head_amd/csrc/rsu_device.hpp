@@ -88,34 +88,77 @@ __device__ __forceinline__ int head_of_block(int bid, int nblk) {
     return bid / grp * grp + (bid % kXcds) * kXcdRun + (bid / kXcds) % kXcdRun;
 }
 
-__device__ __forceinline__ float xor_shfl(float x, int mask) { return __shfl_xor(x, mask, 64); }
+// ---- cross-lane reductions on the VALU (DPP and permlane swaps; no LDS round trip)
+// Lane layouts checked on gfx950: quad_perm 0xB1 / 0x4E exchange lanes i^1 / i^2,
+// row_ror:8 exchanges i^8 inside each row of 16 lanes, row_ror:4 rotates a row by
+// 4, and the two results of permlane16_swap(x, x) / permlane32_swap(x, x) hold
+// x of lane i and of lane i^16 / i^32.
+template <int kCtrl>
+__device__ __forceinline__ float dpp(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), kCtrl,
+                                                                 0xF, 0xF, false));
+}
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppRor4 = 0x124, kDppRor8 = 0x128;
+
+// The two results are copied to scalars before any bit cast: with this toolchain,
+// __builtin_bit_cast of an element of the returned vector reads element 0.
+__device__ __forceinline__ void swap16(float x, float& lo, float& hi) {
+    const unsigned b = __builtin_bit_cast(unsigned, x);
+    const auto p = __builtin_amdgcn_permlane16_swap(b, b, false, false);
+    const unsigned p0 = p[0], p1 = p[1];
+    lo = __uint_as_float(p0);
+    hi = __uint_as_float(p1);
+}
+__device__ __forceinline__ void swap32(float x, float& lo, float& hi) {
+    const unsigned b = __builtin_bit_cast(unsigned, x);
+    const auto p = __builtin_amdgcn_permlane32_swap(b, b, false, false);
+    const unsigned p0 = p[0], p1 = p[1];
+    lo = __uint_as_float(p0);
+    hi = __uint_as_float(p1);
+}
+__device__ __forceinline__ float add_xor16(float x) {
+    float a, b;
+    swap16(x, a, b);
+    return a + b;
+}
+__device__ __forceinline__ float add_xor32(float x) {
+    float a, b;
+    swap32(x, a, b);
+    return a + b;
+}
+__device__ __forceinline__ float max_xor16(float x) {
+    float a, b;
+    swap16(x, a, b);
+    return fmaxf(a, b);
+}
+
+// Sum over the 16 lanes of each DPP row (result in every lane of the row).
+__device__ __forceinline__ float row16_sum(float x) {
+    x += dpp<kDppXor1>(x);
+    x += dpp<kDppXor2>(x);
+    x += dpp<kDppRor8>(x);
+    x += dpp<kDppRor4>(x);
+    return x;
+}
+// Max over the 32 lanes of each half-wave.
+__device__ __forceinline__ float half_wave_max(float x) {
+    x = fmaxf(x, dpp<kDppXor1>(x));
+    x = fmaxf(x, dpp<kDppXor2>(x));
+    x = fmaxf(x, dpp<kDppRor8>(x));
+    x = fmaxf(x, dpp<kDppRor4>(x));
+    return max_xor16(x);
+}
+// Sum over all 64 lanes of a wave (result in every lane).
+__device__ __forceinline__ float wave_sum(float x) { return add_xor32(add_xor16(row16_sum(x))); }
 
 // Sum over the lanes that differ only in lane bits 3..5 (the 8 row lanes of a
 // column group in the fp32-state layout).
+__device__ __forceinline__ float sum_row_lanes(float x) {
+    x += dpp<kDppRor8>(x);
+    return add_xor32(add_xor16(x));
+}
 __device__ __forceinline__ f32x4 sum_row_lanes(f32x4 x) {
-#pragma unroll
-    for (int m = 8; m <= 32; m <<= 1) {
-        x.x += xor_shfl(x.x, m);
-        x.y += xor_shfl(x.y, m);
-        x.z += xor_shfl(x.z, m);
-        x.w += xor_shfl(x.w, m);
-    }
-    return x;
-}
-
-// Sum over all 64 lanes of a wave (result in every lane).
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-    for (int m = 1; m <= 32; m <<= 1) x += xor_shfl(x, m);
-    return x;
-}
-__device__ __forceinline__ f32x2 wave_sum2(f32x2 x) {
-#pragma unroll
-    for (int m = 1; m <= 32; m <<= 1) {
-        x.x += xor_shfl(x.x, m);
-        x.y += xor_shfl(x.y, m);
-    }
-    return x;
+    return f32x4{sum_row_lanes(x.x), sum_row_lanes(x.y), sum_row_lanes(x.z), sum_row_lanes(x.w)};
 }
 
 }  // namespace rsu
