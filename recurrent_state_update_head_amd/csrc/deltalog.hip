@@ -30,7 +30,9 @@ __global__ __launch_bounds__(kThreads) void log_step_kernel(
     constexpr int kCp = kMaxC;                 // row stride of the merge coefficients
     __shared__ f32x4 row_vec[kD];              // (E k, E q, k, E), E = exp(lbar') per key row
     __shared__ f32x2 kq_row[kD];               // (k_r, q_r)
-    __shared__ float Ek[kMaxC * kD];           // Ek[m][r] = exp(lbar' - Lam_m) K_m at row r
+    __shared__ float Ek[kMaxC * kD];           // K_m, turned in place into exp(lbar' - Lam_m) K_m
+    __shared__ float Us[kMaxC * kD];           // U_m
+    __shared__ float Ls[kPerKey ? kMaxC * kD : kMaxC];  // Lam_m
     __shared__ f32x2 coef[kMaxC];              // per entry (Ek_m . k, Ek_m . q)
     __shared__ float kq_part[2];
     __shared__ float kd[kMerge ? kD * kCp : 1];  // merge: the transpose kd[r][m] of Ek
@@ -40,40 +42,51 @@ __global__ __launch_bounds__(kThreads) void log_step_kernel(
     const int ro = lane >> 3;
     const int col = wave * 32 + (lane & 7) * 4;
     const size_t vec_off = static_cast<size_t>(h) * kD;
-    const int gdim = kPerKey ? kD : 1;
+    const size_t ent0 = static_cast<size_t>(h) * C * kD;
 
+    // ---- every load of the step is issued here: log entries, the base tile, inputs
+    Stager<T, kMaxC * kD> sk;
+    Stager<float, kMaxC * kD> su;
+    Stager<float, kPerKey ? kMaxC * kD : 8> sl;
+    sk.load(Klog + ent0, L * kD, tid);
+    su.load(Ulog + ent0, L * kD, tid);
+    float lam_s = 0.f;
+    if constexpr (kPerKey) sl.load(Lam + ent0, L * kD, tid);
+    else if (tid < L) lam_s = Lam[static_cast<size_t>(h) * C + tid];
     float* Sh = Sbase + static_cast<size_t>(h) * kD * kD;
     f32x4 s[kRowsPerThread];
 #pragma unroll
     for (int it = 0; it < kRowsPerThread; ++it) s[it] = stream_load(Sh + (it * 8 + ro) * kD + col);
     const f32x4 vv = load4_in(v, vec_off + col);
     const float bt = beta[h];
-
-    // ---- key-side preparation: thread -> key row r; the first half writes Ek, the
-    // second half (merge only) its transpose
     const int r = tid & (kD - 1);
     const bool first = tid < kD;
     const float kr = load_in(k, vec_off + r), qr = load_in(q, vec_off + r);
     const float gr = kPerKey ? gate[vec_off + r] : gate[h];
-    const float lb_new = (kPerKey ? lbar[vec_off + r] : lbar[h]) + logf(gr);
-    if (first || kMerge) {
-        const T* Kh = Klog + static_cast<size_t>(h) * C * kD;
-        const float* Lh = Lam + static_cast<size_t>(h) * C * gdim;
+    const float lb_old = kPerKey ? lbar[vec_off + r] : lbar[h];
+
+    sk.store(Ek, tid);
+    su.store(Us, tid);
+    if constexpr (kPerKey) sl.store(Ls, tid);
+    else if (tid < L) Ls[tid] = lam_s;
+    __syncthreads();
+
+    // ---- key-side preparation: thread r < 128 owns key row r
+    const float lb_new = lb_old + logf(gr);
+    if (first) {
         for (int m = 0; m < L; ++m) {
-            const float lam = kPerKey ? Lh[static_cast<size_t>(m) * kD + r] : Lh[m];
-            const float e = expf(lb_new - lam) * load_in(Kh, static_cast<size_t>(m) * kD + r);
-            if (first) Ek[m * kD + r] = e;
-            else kd[r * kCp + m] = e;
+            const float lam = kPerKey ? Ls[m * kD + r] : Ls[m];
+            const float e = expf(lb_new - lam) * Ek[m * kD + r];
+            Ek[m * kD + r] = e;  // in place: row r belongs to this thread
+            if (kMerge) kd[r * kCp + m] = e;
         }
-        if (first) {
-            const float E = expf(lb_new);
-            row_vec[r] = f32x4{E * kr, E * qr, kr, E};
-            kq_row[r] = f32x2{kr, qr};
-            const float kq = wave_sum(kr * qr);
-            if (lane == 0) kq_part[wave] = kq;
-        } else if (kMerge) {
+        if (kMerge)
             for (int m = L; m < ((C + 3) & ~3); ++m) kd[r * kCp + m] = 0.f;
-        }
+        const float E = expf(lb_new);
+        row_vec[r] = f32x4{E * kr, E * qr, kr, E};
+        kq_row[r] = f32x2{kr, qr};
+        const float kq = wave_sum(kr * qr);
+        if (lane == 0) kq_part[wave] = kq;
     }
     __syncthreads();
 
@@ -120,10 +133,9 @@ __global__ __launch_bounds__(kThreads) void log_step_kernel(
         p1 += s[it] * rv.x;
         p2 += s[it] * rv.y;
     }
-    const float* Uh = Ulog + static_cast<size_t>(h) * C * kD;
     for (int m = ro; m < L; m += 8) {
         const f32x2 c = coef[m];
-        const f32x4 u = *reinterpret_cast<const f32x4*>(Uh + static_cast<size_t>(m) * kD + col);
+        const f32x4 u = *reinterpret_cast<const f32x4*>(Us + m * kD + col);
         p1 += u * c.x;
         p2 += u * c.y;
     }
@@ -133,7 +145,7 @@ __global__ __launch_bounds__(kThreads) void log_step_kernel(
     const f32x4 b = bt * (vv - p1);
     if (ro == 0) {
         *reinterpret_cast<f32x4*>(y + vec_off + col) = p2 + b * kq;
-        if (!kMerge) *reinterpret_cast<f32x4*>(Ulog + (static_cast<size_t>(h) * C + L) * kD + col) = b;
+        if (!kMerge) *reinterpret_cast<f32x4*>(Ulog + ent0 + static_cast<size_t>(L) * kD + col) = b;
     }
     if (!kMerge) return;
 
@@ -147,7 +159,7 @@ __global__ __launch_bounds__(kThreads) void log_step_kernel(
         f32x4 u[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            u[i] = (m0 + i < L) ? *reinterpret_cast<const f32x4*>(Uh + static_cast<size_t>(m0 + i) * kD + col)
+            u[i] = (m0 + i < L) ? *reinterpret_cast<const f32x4*>(Us + (m0 + i) * kD + col)
                                 : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int it = 0; it < kRowsPerThread; ++it) {

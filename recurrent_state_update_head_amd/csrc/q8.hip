@@ -85,16 +85,21 @@ __global__ __launch_bounds__(kThreads) void q8_quantize_kernel(const float* __re
                     A + static_cast<size_t>(h) * kD, scale_s, wave, lane);
 }
 
+// Dynamic LDS of a window step, in floats: KE[Wp][128] (record keys, turned in
+// place into the decayed keys E), Us[Wp][128] (record corrections), Gs[Wp][128]
+// (record gates, KDA only) and, at the boundary, Et[128][Wp + 4] (E transposed).
+__host__ __device__ constexpr int window_lds_floats(int Wp, bool per_key, bool boundary) {
+    return (2 + (per_key ? 1 : 0)) * Wp * kD + (boundary ? kD * (Wp + 4) : 0);
+}
+
 template <bool kPerKey, bool kBoundary, typename T>
 __global__ __launch_bounds__(kThreads) void q8_window_kernel(
     int W, int pos, int8_t* __restrict__ Z, float* __restrict__ A, T* __restrict__ Kbuf,
     float* __restrict__ Ubuf, float* __restrict__ Gbuf, const T* __restrict__ q,
     const T* __restrict__ k, const T* __restrict__ v, const float* __restrict__ gate,
     const float* __restrict__ beta, float* __restrict__ y) {
-    // dynamic LDS: E[Wp][128], E[j][r] = Gamma_{j+1:l} k_j at key row r (the record's key
-    // decayed to this step, times this step's gate); boundary only: its transpose
-    // Et[128][Wp] and the records' corrections Us[Wp][128]
     extern __shared__ float dyn_lds[];
+    __shared__ float gs_scalar[kMaxW];    // GDN: the records' gates
     __shared__ f32x2 rowv[kD];            // a_r/127 Gamma_{1:l} (k_r, q_r)
     __shared__ f32x2 kq_row[kD];          // (k_r, q_r)
     __shared__ f32x2 coef[kMaxW];         // per record (E_j . k, E_j . q)
@@ -107,45 +112,61 @@ __global__ __launch_bounds__(kThreads) void q8_window_kernel(
     const int wave = tid >> 6, lane = tid & 63;
     const int c4 = lane & 31, ro = lane >> 5;
     const size_t vec_off = static_cast<size_t>(h) * kD;
-    const int gdim = kPerKey ? kD : 1;
-    const int Wp = (W + 3) & ~3;
-    float* E = dyn_lds;
-    float* Et = dyn_lds + kD * Wp;
-    float* Us = dyn_lds + 2 * kD * Wp;
+    const size_t rec0 = static_cast<size_t>(h) * W * kD;
+    const int Wp = (W + 3) & ~3, EtS = Wp + 4;
+    float* KE = dyn_lds;
+    float* Us = KE + Wp * kD;
+    float* Gs = Us + Wp * kD;
+    float* Et = Gs + (kPerKey ? Wp * kD : 0);
 
+    // ---- every load of the step is issued here: codes, records, inputs
     uint32_t* Zh = reinterpret_cast<uint32_t*>(Z + static_cast<size_t>(h) * kD * kD);
     uint32_t zw[kRowsPerThread];
 #pragma unroll
     for (int it = 0; it < kRowsPerThread; ++it)
         zw[it] = __builtin_nontemporal_load(Zh + q8_row(it, wave, ro) * (kD / 4) + c4);
-
-    // ---- key-side preparation: thread -> key row r; the first half writes E, the
-    // second half (boundary only) its transpose
+    Stager<T, kMaxW * kD> sk;
+    Stager<float, kMaxW * kD> su;
+    sk.load(Kbuf + rec0, pos * kD, tid);
+    su.load(Ubuf + rec0, pos * kD, tid);
+    Stager<float, kPerKey ? kMaxW * kD : 8> sg;
+    float g_rec = 1.f;
+    if constexpr (kPerKey) sg.load(Gbuf + rec0, pos * kD, tid);
+    else if (tid < pos) g_rec = Gbuf[static_cast<size_t>(h) * W + tid];
     const int r = tid & (kD - 1);
     const bool first = tid < kD;
     const float kr = load_in(k, vec_off + r), qr = load_in(q, vec_off + r);
     const float gr = kPerKey ? gate[vec_off + r] : gate[h];
-    if (first || kBoundary) {
-        const T* Kh = Kbuf + static_cast<size_t>(h) * W * kD;
-        const float* Gh = Gbuf + static_cast<size_t>(h) * W * gdim;
+    const float ar = A[vec_off + r];
+    const float vr = load_in(v, vec_off + r);
+    const float bt = beta[h];
+
+    sk.store(KE, tid);
+    su.store(Us, tid);
+    if constexpr (kPerKey) sg.store(Gs, tid);
+    else if (tid < pos) gs_scalar[tid] = g_rec;
+    if (kBoundary)  // rows W..Wp-1 of Us meet zero coefficients at the boundary; keep them finite
+        for (int i = W * kD + tid; i < Wp * kD; i += kThreads) Us[i] = 0.f;
+    __syncthreads();
+
+    // ---- key-side preparation: thread r < 128 walks the records of key row r backwards
+    if (first) {
         float G = 1.f;  // product of the gates of the records after j (and before l)
-#pragma unroll 4
         for (int j = pos - 1; j >= 0; --j) {
-            const float e = load_in(Kh, static_cast<size_t>(j) * kD + r) * G * gr;
-            if (first) E[j * kD + r] = e;
-            else Et[r * Wp + j] = e;
-            G *= kPerKey ? Gh[static_cast<size_t>(j) * kD + r] : Gh[j];
+            const float e = KE[j * kD + r] * G * gr;  // Gamma_{j+1:l} k_j at row r
+            KE[j * kD + r] = e;                        // in place: row r belongs to this thread
+            if (kBoundary) Et[r * EtS + j] = e;
+            G *= kPerKey ? Gs[j * kD + r] : gs_scalar[j];
         }
-        if (first) {
-            const float c0 = A[vec_off + r] / 127.f * G * gr;  // a_r/127 Gamma_{1:l} at row r
-            rowv[r] = f32x2{c0 * kr, c0 * qr};
-            kq_row[r] = f32x2{kr, qr};
-            const float kq = wave_sum(kr * qr);
-            if (lane == 0) kq_part[wave] = kq;
-            if (kBoundary) zcoef[r] = c0;
-        } else if (kBoundary) {
-            Et[r * Wp + pos] = kr;
-            for (int j = pos + 1; j < Wp; ++j) Et[r * Wp + j] = 0.f;
+        const float c0 = ar / 127.f * G * gr;  // a_r/127 Gamma_{1:l} at row r
+        rowv[r] = f32x2{c0 * kr, c0 * qr};
+        kq_row[r] = f32x2{kr, qr};
+        const float kq = wave_sum(kr * qr);
+        if (lane == 0) kq_part[wave] = kq;
+        if (kBoundary) {
+            zcoef[r] = c0;
+            Et[r * EtS + pos] = kr;
+            for (int j = pos + 1; j < Wp; ++j) Et[r * EtS + j] = 0.f;
         }
     }
     __syncthreads();
@@ -157,8 +178,8 @@ __global__ __launch_bounds__(kThreads) void q8_window_kernel(
             const int j = j0 + (tid >> 4);
             f32x2 c = {0.f, 0.f};
             if (j < pos) {
-                const f32x4 e0 = *reinterpret_cast<const f32x4*>(E + j * kD + 8 * chunk);
-                const f32x4 e1 = *reinterpret_cast<const f32x4*>(E + j * kD + 8 * chunk + 4);
+                const f32x4 e0 = *reinterpret_cast<const f32x4*>(KE + j * kD + 8 * chunk);
+                const f32x4 e1 = *reinterpret_cast<const f32x4*>(KE + j * kD + 8 * chunk + 4);
                 const f32x2* kqr = kq_row + 8 * chunk;
                 c = e0.x * kqr[0] + e0.y * kqr[1] + e0.z * kqr[2] + e0.w * kqr[3] +
                     e1.x * kqr[4] + e1.y * kqr[5] + e1.z * kqr[6] + e1.w * kqr[7];
@@ -179,10 +200,9 @@ __global__ __launch_bounds__(kThreads) void q8_window_kernel(
         p1 += zf * rv.x;
         p2 += zf * rv.y;
     }
-    const float* Uh = Ubuf + static_cast<size_t>(h) * W * kD;
     for (int j = 2 * wave + ro; j < pos; j += 8) {
         const f32x2 c = coef[j];
-        const f32x4 u = *reinterpret_cast<const f32x4*>(Uh + static_cast<size_t>(j) * kD + 4 * c4);
+        const f32x4 u = *reinterpret_cast<const f32x4*>(Us + j * kD + 4 * c4);
         p1 += u * c.x;
         p2 += u * c.y;
     }
@@ -196,19 +216,19 @@ __global__ __launch_bounds__(kThreads) void q8_window_kernel(
     }
     __syncthreads();
 
-    // ---- correction, output, and the record of this step (thread -> value column)
+    // ---- correction, output, and the record of this step (thread -> value column c == r)
     if (first) {
         const int c = tid;
         const f32x2 acc = red[0][c] + red[1][c] + red[2][c] + red[3][c];
         const float kq = kq_part[0] + kq_part[1];
-        const float u = beta[h] * (load_in(v, vec_off + c) - acc.x);
+        const float u = bt * (vr - acc.x);
         y[vec_off + c] = acc.y + u * kq;
         if (kBoundary) {
             Us[pos * kD + c] = u;
         } else {
-            const size_t rec = (static_cast<size_t>(h) * W + pos) * kD;
+            const size_t rec = rec0 + static_cast<size_t>(pos) * kD;
             Ubuf[rec + c] = u;
-            store_in(Kbuf, rec + c, kr);  // thread c < 128 holds k at row r == c
+            store_in(Kbuf, rec + c, kr);
             if (kPerKey) Gbuf[rec + c] = gr;
             else if (c == 0) Gbuf[static_cast<size_t>(h) * W + pos] = gr;
         }
@@ -216,8 +236,6 @@ __global__ __launch_bounds__(kThreads) void q8_window_kernel(
     if (!kBoundary) return;
 
     // ---- window boundary: S_W = Gamma_{1:W} S^_0 + sum_j Gamma_{j+1:W} k_j u_j^T, requantize
-    for (int i = tid; i < pos * kD; i += kThreads) Us[i] = Uh[i];
-    for (int i = (pos + 1) * kD + tid; i < Wp * kD; i += kThreads) Us[i] = 0.f;
     __syncthreads();
     f32x4 s[kRowsPerThread];
 #pragma unroll
@@ -229,7 +247,7 @@ __global__ __launch_bounds__(kThreads) void q8_window_kernel(
         const f32x4 u3 = *reinterpret_cast<const f32x4*>(Us + (j0 + 3) * kD + 4 * c4);
 #pragma unroll
         for (int it = 0; it < kRowsPerThread; ++it) {
-            const f32x4 e = *reinterpret_cast<const f32x4*>(Et + q8_row(it, wave, ro) * Wp + j0);
+            const f32x4 e = *reinterpret_cast<const f32x4*>(Et + q8_row(it, wave, ro) * EtS + j0);
             s[it] += u0 * e.x + u1 * e.y + u2 * e.z + u3 * e.w;
         }
     }
@@ -241,24 +259,26 @@ hipError_t launch_q8_quantize(int heads, const float* S, int8_t* Z, float* A, hi
     return hipGetLastError();
 }
 
+template <bool kPerKey, bool kBoundary, typename T>
+static hipError_t launch_window_kernel(const StepArgs& a, const WindowArgs& w, hipStream_t stream) {
+    const int Wp = (w.W + 3) & ~3;
+    const size_t lds = sizeof(float) * window_lds_floats(Wp, kPerKey, kBoundary);
+    static const hipError_t attr = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(q8_window_kernel<kPerKey, kBoundary, T>),
+        hipFuncAttributeMaxDynamicSharedMemorySize,
+        static_cast<int>(sizeof(float) * window_lds_floats(kMaxW, kPerKey, kBoundary)));
+    if (attr != hipSuccess) return attr;
+    hipLaunchKernelGGL((q8_window_kernel<kPerKey, kBoundary, T>), dim3(a.heads), dim3(kThreads), lds,
+                       stream, w.W, w.pos, w.Z, w.A, static_cast<T*>(w.Kbuf), w.Ubuf, w.Gbuf,
+                       static_cast<const T*>(a.q), static_cast<const T*>(a.k),
+                       static_cast<const T*>(a.v), a.gate, a.beta, a.y);
+    return hipGetLastError();
+}
+
 template <bool kPerKey, typename T>
 static hipError_t launch_window_t(const StepArgs& a, const WindowArgs& w, hipStream_t stream) {
-    const bool boundary = w.pos == w.W - 1;
-    const int Wp = (w.W + 3) & ~3;
-    if (boundary) {
-        const size_t lds = sizeof(float) * 3 * kD * Wp;
-        hipLaunchKernelGGL((q8_window_kernel<kPerKey, true, T>), dim3(a.heads), dim3(kThreads), lds,
-                           stream, w.W, w.pos, w.Z, w.A, static_cast<T*>(w.Kbuf), w.Ubuf, w.Gbuf,
-                           static_cast<const T*>(a.q), static_cast<const T*>(a.k),
-                           static_cast<const T*>(a.v), a.gate, a.beta, a.y);
-    } else {
-        const size_t lds = sizeof(float) * kD * Wp;
-        hipLaunchKernelGGL((q8_window_kernel<kPerKey, false, T>), dim3(a.heads), dim3(kThreads), lds,
-                           stream, w.W, w.pos, w.Z, w.A, static_cast<T*>(w.Kbuf), w.Ubuf, w.Gbuf,
-                           static_cast<const T*>(a.q), static_cast<const T*>(a.k),
-                           static_cast<const T*>(a.v), a.gate, a.beta, a.y);
-    }
-    return hipGetLastError();
+    return w.pos == w.W - 1 ? launch_window_kernel<kPerKey, true, T>(a, w, stream)
+                            : launch_window_kernel<kPerKey, false, T>(a, w, stream);
 }
 
 hipError_t launch_q8_window(const StepArgs& a, const WindowArgs& w, bool per_key, bool bf16,

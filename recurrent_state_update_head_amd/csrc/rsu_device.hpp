@@ -52,6 +52,46 @@ __device__ __forceinline__ f32x2 load2_in(const bf16_t* p, size_t i) {
     return f32x2{__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u)};
 }
 
+// ---- cooperative staging of a head's small arrays (records, log entries) into LDS
+// as fp32. Every load of the block is issued before any LDS write, so staging costs
+// one memory round trip. n (elements) must be a multiple of 8; at most
+// kMaxElems elements.
+template <typename T, int kMaxElems>
+struct Stager {
+    static constexpr int kPer = 16 / sizeof(T);                             // elements per 16 B
+    static constexpr int kSlots = (kMaxElems / kPer + kThreads - 1) / kThreads;
+    uint4 buf[kSlots];
+    int n;
+    __device__ __forceinline__ void load(const T* __restrict__ src, int n_elems, int tid) {
+        n = n_elems;
+#pragma unroll
+        for (int i = 0; i < kSlots; ++i) {
+            const int c = tid + i * kThreads;
+            // clamp the index instead of branching so the slot stays in registers
+            const int cc = c * kPer < n ? c : 0;
+            buf[i] = n > 0 ? *reinterpret_cast<const uint4*>(src + cc * kPer) : uint4{0u, 0u, 0u, 0u};
+        }
+    }
+    __device__ __forceinline__ void store(float* __restrict__ dst, int tid) const {
+#pragma unroll
+        for (int i = 0; i < kSlots; ++i) {
+            const int c = tid + i * kThreads;
+            if (c * kPer >= n) continue;
+            if constexpr (sizeof(T) == 4) {
+                *reinterpret_cast<uint4*>(dst + c * kPer) = buf[i];
+            } else {
+                const uint32_t w[4] = {buf[i].x, buf[i].y, buf[i].z, buf[i].w};
+                f32x4 lo = {__uint_as_float(w[0] << 16), __uint_as_float(w[0] & 0xffff0000u),
+                            __uint_as_float(w[1] << 16), __uint_as_float(w[1] & 0xffff0000u)};
+                f32x4 hi = {__uint_as_float(w[2] << 16), __uint_as_float(w[2] & 0xffff0000u),
+                            __uint_as_float(w[3] << 16), __uint_as_float(w[3] & 0xffff0000u)};
+                *reinterpret_cast<f32x4*>(dst + c * kPer) = lo;
+                *reinterpret_cast<f32x4*>(dst + c * kPer + 4) = hi;
+            }
+        }
+    }
+};
+
 // Orders this wave's LDS writes before its later LDS reads of other lanes' data
 // (no workgroup barrier: the four waves of a head never exchange data).
 __device__ __forceinline__ void wave_lds_sync() {
