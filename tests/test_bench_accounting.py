@@ -1,0 +1,78 @@
+"""bench.py's algorithmic byte accounting against sizes and formulas the pages print
+(tests/golden/page_figures.json, each entry cited)."""
+import json
+import os
+
+import pytest
+
+import bench
+import workloads as wl
+
+FIG = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "page_figures.json")))
+
+
+def _state_part(w):
+    """Bytes of a dense step that are state traffic (the rest is q/k/v/gates/y)."""
+    d = wl.DK
+    other = 3 * d * (2 if w.qkv == "bf16" else 4) + (4 * d if w.per_key_gate else 4) + 4 + 4 * d
+    return bench.dense_bytes_per_head(w) - other
+
+
+def test_one_gib_state_and_two_gib_per_eager_step():
+    f = FIG["state_1gib"]
+    w = wl.custom(wl.WORKLOADS[2], B=f["B"], H=f["H"])
+    assert 4 * f["dk"] * f["dv"] * w.heads == f["state_bytes"]
+    assert _state_part(w) * w.heads == f["eager_state_traffic_bytes"]
+
+
+def test_dense_step_moves_8_bytes_per_state_element():
+    f = FIG["dense_intensity"]
+    for cid in (1, 2, 3):
+        w = wl.WORKLOADS[cid]
+        assert _state_part(w) == f["bytes_per_state_element_moved"] * wl.DK * wl.DV
+    assert f["flops_per_state"] / f["bytes_per_state_element_moved"] == f["ai"]
+
+
+def test_request_state_size():
+    f = FIG["request_state_144mib"]
+    assert f["heads"] * f["dk"] * f["dv"] * 4 == f["bytes"] == 144 * 2 ** 20
+
+
+@pytest.mark.parametrize("variant", ["gdn", "kda"])
+def test_log_entry_bytes_match_eq9(variant):
+    f = FIG["log_entry_bytes"][f"{variant}_bf16"]
+    w = wl.custom(wl.WORKLOADS[5], variant=variant)
+    eq9 = f["pK"] * wl.DK + f["pU"] * wl.DV + 4 * f["dlambda"]
+    assert eq9 == f["per_head"]
+    # an append at L+1 reads one more entry than an append at L
+    assert bench.log_step_bytes_per_head(w, 1) - bench.log_step_bytes_per_head(w, 0) == eq9
+
+
+@pytest.mark.parametrize("M", FIG["log_traffic_model"]["M"])
+def test_log_cycle_matches_eq10(M):
+    """Cycle-averaged log-entry traffic of bench.py equals eq. 10 exactly."""
+    w = wl.custom(wl.WORKLOADS[5], M=M)
+    d = wl.DK
+    c_entry = 2 * d + 4 * d + 4
+    per_step = [bench.log_step_bytes_per_head(w, L) for L in range(M)]
+    # remove what is not log-entry traffic: base read, lbar, inputs, y, and the merge's base write
+    base = 4 * d * d + 4 + (3 * d * 2 + 4 + 4) + 4 * d
+    entry_traffic = sum(per_step) - M * base - (4 * d * d + 4) - (M - 1) * 4
+    assert entry_traffic / M == pytest.approx(c_entry * ((M - 1) / M + (M - 1) / 2), rel=0, abs=1e-9)
+
+
+def test_window_buffer_8kib():
+    f = FIG["window_buffer_8kib"]
+    assert f["W"] * (f["dk"] + f["dv"]) * f["bytes_per_value"] == f["bytes"]
+    # bench.py's records hold k in its input dtype, u in fp32 and the gate: at bf16 keys
+    w = wl.WORKLOADS[4]
+    rec = bench.window_step_bytes_per_head(w, 1) - bench.window_step_bytes_per_head(w, 0)
+    assert rec == 2 * wl.DK + 4 * wl.DV + 4
+    assert f["W"] * (2 * wl.DK + 2 * wl.DV) == f["bytes"]
+
+
+def test_headline_workload_bytes():
+    w = wl.WORKLOADS[2]
+    assert bench.dense_bytes_per_head(w) == 132360
+    assert bench.cycle_bytes_per_head(wl.WORKLOADS[4]) == pytest.approx(25754, abs=1)
+    assert bench.cycle_bytes_per_head(wl.WORKLOADS[5]) == pytest.approx(78401.5, abs=1e-9)
