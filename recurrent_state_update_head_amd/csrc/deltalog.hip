@@ -44,7 +44,7 @@ __global__ __launch_bounds__(kThreads) void log_step_kernel(
     const size_t vec_off = static_cast<size_t>(h) * kD;
     const size_t ent0 = static_cast<size_t>(h) * C * kD;
 
-    // ---- every load of the step is issued here: log entries, the base tile, inputs
+    // ---- every load of the step is issued here: log entries, inputs, the base tile
     Stager<T, kMaxC * kD> sk;
     Stager<float, kMaxC * kD> su;
     Stager<float, kPerKey ? kMaxC * kD : 8> sl;
@@ -53,10 +53,6 @@ __global__ __launch_bounds__(kThreads) void log_step_kernel(
     float lam_s = 0.f;
     if constexpr (kPerKey) sl.load(Lam + ent0, L * kD, tid);
     else if (tid < L) lam_s = Lam[static_cast<size_t>(h) * C + tid];
-    float* Sh = Sbase + static_cast<size_t>(h) * kD * kD;
-    f32x4 s[kRowsPerThread];
-#pragma unroll
-    for (int it = 0; it < kRowsPerThread; ++it) s[it] = stream_load(Sh + (it * 8 + ro) * kD + col);
     const f32x4 vv = load4_in(v, vec_off + col);
     const float bt = beta[h];
     const int r = tid & (kD - 1);
@@ -64,6 +60,12 @@ __global__ __launch_bounds__(kThreads) void log_step_kernel(
     const float kr = load_in(k, vec_off + r), qr = load_in(q, vec_off + r);
     const float gr = kPerKey ? gate[vec_off + r] : gate[h];
     const float lb_old = kPerKey ? lbar[vec_off + r] : lbar[h];
+    // the base tile last: loads complete in order, so the preparation below waits only
+    // for the log entries and inputs while the tile is still in flight
+    float* Sh = Sbase + static_cast<size_t>(h) * kD * kD;
+    f32x4 s[kRowsPerThread];
+#pragma unroll
+    for (int it = 0; it < kRowsPerThread; ++it) s[it] = stream_load(Sh + (it * 8 + ro) * kD + col);
 
     sk.store(Ek, tid);
     su.store(Us, tid);

@@ -85,11 +85,23 @@ __global__ __launch_bounds__(kThreads) void q8_quantize_kernel(const float* __re
                     A + static_cast<size_t>(h) * kD, scale_s, wave, lane);
 }
 
-// Dynamic LDS of a window step, in floats: KE[Wp][128] (record keys, turned in
+// Dynamic LDS of a window step, in 32-bit words: KE[Wp][128] (record keys, turned in
 // place into the decayed keys E), Us[Wp][128] (record corrections), Gs[Wp][128]
-// (record gates, KDA only) and, at the boundary, Et[128][Wp + 4] (E transposed).
+// (record gates, KDA only) and, at the boundary, Zs[128][kZsStride] (the old codes
+// re-laid out for the MFMA tiles; the padded row stride spreads the LDS banks).
+constexpr int kZsStride = kD / 4 + 1;
 __host__ __device__ constexpr int window_lds_floats(int Wp, bool per_key, bool boundary) {
-    return (2 + (per_key ? 1 : 0)) * Wp * kD + (boundary ? kD * (Wp + 4) : 0);
+    return (2 + (per_key ? 1 : 0)) * Wp * kD + (boundary ? kD * kZsStride : 0);
+}
+
+// Round-half-to-even of |w| <= 2^22 to an integer with one fp32 add: the sum's
+// low mantissa bits are the integer. The code byte is the low byte of the sum's
+// bits after clamping those bits to the codes of -127 .. 127.
+__device__ __forceinline__ uint32_t code_byte(float w) {
+    constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23
+    const int bits = __float_as_int(w + kMagic);
+    const int lo = 0x4B400000 - 127, hi = 0x4B400000 + 127;
+    return static_cast<uint32_t>(min(max(bits, lo), hi)) & 0xffu;
 }
 
 template <bool kPerKey, bool kBoundary, typename T>
@@ -106,25 +118,22 @@ __global__ __launch_bounds__(kThreads) void q8_window_kernel(
     __shared__ f32x2 red[4][kD];          // per-wave column partials
     __shared__ float kq_part[2];
     __shared__ float zcoef[kBoundary ? kD : 1];
-    __shared__ float scale_s[kBoundary ? kD : 1];
 
     const int h = head_of_block(blockIdx.x, gridDim.x), tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
     const int c4 = lane & 31, ro = lane >> 5;
     const size_t vec_off = static_cast<size_t>(h) * kD;
     const size_t rec0 = static_cast<size_t>(h) * W * kD;
-    const int Wp = (W + 3) & ~3, EtS = Wp + 4;
+    const int Wp = (W + 3) & ~3;
     float* KE = dyn_lds;
     float* Us = KE + Wp * kD;
     float* Gs = Us + Wp * kD;
-    float* Et = Gs + (kPerKey ? Wp * kD : 0);
+    uint32_t* Zs = reinterpret_cast<uint32_t*>(Gs + (kPerKey ? Wp * kD : 0));
 
-    // ---- every load of the step is issued here: codes, records, inputs
+    // ---- every load of the step is issued here: records and inputs first, then the
+    // codes, so that the key-side preparation below only waits for the former while
+    // the codes are still in flight (loads complete in order)
     uint32_t* Zh = reinterpret_cast<uint32_t*>(Z + static_cast<size_t>(h) * kD * kD);
-    uint32_t zw[kRowsPerThread];
-#pragma unroll
-    for (int it = 0; it < kRowsPerThread; ++it)
-        zw[it] = __builtin_nontemporal_load(Zh + q8_row(it, wave, ro) * (kD / 4) + c4);
     Stager<T, kMaxW * kD> sk;
     Stager<float, kMaxW * kD> su;
     sk.load(Kbuf + rec0, pos * kD, tid);
@@ -140,6 +149,10 @@ __global__ __launch_bounds__(kThreads) void q8_window_kernel(
     const float ar = A[vec_off + r];
     const float vr = load_in(v, vec_off + r);
     const float bt = beta[h];
+    uint32_t zw[kRowsPerThread];
+#pragma unroll
+    for (int it = 0; it < kRowsPerThread; ++it)
+        zw[it] = __builtin_nontemporal_load(Zh + q8_row(it, wave, ro) * (kD / 4) + c4);
 
     sk.store(KE, tid);
     su.store(Us, tid);
@@ -153,9 +166,7 @@ __global__ __launch_bounds__(kThreads) void q8_window_kernel(
     if (first) {
         float G = 1.f;  // product of the gates of the records after j (and before l)
         for (int j = pos - 1; j >= 0; --j) {
-            const float e = KE[j * kD + r] * G * gr;  // Gamma_{j+1:l} k_j at row r
-            KE[j * kD + r] = e;                        // in place: row r belongs to this thread
-            if (kBoundary) Et[r * EtS + j] = e;
+            KE[j * kD + r] *= G * gr;  // Gamma_{j+1:l} k_j at row r; row r belongs to this thread
             G *= kPerKey ? Gs[j * kD + r] : gs_scalar[j];
         }
         const float c0 = ar / 127.f * G * gr;  // a_r/127 Gamma_{1:l} at row r
@@ -165,8 +176,8 @@ __global__ __launch_bounds__(kThreads) void q8_window_kernel(
         if (lane == 0) kq_part[wave] = kq;
         if (kBoundary) {
             zcoef[r] = c0;
-            Et[r * EtS + pos] = kr;
-            for (int j = pos + 1; j < Wp; ++j) Et[r * EtS + j] = 0.f;
+            KE[pos * kD + r] = kr;  // the current record: no decay after it
+            for (int j = pos + 1; j < Wp; ++j) KE[j * kD + r] = 0.f;
         }
     }
     __syncthreads();
@@ -235,23 +246,49 @@ __global__ __launch_bounds__(kThreads) void q8_window_kernel(
     }
     if (!kBoundary) return;
 
-    // ---- window boundary: S_W = Gamma_{1:W} S^_0 + sum_j Gamma_{j+1:W} k_j u_j^T, requantize
+    // ---- window boundary: S_W = Gamma_{1:W} S^_0 + sum_j Gamma_{j+1:W} k_j u_j^T, requantize.
+    // The record sum is a [128 x Wp] . [Wp x 128] contraction per head, done on the
+    // matrix cores as its transpose with v_mfma_f32_16x16x4f32 (A from lane l is
+    // A[l%16][l/16], B is B[l/16][l%16], result i of lane l is D[4(l/16)+i][l%16]).
+    // Tiles: wave w owns key rows 16*rt + (l%16), rt = 2w, 2w+1, and in value-column
+    // tile ct the 4 columns 16*ct + 4(l/16) .. +3 -- one 32-bit word of codes.
+#pragma unroll
+    for (int it = 0; it < kRowsPerThread; ++it) Zs[q8_row(it, wave, ro) * kZsStride + c4] = zw[it];
     __syncthreads();
-    f32x4 s[kRowsPerThread];
+    const int lr = lane & 15, lq = lane >> 4;
+    for (int a = 0; a < 2; ++a) {  // one 16-row tile band at a time: 8 accumulators live
+        const int row = 16 * (2 * wave + a) + lr;
+        const float zc = zcoef[row];
+        f32x4 acc[8];
 #pragma unroll
-    for (int it = 0; it < kRowsPerThread; ++it) s[it] = unpack_i8x4(zw[it]) * zcoef[q8_row(it, wave, ro)];
-    for (int j0 = 0; j0 < Wp; j0 += 4) {
-        const f32x4 u0 = *reinterpret_cast<const f32x4*>(Us + (j0 + 0) * kD + 4 * c4);
-        const f32x4 u1 = *reinterpret_cast<const f32x4*>(Us + (j0 + 1) * kD + 4 * c4);
-        const f32x4 u2 = *reinterpret_cast<const f32x4*>(Us + (j0 + 2) * kD + 4 * c4);
-        const f32x4 u3 = *reinterpret_cast<const f32x4*>(Us + (j0 + 3) * kD + 4 * c4);
+        for (int ct = 0; ct < 8; ++ct) acc[ct] = unpack_i8x4(Zs[row * kZsStride + 4 * ct + lq]) * zc;
+        for (int k0 = 0; k0 < Wp; k0 += 4) {
+            const float bv = KE[(k0 + lq) * kD + row];
 #pragma unroll
-        for (int it = 0; it < kRowsPerThread; ++it) {
-            const f32x4 e = *reinterpret_cast<const f32x4*>(Et + q8_row(it, wave, ro) * EtS + j0);
-            s[it] += u0 * e.x + u1 * e.y + u2 * e.z + u3 * e.w;
+            for (int ct = 0; ct < 8; ++ct) {
+                const float av = Us[(k0 + lq) * kD + 16 * ct + lr];
+                acc[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc[ct], 0, 0, 0);
+            }
+        }
+        // per-row absmax: 32 values in this lane, then the 4 lanes l, l^16, l^32, l^48
+        float m = 0.f;
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct)
+            m = fmaxf(m, fmaxf(fmaxf(fabsf(acc[ct].x), fabsf(acc[ct].y)),
+                               fmaxf(fabsf(acc[ct].z), fabsf(acc[ct].w))));
+        m = max_xor16(m);
+        float m0, m1;
+        swap32(m, m0, m1);
+        m = fmaxf(m0, m1);
+        const float sc = m > 0.f ? __fdiv_rn(127.f, m) : 0.f;
+        if (lq == 0) A[vec_off + row] = m;
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct) {
+            const uint32_t w = code_byte(acc[ct].x * sc) | (code_byte(acc[ct].y * sc) << 8) |
+                               (code_byte(acc[ct].z * sc) << 16) | (code_byte(acc[ct].w * sc) << 24);
+            __builtin_nontemporal_store(w, Zh + row * (kD / 4) + 4 * ct + lq);
         }
     }
-    requantize_tile(s, Zh, A + vec_off, scale_s, wave, lane);
 }
 
 hipError_t launch_q8_quantize(int heads, const float* S, int8_t* Z, float* A, hipStream_t stream) {
