@@ -85,13 +85,217 @@ __global__ __launch_bounds__(kThreads) void q8_quantize_kernel(const float* __re
                     A + static_cast<size_t>(h) * kD, scale_s, wave, lane);
 }
 
-// Dynamic LDS of a window step, in 32-bit words: KE[Wp][128] (record keys, turned in
-// place into the decayed keys E), Us[Wp][128] (record corrections), Gs[Wp][128]
-// (record gates, KDA only) and, at the boundary, Zs[128][kZsStride] (the old codes
-// re-laid out for the MFMA tiles; the padded row stride spreads the LDS banks).
+// Eight consecutive elements of a key-side vector in their storage type, kept packed
+// in registers until used (bf16: one 16-byte load; fp32: two).
+template <typename T>
+struct Raw8;
+template <>
+struct Raw8<bf16_t> {
+    uint32_t w[4];
+    __device__ __forceinline__ void load(const bf16_t* p) {
+        const uint4 x = *reinterpret_cast<const uint4*>(p);
+        w[0] = x.x; w[1] = x.y; w[2] = x.z; w[3] = x.w;
+    }
+    __device__ __forceinline__ float operator[](int e) const {
+        return (e & 1) ? __uint_as_float(w[e >> 1] & 0xffff0000u) : __uint_as_float(w[e >> 1] << 16);
+    }
+};
+template <>
+struct Raw8<float> {
+    f32x4 lo, hi;
+    __device__ __forceinline__ void load(const float* p) {
+        lo = *reinterpret_cast<const f32x4*>(p);
+        hi = *reinterpret_cast<const f32x4*>(p + 4);
+    }
+    __device__ __forceinline__ float operator[](int e) const { return e < 4 ? lo[e] : hi[e - 4]; }
+};
+
+__device__ __forceinline__ float lane_value(float x, int i) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), i));
+}
+
+// ---- one step inside the window (pos < W - 1): read S_{l-1} in both directions and
+// append this step's record. The records never pass through LDS: the 16 lanes of a
+// DPP row hold 8 keys each of one record and reduce its coefficients
+// (Gamma_{j+1:l} k_j) . k and (Gamma_{j+1:l} k_j) . q in place, and the record
+// corrections u_j are loaded straight into the registers of the row-owners that
+// add c_j u_j to their column partials. Scalar gates (GDN) are multiplied from
+// register copies (lane i of every wave holds g_i), so the step needs two
+// workgroup barriers; per-key gates (KDA) are staged in LDS first (one more).
+template <bool kPerKey, int kWmax, typename T>
+__global__ __launch_bounds__(kThreads) void q8_step_kernel(
+    int W, int pos, const int8_t* __restrict__ Z, const float* __restrict__ A, T* __restrict__ Kbuf,
+    float* __restrict__ Ubuf, float* __restrict__ Gbuf, const T* __restrict__ q,
+    const T* __restrict__ k, const T* __restrict__ v, const float* __restrict__ gate,
+    const float* __restrict__ beta, float* __restrict__ y) {
+    extern __shared__ float gs_lds[];     // KDA: the records' gates [pos][128]
+    __shared__ f32x2 rowv[kD];            // a_r/127 Gamma_{1:l} (k_r, q_r)
+    __shared__ f32x2 coef[kMaxW];         // per record (E_j . k, E_j . q)
+    __shared__ f32x2 red[4][kD];          // per-wave column partials
+    __shared__ float kq_part[2];
+    constexpr int kKSlots = kWmax / 16;   // records per 16-lane group
+    constexpr int kUSlots = kWmax / 8;    // records per row-owner
+
+    const int h = head_of_block(blockIdx.x, gridDim.x), tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
+    const int c4 = lane & 31, ro = lane >> 5, owner = 2 * wave + ro;
+    const int grp = tid >> 4, ch = tid & 15;  // record-key layout: group = record, 8 keys per lane
+    const size_t vec_off = static_cast<size_t>(h) * kD;
+    const size_t rec0 = static_cast<size_t>(h) * W * kD;
+    const int r = tid & (kD - 1);
+    const bool first = tid < kD;
+
+    // ---- every load is issued first: record keys and corrections, gates, inputs, codes
+    Raw8<T> kc[kKSlots];
+#pragma unroll
+    for (int s = 0; s < kKSlots; ++s) {
+        const int j = grp + 16 * s;
+        if (16 * s < pos) kc[s].load(Kbuf + rec0 + static_cast<size_t>(j < pos ? j : 0) * kD + 8 * ch);
+    }
+    f32x4 ur[kUSlots];
+#pragma unroll
+    for (int m = 0; m < kUSlots; ++m) {
+        const int j = owner + 8 * m;
+        ur[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (8 * m < pos)
+            ur[m] = *reinterpret_cast<const f32x4*>(Ubuf + rec0 + static_cast<size_t>(j < pos ? j : 0) * kD + 4 * c4);
+    }
+    float g_lane = 1.f;  // GDN: lane i holds the gate of record i
+    Stager<float, kPerKey ? kWmax * kD : 8> sg;
+    if constexpr (kPerKey) sg.load(Gbuf + rec0, pos * kD, tid);
+    else if (lane < pos) g_lane = Gbuf[static_cast<size_t>(h) * W + lane];
+    Raw8<T> kch, qch;
+    kch.load(k + vec_off + 8 * ch);
+    qch.load(q + vec_off + 8 * ch);
+    f32x4 gch_lo = {1.f, 1.f, 1.f, 1.f}, gch_hi = {1.f, 1.f, 1.f, 1.f};  // KDA: current gates of the 8 keys
+    if constexpr (kPerKey) {
+        gch_lo = *reinterpret_cast<const f32x4*>(gate + vec_off + 8 * ch);
+        gch_hi = *reinterpret_cast<const f32x4*>(gate + vec_off + 8 * ch + 4);
+    }
+    const float kr = load_in(k, vec_off + r), qr = load_in(q, vec_off + r);
+    const float gr = kPerKey ? gate[vec_off + r] : gate[h];
+    const float ar = A[vec_off + r];
+    const float vr = load_in(v, vec_off + r);
+    const float bt = beta[h];
+    const uint32_t* Zh = reinterpret_cast<const uint32_t*>(Z + static_cast<size_t>(h) * kD * kD);
+    uint32_t zw[kRowsPerThread];
+#pragma unroll
+    for (int it = 0; it < kRowsPerThread; ++it)
+        zw[it] = __builtin_nontemporal_load(Zh + q8_row(it, wave, ro) * (kD / 4) + c4);
+
+    if constexpr (kPerKey) {
+        sg.store(gs_lds, tid);
+        __syncthreads();
+    }
+
+    // ---- decays: G_s = prod of the record gates after record grp + 16 s (from the
+    // newest down), Gall = prod of all record gates; the current gate comes on top
+    float Gs[kKSlots][kPerKey ? 8 : 1];
+    float Gall = 1.f;
+    if constexpr (!kPerKey) {
+#pragma unroll
+        for (int s = 0; s < kKSlots; ++s) Gs[s][0] = 1.f;
+        for (int i = pos - 1; i >= 0; --i) {
+            const float gi = lane_value(g_lane, i);
+#pragma unroll
+            for (int s = 0; s < kKSlots; ++s) Gs[s][0] = i > grp + 16 * s ? Gs[s][0] * gi : Gs[s][0];
+            Gall *= gi;
+        }
+    } else {
+#pragma unroll
+        for (int s = 0; s < kKSlots; ++s) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) Gs[s][e] = 1.f;
+            if (16 * s >= pos) continue;
+            for (int i = pos - 1; i > grp + 16 * s; --i) {
+                const f32x4 lo = *reinterpret_cast<const f32x4*>(gs_lds + i * kD + 8 * ch);
+                const f32x4 hi = *reinterpret_cast<const f32x4*>(gs_lds + i * kD + 8 * ch + 4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    Gs[s][e] *= lo[e];
+                    Gs[s][e + 4] *= hi[e];
+                }
+            }
+        }
+        for (int i = pos - 1; i >= 0; --i) Gall *= gs_lds[i * kD + r];
+    }
+
+    // ---- record coefficients, reduced over the 16 lanes of each group
+#pragma unroll
+    for (int s = 0; s < kKSlots; ++s) {
+        if (16 * s >= pos) continue;
+        const int j = grp + 16 * s;
+        float ck = 0.f, cq = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float ge = kPerKey ? (e < 4 ? gch_lo[e] : gch_hi[e - 4]) : gr;
+            const float ej = kc[s][e] * (Gs[s][kPerKey ? e : 0] * ge);  // Gamma_{j+1:l} k_j
+            ck += ej * kch[e];
+            cq += ej * qch[e];
+        }
+        ck = row16_sum(ck);
+        cq = row16_sum(cq);
+        if (ch == 0 && j < pos) coef[j] = f32x2{ck, cq};
+    }
+    if (first) {
+        const float c0 = ar * (1.f / 127.f) * Gall * gr;  // a_r/127 Gamma_{1:l} at row r
+        rowv[r] = f32x2{c0 * kr, c0 * qr};
+        const float kq = wave_sum(kr * qr);
+        if (lane == 0) kq_part[wave] = kq;
+    }
+    __syncthreads();
+
+    // ---- one sweep of the int8 tile for both read vectors, plus the records
+    f32x4 p1 = {0.f, 0.f, 0.f, 0.f}, p2 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int it = 0; it < kRowsPerThread; ++it) {
+        const f32x2 rv = rowv[q8_row(it, wave, ro)];
+        const f32x4 zf = unpack_i8x4(zw[it]);
+        p1 += zf * rv.x;
+        p2 += zf * rv.y;
+    }
+#pragma unroll
+    for (int m = 0; m < kUSlots; ++m) {
+        if (8 * m >= pos) continue;
+        const int j = owner + 8 * m;
+        const f32x2 c = j < pos ? coef[j] : f32x2{0.f, 0.f};
+        p1 += ur[m] * c.x;
+        p2 += ur[m] * c.y;
+    }
+    p1 = f32x4{add_xor32(p1.x), add_xor32(p1.y), add_xor32(p1.z), add_xor32(p1.w)};
+    p2 = f32x4{add_xor32(p2.x), add_xor32(p2.y), add_xor32(p2.z), add_xor32(p2.w)};
+    if (ro == 0) {
+        red[wave][4 * c4 + 0] = f32x2{p1.x, p2.x};
+        red[wave][4 * c4 + 1] = f32x2{p1.y, p2.y};
+        red[wave][4 * c4 + 2] = f32x2{p1.z, p2.z};
+        red[wave][4 * c4 + 3] = f32x2{p1.w, p2.w};
+    }
+    __syncthreads();
+
+    // ---- correction, output, and the record of this step (thread -> value column c == r)
+    if (first) {
+        const int c = tid;
+        const f32x2 acc = red[0][c] + red[1][c] + red[2][c] + red[3][c];
+        const float kq = kq_part[0] + kq_part[1];
+        const float u = bt * (vr - acc.x);
+        y[vec_off + c] = acc.y + u * kq;
+        const size_t rec = rec0 + static_cast<size_t>(pos) * kD;
+        Ubuf[rec + c] = u;
+        store_in(Kbuf, rec + c, kr);
+        if (kPerKey) Gbuf[rec + c] = gr;
+        else if (c == 0) Gbuf[static_cast<size_t>(h) * W + pos] = gr;
+    }
+}
+
+// Dynamic LDS of the boundary step, in 32-bit words, for windows of up to kWmax records:
+// KE[kWmax][128] (record keys, turned in place into the decayed keys E; zero after the
+// last record), Us[kWmax][128] (record corrections; zero after the last), Gs[kWmax][128]
+// (record gates, KDA only) and Zs[128][kZsStride] (the codes re-laid out for the
+// MFMA tiles, then the new codes on their way out; the padded row stride spreads the
+// LDS banks).
 constexpr int kZsStride = kD / 4 + 1;
-__host__ __device__ constexpr int window_lds_floats(int Wp, bool per_key, bool boundary) {
-    return (2 + (per_key ? 1 : 0)) * Wp * kD + (boundary ? kD * kZsStride : 0);
+__host__ __device__ constexpr int boundary_lds_floats(int wmax, bool per_key) {
+    return (2 + (per_key ? 1 : 0)) * wmax * kD + kD * kZsStride;
 }
 
 // Round-half-to-even of |w| <= 2^22 to an integer with one fp32 add: the sum's
@@ -104,31 +308,32 @@ __device__ __forceinline__ uint32_t code_byte(float w) {
     return static_cast<uint32_t>(min(max(bits, lo), hi)) & 0xffu;
 }
 
-template <bool kPerKey, bool kBoundary, typename T>
-__global__ __launch_bounds__(kThreads) void q8_window_kernel(
-    int W, int pos, int8_t* __restrict__ Z, float* __restrict__ A, T* __restrict__ Kbuf,
-    float* __restrict__ Ubuf, float* __restrict__ Gbuf, const T* __restrict__ q,
+// ---- the last step of the window (pos = W - 1): the step itself, then S_W of eq. 4
+// formed from the codes and all W records, and requantized in place.
+template <bool kPerKey, int kWmax, typename T>
+__global__ __launch_bounds__(kThreads) void q8_boundary_kernel(
+    int W, int pos, int8_t* __restrict__ Z, float* __restrict__ A, const T* __restrict__ Kbuf,
+    const float* __restrict__ Ubuf, const float* __restrict__ Gbuf, const T* __restrict__ q,
     const T* __restrict__ k, const T* __restrict__ v, const float* __restrict__ gate,
     const float* __restrict__ beta, float* __restrict__ y) {
     extern __shared__ float dyn_lds[];
-    __shared__ float gs_scalar[kMaxW];    // GDN: the records' gates
+    __shared__ float gsuf[kMaxW + 1];     // GDN: gate products after each record; [kMaxW]: all
     __shared__ f32x2 rowv[kD];            // a_r/127 Gamma_{1:l} (k_r, q_r)
     __shared__ f32x2 kq_row[kD];          // (k_r, q_r)
     __shared__ f32x2 coef[kMaxW];         // per record (E_j . k, E_j . q)
     __shared__ f32x2 red[4][kD];          // per-wave column partials
     __shared__ float kq_part[2];
-    __shared__ float zcoef[kBoundary ? kD : 1];
+    __shared__ float zcoef[kD];
 
     const int h = head_of_block(blockIdx.x, gridDim.x), tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
     const int c4 = lane & 31, ro = lane >> 5;
     const size_t vec_off = static_cast<size_t>(h) * kD;
     const size_t rec0 = static_cast<size_t>(h) * W * kD;
-    const int Wp = (W + 3) & ~3;
     float* KE = dyn_lds;
-    float* Us = KE + Wp * kD;
-    float* Gs = Us + Wp * kD;
-    uint32_t* Zs = reinterpret_cast<uint32_t*>(Gs + (kPerKey ? Wp * kD : 0));
+    float* Us = KE + kWmax * kD;
+    float* Gs = Us + kWmax * kD;
+    uint32_t* Zs = reinterpret_cast<uint32_t*>(Gs + (kPerKey ? kWmax * kD : 0));
 
     // ---- every load of the step is issued here: records and inputs first, then the
     // codes, so that the key-side preparation below only waits for the former while
@@ -154,31 +359,49 @@ __global__ __launch_bounds__(kThreads) void q8_window_kernel(
     for (int it = 0; it < kRowsPerThread; ++it)
         zw[it] = __builtin_nontemporal_load(Zh + q8_row(it, wave, ro) * (kD / 4) + c4);
 
+    if constexpr (!kPerKey) {
+        // wave 0: lane j gets the product of the gates of records j+1 .. pos-1 (newest first)
+        if (wave == 0) {
+            float G = 1.f, Gall = 1.f;
+            for (int i = pos - 1; i >= 0; --i) {
+                const float gi = lane_value(g_rec, i);
+                G = i > lane ? G * gi : G;
+                Gall *= gi;
+            }
+            if (lane < pos) gsuf[lane] = G;
+            if (lane == 0) gsuf[kMaxW] = Gall;
+        }
+    }
     sk.store(KE, tid);
     su.store(Us, tid);
     if constexpr (kPerKey) sg.store(Gs, tid);
-    else if (tid < pos) gs_scalar[tid] = g_rec;
-    if (kBoundary)  // rows W..Wp-1 of Us meet zero coefficients at the boundary; keep them finite
-        for (int i = W * kD + tid; i < Wp * kD; i += kThreads) Us[i] = 0.f;
+    for (int i = W * kD + tid; i < kWmax * kD; i += kThreads) Us[i] = 0.f;  // rows after the last record
     __syncthreads();
 
-    // ---- key-side preparation: thread r < 128 walks the records of key row r backwards
-    if (first) {
-        float G = 1.f;  // product of the gates of the records after j (and before l)
-        for (int j = pos - 1; j >= 0; --j) {
-            KE[j * kD + r] *= G * gr;  // Gamma_{j+1:l} k_j at row r; row r belongs to this thread
-            G *= kPerKey ? Gs[j * kD + r] : gs_scalar[j];
+    // ---- decayed keys E_j = Gamma_{j+1:l} k_j in place; the current key is row pos
+    float G;  // product of all record gates at row r
+    if constexpr (!kPerKey) {
+        for (int i = tid; i < pos * kD; i += kThreads) KE[i] *= gsuf[i >> 7] * gr;
+        G = gsuf[kMaxW];
+    } else {
+        // thread r < 128 walks the records of key row r backwards
+        G = 1.f;
+        if (first) {
+            for (int j = pos - 1; j >= 0; --j) {
+                KE[j * kD + r] *= G * gr;
+                G *= Gs[j * kD + r];
+            }
         }
-        const float c0 = ar / 127.f * G * gr;  // a_r/127 Gamma_{1:l} at row r
+    }
+    if (first) {
+        const float c0 = ar * (1.f / 127.f) * G * gr;  // a_r/127 Gamma_{1:l} at row r
         rowv[r] = f32x2{c0 * kr, c0 * qr};
         kq_row[r] = f32x2{kr, qr};
         const float kq = wave_sum(kr * qr);
         if (lane == 0) kq_part[wave] = kq;
-        if (kBoundary) {
-            zcoef[r] = c0;
-            KE[pos * kD + r] = kr;  // the current record: no decay after it
-            for (int j = pos + 1; j < Wp; ++j) KE[j * kD + r] = 0.f;
-        }
+        zcoef[r] = c0;
+        KE[pos * kD + r] = kr;  // the current record: no decay after it
+        for (int j = pos + 1; j < kWmax; ++j) KE[j * kD + r] = 0.f;
     }
     __syncthreads();
 
@@ -225,50 +448,62 @@ __global__ __launch_bounds__(kThreads) void q8_window_kernel(
         red[wave][4 * c4 + 2] = f32x2{p1.z, p2.z};
         red[wave][4 * c4 + 3] = f32x2{p1.w, p2.w};
     }
+#pragma unroll
+    for (int it = 0; it < kRowsPerThread; ++it) Zs[q8_row(it, wave, ro) * kZsStride + c4] = zw[it];
     __syncthreads();
 
-    // ---- correction, output, and the record of this step (thread -> value column c == r)
+    // ---- correction and output; u of this step becomes row pos of Us
     if (first) {
         const int c = tid;
         const f32x2 acc = red[0][c] + red[1][c] + red[2][c] + red[3][c];
         const float kq = kq_part[0] + kq_part[1];
         const float u = bt * (vr - acc.x);
         y[vec_off + c] = acc.y + u * kq;
-        if (kBoundary) {
-            Us[pos * kD + c] = u;
-        } else {
-            const size_t rec = rec0 + static_cast<size_t>(pos) * kD;
-            Ubuf[rec + c] = u;
-            store_in(Kbuf, rec + c, kr);
-            if (kPerKey) Gbuf[rec + c] = gr;
-            else if (c == 0) Gbuf[static_cast<size_t>(h) * W + pos] = gr;
-        }
+        Us[pos * kD + c] = u;
     }
-    if (!kBoundary) return;
+    __syncthreads();
 
-    // ---- window boundary: S_W = Gamma_{1:W} S^_0 + sum_j Gamma_{j+1:W} k_j u_j^T, requantize.
-    // The record sum is a [128 x Wp] . [Wp x 128] contraction per head, done on the
+    // ---- S_W = Gamma_{1:W} S^_0 + sum_j Gamma_{j+1:W} k_j u_j^T, requantized.
+    // The record sum is a [128 x kWmax] . [kWmax x 128] contraction per head, done on the
     // matrix cores as its transpose with v_mfma_f32_16x16x4f32 (A from lane l is
     // A[l%16][l/16], B is B[l/16][l%16], result i of lane l is D[4(l/16)+i][l%16]).
-    // Tiles: wave w owns key rows 16*rt + (l%16), rt = 2w, 2w+1, and in value-column
-    // tile ct the 4 columns 16*ct + 4(l/16) .. +3 -- one 32-bit word of codes.
-#pragma unroll
-    for (int it = 0; it < kRowsPerThread; ++it) Zs[q8_row(it, wave, ro) * kZsStride + c4] = zw[it];
-    __syncthreads();
+    // Wave w owns key rows 32w .. 32w+31 as two bands of 16 (B = decayed keys, one
+    // row per lane l%16); value-column tile ct (A = corrections) takes the columns
+    // 8m + ct, m = 0..15, so that lane l reads the corrections of columns
+    // 8(l%16) .. +7 with two 128-bit LDS loads and ends up holding the 32
+    // consecutive columns 32(l/16) .. +31 of its row: result i of tile ct is column
+    // 32(l/16) + 8i + ct. All operands of a band are loaded before its MFMAs.
+    constexpr int kSteps = kWmax / 4;
     const int lr = lane & 15, lq = lane >> 4;
-    for (int a = 0; a < 2; ++a) {  // one 16-row tile band at a time: 8 accumulators live
+    f32x4 ua[kSteps][2];
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s) {
+        const float* src = Us + (4 * s + lq) * kD + 8 * lr;
+        ua[s][0] = *reinterpret_cast<const f32x4*>(src);
+        ua[s][1] = *reinterpret_cast<const f32x4*>(src + 4);
+    }
+    for (int a = 0; a < 2; ++a) {  // one 16-row band at a time: 8 accumulators live
         const int row = 16 * (2 * wave + a) + lr;
+        float eb[kSteps];
+#pragma unroll
+        for (int s = 0; s < kSteps; ++s)
+            eb[s] = KE[(4 * s + lq) * kD + row];
+        // old codes of columns 32 lq .. +31: dword d holds columns 32 lq + 4d .. +3
+        uint32_t zo[8];
+#pragma unroll
+        for (int d = 0; d < 8; ++d) zo[d] = Zs[row * kZsStride + 8 * lq + d];
         const float zc = zcoef[row];
         f32x4 acc[8];
 #pragma unroll
-        for (int ct = 0; ct < 8; ++ct) acc[ct] = unpack_i8x4(Zs[row * kZsStride + 4 * ct + lq]) * zc;
-        for (int k0 = 0; k0 < Wp; k0 += 4) {
-            const float bv = KE[(k0 + lq) * kD + row];
+        for (int ct = 0; ct < 8; ++ct)
 #pragma unroll
-            for (int ct = 0; ct < 8; ++ct) {
-                const float av = Us[(k0 + lq) * kD + 16 * ct + lr];
-                acc[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc[ct], 0, 0, 0);
-            }
+            for (int i = 0; i < 4; ++i)
+                acc[ct][i] = static_cast<float>(static_cast<int8_t>((zo[2 * i + ct / 4] >> (8 * (ct % 4))) & 0xffu)) * zc;
+#pragma unroll
+        for (int s = 0; s < kSteps; ++s) {
+#pragma unroll
+            for (int ct = 0; ct < 8; ++ct)
+                acc[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(ua[s][ct / 4][ct % 4], eb[s], acc[ct], 0, 0, 0);
         }
         // per-row absmax: 32 values in this lane, then the 4 lanes l, l^16, l^32, l^48
         float m = 0.f;
@@ -282,12 +517,236 @@ __global__ __launch_bounds__(kThreads) void q8_window_kernel(
         m = fmaxf(m0, m1);
         const float sc = m > 0.f ? __fdiv_rn(127.f, m) : 0.f;
         if (lq == 0) A[vec_off + row] = m;
+        // the new codes replace the old ones in Zs (this lane read exactly these words)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh)
+                Zs[row * kZsStride + 8 * lq + 2 * i + hh] =
+                    code_byte(acc[4 * hh + 0][i] * sc) | (code_byte(acc[4 * hh + 1][i] * sc) << 8) |
+                    (code_byte(acc[4 * hh + 2][i] * sc) << 16) | (code_byte(acc[4 * hh + 3][i] * sc) << 24);
+    }
+    // the wave's 32 rows (32w .. 32w+31, 4 KiB of codes) leave as whole 128-byte rows
+    wave_lds_sync();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int row = 32 * wave + 8 * i + (lane >> 3), d0 = 4 * (lane & 7);
+        const uint32_t* src = Zs + row * kZsStride + d0;
+        const u32x4 w4 = {src[0], src[1], src[2], src[3]};
+        __builtin_nontemporal_store(w4, reinterpret_cast<u32x4*>(Zh + row * (kD / 4) + d0));
+    }
+}
+
+// Three bf16 parts of an fp32 value: hi = bf16(x), mid = bf16(x - hi), lo = bf16(x - hi - mid).
+// Both differences are exact in fp32, so hi + mid + lo equals x to about 2^-27 |x|.
+__device__ __forceinline__ void split3_bf16(float x, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
+    const __bf16 h = static_cast<__bf16>(x);
+    const float r1 = x - static_cast<float>(h);
+    const __bf16 m = static_cast<__bf16>(r1);
+    const float r2 = r1 - static_cast<float>(m);
+    const __bf16 l = static_cast<__bf16>(r2);
+    hi = __builtin_bit_cast(uint16_t, h);
+    mid = __builtin_bit_cast(uint16_t, m);
+    lo = __builtin_bit_cast(uint16_t, l);
+}
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// ---- the last step of the window for scalar gates (GDN), bf16 keys and W <= 16.
+// The decay of record j is a scalar, so it moves onto the correction:
+// S_W = Gamma_{1:W} S^_0 + sum_j k_j (Gamma_{j+1:W} u_j)^T. The keys are exact in
+// bf16; each scaled correction is split into three bf16 parts, and the contraction
+// runs as two v_mfma_f32_16x16x32_bf16 per 16x16 tile (hi and mid parts against the
+// keys, then the lo part): the products are exact and accumulate in fp32, so the
+// result matches an fp32 contraction up to rounding order, at a quarter of the
+// matrix-core time of v_mfma_f32_16x16x4f32. Operand layout (checked on gfx950):
+// lane l supplies A[l%16][8(l/16) + e] and B[8(l/16) + e][l%16], e = 0..7.
+// Records are staged transposed, as 16-byte words of 8 consecutive records:
+// Kt[b][row] (keys of records 8b .. 8b+7 at a key row) and Ut[part][b][column].
+__global__ __launch_bounds__(kThreads) void q8_boundary_bf16_kernel(
+    int W, int pos, int8_t* __restrict__ Z, float* __restrict__ A, const bf16_t* __restrict__ Kbuf,
+    const float* __restrict__ Ubuf, const float* __restrict__ Gbuf, const bf16_t* __restrict__ q,
+    const bf16_t* __restrict__ k, const bf16_t* __restrict__ v, const float* __restrict__ gate,
+    const float* __restrict__ beta, float* __restrict__ y) {
+    constexpr int kRec = 16;              // record slots
+    __shared__ f32x2 rowv[kD];            // a_r/127 Gamma_{1:l} (k_r, q_r)
+    __shared__ f32x2 coef[kRec];          // per record (E_j . k, E_j . q)
+    __shared__ f32x2 red[4][kD];          // per-wave column partials of the code sweep
+    __shared__ f32x2 recp[kD];            // record terms of records 8 .. 15 per column
+    __shared__ float kq_part[2];
+    __shared__ float zcoef[kD];
+    __shared__ float gam[kRec];           // Gamma_{j+1:W}; 1 for the current record
+    __shared__ u32x4 Kt[2][kD];
+    __shared__ u32x4 Ut[3][2][kD];
+    __shared__ uint32_t Zs[kD * kZsStride];
+
+    const int h = head_of_block(blockIdx.x, gridDim.x), tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
+    const int c4 = lane & 31, ro = lane >> 5;
+    const int grp = tid >> 4, ch = tid & 15;         // coefficient layout: record grp, keys 8ch .. +7
+    const int cc = tid & (kD - 1), half = tid >> 7;  // column layout: column / key row cc, records 8 half .. +7
+    const size_t vec_off = static_cast<size_t>(h) * kD;
+    const size_t rec0 = static_cast<size_t>(h) * W * kD;
+    const bool first = tid < kD;
+
+    // ---- every load is issued first: records (two layouts), gates, inputs, then codes
+    Raw8<bf16_t> kc;
+    if (0 < pos) kc.load(Kbuf + rec0 + static_cast<size_t>(grp < pos ? grp : 0) * kD + 8 * ch);
+    float ucol[8];
+    uint32_t kcol[4];  // keys of records 8 half + e at key row cc, two bf16 per word
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const int j = 8 * half + e;
+        const size_t at = rec0 + static_cast<size_t>(j < pos ? j : 0) * kD + cc;
+        ucol[e] = j < pos ? Ubuf[at] : 0.f;
+        const uint32_t kb = j < pos ? static_cast<uint32_t>(Kbuf[at]) : 0u;
+        kcol[e >> 1] = (e & 1) ? (kcol[e >> 1] | (kb << 16)) : kb;
+    }
+    const float g_lane = lane < pos ? Gbuf[static_cast<size_t>(h) * W + lane] : 1.f;
+    Raw8<bf16_t> kch, qch;
+    kch.load(k + vec_off + 8 * ch);
+    qch.load(q + vec_off + 8 * ch);
+    const float kr = load_in(k, vec_off + cc), qr = load_in(q, vec_off + cc);
+    const float gr = gate[h];
+    const float ar = A[vec_off + cc];
+    const float vr = load_in(v, vec_off + cc);
+    const float bt = beta[h];
+    uint32_t* Zh = reinterpret_cast<uint32_t*>(Z + static_cast<size_t>(h) * kD * kD);
+    uint32_t zw[kRowsPerThread];
+#pragma unroll
+    for (int it = 0; it < kRowsPerThread; ++it)
+        zw[it] = __builtin_nontemporal_load(Zh + q8_row(it, wave, ro) * (kD / 4) + c4);
+
+    // ---- gate products (newest first): for record grp, for record = lane, and all
+    float Gg = 1.f, Gl = 1.f, Gall = 1.f;
+    for (int i = pos - 1; i >= 0; --i) {
+        const float gi = lane_value(g_lane, i);
+        Gg = i > grp ? Gg * gi : Gg;
+        Gl = i > lane ? Gl * gi : Gl;
+        Gall *= gi;
+    }
+    if (wave == 0 && lane < kRec) gam[lane] = lane < pos ? Gl * gr : 1.f;
+    if (0 < pos) {
+        float ck = 0.f, cq = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float ej = kc[e] * (Gg * gr);  // Gamma_{j+1:l} k_j
+            ck += ej * kch[e];
+            cq += ej * qch[e];
+        }
+        ck = row16_sum(ck);
+        cq = row16_sum(cq);
+        if (ch == 0 && grp < pos) coef[grp] = f32x2{ck, cq};
+    }
+    if (first) {
+        const float c0 = ar * (1.f / 127.f) * Gall * gr;  // a_r/127 Gamma_{1:l} at row r
+        rowv[cc] = f32x2{c0 * kr, c0 * qr};
+        zcoef[cc] = c0;
+        const float kq = wave_sum(kr * qr);
+        if (lane == 0) kq_part[wave] = kq;
+    }
+    Kt[half][cc] = u32x4{kcol[0], kcol[1], kcol[2], kcol[3]};
+    __syncthreads();
+
+    // ---- code sweep for both read vectors; record terms per column; scaled records staged
+    f32x4 p1 = {0.f, 0.f, 0.f, 0.f}, p2 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int it = 0; it < kRowsPerThread; ++it) {
+        const f32x2 rv = rowv[q8_row(it, wave, ro)];
+        const f32x4 zf = unpack_i8x4(zw[it]);
+        p1 += zf * rv.x;
+        p2 += zf * rv.y;
+    }
+    f32x2 rp = {0.f, 0.f};
+    u32x4 part[3];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const int j = 8 * half + e;
+        const f32x2 c = j < pos ? coef[j] : f32x2{0.f, 0.f};
+        rp += c * ucol[e];
+        uint32_t hi, mid, lo;
+        split3_bf16(gam[j] * ucol[e], hi, mid, lo);
+        const int sh = 16 * (e & 1);
+        part[0][e >> 1] = (e & 1) ? (part[0][e >> 1] | (hi << sh)) : hi;
+        part[1][e >> 1] = (e & 1) ? (part[1][e >> 1] | (mid << sh)) : mid;
+        part[2][e >> 1] = (e & 1) ? (part[2][e >> 1] | (lo << sh)) : lo;
+    }
+#pragma unroll
+    for (int pp = 0; pp < 3; ++pp) Ut[pp][half][cc] = part[pp];
+    p1 = f32x4{add_xor32(p1.x), add_xor32(p1.y), add_xor32(p1.z), add_xor32(p1.w)};
+    p2 = f32x4{add_xor32(p2.x), add_xor32(p2.y), add_xor32(p2.z), add_xor32(p2.w)};
+    if (ro == 0) {
+        red[wave][4 * c4 + 0] = f32x2{p1.x, p2.x};
+        red[wave][4 * c4 + 1] = f32x2{p1.y, p2.y};
+        red[wave][4 * c4 + 2] = f32x2{p1.z, p2.z};
+        red[wave][4 * c4 + 3] = f32x2{p1.w, p2.w};
+    }
+    if (half == 1) recp[cc] = rp;
+#pragma unroll
+    for (int it = 0; it < kRowsPerThread; ++it) Zs[q8_row(it, wave, ro) * kZsStride + c4] = zw[it];
+    __syncthreads();
+
+    // ---- correction and output; the current record (no decay after it) joins the operands
+    if (first) {
+        const int c = cc;
+        const f32x2 acc = red[0][c] + red[1][c] + red[2][c] + red[3][c] + rp + recp[c];
+        const float kq = kq_part[0] + kq_part[1];
+        const float u = bt * (vr - acc.x);
+        y[vec_off + c] = acc.y + u * kq;
+        uint32_t uh, um, ul;
+        split3_bf16(u, uh, um, ul);
+        reinterpret_cast<uint16_t*>(&Ut[0][pos >> 3][c])[pos & 7] = static_cast<uint16_t>(uh);
+        reinterpret_cast<uint16_t*>(&Ut[1][pos >> 3][c])[pos & 7] = static_cast<uint16_t>(um);
+        reinterpret_cast<uint16_t*>(&Ut[2][pos >> 3][c])[pos & 7] = static_cast<uint16_t>(ul);
+        reinterpret_cast<uint16_t*>(&Kt[pos >> 3][c])[pos & 7] = static_cast<uint16_t>(__float_as_uint(kr) >> 16);
+    }
+    __syncthreads();
+
+    // ---- S_W on the matrix cores. Wave w owns key rows 32w .. 32w+31 as two bands of
+    // 16 (B = keys, key row 16 band + l%16); tile ct covers value columns 16ct .. +15
+    // (A = scaled corrections, column 16ct + l%16); result i of lane l is column
+    // 16ct + 4(l/16) + i: one 32-bit word of codes.
+    const int lr = lane & 15, lq = lane >> 4, blk = lq & 1;
+    for (int a = 0; a < 2; ++a) {
+        const int row = 16 * (2 * wave + a) + lr;
+        const bf16x8 bv = __builtin_bit_cast(bf16x8, Kt[blk][row]);
+        const float zc = zcoef[row];
+        f32x4 acc[8];
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct) acc[ct] = unpack_i8x4(Zs[row * kZsStride + 4 * ct + lq]) * zc;
 #pragma unroll
         for (int ct = 0; ct < 8; ++ct) {
-            const uint32_t w = code_byte(acc[ct].x * sc) | (code_byte(acc[ct].y * sc) << 8) |
-                               (code_byte(acc[ct].z * sc) << 16) | (code_byte(acc[ct].w * sc) << 24);
-            __builtin_nontemporal_store(w, Zh + row * (kD / 4) + 4 * ct + lq);
+            const int col = 16 * ct + lr;
+            const bf16x8 a1 = __builtin_bit_cast(bf16x8, Ut[lq < 2 ? 0 : 1][blk][col]);
+            const u32x4 lo = Ut[2][blk][col];
+            const bf16x8 a2 = __builtin_bit_cast(bf16x8, lq < 2 ? lo : u32x4{0u, 0u, 0u, 0u});
+            acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, bv, acc[ct], 0, 0, 0);
+            acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a2, bv, acc[ct], 0, 0, 0);
         }
+        float m = 0.f;
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct)
+            m = fmaxf(m, fmaxf(fmaxf(fabsf(acc[ct].x), fabsf(acc[ct].y)),
+                               fmaxf(fabsf(acc[ct].z), fabsf(acc[ct].w))));
+        m = max_xor16(m);
+        float m0, m1;
+        swap32(m, m0, m1);
+        m = fmaxf(m0, m1);
+        const float sc = m > 0.f ? __fdiv_rn(127.f, m) : 0.f;
+        if (lq == 0) A[vec_off + row] = m;
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct)
+            Zs[row * kZsStride + 4 * ct + lq] = code_byte(acc[ct].x * sc) | (code_byte(acc[ct].y * sc) << 8) |
+                                                (code_byte(acc[ct].z * sc) << 16) |
+                                                (code_byte(acc[ct].w * sc) << 24);
+    }
+    wave_lds_sync();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int row = 32 * wave + 8 * i + (lane >> 3), d0 = 4 * (lane & 7);
+        const uint32_t* src = Zs + row * kZsStride + d0;
+        const u32x4 w4 = {src[0], src[1], src[2], src[3]};
+        __builtin_nontemporal_store(w4, reinterpret_cast<u32x4*>(Zh + row * (kD / 4) + d0));
     }
 }
 
@@ -296,17 +755,26 @@ hipError_t launch_q8_quantize(int heads, const float* S, int8_t* Z, float* A, hi
     return hipGetLastError();
 }
 
-template <bool kPerKey, bool kBoundary, typename T>
-static hipError_t launch_window_kernel(const StepArgs& a, const WindowArgs& w, hipStream_t stream) {
-    const int Wp = (w.W + 3) & ~3;
-    const size_t lds = sizeof(float) * window_lds_floats(Wp, kPerKey, kBoundary);
+template <bool kPerKey, int kWmax, typename T>
+static hipError_t launch_step_kernel(const StepArgs& a, const WindowArgs& w, hipStream_t stream) {
+    const size_t lds = kPerKey ? sizeof(float) * w.pos * kD : 0;
+    hipLaunchKernelGGL((q8_step_kernel<kPerKey, kWmax, T>), dim3(a.heads), dim3(kThreads), lds, stream,
+                       w.W, w.pos, w.Z, w.A, static_cast<T*>(w.Kbuf), w.Ubuf, w.Gbuf,
+                       static_cast<const T*>(a.q), static_cast<const T*>(a.k),
+                       static_cast<const T*>(a.v), a.gate, a.beta, a.y);
+    return hipGetLastError();
+}
+
+template <bool kPerKey, int kWmax, typename T>
+static hipError_t launch_boundary_kernel(const StepArgs& a, const WindowArgs& w, hipStream_t stream) {
+    const size_t lds = sizeof(float) * boundary_lds_floats(kWmax, kPerKey);
     static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(q8_window_kernel<kPerKey, kBoundary, T>),
+        reinterpret_cast<const void*>(q8_boundary_kernel<kPerKey, kWmax, T>),
         hipFuncAttributeMaxDynamicSharedMemorySize,
-        static_cast<int>(sizeof(float) * window_lds_floats(kMaxW, kPerKey, kBoundary)));
+        static_cast<int>(sizeof(float) * boundary_lds_floats(kWmax, kPerKey)));
     if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL((q8_window_kernel<kPerKey, kBoundary, T>), dim3(a.heads), dim3(kThreads), lds,
-                       stream, w.W, w.pos, w.Z, w.A, static_cast<T*>(w.Kbuf), w.Ubuf, w.Gbuf,
+    hipLaunchKernelGGL((q8_boundary_kernel<kPerKey, kWmax, T>), dim3(a.heads), dim3(kThreads), lds, stream,
+                       w.W, w.pos, w.Z, w.A, static_cast<const T*>(w.Kbuf), w.Ubuf, w.Gbuf,
                        static_cast<const T*>(a.q), static_cast<const T*>(a.k),
                        static_cast<const T*>(a.v), a.gate, a.beta, a.y);
     return hipGetLastError();
@@ -314,8 +782,20 @@ static hipError_t launch_window_kernel(const StepArgs& a, const WindowArgs& w, h
 
 template <bool kPerKey, typename T>
 static hipError_t launch_window_t(const StepArgs& a, const WindowArgs& w, hipStream_t stream) {
-    return w.pos == w.W - 1 ? launch_window_kernel<kPerKey, true, T>(a, w, stream)
-                            : launch_window_kernel<kPerKey, false, T>(a, w, stream);
+    if constexpr (!kPerKey && sizeof(T) == 2) {
+        if (w.pos == w.W - 1 && w.W <= 16) {
+            hipLaunchKernelGGL(q8_boundary_bf16_kernel, dim3(a.heads), dim3(kThreads), 0, stream, w.W, w.pos,
+                               w.Z, w.A, static_cast<const bf16_t*>(w.Kbuf), w.Ubuf, w.Gbuf,
+                               static_cast<const bf16_t*>(a.q), static_cast<const bf16_t*>(a.k),
+                               static_cast<const bf16_t*>(a.v), a.gate, a.beta, a.y);
+            return hipGetLastError();
+        }
+    }
+    if (w.pos == w.W - 1)
+        return w.W <= 16 ? launch_boundary_kernel<kPerKey, 16, T>(a, w, stream)
+                         : launch_boundary_kernel<kPerKey, kMaxW, T>(a, w, stream);
+    return w.W <= 16 ? launch_step_kernel<kPerKey, 16, T>(a, w, stream)
+                     : launch_step_kernel<kPerKey, kMaxW, T>(a, w, stream);
 }
 
 hipError_t launch_q8_window(const StepArgs& a, const WindowArgs& w, bool per_key, bool bf16,

@@ -22,6 +22,7 @@ constexpr int kRowsPerThread = 16; // fp32-state layout: 16 rows x 4 columns per
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 using bf16_t = uint16_t;  // raw bfloat16 bits
 
