@@ -216,19 +216,18 @@ def run_gpu(w: wl.Workload, steps: int, warmup: int):
     stream = torch.cuda.current_stream()
     phases = None
     if w.path != "dense":
-        # one untimed pass over whole cycles with an event pair around every launch:
+        # one untimed pass over whole cycles with an event between consecutive launches:
         # average launch time per window position / per live log length
         cyc = w.W if w.path == "q8_window" else w.M
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(4 * cyc)]
-        for a, b in evs:
-            a.record(stream)
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(4 * cyc + 1)]
+        evs[0].record(stream)
+        for e in evs[1:]:
             step()
-            b.record(stream)
+            e.record(stream)
         torch.cuda.synchronize()
         per = [0.0] * cyc
-        for i, (a, b) in enumerate(evs):
-            per[i % cyc] += a.elapsed_time(b) * 1e3 / 4
+        for i in range(4 * cyc):
+            per[i % cyc] += evs[i].elapsed_time(evs[i + 1]) * 1e3 / 4
         key = "pos" if w.path == "q8_window" else "L"
         phases = {f"{key}{i}_us": round(t, 2) for i, t in enumerate(per)}
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
