@@ -81,6 +81,21 @@ def log_step_bytes_per_head(w: wl.Workload, L: int) -> int:
     return rd + wr
 
 
+def slot_lengths(w: wl.Workload) -> np.ndarray:
+    """Initial per-slot live lengths of the mixed-phase log benchmark: every request-head
+    at a seeded random point of its cycle (requests admitted at unrelated times), so
+    about 1/M of the heads merge at each step, spread over the whole grid."""
+    rng = np.random.Generator(np.random.SFC64(np.random.SeedSequence([w.seed, 77])))
+    return rng.integers(0, w.M, size=w.heads).astype(np.int32)
+
+
+def slots_bytes_per_head(w: wl.Workload) -> float:
+    """Average algorithmic bytes per head-update of a mixed-phase step (the multiset of
+    live lengths is the same at every step)."""
+    counts = np.bincount(slot_lengths(w), minlength=w.M)
+    return float(sum(int(counts[L]) * log_step_bytes_per_head(w, L) for L in range(w.M))) / w.heads
+
+
 def cycle_bytes_per_head(w: wl.Workload) -> float:
     """Average algorithmic bytes per head-update over one window / merge cycle."""
     if w.path == "dense":
@@ -153,7 +168,7 @@ def copy_ceiling(torch, rsu, nbytes: int, reps: int = 10) -> float:
     return 2 * n * 4 / sec / 1e9
 
 
-def run_gpu(w: wl.Workload, steps: int, warmup: int):
+def run_gpu(w: wl.Workload, steps: int, warmup: int, slots: bool = False):
     import torch
     import recurrent_state_update_head_amd as rsu
     dev = "cuda"
@@ -198,17 +213,28 @@ def run_gpu(w: wl.Workload, steps: int, warmup: int):
         Kl = torch.zeros(B, H, cap, 128, device=dev, dtype=x["q"].dtype)
         Ul = torch.zeros(B, H, cap, 128, device=dev)
         Lm = torch.zeros((B, H, cap, 128) if kda else (B, H, cap), device=dev)
-        app = rsu.kda_log_append if kda else rsu.gdn_log_append
-        mrg = rsu.kda_log_merge if kda else rsu.gdn_log_merge
-        state["L"] = 0
+        if slots:
+            # every request-head at its own point of the cycle: 1/M of them merge per step
+            Ld = torch.from_numpy(slot_lengths(w)).to(dev).view(B, H)
+            fs = rsu.kda_log_step_slots if kda else rsu.gdn_log_step_slots
 
-        def step():
-            i = state["t"] % n_inputs
-            L = state["L"]
-            f = app if L < C else mrg
-            f(C, L, Sb, lbar, Kl, Ul, Lm, x["q"][i], x["k"][i], x["v"][i], x["gate"][i], x["beta"][i], y)
-            state["L"] = L + 1 if L < C else 0
-            state["t"] += 1
+            def step():
+                i = state["t"] % n_inputs
+                fs(C, Ld, Sb, lbar, Kl, Ul, Lm, x["q"][i], x["k"][i], x["v"][i], x["gate"][i],
+                   x["beta"][i], y)
+                state["t"] += 1
+        else:
+            app = rsu.kda_log_append if kda else rsu.gdn_log_append
+            mrg = rsu.kda_log_merge if kda else rsu.gdn_log_merge
+            state["L"] = 0
+
+            def step():
+                i = state["t"] % n_inputs
+                L = state["L"]
+                f = app if L < C else mrg
+                f(C, L, Sb, lbar, Kl, Ul, Lm, x["q"][i], x["k"][i], x["v"][i], x["gate"][i], x["beta"][i], y)
+                state["L"] = L + 1 if L < C else 0
+                state["t"] += 1
 
     for _ in range(warmup):
         step()
@@ -228,7 +254,7 @@ def run_gpu(w: wl.Workload, steps: int, warmup: int):
         per = [0.0] * cyc
         for i in range(4 * cyc):
             per[i % cyc] += evs[i].elapsed_time(evs[i + 1]) * 1e3 / 4
-        key = "pos" if w.path == "q8_window" else "L"
+        key = "pos" if w.path == "q8_window" else ("step" if slots else "L")
         phases = {f"{key}{i}_us": round(t, 2) for i, t in enumerate(per)}
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
@@ -266,6 +292,32 @@ def run_cpu_baseline(w: wl.Workload, budget_s: float = 10.0, max_steps: int = 40
                       f"(fp64 oracle, {t_total:.1f} s of compute)"}
 
 
+def override_workload(w: wl.Workload, args) -> wl.Workload:
+    """Apply the command-line overrides; the workload's name records them."""
+    ch = {}
+    if args.variant and args.variant != w.variant:
+        ch.update(variant=args.variant, gate_lo=0.8 if args.variant == "kda" else 0.9,
+                  gate_hi=1.0 if args.variant == "kda" else 0.999)
+    if args.B:
+        ch["B"] = args.B
+    if args.H:
+        ch["H"] = args.H
+    if args.M is not None:
+        if w.path != "log" or not 1 <= args.M <= 64:
+            raise SystemExit("--M applies to the log workload, 1 <= M <= 64")
+        ch["M"] = args.M
+    if args.slots and w.path != "log":
+        raise SystemExit("--slots applies to the log workload")
+    if not ch and not args.slots:
+        return w
+    w2 = wl.custom(w, **ch)
+    var = w2.variant
+    tail = {"dense": "", "q8_window": f"_w{w2.W}", "log": f"_m{w2.M}"}[w2.path]
+    path = {"dense": "dense", "q8_window": "q8_window", "log": "log"}[w2.path]
+    name = f"{var}_{path}_b{w2.B}_h{w2.H}{tail}" + ("_slots" if args.slots else "")
+    return wl.custom(w2, name=name)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -273,6 +325,13 @@ def main():
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", choices=sorted(WORKLOAD_BY_FLAG), default="gdn")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--variant", choices=["gdn", "kda"], default=None,
+                    help="override the gate kind of the workload (log and int8 paths)")
+    ap.add_argument("--B", type=int, default=None, help="override the batch size")
+    ap.add_argument("--H", type=int, default=None, help="override the heads per request")
+    ap.add_argument("--M", type=int, default=None, help="log path: merge interval (1..64)")
+    ap.add_argument("--slots", action="store_true",
+                    help="log path: per-slot live lengths, every head at its own cycle point")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -281,18 +340,19 @@ def main():
         sys.exit(2)
 
     w = wl.WORKLOADS[WORKLOAD_BY_FLAG[args.workload]]
+    w = override_workload(w, args)
     cycle = {"dense": 1, "q8_window": w.W, "log": w.M}[w.path]
     steps = args.steps if args.steps is not None else 256
     steps = max(cycle, (steps + cycle - 1) // cycle * cycle)   # whole windows / cycles
     warmup = args.warmup if args.warmup is not None else 2 * cycle
     warmup = (warmup + cycle - 1) // cycle * cycle
 
-    gpu_sec, wall, ceiling, phases = run_gpu(w, steps, warmup)
+    gpu_sec, wall, ceiling, phases = run_gpu(w, steps, warmup, args.slots)
     heads = w.heads
-    per_head = cycle_bytes_per_head(w)
+    per_head = slots_bytes_per_head(w) if args.slots else cycle_bytes_per_head(w)
     launch_sec = gpu_sec / steps
     achieved = per_head * heads / launch_sec / 1e9
-    traffic = counter_traffic(per_head * heads) if args.workload == "gdn" else None
+    traffic = counter_traffic(per_head * heads) if w is wl.WORKLOADS[2] else None
 
     out = {
         "metric": METRIC,
@@ -309,7 +369,8 @@ def main():
         "data": "synthetic (seeded; shapes and distributions of the workload)",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "dk": 128, "dv": 128,
                    "qkv": w.qkv, "state": "int8+f32 scales" if w.path == "q8_window" else "f32",
-                   "W": w.W or None, "M": w.M or None},
+                   "W": w.W or None, "M": w.M or None, "gates": w.variant,
+                   "log_phases": ("per-slot (mixed)" if args.slots else "batch-uniform") if w.path == "log" else None},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
                      "algorithmic_bytes_per_launch": per_head * heads},
@@ -319,7 +380,7 @@ def main():
     }
     if phases:
         out["phases"] = phases
-    if not args.no_cpu_baseline and w.path == "dense":
+    if not args.no_cpu_baseline and w is wl.WORKLOADS[WORKLOAD_BY_FLAG["gdn"]]:
         out["cpu_baseline"] = run_cpu_baseline(w)
     print(json.dumps(out), flush=True)
 

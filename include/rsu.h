@@ -137,7 +137,7 @@ int kda_q8_window(const rsu_dims *dims, int W, int pos, int8_t *Z, float *row_ab
  * *_log_merge (requires L == C >= 0): the same step, but instead of appending
  * it writes the represented state plus the current pair into Sbase (eq. 6)
  * and resets lbar to 0. The caller then sets L = 0.
- * C <= 16.
+ * 0 <= C <= 63 (M = C + 1 <= 64; DeltaLog sec. 4 sweeps M up to 64).
  * ---------------------------------------------------------------------- */
 int gdn_log_append(const rsu_dims *dims, int C, int L, const float *Sbase, float *lbar,
                    void *Klog, float *Ulog, float *Lam, const void *q, const void *k,
@@ -155,6 +155,30 @@ int kda_log_merge(const rsu_dims *dims, int C, int L, float *Sbase, float *lbar,
                   const void *Klog, const float *Ulog, const float *Lam, const void *q,
                   const void *k, const void *v, const float *d, const float *beta,
                   float *y, rsu_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Per-slot live lengths. DeltaLog sec. 4 keeps the live-log length as per-slot
+ * metadata; requests admitted at different times sit at different points of
+ * their append/merge cycle, and its serving prototype splits them into
+ * phase-uniform append and merge batches. These calls serve a mixed batch in
+ * one call instead, without the host knowing any L: two launches on `stream`, an
+ * append pass over the heads with L[h] < C, then a merge pass over the heads with
+ * L[h] == C that also advances every L[h]. L is a device array [B,H] of int32,
+ * read and advanced in place: a head with L[h] < C appends (as *_log_append) and
+ * gets L[h] + 1; a head with L[h] == C merges (as *_log_merge) and gets 0.
+ * Other arguments, layouts and ranges as for *_log_append; Sbase is written for
+ * the merging heads only. L[h] outside [0, C] is not detected: the kernel clamps
+ * it into [0, C] (so every access stays inside the caller's buffers), and the
+ * result for that head is then that of the clamped length.
+ * ---------------------------------------------------------------------- */
+int gdn_log_step_slots(const rsu_dims *dims, int C, int *L, float *Sbase, float *lbar,
+                       void *Klog, float *Ulog, float *Lam, const void *q, const void *k,
+                       const void *v, const float *alpha, const float *beta, float *y,
+                       rsu_stream_t stream);
+int kda_log_step_slots(const rsu_dims *dims, int C, int *L, float *Sbase, float *lbar,
+                       void *Klog, float *Ulog, float *Lam, const void *q, const void *k,
+                       const void *v, const float *d, const float *beta, float *y,
+                       rsu_stream_t stream);
 
 /* ------------------------------------------------------------------------
  * Measurement helper (not part of the recurrence): dst[i] = src[i] for

@@ -49,10 +49,11 @@ def _load():
         lib.oracle_q8_window_step.argtypes = [I64, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P,
                                               P, P, P]
         lib.oracle_log_step.argtypes = [I64, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P, P]
+        lib.oracle_log_step_slots.argtypes = [I64, I, I, I, I, P, P, P, P, P, P, P, P, P, P, P, P]
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = ctypes.c_int
         for f in (lib.oracle_dense_step, lib.oracle_q8_quantize, lib.oracle_q8_window_step,
-                  lib.oracle_log_step):
+                  lib.oracle_log_step, lib.oracle_log_step_slots):
             f.restype = None
         _lib = lib
     return _lib
@@ -173,6 +174,23 @@ class LogState:
                                 _ptr(self.lbar), _ptr(self.K), _ptr(self.U), _ptr(self.Lam),
                                 _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(beta), _ptr(y))
         self.L = self.L + 1 if self.L < self.C else 0
+        return y
+
+    def step_slots(self, Ls, q, k, v, gate, beta):
+        """One step with a live length per head (Ls: int array [nh], each in [0, C],
+        advanced in place): heads with Ls < C append, heads with Ls == C merge."""
+        nh, dk, dv = self.Sbar.shape
+        q, k, v, gate, beta = map(_f64, (q, k, v, gate, beta))
+        _check_step_inputs(nh, dk, dv, self.per_key, q, k, v, gate, beta)
+        if Ls.dtype != np.int32 or Ls.shape != (nh,) or not Ls.flags.c_contiguous:
+            raise ValueError("Ls must be a contiguous int32 array of one live length per head")
+        if (Ls < 0).any() or (Ls > self.C).any():
+            raise ValueError("live lengths must lie in [0, C]")
+        y = np.empty((nh, dv))
+        _load().oracle_log_step_slots(nh, dk, dv, int(self.per_key), self.C,
+                                      Ls.ctypes.data_as(ctypes.c_void_p), _ptr(self.Sbar),
+                                      _ptr(self.lbar), _ptr(self.K), _ptr(self.U), _ptr(self.Lam),
+                                      _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(beta), _ptr(y))
         return y
 
     def logical_state(self) -> np.ndarray:

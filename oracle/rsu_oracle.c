@@ -247,14 +247,13 @@ void oracle_q8_window_step(int64_t nh, int dk, int dv, int per_key, int W, int p
  * Log arrays: K[nh][C][dk], U[nh][C][dv], Lam[nh][C] or [nh][C][dk];
  * lbar[nh] or [nh][dk].
  */
-void oracle_log_step(int64_t nh, int dk, int dv, int per_key, int C, int L,
-                     double *Sbar, double *lbar, double *Klog, double *Ulog, double *Lam,
-                     const double *q, const double *k, const double *v,
-                     const double *gate, const double *beta, double *y)
+static void log_step_head(int64_t h, int dk, int dv, int per_key, int C, int L,
+                          double *Sbar, double *lbar, double *Klog, double *Ulog, double *Lam,
+                          const double *q, const double *k, const double *v,
+                          const double *gate, const double *beta, double *y)
 {
     const int gdim = per_key ? dk : 1;
-#pragma omp parallel for schedule(static)
-    for (int64_t h = 0; h < nh; ++h) {
+    {
         double *Sh = Sbar + (size_t)h * dk * dv;
         double *lb = lbar + (size_t)h * gdim;
         double *Kh = Klog + (size_t)h * C * dk;
@@ -324,5 +323,30 @@ void oracle_log_step(int64_t nh, int dk, int dv, int per_key, int C, int L,
         }
         free(St);
         free(b);
+    }
+}
+
+void oracle_log_step(int64_t nh, int dk, int dv, int per_key, int C, int L,
+                     double *Sbar, double *lbar, double *Klog, double *Ulog, double *Lam,
+                     const double *q, const double *k, const double *v,
+                     const double *gate, const double *beta, double *y)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t h = 0; h < nh; ++h)
+        log_step_head(h, dk, dv, per_key, C, L, Sbar, lbar, Klog, Ulog, Lam, q, k, v, gate, beta, y);
+}
+
+/* The same step with a live length per head (each request slot at its own point
+ * of its append/merge cycle): Ls[h] in [0, C] selects append or merge for head h,
+ * and is advanced here (L + 1 after an append, 0 after a merge). */
+void oracle_log_step_slots(int64_t nh, int dk, int dv, int per_key, int C, int *Ls,
+                           double *Sbar, double *lbar, double *Klog, double *Ulog, double *Lam,
+                           const double *q, const double *k, const double *v,
+                           const double *gate, const double *beta, double *y)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t h = 0; h < nh; ++h) {
+        log_step_head(h, dk, dv, per_key, C, Ls[h], Sbar, lbar, Klog, Ulog, Lam, q, k, v, gate, beta, y);
+        Ls[h] = Ls[h] < C ? Ls[h] + 1 : 0;
     }
 }

@@ -13,7 +13,7 @@ Shapes (B requests, H heads, d = 128):
   Z [B,H,d,d] int8, row_absmax [B,H,d] fp32
   Kbuf [B,H,W,d] (q dtype), Ubuf [B,H,W,d] fp32, Gbuf [B,H,W] or [B,H,W,d] fp32
   Klog [B,H,C,d] (q dtype), Ulog [B,H,C,d] fp32, Lam [B,H,C] or [B,H,C,d] fp32,
-  lbar [B,H] or [B,H,d] fp32
+  lbar [B,H] or [B,H,d] fp32, per-slot live lengths L [B,H] int32
 """
 from __future__ import annotations
 
@@ -55,6 +55,8 @@ _SIGS = {
     "kda_log_append": [_DP, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
     "gdn_log_merge": [_DP, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
     "kda_log_merge": [_DP, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
+    "gdn_log_step_slots": [_DP, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
+    "kda_log_step_slots": [_DP, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
     "rsu_copy_f32": [_P, _P, ctypes.c_int64, _P],
 }
 for _name, _args in _SIGS.items():
@@ -207,6 +209,34 @@ def gdn_log_merge(C, L, Sbase, lbar, Klog, Ulog, Lam, q, k, v, alpha, beta, y):
 
 def kda_log_merge(C, L, Sbase, lbar, Klog, Ulog, Lam, q, k, v, d, beta, y):
     return _log("kda_log_merge", True, C, L, Sbase, lbar, Klog, Ulog, Lam, q, k, v, d, beta, y)
+
+
+def _log_slots(name, per_key, C, L, Sbase, lbar, Klog, Ulog, Lam, q, k, v, gate, beta, y):
+    dims = _dims(q, k, v)
+    _need(L, "L", torch.int32, (dims.B, dims.H))
+    _need(Sbase, "Sbase", torch.float32, (dims.B, dims.H, D, D))
+    _need(lbar, "lbar", torch.float32, _gate_shape(dims.B, dims.H, per_key))
+    if C > 0:
+        _need(Klog, "Klog", q.dtype, (dims.B, dims.H, C, D))
+        _need(Ulog, "Ulog", torch.float32, (dims.B, dims.H, C, D))
+        _need(Lam, "Lam", torch.float32, (dims.B, dims.H, C, D) if per_key else (dims.B, dims.H, C))
+    _step_common(dims, gate, beta, y, per_key, "d" if per_key else "alpha")
+    _call(name, ctypes.byref(dims), int(C), _ptr(L), _ptr(Sbase), _ptr(lbar),
+          _ptr(Klog if C > 0 else None), _ptr(Ulog if C > 0 else None),
+          _ptr(Lam if C > 0 else None), _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(beta), _ptr(y),
+          _stream())
+    return y
+
+
+def gdn_log_step_slots(C, L, Sbase, lbar, Klog, Ulog, Lam, q, k, v, alpha, beta, y):
+    """Decode step with a live length per head (L: int32 [B,H] on the device): heads with
+    L < C append, heads with L == C merge; L is advanced in place."""
+    return _log_slots("gdn_log_step_slots", False, C, L, Sbase, lbar, Klog, Ulog, Lam, q, k, v, alpha,
+                      beta, y)
+
+
+def kda_log_step_slots(C, L, Sbase, lbar, Klog, Ulog, Lam, q, k, v, d, beta, y):
+    return _log_slots("kda_log_step_slots", True, C, L, Sbase, lbar, Klog, Ulog, Lam, q, k, v, d, beta, y)
 
 
 def copy_f32(src: torch.Tensor, dst: torch.Tensor):

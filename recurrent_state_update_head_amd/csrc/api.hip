@@ -109,15 +109,16 @@ int window_common(const char* fn, bool per_key, const rsu_dims* dims, int W, int
                     fn);
 }
 
-int log_common(const char* fn, bool per_key, bool merge, const rsu_dims* dims, int C, int L,
-               float* Sbase, float* lbar, void* Klog, float* Ulog, float* Lam, const void* q,
-               const void* k, const void* v, const float* gate, const float* beta, float* y,
-               rsu_stream_t stream) {
+// mode: 0 append, 1 merge, 2 per-slot live lengths (L ignored, Lslot used)
+int log_common(const char* fn, bool per_key, int mode, const rsu_dims* dims, int C, int L,
+               int* Lslot, float* Sbase, float* lbar, void* Klog, float* Ulog, float* Lam,
+               const void* q, const void* k, const void* v, const float* gate, const float* beta,
+               float* y, rsu_stream_t stream) {
     int heads = 0;
     if (int rc = check_dims(dims, &heads, fn)) return rc;
     if (C < 0 || C > rsu::kMaxC) return fail(RSU_E_RANGE, "%s: C=%d outside [0, %d]", fn, C, rsu::kMaxC);
-    if (merge && L != C) return fail(RSU_E_RANGE, "%s: merge needs L == C, got L=%d C=%d", fn, L, C);
-    if (!merge && (L < 0 || L >= C))
+    if (mode == 1 && L != C) return fail(RSU_E_RANGE, "%s: merge needs L == C, got L=%d C=%d", fn, L, C);
+    if (mode == 0 && (L < 0 || L >= C))
         return fail(RSU_E_RANGE, "%s: append needs 0 <= L < C, got L=%d C=%d", fn, L, C);
     if (heads == 0) return RSU_OK;
     if (int rc = check_ptrs({{Sbase, "Sbase"}, {lbar, "lbar"}, {q, "q"}, {k, "k"}, {v, "v"},
@@ -125,14 +126,17 @@ int log_common(const char* fn, bool per_key, bool merge, const rsu_dims* dims, i
         return rc;
     if (C > 0)
         if (int rc = check_ptrs({{Klog, "Klog"}, {Ulog, "Ulog"}, {Lam, "Lam"}}, fn)) return rc;
+    if (mode == 2)
+        if (int rc = check_ptrs({{Lslot, "L"}}, fn)) return rc;
     rsu::LogArgs l;
     l.C = C;
-    l.L = L;
+    l.L = mode == 2 ? 0 : L;
+    l.Lslot = Lslot;
     l.lbar = lbar;
     l.Klog = Klog;
     l.Ulog = Ulog;
     l.Lam = Lam;
-    return launched(rsu::launch_log(step_args(heads, Sbase, q, k, v, gate, beta, y), l, merge, per_key,
+    return launched(rsu::launch_log(step_args(heads, Sbase, q, k, v, gate, beta, y), l, mode, per_key,
                                     dims->qkv_dtype == RSU_BF16, stream),
                     fn);
 }
@@ -181,21 +185,21 @@ int kda_q8_window(const rsu_dims* dims, int W, int pos, int8_t* Z, float* row_ab
 int gdn_log_append(const rsu_dims* dims, int C, int L, const float* Sbase, float* lbar, void* Klog,
                    float* Ulog, float* Lam, const void* q, const void* k, const void* v,
                    const float* alpha, const float* beta, float* y, rsu_stream_t stream) {
-    return log_common("gdn_log_append", false, false, dims, C, L, const_cast<float*>(Sbase), lbar,
+    return log_common("gdn_log_append", false, 0, dims, C, L, nullptr, const_cast<float*>(Sbase), lbar,
                       Klog, Ulog, Lam, q, k, v, alpha, beta, y, stream);
 }
 
 int kda_log_append(const rsu_dims* dims, int C, int L, const float* Sbase, float* lbar, void* Klog,
                    float* Ulog, float* Lam, const void* q, const void* k, const void* v,
                    const float* d, const float* beta, float* y, rsu_stream_t stream) {
-    return log_common("kda_log_append", true, false, dims, C, L, const_cast<float*>(Sbase), lbar,
+    return log_common("kda_log_append", true, 0, dims, C, L, nullptr, const_cast<float*>(Sbase), lbar,
                       Klog, Ulog, Lam, q, k, v, d, beta, y, stream);
 }
 
 int gdn_log_merge(const rsu_dims* dims, int C, int L, float* Sbase, float* lbar, const void* Klog,
                   const float* Ulog, const float* Lam, const void* q, const void* k, const void* v,
                   const float* alpha, const float* beta, float* y, rsu_stream_t stream) {
-    return log_common("gdn_log_merge", false, true, dims, C, L, Sbase, lbar, const_cast<void*>(Klog),
+    return log_common("gdn_log_merge", false, 1, dims, C, L, nullptr, Sbase, lbar, const_cast<void*>(Klog),
                       const_cast<float*>(Ulog), const_cast<float*>(Lam), q, k, v, alpha, beta, y,
                       stream);
 }
@@ -203,8 +207,22 @@ int gdn_log_merge(const rsu_dims* dims, int C, int L, float* Sbase, float* lbar,
 int kda_log_merge(const rsu_dims* dims, int C, int L, float* Sbase, float* lbar, const void* Klog,
                   const float* Ulog, const float* Lam, const void* q, const void* k, const void* v,
                   const float* d, const float* beta, float* y, rsu_stream_t stream) {
-    return log_common("kda_log_merge", true, true, dims, C, L, Sbase, lbar, const_cast<void*>(Klog),
+    return log_common("kda_log_merge", true, 1, dims, C, L, nullptr, Sbase, lbar, const_cast<void*>(Klog),
                       const_cast<float*>(Ulog), const_cast<float*>(Lam), q, k, v, d, beta, y, stream);
+}
+
+int gdn_log_step_slots(const rsu_dims* dims, int C, int* L, float* Sbase, float* lbar, void* Klog,
+                       float* Ulog, float* Lam, const void* q, const void* k, const void* v,
+                       const float* alpha, const float* beta, float* y, rsu_stream_t stream) {
+    return log_common("gdn_log_step_slots", false, 2, dims, C, 0, L, Sbase, lbar, Klog, Ulog, Lam, q, k,
+                      v, alpha, beta, y, stream);
+}
+
+int kda_log_step_slots(const rsu_dims* dims, int C, int* L, float* Sbase, float* lbar, void* Klog,
+                       float* Ulog, float* Lam, const void* q, const void* k, const void* v,
+                       const float* d, const float* beta, float* y, rsu_stream_t stream) {
+    return log_common("kda_log_step_slots", true, 2, dims, C, 0, L, Sbase, lbar, Klog, Ulog, Lam, q, k,
+                      v, d, beta, y, stream);
 }
 
 int rsu_copy_f32(const float* src, float* dst, int64_t n, rsu_stream_t stream) {

@@ -15,27 +15,48 @@
 // The base is swept once per step for both read vectors (same fp32 layout as
 // the dense step); the key-side replay coefficients K_m . (...) are computed
 // once per head in the preparation phase and shared by all value columns.
-// Append steps only read the 64 KiB base; merge steps also write it.
+// Append steps only read the 64 KiB base; merge steps also write it. With
+// per-slot live lengths (sec. 4 keeps the live length per request slot, so
+// requests admitted at different times are at different points of their cycle),
+// one call serves a mixed batch: an append pass, then a merge pass.
 #include "kernels.hpp"
 #include "rsu_device.hpp"
 
 namespace rsu {
 
-template <bool kPerKey, bool kMerge, typename T>
+// Log entries are staged through registers into LDS in chunks of kChunk entries; the
+// first chunk is issued before the base tile, so short logs cost one round trip.
+constexpr int kChunk = 16;
+
+// Dynamic LDS of a step, in 32-bit words, for n staged entries (n = L for the
+// batch-uniform calls, n = C for the per-slot call): Ek[n][128] (K_m, turned in
+// place into exp(lbar' - Lam_m) K_m), Us[n][128] (U_m), Ls[n][128] (KDA) or Ls[n]
+// rounded up to 4 (GDN), and for steps that may merge kd[128][Cp] (the transpose of
+// Ek, Cp = C rounded up to 4).
+__host__ __device__ constexpr int log_lds_floats(int n, int Cp, bool per_key, bool may_merge) {
+    return 2 * n * kD + (per_key ? n * kD : ((n + 3) & ~3)) + (may_merge ? kD * Cp : 0);
+}
+
+enum LogMode { kAppendMode = 0, kMergeMode = 1, kSlotAppend = 2, kSlotMerge = 3 };
+
+// kMode: append (batch-uniform L < C), merge (L == C), or one of the two passes of a
+// per-slot step, where every head reads its own live length from Lslot[h] (clamped to
+// [0, C]). The append pass serves the heads with L < C and leaves the others alone;
+// the merge pass, launched after it, serves the heads with L == C and advances every
+// Lslot[h]. Two passes keep the appends at the append kernel's register budget (the
+// merge path holds the whole base tile through its update).
+template <bool kPerKey, int kMode, typename T>
 __global__ __launch_bounds__(kThreads) void log_step_kernel(
-    int C, int L, float* __restrict__ Sbase, float* __restrict__ lbar, T* __restrict__ Klog,
-    float* __restrict__ Ulog, float* __restrict__ Lam, const T* __restrict__ q,
-    const T* __restrict__ k, const T* __restrict__ v, const float* __restrict__ gate,
-    const float* __restrict__ beta, float* __restrict__ y) {
-    constexpr int kCp = kMaxC;                 // row stride of the merge coefficients
+    int C, int L_uniform, int* __restrict__ Lslot, float* __restrict__ Sbase,
+    float* __restrict__ lbar, T* __restrict__ Klog, float* __restrict__ Ulog,
+    float* __restrict__ Lam, const T* __restrict__ q, const T* __restrict__ k,
+    const T* __restrict__ v, const float* __restrict__ gate, const float* __restrict__ beta,
+    float* __restrict__ y) {
+    extern __shared__ float dyn_lds[];
     __shared__ f32x4 row_vec[kD];              // (E k, E q, k, E), E = exp(lbar') per key row
     __shared__ f32x2 kq_row[kD];               // (k_r, q_r)
-    __shared__ float Ek[kMaxC * kD];           // K_m, turned in place into exp(lbar' - Lam_m) K_m
-    __shared__ float Us[kMaxC * kD];           // U_m
-    __shared__ float Ls[kPerKey ? kMaxC * kD : kMaxC];  // Lam_m
     __shared__ f32x2 coef[kMaxC];              // per entry (Ek_m . k, Ek_m . q)
     __shared__ float kq_part[2];
-    __shared__ float kd[kMerge ? kD * kCp : 1];  // merge: the transpose kd[r][m] of Ek
 
     const int h = head_of_block(blockIdx.x, gridDim.x), tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
@@ -44,15 +65,43 @@ __global__ __launch_bounds__(kThreads) void log_step_kernel(
     const size_t vec_off = static_cast<size_t>(h) * kD;
     const size_t ent0 = static_cast<size_t>(h) * C * kD;
 
-    // ---- every load of the step is issued here: log entries, inputs, the base tile
-    Stager<T, kMaxC * kD> sk;
-    Stager<float, kMaxC * kD> su;
-    Stager<float, kPerKey ? kMaxC * kD : 8> sl;
-    sk.load(Klog + ent0, L * kD, tid);
-    su.load(Ulog + ent0, L * kD, tid);
+    constexpr bool kSlots = kMode == kSlotAppend || kMode == kSlotMerge;
+    constexpr bool merge = kMode == kMergeMode || kMode == kSlotMerge;
+    int L = L_uniform;
+    if constexpr (kSlots) {
+        L = min(max(Lslot[h], 0), C);
+        if (kMode == kSlotAppend && L == C) return;  // merged by the second pass
+        if (kMode == kSlotMerge && L < C) {          // appended by the first pass
+            if (tid == 0) Lslot[h] = L + 1;
+            return;
+        }
+    }
+    const int n_lds = kSlots ? C : L;
+    const int Cp = (C + 3) & ~3;
+    float* Ek = dyn_lds;
+    float* Us = Ek + n_lds * kD;
+    float* Ls = Us + n_lds * kD;
+    float* kd = Ls + (kPerKey ? n_lds * kD : ((n_lds + 3) & ~3));
+
+    // ---- loads: the first chunk of log entries, inputs, the base tile, then the rest
+    Stager<T, kChunk * kD> sk;
+    Stager<float, kChunk * kD> su;
+    Stager<float, kPerKey ? kChunk * kD : 8> sl;
+    auto issue = [&](int m0) {
+        const int n = min(kChunk, L - m0) * kD;
+        sk.load(Klog + ent0 + static_cast<size_t>(m0) * kD, n, tid);
+        su.load(Ulog + ent0 + static_cast<size_t>(m0) * kD, n, tid);
+        if constexpr (kPerKey) sl.load(Lam + ent0 + static_cast<size_t>(m0) * kD, n, tid);
+    };
+    auto land = [&](int m0) {
+        sk.store(Ek + m0 * kD, tid);
+        su.store(Us + m0 * kD, tid);
+        if constexpr (kPerKey) sl.store(Ls + m0 * kD, tid);
+    };
+    issue(0);
     float lam_s = 0.f;
-    if constexpr (kPerKey) sl.load(Lam + ent0, L * kD, tid);
-    else if (tid < L) lam_s = Lam[static_cast<size_t>(h) * C + tid];
+    if constexpr (!kPerKey)
+        if (tid < L) lam_s = Lam[static_cast<size_t>(h) * C + tid];
     const f32x4 vv = load4_in(v, vec_off + col);
     const float bt = beta[h];
     const int r = tid & (kD - 1);
@@ -60,17 +109,20 @@ __global__ __launch_bounds__(kThreads) void log_step_kernel(
     const float kr = load_in(k, vec_off + r), qr = load_in(q, vec_off + r);
     const float gr = kPerKey ? gate[vec_off + r] : gate[h];
     const float lb_old = kPerKey ? lbar[vec_off + r] : lbar[h];
-    // the base tile last: loads complete in order, so the preparation below waits only
-    // for the log entries and inputs while the tile is still in flight
+    // loads complete in order: the preparation below waits for the first chunk and the
+    // inputs while the base tile is still in flight
     float* Sh = Sbase + static_cast<size_t>(h) * kD * kD;
     f32x4 s[kRowsPerThread];
 #pragma unroll
     for (int it = 0; it < kRowsPerThread; ++it) s[it] = stream_load(Sh + (it * 8 + ro) * kD + col);
 
-    sk.store(Ek, tid);
-    su.store(Us, tid);
-    if constexpr (kPerKey) sl.store(Ls, tid);
-    else if (tid < L) Ls[tid] = lam_s;
+    land(0);
+    for (int m0 = kChunk; m0 < L; m0 += kChunk) {
+        issue(m0);
+        land(m0);
+    }
+    if constexpr (!kPerKey)
+        if (tid < L) Ls[tid] = lam_s;
     __syncthreads();
 
     // ---- key-side preparation: thread r < 128 owns key row r
@@ -80,10 +132,10 @@ __global__ __launch_bounds__(kThreads) void log_step_kernel(
             const float lam = kPerKey ? Ls[m * kD + r] : Ls[m];
             const float e = expf(lb_new - lam) * Ek[m * kD + r];
             Ek[m * kD + r] = e;  // in place: row r belongs to this thread
-            if (kMerge) kd[r * kCp + m] = e;
+            if (merge) kd[r * Cp + m] = e;
         }
-        if (kMerge)
-            for (int m = L; m < ((C + 3) & ~3); ++m) kd[r * kCp + m] = 0.f;
+        if (merge)
+            for (int m = L; m < Cp; ++m) kd[r * Cp + m] = 0.f;
         const float E = expf(lb_new);
         row_vec[r] = f32x4{E * kr, E * qr, kr, E};
         kq_row[r] = f32x2{kr, qr};
@@ -94,24 +146,27 @@ __global__ __launch_bounds__(kThreads) void log_step_kernel(
 
     // ---- replay coefficients: the 16 lanes of a DPP row reduce one entry (8 rows each)
     {
-        const int chunk = tid & 15, m = tid >> 4;
-        f32x2 c = {0.f, 0.f};
-        if (m < L) {
-            const f32x4 e0 = *reinterpret_cast<const f32x4*>(Ek + m * kD + 8 * chunk);
-            const f32x4 e1 = *reinterpret_cast<const f32x4*>(Ek + m * kD + 8 * chunk + 4);
-            const f32x2* kqr = kq_row + 8 * chunk;
-            c = e0.x * kqr[0] + e0.y * kqr[1] + e0.z * kqr[2] + e0.w * kqr[3] +
-                e1.x * kqr[4] + e1.y * kqr[5] + e1.z * kqr[6] + e1.w * kqr[7];
+        const int chunk = tid & 15;
+        for (int m0 = 0; m0 < L; m0 += kThreads / 16) {
+            const int m = m0 + (tid >> 4);
+            f32x2 c = {0.f, 0.f};
+            if (m < L) {
+                const f32x4 e0 = *reinterpret_cast<const f32x4*>(Ek + m * kD + 8 * chunk);
+                const f32x4 e1 = *reinterpret_cast<const f32x4*>(Ek + m * kD + 8 * chunk + 4);
+                const f32x2* kqr = kq_row + 8 * chunk;
+                c = e0.x * kqr[0] + e0.y * kqr[1] + e0.z * kqr[2] + e0.w * kqr[3] +
+                    e1.x * kqr[4] + e1.y * kqr[5] + e1.z * kqr[6] + e1.w * kqr[7];
+            }
+            c.x = row16_sum(c.x);
+            c.y = row16_sum(c.y);
+            if (chunk == 0 && m < L) coef[m] = c;
         }
-        c.x = row16_sum(c.x);
-        c.y = row16_sum(c.y);
-        if (chunk == 0 && m < L) coef[m] = c;
     }
     __syncthreads();
 
-    // metadata: one writer per element (all reads of lbar / Lam are done)
+    // metadata: one writer per element (all reads of lbar / Lam / Lslot are done)
     if (first) {
-        if (kMerge) {
+        if (merge) {
             if (kPerKey) lbar[vec_off + r] = 0.f;
             else if (r == 0) lbar[h] = 0.f;
         } else {
@@ -125,6 +180,7 @@ __global__ __launch_bounds__(kThreads) void log_step_kernel(
                 lbar[h] = lb_new;
             }
         }
+        if (kMode == kSlotMerge && tid == 0) Lslot[h] = 0;
     }
 
     // ---- sweep of the base for both read vectors, plus the log entries
@@ -147,9 +203,9 @@ __global__ __launch_bounds__(kThreads) void log_step_kernel(
     const f32x4 b = bt * (vv - p1);
     if (ro == 0) {
         *reinterpret_cast<f32x4*>(y + vec_off + col) = p2 + b * kq;
-        if (!kMerge) *reinterpret_cast<f32x4*>(Ulog + ent0 + static_cast<size_t>(L) * kD + col) = b;
+        if (!merge) *reinterpret_cast<f32x4*>(Ulog + ent0 + static_cast<size_t>(L) * kD + col) = b;
     }
-    if (!kMerge) return;
+    if (!merge) return;
 
     // ---- merge (eq. 6): Sbar <- D(lbar') Sbar + sum_m D(lbar'-Lam_m) K_m U_m^T + k b^T
 #pragma unroll
@@ -165,7 +221,7 @@ __global__ __launch_bounds__(kThreads) void log_step_kernel(
                                 : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int it = 0; it < kRowsPerThread; ++it) {
-            const f32x4 e = *reinterpret_cast<const f32x4*>(kd + (it * 8 + ro) * kCp + m0);
+            const f32x4 e = *reinterpret_cast<const f32x4*>(kd + (it * 8 + ro) * Cp + m0);
             s[it] += u[0] * e.x + u[1] * e.y + u[2] * e.z + u[3] * e.w;
         }
     }
@@ -173,24 +229,37 @@ __global__ __launch_bounds__(kThreads) void log_step_kernel(
     for (int it = 0; it < kRowsPerThread; ++it) stream_store(Sh + (it * 8 + ro) * kD + col, s[it]);
 }
 
-template <bool kPerKey, bool kMerge, typename T>
+template <bool kPerKey, int kMode, typename T>
 static hipError_t launch_log_t(const StepArgs& a, const LogArgs& l, hipStream_t stream) {
-    hipLaunchKernelGGL((log_step_kernel<kPerKey, kMerge, T>), dim3(a.heads), dim3(kThreads), 0, stream,
-                       l.C, l.L, a.S, l.lbar, static_cast<T*>(l.Klog), l.Ulog, l.Lam,
+    constexpr bool may_merge = kMode == kMergeMode || kMode == kSlotMerge;
+    const int n = (kMode == kSlotAppend || kMode == kSlotMerge) ? l.C : l.L;
+    const size_t lds = sizeof(float) * log_lds_floats(n, (l.C + 3) & ~3, kPerKey, may_merge);
+    static const hipError_t attr = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(log_step_kernel<kPerKey, kMode, T>),
+        hipFuncAttributeMaxDynamicSharedMemorySize,
+        static_cast<int>(sizeof(float) * log_lds_floats(kMaxC, (kMaxC + 3) & ~3, kPerKey, may_merge)));
+    if (attr != hipSuccess) return attr;
+    hipLaunchKernelGGL((log_step_kernel<kPerKey, kMode, T>), dim3(a.heads), dim3(kThreads), lds, stream,
+                       l.C, l.L, l.Lslot, a.S, l.lbar, static_cast<T*>(l.Klog), l.Ulog, l.Lam,
                        static_cast<const T*>(a.q), static_cast<const T*>(a.k),
                        static_cast<const T*>(a.v), a.gate, a.beta, a.y);
     return hipGetLastError();
 }
 
 template <bool kPerKey, typename T>
-static hipError_t launch_log_m(const StepArgs& a, const LogArgs& l, bool merge, hipStream_t stream) {
-    return merge ? launch_log_t<kPerKey, true, T>(a, l, stream) : launch_log_t<kPerKey, false, T>(a, l, stream);
+static hipError_t launch_log_m(const StepArgs& a, const LogArgs& l, int mode, hipStream_t stream) {
+    if (mode == 2) {  // per-slot step: the append pass, then the merge pass on the same stream
+        if (hipError_t e = launch_log_t<kPerKey, kSlotAppend, T>(a, l, stream)) return e;
+        return launch_log_t<kPerKey, kSlotMerge, T>(a, l, stream);
+    }
+    return mode == kMergeMode ? launch_log_t<kPerKey, kMergeMode, T>(a, l, stream)
+                              : launch_log_t<kPerKey, kAppendMode, T>(a, l, stream);
 }
 
-hipError_t launch_log(const StepArgs& a, const LogArgs& l, bool merge, bool per_key, bool bf16,
+hipError_t launch_log(const StepArgs& a, const LogArgs& l, int mode, bool per_key, bool bf16,
                       hipStream_t stream) {
-    if (per_key) return bf16 ? launch_log_m<true, bf16_t>(a, l, merge, stream) : launch_log_m<true, float>(a, l, merge, stream);
-    return bf16 ? launch_log_m<false, bf16_t>(a, l, merge, stream) : launch_log_m<false, float>(a, l, merge, stream);
+    if (per_key) return bf16 ? launch_log_m<true, bf16_t>(a, l, mode, stream) : launch_log_m<true, float>(a, l, mode, stream);
+    return bf16 ? launch_log_m<false, bf16_t>(a, l, mode, stream) : launch_log_m<false, float>(a, l, mode, stream);
 }
 
 }  // namespace rsu

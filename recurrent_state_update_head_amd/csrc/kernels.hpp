@@ -7,7 +7,7 @@
 namespace rsu {
 
 constexpr int kMaxW = 32;  // window length limit of the int8 path (LDS of the boundary step)
-constexpr int kMaxC = 16;  // log capacity limit of the base + log path
+constexpr int kMaxC = 63;  // log capacity limit of the base + log path (M = C + 1 <= 64)
 
 // Per-step inputs shared by every representation; pointers are device pointers.
 struct StepArgs {
@@ -29,7 +29,8 @@ struct WindowArgs {
 };
 
 struct LogArgs {
-    int C, L;
+    int C, L;                     // capacity; batch-uniform live length
+    int* Lslot;                   // per-slot live lengths [heads] (per-slot calls only)
     float* lbar;                  // [heads] or [heads, 128]
     void* Klog;                   // [heads, C, 128] in the input dtype
     float* Ulog;                  // [heads, C, 128]
@@ -41,7 +42,8 @@ hipError_t launch_copy(const float* src, float* dst, int64_t n, hipStream_t stre
 hipError_t launch_q8_quantize(int heads, const float* S, int8_t* Z, float* A, hipStream_t stream);
 hipError_t launch_q8_window(const StepArgs& a, const WindowArgs& w, bool per_key, bool bf16,
                             hipStream_t stream);
-hipError_t launch_log(const StepArgs& a, const LogArgs& l, bool merge, bool per_key, bool bf16,
+// mode: 0 append, 1 merge, 2 per-slot live lengths
+hipError_t launch_log(const StepArgs& a, const LogArgs& l, int mode, bool per_key, bool bf16,
                       hipStream_t stream);
 
 }  // namespace rsu

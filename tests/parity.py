@@ -148,6 +148,58 @@ def run_log(w: wl.Workload, sample: int | None = None, steps: int | None = None)
     return err
 
 
+def run_log_slots(w: wl.Workload, sample: int | None = None, steps: int | None = None,
+                  L0: np.ndarray | None = None):
+    """Per-slot live lengths: the GPU's *_log_step_slots against the oracle's per-slot
+    steps (which equal eager decoding, a pinned property). Heads start at staggered
+    points of their cycle (empty entries, K = U = 0, are a valid log of any length),
+    so appends and merges of different heads share every launch."""
+    m = rsu()
+    B, H = w.B, w.H
+    C = w.M - 1
+    steps = w.steps if steps is None else steps
+    S0 = wl.initial_state(w)
+    heads = np.arange(w.heads) if sample is None else wl.sample_heads(w, sample)
+    hd = torch.from_numpy(heads).to(DEV)
+    Sbase = torch.from_numpy(S0).to(DEV).view(B, H, 128, 128)
+    ref = oracle.LogState(S0[heads].astype(np.float64), C, w.per_key_gate)
+    del S0
+    L_all = (np.arange(w.heads, dtype=np.int32) * 5) % (C + 1) if L0 is None else L0.astype(np.int32)
+    Ld = torch.from_numpy(L_all.copy()).to(DEV).view(B, H)
+    Lref = np.ascontiguousarray(L_all[heads])
+    buf = new_log_buffers(w, C)
+    Klog, Ulog, Lam = (buf["Klog"], buf["Ulog"], buf["Lam"]) if C > 0 else (None, None, None)
+    fn = m.kda_log_step_slots if w.per_key_gate else m.gdn_log_step_slots
+    y = torch.empty(B, H, 128, device=DEV)
+    err = {"y": 0.0, "Sbase": 0.0, "lbar": 0.0, "Ulog": 0.0, "Klog": 0.0, "Lam": 0.0, "L": 0,
+           "merges": 0, "appends": 0}
+    gd = (128,) if w.per_key_gate else ()
+    for t in range(steps):
+        x, d = dev_inputs(w, t)
+        fn(C, Ld, Sbase, buf["lbar"], Klog, Ulog, Lam, d["q"], d["k"], d["v"], d["gate"], d["beta"], y)
+        y_ref = ref.step_slots(Lref, *host_slice(x, heads))
+        Lg = take(Ld, hd, ())
+        err["L"] = max(err["L"], int(np.abs(Lg - Lref).max()))
+        err["y"] = max(err["y"], rel_err(take(y, hd, (128,)), y_ref))
+        merged = np.flatnonzero(Lref == 0)
+        appended = np.flatnonzero(Lref > 0)
+        err["merges"] += len(merged)
+        err["appends"] += len(appended)
+        if len(merged):
+            Sg = take(Sbase, hd[torch.from_numpy(merged).to(DEV)], (128, 128))
+            err["Sbase"] = max(err["Sbase"], rel_err(Sg, ref.Sbar[merged]))
+        for i in appended:
+            mm = int(Lref[i]) - 1
+            h = hd[i:i + 1]
+            err["Ulog"] = max(err["Ulog"], rel_err(take(buf["Ulog"][:, :, mm], h, (128,)), ref.U[i:i + 1, mm]))
+            err["Klog"] = max(err["Klog"], float(np.abs(take(buf["Klog"][:, :, mm].float(), h, (128,)) -
+                                                         ref.K[i:i + 1, mm]).max()))
+            err["Lam"] = max(err["Lam"], float(np.abs(take(buf["Lam"][:, :, mm], h, gd) -
+                                                      ref.Lam[i:i + 1, mm]).max()))
+        err["lbar"] = max(err["lbar"], float(np.abs(take(buf["lbar"], hd, gd) - ref.lbar).max()))
+    return err
+
+
 def new_window_buffers(w: wl.Workload):
     B, H, W = w.B, w.H, w.W
     return {

@@ -97,11 +97,18 @@ def test_window_and_log_ranges(lib):
     largs = [GOOD] * 12
     assert a(ctypes.byref(d), 7, 7, *largs, None) == E_RANGE   # append needs L < C
     assert m(ctypes.byref(d), 7, 6, *largs, None) == E_RANGE   # merge needs L == C
-    assert a(ctypes.byref(d), 17, 0, *largs, None) == E_RANGE  # C above the limit
+    assert a(ctypes.byref(d), 64, 0, *largs, None) == E_RANGE  # C above the limit (M <= 64)
+    assert a(ctypes.byref(d), -1, 0, *largs, None) == E_RANGE
     assert a(ctypes.byref(d), 0, 0, *largs, None) == E_RANGE   # no append with C == 0
     # C == 0 merge may pass NULL log buffers; the NULL base is still caught
     assert m(ctypes.byref(d), 0, 0, None, GOOD, None, None, None, *([GOOD] * 6), None) == E_NULL
     assert "Sbase" in _last(lib)
+    sl = lib.gdn_log_step_slots
+    sl.restype = ctypes.c_int
+    assert sl(ctypes.byref(d), 64, *largs, None) == E_RANGE      # C above the limit
+    assert sl(ctypes.byref(d), 7, None, *([GOOD] * 11), None) == E_NULL  # the live-length array
+    assert "L is NULL" in _last(lib)
+    assert sl(ctypes.byref(d), 7, ODD, *([GOOD] * 11), None) == E_ALIGN
 
 
 def test_copy_validation(lib):

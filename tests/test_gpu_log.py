@@ -10,7 +10,7 @@ import torch
 
 import workloads as wl
 from parity import (DEV, TOL_F32, dev_inputs, log_step, new_log_buffers, rel_err, rsu, run_log,
-                    say)
+                    run_log_slots, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -25,7 +25,8 @@ def _check(err, name):
 @pytest.mark.parametrize("variant,M,B,H,qkv", [("gdn", 8, 3, 7, "bf16"), ("gdn", 1, 2, 3, "bf16"),
                                                ("gdn", 2, 2, 2, "f32"), ("kda", 4, 2, 5, "bf16"),
                                                ("kda", 8, 1, 3, "f32"), ("gdn", 17, 1, 2, "bf16"),
-                                               ("gdn", 8, 10, 10, "bf16")])
+                                               ("gdn", 8, 10, 10, "bf16"), ("gdn", 32, 2, 3, "bf16"),
+                                               ("kda", 64, 1, 2, "bf16"), ("gdn", 64, 1, 3, "f32")])
 def test_log_small_all_heads(variant, M, B, H, qkv):
     w = wl.custom(wl.WORKLOADS[5], B=B, H=H, M=M, qkv=qkv, steps=2 * M + 3, variant=variant,
                   gate_lo=0.8 if variant == "kda" else 0.9, gate_hi=1.0 if variant == "kda" else 0.999)
@@ -64,3 +65,30 @@ def test_log_matches_gpu_eager(variant):
                                        S_eager.cpu().numpy().reshape(-1, 128 * 128)))
     say(f"[log] GPU log vs GPU eager ({variant}): {worst:.3e}")
     assert worst < TOL_F32
+
+
+def _check_slots(err, name, C):
+    say(f"[log slots] {name}: {err}")
+    assert err["L"] == 0
+    assert err["merges"] > 0 and (err["appends"] > 0 or C == 0)
+    assert err["y"] < TOL_F32 and err["Sbase"] < TOL_F32 and err["Ulog"] < TOL_F32
+    assert err["Klog"] == 0.0
+    assert err["lbar"] < 1e-5 and err["Lam"] < 1e-5
+
+
+@pytest.mark.parametrize("variant,M,B,H,qkv", [("gdn", 8, 2, 5, "bf16"), ("kda", 4, 2, 5, "bf16"),
+                                               ("gdn", 1, 1, 3, "f32"), ("kda", 32, 1, 4, "f32"),
+                                               ("gdn", 64, 1, 3, "bf16")])
+def test_log_slots_mixed_phases(variant, M, B, H, qkv):
+    """Per-slot live lengths: heads at staggered points of their cycle, so appends and
+    merges of different heads share each launch; live lengths advance on the device."""
+    w = wl.custom(wl.WORKLOADS[5], B=B, H=H, M=M, qkv=qkv, steps=2 * M + 3, variant=variant,
+                  gate_lo=0.8 if variant == "kda" else 0.9, gate_hi=1.0 if variant == "kda" else 0.999)
+    _check_slots(run_log_slots(w), f"{variant} M={M} B={B} H={H} {qkv}", M - 1)
+
+
+def test_log_slots_b256_h48_sampled():
+    """Per-slot live lengths at full size (B=256, H=48, M=8), 64 sampled heads."""
+    w = wl.WORKLOADS[5]
+    say(f"[log slots] {w.name}: full size, 64 sampled heads, 24 steps")
+    _check_slots(run_log_slots(w, sample=64, steps=24), w.name + " slots", w.M - 1)

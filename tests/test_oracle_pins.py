@@ -267,7 +267,8 @@ def test_window_readout_matches_eq9(per_key):
 
 # ---------------------------------------------------------------- log path
 
-@pytest.mark.parametrize("per_key,M", [(False, 1), (False, 2), (False, 8), (True, 4), (True, 8)])
+@pytest.mark.parametrize("per_key,M", [(False, 1), (False, 2), (False, 8), (True, 4), (True, 8),
+                                       (False, 64), (True, 32)])
 def test_log_equals_eager(per_key, M):
     nh, dk, dv, T = 5, 128, 128, 3 * M + 2
     S0 = RNG.standard_normal((nh, dk, dv)) * 0.02
@@ -283,6 +284,34 @@ def test_log_equals_eager(per_key, M):
             # right after a merge: the base alone is the state, and lbar is reset
             np.testing.assert_allclose(ls.Sbar, S_eager, rtol=0, atol=1e-12)
             assert not ls.lbar.any()
+
+
+@pytest.mark.parametrize("per_key", [False, True])
+def test_log_slots_equal_eager(per_key):
+    """Per-slot live lengths (DeltaLog sec. 4: one live length per request slot): every
+    head sits at its own point of its append/merge cycle, merges at its own steps, and
+    still decodes exactly like eager dense updates (eq. 7 at every step)."""
+    nh, dk, dv, C = 6, 128, 128, 4
+    S0 = RNG.standard_normal((nh, dk, dv)) * 0.02
+    S_eager = S0.copy()
+    ls = oracle.LogState(S0, C, per_key)
+    # empty entries (K = U = 0) are a valid log of any length: each head starts elsewhere
+    Ls = np.array([0, 1, 2, 3, 4, 4], dtype=np.int32)
+    merged = np.zeros(nh, dtype=int)
+    for t in range(2 * C + 3):
+        q, k, v, g, b = _inputs(nh, dk, dv, per_key, RNG)
+        was_full = Ls == C
+        y_e = oracle.dense_step(S_eager, q, k, v, g, b)
+        y_l = ls.step_slots(Ls, q, k, v, g, b)
+        np.testing.assert_allclose(y_l, y_e, rtol=0, atol=1e-12)
+        np.testing.assert_array_equal(Ls[was_full], 0)
+        merged += was_full
+        for h in np.flatnonzero(was_full):
+            # right after its merge, a head's base alone is its state
+            np.testing.assert_allclose(ls.Sbar[h], S_eager[h], rtol=0, atol=1e-12)
+    assert (merged >= 2).all()
+    with pytest.raises(ValueError):
+        ls.step_slots(np.array([0, 1, 2, 3, 4, 5], dtype=np.int32), q, k, v, g, b)
 
 
 def test_log_slot_reset_leaves_base():
