@@ -76,3 +76,28 @@ def test_headline_workload_bytes():
     assert bench.dense_bytes_per_head(w) == 132360
     assert bench.cycle_bytes_per_head(wl.WORKLOADS[4]) == pytest.approx(25754, abs=1)
     assert bench.cycle_bytes_per_head(wl.WORKLOADS[5]) == pytest.approx(78401.5, abs=1e-9)
+
+
+@pytest.mark.parametrize("variant,M", [("gdn", 1), ("gdn", 2), ("gdn", 8), ("gdn", 64), ("kda", 4), ("kda", 16)])
+def test_log_cycle_bytes_follow_the_traffic_model(variant, M):
+    """DeltaLog sec. 3.2, eqs. 10-11: per step the base is read (C_state), written once
+    per M steps (C_state / M), an entry is appended in M-1 of M steps and (M-1)/2
+    entries are replayed on average (C_log(M) = ((M-1)/M + (M-1)/2) C_entry), and the
+    cumulative log-decay is read and written (2 C_decay). The rest is T_common (q, k,
+    v, gate, beta, y). bench.py's cycle average must be exactly that sum."""
+    from fractions import Fraction as Fr
+    w = wl.custom(wl.WORKLOADS[5], variant=variant, M=M)
+    d = wl.DK
+    gdim = d if w.per_key_gate else 1
+    c_state = 4 * d * d
+    c_entry = d * 2 + 4 * d + 4 * gdim          # bf16 key factor, fp32 value factor, Lam
+    c_decay = 4 * gdim
+    t_common = 3 * d * 2 + 4 * gdim + 4 + 4 * d  # bf16 q/k/v, gate, beta, fp32 y
+    c_log = (Fr(M - 1, M) + Fr(M - 1, 2)) * c_entry
+    model = t_common + c_state + Fr(c_state, M) + c_log + 2 * c_decay
+    assert Fr(bench.cycle_bytes_per_head(w)) == model
+    # a batch at random cycle points moves, per head, what its live-length mix dictates
+    w2 = wl.custom(w, B=8, H=16)
+    L = bench.slot_lengths(w2)
+    per = [bench.log_step_bytes_per_head(w2, int(x)) for x in L]
+    assert bench.slots_bytes_per_head(w2) == pytest.approx(sum(per) / len(per), rel=1e-15)
