@@ -1,0 +1,109 @@
+"""fp64 oracle of LeapQuant's window-boundary format -- TEST INFRASTRUCTURE.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and ``bench.py``'s ``cpu_baseline`` leg may
+import this module. It shares no code with the HIP library. Plain numpy in fp64.
+
+The format (LeapQuant sec. 3.3 eqs. 5-6, sec. 3.4 eq. 7, App. B.3 eq. 10): at a window
+boundary the reconstructed state S is split into r compensator tokens and a residual,
+
+    S = C * dequant(Z, B) + Kt Ut^T,   C = Diag(c),   dequant(Z, B)_ij = Z_ij B_j / 127,
+
+where (Kt, Ut) are r key/value vector pairs stored in fp16 that approximate S's
+dominant low-rank part (the argmin of ||S - K U^T||_F), c is a per-key-row smoothing
+scale (the square root of the row's mean absolute residual, floored), and Z / B are
+the int8 payload and fp32 per-value-channel absmax of the smoothed residual C^{-1} R.
+Inside a window the state is that representation plus the buffered real-token
+records; eq. 10 reads it without materializing it.
+
+Readings taken where the pages are silent (stated once here, used everywhere):
+  * the fit is subspace (block power) iteration for the top-r right singular
+    subspace: V <- MGS(S^T S V), repeated n_iter times, then Kt = S V, Ut = V;
+    MGS is modified Gram-Schmidt over the columns in order, a zero column stays zero;
+  * the start is the previous window's Ut (orthonormalized); the first fit, from a
+    plain state, starts from the first r Walsh (Sylvester-Hadamard) columns;
+  * Kt and Ut are rounded to fp16 (round to nearest even) and the residual is taken
+    against the rounded tokens, so the stored pieces add up to the reconstruction;
+  * the smoothing floor is 1e-6 on c; c and B are stored in fp32;
+  * codes round half to even and are clamped to [-127, 127]; B_j = 0 gives Z = 0.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+R_TOKENS = 4
+C_FLOOR = 1e-6
+
+
+def walsh_start(d: int = 128, r: int = R_TOKENS) -> np.ndarray:
+    """The first r Walsh columns of the d x d Sylvester-Hadamard matrix, orthonormal:
+    entry (i, h) is (-1)^popcount(i & h) / sqrt(d)."""
+    i = np.arange(d)[:, None]
+    h = np.arange(r)[None, :]
+    bits = np.vectorize(lambda x: bin(int(x)).count("1"))(i & h)
+    return np.where(bits % 2 == 0, 1.0, -1.0) / np.sqrt(d)
+
+
+def mgs(W: np.ndarray) -> np.ndarray:
+    """Modified Gram-Schmidt over the columns of W, in order; a column with zero norm
+    after the projections stays zero."""
+    Q = np.array(W, dtype=np.float64, copy=True)
+    r = Q.shape[1]
+    for h in range(r):
+        v = Q[:, h]
+        for g in range(h):
+            v = v - (Q[:, g] @ v) * Q[:, g]
+        n = np.sqrt(v @ v)
+        Q[:, h] = v / n if n > 0 else 0.0
+    return Q
+
+
+def fit(S: np.ndarray, V0: np.ndarray, n_iter: int):
+    """Compensator tokens of S: n_iter steps of V <- MGS(S^T (S V)) from MGS(V0);
+    returns (Kt, Ut) = (S V, V), unrounded (LeapQuant sec. 3.3, eqs. 5-6)."""
+    V = mgs(V0)
+    for _ in range(n_iter):
+        V = mgs(S.T @ (S @ V))
+    return S @ V, V
+
+
+def to_fp16(x: np.ndarray) -> np.ndarray:
+    """Round to the nearest fp16 (ties to even), returned widened to fp64."""
+    return np.asarray(x, dtype=np.float64).astype(np.float16).astype(np.float64)
+
+
+def smooth_quantize(S: np.ndarray, K16: np.ndarray, U16: np.ndarray):
+    """Residual, smoothing and per-value-channel int8 (LeapQuant sec. 3.4, eq. 7).
+
+    Returns Z (int8), B (fp32 values in fp64), c (fp32 values in fp64) and w, the
+    exact pre-rounding code values (for the tie band of parity checks)."""
+    R = S - K16 @ U16.T
+    m = np.mean(np.abs(R), axis=1)
+    c = np.float32(np.maximum(np.sqrt(m), C_FLOOR)).astype(np.float64)
+    X = R / c[:, None]
+    B = np.max(np.abs(X), axis=0).astype(np.float32).astype(np.float64)
+    w = np.zeros_like(X)
+    nz = B > 0
+    w[:, nz] = X[:, nz] * 127.0 / B[nz][None, :]
+    Z = np.clip(np.rint(w), -127, 127).astype(np.int8)
+    return Z, B, c, w
+
+
+def boundary(S: np.ndarray, V0: np.ndarray, n_iter: int) -> dict:
+    """The whole boundary: fit, fp16 tokens, residual, smoothing, payload."""
+    K, U = fit(S, V0, n_iter)
+    K16, U16 = to_fp16(K), to_fp16(U)
+    Z, B, c, w = smooth_quantize(S, K16, U16)
+    return {"K": K, "U": U, "K16": K16, "U16": U16, "Z": Z, "B": B, "c": c, "w": w}
+
+
+def represent(Z, B, c, K16, U16) -> np.ndarray:
+    """The state a window starts from: C dequant(Z, B) + Kt Ut^T (eq. 7 at l = 0)."""
+    Zf = np.asarray(Z, dtype=np.float64)
+    return np.asarray(c, np.float64)[:, None] * (Zf * (np.asarray(B, np.float64) / 127.0)[None, :]) + \
+        np.asarray(K16, np.float64) @ np.asarray(U16, np.float64).T
+
+
+def bytes_per_element(d: int = 128, r: int = R_TOKENS) -> float:
+    """Stored bytes per state element at a boundary: int8 payload, fp32 B and c,
+    fp16 token pairs (LeapQuant sec. 4.3)."""
+    return (d * d * 1 + d * 4 + d * 4 + 2 * r * d * 2) / (d * d)
