@@ -157,6 +157,39 @@ int kda_log_merge(const rsu_dims *dims, int C, int L, float *Sbase, float *lbar,
                   float *y, rsu_stream_t stream);
 
 /* ------------------------------------------------------------------------
+ * LeapQuant's window-boundary format (LeapQuant sec. 3.3 eqs. 5-6, sec. 3.4
+ * eq. 7, App. B.3 eq. 10), for scalar gates (GDN). A window starts from
+ *   S_0 = C dequant(Z, B) + Kt Ut^T,  C = Diag(row_smooth),
+ *   dequant(Z, B)_ij = Z_ij * col_absmax_j / 127,
+ * i.e. r = 4 compensator token pairs (Kt, Ut) in fp16 that hold the dominant
+ * low-rank part, a per-key-row smoothing scale, and an int8 payload of the
+ * smoothed residual with one fp32 absmax per value column.
+ *   Z [B,H,d_k,d_v] int8, col_absmax [B,H,d_v] fp32, row_smooth [B,H,d_k] fp32,
+ *   Kc, Uc [B,H,4,d] fp16 (token-major: Kc[b][h][t][i] is key row i of token t).
+ * The tokens are fitted by subspace iteration: V <- MGS(S^T S V), n_iter times,
+ * Kt = S V, Ut = V (MGS = modified Gram-Schmidt over the 4 columns in order), then
+ * rounded to fp16; the residual R = S - Kt Ut^T (with the rounded tokens) gets
+ * row_smooth_i = max(sqrt(mean_j |R_ij|), 1e-6) and the payload of R_ij / row_smooth_i,
+ * rounded half to even into [-127, 127] per value column.
+ *
+ * gdn_lq_quantize: converts plain fp32 states S into the format; the fit starts
+ *   from the first 4 Walsh columns ((-1)^popcount(i & t) / sqrt(d)). S is only read.
+ * gdn_lq_window: one decode step inside a window, like gdn_q8_window (records
+ *   Kbuf [B,H,W,d] bf16, Ubuf [B,H,W,d] fp32, Gbuf [B,H,W] fp32 as there), reading
+ *   by eq. 10; at pos = W-1 it forms S_W, refits the tokens starting from the
+ *   current Ut, and rewrites Z, col_absmax, row_smooth, Kc and Uc in place.
+ * Requires bf16 q/k/v (else RSU_E_DTYPE), 1 <= W <= 16, 0 <= pos < W,
+ * 0 <= n_iter <= 64 (else RSU_E_RANGE). Other rules as for the int8 window.
+ * ---------------------------------------------------------------------- */
+int gdn_lq_quantize(const rsu_dims *dims, const float *S, int n_iter, int8_t *Z,
+                    float *col_absmax, float *row_smooth, void *Kc, void *Uc,
+                    rsu_stream_t stream);
+int gdn_lq_window(const rsu_dims *dims, int W, int pos, int n_iter, int8_t *Z,
+                  float *col_absmax, float *row_smooth, void *Kc, void *Uc, void *Kbuf,
+                  float *Ubuf, float *Gbuf, const void *q, const void *k, const void *v,
+                  const float *alpha, const float *beta, float *y, rsu_stream_t stream);
+
+/* ------------------------------------------------------------------------
  * Per-slot live lengths. DeltaLog sec. 4 keeps the live-log length as per-slot
  * metadata; requests admitted at different times sit at different points of
  * their append/merge cycle, and its serving prototype splits them into

@@ -14,6 +14,8 @@ Shapes (B requests, H heads, d = 128):
   Kbuf [B,H,W,d] (q dtype), Ubuf [B,H,W,d] fp32, Gbuf [B,H,W] or [B,H,W,d] fp32
   Klog [B,H,C,d] (q dtype), Ulog [B,H,C,d] fp32, Lam [B,H,C] or [B,H,C,d] fp32,
   lbar [B,H] or [B,H,d] fp32, per-slot live lengths L [B,H] int32
+  LeapQuant format: Z [B,H,d,d] int8, col_absmax [B,H,d] fp32, row_smooth [B,H,d] fp32,
+  Kc, Uc [B,H,4,d] fp16
 """
 from __future__ import annotations
 
@@ -55,6 +57,8 @@ _SIGS = {
     "kda_log_append": [_DP, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
     "gdn_log_merge": [_DP, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
     "kda_log_merge": [_DP, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
+    "gdn_lq_quantize": [_DP, _P, _I, _P, _P, _P, _P, _P, _P],
+    "gdn_lq_window": [_DP, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
     "gdn_log_step_slots": [_DP, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
     "kda_log_step_slots": [_DP, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
     "rsu_copy_f32": [_P, _P, ctypes.c_int64, _P],
@@ -237,6 +241,43 @@ def gdn_log_step_slots(C, L, Sbase, lbar, Klog, Ulog, Lam, q, k, v, alpha, beta,
 
 def kda_log_step_slots(C, L, Sbase, lbar, Klog, Ulog, Lam, q, k, v, d, beta, y):
     return _log_slots("kda_log_step_slots", True, C, L, Sbase, lbar, Klog, Ulog, Lam, q, k, v, d, beta, y)
+
+
+def _lq_state(B, H, Z, col_absmax, row_smooth, Kc, Uc):
+    _need(Z, "Z", torch.int8, (B, H, D, D))
+    _need(col_absmax, "col_absmax", torch.float32, (B, H, D))
+    _need(row_smooth, "row_smooth", torch.float32, (B, H, D))
+    _need(Kc, "Kc", torch.float16, (B, H, 4, D))
+    _need(Uc, "Uc", torch.float16, (B, H, 4, D))
+
+
+def gdn_lq_quantize(S, n_iter, Z, col_absmax, row_smooth, Kc, Uc):
+    """Convert fp32 states into LeapQuant's boundary format (tokens fitted with n_iter
+    subspace iterations from the Walsh start)."""
+    if S.dim() != 4:
+        raise ValueError("S must be [B, H, 128, 128]")
+    B, H = S.shape[0], S.shape[1]
+    _need(S, "S", torch.float32, (B, H, D, D))
+    _lq_state(B, H, Z, col_absmax, row_smooth, Kc, Uc)
+    dims = _Dims(B, H, D, D, RSU_F32)
+    _call("gdn_lq_quantize", ctypes.byref(dims), _ptr(S), int(n_iter), _ptr(Z), _ptr(col_absmax),
+          _ptr(row_smooth), _ptr(Kc), _ptr(Uc), _stream())
+
+
+def gdn_lq_window(W, pos, n_iter, Z, col_absmax, row_smooth, Kc, Uc, Kbuf, Ubuf, Gbuf, q, k, v, alpha,
+                  beta, y):
+    """One decode step in LeapQuant's format (eq. 10 readout; at pos = W - 1 the refit)."""
+    dims = _dims(q, k, v)
+    B, H = dims.B, dims.H
+    _lq_state(B, H, Z, col_absmax, row_smooth, Kc, Uc)
+    _need(Kbuf, "Kbuf", q.dtype, (B, H, W, D))
+    _need(Ubuf, "Ubuf", torch.float32, (B, H, W, D))
+    _need(Gbuf, "Gbuf", torch.float32, (B, H, W))
+    _step_common(dims, alpha, beta, y, False, "alpha")
+    _call("gdn_lq_window", ctypes.byref(dims), int(W), int(pos), int(n_iter), _ptr(Z), _ptr(col_absmax),
+          _ptr(row_smooth), _ptr(Kc), _ptr(Uc), _ptr(Kbuf), _ptr(Ubuf), _ptr(Gbuf), _ptr(q), _ptr(k), _ptr(v),
+          _ptr(alpha), _ptr(beta), _ptr(y), _stream())
+    return y
 
 
 def copy_f32(src: torch.Tensor, dst: torch.Tensor):

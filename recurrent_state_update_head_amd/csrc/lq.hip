@@ -1,0 +1,683 @@
+// lq.hip -- LeapQuant's window-boundary format for scalar gates (GDN) and bf16 keys.
+//
+// A window starts from (LeapQuant sec. 3.3 eqs. 5-6, sec. 3.4 eq. 7)
+//   S_0 = C dequant(Z, B) + Kt Ut^T,  C = Diag(c),  dequant(Z, B)_ij = Z_ij B_j / 127,
+// with r = 4 compensator tokens (Kt, Ut) in fp16, a per-key-row smoothing scale c and a
+// per-value-channel int8 payload Z with fp32 absmax B. Inside the window the readout is
+// eq. 10 (App. B.3):
+//   S_l^T x = B Z^T/127 (C Gamma_{1:l} x) + Ut (Kt^T Gamma_{1:l} x) + sum_j u_j (k_j^T Gamma_{j+1:l} x),
+// i.e. the int8 sweep with c and the decay folded into the read vector and B applied per
+// value column to the swept partials, the token pairs as four more records decayed by
+// every gate of the window, and the real records as in the per-row int8 path.
+// At the window's last step the state S_W (eq. 7) is formed, the tokens are refitted to
+// it by subspace iteration (V <- MGS(S^T S V) from the previous window's Ut, Kt = S V,
+// Ut = V, both rounded to fp16), and the residual S_W - Kt Ut^T is smoothed
+// (c_i = max(sqrt(mean_j |R_ij|), 1e-6)) and quantized per value channel.
+#include "kernels.hpp"
+#include "rsu_device.hpp"
+
+namespace rsu {
+
+constexpr int kTok = 4;                 // compensator tokens per head
+constexpr float kSmoothFloor = 1e-6f;   // floor of the smoothing scale
+typedef _Float16 half_t;
+
+// Int8 tiles use the per-row int8 path's thread layout: lane l of wave w owns one 32-bit
+// word of codes (4 columns) in each of the 16 rows 8 it + 2 w + (l >> 5).
+__device__ __forceinline__ int lq_row(int it, int wave, int ro) { return 8 * it + 2 * wave + ro; }
+
+__device__ __forceinline__ f32x4 unpack_codes(uint32_t w) {
+    return f32x4{static_cast<float>(static_cast<int8_t>(w & 0xffu)),
+                 static_cast<float>(static_cast<int8_t>((w >> 8) & 0xffu)),
+                 static_cast<float>(static_cast<int8_t>((w >> 16) & 0xffu)),
+                 static_cast<float>(static_cast<int8_t>(w >> 24))};
+}
+
+// Code byte of w = x * (127 / B): round half to even with one fp32 add (the low mantissa
+// bits of w + 1.5 * 2^23 are the integer), then clamp the bits to the codes -127 .. 127.
+__device__ __forceinline__ uint32_t lq_code(float w) {
+    constexpr float kMagic = 12582912.0f;
+    const int bits = __float_as_int(w + kMagic);
+    return static_cast<uint32_t>(min(max(bits, 0x4B400000 - 127), 0x4B400000 + 127)) & 0xffu;
+}
+
+// ---------------------------------------------------------------- the refit
+// LDS of the refit, in floats: the state S [128 x 128] with element (r, c) at
+// r * 128 + (c ^ (r & 63)) (the XOR spreads both row-wise and column-wise sweeps over
+// the banks), then V, Y, W, Kr, Ur [128] x f32x4 (token t of row / column i in
+// element t of entry i) and 128 per-column scales.
+constexpr int kRefitFloats = kD * kD + 5 * 4 * kD + kD;
+__device__ __forceinline__ int swz(int r, int c) { return r * kD + (c ^ (r & 63)); }
+
+struct RefitLds {
+    float* S;
+    f32x4 *V, *Y, *W, *Kr, *Ur;
+    float* sc;
+    __device__ explicit RefitLds(float* base)
+        : S(base), V(reinterpret_cast<f32x4*>(base + kD * kD)), Y(V + kD), W(Y + kD), Kr(W + kD),
+          Ur(Kr + kD), sc(reinterpret_cast<float*>(Ur + kD)) {}
+};
+
+// W -> V: modified Gram-Schmidt over the 4 columns in order (wave 0; lane l holds rows
+// 2l and 2l + 1); a column with zero norm after the projections stays zero.
+__device__ __forceinline__ void refit_mgs(const RefitLds& L, int wave, int lane) {
+    if (wave == 0) {
+        f32x4 a = L.W[2 * lane], b = L.W[2 * lane + 1];
+#pragma unroll
+        for (int t = 0; t < kTok; ++t) {
+#pragma unroll
+            for (int g = 0; g < t; ++g) {
+                const float d = wave_sum(a[g] * a[t] + b[g] * b[t]);
+                a[t] -= d * a[g];
+                b[t] -= d * b[g];
+            }
+            const float n2 = wave_sum(a[t] * a[t] + b[t] * b[t]);
+            const float inv = n2 > 0.f ? 1.f / sqrtf(n2) : 0.f;
+            a[t] *= inv;
+            b[t] *= inv;
+        }
+        L.V[2 * lane] = a;
+        L.V[2 * lane + 1] = b;
+    }
+    __syncthreads();
+}
+
+// Y = S V (thread (row, half) sums 64 columns; the two halves of a row are lanes 2i, 2i+1)
+__device__ __forceinline__ void refit_sv(const RefitLds& L, int rc, int hf) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < 64; ++c) {
+        const int col = 64 * hf + ((c + 32 * hf) & 63);
+        acc += L.S[swz(rc, col)] * L.V[col];
+    }
+    acc = f32x4{acc.x + dpp<kDppXor1>(acc.x), acc.y + dpp<kDppXor1>(acc.y), acc.z + dpp<kDppXor1>(acc.z),
+                acc.w + dpp<kDppXor1>(acc.w)};
+    if (hf == 0) L.Y[rc] = acc;
+    __syncthreads();
+}
+
+// W = S^T Y (thread (column, half) sums 64 rows)
+__device__ __forceinline__ void refit_sty(const RefitLds& L, int rc, int hf) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int r = 0; r < 64; ++r) {
+        const int row = 64 * hf + ((r + 32 * hf) & 63);
+        acc += L.S[swz(row, rc)] * L.Y[row];
+    }
+    acc = f32x4{acc.x + dpp<kDppXor1>(acc.x), acc.y + dpp<kDppXor1>(acc.y), acc.z + dpp<kDppXor1>(acc.z),
+                acc.w + dpp<kDppXor1>(acc.w)};
+    if (hf == 0) L.W[rc] = acc;
+    __syncthreads();
+}
+
+// The refit of one head. On entry S holds the state and W the start vectors; every
+// thread of the workgroup calls it. Writes Z, B, c and the fp16 tokens of the head.
+__device__ void lq_refit(const RefitLds& L, int n_iter, int tid, uint32_t* __restrict__ Zh,
+                         float* __restrict__ Bh, float* __restrict__ Ch, half_t* __restrict__ Kh,
+                         half_t* __restrict__ Uh) {
+    const int wave = tid >> 6, lane = tid & 63;
+    const int rc = tid >> 1, hf = tid & 1;
+    refit_mgs(L, wave, lane);
+    for (int it = 0; it < n_iter; ++it) {
+        refit_sv(L, rc, hf);
+        refit_sty(L, rc, hf);
+        refit_mgs(L, wave, lane);
+    }
+    refit_sv(L, rc, hf);  // Kt = S V
+
+    // fp16 tokens (stored), and their exact fp32 values for the residual
+    if (tid < kD) {
+        const f32x4 kv = L.Y[tid], uv = L.V[tid];
+        f32x4 kr, ur;
+#pragma unroll
+        for (int t = 0; t < kTok; ++t) {
+            const half_t kh = static_cast<half_t>(kv[t]);
+            const half_t uh = static_cast<half_t>(uv[t]);
+            kr[t] = static_cast<float>(kh);
+            ur[t] = static_cast<float>(uh);
+            Kh[t * kD + tid] = kh;
+            Uh[t * kD + tid] = uh;
+        }
+        L.Kr[tid] = kr;
+        L.Ur[tid] = ur;
+    }
+    __syncthreads();
+
+    // residual R = S - Kt Ut^T in place, row smoothing c, then X = R / c in place
+    {
+        const f32x4 kr = L.Kr[rc];
+        float asum = 0.f;
+        for (int c = 0; c < 64; ++c) {
+            const int col = 64 * hf + ((c + 32 * hf) & 63);
+            const int p = swz(rc, col);
+            const f32x4 u = L.Ur[col];
+            const float r = L.S[p] - (kr.x * u.x + kr.y * u.y + kr.z * u.z + kr.w * u.w);
+            L.S[p] = r;
+            asum += fabsf(r);
+        }
+        asum += dpp<kDppXor1>(asum);
+        const float cs = fmaxf(sqrtf(asum * (1.f / kD)), kSmoothFloor);
+        if (hf == 0) Ch[rc] = cs;
+        const float ic = 1.f / cs;
+        for (int c = 0; c < 64; ++c) {
+            const int p = swz(rc, 64 * hf + c);
+            L.S[p] *= ic;
+        }
+    }
+    __syncthreads();
+
+    // per-value-channel absmax B and the code scale 127 / B
+    {
+        float m = 0.f;
+        for (int r = 0; r < 64; ++r) {
+            const int row = 64 * hf + ((r + 32 * hf) & 63);
+            m = fmaxf(m, fabsf(L.S[swz(row, rc)]));
+        }
+        m = fmaxf(m, dpp<kDppXor1>(m));
+        if (hf == 0) {
+            Bh[rc] = m;
+            L.sc[rc] = m > 0.f ? __fdiv_rn(127.f, m) : 0.f;
+        }
+    }
+    __syncthreads();
+
+    // codes: thread (row, half) packs its 64 columns into 16 words, written over its own
+    // half-row of S (a block only this thread reads), then whole rows leave together
+    {
+        float x[64];
+#pragma unroll
+        for (int c = 0; c < 64; ++c) x[c] = L.S[swz(rc, 64 * hf + c)];
+        uint32_t* Su = reinterpret_cast<uint32_t*>(L.S);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const int c0 = 64 * hf + 4 * j;
+            Su[rc * kD + 64 * hf + j] = lq_code(x[4 * j] * L.sc[c0]) | (lq_code(x[4 * j + 1] * L.sc[c0 + 1]) << 8) |
+                                        (lq_code(x[4 * j + 2] * L.sc[c0 + 2]) << 16) |
+                                        (lq_code(x[4 * j + 3] * L.sc[c0 + 3]) << 24);
+        }
+    }
+    __syncthreads();
+    {
+        const uint32_t* Su = reinterpret_cast<const uint32_t*>(L.S);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int qd = tid + kThreads * m;
+            const int row = qd >> 3, d = 4 * (qd & 7);  // word d .. d+3 of the row's 32
+            const u32x4 w4 = *reinterpret_cast<const u32x4*>(Su + row * kD + 64 * (d >> 4) + (d & 15));
+            __builtin_nontemporal_store(w4, reinterpret_cast<u32x4*>(Zh + row * (kD / 4) + d));
+        }
+    }
+}
+
+// ---------------------------------------------------------------- conversion of a plain state
+__global__ __launch_bounds__(kThreads) void lq_quantize_kernel(const float* __restrict__ S, int n_iter,
+                                                               int8_t* __restrict__ Z, float* __restrict__ B,
+                                                               float* __restrict__ Cs, half_t* __restrict__ Kc,
+                                                               half_t* __restrict__ Uc) {
+    extern __shared__ float lds[];
+    const RefitLds L(lds);
+    const int h = head_of_block(blockIdx.x, gridDim.x), tid = threadIdx.x;
+    const float* Sh = S + static_cast<size_t>(h) * kD * kD;
+#pragma unroll 4
+    for (int m = 0; m < kD * kD / 4 / kThreads; ++m) {
+        const int qd = tid + kThreads * m;
+        const int row = qd >> 5, c4 = qd & 31;
+        const f32x4 v = stream_load(Sh + row * kD + 4 * c4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) L.S[swz(row, 4 * c4 + e)] = v[e];
+    }
+    if (tid < kD) {  // the first 4 Walsh columns: (-1)^popcount(i & t) / sqrt(128)
+        constexpr float s = 0.08838834764831845f;
+        f32x4 w;
+#pragma unroll
+        for (int t = 0; t < kTok; ++t) w[t] = (__builtin_popcount(tid & t) & 1) ? -s : s;
+        L.W[tid] = w;
+    }
+    __syncthreads();
+    const size_t vo = static_cast<size_t>(h) * kD;
+    lq_refit(L, n_iter, tid, reinterpret_cast<uint32_t*>(Z + vo * kD), B + vo, Cs + vo,
+             Kc + vo * kTok, Uc + vo * kTok);
+}
+
+// ---------------------------------------------------------------- in-window step
+// Threads and loads as in the per-row int8 step (records in registers, 16-lane groups
+// for the record coefficients, row-owners for the record corrections); the tokens are
+// four more records: groups 0..3 reduce (Kt_t . k, Kt_t . q) and owners 0..3 add
+// Ut_t c_t. The swept payload partials are scaled by B_j / 127 per column first.
+__global__ __launch_bounds__(kThreads) void lq_step_kernel(
+    int W, int pos, const int8_t* __restrict__ Z, const float* __restrict__ Bcol,
+    const float* __restrict__ Csm, const half_t* __restrict__ Kc, const half_t* __restrict__ Uc,
+    bf16_t* __restrict__ Kbuf, float* __restrict__ Ubuf, float* __restrict__ Gbuf,
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
+    const float* __restrict__ gate, const float* __restrict__ beta, float* __restrict__ y) {
+    __shared__ f32x2 rowv[kD];
+    __shared__ f32x2 coef[16];
+    __shared__ f32x2 ctok[kTok];
+    __shared__ f32x2 red[4][kD];
+    __shared__ float kq_part[2];
+
+    const int h = head_of_block(blockIdx.x, gridDim.x), tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
+    const int c4 = lane & 31, ro = lane >> 5, owner = 2 * wave + ro;
+    const int grp = tid >> 4, ch = tid & 15;
+    const size_t vec_off = static_cast<size_t>(h) * kD;
+    const size_t rec0 = static_cast<size_t>(h) * W * kD;
+    const size_t tok0 = static_cast<size_t>(h) * kTok * kD;
+    const int r = tid & (kD - 1);
+    const bool first = tid < kD;
+
+    // ---- loads: records, tokens, gates, inputs, then the codes
+    uint32_t kc[4] = {0u, 0u, 0u, 0u};
+    if (0 < pos) {
+        const uint4 x = *reinterpret_cast<const uint4*>(Kbuf + rec0 + static_cast<size_t>(grp < pos ? grp : 0) * kD + 8 * ch);
+        kc[0] = x.x; kc[1] = x.y; kc[2] = x.z; kc[3] = x.w;
+    }
+    f32x4 ur[2];
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+        const int j = owner + 8 * m;
+        ur[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (8 * m < pos)
+            ur[m] = *reinterpret_cast<const f32x4*>(Ubuf + rec0 + static_cast<size_t>(j < pos ? j : 0) * kD + 4 * c4);
+    }
+    // token keys (groups 0..3, 8 keys per lane) and token values (owners 0..3, 4 columns)
+    uint4 ktw = {0u, 0u, 0u, 0u};
+    if (grp < kTok) ktw = *reinterpret_cast<const uint4*>(Kc + tok0 + grp * kD + 8 * ch);
+    uint2 utw = {0u, 0u};
+    if (owner < kTok) utw = *reinterpret_cast<const uint2*>(Uc + tok0 + owner * kD + 4 * c4);
+    const float g_lane = lane < pos ? Gbuf[static_cast<size_t>(h) * W + lane] : 1.f;
+    const uint4 kchw = *reinterpret_cast<const uint4*>(k + vec_off + 8 * ch);
+    const uint4 qchw = *reinterpret_cast<const uint4*>(q + vec_off + 8 * ch);
+    const f32x4 bsc = *reinterpret_cast<const f32x4*>(Bcol + vec_off + 4 * c4) * (1.f / 127.f);
+    const float kr = load_in(k, vec_off + r), qr = load_in(q, vec_off + r);
+    const float gr = gate[h];
+    const float cr = Csm[vec_off + r];
+    const float vr = load_in(v, vec_off + r);
+    const float bt = beta[h];
+    const uint32_t* Zh = reinterpret_cast<const uint32_t*>(Z + static_cast<size_t>(h) * kD * kD);
+    uint32_t zw[kRowsPerThread];
+#pragma unroll
+    for (int it = 0; it < kRowsPerThread; ++it)
+        zw[it] = __builtin_nontemporal_load(Zh + lq_row(it, wave, ro) * (kD / 4) + c4);
+
+    // ---- decays (newest gate first): after record grp, and over the whole window so far
+    float Gg = 1.f, Gall = 1.f;
+    for (int i = pos - 1; i >= 0; --i) {
+        const float gi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, g_lane), i));
+        Gg = i > grp ? Gg * gi : Gg;
+        Gall *= gi;
+    }
+    const uint32_t kcw[4] = {kchw.x, kchw.y, kchw.z, kchw.w};
+    const uint32_t qcw[4] = {qchw.x, qchw.y, qchw.z, qchw.w};
+    auto bfe = [](const uint32_t (&w)[4], int e) {
+        return (e & 1) ? __uint_as_float(w[e >> 1] & 0xffff0000u) : __uint_as_float(w[e >> 1] << 16);
+    };
+    if (0 < pos) {
+        float ck = 0.f, cq = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float ej = bfe(kc, e) * (Gg * gr);
+            ck += ej * bfe(kcw, e);
+            cq += ej * bfe(qcw, e);
+        }
+        ck = row16_sum(ck);
+        cq = row16_sum(cq);
+        if (ch == 0 && grp < pos) coef[grp] = f32x2{ck, cq};
+    }
+    if (wave == 0) {  // groups 0..3: token coefficients, decayed by every gate of the window
+        const half_t* kt = reinterpret_cast<const half_t*>(&ktw);
+        float ck = 0.f, cq = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float ej = static_cast<float>(kt[e]) * (Gall * gr);
+            ck += ej * bfe(kcw, e);
+            cq += ej * bfe(qcw, e);
+        }
+        ck = row16_sum(ck);
+        cq = row16_sum(cq);
+        if (ch == 0) ctok[grp] = f32x2{ck, cq};
+    }
+    if (first) {
+        const float c0 = cr * Gall * gr;  // c_r Gamma_{1:l} at row r
+        rowv[r] = f32x2{c0 * kr, c0 * qr};
+        const float kq = wave_sum(kr * qr);
+        if (lane == 0) kq_part[wave] = kq;
+    }
+    __syncthreads();
+
+    // ---- payload sweep, scaled per column; then token and record terms
+    f32x4 p1 = {0.f, 0.f, 0.f, 0.f}, p2 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int it = 0; it < kRowsPerThread; ++it) {
+        const f32x2 rv = rowv[lq_row(it, wave, ro)];
+        const f32x4 zf = unpack_codes(zw[it]);
+        p1 += zf * rv.x;
+        p2 += zf * rv.y;
+    }
+    p1 *= bsc;
+    p2 *= bsc;
+    if (owner < kTok) {
+        const half_t* ut = reinterpret_cast<const half_t*>(&utw);
+        const f32x4 u = {static_cast<float>(ut[0]), static_cast<float>(ut[1]), static_cast<float>(ut[2]),
+                         static_cast<float>(ut[3])};
+        const f32x2 c = ctok[owner];
+        p1 += u * c.x;
+        p2 += u * c.y;
+    }
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+        if (8 * m >= pos) continue;
+        const int j = owner + 8 * m;
+        const f32x2 c = j < pos ? coef[j] : f32x2{0.f, 0.f};
+        p1 += ur[m] * c.x;
+        p2 += ur[m] * c.y;
+    }
+    p1 = f32x4{add_xor32(p1.x), add_xor32(p1.y), add_xor32(p1.z), add_xor32(p1.w)};
+    p2 = f32x4{add_xor32(p2.x), add_xor32(p2.y), add_xor32(p2.z), add_xor32(p2.w)};
+    if (ro == 0) {
+        red[wave][4 * c4 + 0] = f32x2{p1.x, p2.x};
+        red[wave][4 * c4 + 1] = f32x2{p1.y, p2.y};
+        red[wave][4 * c4 + 2] = f32x2{p1.z, p2.z};
+        red[wave][4 * c4 + 3] = f32x2{p1.w, p2.w};
+    }
+    __syncthreads();
+
+    if (first) {
+        const int c = tid;
+        const f32x2 acc = red[0][c] + red[1][c] + red[2][c] + red[3][c];
+        const float kq = kq_part[0] + kq_part[1];
+        const float u = bt * (vr - acc.x);
+        y[vec_off + c] = acc.y + u * kq;
+        const size_t rec = rec0 + static_cast<size_t>(pos) * kD;
+        Ubuf[rec + c] = u;
+        store_in(Kbuf, rec + c, kr);
+        if (c == 0) Gbuf[static_cast<size_t>(h) * W + pos] = gr;
+    }
+}
+
+// ---------------------------------------------------------------- the window's last step
+// The step as in the per-row bf16 boundary (column-owner record terms, scaled records
+// staged transposed for the bf16-split MFMA), with the payload terms scaled by B and c
+// and the token pairs added; then S_W is formed on the matrix cores (payload init, the
+// records' two bf16 MFMAs per tile, the tokens' one fp32 MFMA per tile), staged in LDS,
+// and refitted. Dynamic LDS is one region used twice: first for the step and the
+// contraction operands, then (after a barrier) for the refit.
+constexpr int kZsStride = kD / 4 + 1;
+// floats of the step-phase region: Kt (4 KB), Ut (12 KB), Zs, Ktok, Utok, red, recp
+constexpr int kStepFloats = 2 * kD * 4 + 3 * 2 * kD * 4 + kD * kZsStride + 2 * kTok * kD + 4 * kD * 2 + kD * 2;
+constexpr int kLqBoundaryFloats = kRefitFloats > kStepFloats ? kRefitFloats : kStepFloats;
+static_assert(kStepFloats <= kD * kD, "the step-phase region must lie inside the refit's state region");
+
+__device__ __forceinline__ void split3_bf16(float x, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
+    const __bf16 a = static_cast<__bf16>(x);
+    const float r1 = x - static_cast<float>(a);
+    const __bf16 b = static_cast<__bf16>(r1);
+    const float r2 = r1 - static_cast<float>(b);
+    const __bf16 c = static_cast<__bf16>(r2);
+    hi = __builtin_bit_cast(uint16_t, a);
+    mid = __builtin_bit_cast(uint16_t, b);
+    lo = __builtin_bit_cast(uint16_t, c);
+}
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+__global__ __launch_bounds__(kThreads) void lq_boundary_kernel(
+    int W, int pos, int n_iter, int8_t* __restrict__ Z, float* __restrict__ Bcol, float* __restrict__ Csm,
+    half_t* __restrict__ Kc, half_t* __restrict__ Uc, const bf16_t* __restrict__ Kbuf,
+    const float* __restrict__ Ubuf, const float* __restrict__ Gbuf, const bf16_t* __restrict__ q,
+    const bf16_t* __restrict__ k, const bf16_t* __restrict__ v, const float* __restrict__ gate,
+    const float* __restrict__ beta, float* __restrict__ y) {
+    constexpr int kRec = 16;
+    extern __shared__ float dyn_lds[];
+    __shared__ f32x2 rowv[kD];
+    __shared__ f32x2 coef[kRec];
+    __shared__ f32x2 ctok[kTok];
+    __shared__ float kq_part[2];
+    __shared__ float zcoef[kD];
+    __shared__ float gam[kRec];
+
+    // step-phase views of the dynamic region
+    u32x4* Kt = reinterpret_cast<u32x4*>(dyn_lds);                 // [2][128]
+    u32x4* Ut = Kt + 2 * kD;                                        // [3][2][128]
+    uint32_t* Zs = reinterpret_cast<uint32_t*>(Ut + 3 * 2 * kD);   // [128][33]
+    float* Ktok = reinterpret_cast<float*>(Zs + kD * kZsStride);   // [4][128]
+    float* Utok = Ktok + kTok * kD;                                 // [4][128], scaled by Gamma_{1:W}
+    f32x2* red = reinterpret_cast<f32x2*>(Utok + kTok * kD);       // [4][128]
+    f32x2* recp = red + 4 * kD;                                     // [128]
+    // refit views (the state region overlaps every step-phase array above)
+    const RefitLds L(dyn_lds);
+    float* bscs = L.sc;   // B / 127 of the old payload, until the refit writes the new scales
+
+    const int h = head_of_block(blockIdx.x, gridDim.x), tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
+    const int c4 = lane & 31, ro = lane >> 5;
+    const int grp = tid >> 4, ch = tid & 15;
+    const int cc = tid & (kD - 1), half = tid >> 7;
+    const size_t vec_off = static_cast<size_t>(h) * kD;
+    const size_t rec0 = static_cast<size_t>(h) * W * kD;
+    const size_t tok0 = static_cast<size_t>(h) * kTok * kD;
+    const bool first = tid < kD;
+
+    // ---- loads
+    uint32_t kcr[4] = {0u, 0u, 0u, 0u};
+    if (0 < pos) {
+        const uint4 x = *reinterpret_cast<const uint4*>(Kbuf + rec0 + static_cast<size_t>(grp < pos ? grp : 0) * kD + 8 * ch);
+        kcr[0] = x.x; kcr[1] = x.y; kcr[2] = x.z; kcr[3] = x.w;
+    }
+    float ucol[8];
+    uint32_t kcol[4];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const int j = 8 * half + e;
+        const size_t at = rec0 + static_cast<size_t>(j < pos ? j : 0) * kD + cc;
+        ucol[e] = j < pos ? Ubuf[at] : 0.f;
+        const uint32_t kb = j < pos ? static_cast<uint32_t>(Kbuf[at]) : 0u;
+        kcol[e >> 1] = (e & 1) ? (kcol[e >> 1] | (kb << 16)) : kb;
+    }
+    uint4 ktw = {0u, 0u, 0u, 0u};
+    if (grp < kTok) ktw = *reinterpret_cast<const uint4*>(Kc + tok0 + grp * kD + 8 * ch);
+    // token t at row / column cc (threads < 128: keys; threads >= 128: values)
+    half_t tokv[kTok];
+#pragma unroll
+    for (int t = 0; t < kTok; ++t) tokv[t] = (first ? Kc : Uc)[tok0 + t * kD + cc];
+    const float g_lane = lane < pos ? Gbuf[static_cast<size_t>(h) * W + lane] : 1.f;
+    const uint4 kchw = *reinterpret_cast<const uint4*>(k + vec_off + 8 * ch);
+    const uint4 qchw = *reinterpret_cast<const uint4*>(q + vec_off + 8 * ch);
+    const float kr = load_in(k, vec_off + cc), qr = load_in(q, vec_off + cc);
+    const float gr = gate[h];
+    const float cr = Csm[vec_off + cc];
+    const float bcc = Bcol[vec_off + cc];
+    const float vr = load_in(v, vec_off + cc);
+    const float bt = beta[h];
+    uint32_t* Zh = reinterpret_cast<uint32_t*>(Z + static_cast<size_t>(h) * kD * kD);
+    uint32_t zw[kRowsPerThread];
+#pragma unroll
+    for (int it = 0; it < kRowsPerThread; ++it)
+        zw[it] = __builtin_nontemporal_load(Zh + lq_row(it, wave, ro) * (kD / 4) + c4);
+
+    // ---- gate products (newest first): after record grp, after record = lane, all
+    float Gg = 1.f, Gl = 1.f, Gall = 1.f;
+    for (int i = pos - 1; i >= 0; --i) {
+        const float gi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, g_lane), i));
+        Gg = i > grp ? Gg * gi : Gg;
+        Gl = i > lane ? Gl * gi : Gl;
+        Gall *= gi;
+    }
+    const float gam_all = Gall * gr;  // Gamma_{1:W}
+    if (wave == 0 && lane < kRec) gam[lane] = lane < pos ? Gl * gr : 1.f;
+    const uint32_t kcw[4] = {kchw.x, kchw.y, kchw.z, kchw.w};
+    const uint32_t qcw[4] = {qchw.x, qchw.y, qchw.z, qchw.w};
+    auto bfe = [](const uint32_t (&w)[4], int e) {
+        return (e & 1) ? __uint_as_float(w[e >> 1] & 0xffff0000u) : __uint_as_float(w[e >> 1] << 16);
+    };
+    if (0 < pos) {
+        float ck = 0.f, cq = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float ej = bfe(kcr, e) * (Gg * gr);
+            ck += ej * bfe(kcw, e);
+            cq += ej * bfe(qcw, e);
+        }
+        ck = row16_sum(ck);
+        cq = row16_sum(cq);
+        if (ch == 0 && grp < pos) coef[grp] = f32x2{ck, cq};
+    }
+    if (wave == 0) {
+        const half_t* kt = reinterpret_cast<const half_t*>(&ktw);
+        float ck = 0.f, cq = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float ej = static_cast<float>(kt[e]) * gam_all;
+            ck += ej * bfe(kcw, e);
+            cq += ej * bfe(qcw, e);
+        }
+        ck = row16_sum(ck);
+        cq = row16_sum(cq);
+        if (ch == 0) ctok[grp] = f32x2{ck, cq};
+    }
+    if (first) {
+        const float c0 = cr * gam_all;
+        rowv[cc] = f32x2{c0 * kr, c0 * qr};
+        zcoef[cc] = c0;
+        bscs[cc] = bcc * (1.f / 127.f);
+        const float kq = wave_sum(kr * qr);
+        if (lane == 0) kq_part[wave] = kq;
+    }
+    // token operands of the contraction, and the unscaled values as the refit's start
+#pragma unroll
+    for (int t = 0; t < kTok; ++t) {
+        const float x = static_cast<float>(tokv[t]);
+        if (first) Ktok[t * kD + cc] = x;
+        else Utok[t * kD + cc] = x * gam_all;
+    }
+    if (!first) L.W[cc] = f32x4{static_cast<float>(tokv[0]), static_cast<float>(tokv[1]),
+                                static_cast<float>(tokv[2]), static_cast<float>(tokv[3])};
+    Kt[half * kD + cc] = u32x4{kcol[0], kcol[1], kcol[2], kcol[3]};
+    __syncthreads();
+
+    // ---- payload sweep; record terms per column; scaled records staged for the MFMA
+    f32x4 p1 = {0.f, 0.f, 0.f, 0.f}, p2 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int it = 0; it < kRowsPerThread; ++it) {
+        const f32x2 rvv = rowv[lq_row(it, wave, ro)];
+        const f32x4 zf = unpack_codes(zw[it]);
+        p1 += zf * rvv.x;
+        p2 += zf * rvv.y;
+    }
+    f32x2 rp = {0.f, 0.f};
+    u32x4 part[3];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const int j = 8 * half + e;
+        const f32x2 c = j < pos ? coef[j] : f32x2{0.f, 0.f};
+        rp += c * ucol[e];
+        uint32_t hi, mid, lo;
+        split3_bf16(gam[j] * ucol[e], hi, mid, lo);
+        const int sh = 16 * (e & 1);
+        part[0][e >> 1] = (e & 1) ? (part[0][e >> 1] | (hi << sh)) : hi;
+        part[1][e >> 1] = (e & 1) ? (part[1][e >> 1] | (mid << sh)) : mid;
+        part[2][e >> 1] = (e & 1) ? (part[2][e >> 1] | (lo << sh)) : lo;
+    }
+#pragma unroll
+    for (int pp = 0; pp < 3; ++pp) Ut[(pp * 2 + half) * kD + cc] = part[pp];
+    p1 = f32x4{add_xor32(p1.x), add_xor32(p1.y), add_xor32(p1.z), add_xor32(p1.w)};
+    p2 = f32x4{add_xor32(p2.x), add_xor32(p2.y), add_xor32(p2.z), add_xor32(p2.w)};
+    if (ro == 0) {
+        red[wave * kD + 4 * c4 + 0] = f32x2{p1.x, p2.x};
+        red[wave * kD + 4 * c4 + 1] = f32x2{p1.y, p2.y};
+        red[wave * kD + 4 * c4 + 2] = f32x2{p1.z, p2.z};
+        red[wave * kD + 4 * c4 + 3] = f32x2{p1.w, p2.w};
+    }
+    if (half == 1) recp[cc] = rp;
+#pragma unroll
+    for (int it = 0; it < kRowsPerThread; ++it) Zs[lq_row(it, wave, ro) * kZsStride + c4] = zw[it];
+    __syncthreads();
+
+    // ---- correction and output; the current record joins the contraction operands
+    if (first) {
+        const int c = cc;
+        f32x2 acc = (red[c] + red[kD + c] + red[2 * kD + c] + red[3 * kD + c]) * bscs[c];
+        acc += rp + recp[c];
+        const f32x4 ut = L.W[c];
+        acc += ctok[0] * ut.x + ctok[1] * ut.y + ctok[2] * ut.z + ctok[3] * ut.w;
+        const float kq = kq_part[0] + kq_part[1];
+        const float u = bt * (vr - acc.x);
+        y[vec_off + c] = acc.y + u * kq;
+        uint32_t uh, um, ul;
+        split3_bf16(u, uh, um, ul);
+        reinterpret_cast<uint16_t*>(&Ut[(0 * 2 + (pos >> 3)) * kD + c])[pos & 7] = static_cast<uint16_t>(uh);
+        reinterpret_cast<uint16_t*>(&Ut[(1 * 2 + (pos >> 3)) * kD + c])[pos & 7] = static_cast<uint16_t>(um);
+        reinterpret_cast<uint16_t*>(&Ut[(2 * 2 + (pos >> 3)) * kD + c])[pos & 7] = static_cast<uint16_t>(ul);
+        reinterpret_cast<uint16_t*>(&Kt[(pos >> 3) * kD + c])[pos & 7] = static_cast<uint16_t>(__float_as_uint(kr) >> 16);
+    }
+    __syncthreads();
+
+    // ---- S_W on the matrix cores, both bands of the wave's 32 rows held in registers.
+    // Lane l holds, in tile ct of band a, key row 32w + 16a + l%16 and value columns
+    // 16ct + 4(l/16) .. +3 (result layout of v_mfma_f32_16x16x{32_bf16,4f32}).
+    const int lr = lane & 15, lq = lane >> 4, blk = lq & 1;
+    f32x4 acc[2][8];
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+        const int row = 16 * (2 * wave + a) + lr;
+        const bf16x8 bv = __builtin_bit_cast(bf16x8, Kt[blk * kD + row]);
+        const float zc = zcoef[row];
+        const float bk = Ktok[lq * kD + row];
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct) {
+            const f32x4 bs = *reinterpret_cast<const f32x4*>(bscs + 16 * ct + 4 * lq);
+            acc[a][ct] = unpack_codes(Zs[row * kZsStride + 4 * ct + lq]) * (bs * zc);
+            const int col = 16 * ct + lr;
+            const bf16x8 a1 = __builtin_bit_cast(bf16x8, Ut[((lq < 2 ? 0 : 1) * 2 + blk) * kD + col]);
+            const u32x4 lo = Ut[(2 * 2 + blk) * kD + col];
+            const bf16x8 a2 = __builtin_bit_cast(bf16x8, lq < 2 ? lo : u32x4{0u, 0u, 0u, 0u});
+            acc[a][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, bv, acc[a][ct], 0, 0, 0);
+            acc[a][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a2, bv, acc[a][ct], 0, 0, 0);
+            acc[a][ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(Utok[lq * kD + col], bk, acc[a][ct], 0, 0, 0);
+        }
+    }
+    __syncthreads();  // every read of the step-phase arrays is done: the region becomes S
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+        const int row = 16 * (2 * wave + a) + lr;
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) L.S[swz(row, 16 * ct + 4 * lq + i)] = acc[a][ct][i];
+    }
+    __syncthreads();
+    lq_refit(L, n_iter, tid, Zh, Bcol + vec_off, Csm + vec_off, Kc + tok0, Uc + tok0);
+}
+
+// ---------------------------------------------------------------- launchers
+static hipError_t set_lds(const void* fn, int floats) {
+    return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
+                               static_cast<int>(sizeof(float) * floats));
+}
+
+hipError_t launch_lq_quantize(int heads, const float* S, int n_iter, int8_t* Z, float* B, float* C,
+                              void* Kc, void* Uc, hipStream_t stream) {
+    static const hipError_t attr = set_lds(reinterpret_cast<const void*>(lq_quantize_kernel), kRefitFloats);
+    if (attr != hipSuccess) return attr;
+    hipLaunchKernelGGL(lq_quantize_kernel, dim3(heads), dim3(kThreads), sizeof(float) * kRefitFloats, stream,
+                       S, n_iter, Z, B, C, static_cast<half_t*>(Kc), static_cast<half_t*>(Uc));
+    return hipGetLastError();
+}
+
+hipError_t launch_lq_window(const StepArgs& a, const LqArgs& w, hipStream_t stream) {
+    if (w.pos == w.W - 1) {
+        static const hipError_t attr = set_lds(reinterpret_cast<const void*>(lq_boundary_kernel), kLqBoundaryFloats);
+        if (attr != hipSuccess) return attr;
+        hipLaunchKernelGGL(lq_boundary_kernel, dim3(a.heads), dim3(kThreads), sizeof(float) * kLqBoundaryFloats,
+                           stream, w.W, w.pos, w.n_iter, w.Z, w.B, w.C, static_cast<half_t*>(w.Kc),
+                           static_cast<half_t*>(w.Uc), static_cast<const bf16_t*>(w.Kbuf), w.Ubuf, w.Gbuf,
+                           static_cast<const bf16_t*>(a.q), static_cast<const bf16_t*>(a.k),
+                           static_cast<const bf16_t*>(a.v), a.gate, a.beta, a.y);
+        return hipGetLastError();
+    }
+    hipLaunchKernelGGL(lq_step_kernel, dim3(a.heads), dim3(kThreads), 0, stream, w.W, w.pos, w.Z, w.B, w.C,
+                       static_cast<const half_t*>(w.Kc), static_cast<const half_t*>(w.Uc),
+                       static_cast<bf16_t*>(w.Kbuf), w.Ubuf, w.Gbuf, static_cast<const bf16_t*>(a.q),
+                       static_cast<const bf16_t*>(a.k), static_cast<const bf16_t*>(a.v), a.gate, a.beta, a.y);
+    return hipGetLastError();
+}
+
+}  // namespace rsu

@@ -200,6 +200,113 @@ def run_log_slots(w: wl.Workload, sample: int | None = None, steps: int | None =
     return err
 
 
+def new_lq_buffers(w: wl.Workload):
+    B, H, W = w.B, w.H, w.W
+    return {
+        "Z": torch.zeros(B, H, 128, 128, device=DEV, dtype=torch.int8),
+        "B": torch.zeros(B, H, 128, device=DEV),
+        "C": torch.zeros(B, H, 128, device=DEV),
+        "Kc": torch.zeros(B, H, 4, 128, device=DEV, dtype=torch.float16),
+        "Uc": torch.zeros(B, H, 4, 128, device=DEV, dtype=torch.float16),
+        "Kbuf": torch.zeros(B, H, W, 128, device=DEV, dtype=qkv_dtype(w)),
+        "Ubuf": torch.zeros(B, H, W, 128, device=DEV),
+        "Gbuf": torch.zeros(B, H, W, device=DEV),
+    }
+
+
+def lq_host(buf, hd):
+    """The GPU's representation of the sampled heads: Z, B, c, and the tokens as [n, 128, 4]."""
+    Z = take(buf["Z"], hd, (128, 128)).astype(np.int64)
+    Bc = take(buf["B"], hd, (128,)).astype(np.float64)
+    C = take(buf["C"], hd, (128,)).astype(np.float64)
+    K16 = np.transpose(take(buf["Kc"].float(), hd, (4, 128)), (0, 2, 1)).astype(np.float64)
+    U16 = np.transpose(take(buf["Uc"].float(), hd, (4, 128)), (0, 2, 1)).astype(np.float64)
+    return Z, Bc, C, K16, U16
+
+
+def check_lq_refit(S_ref, V0, n_iter, rep, err, tie_band=1e-3, mat_rel=1e-6):
+    """Teacher-forced check of one refit.
+
+    Tokens: against the oracle's fit of the same state from the same start (the
+    product K U^T, each key token, each value-vector entry; fp16 rounding level).
+    Residual pieces: recomputed by the oracle from the GPU's own fp16 tokens. The
+    residual R = S - K U^T cancels most of S where the tokens sit (the outlier rows
+    and columns), so the GPU's fp32 state error, relative to the uncancelled
+    magnitude m = |S| + |K U^T|, is what the GPU's c and B inherit: their errors are
+    measured against m (mean of m per row for c^2, max of m / c per column for B).
+    Codes are recomputed from the GPU's own c and B; a code may differ by 1 only where
+    the exact code lies within 1e-3 LSB of a tie, widened by mat_rel * m in LSB units."""
+    from oracle import lq as lqo
+    Z, Bc, C, K16, U16 = rep
+    for i in range(S_ref.shape[0]):
+        K, U = lqo.fit(S_ref[i], V0[i], n_iter)
+        Kr, Ur = lqo.to_fp16(K), lqo.to_fp16(U)
+        Pg, Pr = K16[i] @ U16[i].T, Kr @ Ur.T
+        err["tok"] = max(err["tok"], float(np.linalg.norm(Pg - Pr) / max(np.linalg.norm(Pr), 1e-300)))
+        kmax = max(np.linalg.norm(Kr, axis=0).max(), 1e-300)
+        err["tok_k"] = max(err["tok_k"], float(np.linalg.norm(K16[i] - Kr, axis=0).max() / kmax))
+        err["tok_u"] = max(err["tok_u"], float(np.abs(U16[i] - Ur).max()))
+        R = S_ref[i] - Pg
+        mag = np.abs(S_ref[i]) + np.abs(Pg)
+        c_ref = np.maximum(np.sqrt(np.mean(np.abs(R), axis=1)), lqo.C_FLOOR)
+        err["c"] = max(err["c"], float(np.max(np.abs(C[i] ** 2 - c_ref ** 2) / np.mean(mag, axis=1))))
+        X = R / C[i][:, None]
+        B_ref = np.max(np.abs(X), axis=0)
+        xmag = np.max(mag / C[i][:, None], axis=0)
+        err["B"] = max(err["B"], float(np.max(np.abs(Bc[i] - B_ref) / np.maximum(xmag, 1e-300))))
+        nz = Bc[i] > 0
+        w = np.zeros_like(X)
+        w[:, nz] = X[:, nz] * 127.0 / Bc[i][nz][None, :]
+        Zr = np.clip(np.rint(w), -127, 127).astype(np.int64)
+        dz = np.abs(Z[i] - Zr)
+        err["z_maxdiff"] = max(err["z_maxdiff"], int(dz.max()))
+        flips = dz > 0
+        err["z_flips"] += int(flips.sum())
+        band = np.full_like(w, tie_band)
+        band[:, nz] += mat_rel * 127.0 * (mag[:, nz] / C[i][:, None]) / Bc[i][nz][None, :]
+        near = np.abs(np.abs(w - np.floor(w)) - 0.5) < band
+        err["z_flips_outside_band"] += int((flips & ~near).sum())
+
+
+def run_lq(w: wl.Workload, n_iter: int = 1, n_iter0: int = 8, sample: int | None = None,
+           steps: int | None = None):
+    """LeapQuant's format on the GPU against the oracle, teacher-forced per window: the
+    conversion of the initial state, every in-window output against dense decoding from
+    the GPU's window-start representation, and every boundary refit."""
+    from oracle import lq as lqo
+    m = rsu()
+    B, H, W = w.B, w.H, w.W
+    steps = w.steps if steps is None else steps
+    S0 = wl.initial_state(w)
+    heads = np.arange(w.heads) if sample is None else wl.sample_heads(w, sample)
+    hd = torch.from_numpy(heads).to(DEV)
+    buf = new_lq_buffers(w)
+    Sd = torch.from_numpy(S0).to(DEV).view(B, H, 128, 128)
+    m.gdn_lq_quantize(Sd, n_iter0, buf["Z"], buf["B"], buf["C"], buf["Kc"], buf["Uc"])
+    err = {"y": 0.0, "tok": 0.0, "tok_k": 0.0, "tok_u": 0.0, "c": 0.0, "B": 0.0, "z_maxdiff": 0,
+           "z_flips": 0, "z_flips_outside_band": 0, "boundaries": 0}
+    S_ref = S0[heads].astype(np.float64)
+    del Sd, S0
+    walsh = np.broadcast_to(lqo.walsh_start(), (len(heads), 128, 4))
+    check_lq_refit(S_ref, walsh, n_iter0, lq_host(buf, hd), err)
+    y = torch.empty(B, H, 128, device=DEV)
+    for t0 in range(0, steps, W):
+        rep = lq_host(buf, hd)
+        S = np.stack([lqo.represent(rep[0][i], rep[1][i], rep[2][i], rep[3][i], rep[4][i])
+                      for i in range(len(heads))])
+        n = min(W, steps - t0)
+        for pos in range(n):
+            x, d = dev_inputs(w, t0 + pos)
+            m.gdn_lq_window(W, pos, n_iter, buf["Z"], buf["B"], buf["C"], buf["Kc"], buf["Uc"], buf["Kbuf"],
+                            buf["Ubuf"], buf["Gbuf"], d["q"], d["k"], d["v"], d["gate"], d["beta"], y)
+            y_ref = oracle.dense_step(S, *host_slice(x, heads))
+            err["y"] = max(err["y"], rel_err(take(y, hd, (128,)), y_ref))
+        if n == W:
+            check_lq_refit(S, rep[4], n_iter, lq_host(buf, hd), err)
+            err["boundaries"] += 1
+    return err
+
+
 def new_window_buffers(w: wl.Workload):
     B, H, W = w.B, w.H, w.W
     return {

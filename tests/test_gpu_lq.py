@@ -1,0 +1,63 @@
+"""GPU parity of LeapQuant's window-boundary format (compensator tokens, residual
+smoothing, per-value-channel int8; eq. 10 readout) against the fp64 oracle, teacher-forced
+per window (the oracle restarts from the GPU's representation at every window start and
+recomputes each refit's payload from the GPU's own fp16 tokens).
+
+Bars: outputs within 1e-4 norm-wise relative error; the token product Kt Ut^T within
+2e-3 (fp16 rounding of the tokens, 2^-11, plus fp32 iteration error), each key token
+within 4e-3 of the largest and each value-vector entry within 2e-3 absolute; c^2 and B
+within 1e-5 of the uncancelled magnitude |S| + |Kt Ut^T| they are computed from (the
+residual cancels the outliers the tokens hold, which amplifies the fp32 state's
+rounding relative to the residual itself); payload codes, recomputed from the GPU's c
+and B, within 1 LSB and different only near a rounding tie (1e-3 LSB plus the fp32
+error of the uncancelled value, 1e-6 of it, in LSB units)."""
+import numpy as np
+import pytest
+import torch
+
+import workloads as wl
+from parity import DEV, TOL_Q8, lq_host, new_lq_buffers, rsu, run_lq, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _check(err, name, boundaries=True):
+    say(f"[lq] {name}: {err}")
+    assert err["y"] < TOL_Q8
+    assert err["tok"] < 2e-3 and err["tok_k"] < 4e-3 and err["tok_u"] < 2e-3
+    assert err["c"] < 1e-5 and err["B"] < 1e-5
+    assert err["z_maxdiff"] <= 1 and err["z_flips_outside_band"] == 0
+    if boundaries:
+        assert err["boundaries"] > 0
+
+
+@pytest.mark.parametrize("W,B,H,n_iter", [(16, 2, 5, 1), (16, 3, 4, 2), (5, 2, 3, 1), (1, 2, 2, 0),
+                                          (16, 10, 10, 1)])
+def test_lq_windows_small(W, B, H, n_iter):
+    w = wl.custom(wl.WORKLOADS[6], B=B, H=H, W=W, steps=2 * W + min(W, 3))
+    _check(run_lq(w, n_iter=n_iter), f"W={W} B={B} H={H} n_iter={n_iter}")
+
+
+@pytest.mark.parametrize("n_iter0", [0, 3])
+def test_lq_quantize_start_iterations(n_iter0):
+    w = wl.custom(wl.WORKLOADS[6], B=2, H=3, W=16, steps=0)
+    _check(run_lq(w, n_iter0=n_iter0, steps=0), f"quantize n_iter0={n_iter0}", boundaries=False)
+
+
+def test_lq_zero_state_gives_zero_tokens_and_payload():
+    m = rsu()
+    S = torch.zeros(1, 2, 128, 128, device=DEV)
+    w = wl.custom(wl.WORKLOADS[6], B=1, H=2, W=16)
+    buf = new_lq_buffers(w)
+    buf["C"].fill_(7.0)
+    m.gdn_lq_quantize(S, 4, buf["Z"], buf["B"], buf["C"], buf["Kc"], buf["Uc"])
+    assert not buf["Z"].any() and not buf["B"].any() and not buf["Kc"].any()
+    np.testing.assert_array_equal(buf["C"].cpu().numpy(), np.float32(1e-6))
+
+
+def test_lq_b256_h48_full_size_sampled():
+    """The int8 workload's inputs (B=256, H=48, W=16) in LeapQuant's format, 64 sampled
+    heads, 3 windows, one warm-started iteration per refit."""
+    w = wl.WORKLOADS[6]
+    say(f"[lq] {w.name}: full size, 64 sampled heads, 48 steps")
+    _check(run_lq(w, n_iter=1, sample=64, steps=48), w.name)

@@ -37,7 +37,7 @@ class Workload:
     cid: int
     name: str
     variant: str          # "gdn" (scalar gate alpha) or "kda" (per-key gate d)
-    path: str             # "dense", "q8_window" or "log"
+    path: str             # "dense", "q8_window", "lq_window" or "log"
     B: int
     H: int
     steps: int
@@ -69,6 +69,9 @@ WORKLOADS = {
     4: Workload(4, "gdn_q8_window_b256_h48_w16", "gdn", "q8_window", 256, 48, 256, "bf16",
                 0.90, 0.999, W=16, outliers=True),
     5: Workload(5, "gdn_log_b256_h48_m8", "gdn", "log", 256, 48, 128, "bf16", 0.90, 0.999, M=8),
+    # LeapQuant's boundary format on the int8 workload's own inputs (same seed as 4)
+    6: Workload(4, "gdn_lq_window_b256_h48_w16", "gdn", "lq_window", 256, 48, 256, "bf16",
+                0.90, 0.999, W=16, outliers=True),
 }
 
 
