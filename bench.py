@@ -39,7 +39,8 @@ KERNEL_SOURCES = {
               "recurrent_state_update_head_amd/csrc/rsu_device.hpp"],
 }
 
-WORKLOAD_BY_FLAG = {"gdn": 2, "gdn_small": 1, "kda": 3, "q8": 4, "log": 5}
+WORKLOAD_BY_FLAG = {"gdn": 2, "gdn_small": 1, "kda": 3, "q8": 4, "log": 5, "lq": 6}
+LQ_TOKENS = 4
 
 
 # ----------------------------------------------------------------- byte accounting
@@ -65,6 +66,19 @@ def window_step_bytes_per_head(w: wl.Workload, pos: int) -> int:
     inputs = 3 * d * _in_bytes(w) + 4 * gdim + 4
     rd = d * d + 4 * d + pos * rec + inputs
     wr = 4 * d + ((d * d + 4 * d) if pos == w.W - 1 else rec)
+    return rd + wr
+
+
+def lq_step_bytes_per_head(w: wl.Workload, pos: int) -> int:
+    """LeapQuant-format window step at position pos: payload codes, per-column absmax and
+    per-row smoothing scales, the fp16 token pairs, the pos records, the step inputs, y,
+    and either the record write or (at the boundary) the whole new representation."""
+    d = wl.DK
+    rec = d * _in_bytes(w) + 4 * d + 4
+    inputs = 3 * d * _in_bytes(w) + 4 + 4
+    rep = d * d + 4 * d + 4 * d + 2 * LQ_TOKENS * d * 2
+    rd = rep + pos * rec + inputs
+    wr = 4 * d + (rep if pos == w.W - 1 else rec)
     return rd + wr
 
 
@@ -102,6 +116,8 @@ def cycle_bytes_per_head(w: wl.Workload) -> float:
         return float(dense_bytes_per_head(w))
     if w.path == "q8_window":
         return sum(window_step_bytes_per_head(w, p) for p in range(w.W)) / w.W
+    if w.path == "lq_window":
+        return sum(lq_step_bytes_per_head(w, p) for p in range(w.W)) / w.W
     return sum(log_step_bytes_per_head(w, L) for L in range(w.M)) / w.M
 
 
@@ -168,12 +184,12 @@ def copy_ceiling(torch, rsu, nbytes: int, reps: int = 10) -> float:
     return 2 * n * 4 / sec / 1e9
 
 
-def run_gpu(w: wl.Workload, steps: int, warmup: int, slots: bool = False):
+def run_gpu(w: wl.Workload, steps: int, warmup: int, slots: bool = False, n_iter: int = 1):
     import torch
     import recurrent_state_update_head_amd as rsu
     dev = "cuda"
     B, H = w.B, w.H
-    n_inputs = {"dense": w.steps, "q8_window": w.W, "log": w.M}[w.path]
+    n_inputs = {"dense": w.steps, "q8_window": w.W, "lq_window": w.W, "log": w.M}[w.path]
     n_inputs = min(n_inputs, max(1, w.steps))
     x = _dev_inputs(w, n_inputs, torch, dev)
     y = torch.empty(B, H, 128, device=dev)
@@ -204,6 +220,25 @@ def run_gpu(w: wl.Workload, steps: int, warmup: int, slots: bool = False):
             t = state["t"]
             i = t % n_inputs
             fn(W, t % W, Z, A, Kb, Ub, Gb, x["q"][i], x["k"][i], x["v"][i], x["gate"][i], x["beta"][i], y)
+            state["t"] += 1
+    elif w.path == "lq_window":
+        W = w.W
+        Z = torch.empty(B, H, 128, 128, device=dev, dtype=torch.int8)
+        Bc = torch.empty(B, H, 128, device=dev)
+        Cs = torch.empty(B, H, 128, device=dev)
+        Kc = torch.empty(B, H, LQ_TOKENS, 128, device=dev, dtype=torch.float16)
+        Uc = torch.empty_like(Kc)
+        rsu.gdn_lq_quantize(S0, 8, Z, Bc, Cs, Kc, Uc)
+        del S0
+        Kb = torch.zeros(B, H, W, 128, device=dev, dtype=x["q"].dtype)
+        Ub = torch.zeros(B, H, W, 128, device=dev)
+        Gb = torch.zeros(B, H, W, device=dev)
+
+        def step():
+            t = state["t"]
+            i = t % n_inputs
+            rsu.gdn_lq_window(W, t % W, n_iter, Z, Bc, Cs, Kc, Uc, Kb, Ub, Gb, x["q"][i], x["k"][i], x["v"][i],
+                              x["gate"][i], x["beta"][i], y)
             state["t"] += 1
     else:
         C = w.M - 1
@@ -244,7 +279,7 @@ def run_gpu(w: wl.Workload, steps: int, warmup: int, slots: bool = False):
     if w.path != "dense":
         # one untimed pass over whole cycles with an event between consecutive launches:
         # average launch time per window position / per live log length
-        cyc = w.W if w.path == "q8_window" else w.M
+        cyc = w.W if w.path in ("q8_window", "lq_window") else w.M
         evs = [torch.cuda.Event(enable_timing=True) for _ in range(4 * cyc + 1)]
         evs[0].record(stream)
         for e in evs[1:]:
@@ -254,7 +289,7 @@ def run_gpu(w: wl.Workload, steps: int, warmup: int, slots: bool = False):
         per = [0.0] * cyc
         for i in range(4 * cyc):
             per[i % cyc] += evs[i].elapsed_time(evs[i + 1]) * 1e3 / 4
-        key = "pos" if w.path == "q8_window" else ("step" if slots else "L")
+        key = "pos" if w.path in ("q8_window", "lq_window") else ("step" if slots else "L")
         phases = {f"{key}{i}_us": round(t, 2) for i, t in enumerate(per)}
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
@@ -312,8 +347,8 @@ def override_workload(w: wl.Workload, args) -> wl.Workload:
         return w
     w2 = wl.custom(w, **ch)
     var = w2.variant
-    tail = {"dense": "", "q8_window": f"_w{w2.W}", "log": f"_m{w2.M}"}[w2.path]
-    path = {"dense": "dense", "q8_window": "q8_window", "log": "log"}[w2.path]
+    tail = {"dense": "", "q8_window": f"_w{w2.W}", "lq_window": f"_w{w2.W}", "log": f"_m{w2.M}"}[w2.path]
+    path = w2.path
     name = f"{var}_{path}_b{w2.B}_h{w2.H}{tail}" + ("_slots" if args.slots else "")
     return wl.custom(w2, name=name)
 
@@ -330,6 +365,8 @@ def main():
     ap.add_argument("--B", type=int, default=None, help="override the batch size")
     ap.add_argument("--H", type=int, default=None, help="override the heads per request")
     ap.add_argument("--M", type=int, default=None, help="log path: merge interval (1..64)")
+    ap.add_argument("--n-iter", type=int, default=1,
+                    help="lq path: subspace iterations per boundary refit (warm-started)")
     ap.add_argument("--slots", action="store_true",
                     help="log path: per-slot live lengths, every head at its own cycle point")
     args = ap.parse_args()
@@ -341,13 +378,13 @@ def main():
 
     w = wl.WORKLOADS[WORKLOAD_BY_FLAG[args.workload]]
     w = override_workload(w, args)
-    cycle = {"dense": 1, "q8_window": w.W, "log": w.M}[w.path]
+    cycle = {"dense": 1, "q8_window": w.W, "lq_window": w.W, "log": w.M}[w.path]
     steps = args.steps if args.steps is not None else 256
     steps = max(cycle, (steps + cycle - 1) // cycle * cycle)   # whole windows / cycles
     warmup = args.warmup if args.warmup is not None else 2 * cycle
     warmup = (warmup + cycle - 1) // cycle * cycle
 
-    gpu_sec, wall, ceiling, phases = run_gpu(w, steps, warmup, args.slots)
+    gpu_sec, wall, ceiling, phases = run_gpu(w, steps, warmup, args.slots, args.n_iter)
     heads = w.heads
     per_head = slots_bytes_per_head(w) if args.slots else cycle_bytes_per_head(w)
     launch_sec = gpu_sec / steps
@@ -368,9 +405,11 @@ def main():
         "dtype": "f32",
         "data": "synthetic (seeded; shapes and distributions of the workload)",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "dk": 128, "dv": 128,
-                   "qkv": w.qkv, "state": "int8+f32 scales" if w.path == "q8_window" else "f32",
+                   "qkv": w.qkv, "state": {"q8_window": "int8+f32 scales",
+                                            "lq_window": "int8+f32 scales+4 fp16 token pairs"}.get(w.path, "f32"),
                    "W": w.W or None, "M": w.M or None, "gates": w.variant,
-                   "log_phases": ("per-slot (mixed)" if args.slots else "batch-uniform") if w.path == "log" else None},
+                   "log_phases": ("per-slot (mixed)" if args.slots else "batch-uniform") if w.path == "log" else None,
+                   "refit_iterations": args.n_iter if w.path == "lq_window" else None},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
                      "algorithmic_bytes_per_launch": per_head * heads},

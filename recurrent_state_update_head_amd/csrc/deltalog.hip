@@ -52,7 +52,7 @@ __global__ __launch_bounds__(kThreads) void log_step_kernel(
     float* __restrict__ Lam, const T* __restrict__ q, const T* __restrict__ k,
     const T* __restrict__ v, const float* __restrict__ gate, const float* __restrict__ beta,
     float* __restrict__ y) {
-    extern __shared__ float dyn_lds[];
+    extern __shared__ __align__(16) float dyn_lds[];
     __shared__ f32x4 row_vec[kD];              // (E k, E q, k, E), E = exp(lbar') per key row
     __shared__ f32x2 kq_row[kD];               // (k_r, q_r)
     __shared__ f32x2 coef[kMaxC];              // per entry (Ek_m . k, Ek_m . q)

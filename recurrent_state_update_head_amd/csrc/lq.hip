@@ -42,12 +42,16 @@ __device__ __forceinline__ uint32_t lq_code(float w) {
 }
 
 // ---------------------------------------------------------------- the refit
-// LDS of the refit, in floats: the state S [128 x 128] with element (r, c) at
-// r * 128 + (c ^ (r & 63)) (the XOR spreads both row-wise and column-wise sweeps over
-// the banks), then V, Y, W, Kr, Ur [128] x f32x4 (token t of row / column i in
-// element t of entry i) and 128 per-column scales.
+// LDS of the refit, in floats: the state S [128 x 128] row-major in 16-byte units, unit
+// u of row r stored at unit u ^ f(r), f(r) = (r & 7) ^ ((r & 1) << 3); then V, Y, W, Kr,
+// Ur [128] x f32x4 (token t of row / column i in element t of entry i) and 128
+// per-column scales. The refit sweeps S in two layouts, both conflict-free with that
+// swizzle: row halves (thread 2i + h owns row i, units 16h .. 16h+15, the second half
+// starting 8 units later) and the dense step's column slabs (wave w owns columns
+// 32w .. 32w+31, lane l the 4 columns of unit 8w + (l & 7) in rows 8 it + (l >> 3)).
 constexpr int kRefitFloats = kD * kD + 5 * 4 * kD + kD;
-__device__ __forceinline__ int swz(int r, int c) { return r * kD + (c ^ (r & 63)); }
+__device__ __forceinline__ int sw_unit(int r, int u) { return u ^ ((r & 7) ^ ((r & 1) << 3)); }
+__device__ __forceinline__ int sidx(int r, int c) { return r * kD + 4 * sw_unit(r, c >> 2) + (c & 3); }
 
 struct RefitLds {
     float* S;
@@ -56,7 +60,17 @@ struct RefitLds {
     __device__ explicit RefitLds(float* base)
         : S(base), V(reinterpret_cast<f32x4*>(base + kD * kD)), Y(V + kD), W(Y + kD), Kr(W + kD),
           Ur(Kr + kD), sc(reinterpret_cast<float*>(Ur + kD)) {}
+    __device__ f32x4& unit(int r, int u) const { return reinterpret_cast<f32x4*>(S + r * kD)[sw_unit(r, u)]; }
 };
+
+__device__ __forceinline__ float max_row_lanes(float x) {
+    x = fmaxf(x, dpp<kDppRor8>(x));
+    float a, b;
+    swap16(x, a, b);
+    x = fmaxf(a, b);
+    swap32(x, a, b);
+    return fmaxf(a, b);
+}
 
 // W -> V: modified Gram-Schmidt over the 4 columns in order (wave 0; lane l holds rows
 // 2l and 2l + 1); a column with zero norm after the projections stays zero.
@@ -82,12 +96,17 @@ __device__ __forceinline__ void refit_mgs(const RefitLds& L, int wave, int lane)
     __syncthreads();
 }
 
-// Y = S V (thread (row, half) sums 64 columns; the two halves of a row are lanes 2i, 2i+1)
+// unit k of the half-row walk of thread (row, half)
+__device__ __forceinline__ int half_unit(int hf, int k) { return 16 * hf + ((k + 8 * hf) & 15); }
+
+// Y = S V over row halves (the two halves of a row are lanes 2i, 2i+1)
 __device__ __forceinline__ void refit_sv(const RefitLds& L, int rc, int hf) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int c = 0; c < 64; ++c) {
-        const int col = 64 * hf + ((c + 32 * hf) & 63);
-        acc += L.S[swz(rc, col)] * L.V[col];
+#pragma unroll 4
+    for (int k = 0; k < 16; ++k) {
+        const int u = half_unit(hf, k);
+        const f32x4 sv = L.unit(rc, u);
+        acc += sv.x * L.V[4 * u] + sv.y * L.V[4 * u + 1] + sv.z * L.V[4 * u + 2] + sv.w * L.V[4 * u + 3];
     }
     acc = f32x4{acc.x + dpp<kDppXor1>(acc.x), acc.y + dpp<kDppXor1>(acc.y), acc.z + dpp<kDppXor1>(acc.z),
                 acc.w + dpp<kDppXor1>(acc.w)};
@@ -95,16 +114,25 @@ __device__ __forceinline__ void refit_sv(const RefitLds& L, int rc, int hf) {
     __syncthreads();
 }
 
-// W = S^T Y (thread (column, half) sums 64 rows)
-__device__ __forceinline__ void refit_sty(const RefitLds& L, int rc, int hf) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int r = 0; r < 64; ++r) {
-        const int row = 64 * hf + ((r + 32 * hf) & 63);
-        acc += L.S[swz(row, rc)] * L.Y[row];
+// W = S^T Y over column slabs: 16 rows per lane, then the 8 row lanes of each column group
+__device__ __forceinline__ void refit_sty(const RefitLds& L, int wave, int lane) {
+    const int uu = 8 * wave + (lane & 7), ro = lane >> 3;
+    f32x4 acc[4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll 4
+    for (int it = 0; it < 16; ++it) {
+        const int row = 8 * it + ro;
+        const f32x4 sv = L.unit(row, uu);
+        const f32x4 yv = L.Y[row];
+        acc[0] += sv.x * yv;
+        acc[1] += sv.y * yv;
+        acc[2] += sv.z * yv;
+        acc[3] += sv.w * yv;
     }
-    acc = f32x4{acc.x + dpp<kDppXor1>(acc.x), acc.y + dpp<kDppXor1>(acc.y), acc.z + dpp<kDppXor1>(acc.z),
-                acc.w + dpp<kDppXor1>(acc.w)};
-    if (hf == 0) L.W[rc] = acc;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] = sum_row_lanes(acc[e]);
+    if (ro == 0)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) L.W[4 * uu + e] = acc[e];
     __syncthreads();
 }
 
@@ -118,7 +146,7 @@ __device__ void lq_refit(const RefitLds& L, int n_iter, int tid, uint32_t* __res
     refit_mgs(L, wave, lane);
     for (int it = 0; it < n_iter; ++it) {
         refit_sv(L, rc, hf);
-        refit_sty(L, rc, hf);
+        refit_sty(L, wave, lane);
         refit_mgs(L, wave, lane);
     }
     refit_sv(L, rc, hf);  // Kt = S V
@@ -141,57 +169,68 @@ __device__ void lq_refit(const RefitLds& L, int n_iter, int tid, uint32_t* __res
     }
     __syncthreads();
 
-    // residual R = S - Kt Ut^T in place, row smoothing c, then X = R / c in place
+    // residual R = S - Kt Ut^T in place over row halves, row smoothing c, X = R / c
     {
         const f32x4 kr = L.Kr[rc];
         float asum = 0.f;
-        for (int c = 0; c < 64; ++c) {
-            const int col = 64 * hf + ((c + 32 * hf) & 63);
-            const int p = swz(rc, col);
-            const f32x4 u = L.Ur[col];
-            const float r = L.S[p] - (kr.x * u.x + kr.y * u.y + kr.z * u.z + kr.w * u.w);
-            L.S[p] = r;
-            asum += fabsf(r);
+#pragma unroll 4
+        for (int k = 0; k < 16; ++k) {
+            const int u = half_unit(hf, k);
+            f32x4 sv = L.unit(rc, u);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const f32x4 uv = L.Ur[4 * u + e];
+                sv[e] -= kr.x * uv.x + kr.y * uv.y + kr.z * uv.z + kr.w * uv.w;
+                asum += fabsf(sv[e]);
+            }
+            L.unit(rc, u) = sv;
         }
         asum += dpp<kDppXor1>(asum);
         const float cs = fmaxf(sqrtf(asum * (1.f / kD)), kSmoothFloor);
         if (hf == 0) Ch[rc] = cs;
         const float ic = 1.f / cs;
-        for (int c = 0; c < 64; ++c) {
-            const int p = swz(rc, 64 * hf + c);
-            L.S[p] *= ic;
+#pragma unroll 4
+        for (int k = 0; k < 16; ++k) {
+            const int u = half_unit(hf, k);
+            L.unit(rc, u) = L.unit(rc, u) * ic;
         }
     }
     __syncthreads();
 
-    // per-value-channel absmax B and the code scale 127 / B
+    // per-value-channel absmax B and the code scale 127 / B, over column slabs
     {
-        float m = 0.f;
-        for (int r = 0; r < 64; ++r) {
-            const int row = 64 * hf + ((r + 32 * hf) & 63);
-            m = fmaxf(m, fabsf(L.S[swz(row, rc)]));
+        const int uu = 8 * wave + (lane & 7), ro = lane >> 3;
+        f32x4 m = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+        for (int it = 0; it < 16; ++it) {
+            const f32x4 sv = L.unit(8 * it + ro, uu);
+            m = f32x4{fmaxf(m.x, fabsf(sv.x)), fmaxf(m.y, fabsf(sv.y)), fmaxf(m.z, fabsf(sv.z)),
+                      fmaxf(m.w, fabsf(sv.w))};
         }
-        m = fmaxf(m, dpp<kDppXor1>(m));
-        if (hf == 0) {
-            Bh[rc] = m;
-            L.sc[rc] = m > 0.f ? __fdiv_rn(127.f, m) : 0.f;
-        }
-    }
-    __syncthreads();
-
-    // codes: thread (row, half) packs its 64 columns into 16 words, written over its own
-    // half-row of S (a block only this thread reads), then whole rows leave together
-    {
-        float x[64];
+        m = f32x4{max_row_lanes(m.x), max_row_lanes(m.y), max_row_lanes(m.z), max_row_lanes(m.w)};
+        if (ro == 0) {
 #pragma unroll
-        for (int c = 0; c < 64; ++c) x[c] = L.S[swz(rc, 64 * hf + c)];
+            for (int e = 0; e < 4; ++e) {
+                Bh[4 * uu + e] = m[e];
+                L.sc[4 * uu + e] = m[e] > 0.f ? __fdiv_rn(127.f, m[e]) : 0.f;
+            }
+        }
+    }
+    __syncthreads();
+
+    // codes over row halves: 16 words per thread, written over its own half-row of S
+    // (a block only this thread touches), then whole rows leave together
+    {
+        f32x4 x[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) x[j] = L.unit(rc, 16 * hf + j);
         uint32_t* Su = reinterpret_cast<uint32_t*>(L.S);
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
             const int c0 = 64 * hf + 4 * j;
-            Su[rc * kD + 64 * hf + j] = lq_code(x[4 * j] * L.sc[c0]) | (lq_code(x[4 * j + 1] * L.sc[c0 + 1]) << 8) |
-                                        (lq_code(x[4 * j + 2] * L.sc[c0 + 2]) << 16) |
-                                        (lq_code(x[4 * j + 3] * L.sc[c0 + 3]) << 24);
+            Su[rc * kD + 64 * hf + j] = lq_code(x[j].x * L.sc[c0]) | (lq_code(x[j].y * L.sc[c0 + 1]) << 8) |
+                                        (lq_code(x[j].z * L.sc[c0 + 2]) << 16) |
+                                        (lq_code(x[j].w * L.sc[c0 + 3]) << 24);
         }
     }
     __syncthreads();
@@ -200,7 +239,7 @@ __device__ void lq_refit(const RefitLds& L, int n_iter, int tid, uint32_t* __res
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
             const int qd = tid + kThreads * m;
-            const int row = qd >> 3, d = 4 * (qd & 7);  // word d .. d+3 of the row's 32
+            const int row = qd >> 3, d = 4 * (qd & 7);  // words d .. d+3 of the row's 32
             const u32x4 w4 = *reinterpret_cast<const u32x4*>(Su + row * kD + 64 * (d >> 4) + (d & 15));
             __builtin_nontemporal_store(w4, reinterpret_cast<u32x4*>(Zh + row * (kD / 4) + d));
         }
@@ -212,7 +251,7 @@ __global__ __launch_bounds__(kThreads) void lq_quantize_kernel(const float* __re
                                                                int8_t* __restrict__ Z, float* __restrict__ B,
                                                                float* __restrict__ Cs, half_t* __restrict__ Kc,
                                                                half_t* __restrict__ Uc) {
-    extern __shared__ float lds[];
+    extern __shared__ __align__(16) float lds[];
     const RefitLds L(lds);
     const int h = head_of_block(blockIdx.x, gridDim.x), tid = threadIdx.x;
     const float* Sh = S + static_cast<size_t>(h) * kD * kD;
@@ -220,9 +259,7 @@ __global__ __launch_bounds__(kThreads) void lq_quantize_kernel(const float* __re
     for (int m = 0; m < kD * kD / 4 / kThreads; ++m) {
         const int qd = tid + kThreads * m;
         const int row = qd >> 5, c4 = qd & 31;
-        const f32x4 v = stream_load(Sh + row * kD + 4 * c4);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) L.S[swz(row, 4 * c4 + e)] = v[e];
+        L.unit(row, c4) = stream_load(Sh + row * kD + 4 * c4);
     }
     if (tid < kD) {  // the first 4 Walsh columns: (-1)^popcount(i & t) / sqrt(128)
         constexpr float s = 0.08838834764831845f;
@@ -426,7 +463,7 @@ __global__ __launch_bounds__(kThreads) void lq_boundary_kernel(
     const bf16_t* __restrict__ k, const bf16_t* __restrict__ v, const float* __restrict__ gate,
     const float* __restrict__ beta, float* __restrict__ y) {
     constexpr int kRec = 16;
-    extern __shared__ float dyn_lds[];
+    extern __shared__ __align__(16) float dyn_lds[];
     __shared__ f32x2 rowv[kD];
     __shared__ f32x2 coef[kRec];
     __shared__ f32x2 ctok[kTok];
@@ -639,9 +676,7 @@ __global__ __launch_bounds__(kThreads) void lq_boundary_kernel(
     for (int a = 0; a < 2; ++a) {
         const int row = 16 * (2 * wave + a) + lr;
 #pragma unroll
-        for (int ct = 0; ct < 8; ++ct)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) L.S[swz(row, 16 * ct + 4 * lq + i)] = acc[a][ct][i];
+        for (int ct = 0; ct < 8; ++ct) L.unit(row, 4 * ct + lq) = acc[a][ct];
     }
     __syncthreads();
     lq_refit(L, n_iter, tid, Zh, Bcol + vec_off, Csm + vec_off, Kc + tok0, Uc + tok0);

@@ -128,7 +128,7 @@ __global__ __launch_bounds__(kThreads) void q8_step_kernel(
     float* __restrict__ Ubuf, float* __restrict__ Gbuf, const T* __restrict__ q,
     const T* __restrict__ k, const T* __restrict__ v, const float* __restrict__ gate,
     const float* __restrict__ beta, float* __restrict__ y) {
-    extern __shared__ float gs_lds[];     // KDA: the records' gates [pos][128]
+    extern __shared__ __align__(16) float gs_lds[];     // KDA: the records' gates [pos][128]
     __shared__ f32x2 rowv[kD];            // a_r/127 Gamma_{1:l} (k_r, q_r)
     __shared__ f32x2 coef[kMaxW];         // per record (E_j . k, E_j . q)
     __shared__ f32x2 red[4][kD];          // per-wave column partials
@@ -316,7 +316,7 @@ __global__ __launch_bounds__(kThreads) void q8_boundary_kernel(
     const float* __restrict__ Ubuf, const float* __restrict__ Gbuf, const T* __restrict__ q,
     const T* __restrict__ k, const T* __restrict__ v, const float* __restrict__ gate,
     const float* __restrict__ beta, float* __restrict__ y) {
-    extern __shared__ float dyn_lds[];
+    extern __shared__ __align__(16) float dyn_lds[];
     __shared__ float gsuf[kMaxW + 1];     // GDN: gate products after each record; [kMaxW]: all
     __shared__ f32x2 rowv[kD];            // a_r/127 Gamma_{1:l} (k_r, q_r)
     __shared__ f32x2 kq_row[kD];          // (k_r, q_r)
