@@ -42,26 +42,50 @@ __device__ __forceinline__ uint32_t lq_code(float w) {
 }
 
 // ---------------------------------------------------------------- the refit
-// LDS of the refit, in floats: the state S [128 x 128] row-major in 16-byte units, unit
-// u of row r stored at unit u ^ f(r), f(r) = (r & 7) ^ ((r & 1) << 3); then V, Y, W, Kr,
-// Ur [128] x f32x4 (token t of row / column i in element t of entry i) and 128
-// per-column scales. The refit sweeps S in two layouts, both conflict-free with that
-// swizzle: row halves (thread 2i + h owns row i, units 16h .. 16h+15, the second half
-// starting 8 units later) and the dense step's column slabs (wave w owns columns
-// 32w .. 32w+31, lane l the 4 columns of unit 8w + (l & 7) in rows 8 it + (l >> 3)).
-constexpr int kRefitFloats = kD * kD + 5 * 4 * kD + kD;
-__device__ __forceinline__ int sw_unit(int r, int u) { return u ^ ((r & 7) ^ ((r & 1) << 3)); }
-__device__ __forceinline__ int sidx(int r, int c) { return r * kD + 4 * sw_unit(r, c >> 2) + (c & 3); }
+// The refit holds the state in registers: lane l of wave w owns the 4 columns of unit
+// uu = 8 w + (l & 7) (columns 4 uu .. 4 uu + 3) in the 16 rows 8 it + (l >> 3). Products
+// with V sum over the 8 column lanes of a row (DPP) and then over the 4 waves (LDS);
+// products with S^T and the per-column absmax sum over the 8 row lanes of a column
+// group inside the wave.
+//
+// LDS of the refit, in floats. A region of kRefitRegionFloats holds the staged codes
+// (128 rows of kCodeStride words) and V, Y, Kr, Ur [128] x f32x4 (token t of row or
+// column i in element t of entry i), the per-wave partials Yp [4][128] x f32x4 (also the
+// per-wave row sums of |R|) and the row factors 1 / c [128]. W [128] x f32x4, the start
+// vectors and the S^T Y products, lies outside the region: the boundary writes it
+// before its state region (which the refit region reuses) is free.
+constexpr int kCodeStride = 40;  // 16-byte rows; rows 8 apart in banks
+constexpr int kRefitRegionFloats = kD * kCodeStride + 4 * 4 * kD + 4 * 4 * kD + kD;
+constexpr int kRefitQuantizeFloats = kRefitRegionFloats + 4 * kD;
 
 struct RefitLds {
-    float* S;
-    f32x4 *V, *Y, *W, *Kr, *Ur;
-    float* sc;
-    __device__ explicit RefitLds(float* base)
-        : S(base), V(reinterpret_cast<f32x4*>(base + kD * kD)), Y(V + kD), W(Y + kD), Kr(W + kD),
-          Ur(Kr + kD), sc(reinterpret_cast<float*>(Ur + kD)) {}
-    __device__ f32x4& unit(int r, int u) const { return reinterpret_cast<f32x4*>(S + r * kD)[sw_unit(r, u)]; }
+    uint32_t* codes;
+    f32x4 *V, *Y, *Kr, *Ur, *Yp, *W;
+    float* ic;
+    __device__ RefitLds(float* region, float* w_area)
+        : codes(reinterpret_cast<uint32_t*>(region)),
+          V(reinterpret_cast<f32x4*>(region + kD * kCodeStride)), Y(V + kD), Kr(Y + kD), Ur(Kr + kD),
+          Yp(Ur + kD), W(reinterpret_cast<f32x4*>(w_area)), ic(reinterpret_cast<float*>(Yp + 4 * kD)) {}
+    __device__ float* Ap() const { return reinterpret_cast<float*>(Yp); }
 };
+
+// Sum over the 8 lanes that differ in lane bits 0..2 (quad sums, then the mirrored
+// quad inside each half-row of 8 lanes).
+__device__ __forceinline__ float sum_col_lanes(float x) {
+    x += dpp<kDppXor1>(x);
+    x += dpp<kDppXor2>(x);
+    return x + dpp<kDppHalfMirror>(x);
+}
+__device__ __forceinline__ f32x4 sum_col_lanes(f32x4 x) {
+    return f32x4{sum_col_lanes(x.x), sum_col_lanes(x.y), sum_col_lanes(x.z), sum_col_lanes(x.w)};
+}
+
+// y + a x element by element, written without a splat of a: the refit's state is
+// invariant across the fit's iterations, and splats of it would be hoisted out of the
+// loop as four registers each.
+__device__ __forceinline__ f32x4 axpy(float a, f32x4 x, f32x4 y) {
+    return f32x4{fmaf(a, x.x, y.x), fmaf(a, x.y, y.y), fmaf(a, x.z, y.z), fmaf(a, x.w, y.w)};
+}
 
 __device__ __forceinline__ float max_row_lanes(float x) {
     x = fmaxf(x, dpp<kDppRor8>(x));
@@ -96,37 +120,31 @@ __device__ __forceinline__ void refit_mgs(const RefitLds& L, int wave, int lane)
     __syncthreads();
 }
 
-// unit k of the half-row walk of thread (row, half)
-__device__ __forceinline__ int half_unit(int hf, int k) { return 16 * hf + ((k + 8 * hf) & 15); }
-
-// Y = S V over row halves (the two halves of a row are lanes 2i, 2i+1)
-__device__ __forceinline__ void refit_sv(const RefitLds& L, int rc, int hf) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-    for (int k = 0; k < 16; ++k) {
-        const int u = half_unit(hf, k);
-        const f32x4 sv = L.unit(rc, u);
-        acc += sv.x * L.V[4 * u] + sv.y * L.V[4 * u + 1] + sv.z * L.V[4 * u + 2] + sv.w * L.V[4 * u + 3];
+// Y = S V
+__device__ __forceinline__ void refit_sv(const RefitLds& L, const f32x4 (&s)[16], int wave, int lane, int tid) {
+    const int uu = 8 * wave + (lane & 7), ro = lane >> 3;
+    const f32x4 v0 = L.V[4 * uu], v1 = L.V[4 * uu + 1], v2 = L.V[4 * uu + 2], v3 = L.V[4 * uu + 3];
+#pragma unroll
+    for (int it = 0; it < 16; ++it) {
+        const f32x4 p = sum_col_lanes(axpy(s[it].w, v3, axpy(s[it].z, v2, axpy(s[it].y, v1, s[it].x * v0))));
+        if ((lane & 7) == 0) L.Yp[wave * kD + 8 * it + ro] = p;
     }
-    acc = f32x4{acc.x + dpp<kDppXor1>(acc.x), acc.y + dpp<kDppXor1>(acc.y), acc.z + dpp<kDppXor1>(acc.z),
-                acc.w + dpp<kDppXor1>(acc.w)};
-    if (hf == 0) L.Y[rc] = acc;
+    __syncthreads();
+    if (tid < kD) L.Y[tid] = (L.Yp[tid] + L.Yp[kD + tid]) + (L.Yp[2 * kD + tid] + L.Yp[3 * kD + tid]);
     __syncthreads();
 }
 
-// W = S^T Y over column slabs: 16 rows per lane, then the 8 row lanes of each column group
-__device__ __forceinline__ void refit_sty(const RefitLds& L, int wave, int lane) {
+// W = S^T Y
+__device__ __forceinline__ void refit_sty(const RefitLds& L, const f32x4 (&s)[16], int wave, int lane) {
     const int uu = 8 * wave + (lane & 7), ro = lane >> 3;
     f32x4 acc[4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-#pragma unroll 4
+#pragma unroll
     for (int it = 0; it < 16; ++it) {
-        const int row = 8 * it + ro;
-        const f32x4 sv = L.unit(row, uu);
-        const f32x4 yv = L.Y[row];
-        acc[0] += sv.x * yv;
-        acc[1] += sv.y * yv;
-        acc[2] += sv.z * yv;
-        acc[3] += sv.w * yv;
+        const f32x4 yv = L.Y[8 * it + ro];
+        acc[0] = axpy(s[it].x, yv, acc[0]);
+        acc[1] = axpy(s[it].y, yv, acc[1]);
+        acc[2] = axpy(s[it].z, yv, acc[2]);
+        acc[3] = axpy(s[it].w, yv, acc[3]);
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) acc[e] = sum_row_lanes(acc[e]);
@@ -136,20 +154,21 @@ __device__ __forceinline__ void refit_sty(const RefitLds& L, int wave, int lane)
     __syncthreads();
 }
 
-// The refit of one head. On entry S holds the state and W the start vectors; every
-// thread of the workgroup calls it. Writes Z, B, c and the fp16 tokens of the head.
-__device__ void lq_refit(const RefitLds& L, int n_iter, int tid, uint32_t* __restrict__ Zh,
-                         float* __restrict__ Bh, float* __restrict__ Ch, half_t* __restrict__ Kh,
-                         half_t* __restrict__ Uh) {
+// The refit of one head. On entry s holds the lane's part of the state and W the start
+// vectors; every thread of the workgroup calls it. Writes Z, B, c and the fp16 tokens.
+__device__ __forceinline__ void lq_refit(const RefitLds& L, f32x4 (&s)[16], int n_iter, int tid,
+                                         uint32_t* __restrict__ Zh, float* __restrict__ Bh,
+                                         float* __restrict__ Ch, half_t* __restrict__ Kh,
+                                         half_t* __restrict__ Uh) {
     const int wave = tid >> 6, lane = tid & 63;
-    const int rc = tid >> 1, hf = tid & 1;
+    const int uu = 8 * wave + (lane & 7), ro = lane >> 3;
     refit_mgs(L, wave, lane);
     for (int it = 0; it < n_iter; ++it) {
-        refit_sv(L, rc, hf);
-        refit_sty(L, wave, lane);
+        refit_sv(L, s, wave, lane, tid);
+        refit_sty(L, s, wave, lane);
         refit_mgs(L, wave, lane);
     }
-    refit_sv(L, rc, hf);  // Kt = S V
+    refit_sv(L, s, wave, lane, tid);  // Kt = S V
 
     // fp16 tokens (stored), and their exact fp32 values for the residual
     if (tid < kD) {
@@ -169,80 +188,57 @@ __device__ void lq_refit(const RefitLds& L, int n_iter, int tid, uint32_t* __res
     }
     __syncthreads();
 
-    // residual R = S - Kt Ut^T in place over row halves, row smoothing c, X = R / c
+    // residual R = S - Kt Ut^T in registers, and each row's sum of |R|
     {
-        const f32x4 kr = L.Kr[rc];
-        float asum = 0.f;
-#pragma unroll 4
-        for (int k = 0; k < 16; ++k) {
-            const int u = half_unit(hf, k);
-            f32x4 sv = L.unit(rc, u);
+        const f32x4 u0 = L.Ur[4 * uu], u1 = L.Ur[4 * uu + 1], u2 = L.Ur[4 * uu + 2], u3 = L.Ur[4 * uu + 3];
+        float* Ap = L.Ap();
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const f32x4 uv = L.Ur[4 * u + e];
-                sv[e] -= kr.x * uv.x + kr.y * uv.y + kr.z * uv.z + kr.w * uv.w;
-                asum += fabsf(sv[e]);
-            }
-            L.unit(rc, u) = sv;
-        }
-        asum += dpp<kDppXor1>(asum);
-        const float cs = fmaxf(sqrtf(asum * (1.f / kD)), kSmoothFloor);
-        if (hf == 0) Ch[rc] = cs;
-        const float ic = 1.f / cs;
-#pragma unroll 4
-        for (int k = 0; k < 16; ++k) {
-            const int u = half_unit(hf, k);
-            L.unit(rc, u) = L.unit(rc, u) * ic;
-        }
-    }
-    __syncthreads();
-
-    // per-value-channel absmax B and the code scale 127 / B, over column slabs
-    {
-        const int uu = 8 * wave + (lane & 7), ro = lane >> 3;
-        f32x4 m = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
         for (int it = 0; it < 16; ++it) {
-            const f32x4 sv = L.unit(8 * it + ro, uu);
-            m = f32x4{fmaxf(m.x, fabsf(sv.x)), fmaxf(m.y, fabsf(sv.y)), fmaxf(m.z, fabsf(sv.z)),
-                      fmaxf(m.w, fabsf(sv.w))};
+            const f32x4 kr = L.Kr[8 * it + ro];
+            s[it].x -= kr.x * u0.x + kr.y * u0.y + kr.z * u0.z + kr.w * u0.w;
+            s[it].y -= kr.x * u1.x + kr.y * u1.y + kr.z * u1.z + kr.w * u1.w;
+            s[it].z -= kr.x * u2.x + kr.y * u2.y + kr.z * u2.z + kr.w * u2.w;
+            s[it].w -= kr.x * u3.x + kr.y * u3.y + kr.z * u3.z + kr.w * u3.w;
+            const float a = sum_col_lanes((fabsf(s[it].x) + fabsf(s[it].y)) + (fabsf(s[it].z) + fabsf(s[it].w)));
+            if ((lane & 7) == 0) Ap[wave * kD + 8 * it + ro] = a;
         }
-        m = f32x4{max_row_lanes(m.x), max_row_lanes(m.y), max_row_lanes(m.z), max_row_lanes(m.w)};
-        if (ro == 0) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                Bh[4 * uu + e] = m[e];
-                L.sc[4 * uu + e] = m[e] > 0.f ? __fdiv_rn(127.f, m[e]) : 0.f;
-            }
+        __syncthreads();
+        if (tid < kD) {
+            const float asum = (Ap[tid] + Ap[kD + tid]) + (Ap[2 * kD + tid] + Ap[3 * kD + tid]);
+            const float cs = fmaxf(sqrtf(asum * (1.f / kD)), kSmoothFloor);
+            Ch[tid] = cs;
+            L.ic[tid] = 1.f / cs;
         }
+        __syncthreads();
     }
-    __syncthreads();
 
-    // codes over row halves: 16 words per thread, written over its own half-row of S
-    // (a block only this thread touches), then whole rows leave together
-    {
-        f32x4 x[16];
+    // X = R / c, the per-value-channel absmax B and the code scale 127 / B
+    f32x4 m = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int j = 0; j < 16; ++j) x[j] = L.unit(rc, 16 * hf + j);
-        uint32_t* Su = reinterpret_cast<uint32_t*>(L.S);
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            const int c0 = 64 * hf + 4 * j;
-            Su[rc * kD + 64 * hf + j] = lq_code(x[j].x * L.sc[c0]) | (lq_code(x[j].y * L.sc[c0 + 1]) << 8) |
-                                        (lq_code(x[j].z * L.sc[c0 + 2]) << 16) |
-                                        (lq_code(x[j].w * L.sc[c0 + 3]) << 24);
-        }
+    for (int it = 0; it < 16; ++it) {
+        s[it] *= L.ic[8 * it + ro];
+        m = f32x4{fmaxf(m.x, fabsf(s[it].x)), fmaxf(m.y, fabsf(s[it].y)), fmaxf(m.z, fabsf(s[it].z)),
+                  fmaxf(m.w, fabsf(s[it].w))};
     }
-    __syncthreads();
-    {
-        const uint32_t* Su = reinterpret_cast<const uint32_t*>(L.S);
+    m = f32x4{max_row_lanes(m.x), max_row_lanes(m.y), max_row_lanes(m.z), max_row_lanes(m.w)};
+    f32x4 sc;
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            const int qd = tid + kThreads * m;
-            const int row = qd >> 3, d = 4 * (qd & 7);  // words d .. d+3 of the row's 32
-            const u32x4 w4 = *reinterpret_cast<const u32x4*>(Su + row * kD + 64 * (d >> 4) + (d & 15));
-            __builtin_nontemporal_store(w4, reinterpret_cast<u32x4*>(Zh + row * (kD / 4) + d));
-        }
+    for (int e = 0; e < 4; ++e) sc[e] = m[e] > 0.f ? __fdiv_rn(127.f, m[e]) : 0.f;
+    if (ro == 0) *reinterpret_cast<f32x4*>(Bh + 4 * uu) = m;
+
+    // codes: one word per row and unit, staged so that whole rows leave together
+#pragma unroll
+    for (int it = 0; it < 16; ++it)
+        L.codes[(8 * it + ro) * kCodeStride + uu] = lq_code(s[it].x * sc.x) | (lq_code(s[it].y * sc.y) << 8) |
+                                                    (lq_code(s[it].z * sc.z) << 16) |
+                                                    (lq_code(s[it].w * sc.w) << 24);
+    __syncthreads();
+#pragma unroll
+    for (int mm = 0; mm < 4; ++mm) {
+        const int qd = tid + kThreads * mm;
+        const int row = qd >> 3, d = 4 * (qd & 7);  // words d .. d+3 of the row's 32
+        const u32x4 w4 = *reinterpret_cast<const u32x4*>(L.codes + row * kCodeStride + d);
+        __builtin_nontemporal_store(w4, reinterpret_cast<u32x4*>(Zh + row * (kD / 4) + d));
     }
 }
 
@@ -252,25 +248,24 @@ __global__ __launch_bounds__(kThreads) void lq_quantize_kernel(const float* __re
                                                                float* __restrict__ Cs, half_t* __restrict__ Kc,
                                                                half_t* __restrict__ Uc) {
     extern __shared__ __align__(16) float lds[];
-    const RefitLds L(lds);
+    const RefitLds L(lds, lds + kRefitRegionFloats);
     const int h = head_of_block(blockIdx.x, gridDim.x), tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
+    const int uu = 8 * wave + (lane & 7), ro = lane >> 3;
     const float* Sh = S + static_cast<size_t>(h) * kD * kD;
-#pragma unroll 4
-    for (int m = 0; m < kD * kD / 4 / kThreads; ++m) {
-        const int qd = tid + kThreads * m;
-        const int row = qd >> 5, c4 = qd & 31;
-        L.unit(row, c4) = stream_load(Sh + row * kD + 4 * c4);
-    }
+    f32x4 s[16];
+#pragma unroll
+    for (int it = 0; it < 16; ++it) s[it] = stream_load(Sh + (8 * it + ro) * kD + 4 * uu);
     if (tid < kD) {  // the first 4 Walsh columns: (-1)^popcount(i & t) / sqrt(128)
-        constexpr float s = 0.08838834764831845f;
+        constexpr float sq = 0.08838834764831845f;
         f32x4 w;
 #pragma unroll
-        for (int t = 0; t < kTok; ++t) w[t] = (__builtin_popcount(tid & t) & 1) ? -s : s;
+        for (int t = 0; t < kTok; ++t) w[t] = (__builtin_popcount(tid & t) & 1) ? -sq : sq;
         L.W[tid] = w;
     }
     __syncthreads();
     const size_t vo = static_cast<size_t>(h) * kD;
-    lq_refit(L, n_iter, tid, reinterpret_cast<uint32_t*>(Z + vo * kD), B + vo, Cs + vo,
+    lq_refit(L, s, n_iter, tid, reinterpret_cast<uint32_t*>(Z + vo * kD), B + vo, Cs + vo,
              Kc + vo * kTok, Uc + vo * kTok);
 }
 
@@ -434,14 +429,24 @@ __global__ __launch_bounds__(kThreads) void lq_step_kernel(
 // The step as in the per-row bf16 boundary (column-owner record terms, scaled records
 // staged transposed for the bf16-split MFMA), with the payload terms scaled by B and c
 // and the token pairs added; then S_W is formed on the matrix cores (payload init, the
-// records' two bf16 MFMAs per tile, the tokens' one fp32 MFMA per tile), staged in LDS,
-// and refitted. Dynamic LDS is one region used twice: first for the step and the
-// contraction operands, then (after a barrier) for the refit.
+// records' two bf16 MFMAs per tile, the tokens' one fp32 MFMA per tile), passed through
+// LDS into the refit's register layout, and refitted. The first kD * kD floats of
+// dynamic LDS are one region used three times: the step and the contraction operands,
+// then the state on its way between the two register layouts, then the refit's arrays.
+// After it lie W (the old Ut, the refit's start) and the old payload's B / 127.
 constexpr int kZsStride = kD / 4 + 1;
 // floats of the step-phase region: Kt (4 KB), Ut (12 KB), Zs, Ktok, Utok, red, recp
 constexpr int kStepFloats = 2 * kD * 4 + 3 * 2 * kD * 4 + kD * kZsStride + 2 * kTok * kD + 4 * kD * 2 + kD * 2;
-constexpr int kLqBoundaryFloats = kRefitFloats > kStepFloats ? kRefitFloats : kStepFloats;
-static_assert(kStepFloats <= kD * kD, "the step-phase region must lie inside the refit's state region");
+constexpr int kLqBoundaryFloats = kD * kD + 4 * kD + kD;
+static_assert(kStepFloats <= kD * kD, "the step-phase arrays must lie inside the shared region");
+static_assert(kRefitRegionFloats <= kD * kD, "the refit's arrays must lie inside the shared region");
+
+// The state in transit: row r in 16-byte units, unit u stored at u ^ f(r) with
+// f(r) = (r & 7) ^ ((r & 1) << 3), so that the MFMA-layout writes and the refit-layout
+// reads both spread over the banks.
+__device__ __forceinline__ f32x4& state_unit(float* base, int r, int u) {
+    return reinterpret_cast<f32x4*>(base + r * kD)[u ^ ((r & 7) ^ ((r & 1) << 3))];
+}
 
 __device__ __forceinline__ void split3_bf16(float x, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
     const __bf16 a = static_cast<__bf16>(x);
@@ -479,9 +484,9 @@ __global__ __launch_bounds__(kThreads) void lq_boundary_kernel(
     float* Utok = Ktok + kTok * kD;                                 // [4][128], scaled by Gamma_{1:W}
     f32x2* red = reinterpret_cast<f32x2*>(Utok + kTok * kD);       // [4][128]
     f32x2* recp = red + 4 * kD;                                     // [128]
-    // refit views (the state region overlaps every step-phase array above)
-    const RefitLds L(dyn_lds);
-    float* bscs = L.sc;   // B / 127 of the old payload, until the refit writes the new scales
+    // refit views (its region overlaps every step-phase array above; W and bscs do not)
+    const RefitLds L(dyn_lds, dyn_lds + kD * kD);
+    float* bscs = dyn_lds + kD * kD + 4 * kD;   // B / 127 of the old payload
 
     const int h = head_of_block(blockIdx.x, gridDim.x), tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
@@ -671,15 +676,22 @@ __global__ __launch_bounds__(kThreads) void lq_boundary_kernel(
             acc[a][ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(Utok[lq * kD + col], bk, acc[a][ct], 0, 0, 0);
         }
     }
-    __syncthreads();  // every read of the step-phase arrays is done: the region becomes S
+    __syncthreads();  // every read of the step-phase arrays is done: the region holds S
 #pragma unroll
     for (int a = 0; a < 2; ++a) {
         const int row = 16 * (2 * wave + a) + lr;
 #pragma unroll
-        for (int ct = 0; ct < 8; ++ct) L.unit(row, 4 * ct + lq) = acc[a][ct];
+        for (int ct = 0; ct < 8; ++ct) state_unit(dyn_lds, row, 4 * ct + lq) = acc[a][ct];
     }
     __syncthreads();
-    lq_refit(L, n_iter, tid, Zh, Bcol + vec_off, Csm + vec_off, Kc + tok0, Uc + tok0);
+    f32x4 s[16];
+    {
+        const int uu = 8 * wave + (lane & 7), rr = lane >> 3;
+#pragma unroll
+        for (int it = 0; it < 16; ++it) s[it] = state_unit(dyn_lds, 8 * it + rr, uu);
+    }
+    __syncthreads();  // the region is free for the refit's arrays
+    lq_refit(L, s, n_iter, tid, Zh, Bcol + vec_off, Csm + vec_off, Kc + tok0, Uc + tok0);
 }
 
 // ---------------------------------------------------------------- launchers
@@ -690,9 +702,9 @@ static hipError_t set_lds(const void* fn, int floats) {
 
 hipError_t launch_lq_quantize(int heads, const float* S, int n_iter, int8_t* Z, float* B, float* C,
                               void* Kc, void* Uc, hipStream_t stream) {
-    static const hipError_t attr = set_lds(reinterpret_cast<const void*>(lq_quantize_kernel), kRefitFloats);
+    static const hipError_t attr = set_lds(reinterpret_cast<const void*>(lq_quantize_kernel), kRefitQuantizeFloats);
     if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL(lq_quantize_kernel, dim3(heads), dim3(kThreads), sizeof(float) * kRefitFloats, stream,
+    hipLaunchKernelGGL(lq_quantize_kernel, dim3(heads), dim3(kThreads), sizeof(float) * kRefitQuantizeFloats, stream,
                        S, n_iter, Z, B, C, static_cast<half_t*>(Kc), static_cast<half_t*>(Uc));
     return hipGetLastError();
 }

@@ -132,14 +132,15 @@ __device__ __forceinline__ int head_of_block(int bid, int nblk) {
 // ---- cross-lane reductions on the VALU (DPP and permlane swaps; no LDS round trip)
 // Lane layouts checked on gfx950: quad_perm 0xB1 / 0x4E exchange lanes i^1 / i^2,
 // row_ror:8 exchanges i^8 inside each row of 16 lanes, row_ror:4 rotates a row by
-// 4, and the two results of permlane16_swap(x, x) / permlane32_swap(x, x) hold
-// x of lane i and of lane i^16 / i^32.
+// 4, row_half_mirror reverses each group of 8 lanes (lane i reads lane i^7), and the
+// two results of permlane16_swap(x, x) / permlane32_swap(x, x) hold x of lane i and
+// of lane i^16 / i^32.
 template <int kCtrl>
 __device__ __forceinline__ float dpp(float x) {
     return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), kCtrl,
                                                                  0xF, 0xF, false));
 }
-constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppRor4 = 0x124, kDppRor8 = 0x128;
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppRor4 = 0x124, kDppRor8 = 0x128, kDppHalfMirror = 0x141;
 
 // The two results are copied to scalars before any bit cast: with this toolchain,
 // __builtin_bit_cast of an element of the returned vector reads element 0.
