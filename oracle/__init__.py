@@ -50,10 +50,14 @@ def _load():
                                               P, P, P]
         lib.oracle_log_step.argtypes = [I64, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P, P]
         lib.oracle_log_step_slots.argtypes = [I64, I, I, I, I, P, P, P, P, P, P, P, P, P, P, P, P]
+        lib.oracle_rwkv6_step.argtypes = [I64, I, I, P, P, P, P, P, P]
+        lib.oracle_rwkv6_log_step.argtypes = [I64, I, I, I, I, P, P, P, P, P, P, P, P, P, P]
+        lib.oracle_rwkv6_log_step_slots.argtypes = [I64, I, I, I, P, P, P, P, P, P, P, P, P, P, P]
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = ctypes.c_int
         for f in (lib.oracle_dense_step, lib.oracle_q8_quantize, lib.oracle_q8_window_step,
-                  lib.oracle_log_step, lib.oracle_log_step_slots):
+                  lib.oracle_log_step, lib.oracle_log_step_slots, lib.oracle_rwkv6_step,
+                  lib.oracle_rwkv6_log_step, lib.oracle_rwkv6_log_step_slots):
             f.restype = None
         _lib = lib
     return _lib
@@ -89,6 +93,18 @@ def dense_step(S: np.ndarray, q, k, v, gate, beta) -> np.ndarray:
     y = np.empty((nh, dv))
     _load().oracle_dense_step(nh, dk, dv, per_key, _ptr(S), _ptr(q), _ptr(k), _ptr(v),
                               _ptr(gate), _ptr(beta), _ptr(y))
+    return y
+
+
+def rwkv6_step(S: np.ndarray, q, k, v, w) -> np.ndarray:
+    """One RWKV6 decode step in the pages' common form, S <- Diag(w) S + k v^T and
+    y = S^T q, on fp64 states S[nh, dk, dv] (updated in place); w is [nh, dk]."""
+    assert S.dtype == np.float64 and S.flags.c_contiguous
+    nh, dk, dv = S.shape
+    q, k, v, w = map(_f64, (q, k, v, w))
+    assert q.shape == (nh, dk) and k.shape == (nh, dk) and v.shape == (nh, dv) and w.shape == (nh, dk)
+    y = np.empty((nh, dv))
+    _load().oracle_rwkv6_step(nh, dk, dv, _ptr(S), _ptr(q), _ptr(k), _ptr(v), _ptr(w), _ptr(y))
     return y
 
 
@@ -151,12 +167,14 @@ class WindowState:
 
 class LogState:
     """The base + log representation of nh heads (DeltaLog sec. 3.1): dense base
-    Sbar, cumulative log-decay lbar, and a log of capacity C = M - 1."""
+    Sbar, cumulative log-decay lbar, and a log of capacity C = M - 1. ``rwkv6``
+    selects the update without the delta read (per-key decay, pair (k, v))."""
 
-    def __init__(self, Sbar: np.ndarray, C: int, per_key: bool):
+    def __init__(self, Sbar: np.ndarray, C: int, per_key: bool, rwkv6: bool = False):
         nh, dk, dv = Sbar.shape
         self.Sbar = _f64(Sbar).copy()
-        self.C, self.per_key = C, per_key
+        self.C, self.per_key, self.rwkv6 = C, per_key or rwkv6, rwkv6
+        per_key = self.per_key
         gd = (dk,) if per_key else ()
         self.lbar = np.zeros((nh,) + gd)
         cap = max(C, 1)
@@ -165,8 +183,17 @@ class LogState:
         self.Lam = np.zeros((nh, cap) + gd)
         self.L = 0
 
-    def step(self, q, k, v, gate, beta):
+    def step(self, q, k, v, gate, beta=None):
         nh, dk, dv = self.Sbar.shape
+        if self.rwkv6:
+            q, k, v, w = map(_f64, (q, k, v, gate))
+            assert w.shape == (nh, dk)
+            y = np.empty((nh, dv))
+            _load().oracle_rwkv6_log_step(nh, dk, dv, self.C, self.L, _ptr(self.Sbar), _ptr(self.lbar),
+                                          _ptr(self.K), _ptr(self.U), _ptr(self.Lam), _ptr(q), _ptr(k),
+                                          _ptr(v), _ptr(w), _ptr(y))
+            self.L = self.L + 1 if self.L < self.C else 0
+            return y
         q, k, v, gate, beta = map(_f64, (q, k, v, gate, beta))
         _check_step_inputs(nh, dk, dv, self.per_key, q, k, v, gate, beta)
         y = np.empty((nh, dv))
@@ -176,17 +203,24 @@ class LogState:
         self.L = self.L + 1 if self.L < self.C else 0
         return y
 
-    def step_slots(self, Ls, q, k, v, gate, beta):
+    def step_slots(self, Ls, q, k, v, gate, beta=None):
         """One step with a live length per head (Ls: int array [nh], each in [0, C],
         advanced in place): heads with Ls < C append, heads with Ls == C merge."""
         nh, dk, dv = self.Sbar.shape
-        q, k, v, gate, beta = map(_f64, (q, k, v, gate, beta))
-        _check_step_inputs(nh, dk, dv, self.per_key, q, k, v, gate, beta)
         if Ls.dtype != np.int32 or Ls.shape != (nh,) or not Ls.flags.c_contiguous:
             raise ValueError("Ls must be a contiguous int32 array of one live length per head")
         if (Ls < 0).any() or (Ls > self.C).any():
             raise ValueError("live lengths must lie in [0, C]")
         y = np.empty((nh, dv))
+        if self.rwkv6:
+            q, k, v, w = map(_f64, (q, k, v, gate))
+            assert w.shape == (nh, dk)
+            _load().oracle_rwkv6_log_step_slots(nh, dk, dv, self.C, Ls.ctypes.data_as(ctypes.c_void_p),
+                                                _ptr(self.Sbar), _ptr(self.lbar), _ptr(self.K), _ptr(self.U),
+                                                _ptr(self.Lam), _ptr(q), _ptr(k), _ptr(v), _ptr(w), _ptr(y))
+            return y
+        q, k, v, gate, beta = map(_f64, (q, k, v, gate, beta))
+        _check_step_inputs(nh, dk, dv, self.per_key, q, k, v, gate, beta)
         _load().oracle_log_step_slots(nh, dk, dv, int(self.per_key), self.C,
                                       Ls.ctypes.data_as(ctypes.c_void_p), _ptr(self.Sbar),
                                       _ptr(self.lbar), _ptr(self.K), _ptr(self.U), _ptr(self.Lam),

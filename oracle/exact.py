@@ -126,10 +126,18 @@ def explicit_schedule_run(S0: Mat, inputs, W: int):
     return ys, bounds
 
 
-def log_run(S0: Mat, inputs, M: int):
+def rwkv6_step(S: Mat, q: Vec, k: Vec, v: Vec, w: Vec):
+    """RWKV6 in the pages' common form: S <- Diag(w) S + k v^T, y = S^T q."""
+    dk, dv = len(S), len(S[0])
+    Sn = [[w[i] * S[i][j] + k[i] * v[j] for j in range(dv)] for i in range(dk)]
+    return Sn, [sum(Sn[i][j] * q[i] for i in range(dk)) for j in range(dv)]
+
+
+def log_run(S0: Mat, inputs, M: int, delta: bool = True):
     """Base + log (DeltaLog Alg. 1, eqs. 4-7) with decays as exact gate products:
     D(lbar) is the product of the gates since the last merge and D(lbar - Lam_m) the
-    product of the gates after entry m. Returns (ys, logical states after each step)."""
+    product of the gates after entry m. Without the delta rule (RWKV6) the value-side
+    factor is v itself. Returns (ys, logical states after each step)."""
     dk, dv = len(S0), len(S0[0])
     C = M - 1
     Sbar = [row[:] for row in S0]
@@ -150,7 +158,10 @@ def log_run(S0: Mat, inputs, M: int):
 
     for (q, k, v, g, beta) in inputs:
         Sold = logical(dec, log_entries)
-        b = [beta * (v[j] - sum(g[i] * Sold[i][j] * k[i] for i in range(dk))) for j in range(dv)]
+        if delta:
+            b = [beta * (v[j] - sum(g[i] * Sold[i][j] * k[i] for i in range(dk))) for j in range(dv)]
+        else:
+            b = list(v)
         dec = [dec[i] * g[i] for i in range(dk)]
         Snew = logical(dec, log_entries)
         Snew = [[Snew[i][j] + k[i] * b[j] for j in range(dv)] for i in range(dk)]
@@ -165,11 +176,11 @@ def log_run(S0: Mat, inputs, M: int):
     return ys, states
 
 
-def eager_run(S0: Mat, inputs):
+def eager_run(S0: Mat, inputs, delta: bool = True):
     S = [row[:] for row in S0]
     ys, states = [], []
     for (q, k, v, g, beta) in inputs:
-        S, y = dense_step(S, q, k, v, g, beta)
+        S, y = dense_step(S, q, k, v, g, beta) if delta else rwkv6_step(S, q, k, v, g)
         ys.append(y)
         states.append(S)
     return ys, states

@@ -77,6 +77,34 @@ void oracle_dense_step(int64_t nh, int dk, int dv, int per_key, double *S,
 }
 
 /*
+ * One RWKV6 decode step in the common form the pages use (DeltaLog, Table 1, the
+ * RWKV6 row: state transform D(lambda_t) S_{t-1}, update pair (k_t, v_t), diagonal
+ * decay; LeapQuant, App. A, eq. 1 with read vector b_t = 0 and output o_t = S_t^T q_t).
+ * w is the per-key decay factor (w = exp(lambda)); there is no delta read and no beta:
+ *   S = Diag(w) S + k v^T,   y = S^T q
+ */
+void oracle_rwkv6_step(int64_t nh, int dk, int dv, double *S, const double *q, const double *k,
+                       const double *v, const double *w, double *y)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t h = 0; h < nh; ++h) {
+        double *Sh = S + (size_t)h * dk * dv;
+        const double *qh = q + (size_t)h * dk, *kh = k + (size_t)h * dk;
+        const double *vh = v + (size_t)h * dv, *wh = w + (size_t)h * dk;
+        double *yh = y + (size_t)h * dv;
+        for (int i = 0; i < dk; ++i)
+            for (int j = 0; j < dv; ++j)
+                Sh[IDX2(i, j, dv)] = wh[i] * Sh[IDX2(i, j, dv)] + kh[i] * vh[j];
+        for (int j = 0; j < dv; ++j) {
+            double acc = 0.0;
+            for (int i = 0; i < dk; ++i)
+                acc += Sh[IDX2(i, j, dv)] * qh[i];
+            yh[j] = acc;
+        }
+    }
+}
+
+/*
  * Symmetric per-key-row int8 quantizer (STEPQuant notes, the uniform per-row
  * absmax baseline; LeapQuant, App. B.3, the /127 convention).
  *   a_i = max_j |S_ij|          stored as fp32
@@ -247,7 +275,7 @@ void oracle_q8_window_step(int64_t nh, int dk, int dv, int per_key, int W, int p
  * Log arrays: K[nh][C][dk], U[nh][C][dv], Lam[nh][C] or [nh][C][dk];
  * lbar[nh] or [nh][dk].
  */
-static void log_step_head(int64_t h, int dk, int dv, int per_key, int C, int L,
+static void log_step_head(int64_t h, int dk, int dv, int per_key, int delta, int C, int L,
                           double *Sbar, double *lbar, double *Klog, double *Ulog, double *Lam,
                           const double *q, const double *k, const double *v,
                           const double *gate, const double *beta, double *y)
@@ -278,8 +306,13 @@ static void log_step_head(int64_t h, int dk, int dv, int per_key, int C, int L,
             }
         }
         /* 1. the old-state read of the delta rule, along the decayed key:
-              p = (D(lambda_t) S_{t-1})^T k with lambda_t = ln g_t */
+              p = (D(lambda_t) S_{t-1})^T k with lambda_t = ln g_t; without the delta
+              rule (RWKV6, DeltaLog Table 1) the value-side factor is v itself */
         for (int j = 0; j < dv; ++j) {
+            if (!delta) {
+                b[j] = vh[j];
+                continue;
+            }
             double p = 0.0;
             for (int i = 0; i < dk; ++i) {
                 double lam = log(gate_at(gh, per_key, i));
@@ -333,7 +366,7 @@ void oracle_log_step(int64_t nh, int dk, int dv, int per_key, int C, int L,
 {
 #pragma omp parallel for schedule(static)
     for (int64_t h = 0; h < nh; ++h)
-        log_step_head(h, dk, dv, per_key, C, L, Sbar, lbar, Klog, Ulog, Lam, q, k, v, gate, beta, y);
+        log_step_head(h, dk, dv, per_key, 1, C, L, Sbar, lbar, Klog, Ulog, Lam, q, k, v, gate, beta, y);
 }
 
 /* The same step with a live length per head (each request slot at its own point
@@ -346,7 +379,30 @@ void oracle_log_step_slots(int64_t nh, int dk, int dv, int per_key, int C, int *
 {
 #pragma omp parallel for schedule(static)
     for (int64_t h = 0; h < nh; ++h) {
-        log_step_head(h, dk, dv, per_key, C, Ls[h], Sbar, lbar, Klog, Ulog, Lam, q, k, v, gate, beta, y);
+        log_step_head(h, dk, dv, per_key, 1, C, Ls[h], Sbar, lbar, Klog, Ulog, Lam, q, k, v, gate, beta, y);
+        Ls[h] = Ls[h] < C ? Ls[h] + 1 : 0;
+    }
+}
+
+/* The base + log step for RWKV6 (DeltaLog sec. 3.4: per-key log-decay metadata as for
+ * KDA, update pair (k, v) with no old-state correction): Alg. 1 with b = v. */
+void oracle_rwkv6_log_step(int64_t nh, int dk, int dv, int C, int L, double *Sbar, double *lbar,
+                           double *Klog, double *Ulog, double *Lam, const double *q,
+                           const double *k, const double *v, const double *w, double *y)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t h = 0; h < nh; ++h)
+        log_step_head(h, dk, dv, 1, 0, C, L, Sbar, lbar, Klog, Ulog, Lam, q, k, v, w, NULL, y);
+}
+
+void oracle_rwkv6_log_step_slots(int64_t nh, int dk, int dv, int C, int *Ls, double *Sbar,
+                                 double *lbar, double *Klog, double *Ulog, double *Lam,
+                                 const double *q, const double *k, const double *v,
+                                 const double *w, double *y)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t h = 0; h < nh; ++h) {
+        log_step_head(h, dk, dv, 1, 0, C, Ls[h], Sbar, lbar, Klog, Ulog, Lam, q, k, v, w, NULL, y);
         Ls[h] = Ls[h] < C ? Ls[h] + 1 : 0;
     }
 }
