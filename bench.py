@@ -39,7 +39,8 @@ KERNEL_SOURCES = {
               "recurrent_state_update_head_amd/csrc/rsu_device.hpp"],
 }
 
-WORKLOAD_BY_FLAG = {"gdn": 2, "gdn_small": 1, "kda": 3, "q8": 4, "log": 5, "lq": 6}
+WORKLOAD_BY_FLAG = {"gdn": 2, "gdn_small": 1, "kda": 3, "q8": 4, "log": 5, "lq": 6, "rwkv6": 7,
+                    "rwkv6_log": 8}
 LQ_TOKENS = 4
 
 
@@ -49,11 +50,15 @@ def _in_bytes(w: wl.Workload) -> int:
     return 2 if w.qkv == "bf16" else 4
 
 
+def _beta_bytes(w: wl.Workload) -> int:
+    return 0 if w.variant == "rwkv6" else 4     # RWKV6 has no write strength
+
+
 def dense_bytes_per_head(w: wl.Workload) -> int:
     """State read + write (fp32), q/k/v in their dtype, gate, beta, y (fp32)."""
     d = wl.DK
     gate = 4 * d if w.per_key_gate else 4
-    return 2 * 4 * d * d + 3 * d * _in_bytes(w) + gate + 4 + 4 * d
+    return 2 * 4 * d * d + 3 * d * _in_bytes(w) + gate + _beta_bytes(w) + 4 * d
 
 
 def window_step_bytes_per_head(w: wl.Workload, pos: int) -> int:
@@ -84,12 +89,15 @@ def lq_step_bytes_per_head(w: wl.Workload, pos: int) -> int:
 
 def log_step_bytes_per_head(w: wl.Workload, L: int) -> int:
     """Base+log step with L live entries: base read, L entries read, lbar, inputs,
-    y, and either the entry + lbar write (append) or the base + lbar write (merge)."""
+    y, and either the entry + lbar write (append) or the base + lbar write (merge).
+    Entries hold k in the input dtype, the value factor in fp32 (delta rule) or in the
+    input dtype (RWKV6's raw value), and the log-decay snapshot."""
     d = wl.DK
     C = w.M - 1
     gdim = d if w.per_key_gate else 1
-    ent = d * _in_bytes(w) + 4 * d + 4 * gdim
-    inputs = 3 * d * _in_bytes(w) + 4 * gdim + 4
+    ubytes = _in_bytes(w) if w.variant == "rwkv6" else 4
+    ent = d * _in_bytes(w) + ubytes * d + 4 * gdim
+    inputs = 3 * d * _in_bytes(w) + 4 * gdim + _beta_bytes(w)
     rd = 4 * d * d + L * ent + 4 * gdim + inputs
     wr = 4 * d + (4 * d * d + 4 * gdim if L == C else ent + 4 * gdim)
     return rd + wr
@@ -197,7 +205,14 @@ def run_gpu(w: wl.Workload, steps: int, warmup: int, slots: bool = False, n_iter
     kda = w.per_key_gate
     state = {"t": 0}
 
-    if w.path == "dense":
+    if w.path == "dense" and w.variant == "rwkv6":
+        S = S0
+
+        def step():
+            i = state["t"] % n_inputs
+            rsu.rwkv6_decode_step(S, x["q"][i], x["k"][i], x["v"][i], x["gate"][i], y)
+            state["t"] += 1
+    elif w.path == "dense":
         fn = rsu.kda_decode_step if kda else rsu.gdn_decode_step
         S = S0
 
@@ -246,12 +261,20 @@ def run_gpu(w: wl.Workload, steps: int, warmup: int, slots: bool = False, n_iter
         lbar = torch.zeros((B, H, 128) if kda else (B, H), device=dev)
         cap = max(C, 1)
         Kl = torch.zeros(B, H, cap, 128, device=dev, dtype=x["q"].dtype)
-        Ul = torch.zeros(B, H, cap, 128, device=dev)
+        rwkv6 = w.variant == "rwkv6"
+        Ul = torch.zeros(B, H, cap, 128, device=dev, dtype=x["q"].dtype if rwkv6 else torch.float32)
         Lm = torch.zeros((B, H, cap, 128) if kda else (B, H, cap), device=dev)
+        if rwkv6:
+            # RWKV6's calls take no beta; wrap them to the delta-rule calls' argument list
+            def _nb(f):
+                return lambda C_, L_, Sb_, lb_, K_, U_, Lm_, q_, k_, v_, g_, b_, y_: \
+                    f(C_, L_, Sb_, lb_, K_, U_, Lm_, q_, k_, v_, g_, y_)
         if slots:
             # every request-head at its own point of the cycle: 1/M of them merge per step
             Ld = torch.from_numpy(slot_lengths(w)).to(dev).view(B, H)
             fs = rsu.kda_log_step_slots if kda else rsu.gdn_log_step_slots
+            if rwkv6:
+                fs = _nb(rsu.rwkv6_log_step_slots)
 
             def step():
                 i = state["t"] % n_inputs
@@ -261,6 +284,8 @@ def run_gpu(w: wl.Workload, steps: int, warmup: int, slots: bool = False, n_iter
         else:
             app = rsu.kda_log_append if kda else rsu.gdn_log_append
             mrg = rsu.kda_log_merge if kda else rsu.gdn_log_merge
+            if rwkv6:
+                app, mrg = _nb(rsu.rwkv6_log_append), _nb(rsu.rwkv6_log_merge)
             state["L"] = 0
 
             def step():
@@ -331,8 +356,10 @@ def override_workload(w: wl.Workload, args) -> wl.Workload:
     """Apply the command-line overrides; the workload's name records them."""
     ch = {}
     if args.variant and args.variant != w.variant:
-        ch.update(variant=args.variant, gate_lo=0.8 if args.variant == "kda" else 0.9,
-                  gate_hi=1.0 if args.variant == "kda" else 0.999)
+        if w.path not in ("dense", "log") and args.variant != "kda" or w.path == "lq_window":
+            raise SystemExit(f"--variant {args.variant} does not apply to the {w.path} workload")
+        per_key = args.variant in ("kda", "rwkv6")
+        ch.update(variant=args.variant, gate_lo=0.8 if per_key else 0.9, gate_hi=1.0 if per_key else 0.999)
     if args.B:
         ch["B"] = args.B
     if args.H:
@@ -360,8 +387,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", choices=sorted(WORKLOAD_BY_FLAG), default="gdn")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--variant", choices=["gdn", "kda"], default=None,
-                    help="override the gate kind of the workload (log and int8 paths)")
+    ap.add_argument("--variant", choices=["gdn", "kda", "rwkv6"], default=None,
+                    help="override the update kind of the workload (dense and log paths; kda also int8)")
     ap.add_argument("--B", type=int, default=None, help="override the batch size")
     ap.add_argument("--H", type=int, default=None, help="override the heads per request")
     ap.add_argument("--M", type=int, default=None, help="log path: merge interval (1..64)")

@@ -1,6 +1,7 @@
 /*
  * rsu.h -- C ABI of the MI355X (gfx950) decode-step library for delta-rule
- * recurrent states (Gated DeltaNet and Kimi Delta Attention).
+ * recurrent states (Gated DeltaNet and Kimi Delta Attention), and for RWKV6's
+ * decayed linear-attention state in the same common form.
  *
  * Per head the state S is d_k x d_v = 128 x 128; row i is a key channel and
  * column j a value channel. One decode step applies the retention gate g
@@ -212,6 +213,35 @@ int kda_log_step_slots(const rsu_dims *dims, int C, int *L, float *Sbase, float 
                        void *Klog, float *Ulog, float *Lam, const void *q, const void *k,
                        const void *v, const float *d, const float *beta, float *y,
                        rsu_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * RWKV6 in the pages' common form (DeltaLog Table 1, the RWKV6 row: state
+ * transform D(lambda) S, update pair (k, v), per-key decay; LeapQuant App. A,
+ * eq. 1 with read vector 0): no delta read and no beta,
+ *     S <- Diag(w) S + k v^T,   y = S^T q,
+ * with w [B,H,d_k] fp32 the per-key decay (w > 0 for the log calls, which take
+ * ln w). RWKV6's own extra term for the current token is not part of this form.
+ *
+ * rwkv6_decode_step: the dense fp32 state S, read once, written once, in place.
+ * rwkv6_log_append / rwkv6_log_merge / rwkv6_log_step_slots: the base + log
+ * representation as for KDA (lbar [B,H,d_k], Lam [B,H,C,d_k] fp32) with the
+ * value factor b = v: Ulog [B,H,C,d_v] holds the raw values in qkv_dtype (the
+ * page keeps both RWKV6 log factors in bf16, DeltaLog sec. 3.4 and Table 3).
+ * Arguments, ranges, the live-length protocol and errors as for the KDA calls,
+ * without beta.
+ * ---------------------------------------------------------------------- */
+int rwkv6_decode_step(const rsu_dims *dims, float *S, const void *q, const void *k,
+                      const void *v, const float *w, float *y, rsu_stream_t stream);
+int rwkv6_log_append(const rsu_dims *dims, int C, int L, const float *Sbase, float *lbar,
+                     void *Klog, void *Ulog, float *Lam, const void *q, const void *k,
+                     const void *v, const float *w, float *y, rsu_stream_t stream);
+int rwkv6_log_merge(const rsu_dims *dims, int C, int L, float *Sbase, float *lbar,
+                    const void *Klog, const void *Ulog, const float *Lam, const void *q,
+                    const void *k, const void *v, const float *w, float *y,
+                    rsu_stream_t stream);
+int rwkv6_log_step_slots(const rsu_dims *dims, int C, int *L, float *Sbase, float *lbar,
+                         void *Klog, void *Ulog, float *Lam, const void *q, const void *k,
+                         const void *v, const float *w, float *y, rsu_stream_t stream);
 
 /* ------------------------------------------------------------------------
  * Measurement helper (not part of the recurrence): dst[i] = src[i] for

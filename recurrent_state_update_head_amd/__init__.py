@@ -61,6 +61,10 @@ _SIGS = {
     "gdn_lq_window": [_DP, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
     "gdn_log_step_slots": [_DP, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
     "kda_log_step_slots": [_DP, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
+    "rwkv6_decode_step": [_DP, _P, _P, _P, _P, _P, _P, _P],
+    "rwkv6_log_append": [_DP, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
+    "rwkv6_log_merge": [_DP, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
+    "rwkv6_log_step_slots": [_DP, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
     "rsu_copy_f32": [_P, _P, ctypes.c_int64, _P],
 }
 for _name, _args in _SIGS.items():
@@ -241,6 +245,57 @@ def gdn_log_step_slots(C, L, Sbase, lbar, Klog, Ulog, Lam, q, k, v, alpha, beta,
 
 def kda_log_step_slots(C, L, Sbase, lbar, Klog, Ulog, Lam, q, k, v, d, beta, y):
     return _log_slots("kda_log_step_slots", True, C, L, Sbase, lbar, Klog, Ulog, Lam, q, k, v, d, beta, y)
+
+
+def rwkv6_decode_step(S, q, k, v, w, y):
+    """One RWKV6 step in the common form (S <- Diag(w) S + k v^T, y = S^T q; no beta):
+    S updated in place, y written. Returns y."""
+    dims = _dims(q, k, v)
+    _need(S, "S", torch.float32, (dims.B, dims.H, D, D))
+    _need(w, "w", torch.float32, (dims.B, dims.H, D))
+    _need(y, "y", torch.float32, (dims.B, dims.H, D))
+    _call("rwkv6_decode_step", ctypes.byref(dims), _ptr(S), _ptr(q), _ptr(k), _ptr(v), _ptr(w), _ptr(y),
+          _stream())
+    return y
+
+
+def _rwkv6_log(name, C, L, Sbase, lbar, Klog, Ulog, Lam, q, k, v, w, y):
+    """L: an int for the batch-uniform calls, an int32 [B,H] device tensor per slot."""
+    dims = _dims(q, k, v)
+    B, H = dims.B, dims.H
+    slots = isinstance(L, torch.Tensor)
+    if slots:
+        _need(L, "L", torch.int32, (B, H))
+    _need(Sbase, "Sbase", torch.float32, (B, H, D, D))
+    _need(lbar, "lbar", torch.float32, (B, H, D))
+    if C > 0:
+        _need(Klog, "Klog", q.dtype, (B, H, C, D))
+        _need(Ulog, "Ulog", q.dtype, (B, H, C, D))
+        _need(Lam, "Lam", torch.float32, (B, H, C, D))
+    _need(w, "w", torch.float32, (B, H, D))
+    _need(y, "y", torch.float32, (B, H, D))
+    _call(name, ctypes.byref(dims), int(C), _ptr(L) if slots else int(L), _ptr(Sbase), _ptr(lbar),
+          _ptr(Klog if C > 0 else None), _ptr(Ulog if C > 0 else None), _ptr(Lam if C > 0 else None),
+          _ptr(q), _ptr(k), _ptr(v), _ptr(w), _ptr(y), _stream())
+    return y
+
+
+def rwkv6_log_append(C, L, Sbase, lbar, Klog, Ulog, Lam, q, k, v, w, y):
+    """RWKV6 base + log step that appends (k, v) as entry L (requires L < C); Ulog holds
+    the raw values in q's dtype. The caller then sets L += 1."""
+    return _rwkv6_log("rwkv6_log_append", C, int(L), Sbase, lbar, Klog, Ulog, Lam, q, k, v, w, y)
+
+
+def rwkv6_log_merge(C, L, Sbase, lbar, Klog, Ulog, Lam, q, k, v, w, y):
+    """RWKV6 base + log step that folds the log into Sbase (requires L == C)."""
+    return _rwkv6_log("rwkv6_log_merge", C, int(L), Sbase, lbar, Klog, Ulog, Lam, q, k, v, w, y)
+
+
+def rwkv6_log_step_slots(C, L, Sbase, lbar, Klog, Ulog, Lam, q, k, v, w, y):
+    """RWKV6 base + log step with a live length per head (L: int32 [B,H] on the device)."""
+    if not isinstance(L, torch.Tensor):
+        raise ValueError("L must be an int32 [B, H] device tensor")
+    return _rwkv6_log("rwkv6_log_step_slots", C, L, Sbase, lbar, Klog, Ulog, Lam, q, k, v, w, y)
 
 
 def _lq_state(B, H, Z, col_absmax, row_smooth, Kc, Uc):

@@ -69,17 +69,25 @@ rsu::StepArgs step_args(int heads, float* S, const void* q, const void* k, const
     return a;
 }
 
-int dense_common(const char* fn, bool per_key, const rsu_dims* dims, float* S, const void* q,
+// The update kinds: scalar gate with the delta rule (GDN), per-key gate with the delta
+// rule (KDA), per-key decay without it (RWKV6: no beta).
+enum class Kind { gdn, kda, rwkv6 };
+const char* gate_name(Kind m) { return m == Kind::gdn ? "alpha" : m == Kind::kda ? "d" : "w"; }
+
+int dense_common(const char* fn, Kind m, const rsu_dims* dims, float* S, const void* q,
                  const void* k, const void* v, const float* gate, const float* beta, float* y,
                  rsu_stream_t stream) {
     int heads = 0;
     if (int rc = check_dims(dims, &heads, fn)) return rc;
     if (heads == 0) return RSU_OK;
-    if (int rc = check_ptrs({{S, "S"}, {q, "q"}, {k, "k"}, {v, "v"}, {gate, per_key ? "d" : "alpha"},
-                             {beta, "beta"}, {y, "y"}}, fn))
+    if (int rc = check_ptrs({{S, "S"}, {q, "q"}, {k, "k"}, {v, "v"}, {gate, gate_name(m)}, {y, "y"}}, fn))
         return rc;
-    return launched(rsu::launch_dense(step_args(heads, S, q, k, v, gate, beta, y), per_key,
-                                      dims->qkv_dtype == RSU_BF16, stream),
+    if (m != Kind::rwkv6)
+        if (int rc = check_ptrs({{beta, "beta"}}, fn)) return rc;
+    const rsu::StepArgs a = step_args(heads, S, q, k, v, gate, beta, y);
+    const bool bf16 = dims->qkv_dtype == RSU_BF16;
+    return launched(m == Kind::rwkv6 ? rsu::launch_rwkv6(a, bf16, stream)
+                                     : rsu::launch_dense(a, m == Kind::kda, bf16, stream),
                     fn);
 }
 
@@ -110,8 +118,8 @@ int window_common(const char* fn, bool per_key, const rsu_dims* dims, int W, int
 }
 
 // mode: 0 append, 1 merge, 2 per-slot live lengths (L ignored, Lslot used)
-int log_common(const char* fn, bool per_key, int mode, const rsu_dims* dims, int C, int L,
-               int* Lslot, float* Sbase, float* lbar, void* Klog, float* Ulog, float* Lam,
+int log_common(const char* fn, Kind m, int mode, const rsu_dims* dims, int C, int L,
+               int* Lslot, float* Sbase, float* lbar, void* Klog, void* Ulog, float* Lam,
                const void* q, const void* k, const void* v, const float* gate, const float* beta,
                float* y, rsu_stream_t stream) {
     int heads = 0;
@@ -122,8 +130,10 @@ int log_common(const char* fn, bool per_key, int mode, const rsu_dims* dims, int
         return fail(RSU_E_RANGE, "%s: append needs 0 <= L < C, got L=%d C=%d", fn, L, C);
     if (heads == 0) return RSU_OK;
     if (int rc = check_ptrs({{Sbase, "Sbase"}, {lbar, "lbar"}, {q, "q"}, {k, "k"}, {v, "v"},
-                             {gate, per_key ? "d" : "alpha"}, {beta, "beta"}, {y, "y"}}, fn))
+                             {gate, gate_name(m)}, {y, "y"}}, fn))
         return rc;
+    if (m != Kind::rwkv6)
+        if (int rc = check_ptrs({{beta, "beta"}}, fn)) return rc;
     if (C > 0)
         if (int rc = check_ptrs({{Klog, "Klog"}, {Ulog, "Ulog"}, {Lam, "Lam"}}, fn)) return rc;
     if (mode == 2)
@@ -136,8 +146,10 @@ int log_common(const char* fn, bool per_key, int mode, const rsu_dims* dims, int
     l.Klog = Klog;
     l.Ulog = Ulog;
     l.Lam = Lam;
-    return launched(rsu::launch_log(step_args(heads, Sbase, q, k, v, gate, beta, y), l, mode, per_key,
-                                    dims->qkv_dtype == RSU_BF16, stream),
+    const rsu::StepArgs a = step_args(heads, Sbase, q, k, v, gate, beta, y);
+    const bool bf16 = dims->qkv_dtype == RSU_BF16;
+    return launched(m == Kind::rwkv6 ? rsu::launch_rwkv6_log(a, l, mode, bf16, stream)
+                                     : rsu::launch_log(a, l, mode, m == Kind::kda, bf16, stream),
                     fn);
 }
 
@@ -151,12 +163,12 @@ const char* rsu_last_error(void) { return g_err; }
 
 int gdn_decode_step(const rsu_dims* dims, float* S, const void* q, const void* k, const void* v,
                     const float* alpha, const float* beta, float* y, rsu_stream_t stream) {
-    return dense_common("gdn_decode_step", false, dims, S, q, k, v, alpha, beta, y, stream);
+    return dense_common("gdn_decode_step", Kind::gdn, dims, S, q, k, v, alpha, beta, y, stream);
 }
 
 int kda_decode_step(const rsu_dims* dims, float* S, const void* q, const void* k, const void* v,
                     const float* d, const float* beta, float* y, rsu_stream_t stream) {
-    return dense_common("kda_decode_step", true, dims, S, q, k, v, d, beta, y, stream);
+    return dense_common("kda_decode_step", Kind::kda, dims, S, q, k, v, d, beta, y, stream);
 }
 
 int q8_quantize(const rsu_dims* dims, const float* S, int8_t* Z, float* row_absmax,
@@ -185,21 +197,21 @@ int kda_q8_window(const rsu_dims* dims, int W, int pos, int8_t* Z, float* row_ab
 int gdn_log_append(const rsu_dims* dims, int C, int L, const float* Sbase, float* lbar, void* Klog,
                    float* Ulog, float* Lam, const void* q, const void* k, const void* v,
                    const float* alpha, const float* beta, float* y, rsu_stream_t stream) {
-    return log_common("gdn_log_append", false, 0, dims, C, L, nullptr, const_cast<float*>(Sbase), lbar,
+    return log_common("gdn_log_append", Kind::gdn, 0, dims, C, L, nullptr, const_cast<float*>(Sbase), lbar,
                       Klog, Ulog, Lam, q, k, v, alpha, beta, y, stream);
 }
 
 int kda_log_append(const rsu_dims* dims, int C, int L, const float* Sbase, float* lbar, void* Klog,
                    float* Ulog, float* Lam, const void* q, const void* k, const void* v,
                    const float* d, const float* beta, float* y, rsu_stream_t stream) {
-    return log_common("kda_log_append", true, 0, dims, C, L, nullptr, const_cast<float*>(Sbase), lbar,
+    return log_common("kda_log_append", Kind::kda, 0, dims, C, L, nullptr, const_cast<float*>(Sbase), lbar,
                       Klog, Ulog, Lam, q, k, v, d, beta, y, stream);
 }
 
 int gdn_log_merge(const rsu_dims* dims, int C, int L, float* Sbase, float* lbar, const void* Klog,
                   const float* Ulog, const float* Lam, const void* q, const void* k, const void* v,
                   const float* alpha, const float* beta, float* y, rsu_stream_t stream) {
-    return log_common("gdn_log_merge", false, 1, dims, C, L, nullptr, Sbase, lbar, const_cast<void*>(Klog),
+    return log_common("gdn_log_merge", Kind::gdn, 1, dims, C, L, nullptr, Sbase, lbar, const_cast<void*>(Klog),
                       const_cast<float*>(Ulog), const_cast<float*>(Lam), q, k, v, alpha, beta, y,
                       stream);
 }
@@ -207,7 +219,7 @@ int gdn_log_merge(const rsu_dims* dims, int C, int L, float* Sbase, float* lbar,
 int kda_log_merge(const rsu_dims* dims, int C, int L, float* Sbase, float* lbar, const void* Klog,
                   const float* Ulog, const float* Lam, const void* q, const void* k, const void* v,
                   const float* d, const float* beta, float* y, rsu_stream_t stream) {
-    return log_common("kda_log_merge", true, 1, dims, C, L, nullptr, Sbase, lbar, const_cast<void*>(Klog),
+    return log_common("kda_log_merge", Kind::kda, 1, dims, C, L, nullptr, Sbase, lbar, const_cast<void*>(Klog),
                       const_cast<float*>(Ulog), const_cast<float*>(Lam), q, k, v, d, beta, y, stream);
 }
 
@@ -259,15 +271,42 @@ int gdn_lq_window(const rsu_dims* dims, int W, int pos, int n_iter, int8_t* Z, f
 int gdn_log_step_slots(const rsu_dims* dims, int C, int* L, float* Sbase, float* lbar, void* Klog,
                        float* Ulog, float* Lam, const void* q, const void* k, const void* v,
                        const float* alpha, const float* beta, float* y, rsu_stream_t stream) {
-    return log_common("gdn_log_step_slots", false, 2, dims, C, 0, L, Sbase, lbar, Klog, Ulog, Lam, q, k,
+    return log_common("gdn_log_step_slots", Kind::gdn, 2, dims, C, 0, L, Sbase, lbar, Klog, Ulog, Lam, q, k,
                       v, alpha, beta, y, stream);
 }
 
 int kda_log_step_slots(const rsu_dims* dims, int C, int* L, float* Sbase, float* lbar, void* Klog,
                        float* Ulog, float* Lam, const void* q, const void* k, const void* v,
                        const float* d, const float* beta, float* y, rsu_stream_t stream) {
-    return log_common("kda_log_step_slots", true, 2, dims, C, 0, L, Sbase, lbar, Klog, Ulog, Lam, q, k,
+    return log_common("kda_log_step_slots", Kind::kda, 2, dims, C, 0, L, Sbase, lbar, Klog, Ulog, Lam, q, k,
                       v, d, beta, y, stream);
+}
+
+int rwkv6_decode_step(const rsu_dims* dims, float* S, const void* q, const void* k, const void* v,
+                      const float* w, float* y, rsu_stream_t stream) {
+    return dense_common("rwkv6_decode_step", Kind::rwkv6, dims, S, q, k, v, w, nullptr, y, stream);
+}
+
+int rwkv6_log_append(const rsu_dims* dims, int C, int L, const float* Sbase, float* lbar, void* Klog,
+                     void* Ulog, float* Lam, const void* q, const void* k, const void* v, const float* w,
+                     float* y, rsu_stream_t stream) {
+    return log_common("rwkv6_log_append", Kind::rwkv6, 0, dims, C, L, nullptr, const_cast<float*>(Sbase),
+                      lbar, Klog, Ulog, Lam, q, k, v, w, nullptr, y, stream);
+}
+
+int rwkv6_log_merge(const rsu_dims* dims, int C, int L, float* Sbase, float* lbar, const void* Klog,
+                    const void* Ulog, const float* Lam, const void* q, const void* k, const void* v,
+                    const float* w, float* y, rsu_stream_t stream) {
+    return log_common("rwkv6_log_merge", Kind::rwkv6, 1, dims, C, L, nullptr, Sbase, lbar,
+                      const_cast<void*>(Klog), const_cast<void*>(Ulog), const_cast<float*>(Lam), q, k, v,
+                      w, nullptr, y, stream);
+}
+
+int rwkv6_log_step_slots(const rsu_dims* dims, int C, int* L, float* Sbase, float* lbar, void* Klog,
+                         void* Ulog, float* Lam, const void* q, const void* k, const void* v, const float* w,
+                         float* y, rsu_stream_t stream) {
+    return log_common("rwkv6_log_step_slots", Kind::rwkv6, 2, dims, C, 0, L, Sbase, lbar, Klog, Ulog, Lam, q,
+                      k, v, w, nullptr, y, stream);
 }
 
 int rsu_copy_f32(const float* src, float* dst, int64_t n, rsu_stream_t stream) {

@@ -19,6 +19,12 @@
 // per-slot live lengths (sec. 4 keeps the live length per request slot, so
 // requests admitted at different times are at different points of their cycle),
 // one call serves a mixed batch: an append pass, then a merge pass.
+//
+// RWKV6 (DeltaLog Table 1 and sec. 3.4: per-key decay, update pair (k, v)) takes the
+// same steps without the delta read: b = v, and its value-side factors are stored in
+// the input dtype (both factors bf16 for bf16 inputs, as the page's RWKV6 log keeps them).
+#include <type_traits>
+
 #include "kernels.hpp"
 #include "rsu_device.hpp"
 
@@ -45,10 +51,12 @@ enum LogMode { kAppendMode = 0, kMergeMode = 1, kSlotAppend = 2, kSlotMerge = 3 
 // the merge pass, launched after it, serves the heads with L == C and advances every
 // Lslot[h]. Two passes keep the appends at the append kernel's register budget (the
 // merge path holds the whole base tile through its update).
-template <bool kPerKey, int kMode, typename T>
+// kDelta: the delta rule's correction b = beta (v - p) (GDN, KDA); without it b = v
+// (RWKV6). UT: the stored type of the value-side factors.
+template <bool kPerKey, bool kDelta, int kMode, typename T, typename UT>
 __global__ __launch_bounds__(kThreads) void log_step_kernel(
     int C, int L_uniform, int* __restrict__ Lslot, float* __restrict__ Sbase,
-    float* __restrict__ lbar, T* __restrict__ Klog, float* __restrict__ Ulog,
+    float* __restrict__ lbar, T* __restrict__ Klog, UT* __restrict__ Ulog,
     float* __restrict__ Lam, const T* __restrict__ q, const T* __restrict__ k,
     const T* __restrict__ v, const float* __restrict__ gate, const float* __restrict__ beta,
     float* __restrict__ y) {
@@ -85,7 +93,7 @@ __global__ __launch_bounds__(kThreads) void log_step_kernel(
 
     // ---- loads: the first chunk of log entries, inputs, the base tile, then the rest
     Stager<T, kChunk * kD> sk;
-    Stager<float, kChunk * kD> su;
+    Stager<UT, kChunk * kD> su;
     Stager<float, kPerKey ? kChunk * kD : 8> sl;
     auto issue = [&](int m0) {
         const int n = min(kChunk, L - m0) * kD;
@@ -103,7 +111,7 @@ __global__ __launch_bounds__(kThreads) void log_step_kernel(
     if constexpr (!kPerKey)
         if (tid < L) lam_s = Lam[static_cast<size_t>(h) * C + tid];
     const f32x4 vv = load4_in(v, vec_off + col);
-    const float bt = beta[h];
+    const float bt = kDelta ? beta[h] : 1.f;
     const int r = tid & (kD - 1);
     const bool first = tid < kD;
     const float kr = load_in(k, vec_off + r), qr = load_in(q, vec_off + r);
@@ -188,22 +196,22 @@ __global__ __launch_bounds__(kThreads) void log_step_kernel(
 #pragma unroll
     for (int it = 0; it < kRowsPerThread; ++it) {
         const f32x4 rv = row_vec[it * 8 + ro];
-        p1 += s[it] * rv.x;
+        if constexpr (kDelta) p1 += s[it] * rv.x;
         p2 += s[it] * rv.y;
     }
     for (int m = ro; m < L; m += 8) {
         const f32x2 c = coef[m];
         const f32x4 u = *reinterpret_cast<const f32x4*>(Us + m * kD + col);
-        p1 += u * c.x;
+        if constexpr (kDelta) p1 += u * c.x;
         p2 += u * c.y;
     }
-    p1 = sum_row_lanes(p1);
+    if constexpr (kDelta) p1 = sum_row_lanes(p1);
     p2 = sum_row_lanes(p2);
     const float kq = kq_part[0] + kq_part[1];
-    const f32x4 b = bt * (vv - p1);
+    const f32x4 b = kDelta ? bt * (vv - p1) : vv;
     if (ro == 0) {
         *reinterpret_cast<f32x4*>(y + vec_off + col) = p2 + b * kq;
-        if (!merge) *reinterpret_cast<f32x4*>(Ulog + ent0 + static_cast<size_t>(L) * kD + col) = b;
+        if (!merge) store4_in(Ulog, ent0 + static_cast<size_t>(L) * kD + col, b);
     }
     if (!merge) return;
 
@@ -229,37 +237,47 @@ __global__ __launch_bounds__(kThreads) void log_step_kernel(
     for (int it = 0; it < kRowsPerThread; ++it) stream_store(Sh + (it * 8 + ro) * kD + col, s[it]);
 }
 
-template <bool kPerKey, int kMode, typename T>
+template <bool kPerKey, bool kDelta, int kMode, typename T>
 static hipError_t launch_log_t(const StepArgs& a, const LogArgs& l, hipStream_t stream) {
+    using UT = std::conditional_t<kDelta, float, T>;
+    constexpr auto kernel = log_step_kernel<kPerKey, kDelta, kMode, T, UT>;
     constexpr bool may_merge = kMode == kMergeMode || kMode == kSlotMerge;
     const int n = (kMode == kSlotAppend || kMode == kSlotMerge) ? l.C : l.L;
     const size_t lds = sizeof(float) * log_lds_floats(n, (l.C + 3) & ~3, kPerKey, may_merge);
     static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(log_step_kernel<kPerKey, kMode, T>),
+        reinterpret_cast<const void*>(kernel),
         hipFuncAttributeMaxDynamicSharedMemorySize,
         static_cast<int>(sizeof(float) * log_lds_floats(kMaxC, (kMaxC + 3) & ~3, kPerKey, may_merge)));
     if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL((log_step_kernel<kPerKey, kMode, T>), dim3(a.heads), dim3(kThreads), lds, stream,
-                       l.C, l.L, l.Lslot, a.S, l.lbar, static_cast<T*>(l.Klog), l.Ulog, l.Lam,
+    hipLaunchKernelGGL(kernel, dim3(a.heads), dim3(kThreads), lds, stream,
+                       l.C, l.L, l.Lslot, a.S, l.lbar, static_cast<T*>(l.Klog), static_cast<UT*>(l.Ulog), l.Lam,
                        static_cast<const T*>(a.q), static_cast<const T*>(a.k),
                        static_cast<const T*>(a.v), a.gate, a.beta, a.y);
     return hipGetLastError();
 }
 
-template <bool kPerKey, typename T>
+template <bool kPerKey, bool kDelta, typename T>
 static hipError_t launch_log_m(const StepArgs& a, const LogArgs& l, int mode, hipStream_t stream) {
     if (mode == 2) {  // per-slot step: the append pass, then the merge pass on the same stream
-        if (hipError_t e = launch_log_t<kPerKey, kSlotAppend, T>(a, l, stream)) return e;
-        return launch_log_t<kPerKey, kSlotMerge, T>(a, l, stream);
+        if (hipError_t e = launch_log_t<kPerKey, kDelta, kSlotAppend, T>(a, l, stream)) return e;
+        return launch_log_t<kPerKey, kDelta, kSlotMerge, T>(a, l, stream);
     }
-    return mode == kMergeMode ? launch_log_t<kPerKey, kMergeMode, T>(a, l, stream)
-                              : launch_log_t<kPerKey, kAppendMode, T>(a, l, stream);
+    return mode == kMergeMode ? launch_log_t<kPerKey, kDelta, kMergeMode, T>(a, l, stream)
+                              : launch_log_t<kPerKey, kDelta, kAppendMode, T>(a, l, stream);
 }
 
 hipError_t launch_log(const StepArgs& a, const LogArgs& l, int mode, bool per_key, bool bf16,
                       hipStream_t stream) {
-    if (per_key) return bf16 ? launch_log_m<true, bf16_t>(a, l, mode, stream) : launch_log_m<true, float>(a, l, mode, stream);
-    return bf16 ? launch_log_m<false, bf16_t>(a, l, mode, stream) : launch_log_m<false, float>(a, l, mode, stream);
+    if (per_key)
+        return bf16 ? launch_log_m<true, true, bf16_t>(a, l, mode, stream)
+                    : launch_log_m<true, true, float>(a, l, mode, stream);
+    return bf16 ? launch_log_m<false, true, bf16_t>(a, l, mode, stream)
+                : launch_log_m<false, true, float>(a, l, mode, stream);
+}
+
+hipError_t launch_rwkv6_log(const StepArgs& a, const LogArgs& l, int mode, bool bf16, hipStream_t stream) {
+    return bf16 ? launch_log_m<true, false, bf16_t>(a, l, mode, stream)
+                : launch_log_m<true, false, float>(a, l, mode, stream);
 }
 
 }  // namespace rsu

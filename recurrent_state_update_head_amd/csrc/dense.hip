@@ -1,9 +1,11 @@
-// dense.hip -- one eager decode step on the dense fp32 state (GDN and KDA).
+// dense.hip -- one eager decode step on the dense fp32 state (GDN, KDA, RWKV6).
 //
 // Recurrence (LeapQuant, App. A, the GDN and KDA expansions, with beta carried
 // by the correction): with g the gate (alpha repeated over the key rows for
 // GDN, the per-key vector d for KDA),
 //   p = S^T (g * k),  u = beta (v - p),  S <- Diag(g) S + k u^T,  y = S^T q.
+// RWKV6 (DeltaLog, Table 1; App. A eq. 1 with read vector 0) has no delta read:
+// u = v, with the per-key decay w as g.
 // The readout is taken from the updated state; it is evaluated in the same pass
 // as p through the identity S_new^T q = S^T (g * q) + u (k . q), so the state
 // is loaded once, reduced once (two column sums at the same time), updated in
@@ -15,7 +17,7 @@
 
 namespace rsu {
 
-template <bool kPerKey, typename T>
+template <bool kPerKey, bool kDelta, typename T>
 __global__ __launch_bounds__(kThreads) void dense_step_kernel(
     float* __restrict__ S, const T* __restrict__ q, const T* __restrict__ k,
     const T* __restrict__ v, const float* __restrict__ gate, const float* __restrict__ beta,
@@ -37,7 +39,7 @@ __global__ __launch_bounds__(kThreads) void dense_step_kernel(
     const float alpha = kPerKey ? 1.f : gate[h];
     const f32x2 g2 = kPerKey ? *reinterpret_cast<const f32x2*>(gate + vec_off + 2 * lane) : f32x2{alpha, alpha};
     const f32x4 vv = load4_in(v, vec_off + col);
-    const float b = beta[h];
+    const float b = kDelta ? beta[h] : 1.f;
 
     float* Sh = S + static_cast<size_t>(h) * kD * kD;
     f32x4 s[kRowsPerThread];
@@ -55,13 +57,13 @@ __global__ __launch_bounds__(kThreads) void dense_step_kernel(
 #pragma unroll
     for (int it = 0; it < kRowsPerThread; ++it) {
         const f32x4 rv = row_vec[wave][it * 8 + ro];
-        p += s[it] * rv.x;
+        if constexpr (kDelta) p += s[it] * rv.x;
         r += s[it] * rv.y;
     }
-    p = sum_row_lanes(p);
+    if constexpr (kDelta) p = sum_row_lanes(p);
     r = sum_row_lanes(r);
 
-    const f32x4 u = b * (vv - p);
+    const f32x4 u = kDelta ? b * (vv - p) : vv;
     if (ro == 0) *reinterpret_cast<f32x4*>(y + vec_off + col) = r + u * kq;
 
 #pragma unroll
@@ -93,17 +95,22 @@ __global__ __launch_bounds__(kThreads) void copy_kernel(const float* __restrict_
     }
 }
 
-template <bool kPerKey, typename T>
+template <bool kPerKey, bool kDelta, typename T>
 static hipError_t launch_dense_t(const StepArgs& a, hipStream_t stream) {
-    hipLaunchKernelGGL((dense_step_kernel<kPerKey, T>), dim3(a.heads), dim3(kThreads), 0, stream,
+    hipLaunchKernelGGL((dense_step_kernel<kPerKey, kDelta, T>), dim3(a.heads), dim3(kThreads), 0, stream,
                        a.S, static_cast<const T*>(a.q), static_cast<const T*>(a.k),
                        static_cast<const T*>(a.v), a.gate, a.beta, a.y);
     return hipGetLastError();
 }
 
 hipError_t launch_dense(const StepArgs& a, bool per_key, bool bf16, hipStream_t stream) {
-    if (per_key) return bf16 ? launch_dense_t<true, bf16_t>(a, stream) : launch_dense_t<true, float>(a, stream);
-    return bf16 ? launch_dense_t<false, bf16_t>(a, stream) : launch_dense_t<false, float>(a, stream);
+    if (per_key)
+        return bf16 ? launch_dense_t<true, true, bf16_t>(a, stream) : launch_dense_t<true, true, float>(a, stream);
+    return bf16 ? launch_dense_t<false, true, bf16_t>(a, stream) : launch_dense_t<false, true, float>(a, stream);
+}
+
+hipError_t launch_rwkv6(const StepArgs& a, bool bf16, hipStream_t stream) {
+    return bf16 ? launch_dense_t<true, false, bf16_t>(a, stream) : launch_dense_t<true, false, float>(a, stream);
 }
 
 hipError_t launch_copy(const float* src, float* dst, int64_t n, hipStream_t stream) {

@@ -33,11 +33,13 @@ struct LogArgs {
     int* Lslot;                   // per-slot live lengths [heads] (per-slot calls only)
     float* lbar;                  // [heads] or [heads, 128]
     void* Klog;                   // [heads, C, 128] in the input dtype
-    float* Ulog;                  // [heads, C, 128]
+    void* Ulog;                   // [heads, C, 128] fp32 (delta rule) or the input dtype (RWKV6)
     float* Lam;                   // [heads, C] or [heads, C, 128]
 };
 
 hipError_t launch_dense(const StepArgs& a, bool per_key, bool bf16, hipStream_t stream);
+// RWKV6: S <- Diag(w) S + k v^T, y = S^T q (gate = w [heads, 128]; beta unused)
+hipError_t launch_rwkv6(const StepArgs& a, bool bf16, hipStream_t stream);
 hipError_t launch_copy(const float* src, float* dst, int64_t n, hipStream_t stream);
 hipError_t launch_q8_quantize(int heads, const float* S, int8_t* Z, float* A, hipStream_t stream);
 hipError_t launch_q8_window(const StepArgs& a, const WindowArgs& w, bool per_key, bool bf16,
@@ -63,5 +65,6 @@ hipError_t launch_lq_window(const StepArgs& a, const LqArgs& w, hipStream_t stre
 // mode: 0 append, 1 merge, 2 per-slot live lengths
 hipError_t launch_log(const StepArgs& a, const LogArgs& l, int mode, bool per_key, bool bf16,
                       hipStream_t stream);
+hipError_t launch_rwkv6_log(const StepArgs& a, const LogArgs& l, int mode, bool bf16, hipStream_t stream);
 
 }  // namespace rsu

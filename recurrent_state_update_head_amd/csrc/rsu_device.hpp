@@ -107,6 +107,17 @@ __device__ __forceinline__ void store_in(bf16_t* p, size_t i, float x) {
     p[i] = static_cast<bf16_t>(__float_as_uint(x) >> 16);
 }
 
+// Four consecutive elements at a 4-element-aligned index (bf16: values that came from
+// bf16 inputs, copied bit-exactly).
+__device__ __forceinline__ void store4_in(float* p, size_t i, f32x4 x) {
+    *reinterpret_cast<f32x4*>(p + i) = x;
+}
+__device__ __forceinline__ void store4_in(bf16_t* p, size_t i, f32x4 x) {
+    const uint2 w = {(__float_as_uint(x.x) >> 16) | (__float_as_uint(x.y) & 0xffff0000u),
+                     (__float_as_uint(x.z) >> 16) | (__float_as_uint(x.w) & 0xffff0000u)};
+    *reinterpret_cast<uint2*>(p + i) = w;
+}
+
 // State streaming: the state is touched once per step, so bypass cache retention.
 __device__ __forceinline__ f32x4 stream_load(const float* p) {
     return __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));

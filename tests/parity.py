@@ -63,7 +63,7 @@ def take(t: torch.Tensor, heads_dev: torch.Tensor, inner) -> np.ndarray:
 
 
 def run_dense(w: wl.Workload, sample: int | None = None):
-    """Dense GDN/KDA steps on the GPU against the eager oracle; returns (max y err, final S err)."""
+    """Dense GDN/KDA/RWKV6 steps on the GPU against the eager oracle; returns (max y err, final S err)."""
     m = rsu()
     B, H = w.B, w.H
     S0 = wl.initial_state(w)
@@ -77,8 +77,12 @@ def run_dense(w: wl.Workload, sample: int | None = None):
     worst_y = 0.0
     for t in range(w.steps):
         x, d = dev_inputs(w, t)
-        fn(S, d["q"], d["k"], d["v"], d["gate"], d["beta"], y)
-        y_ref = oracle.dense_step(S_ref, *host_slice(x, heads))
+        if w.variant == "rwkv6":
+            m.rwkv6_decode_step(S, d["q"], d["k"], d["v"], d["gate"], y)
+            y_ref = oracle.rwkv6_step(S_ref, *host_slice(x, heads)[:4])
+        else:
+            fn(S, d["q"], d["k"], d["v"], d["gate"], d["beta"], y)
+            y_ref = oracle.dense_step(S_ref, *host_slice(x, heads))
         worst_y = max(worst_y, rel_err(take(y, hd, (128,)), y_ref))
     worst_S = rel_err(take(S, hd, (128, 128)), S_ref)
     return worst_y, worst_S
@@ -91,7 +95,8 @@ def new_log_buffers(w: wl.Workload, C: int):
     return {
         "lbar": torch.zeros((B, H, 128) if per_key else (B, H), device=DEV),
         "Klog": torch.zeros(B, H, cap, 128, device=DEV, dtype=qkv_dtype(w)),
-        "Ulog": torch.zeros(B, H, cap, 128, device=DEV),
+        "Ulog": torch.zeros(B, H, cap, 128, device=DEV,
+                            dtype=qkv_dtype(w) if w.variant == "rwkv6" else torch.float32),
         "Lam": torch.zeros((B, H, cap, 128) if per_key else (B, H, cap), device=DEV),
     }
 
@@ -101,6 +106,10 @@ def log_step(w: wl.Workload, C: int, L: int, Sbase, buf, d, y):
     m = rsu()
     kda = w.per_key_gate
     Klog, Ulog, Lam = (buf["Klog"], buf["Ulog"], buf["Lam"]) if C > 0 else (None, None, None)
+    if w.variant == "rwkv6":
+        fn = m.rwkv6_log_append if L < C else m.rwkv6_log_merge
+        fn(C, L, Sbase, buf["lbar"], Klog, Ulog, Lam, d["q"], d["k"], d["v"], d["gate"], y)
+        return L + 1 if L < C else 0
     if L < C:
         (m.kda_log_append if kda else m.gdn_log_append)(
             C, L, Sbase, buf["lbar"], Klog, Ulog, Lam, d["q"], d["k"], d["v"], d["gate"], d["beta"], y)
@@ -120,7 +129,7 @@ def run_log(w: wl.Workload, sample: int | None = None, steps: int | None = None)
     heads = np.arange(w.heads) if sample is None else wl.sample_heads(w, sample)
     hd = torch.from_numpy(heads).to(DEV)
     Sbase = torch.from_numpy(S0).to(DEV).view(B, H, 128, 128)
-    ref = oracle.LogState(S0[heads].astype(np.float64), C, w.per_key_gate)
+    ref = oracle.LogState(S0[heads].astype(np.float64), C, w.per_key_gate, rwkv6=w.variant == "rwkv6")
     del S0
     buf = new_log_buffers(w, C)
     y = torch.empty(B, H, 128, device=DEV)
@@ -137,7 +146,7 @@ def run_log(w: wl.Workload, sample: int | None = None, steps: int | None = None)
         else:
             m = L - 1
             gd = (128,) if w.per_key_gate else ()
-            Ug = take(buf["Ulog"][:, :, m], hd, (128,))
+            Ug = take(buf["Ulog"][:, :, m].float(), hd, (128,))
             err["Ulog"] = max(err["Ulog"], rel_err(Ug, ref.U[:, m]))
             Kg = take(buf["Klog"][:, :, m].float(), hd, (128,))
             err["Klog"] = max(err["Klog"], float(np.abs(Kg - ref.K[:, m]).max()))
@@ -162,7 +171,7 @@ def run_log_slots(w: wl.Workload, sample: int | None = None, steps: int | None =
     heads = np.arange(w.heads) if sample is None else wl.sample_heads(w, sample)
     hd = torch.from_numpy(heads).to(DEV)
     Sbase = torch.from_numpy(S0).to(DEV).view(B, H, 128, 128)
-    ref = oracle.LogState(S0[heads].astype(np.float64), C, w.per_key_gate)
+    ref = oracle.LogState(S0[heads].astype(np.float64), C, w.per_key_gate, rwkv6=w.variant == "rwkv6")
     del S0
     L_all = (np.arange(w.heads, dtype=np.int32) * 5) % (C + 1) if L0 is None else L0.astype(np.int32)
     Ld = torch.from_numpy(L_all.copy()).to(DEV).view(B, H)
@@ -170,6 +179,9 @@ def run_log_slots(w: wl.Workload, sample: int | None = None, steps: int | None =
     buf = new_log_buffers(w, C)
     Klog, Ulog, Lam = (buf["Klog"], buf["Ulog"], buf["Lam"]) if C > 0 else (None, None, None)
     fn = m.kda_log_step_slots if w.per_key_gate else m.gdn_log_step_slots
+    if w.variant == "rwkv6":
+        def fn(C, L, Sb, lb, K, U, Lm, q, k, v, g, b, y):
+            return m.rwkv6_log_step_slots(C, L, Sb, lb, K, U, Lm, q, k, v, g, y)
     y = torch.empty(B, H, 128, device=DEV)
     err = {"y": 0.0, "Sbase": 0.0, "lbar": 0.0, "Ulog": 0.0, "Klog": 0.0, "Lam": 0.0, "L": 0,
            "merges": 0, "appends": 0}
@@ -191,7 +203,8 @@ def run_log_slots(w: wl.Workload, sample: int | None = None, steps: int | None =
         for i in appended:
             mm = int(Lref[i]) - 1
             h = hd[i:i + 1]
-            err["Ulog"] = max(err["Ulog"], rel_err(take(buf["Ulog"][:, :, mm], h, (128,)), ref.U[i:i + 1, mm]))
+            err["Ulog"] = max(err["Ulog"], rel_err(take(buf["Ulog"][:, :, mm].float(), h, (128,)),
+                                                   ref.U[i:i + 1, mm]))
             err["Klog"] = max(err["Klog"], float(np.abs(take(buf["Klog"][:, :, mm].float(), h, (128,)) -
                                                          ref.K[i:i + 1, mm]).max()))
             err["Lam"] = max(err["Lam"], float(np.abs(take(buf["Lam"][:, :, mm], h, gd) -

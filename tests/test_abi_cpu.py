@@ -137,3 +137,29 @@ def test_copy_validation(lib):
     assert c(GOOD, GOOD, 6, None) == E_DIMS
     assert c(GOOD, ODD, 8, None) == E_ALIGN
     assert c(None, None, 0, None) == RSU_OK
+
+
+def test_rwkv6_validation(lib):
+    f = lib.rwkv6_decode_step
+    f.restype = ctypes.c_int
+    d = Dims(2, 3, 128, 128, 1)
+    # no beta: six arrays; a NULL decay is named as w
+    assert f(ctypes.byref(d), GOOD, GOOD, GOOD, GOOD, None, GOOD, None) == E_NULL
+    assert "w is NULL" in _last(lib)
+    assert f(ctypes.byref(Dims(2, 3, 128, 64, 1)), *([GOOD] * 6), None) == E_DIMS
+    assert f(ctypes.byref(d), GOOD, GOOD, GOOD, GOOD, GOOD, ODD, None) == E_ALIGN
+    assert f(ctypes.byref(Dims(0, 3, 128, 128, 1)), *([None] * 6), None) == RSU_OK
+    a = lib.rwkv6_log_append
+    a.restype = ctypes.c_int
+    m = lib.rwkv6_log_merge
+    m.restype = ctypes.c_int
+    sl = lib.rwkv6_log_step_slots
+    sl.restype = ctypes.c_int
+    largs = [GOOD] * 10                                        # Sbase .. y
+    assert a(ctypes.byref(d), 3, 3, *largs, None) == E_RANGE    # append needs L < C
+    assert m(ctypes.byref(d), 3, 2, *largs, None) == E_RANGE    # merge needs L == C
+    assert a(ctypes.byref(d), 64, 0, *largs, None) == E_RANGE
+    assert a(ctypes.byref(d), 3, 0, *([GOOD] * 8), None, GOOD, None) == E_NULL  # w
+    assert "w is NULL" in _last(lib)
+    assert sl(ctypes.byref(d), 3, None, *([GOOD] * 10), None) == E_NULL       # live lengths
+    assert sl(ctypes.byref(d), 3, GOOD, GOOD, GOOD, GOOD, ODD, *([GOOD] * 6), None) == E_ALIGN

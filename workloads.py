@@ -36,7 +36,7 @@ _TAG_S0, _TAG_Q, _TAG_K, _TAG_V, _TAG_GATE, _TAG_BETA, _TAG_OUTLIER = range(7)
 class Workload:
     cid: int
     name: str
-    variant: str          # "gdn" (scalar gate alpha) or "kda" (per-key gate d)
+    variant: str          # "gdn" (scalar gate alpha), "kda" (per-key gate d) or "rwkv6" (per-key decay w, no delta read)
     path: str             # "dense", "q8_window", "lq_window" or "log"
     B: int
     H: int
@@ -59,7 +59,7 @@ class Workload:
 
     @property
     def per_key_gate(self) -> bool:
-        return self.variant == "kda"
+        return self.variant in ("kda", "rwkv6")
 
 
 WORKLOADS = {
@@ -72,6 +72,10 @@ WORKLOADS = {
     # LeapQuant's boundary format on the int8 workload's own inputs (same seed as 4)
     6: Workload(4, "gdn_lq_window_b256_h48_w16", "gdn", "lq_window", 256, 48, 256, "bf16",
                 0.90, 0.999, W=16, outliers=True),
+    # RWKV6 at the shape of DeltaLog's kernel study (Table 3: 32 heads of 128 x 128, M = 4),
+    # batch 128 as in its interval sweep; per-key decays drawn like KDA's gates
+    7: Workload(7, "rwkv6_dense_b128_h32_bf16", "rwkv6", "dense", 128, 32, 32, "bf16", 0.80, 1.0),
+    8: Workload(8, "rwkv6_log_b128_h32_m4", "rwkv6", "log", 128, 32, 128, "bf16", 0.80, 1.0, M=4),
 }
 
 
