@@ -158,6 +158,39 @@ def test_eq10_readout_equals_dense_decoding_from_the_represented_state():
         recs.append((k[0], u, g[0]))
 
 
+def test_eq10_readout_with_per_key_decays_equals_dense_kda_decoding():
+    """Eq. 10 with KDA's per-key gates: Gamma is diagonal over the key rows, so it scales
+    the read vector row by row (payload and token keys alike) and each record's key;
+    term by term this equals dense KDA decoding from the represented state."""
+    d, W = 128, 5
+    S = _gapped(noise=0.05)
+    rep = lq.boundary(S, lq.walsh_start(), 1)
+    S0 = lq.represent(rep["Z"], rep["B"], rep["c"], rep["K16"], rep["U16"])
+    Sd = S0[None].copy()
+    recs = []
+    for t in range(W):
+        q = RNG.standard_normal((1, d))
+        k = RNG.standard_normal((1, d))
+        k /= np.linalg.norm(k)
+        v = RNG.standard_normal((1, d))
+        g = RNG.uniform(0.8, 1.0, (1, d))
+        b = np.array([RNG.uniform(0.0, 1.0)])
+        y_dense = oracle.dense_step(Sd, q, k, v, g, b)[0]
+        gam_all = np.prod([r[2] for r in recs] + [g[0]], axis=0)          # per key row
+
+        def read(x):
+            out = (rep["B"] / 127.0) * (rep["Z"].astype(np.float64).T @ (rep["c"] * gam_all * x))
+            out += rep["U16"] @ (rep["K16"].T @ (gam_all * x))
+            for j, (kj, uj, _) in enumerate(recs):
+                dec = np.prod([r[2] for r in recs[j + 1:]] + [g[0]], axis=0)
+                out += uj * (kj @ (dec * x))
+            return out
+        p = read(k[0])
+        u = b[0] * (v[0] - p)
+        np.testing.assert_allclose(read(q[0]) + u * (k[0] @ q[0]), y_dense, rtol=0, atol=1e-11)
+        recs.append((k[0], u, g[0]))
+
+
 def test_boundary_bytes_per_element_match_the_page():
     f = FIG["leapquant_boundary_bytes"]
     bpe = lq.bytes_per_element(f["dk"], f["r"])
