@@ -40,7 +40,7 @@ KERNEL_SOURCES = {
 }
 
 WORKLOAD_BY_FLAG = {"gdn": 2, "gdn_small": 1, "kda": 3, "q8": 4, "log": 5, "lq": 6, "rwkv6": 7,
-                    "rwkv6_log": 8}
+                    "rwkv6_log": 8, "kda_lq": 9}
 LQ_TOKENS = 4
 
 
@@ -79,8 +79,9 @@ def lq_step_bytes_per_head(w: wl.Workload, pos: int) -> int:
     per-row smoothing scales, the fp16 token pairs, the pos records, the step inputs, y,
     and either the record write or (at the boundary) the whole new representation."""
     d = wl.DK
-    rec = d * _in_bytes(w) + 4 * d + 4
-    inputs = 3 * d * _in_bytes(w) + 4 + 4
+    gdim = d if w.per_key_gate else 1
+    rec = d * _in_bytes(w) + 4 * d + 4 * gdim
+    inputs = 3 * d * _in_bytes(w) + 4 * gdim + 4
     rep = d * d + 4 * d + 4 * d + 2 * LQ_TOKENS * d * 2
     rd = rep + pos * rec + inputs
     wr = 4 * d + (rep if pos == w.W - 1 else rec)
@@ -243,17 +244,18 @@ def run_gpu(w: wl.Workload, steps: int, warmup: int, slots: bool = False, n_iter
         Cs = torch.empty(B, H, 128, device=dev)
         Kc = torch.empty(B, H, LQ_TOKENS, 128, device=dev, dtype=torch.float16)
         Uc = torch.empty_like(Kc)
-        rsu.gdn_lq_quantize(S0, 8, Z, Bc, Cs, Kc, Uc)
+        (rsu.kda_lq_quantize if kda else rsu.gdn_lq_quantize)(S0, 8, Z, Bc, Cs, Kc, Uc)
         del S0
         Kb = torch.zeros(B, H, W, 128, device=dev, dtype=x["q"].dtype)
         Ub = torch.zeros(B, H, W, 128, device=dev)
-        Gb = torch.zeros(B, H, W, device=dev)
+        Gb = torch.zeros((B, H, W, 128) if kda else (B, H, W), device=dev)
+        win = rsu.kda_lq_window if kda else rsu.gdn_lq_window
 
         def step():
             t = state["t"]
             i = t % n_inputs
-            rsu.gdn_lq_window(W, t % W, n_iter, Z, Bc, Cs, Kc, Uc, Kb, Ub, Gb, x["q"][i], x["k"][i], x["v"][i],
-                              x["gate"][i], x["beta"][i], y)
+            win(W, t % W, n_iter, Z, Bc, Cs, Kc, Uc, Kb, Ub, Gb, x["q"][i], x["k"][i], x["v"][i],
+                x["gate"][i], x["beta"][i], y)
             state["t"] += 1
     else:
         C = w.M - 1
@@ -356,7 +358,7 @@ def override_workload(w: wl.Workload, args) -> wl.Workload:
     """Apply the command-line overrides; the workload's name records them."""
     ch = {}
     if args.variant and args.variant != w.variant:
-        if w.path not in ("dense", "log") and args.variant != "kda" or w.path == "lq_window":
+        if w.path not in ("dense", "log") and args.variant != "kda":
             raise SystemExit(f"--variant {args.variant} does not apply to the {w.path} workload")
         per_key = args.variant in ("kda", "rwkv6")
         ch.update(variant=args.variant, gate_lo=0.8 if per_key else 0.9, gate_hi=1.0 if per_key else 0.999)

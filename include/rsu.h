@@ -159,7 +159,8 @@ int kda_log_merge(const rsu_dims *dims, int C, int L, float *Sbase, float *lbar,
 
 /* ------------------------------------------------------------------------
  * LeapQuant's window-boundary format (LeapQuant sec. 3.3 eqs. 5-6, sec. 3.4
- * eq. 7, App. B.3 eq. 10), for scalar gates (GDN). A window starts from
+ * eq. 7, App. B.3 eq. 10), for scalar (GDN) and per-key (KDA) gates. A window
+ * starts from
  *   S_0 = C dequant(Z, B) + Kt Ut^T,  C = Diag(row_smooth),
  *   dequant(Z, B)_ij = Z_ij * col_absmax_j / 127,
  * i.e. r = 4 compensator token pairs (Kt, Ut) in fp16 that hold the dominant
@@ -179,6 +180,9 @@ int kda_log_merge(const rsu_dims *dims, int C, int L, float *Sbase, float *lbar,
  *   Kbuf [B,H,W,d] bf16, Ubuf [B,H,W,d] fp32, Gbuf [B,H,W] fp32 as there), reading
  *   by eq. 10; at pos = W-1 it forms S_W, refits the tokens starting from the
  *   current Ut, and rewrites Z, col_absmax, row_smooth, Kc and Uc in place.
+ * kda_lq_window: the same with the per-key gate d [B,H,d_k] and Gbuf [B,H,W,d_k]
+ *   (Gamma in eq. 10 is diagonal over the key rows). kda_lq_quantize is the same
+ *   conversion as gdn_lq_quantize (the format does not depend on the gates).
  * Requires bf16 q/k/v (else RSU_E_DTYPE), 1 <= W <= 16, 0 <= pos < W,
  * 0 <= n_iter <= 64 (else RSU_E_RANGE). Other rules as for the int8 window.
  * ---------------------------------------------------------------------- */
@@ -189,6 +193,13 @@ int gdn_lq_window(const rsu_dims *dims, int W, int pos, int n_iter, int8_t *Z,
                   float *col_absmax, float *row_smooth, void *Kc, void *Uc, void *Kbuf,
                   float *Ubuf, float *Gbuf, const void *q, const void *k, const void *v,
                   const float *alpha, const float *beta, float *y, rsu_stream_t stream);
+int kda_lq_quantize(const rsu_dims *dims, const float *S, int n_iter, int8_t *Z,
+                    float *col_absmax, float *row_smooth, void *Kc, void *Uc,
+                    rsu_stream_t stream);
+int kda_lq_window(const rsu_dims *dims, int W, int pos, int n_iter, int8_t *Z,
+                  float *col_absmax, float *row_smooth, void *Kc, void *Uc, void *Kbuf,
+                  float *Ubuf, float *Gbuf, const void *q, const void *k, const void *v,
+                  const float *d, const float *beta, float *y, rsu_stream_t stream);
 
 /* ------------------------------------------------------------------------
  * Per-slot live lengths. DeltaLog sec. 4 keeps the live-log length as per-slot

@@ -59,6 +59,8 @@ _SIGS = {
     "kda_log_merge": [_DP, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
     "gdn_lq_quantize": [_DP, _P, _I, _P, _P, _P, _P, _P, _P],
     "gdn_lq_window": [_DP, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
+    "kda_lq_quantize": [_DP, _P, _I, _P, _P, _P, _P, _P, _P],
+    "kda_lq_window": [_DP, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
     "gdn_log_step_slots": [_DP, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
     "kda_log_step_slots": [_DP, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
     "rwkv6_decode_step": [_DP, _P, _P, _P, _P, _P, _P, _P],
@@ -306,33 +308,54 @@ def _lq_state(B, H, Z, col_absmax, row_smooth, Kc, Uc):
     _need(Uc, "Uc", torch.float16, (B, H, 4, D))
 
 
-def gdn_lq_quantize(S, n_iter, Z, col_absmax, row_smooth, Kc, Uc):
-    """Convert fp32 states into LeapQuant's boundary format (tokens fitted with n_iter
-    subspace iterations from the Walsh start)."""
+def _lq_quantize(name, S, n_iter, Z, col_absmax, row_smooth, Kc, Uc):
     if S.dim() != 4:
         raise ValueError("S must be [B, H, 128, 128]")
     B, H = S.shape[0], S.shape[1]
     _need(S, "S", torch.float32, (B, H, D, D))
     _lq_state(B, H, Z, col_absmax, row_smooth, Kc, Uc)
     dims = _Dims(B, H, D, D, RSU_F32)
-    _call("gdn_lq_quantize", ctypes.byref(dims), _ptr(S), int(n_iter), _ptr(Z), _ptr(col_absmax),
+    _call(name, ctypes.byref(dims), _ptr(S), int(n_iter), _ptr(Z), _ptr(col_absmax),
           _ptr(row_smooth), _ptr(Kc), _ptr(Uc), _stream())
 
 
-def gdn_lq_window(W, pos, n_iter, Z, col_absmax, row_smooth, Kc, Uc, Kbuf, Ubuf, Gbuf, q, k, v, alpha,
-                  beta, y):
-    """One decode step in LeapQuant's format (eq. 10 readout; at pos = W - 1 the refit)."""
+def gdn_lq_quantize(S, n_iter, Z, col_absmax, row_smooth, Kc, Uc):
+    """Convert fp32 states into LeapQuant's boundary format (tokens fitted with n_iter
+    subspace iterations from the Walsh start)."""
+    _lq_quantize("gdn_lq_quantize", S, n_iter, Z, col_absmax, row_smooth, Kc, Uc)
+
+
+def kda_lq_quantize(S, n_iter, Z, col_absmax, row_smooth, Kc, Uc):
+    """The same conversion for KDA states (the format does not depend on the gates)."""
+    _lq_quantize("kda_lq_quantize", S, n_iter, Z, col_absmax, row_smooth, Kc, Uc)
+
+
+def _lq_window(name, per_key, W, pos, n_iter, Z, col_absmax, row_smooth, Kc, Uc, Kbuf, Ubuf, Gbuf, q, k, v,
+               gate, beta, y):
     dims = _dims(q, k, v)
     B, H = dims.B, dims.H
     _lq_state(B, H, Z, col_absmax, row_smooth, Kc, Uc)
     _need(Kbuf, "Kbuf", q.dtype, (B, H, W, D))
     _need(Ubuf, "Ubuf", torch.float32, (B, H, W, D))
-    _need(Gbuf, "Gbuf", torch.float32, (B, H, W))
-    _step_common(dims, alpha, beta, y, False, "alpha")
-    _call("gdn_lq_window", ctypes.byref(dims), int(W), int(pos), int(n_iter), _ptr(Z), _ptr(col_absmax),
+    _need(Gbuf, "Gbuf", torch.float32, (B, H, W, D) if per_key else (B, H, W))
+    _step_common(dims, gate, beta, y, per_key, "d" if per_key else "alpha")
+    _call(name, ctypes.byref(dims), int(W), int(pos), int(n_iter), _ptr(Z), _ptr(col_absmax),
           _ptr(row_smooth), _ptr(Kc), _ptr(Uc), _ptr(Kbuf), _ptr(Ubuf), _ptr(Gbuf), _ptr(q), _ptr(k), _ptr(v),
-          _ptr(alpha), _ptr(beta), _ptr(y), _stream())
+          _ptr(gate), _ptr(beta), _ptr(y), _stream())
     return y
+
+
+def gdn_lq_window(W, pos, n_iter, Z, col_absmax, row_smooth, Kc, Uc, Kbuf, Ubuf, Gbuf, q, k, v, alpha,
+                  beta, y):
+    """One decode step in LeapQuant's format (eq. 10 readout; at pos = W - 1 the refit)."""
+    return _lq_window("gdn_lq_window", False, W, pos, n_iter, Z, col_absmax, row_smooth, Kc, Uc, Kbuf, Ubuf,
+                      Gbuf, q, k, v, alpha, beta, y)
+
+
+def kda_lq_window(W, pos, n_iter, Z, col_absmax, row_smooth, Kc, Uc, Kbuf, Ubuf, Gbuf, q, k, v, d, beta, y):
+    """The same step with KDA's per-key gate d (Gbuf holds [B, H, W, 128] gates)."""
+    return _lq_window("kda_lq_window", True, W, pos, n_iter, Z, col_absmax, row_smooth, Kc, Uc, Kbuf, Ubuf,
+                      Gbuf, q, k, v, d, beta, y)
 
 
 def copy_f32(src: torch.Tensor, dst: torch.Tensor):

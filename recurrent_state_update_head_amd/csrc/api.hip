@@ -153,6 +153,51 @@ int log_common(const char* fn, Kind m, int mode, const rsu_dims* dims, int C, in
                     fn);
 }
 
+int lq_quantize_common(const char* fn, const rsu_dims* dims, const float* S, int n_iter, int8_t* Z,
+                       float* col_absmax, float* row_smooth, void* Kc, void* Uc, rsu_stream_t stream) {
+    int heads = 0;
+    if (int rc = check_dims(dims, &heads, fn)) return rc;
+    if (n_iter < 0 || n_iter > 64) return fail(RSU_E_RANGE, "%s: n_iter=%d outside [0, 64]", fn, n_iter);
+    if (heads == 0) return RSU_OK;
+    if (int rc = check_ptrs({{S, "S"}, {Z, "Z"}, {col_absmax, "col_absmax"}, {row_smooth, "row_smooth"},
+                             {Kc, "Kc"}, {Uc, "Uc"}}, fn))
+        return rc;
+    return launched(rsu::launch_lq_quantize(heads, S, n_iter, Z, col_absmax, row_smooth, Kc, Uc, stream), fn);
+}
+
+int lq_window_common(const char* fn, Kind m, const rsu_dims* dims, int W, int pos, int n_iter, int8_t* Z,
+                     float* col_absmax, float* row_smooth, void* Kc, void* Uc, void* Kbuf, float* Ubuf,
+                     float* Gbuf, const void* q, const void* k, const void* v, const float* gate,
+                     const float* beta, float* y, rsu_stream_t stream) {
+    int heads = 0;
+    if (int rc = check_dims(dims, &heads, fn)) return rc;
+    if (dims->qkv_dtype != RSU_BF16)
+        return fail(RSU_E_DTYPE, "%s: only bf16 q/k/v are supported (the keys enter the MFMA exactly)", fn);
+    if (W < 1 || W > 16) return fail(RSU_E_RANGE, "%s: W=%d outside [1, 16]", fn, W);
+    if (pos < 0 || pos >= W) return fail(RSU_E_RANGE, "%s: pos=%d outside [0, W)", fn, pos);
+    if (n_iter < 0 || n_iter > 64) return fail(RSU_E_RANGE, "%s: n_iter=%d outside [0, 64]", fn, n_iter);
+    if (heads == 0) return RSU_OK;
+    if (int rc = check_ptrs({{Z, "Z"}, {col_absmax, "col_absmax"}, {row_smooth, "row_smooth"}, {Kc, "Kc"},
+                             {Uc, "Uc"}, {Kbuf, "Kbuf"}, {Ubuf, "Ubuf"}, {Gbuf, "Gbuf"}, {q, "q"}, {k, "k"},
+                             {v, "v"}, {gate, gate_name(m)}, {beta, "beta"}, {y, "y"}}, fn))
+        return rc;
+    rsu::LqArgs w;
+    w.W = W;
+    w.pos = pos;
+    w.n_iter = n_iter;
+    w.Z = Z;
+    w.B = col_absmax;
+    w.C = row_smooth;
+    w.Kc = Kc;
+    w.Uc = Uc;
+    w.Kbuf = Kbuf;
+    w.Ubuf = Ubuf;
+    w.Gbuf = Gbuf;
+    return launched(rsu::launch_lq_window(step_args(heads, nullptr, q, k, v, gate, beta, y), w, m == Kind::kda,
+                                          stream),
+                    fn);
+}
+
 }  // namespace
 
 extern "C" {
@@ -225,47 +270,28 @@ int kda_log_merge(const rsu_dims* dims, int C, int L, float* Sbase, float* lbar,
 
 int gdn_lq_quantize(const rsu_dims* dims, const float* S, int n_iter, int8_t* Z, float* col_absmax,
                     float* row_smooth, void* Kc, void* Uc, rsu_stream_t stream) {
-    const char* fn = "gdn_lq_quantize";
-    int heads = 0;
-    if (int rc = check_dims(dims, &heads, fn)) return rc;
-    if (n_iter < 0 || n_iter > 64) return fail(RSU_E_RANGE, "%s: n_iter=%d outside [0, 64]", fn, n_iter);
-    if (heads == 0) return RSU_OK;
-    if (int rc = check_ptrs({{S, "S"}, {Z, "Z"}, {col_absmax, "col_absmax"}, {row_smooth, "row_smooth"},
-                             {Kc, "Kc"}, {Uc, "Uc"}}, fn))
-        return rc;
-    return launched(rsu::launch_lq_quantize(heads, S, n_iter, Z, col_absmax, row_smooth, Kc, Uc, stream), fn);
+    return lq_quantize_common("gdn_lq_quantize", dims, S, n_iter, Z, col_absmax, row_smooth, Kc, Uc, stream);
+}
+
+int kda_lq_quantize(const rsu_dims* dims, const float* S, int n_iter, int8_t* Z, float* col_absmax,
+                    float* row_smooth, void* Kc, void* Uc, rsu_stream_t stream) {
+    return lq_quantize_common("kda_lq_quantize", dims, S, n_iter, Z, col_absmax, row_smooth, Kc, Uc, stream);
 }
 
 int gdn_lq_window(const rsu_dims* dims, int W, int pos, int n_iter, int8_t* Z, float* col_absmax,
                   float* row_smooth, void* Kc, void* Uc, void* Kbuf, float* Ubuf, float* Gbuf,
                   const void* q, const void* k, const void* v, const float* alpha, const float* beta,
                   float* y, rsu_stream_t stream) {
-    const char* fn = "gdn_lq_window";
-    int heads = 0;
-    if (int rc = check_dims(dims, &heads, fn)) return rc;
-    if (dims->qkv_dtype != RSU_BF16)
-        return fail(RSU_E_DTYPE, "%s: only bf16 q/k/v are supported (the keys enter the MFMA exactly)", fn);
-    if (W < 1 || W > 16) return fail(RSU_E_RANGE, "%s: W=%d outside [1, 16]", fn, W);
-    if (pos < 0 || pos >= W) return fail(RSU_E_RANGE, "%s: pos=%d outside [0, W)", fn, pos);
-    if (n_iter < 0 || n_iter > 64) return fail(RSU_E_RANGE, "%s: n_iter=%d outside [0, 64]", fn, n_iter);
-    if (heads == 0) return RSU_OK;
-    if (int rc = check_ptrs({{Z, "Z"}, {col_absmax, "col_absmax"}, {row_smooth, "row_smooth"}, {Kc, "Kc"},
-                             {Uc, "Uc"}, {Kbuf, "Kbuf"}, {Ubuf, "Ubuf"}, {Gbuf, "Gbuf"}, {q, "q"}, {k, "k"},
-                             {v, "v"}, {alpha, "alpha"}, {beta, "beta"}, {y, "y"}}, fn))
-        return rc;
-    rsu::LqArgs w;
-    w.W = W;
-    w.pos = pos;
-    w.n_iter = n_iter;
-    w.Z = Z;
-    w.B = col_absmax;
-    w.C = row_smooth;
-    w.Kc = Kc;
-    w.Uc = Uc;
-    w.Kbuf = Kbuf;
-    w.Ubuf = Ubuf;
-    w.Gbuf = Gbuf;
-    return launched(rsu::launch_lq_window(step_args(heads, nullptr, q, k, v, alpha, beta, y), w, stream), fn);
+    return lq_window_common("gdn_lq_window", Kind::gdn, dims, W, pos, n_iter, Z, col_absmax, row_smooth, Kc, Uc,
+                            Kbuf, Ubuf, Gbuf, q, k, v, alpha, beta, y, stream);
+}
+
+int kda_lq_window(const rsu_dims* dims, int W, int pos, int n_iter, int8_t* Z, float* col_absmax,
+                  float* row_smooth, void* Kc, void* Uc, void* Kbuf, float* Ubuf, float* Gbuf,
+                  const void* q, const void* k, const void* v, const float* d, const float* beta,
+                  float* y, rsu_stream_t stream) {
+    return lq_window_common("kda_lq_window", Kind::kda, dims, W, pos, n_iter, Z, col_absmax, row_smooth, Kc, Uc,
+                            Kbuf, Ubuf, Gbuf, q, k, v, d, beta, y, stream);
 }
 
 int gdn_log_step_slots(const rsu_dims* dims, int C, int* L, float* Sbase, float* lbar, void* Klog,

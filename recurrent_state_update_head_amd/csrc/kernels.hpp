@@ -44,7 +44,7 @@ hipError_t launch_copy(const float* src, float* dst, int64_t n, hipStream_t stre
 hipError_t launch_q8_quantize(int heads, const float* S, int8_t* Z, float* A, hipStream_t stream);
 hipError_t launch_q8_window(const StepArgs& a, const WindowArgs& w, bool per_key, bool bf16,
                             hipStream_t stream);
-// LeapQuant's boundary format (GDN, bf16 keys, W <= 16): payload, per-column absmax,
+// LeapQuant's boundary format (GDN or KDA, bf16 keys, W <= 16): payload, per-column absmax,
 // per-row smoothing scales, fp16 token pairs [heads][4][128], and the window's records.
 struct LqArgs {
     int W, pos, n_iter;
@@ -55,12 +55,12 @@ struct LqArgs {
     void* Uc;                     // [heads, 4, 128] fp16
     void* Kbuf;                   // [heads, W, 128] bf16
     float* Ubuf;                  // [heads, W, 128]
-    float* Gbuf;                  // [heads, W]
+    float* Gbuf;                  // [heads, W] (GDN) or [heads, W, 128] (KDA)
 };
 
 hipError_t launch_lq_quantize(int heads, const float* S, int n_iter, int8_t* Z, float* B, float* C,
                               void* Kc, void* Uc, hipStream_t stream);
-hipError_t launch_lq_window(const StepArgs& a, const LqArgs& w, hipStream_t stream);
+hipError_t launch_lq_window(const StepArgs& a, const LqArgs& w, bool per_key, hipStream_t stream);
 
 // mode: 0 append, 1 merge, 2 per-slot live lengths
 hipError_t launch_log(const StepArgs& a, const LogArgs& l, int mode, bool per_key, bool bf16,

@@ -274,12 +274,18 @@ __global__ __launch_bounds__(kThreads) void lq_quantize_kernel(const float* __re
 // for the record coefficients, row-owners for the record corrections); the tokens are
 // four more records: groups 0..3 reduce (Kt_t . k, Kt_t . q) and owners 0..3 add
 // Ut_t c_t. The swept payload partials are scaled by B_j / 127 per column first.
+// With per-key gates (KDA) Gamma is diagonal over the key rows: the records' gates are
+// staged in LDS, each lane forms the decay products of its 8 keys (after its record
+// for the record terms, over the whole window for the token terms), and the payload's
+// read vector takes the decay of its own row.
+template <bool kPerKey>
 __global__ __launch_bounds__(kThreads) void lq_step_kernel(
     int W, int pos, const int8_t* __restrict__ Z, const float* __restrict__ Bcol,
     const float* __restrict__ Csm, const half_t* __restrict__ Kc, const half_t* __restrict__ Uc,
     bf16_t* __restrict__ Kbuf, float* __restrict__ Ubuf, float* __restrict__ Gbuf,
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const float* __restrict__ gate, const float* __restrict__ beta, float* __restrict__ y) {
+    extern __shared__ __align__(16) float gs_lds[];   // KDA: the records' gates [pos][128]
     __shared__ f32x2 rowv[kD];
     __shared__ f32x2 coef[16];
     __shared__ f32x2 ctok[kTok];
@@ -315,12 +321,20 @@ __global__ __launch_bounds__(kThreads) void lq_step_kernel(
     if (grp < kTok) ktw = *reinterpret_cast<const uint4*>(Kc + tok0 + grp * kD + 8 * ch);
     uint2 utw = {0u, 0u};
     if (owner < kTok) utw = *reinterpret_cast<const uint2*>(Uc + tok0 + owner * kD + 4 * c4);
-    const float g_lane = lane < pos ? Gbuf[static_cast<size_t>(h) * W + lane] : 1.f;
+    float g_lane = 1.f;  // GDN: lane i holds the gate of record i
+    Stager<float, kPerKey ? 16 * kD : 8> sg;
+    if constexpr (kPerKey) sg.load(Gbuf + rec0, pos * kD, tid);
+    else if (lane < pos) g_lane = Gbuf[static_cast<size_t>(h) * W + lane];
     const uint4 kchw = *reinterpret_cast<const uint4*>(k + vec_off + 8 * ch);
     const uint4 qchw = *reinterpret_cast<const uint4*>(q + vec_off + 8 * ch);
+    f32x4 gch_lo = {1.f, 1.f, 1.f, 1.f}, gch_hi = {1.f, 1.f, 1.f, 1.f};  // KDA: current gates of the 8 keys
+    if constexpr (kPerKey) {
+        gch_lo = *reinterpret_cast<const f32x4*>(gate + vec_off + 8 * ch);
+        gch_hi = *reinterpret_cast<const f32x4*>(gate + vec_off + 8 * ch + 4);
+    }
     const f32x4 bsc = *reinterpret_cast<const f32x4*>(Bcol + vec_off + 4 * c4) * (1.f / 127.f);
     const float kr = load_in(k, vec_off + r), qr = load_in(q, vec_off + r);
-    const float gr = gate[h];
+    const float gr = kPerKey ? gate[vec_off + r] : gate[h];
     const float cr = Csm[vec_off + r];
     const float vr = load_in(v, vec_off + r);
     const float bt = beta[h];
@@ -330,13 +344,37 @@ __global__ __launch_bounds__(kThreads) void lq_step_kernel(
     for (int it = 0; it < kRowsPerThread; ++it)
         zw[it] = __builtin_nontemporal_load(Zh + lq_row(it, wave, ro) * (kD / 4) + c4);
 
-    // ---- decays (newest gate first): after record grp, and over the whole window so far
+    // ---- decays (newest gate first): after record grp, and over the whole window so far.
+    // Per key (KDA): Ge[e] after record grp and Gt[e] over the window for the lane's 8
+    // keys, Gall for row r; the current gate comes on top of each.
     float Gg = 1.f, Gall = 1.f;
-    for (int i = pos - 1; i >= 0; --i) {
-        const float gi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, g_lane), i));
-        Gg = i > grp ? Gg * gi : Gg;
-        Gall *= gi;
+    float Ge[kPerKey ? 8 : 1], Gt[kPerKey ? 8 : 1];
+    if constexpr (!kPerKey) {
+        for (int i = pos - 1; i >= 0; --i) {
+            const float gi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, g_lane), i));
+            Gg = i > grp ? Gg * gi : Gg;
+            Gall *= gi;
+        }
+    } else {
+        sg.store(gs_lds, tid);
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < 8; ++e) Ge[e] = Gt[e] = 1.f;
+        for (int i = pos - 1; i >= 0; --i) {
+            const f32x4 lo = *reinterpret_cast<const f32x4*>(gs_lds + i * kD + 8 * ch);
+            const f32x4 hi = *reinterpret_cast<const f32x4*>(gs_lds + i * kD + 8 * ch + 4);
+            const bool after = i > grp;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                Gt[e] *= lo[e];
+                Gt[e + 4] *= hi[e];
+                Ge[e] = after ? Ge[e] * lo[e] : Ge[e];
+                Ge[e + 4] = after ? Ge[e + 4] * hi[e] : Ge[e + 4];
+            }
+        }
+        for (int i = pos - 1; i >= 0; --i) Gall *= gs_lds[i * kD + r];
     }
+    auto gcur = [&](int e) { return e < 4 ? gch_lo[e] : gch_hi[e - 4]; };
     const uint32_t kcw[4] = {kchw.x, kchw.y, kchw.z, kchw.w};
     const uint32_t qcw[4] = {qchw.x, qchw.y, qchw.z, qchw.w};
     auto bfe = [](const uint32_t (&w)[4], int e) {
@@ -346,7 +384,7 @@ __global__ __launch_bounds__(kThreads) void lq_step_kernel(
         float ck = 0.f, cq = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const float ej = bfe(kc, e) * (Gg * gr);
+            const float ej = bfe(kc, e) * (kPerKey ? Ge[e] * gcur(e) : Gg * gr);
             ck += ej * bfe(kcw, e);
             cq += ej * bfe(qcw, e);
         }
@@ -359,7 +397,7 @@ __global__ __launch_bounds__(kThreads) void lq_step_kernel(
         float ck = 0.f, cq = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const float ej = static_cast<float>(kt[e]) * (Gall * gr);
+            const float ej = static_cast<float>(kt[e]) * (kPerKey ? Gt[e] * gcur(e) : Gall * gr);
             ck += ej * bfe(kcw, e);
             cq += ej * bfe(qcw, e);
         }
@@ -421,7 +459,8 @@ __global__ __launch_bounds__(kThreads) void lq_step_kernel(
         const size_t rec = rec0 + static_cast<size_t>(pos) * kD;
         Ubuf[rec + c] = u;
         store_in(Kbuf, rec + c, kr);
-        if (c == 0) Gbuf[static_cast<size_t>(h) * W + pos] = gr;
+        if (kPerKey) Gbuf[rec + c] = gr;
+        else if (c == 0) Gbuf[static_cast<size_t>(h) * W + pos] = gr;
     }
 }
 
@@ -694,6 +733,243 @@ __global__ __launch_bounds__(kThreads) void lq_boundary_kernel(
     lq_refit(L, s, n_iter, tid, Zh, Bcol + vec_off, Csm + vec_off, Kc + tok0, Uc + tok0);
 }
 
+// ---------------------------------------------------------------- the last step, per-key gates
+// KDA's boundary. The step as in the general per-row int8 boundary: records, their gates
+// and keys staged in LDS as fp32, the decayed keys E_j = Gamma_{j+1:W} k_j formed by one
+// thread per key row walking the records backwards; the payload terms scaled by c and B,
+// and the token pairs as four more records whose keys carry the whole window's decay.
+// S_W = Gamma_{1:W} (C dequant(Z, B) + Kt Ut^T) + sum_j E_j u_j^T then forms on the
+// matrix cores in fp32 (the decayed keys are not bf16-exact): per 16 x 16 tile the
+// payload initialises the accumulator, four v_mfma_f32_16x16x4f32 add the 16 records and
+// one adds the 4 tokens, using the general boundary's operand layout (tile ct holds the
+// value columns 8m + ct; lane l ends with columns 32(l/16) + 8i + ct of its row). The
+// result passes through LDS into the refit's register layout.
+constexpr int kKdaRec = 16;
+// floats of the step-phase arrays: KE, Us, Gs [16][128], Zs, decayed token keys and
+// token values [4][128], red [4][128] x 2
+constexpr int kKdaStepFloats = 3 * kKdaRec * kD + kD * kZsStride + 2 * kTok * kD + 4 * kD * 2;
+static_assert(kKdaStepFloats <= kD * kD, "the step-phase arrays must lie inside the shared region");
+
+__global__ __launch_bounds__(kThreads) void lq_boundary_kda_kernel(
+    int W, int pos, int n_iter, int8_t* __restrict__ Z, float* __restrict__ Bcol, float* __restrict__ Csm,
+    half_t* __restrict__ Kc, half_t* __restrict__ Uc, const bf16_t* __restrict__ Kbuf,
+    const float* __restrict__ Ubuf, const float* __restrict__ Gbuf, const bf16_t* __restrict__ q,
+    const bf16_t* __restrict__ k, const bf16_t* __restrict__ v, const float* __restrict__ gate,
+    const float* __restrict__ beta, float* __restrict__ y) {
+    extern __shared__ __align__(16) float dyn_lds[];
+    __shared__ f32x2 rowv[kD];       // c_r Gamma_{1:W,r} (k_r, q_r)
+    __shared__ f32x2 kq_row[kD];     // (k_r, q_r)
+    __shared__ f32x2 coef[kKdaRec];  // per record (E_j . k, E_j . q)
+    __shared__ f32x2 ctok[kTok];     // per token ((Gamma Kt_t) . k, (Gamma Kt_t) . q)
+    __shared__ float kq_part[2];
+    __shared__ float zcoef[kD];      // c_r Gamma_{1:W,r}
+
+    float* KE = dyn_lds;                                            // [16][128]
+    float* Us = KE + kKdaRec * kD;                                  // [16][128]
+    float* Gs = Us + kKdaRec * kD;                                  // [16][128]
+    uint32_t* Zs = reinterpret_cast<uint32_t*>(Gs + kKdaRec * kD);  // [128][33]
+    float* Kt4 = reinterpret_cast<float*>(Zs + kD * kZsStride);    // [4][128] Gamma_{1:W} Kt
+    float* Ut4 = Kt4 + kTok * kD;                                   // [4][128] Ut
+    f32x2* red = reinterpret_cast<f32x2*>(Ut4 + kTok * kD);        // [4][128]
+    const RefitLds L(dyn_lds, dyn_lds + kD * kD);
+    float* bscs = dyn_lds + kD * kD + 4 * kD;                       // B / 127 of the old payload
+
+    const int h = head_of_block(blockIdx.x, gridDim.x), tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
+    const int c4 = lane & 31, ro = lane >> 5;
+    const int r = tid & (kD - 1);
+    const bool first = tid < kD;
+    const size_t vec_off = static_cast<size_t>(h) * kD;
+    const size_t rec0 = static_cast<size_t>(h) * W * kD;
+    const size_t tok0 = static_cast<size_t>(h) * kTok * kD;
+    uint32_t* Zh = reinterpret_cast<uint32_t*>(Z + static_cast<size_t>(h) * kD * kD);
+
+    // ---- loads: records, gates, tokens and inputs first, then the codes
+    Stager<bf16_t, kKdaRec * kD> sk;
+    Stager<float, kKdaRec * kD> su;
+    Stager<float, kKdaRec * kD> sg;
+    sk.load(Kbuf + rec0, pos * kD, tid);
+    su.load(Ubuf + rec0, pos * kD, tid);
+    sg.load(Gbuf + rec0, pos * kD, tid);
+    half_t tokv[kTok];  // token t at row / column r (threads < 128: keys; threads >= 128: values)
+#pragma unroll
+    for (int t = 0; t < kTok; ++t) tokv[t] = (first ? Kc : Uc)[tok0 + t * kD + r];
+    const float kr = load_in(k, vec_off + r), qr = load_in(q, vec_off + r);
+    const float gr = gate[vec_off + r];
+    const float cr = Csm[vec_off + r];
+    const float bcc = Bcol[vec_off + r];
+    const float vr = load_in(v, vec_off + r);
+    const float bt = beta[h];
+    uint32_t zw[kRowsPerThread];
+#pragma unroll
+    for (int it = 0; it < kRowsPerThread; ++it)
+        zw[it] = __builtin_nontemporal_load(Zh + lq_row(it, wave, ro) * (kD / 4) + c4);
+
+    sk.store(KE, tid);
+    su.store(Us, tid);
+    sg.store(Gs, tid);
+    for (int i = pos * kD + tid; i < kKdaRec * kD; i += kThreads) Us[i] = 0.f;  // rows pos .. 15
+    __syncthreads();
+
+    // ---- decayed keys in place (thread r < 128 walks key row r from the newest record),
+    // read vectors, token keys with the whole window's decay; token values and the refit's
+    // start (the old Ut, unscaled) from threads >= 128
+    if (first) {
+        float G = 1.f;
+        for (int j = pos - 1; j >= 0; --j) {
+            KE[j * kD + r] *= G * gr;
+            G *= Gs[j * kD + r];
+        }
+        const float gam = G * gr;  // Gamma_{1:W} at row r
+        const float c0 = cr * gam;
+        rowv[r] = f32x2{c0 * kr, c0 * qr};
+        kq_row[r] = f32x2{kr, qr};
+        zcoef[r] = c0;
+        KE[pos * kD + r] = kr;  // the current record: no decay after it
+        for (int j = pos + 1; j < kKdaRec; ++j) KE[j * kD + r] = 0.f;
+#pragma unroll
+        for (int t = 0; t < kTok; ++t) Kt4[t * kD + r] = static_cast<float>(tokv[t]) * gam;
+        const float kq = wave_sum(kr * qr);
+        if (lane == 0) kq_part[wave] = kq;
+    } else {
+#pragma unroll
+        for (int t = 0; t < kTok; ++t) Ut4[t * kD + r] = static_cast<float>(tokv[t]);
+        L.W[r] = f32x4{static_cast<float>(tokv[0]), static_cast<float>(tokv[1]), static_cast<float>(tokv[2]),
+                       static_cast<float>(tokv[3])};
+        bscs[r] = bcc * (1.f / 127.f);
+    }
+    __syncthreads();
+
+    // ---- record and token coefficients: the 16 lanes of a DPP row reduce one (8 rows each)
+    {
+        const int chunk = tid & 15, j = tid >> 4;
+        auto dot8 = [&](const float* e) {
+            const f32x4 e0 = *reinterpret_cast<const f32x4*>(e + 8 * chunk);
+            const f32x4 e1 = *reinterpret_cast<const f32x4*>(e + 8 * chunk + 4);
+            const f32x2* kqr = kq_row + 8 * chunk;
+            f32x2 c = e0.x * kqr[0] + e0.y * kqr[1] + e0.z * kqr[2] + e0.w * kqr[3] + e1.x * kqr[4] +
+                      e1.y * kqr[5] + e1.z * kqr[6] + e1.w * kqr[7];
+            return f32x2{row16_sum(c.x), row16_sum(c.y)};
+        };
+        const f32x2 c = dot8(KE + (j < pos ? j : 0) * kD);
+        if (chunk == 0 && j < pos) coef[j] = c;
+        if (wave == 0) {  // groups 0..3 again: the tokens
+            const f32x2 ct = dot8(Kt4 + j * kD);
+            if (chunk == 0) ctok[j] = ct;
+        }
+    }
+    __syncthreads();
+
+    // ---- payload sweep scaled per column, record and token terms; codes re-laid out
+    f32x4 p1 = {0.f, 0.f, 0.f, 0.f}, p2 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int it = 0; it < kRowsPerThread; ++it) {
+        const f32x2 rv = rowv[lq_row(it, wave, ro)];
+        const f32x4 zf = unpack_codes(zw[it]);
+        p1 += zf * rv.x;
+        p2 += zf * rv.y;
+    }
+    const f32x4 bs = *reinterpret_cast<const f32x4*>(bscs + 4 * c4);
+    p1 *= bs;
+    p2 *= bs;
+    const int owner = 2 * wave + ro;
+    for (int j = owner; j < pos; j += 8) {
+        const f32x2 c = coef[j];
+        const f32x4 u = *reinterpret_cast<const f32x4*>(Us + j * kD + 4 * c4);
+        p1 += u * c.x;
+        p2 += u * c.y;
+    }
+    if (owner < kTok) {
+        const f32x2 c = ctok[owner];
+        const f32x4 u = *reinterpret_cast<const f32x4*>(Ut4 + owner * kD + 4 * c4);
+        p1 += u * c.x;
+        p2 += u * c.y;
+    }
+    p1 = f32x4{add_xor32(p1.x), add_xor32(p1.y), add_xor32(p1.z), add_xor32(p1.w)};
+    p2 = f32x4{add_xor32(p2.x), add_xor32(p2.y), add_xor32(p2.z), add_xor32(p2.w)};
+    if (ro == 0) {
+        red[wave * kD + 4 * c4 + 0] = f32x2{p1.x, p2.x};
+        red[wave * kD + 4 * c4 + 1] = f32x2{p1.y, p2.y};
+        red[wave * kD + 4 * c4 + 2] = f32x2{p1.z, p2.z};
+        red[wave * kD + 4 * c4 + 3] = f32x2{p1.w, p2.w};
+    }
+#pragma unroll
+    for (int it = 0; it < kRowsPerThread; ++it) Zs[lq_row(it, wave, ro) * kZsStride + c4] = zw[it];
+    __syncthreads();
+
+    // ---- correction and output; u of this step becomes row pos of Us
+    if (first) {
+        const int c = tid;
+        const f32x2 acc = red[c] + red[kD + c] + red[2 * kD + c] + red[3 * kD + c];
+        const float kq = kq_part[0] + kq_part[1];
+        const float u = bt * (vr - acc.x);
+        y[vec_off + c] = acc.y + u * kq;
+        Us[pos * kD + c] = u;
+    }
+    __syncthreads();
+
+    // ---- S_W on the matrix cores, both 16-row bands of the wave held in registers
+    const int lr = lane & 15, lq = lane >> 4;
+    f32x4 ua[kKdaRec / 4][2];
+#pragma unroll
+    for (int s4 = 0; s4 < kKdaRec / 4; ++s4) {
+        const float* src = Us + (4 * s4 + lq) * kD + 8 * lr;
+        ua[s4][0] = *reinterpret_cast<const f32x4*>(src);
+        ua[s4][1] = *reinterpret_cast<const f32x4*>(src + 4);
+    }
+    f32x4 utk[2];
+    utk[0] = *reinterpret_cast<const f32x4*>(Ut4 + lq * kD + 8 * lr);
+    utk[1] = *reinterpret_cast<const f32x4*>(Ut4 + lq * kD + 8 * lr + 4);
+    f32x4 acc[2][8];
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+        const int row = 16 * (2 * wave + a) + lr;
+        float eb[kKdaRec / 4];
+#pragma unroll
+        for (int s4 = 0; s4 < kKdaRec / 4; ++s4) eb[s4] = KE[(4 * s4 + lq) * kD + row];
+        const float kb = Kt4[lq * kD + row];
+        const float zc = zcoef[row];
+#pragma unroll
+        for (int d = 0; d < 8; ++d) {  // dword d: columns 32 lq + 4d .. +3
+            const uint32_t zd = Zs[row * kZsStride + 8 * lq + d];
+            const f32x4 bsd = *reinterpret_cast<const f32x4*>(bscs + 32 * lq + 4 * d);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {  // column 32 lq + 8 i + ct with i = d / 2, ct = 4 (d % 2) + e
+                const float zf = static_cast<float>(static_cast<int8_t>((zd >> (8 * e)) & 0xffu));
+                acc[a][4 * (d & 1) + e][d >> 1] = zf * (bsd[e] * zc);
+            }
+        }
+#pragma unroll
+        for (int s4 = 0; s4 < kKdaRec / 4; ++s4)
+#pragma unroll
+            for (int ct = 0; ct < 8; ++ct)
+                acc[a][ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(ua[s4][ct / 4][ct % 4], eb[s4], acc[a][ct], 0, 0, 0);
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct)
+            acc[a][ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(utk[ct / 4][ct % 4], kb, acc[a][ct], 0, 0, 0);
+    }
+    __syncthreads();  // every read of the step-phase arrays is done: the region holds S
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+        const int row = 16 * (2 * wave + a) + lr;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh)
+                state_unit(dyn_lds, row, 8 * lq + 2 * i + hh) =
+                    f32x4{acc[a][4 * hh][i], acc[a][4 * hh + 1][i], acc[a][4 * hh + 2][i], acc[a][4 * hh + 3][i]};
+    }
+    __syncthreads();
+    f32x4 s[16];
+    {
+        const int uu = 8 * wave + (lane & 7), rr = lane >> 3;
+#pragma unroll
+        for (int it = 0; it < 16; ++it) s[it] = state_unit(dyn_lds, 8 * it + rr, uu);
+    }
+    __syncthreads();  // the region is free for the refit's arrays
+    lq_refit(L, s, n_iter, tid, Zh, Bcol + vec_off, Csm + vec_off, Kc + tok0, Uc + tok0);
+}
+
 // ---------------------------------------------------------------- launchers
 static hipError_t set_lds(const void* fn, int floats) {
     return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -709,21 +985,36 @@ hipError_t launch_lq_quantize(int heads, const float* S, int n_iter, int8_t* Z, 
     return hipGetLastError();
 }
 
-hipError_t launch_lq_window(const StepArgs& a, const LqArgs& w, hipStream_t stream) {
+hipError_t launch_lq_window(const StepArgs& a, const LqArgs& w, bool per_key, hipStream_t stream) {
     if (w.pos == w.W - 1) {
-        static const hipError_t attr = set_lds(reinterpret_cast<const void*>(lq_boundary_kernel), kLqBoundaryFloats);
-        if (attr != hipSuccess) return attr;
-        hipLaunchKernelGGL(lq_boundary_kernel, dim3(a.heads), dim3(kThreads), sizeof(float) * kLqBoundaryFloats,
-                           stream, w.W, w.pos, w.n_iter, w.Z, w.B, w.C, static_cast<half_t*>(w.Kc),
-                           static_cast<half_t*>(w.Uc), static_cast<const bf16_t*>(w.Kbuf), w.Ubuf, w.Gbuf,
-                           static_cast<const bf16_t*>(a.q), static_cast<const bf16_t*>(a.k),
-                           static_cast<const bf16_t*>(a.v), a.gate, a.beta, a.y);
+        static const hipError_t attr_gdn = set_lds(reinterpret_cast<const void*>(lq_boundary_kernel), kLqBoundaryFloats);
+        static const hipError_t attr_kda = set_lds(reinterpret_cast<const void*>(lq_boundary_kda_kernel), kLqBoundaryFloats);
+        if (hipError_t e = per_key ? attr_kda : attr_gdn) return e;
+        if (per_key)
+            hipLaunchKernelGGL(lq_boundary_kda_kernel, dim3(a.heads), dim3(kThreads), sizeof(float) * kLqBoundaryFloats,
+                               stream, w.W, w.pos, w.n_iter, w.Z, w.B, w.C, static_cast<half_t*>(w.Kc),
+                               static_cast<half_t*>(w.Uc), static_cast<const bf16_t*>(w.Kbuf), w.Ubuf, w.Gbuf,
+                               static_cast<const bf16_t*>(a.q), static_cast<const bf16_t*>(a.k),
+                               static_cast<const bf16_t*>(a.v), a.gate, a.beta, a.y);
+        else
+            hipLaunchKernelGGL(lq_boundary_kernel, dim3(a.heads), dim3(kThreads), sizeof(float) * kLqBoundaryFloats,
+                               stream, w.W, w.pos, w.n_iter, w.Z, w.B, w.C, static_cast<half_t*>(w.Kc),
+                               static_cast<half_t*>(w.Uc), static_cast<const bf16_t*>(w.Kbuf), w.Ubuf, w.Gbuf,
+                               static_cast<const bf16_t*>(a.q), static_cast<const bf16_t*>(a.k),
+                               static_cast<const bf16_t*>(a.v), a.gate, a.beta, a.y);
         return hipGetLastError();
     }
-    hipLaunchKernelGGL(lq_step_kernel, dim3(a.heads), dim3(kThreads), 0, stream, w.W, w.pos, w.Z, w.B, w.C,
-                       static_cast<const half_t*>(w.Kc), static_cast<const half_t*>(w.Uc),
-                       static_cast<bf16_t*>(w.Kbuf), w.Ubuf, w.Gbuf, static_cast<const bf16_t*>(a.q),
-                       static_cast<const bf16_t*>(a.k), static_cast<const bf16_t*>(a.v), a.gate, a.beta, a.y);
+    if (per_key)
+        hipLaunchKernelGGL(lq_step_kernel<true>, dim3(a.heads), dim3(kThreads), sizeof(float) * w.pos * kD, stream,
+                           w.W, w.pos, w.Z, w.B, w.C, static_cast<const half_t*>(w.Kc),
+                           static_cast<const half_t*>(w.Uc), static_cast<bf16_t*>(w.Kbuf), w.Ubuf, w.Gbuf,
+                           static_cast<const bf16_t*>(a.q), static_cast<const bf16_t*>(a.k),
+                           static_cast<const bf16_t*>(a.v), a.gate, a.beta, a.y);
+    else
+        hipLaunchKernelGGL(lq_step_kernel<false>, dim3(a.heads), dim3(kThreads), 0, stream, w.W, w.pos, w.Z, w.B,
+                           w.C, static_cast<const half_t*>(w.Kc), static_cast<const half_t*>(w.Uc),
+                           static_cast<bf16_t*>(w.Kbuf), w.Ubuf, w.Gbuf, static_cast<const bf16_t*>(a.q),
+                           static_cast<const bf16_t*>(a.k), static_cast<const bf16_t*>(a.v), a.gate, a.beta, a.y);
     return hipGetLastError();
 }
 

@@ -223,7 +223,7 @@ def new_lq_buffers(w: wl.Workload):
         "Uc": torch.zeros(B, H, 4, 128, device=DEV, dtype=torch.float16),
         "Kbuf": torch.zeros(B, H, W, 128, device=DEV, dtype=qkv_dtype(w)),
         "Ubuf": torch.zeros(B, H, W, 128, device=DEV),
-        "Gbuf": torch.zeros(B, H, W, device=DEV),
+        "Gbuf": torch.zeros((B, H, W, 128) if w.per_key_gate else (B, H, W), device=DEV),
     }
 
 
@@ -295,7 +295,9 @@ def run_lq(w: wl.Workload, n_iter: int = 1, n_iter0: int = 8, sample: int | None
     hd = torch.from_numpy(heads).to(DEV)
     buf = new_lq_buffers(w)
     Sd = torch.from_numpy(S0).to(DEV).view(B, H, 128, 128)
-    m.gdn_lq_quantize(Sd, n_iter0, buf["Z"], buf["B"], buf["C"], buf["Kc"], buf["Uc"])
+    quantize = m.kda_lq_quantize if w.per_key_gate else m.gdn_lq_quantize
+    window = m.kda_lq_window if w.per_key_gate else m.gdn_lq_window
+    quantize(Sd, n_iter0, buf["Z"], buf["B"], buf["C"], buf["Kc"], buf["Uc"])
     err = {"y": 0.0, "tok": 0.0, "tok_k": 0.0, "tok_u": 0.0, "c": 0.0, "B": 0.0, "z_maxdiff": 0,
            "z_flips": 0, "z_flips_outside_band": 0, "boundaries": 0}
     S_ref = S0[heads].astype(np.float64)
@@ -310,8 +312,8 @@ def run_lq(w: wl.Workload, n_iter: int = 1, n_iter0: int = 8, sample: int | None
         n = min(W, steps - t0)
         for pos in range(n):
             x, d = dev_inputs(w, t0 + pos)
-            m.gdn_lq_window(W, pos, n_iter, buf["Z"], buf["B"], buf["C"], buf["Kc"], buf["Uc"], buf["Kbuf"],
-                            buf["Ubuf"], buf["Gbuf"], d["q"], d["k"], d["v"], d["gate"], d["beta"], y)
+            window(W, pos, n_iter, buf["Z"], buf["B"], buf["C"], buf["Kc"], buf["Uc"], buf["Kbuf"],
+                   buf["Ubuf"], buf["Gbuf"], d["q"], d["k"], d["v"], d["gate"], d["beta"], y)
             y_ref = oracle.dense_step(S, *host_slice(x, heads))
             err["y"] = max(err["y"], rel_err(take(y, hd, (128,)), y_ref))
         if n == W:

@@ -38,6 +38,20 @@ def test_lq_windows_small(W, B, H, n_iter):
     _check(run_lq(w, n_iter=n_iter), f"W={W} B={B} H={H} n_iter={n_iter}")
 
 
+@pytest.mark.parametrize("W,B,H,n_iter", [(16, 2, 5, 1), (16, 3, 4, 2), (7, 2, 3, 1), (1, 2, 2, 0)])
+def test_lq_kda_windows_small(W, B, H, n_iter):
+    """Per-key gates (KDA): Gamma of eq. 10 is diagonal over the key rows."""
+    w = wl.custom(wl.WORKLOADS[9], B=B, H=H, W=W, steps=2 * W + min(W, 3))
+    _check(run_lq(w, n_iter=n_iter), f"kda W={W} B={B} H={H} n_iter={n_iter}")
+
+
+def test_lq_kda_b128_h32_full_size_sampled():
+    """The KDA LeapQuant workload (B=128, H=32, W=16), 64 sampled heads, 3 windows."""
+    w = wl.WORKLOADS[9]
+    say(f"[lq] {w.name}: full size, 64 sampled heads, 48 steps")
+    _check(run_lq(w, n_iter=1, sample=64, steps=48), w.name)
+
+
 @pytest.mark.parametrize("n_iter0", [0, 3])
 def test_lq_quantize_start_iterations(n_iter0):
     w = wl.custom(wl.WORKLOADS[6], B=2, H=3, W=16, steps=0)

@@ -74,6 +74,9 @@ WORKLOADS = {
                 0.90, 0.999, W=16, outliers=True),
     # RWKV6 at the shape of DeltaLog's kernel study (Table 3: 32 heads of 128 x 128, M = 4),
     # batch 128 as in its interval sweep; per-key decays drawn like KDA's gates
+    # LeapQuant's format with KDA gates on the KDA workload's shape (same outliers as 4)
+    9: Workload(9, "kda_lq_window_b128_h32_w16", "kda", "lq_window", 128, 32, 256, "bf16", 0.80, 1.0,
+                W=16, outliers=True),
     7: Workload(7, "rwkv6_dense_b128_h32_bf16", "rwkv6", "dense", 128, 32, 32, "bf16", 0.80, 1.0),
     8: Workload(8, "rwkv6_log_b128_h32_m4", "rwkv6", "log", 128, 32, 128, "bf16", 0.80, 1.0, M=4),
 }
