@@ -51,13 +51,14 @@ def _load():
         lib.oracle_log_step.argtypes = [I64, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P, P]
         lib.oracle_log_step_slots.argtypes = [I64, I, I, I, I, P, P, P, P, P, P, P, P, P, P, P, P]
         lib.oracle_rwkv6_step.argtypes = [I64, I, I, P, P, P, P, P, P]
+        lib.oracle_rwkv7_step.argtypes = [I64, I, I, P, P, P, P, P, P, P, P]
         lib.oracle_rwkv6_log_step.argtypes = [I64, I, I, I, I, P, P, P, P, P, P, P, P, P, P]
         lib.oracle_rwkv6_log_step_slots.argtypes = [I64, I, I, I, P, P, P, P, P, P, P, P, P, P, P]
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = ctypes.c_int
         for f in (lib.oracle_dense_step, lib.oracle_q8_quantize, lib.oracle_q8_window_step,
                   lib.oracle_log_step, lib.oracle_log_step_slots, lib.oracle_rwkv6_step,
-                  lib.oracle_rwkv6_log_step, lib.oracle_rwkv6_log_step_slots):
+                  lib.oracle_rwkv6_log_step, lib.oracle_rwkv6_log_step_slots, lib.oracle_rwkv7_step):
             f.restype = None
         _lib = lib
     return _lib
@@ -105,6 +106,20 @@ def rwkv6_step(S: np.ndarray, q, k, v, w) -> np.ndarray:
     assert q.shape == (nh, dk) and k.shape == (nh, dk) and v.shape == (nh, dv) and w.shape == (nh, dk)
     y = np.empty((nh, dv))
     _load().oracle_rwkv6_step(nh, dk, dv, _ptr(S), _ptr(q), _ptr(k), _ptr(v), _ptr(w), _ptr(y))
+    return y
+
+
+def rwkv7_step(S: np.ndarray, q, k, v, w, kappa, a) -> np.ndarray:
+    """One RWKV7 decode step as its two sub-steps (erase along kappa read with a * kappa,
+    then write k v^T), y = S^T q, on fp64 states S[nh, dk, dv] (updated in place)."""
+    assert S.dtype == np.float64 and S.flags.c_contiguous
+    nh, dk, dv = S.shape
+    q, k, v, w, kappa, a = map(_f64, (q, k, v, w, kappa, a))
+    for x, n in ((q, dk), (k, dk), (v, dv), (w, dk), (kappa, dk), (a, dk)):
+        assert x.shape == (nh, n)
+    y = np.empty((nh, dv))
+    _load().oracle_rwkv7_step(nh, dk, dv, _ptr(S), _ptr(q), _ptr(k), _ptr(v), _ptr(w), _ptr(kappa), _ptr(a),
+                              _ptr(y))
     return y
 
 

@@ -133,6 +133,14 @@ def rwkv6_step(S: Mat, q: Vec, k: Vec, v: Vec, w: Vec):
     return Sn, [sum(Sn[i][j] * q[i] for i in range(dk)) for j in range(dv)]
 
 
+def rwkv7_step(S: Mat, q: Vec, k: Vec, v: Vec, w: Vec, kappa: Vec, a: Vec):
+    """RWKV7 as the product of its transition: S <- (Diag(w) - kappa (a * kappa)^T) S + k v^T."""
+    dk, dv = len(S), len(S[0])
+    T = [[(w[i] if i == m else 0) - kappa[i] * a[m] * kappa[m] for m in range(dk)] for i in range(dk)]
+    Sn = [[sum(T[i][m] * S[m][j] for m in range(dk)) + k[i] * v[j] for j in range(dv)] for i in range(dk)]
+    return Sn, [sum(Sn[i][j] * q[i] for i in range(dk)) for j in range(dv)]
+
+
 def log_run(S0: Mat, inputs, M: int, delta: bool = True):
     """Base + log (DeltaLog Alg. 1, eqs. 4-7) with decays as exact gate products:
     D(lbar) is the product of the gates since the last merge and D(lbar - Lam_m) the

@@ -105,6 +105,49 @@ void oracle_rwkv6_step(int64_t nh, int dk, int dv, double *S, const double *q, c
 }
 
 /*
+ * One RWKV7 decode step as two sub-steps of the general update (LeapQuant, App. A,
+ * "models with a separate erase direction": the transition Diag(w) - kappa (a * kappa)^T
+ * splits into an erase with v = 0 and a pure write with D = I and read vector 0):
+ *   S' = Diag(w) S + kappa (0 - S^T (a * kappa))^T      erase along kappa, read with a * kappa
+ *   S  = S' + k v^T                                       write
+ *   y  = S^T q
+ * w is the per-key decay, kappa the removal key, a the per-key erase rate.
+ */
+void oracle_rwkv7_step(int64_t nh, int dk, int dv, double *S, const double *q, const double *k,
+                       const double *v, const double *w, const double *kappa, const double *a,
+                       double *y)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t h = 0; h < nh; ++h) {
+        double *Sh = S + (size_t)h * dk * dv;
+        const double *qh = q + (size_t)h * dk, *kh = k + (size_t)h * dk;
+        const double *vh = v + (size_t)h * dv, *wh = w + (size_t)h * dk;
+        const double *ch = kappa + (size_t)h * dk, *ah = a + (size_t)h * dk;
+        double *yh = y + (size_t)h * dv;
+        double *u = (double *)malloc(sizeof(double) * dv);
+        for (int j = 0; j < dv; ++j) {          /* erase: u = 0 - S^T (a * kappa) */
+            double p = 0.0;
+            for (int i = 0; i < dk; ++i)
+                p += Sh[IDX2(i, j, dv)] * ah[i] * ch[i];
+            u[j] = 0.0 - p;
+        }
+        for (int i = 0; i < dk; ++i)
+            for (int j = 0; j < dv; ++j)
+                Sh[IDX2(i, j, dv)] = wh[i] * Sh[IDX2(i, j, dv)] + ch[i] * u[j];
+        for (int i = 0; i < dk; ++i)            /* write */
+            for (int j = 0; j < dv; ++j)
+                Sh[IDX2(i, j, dv)] += kh[i] * vh[j];
+        for (int j = 0; j < dv; ++j) {
+            double acc = 0.0;
+            for (int i = 0; i < dk; ++i)
+                acc += Sh[IDX2(i, j, dv)] * qh[i];
+            yh[j] = acc;
+        }
+        free(u);
+    }
+}
+
+/*
  * Symmetric per-key-row int8 quantizer (STEPQuant notes, the uniform per-row
  * absmax baseline; LeapQuant, App. B.3, the /127 convention).
  *   a_i = max_j |S_ij|          stored as fp32

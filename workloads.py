@@ -29,14 +29,15 @@ DK = 128
 DV = 128
 
 # tensor tags of the substreams
-_TAG_S0, _TAG_Q, _TAG_K, _TAG_V, _TAG_GATE, _TAG_BETA, _TAG_OUTLIER = range(7)
+_TAG_S0, _TAG_Q, _TAG_K, _TAG_V, _TAG_GATE, _TAG_BETA, _TAG_OUTLIER, _TAG_KAPPA, _TAG_A = range(9)
 
 
 @dataclasses.dataclass(frozen=True)
 class Workload:
     cid: int
     name: str
-    variant: str          # "gdn" (scalar gate alpha), "kda" (per-key gate d) or "rwkv6" (per-key decay w, no delta read)
+    variant: str          # "gdn" (scalar gate alpha), "kda" (per-key gate d), "rwkv6" (per-key decay w,
+                          # no delta read) or "rwkv7" (per-key decay w, erase along kappa read with a * kappa)
     path: str             # "dense", "q8_window", "lq_window" or "log"
     B: int
     H: int
@@ -59,7 +60,7 @@ class Workload:
 
     @property
     def per_key_gate(self) -> bool:
-        return self.variant in ("kda", "rwkv6")
+        return self.variant in ("kda", "rwkv6", "rwkv7")
 
 
 WORKLOADS = {
@@ -77,6 +78,7 @@ WORKLOADS = {
     # LeapQuant's format with KDA gates on the KDA workload's shape (same outliers as 4)
     9: Workload(9, "kda_lq_window_b128_h32_w16", "kda", "lq_window", 128, 32, 256, "bf16", 0.80, 1.0,
                 W=16, outliers=True),
+    10: Workload(10, "rwkv7_dense_b128_h32_bf16", "rwkv7", "dense", 128, 32, 32, "bf16", 0.80, 1.0),
     7: Workload(7, "rwkv6_dense_b128_h32_bf16", "rwkv6", "dense", 128, 32, 32, "bf16", 0.80, 1.0),
     8: Workload(8, "rwkv6_log_b128_h32_m4", "rwkv6", "log", 128, 32, 128, "bf16", 0.80, 1.0, M=4),
 }
@@ -160,7 +162,8 @@ def step_inputs(wl: Workload, t: int) -> dict:
     workload's input dtype (fp32 values, bf16-representable when qkv == bf16).
     v: N(0,1) in the input dtype. gate: alpha ~ U(lo, hi) per head [B*H] for
     GDN, d ~ U(lo, hi) per key channel [B*H, 128] for KDA. beta ~ U(0, 1) [B*H].
-    All arrays are fp32.
+    RWKV7 also draws its removal key kappa (N(0,1), L2-normalised, input dtype) and its
+    per-key erase rate a ~ U(0, 1) [B*H, 128]. All arrays are fp32.
     """
     n = wl.heads
     f32 = np.float32
@@ -172,7 +175,12 @@ def step_inputs(wl: Workload, t: int) -> dict:
     gate = (lo + (hi - lo) * _rng(wl, _TAG_GATE, t).random(gshape)).astype(f32)
     gate = np.clip(gate, f32(lo), f32(hi))
     beta = _rng(wl, _TAG_BETA, t).random((n,), dtype=f32)
-    return {"q": q, "k": k, "v": v, "gate": gate, "beta": beta}
+    out = {"q": q, "k": k, "v": v, "gate": gate, "beta": beta}
+    if wl.variant == "rwkv7":
+        out["kappa"] = _cast(wl, _unit_rows(_rng(wl, _TAG_KAPPA, t).standard_normal((n, DK), dtype=f32)
+                                            .astype(np.float64)))
+        out["a"] = _rng(wl, _TAG_A, t).random((n, DK), dtype=f32)
+    return out
 
 
 def sample_heads(wl: Workload, count: int, seed: int = 7) -> np.ndarray:
