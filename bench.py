@@ -40,7 +40,7 @@ KERNEL_SOURCES = {
 }
 
 WORKLOAD_BY_FLAG = {"gdn": 2, "gdn_small": 1, "kda": 3, "q8": 4, "log": 5, "lq": 6, "rwkv6": 7,
-                    "rwkv6_log": 8, "kda_lq": 9}
+                    "rwkv6_log": 8, "kda_lq": 9, "rwkv7": 10}
 LQ_TOKENS = 4
 
 
@@ -51,14 +51,15 @@ def _in_bytes(w: wl.Workload) -> int:
 
 
 def _beta_bytes(w: wl.Workload) -> int:
-    return 0 if w.variant == "rwkv6" else 4     # RWKV6 has no write strength
+    return 0 if w.variant in ("rwkv6", "rwkv7") else 4     # RWKV6 / RWKV7 have no write strength
 
 
 def dense_bytes_per_head(w: wl.Workload) -> int:
     """State read + write (fp32), q/k/v in their dtype, gate, beta, y (fp32)."""
     d = wl.DK
     gate = 4 * d if w.per_key_gate else 4
-    return 2 * 4 * d * d + 3 * d * _in_bytes(w) + gate + _beta_bytes(w) + 4 * d
+    extra = d * _in_bytes(w) + 4 * d if w.variant == "rwkv7" else 0     # RWKV7's kappa and erase rate a
+    return 2 * 4 * d * d + 3 * d * _in_bytes(w) + gate + _beta_bytes(w) + 4 * d + extra
 
 
 def window_step_bytes_per_head(w: wl.Workload, pos: int) -> int:
@@ -164,11 +165,14 @@ def _dev_inputs(w, steps, torch, dev):
     """All steps' inputs stacked on the device: dict of [steps, B, H, ...] tensors."""
     dt = torch.bfloat16 if w.qkv == "bf16" else torch.float32
     B, H = w.B, w.H
-    out = {n: [] for n in ("q", "k", "v", "gate", "beta")}
+    names = ("q", "k", "v", "gate", "beta") + (("kappa", "a") if w.variant == "rwkv7" else ())
+    out = {n: [] for n in names}
     for t in range(steps):
         x = wl.step_inputs(w, t)
-        for n in ("q", "k", "v"):
+        for n in ("q", "k", "v") + (("kappa",) if w.variant == "rwkv7" else ()):
             out[n].append(torch.from_numpy(x[n]).to(dev).to(dt).view(B, H, 128))
+        if w.variant == "rwkv7":
+            out["a"].append(torch.from_numpy(x["a"]).to(dev).view(B, H, 128))
         out["gate"].append(torch.from_numpy(x["gate"]).to(dev).view((B, H, 128) if w.per_key_gate else (B, H)))
         out["beta"].append(torch.from_numpy(x["beta"]).to(dev).view(B, H))
     return {n: torch.stack(v) for n, v in out.items()}
@@ -206,7 +210,14 @@ def run_gpu(w: wl.Workload, steps: int, warmup: int, slots: bool = False, n_iter
     kda = w.per_key_gate
     state = {"t": 0}
 
-    if w.path == "dense" and w.variant == "rwkv6":
+    if w.path == "dense" and w.variant == "rwkv7":
+        S = S0
+
+        def step():
+            i = state["t"] % n_inputs
+            rsu.rwkv7_decode_step(S, x["q"][i], x["k"][i], x["v"][i], x["kappa"][i], x["gate"][i], x["a"][i], y)
+            state["t"] += 1
+    elif w.path == "dense" and w.variant == "rwkv6":
         S = S0
 
         def step():

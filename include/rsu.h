@@ -1,7 +1,7 @@
 /*
  * rsu.h -- C ABI of the MI355X (gfx950) decode-step library for delta-rule
  * recurrent states (Gated DeltaNet and Kimi Delta Attention), and for RWKV6's
- * decayed linear-attention state in the same common form.
+ * and RWKV7's states in the same common form.
  *
  * Per head the state S is d_k x d_v = 128 x 128; row i is a key channel and
  * column j a value channel. One decode step applies the retention gate g
@@ -253,6 +253,20 @@ int rwkv6_log_merge(const rsu_dims *dims, int C, int L, float *Sbase, float *lba
 int rwkv6_log_step_slots(const rsu_dims *dims, int C, int *L, float *Sbase, float *lbar,
                          void *Klog, void *Ulog, float *Lam, const void *q, const void *k,
                          const void *v, const float *w, float *y, rsu_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * RWKV7 as two sub-steps of the general update (LeapQuant App. A, models with a
+ * separate erase direction: the transition Diag(w) - kappa (a * kappa)^T):
+ *     S' = Diag(w) S + kappa (0 - S^T (a * kappa))^T     erase along kappa
+ *     S  = S' + k v^T,   y = S^T q                        write, then the output
+ * q, k, v, kappa [B,H,d] in qkv_dtype (kappa is the removal key), w [B,H,d_k] fp32
+ * the per-key decay, a [B,H,d_k] fp32 the per-key erase rate. No beta. The dense
+ * state S is read once and written once, in place; both sub-steps happen in the same
+ * pass. Arguments and errors as for rwkv6_decode_step.
+ * ---------------------------------------------------------------------- */
+int rwkv7_decode_step(const rsu_dims *dims, float *S, const void *q, const void *k,
+                      const void *v, const void *kappa, const float *w, const float *a,
+                      float *y, rsu_stream_t stream);
 
 /* ------------------------------------------------------------------------
  * Measurement helper (not part of the recurrence): dst[i] = src[i] for

@@ -64,6 +64,7 @@ _SIGS = {
     "gdn_log_step_slots": [_DP, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
     "kda_log_step_slots": [_DP, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
     "rwkv6_decode_step": [_DP, _P, _P, _P, _P, _P, _P, _P],
+    "rwkv7_decode_step": [_DP, _P, _P, _P, _P, _P, _P, _P, _P, _P],
     "rwkv6_log_append": [_DP, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
     "rwkv6_log_merge": [_DP, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
     "rwkv6_log_step_slots": [_DP, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
@@ -258,6 +259,20 @@ def rwkv6_decode_step(S, q, k, v, w, y):
     _need(y, "y", torch.float32, (dims.B, dims.H, D))
     _call("rwkv6_decode_step", ctypes.byref(dims), _ptr(S), _ptr(q), _ptr(k), _ptr(v), _ptr(w), _ptr(y),
           _stream())
+    return y
+
+
+def rwkv7_decode_step(S, q, k, v, kappa, w, a, y):
+    """One RWKV7 step (erase along kappa read with a * kappa, then write k v^T; y = S^T q):
+    S updated in place, y written. kappa in q's dtype; w and a fp32 [B, H, 128]."""
+    dims = _dims(q, k, v)
+    _need(S, "S", torch.float32, (dims.B, dims.H, D, D))
+    _need(kappa, "kappa", q.dtype, (dims.B, dims.H, D))
+    _need(w, "w", torch.float32, (dims.B, dims.H, D))
+    _need(a, "a", torch.float32, (dims.B, dims.H, D))
+    _need(y, "y", torch.float32, (dims.B, dims.H, D))
+    _call("rwkv7_decode_step", ctypes.byref(dims), _ptr(S), _ptr(q), _ptr(k), _ptr(v), _ptr(kappa), _ptr(w),
+          _ptr(a), _ptr(y), _stream())
     return y
 
 

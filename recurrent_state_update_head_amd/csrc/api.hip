@@ -313,6 +313,20 @@ int rwkv6_decode_step(const rsu_dims* dims, float* S, const void* q, const void*
     return dense_common("rwkv6_decode_step", Kind::rwkv6, dims, S, q, k, v, w, nullptr, y, stream);
 }
 
+int rwkv7_decode_step(const rsu_dims* dims, float* S, const void* q, const void* k, const void* v,
+                      const void* kappa, const float* w, const float* a, float* y, rsu_stream_t stream) {
+    const char* fn = "rwkv7_decode_step";
+    int heads = 0;
+    if (int rc = check_dims(dims, &heads, fn)) return rc;
+    if (heads == 0) return RSU_OK;
+    if (int rc = check_ptrs({{S, "S"}, {q, "q"}, {k, "k"}, {v, "v"}, {kappa, "kappa"}, {w, "w"}, {a, "a"},
+                             {y, "y"}}, fn))
+        return rc;
+    return launched(rsu::launch_rwkv7(step_args(heads, S, q, k, v, w, nullptr, y), kappa, a,
+                                      dims->qkv_dtype == RSU_BF16, stream),
+                    fn);
+}
+
 int rwkv6_log_append(const rsu_dims* dims, int C, int L, const float* Sbase, float* lbar, void* Klog,
                      void* Ulog, float* Lam, const void* q, const void* k, const void* v, const float* w,
                      float* y, rsu_stream_t stream) {

@@ -1,4 +1,4 @@
-// dense.hip -- one eager decode step on the dense fp32 state (GDN, KDA, RWKV6).
+// dense.hip -- one eager decode step on the dense fp32 state (GDN, KDA, RWKV6, RWKV7).
 //
 // Recurrence (LeapQuant, App. A, the GDN and KDA expansions, with beta carried
 // by the correction): with g the gate (alpha repeated over the key rows for
@@ -74,6 +74,68 @@ __global__ __launch_bounds__(kThreads) void dense_step_kernel(
     }
 }
 
+// RWKV7 (LeapQuant, App. A, models with a separate erase direction): the erase sub-step
+// reads S along a * kappa and the output reads the result along q; both reads come
+// from the old state, so one sweep gives p = S^T (a * kappa) and r = S^T (w * q), and
+//   u = 0 - p,  S <- Diag(w) S + kappa u^T + k v^T,  y = r + u (kappa . q) + v (k . q):
+// the state crosses HBM once in and once out, as in the single-record step.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void rwkv7_step_kernel(
+    float* __restrict__ S, const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    const T* __restrict__ kappa, const float* __restrict__ w, const float* __restrict__ a,
+    float* __restrict__ y) {
+    // per wave, per key row: (a * kappa, w * q, kappa, w) and k
+    __shared__ f32x4 row_vec[kThreads / 64][kD];
+    __shared__ float krow[kThreads / 64][kD];
+
+    const int h = head_of_block(blockIdx.x, gridDim.x);
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
+    const int ro = lane >> 3;
+    const int col = wave * 32 + (lane & 7) * 4;
+    const size_t vec_off = static_cast<size_t>(h) * kD;
+
+    const f32x2 k2 = load2_in(k, vec_off + 2 * lane);
+    const f32x2 q2 = load2_in(q, vec_off + 2 * lane);
+    const f32x2 c2 = load2_in(kappa, vec_off + 2 * lane);
+    const f32x2 w2 = *reinterpret_cast<const f32x2*>(w + vec_off + 2 * lane);
+    const f32x2 a2 = *reinterpret_cast<const f32x2*>(a + vec_off + 2 * lane);
+    const f32x4 vv = load4_in(v, vec_off + col);
+
+    float* Sh = S + static_cast<size_t>(h) * kD * kD;
+    f32x4 s[kRowsPerThread];
+#pragma unroll
+    for (int it = 0; it < kRowsPerThread; ++it)
+        s[it] = stream_load(Sh + (it * 8 + ro) * kD + col);
+
+    row_vec[wave][2 * lane] = f32x4{a2.x * c2.x, w2.x * q2.x, c2.x, w2.x};
+    row_vec[wave][2 * lane + 1] = f32x4{a2.y * c2.y, w2.y * q2.y, c2.y, w2.y};
+    krow[wave][2 * lane] = k2.x;
+    krow[wave][2 * lane + 1] = k2.y;
+    const float cq = wave_sum(c2.x * q2.x + c2.y * q2.y);
+    const float kq = wave_sum(k2.x * q2.x + k2.y * q2.y);
+    wave_lds_sync();
+
+    f32x4 p = {0.f, 0.f, 0.f, 0.f}, r = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int it = 0; it < kRowsPerThread; ++it) {
+        const f32x4 rv = row_vec[wave][it * 8 + ro];
+        p += s[it] * rv.x;
+        r += s[it] * rv.y;
+    }
+    p = sum_row_lanes(p);
+    r = sum_row_lanes(r);
+
+    const f32x4 u = 0.f - p;
+    if (ro == 0) *reinterpret_cast<f32x4*>(y + vec_off + col) = r + u * cq + vv * kq;
+
+#pragma unroll
+    for (int it = 0; it < kRowsPerThread; ++it) {
+        const f32x4 rv = row_vec[wave][it * 8 + ro];
+        stream_store(Sh + (it * 8 + ro) * kD + col, s[it] * rv.w + rv.z * u + krow[wave][it * 8 + ro] * vv);
+    }
+}
+
 // Read+write copy with the same access pattern, for the practical HBM ceiling.
 __global__ __launch_bounds__(kThreads) void copy_kernel(const float* __restrict__ src,
                                                         float* __restrict__ dst, int64_t n) {
@@ -111,6 +173,21 @@ hipError_t launch_dense(const StepArgs& a, bool per_key, bool bf16, hipStream_t 
 
 hipError_t launch_rwkv6(const StepArgs& a, bool bf16, hipStream_t stream) {
     return bf16 ? launch_dense_t<true, false, bf16_t>(a, stream) : launch_dense_t<true, false, float>(a, stream);
+}
+
+hipError_t launch_rwkv7(const StepArgs& a, const void* kappa, const float* erase_rate, bool bf16,
+                        hipStream_t stream) {
+    if (bf16)
+        hipLaunchKernelGGL(rwkv7_step_kernel<bf16_t>, dim3(a.heads), dim3(kThreads), 0, stream, a.S,
+                           static_cast<const bf16_t*>(a.q), static_cast<const bf16_t*>(a.k),
+                           static_cast<const bf16_t*>(a.v), static_cast<const bf16_t*>(kappa), a.gate, erase_rate,
+                           a.y);
+    else
+        hipLaunchKernelGGL(rwkv7_step_kernel<float>, dim3(a.heads), dim3(kThreads), 0, stream, a.S,
+                           static_cast<const float*>(a.q), static_cast<const float*>(a.k),
+                           static_cast<const float*>(a.v), static_cast<const float*>(kappa), a.gate, erase_rate,
+                           a.y);
+    return hipGetLastError();
 }
 
 hipError_t launch_copy(const float* src, float* dst, int64_t n, hipStream_t stream) {

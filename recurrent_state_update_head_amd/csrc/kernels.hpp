@@ -40,6 +40,10 @@ struct LogArgs {
 hipError_t launch_dense(const StepArgs& a, bool per_key, bool bf16, hipStream_t stream);
 // RWKV6: S <- Diag(w) S + k v^T, y = S^T q (gate = w [heads, 128]; beta unused)
 hipError_t launch_rwkv6(const StepArgs& a, bool bf16, hipStream_t stream);
+// RWKV7: erase along kappa read with erase_rate * kappa, then write k v^T (gate = w [heads, 128];
+// kappa [heads, 128] in the input dtype, erase_rate [heads, 128] fp32; beta unused)
+hipError_t launch_rwkv7(const StepArgs& a, const void* kappa, const float* erase_rate, bool bf16,
+                        hipStream_t stream);
 hipError_t launch_copy(const float* src, float* dst, int64_t n, hipStream_t stream);
 hipError_t launch_q8_quantize(int heads, const float* S, int8_t* Z, float* A, hipStream_t stream);
 hipError_t launch_q8_window(const StepArgs& a, const WindowArgs& w, bool per_key, bool bf16,

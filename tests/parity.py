@@ -42,6 +42,9 @@ def dev_inputs(w: wl.Workload, t: int):
     d = {n: torch.from_numpy(x[n]).to(DEV).to(dt).view(B, H, 128) for n in ("q", "k", "v")}
     d["gate"] = torch.from_numpy(x["gate"]).to(DEV).view((B, H, 128) if w.per_key_gate else (B, H))
     d["beta"] = torch.from_numpy(x["beta"]).to(DEV).view(B, H)
+    if "kappa" in x:
+        d["kappa"] = torch.from_numpy(x["kappa"]).to(DEV).to(dt).view(B, H, 128)
+        d["a"] = torch.from_numpy(x["a"]).to(DEV).view(B, H, 128)
     return x, d
 
 
@@ -80,6 +83,9 @@ def run_dense(w: wl.Workload, sample: int | None = None):
         if w.variant == "rwkv6":
             m.rwkv6_decode_step(S, d["q"], d["k"], d["v"], d["gate"], y)
             y_ref = oracle.rwkv6_step(S_ref, *host_slice(x, heads)[:4])
+        elif w.variant == "rwkv7":
+            m.rwkv7_decode_step(S, d["q"], d["k"], d["v"], d["kappa"], d["gate"], d["a"], y)
+            y_ref = oracle.rwkv7_step(S_ref, *host_slice(x, heads)[:4], x["kappa"][heads], x["a"][heads])
         else:
             fn(S, d["q"], d["k"], d["v"], d["gate"], d["beta"], y)
             y_ref = oracle.dense_step(S_ref, *host_slice(x, heads))

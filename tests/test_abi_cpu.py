@@ -163,3 +163,17 @@ def test_rwkv6_validation(lib):
     assert "w is NULL" in _last(lib)
     assert sl(ctypes.byref(d), 3, None, *([GOOD] * 10), None) == E_NULL       # live lengths
     assert sl(ctypes.byref(d), 3, GOOD, GOOD, GOOD, GOOD, ODD, *([GOOD] * 6), None) == E_ALIGN
+
+
+def test_rwkv7_validation(lib):
+    f = lib.rwkv7_decode_step
+    f.restype = ctypes.c_int
+    d = Dims(2, 3, 128, 128, 1)
+    # S, q, k, v, kappa, w, a, y
+    assert f(ctypes.byref(d), GOOD, GOOD, GOOD, GOOD, None, GOOD, GOOD, GOOD, None) == E_NULL
+    assert "kappa is NULL" in _last(lib)
+    assert f(ctypes.byref(d), GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, None, GOOD, None) == E_NULL
+    assert "a is NULL" in _last(lib)
+    assert f(ctypes.byref(d), GOOD, GOOD, GOOD, GOOD, GOOD, ODD, GOOD, GOOD, None) == E_ALIGN
+    assert f(ctypes.byref(Dims(2, 3, 128, 128, 5)), *([GOOD] * 8), None) == E_DTYPE
+    assert f(ctypes.byref(Dims(0, 3, 128, 128, 1)), *([None] * 8), None) == RSU_OK
