@@ -52,13 +52,16 @@ def _load():
         lib.oracle_log_step_slots.argtypes = [I64, I, I, I, I, P, P, P, P, P, P, P, P, P, P, P, P]
         lib.oracle_rwkv6_step.argtypes = [I64, I, I, P, P, P, P, P, P]
         lib.oracle_rwkv7_step.argtypes = [I64, I, I, P, P, P, P, P, P, P, P]
+        lib.oracle_rwkv7_q8_window_step.argtypes = [I64, I, I, I, I, P, P, P, P, P, P, P, P, P, P, P, P, P,
+                                                    P]
         lib.oracle_rwkv6_log_step.argtypes = [I64, I, I, I, I, P, P, P, P, P, P, P, P, P, P]
         lib.oracle_rwkv6_log_step_slots.argtypes = [I64, I, I, I, P, P, P, P, P, P, P, P, P, P, P]
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = ctypes.c_int
         for f in (lib.oracle_dense_step, lib.oracle_q8_quantize, lib.oracle_q8_window_step,
                   lib.oracle_log_step, lib.oracle_log_step_slots, lib.oracle_rwkv6_step,
-                  lib.oracle_rwkv6_log_step, lib.oracle_rwkv6_log_step_slots, lib.oracle_rwkv7_step):
+                  lib.oracle_rwkv6_log_step, lib.oracle_rwkv6_log_step_slots, lib.oracle_rwkv7_step,
+                  lib.oracle_rwkv7_q8_window_step):
             f.restype = None
         _lib = lib
     return _lib
@@ -178,6 +181,41 @@ class WindowState:
         if want_boundary:
             return y, Sw, w
         return y
+
+
+class Rwkv7WindowState:
+    """RWKV7 on the int8 window representation: window-start (Z, a) plus two records per
+    token (erase along kappa, then write k v^T; LeapQuant App. A), 2W records per window."""
+
+    def __init__(self, Z: np.ndarray, a: np.ndarray, W: int):
+        nh, dk, dv = Z.shape
+        self.Z = np.ascontiguousarray(Z, dtype=np.int8).copy()
+        self.a = np.ascontiguousarray(a, dtype=np.float32).copy()
+        self.W = W
+        self.G = np.zeros((nh, 2 * W, dk))
+        self.K = np.zeros((nh, 2 * W, dk))
+        self.U = np.zeros((nh, 2 * W, dv))
+        self.pos = 0
+
+    def step(self, q, k, v, w, kappa, erase, want_boundary: bool = False):
+        nh, dk, dv = self.Z.shape
+        q, k, v, w, kappa, erase = map(_f64, (q, k, v, w, kappa, erase))
+        for x, n in ((q, dk), (k, dk), (v, dv), (w, dk), (kappa, dk), (erase, dk)):
+            assert x.shape == (nh, n)
+        y = np.empty((nh, dv))
+        boundary = self.pos == self.W - 1
+        Sw = np.empty((nh, dk, dv)) if (boundary and want_boundary) else None
+        wq = np.empty((nh, dk, dv)) if (boundary and want_boundary) else None
+        _load().oracle_rwkv7_q8_window_step(
+            nh, dk, dv, self.W, self.pos, _ptr(self.Z), _ptr(self.a), _ptr(self.G), _ptr(self.K),
+            _ptr(self.U), _ptr(q), _ptr(k), _ptr(v), _ptr(w), _ptr(kappa), _ptr(erase), _ptr(y),
+            _ptr(Sw) if Sw is not None else None, _ptr(wq) if wq is not None else None)
+        self.pos = 0 if boundary else self.pos + 1
+        if boundary:
+            self.G[:] = 0
+            self.K[:] = 0
+            self.U[:] = 0
+        return (y, Sw, wq) if (boundary and want_boundary) else y
 
 
 class LogState:

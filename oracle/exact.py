@@ -141,6 +141,62 @@ def rwkv7_step(S: Mat, q: Vec, k: Vec, v: Vec, w: Vec, kappa: Vec, a: Vec):
     return Sn, [sum(Sn[i][j] * q[i] for i in range(dk)) for j in range(dv)]
 
 
+def rwkv7_window_run(S0: Mat, inputs, W: int):
+    """RWKV7 on the per-window representation with exact arithmetic: two records per token
+    (erase: gate w, key kappa, u = -S^T (a * kappa); write: gate 1, key k, u = v), the state
+    materialized by eq. 4 from the window-start state and the records, requantized at
+    every window end. inputs: (q, k, v, w, kappa, a) per token. Returns (ys, boundaries)."""
+    dk, dv = len(S0), len(S0[0])
+    Z, a = quantize(S0)
+    ys, bounds = [], []
+    recs = []          # (gate vector, key, u)
+
+    def mat(base):
+        out = []
+        for i in range(dk):
+            g = F(1)
+            for (gv, _, _) in recs:
+                g *= gv[i]
+            row = [g * base[i][j] for j in range(dv)]
+            for m, (_, km, um) in enumerate(recs):
+                c = km[i]
+                for (gv, _, _) in recs[m + 1:]:
+                    c *= gv[i]
+                for j in range(dv):
+                    row[j] += c * um[j]
+            out.append(row)
+        return out
+
+    for t, (q, k, v, w, kappa, er) in enumerate(inputs):
+        base = dequant(Z, a)
+        S = mat(base)
+        ue = [-sum(S[i][j] * er[i] * kappa[i] for i in range(dk)) for j in range(dv)]
+        recs.append((list(w), list(kappa), ue))
+        recs.append(([F(1)] * dk, list(k), list(v)))
+        S = mat(base)
+        ys.append([sum(S[i][j] * q[i] for i in range(dk)) for j in range(dv)])
+        if (t + 1) % W == 0:
+            Z, a = quantize(S)
+            bounds.append((Z, a))
+            recs = []
+    return ys, bounds
+
+
+def rwkv7_explicit_run(S0: Mat, inputs, W: int):
+    """Dequantize at each window start, run dense RWKV7 steps, requantize at its end."""
+    Z, a = quantize(S0)
+    ys, bounds = [], []
+    S = dequant(Z, a)
+    for t, (q, k, v, w, kappa, er) in enumerate(inputs):
+        S, y = rwkv7_step(S, q, k, v, w, kappa, er)
+        ys.append(y)
+        if (t + 1) % W == 0:
+            Z, a = quantize(S)
+            bounds.append((Z, a))
+            S = dequant(Z, a)
+    return ys, bounds
+
+
 def log_run(S0: Mat, inputs, M: int, delta: bool = True):
     """Base + log (DeltaLog Alg. 1, eqs. 4-7) with decays as exact gate products:
     D(lbar) is the product of the gates since the last merge and D(lbar - Lam_m) the

@@ -303,6 +303,71 @@ void oracle_q8_window_step(int64_t nh, int dk, int dv, int per_key, int W, int p
 }
 
 /*
+ * One RWKV7 token on the per-window int8 state. Each token is two records (LeapQuant,
+ * App. A: an erase sub-step with D = Diag(w), key kappa, read vector a * kappa and v = 0,
+ * then a write sub-step with D = I, key k and read vector 0), so a window of W tokens
+ * buffers 2W records, erase_0, write_0, erase_1, ..., with gates w_0, 1, w_1, 1, ...;
+ * eq. 4 over them is the same cumulative-decay sum as for one record per token.
+ * Token pos (0-based) sees the 2 pos records before it:
+ *   S_{t-1} = eq. 4 over records 0 .. 2pos-1
+ *   u_e = 0 - S_{t-1}^T (a * kappa)        record 2 pos   = (w, kappa, u_e)
+ *   u_w = v                                 record 2 pos+1 = (1, k, v)
+ *   S_t = eq. 4 over records 0 .. 2pos+1,   y = S_t^T q
+ * and at the last token (pos = W-1) S_W is quantized into the next window's (Z, a).
+ * Records: G[nh][2W][dk], K[nh][2W][dk], U[nh][2W][dv].
+ */
+void oracle_rwkv7_q8_window_step(int64_t nh, int dk, int dv, int W, int pos, int8_t *Z, float *a,
+                                 double *G, double *K, double *U, const double *q, const double *k,
+                                 const double *v, const double *w, const double *kappa,
+                                 const double *erase, double *y, double *Sw_out, double *w_out)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t h = 0; h < nh; ++h) {
+        int8_t *Zh = Z + (size_t)h * dk * dv;
+        float *ah = a + (size_t)h * dk;
+        double *Gh = G + (size_t)h * 2 * W * dk;
+        double *Kh = K + (size_t)h * 2 * W * dk;
+        double *Uh = U + (size_t)h * 2 * W * dv;
+        const double *qh = q + (size_t)h * dk, *kh = k + (size_t)h * dk, *vh = v + (size_t)h * dv;
+        const double *wh = w + (size_t)h * dk, *ch = kappa + (size_t)h * dk, *eh = erase + (size_t)h * dk;
+        double *yh = y + (size_t)h * dv;
+        const int re = 2 * pos, rw = 2 * pos + 1;
+
+        double *S0 = (double *)malloc(sizeof(double) * dk * dv);
+        double *St = (double *)malloc(sizeof(double) * dk * dv);
+        dequant_head(dk, dv, Zh, ah, S0);
+        window_materialize(dk, dv, 1, re, S0, Gh, Kh, Uh, St);          /* S_{t-1} */
+        for (int j = 0; j < dv; ++j) {
+            double p = 0.0;
+            for (int i = 0; i < dk; ++i)
+                p += St[IDX2(i, j, dv)] * eh[i] * ch[i];
+            Uh[IDX2(re, j, dv)] = 0.0 - p;
+            Uh[IDX2(rw, j, dv)] = vh[j];
+        }
+        for (int i = 0; i < dk; ++i) {
+            Gh[IDX2(re, i, dk)] = wh[i];
+            Kh[IDX2(re, i, dk)] = ch[i];
+            Gh[IDX2(rw, i, dk)] = 1.0;
+            Kh[IDX2(rw, i, dk)] = kh[i];
+        }
+        window_materialize(dk, dv, 1, rw + 1, S0, Gh, Kh, Uh, St);      /* S_t */
+        for (int j = 0; j < dv; ++j) {
+            double acc = 0.0;
+            for (int i = 0; i < dk; ++i)
+                acc += St[IDX2(i, j, dv)] * qh[i];
+            yh[j] = acc;
+        }
+        if (pos == W - 1) {
+            if (Sw_out)
+                memcpy(Sw_out + (size_t)h * dk * dv, St, sizeof(double) * dk * dv);
+            oracle_q8_quantize(dk, dv, St, Zh, ah, w_out ? w_out + (size_t)h * dk * dv : NULL);
+        }
+        free(S0);
+        free(St);
+    }
+}
+
+/*
  * One step of the base + log representation (DeltaLog, sec. 3.1, Algorithm 1,
  * eqs. 2-7). The physical state of a head is the dense base Sbar, the cumulative
  * log-decay lbar (one value, or one per key channel) and L live log entries

@@ -8,6 +8,12 @@ the RWKV6 step at a = 0, an exact substitution onto the (separately pinned) KDA 
 erase removing the kappa direction completely at w = 1, a = 1, joint linearity, and exact
 rational brute force. A slip such as reading the erase from the decayed state, dropping
 the erase rate or swapping the order of the two sub-steps fails at least one of them.
+
+On the per-window int8 representation each token is two records (App. A: the same
+treatment as a DeltaProduct token with n = 2): gates w and 1, keys kappa and k, values
+-S^T (a * kappa) and v. Pins: the window equals the explicit dequantize / dense steps /
+requantize schedule (fp64 for W in {1, 2, 3, 16}, and with equality in exact rationals),
+and a = 0 leaves erase records that only decay (the single-record RWKV6 readout).
 """
 import numpy as np
 import pytest
@@ -110,3 +116,80 @@ def test_exact_rationals_match_the_fp64_oracle():
         y64 = oracle.rwkv7_step(S64, q[None], k[None], v[None], w[None], kappa[None], a[None])
         np.testing.assert_allclose(S64[0], np.array(Sx, dtype=float), rtol=0, atol=1e-13)
         np.testing.assert_allclose(y64[0], np.array(yx, dtype=float), rtol=0, atol=1e-13)
+
+
+# ---------------------------------------------------------------- two records per token
+
+def _explicit_schedule(S0, steps, W):
+    """Dequantize, run W dense RWKV7 steps, requantize (what eq. 4 over 2W records unrolls)."""
+    Z, a = oracle.q8_quantize(S0)
+    S = oracle.dequant(Z, a)
+    ys, bounds = [], []
+    for t, st in enumerate(steps):
+        ys.append(oracle.rwkv7_step(S, *st))
+        if (t + 1) % W == 0:
+            Z, a, w = oracle.q8_quantize(S, with_w=True)
+            bounds.append((Z, a, w, S.copy()))
+            S = oracle.dequant(Z, a)
+    return ys, bounds
+
+
+@pytest.mark.parametrize("W,T", [(1, 4), (2, 6), (3, 9), (16, 40)])
+def test_window_with_two_records_per_token_equals_explicit_schedule(W, T):
+    nh, dk, dv = 5, 128, 128
+    S0 = RNG.standard_normal((nh, dk, dv)) * 0.02
+    S0[:, 5, :] *= 50
+    S0[:, :, 9] *= 50
+    steps = [_inputs(nh, dk, dv, RNG) for _ in range(T)]
+    ys_ref, bounds = _explicit_schedule(S0, steps, W)
+    Z, a = oracle.q8_quantize(S0)
+    ws = oracle.Rwkv7WindowState(Z, a, W)
+    nb = 0
+    for t, st in enumerate(steps):
+        if ws.pos == W - 1:
+            y, Sw, w = ws.step(*st, want_boundary=True)
+            Zr, ar, wr, Sr = bounds[nb]
+            nb += 1
+            np.testing.assert_allclose(Sw, Sr, rtol=0, atol=1e-12)
+            np.testing.assert_array_equal(ws.a, ar)
+            near_tie = np.abs(np.abs(wr - np.trunc(wr)) - 0.5) < 1e-9
+            assert np.all((ws.Z == Zr) | near_tie)
+        else:
+            y = ws.step(*st)
+            # the token's two records: (w, kappa, -S^T (a kappa)) and (1, k, v)
+            p = ws.pos - 1
+            np.testing.assert_array_equal(ws.G[:, 2 * p], st[3])
+            np.testing.assert_array_equal(ws.K[:, 2 * p], st[4])
+            np.testing.assert_array_equal(ws.G[:, 2 * p + 1], 1.0)
+            np.testing.assert_array_equal(ws.K[:, 2 * p + 1], st[1])
+            np.testing.assert_array_equal(ws.U[:, 2 * p + 1], st[2])
+        np.testing.assert_allclose(y, ys_ref[t], rtol=0, atol=1e-11)
+
+
+def test_window_with_zero_erase_rate_has_pure_decay_erase_records():
+    """a = 0: every erase record carries u = 0, so it only decays (the single-record
+    RWKV6 form inside the window)."""
+    nh, dk, dv, W = 3, 128, 128, 4
+    S0 = RNG.standard_normal((nh, dk, dv)) * 0.02
+    Z, a = oracle.q8_quantize(S0)
+    ws = oracle.Rwkv7WindowState(Z, a, W)
+    S = oracle.dequant(Z, a)
+    for _ in range(W - 1):
+        q, k, v, w, kappa, _ = _inputs(nh, dk, dv, RNG)
+        y = ws.step(q, k, v, w, kappa, np.zeros((nh, dk)))
+        y6 = oracle.rwkv6_step(S, q, k, v, w)
+        np.testing.assert_allclose(y, y6, rtol=0, atol=1e-12)
+        assert not ws.U[:, 2 * (ws.pos - 1)].any()
+
+
+@pytest.mark.parametrize("W,T", [(1, 3), (2, 4), (3, 6)])
+def test_exact_window_with_two_records_equals_explicit_schedule(W, T):
+    rng = np.random.default_rng(90 + W)
+    dk, dv = 4, 3
+    S0 = exact.frac_mat(rng.standard_normal((dk, dv)))
+    fs = []
+    for _ in range(T):
+        q, k, v = rng.standard_normal(dk), rng.standard_normal(dk), rng.standard_normal(dv)
+        w, kappa, er = rng.uniform(0.8, 1, dk), rng.standard_normal(dk), rng.uniform(0, 1, dk)
+        fs.append(tuple(exact.frac_vec(x) for x in (q, k, v, w, kappa, er)))
+    assert exact.rwkv7_window_run(S0, fs, W) == exact.rwkv7_explicit_run(S0, fs, W)
