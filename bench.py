@@ -40,7 +40,7 @@ KERNEL_SOURCES = {
 }
 
 WORKLOAD_BY_FLAG = {"gdn": 2, "gdn_small": 1, "kda": 3, "q8": 4, "log": 5, "lq": 6, "rwkv6": 7,
-                    "rwkv6_log": 8, "kda_lq": 9, "rwkv7": 10}
+                    "rwkv6_log": 8, "kda_lq": 9, "rwkv7": 10, "rwkv7_q8": 11}
 LQ_TOKENS = 4
 
 
@@ -70,8 +70,26 @@ def window_step_bytes_per_head(w: wl.Workload, pos: int) -> int:
     gdim = d if w.per_key_gate else 1
     rec = d * _in_bytes(w) + 4 * d + 4 * gdim
     inputs = 3 * d * _in_bytes(w) + 4 * gdim + 4
+    if w.variant == "rwkv7":
+        return rwkv7_window_step_bytes_per_head(w, pos)
     rd = d * d + 4 * d + pos * rec + inputs
     wr = 4 * d + ((d * d + 4 * d) if pos == w.W - 1 else rec)
+    return rd + wr
+
+
+def rwkv7_window_step_bytes_per_head(w: wl.Workload, pos: int) -> int:
+    """RWKV7 on the int8 window, two records per token: the step reads codes + row scales,
+    its 2 pos records (key in the input dtype, value and per-key gate fp32), q, k, v, kappa,
+    w and a, and writes y and its two records; at the last token a second pass reads the
+    codes, scales and all 2W records and writes the requantized codes and scales."""
+    d = wl.DK
+    rec = d * _in_bytes(w) + 4 * d + 4 * d
+    inputs = 4 * d * _in_bytes(w) + 2 * 4 * d
+    rd = d * d + 4 * d + 2 * pos * rec + inputs
+    wr = 4 * d + 2 * rec
+    if pos == w.W - 1:
+        rd += d * d + 4 * d + 2 * w.W * rec
+        wr += d * d + 4 * d
     return rd + wr
 
 
@@ -231,6 +249,22 @@ def run_gpu(w: wl.Workload, steps: int, warmup: int, slots: bool = False, n_iter
         def step():
             i = state["t"] % n_inputs
             fn(S, x["q"][i], x["k"][i], x["v"][i], x["gate"][i], x["beta"][i], y)
+            state["t"] += 1
+    elif w.path == "q8_window" and w.variant == "rwkv7":
+        W = w.W
+        Z = torch.empty(B, H, 128, 128, device=dev, dtype=torch.int8)
+        A = torch.empty(B, H, 128, device=dev)
+        rsu.q8_quantize(S0, Z, A)
+        del S0
+        Kb = torch.zeros(B, H, 2 * W, 128, device=dev, dtype=x["q"].dtype)
+        Ub = torch.zeros(B, H, 2 * W, 128, device=dev)
+        Gb = torch.zeros(B, H, 2 * W, 128, device=dev)
+
+        def step():
+            t = state["t"]
+            i = t % n_inputs
+            rsu.rwkv7_q8_window(W, t % W, Z, A, Kb, Ub, Gb, x["q"][i], x["k"][i], x["v"][i], x["kappa"][i],
+                                x["gate"][i], x["a"][i], y)
             state["t"] += 1
     elif w.path == "q8_window":
         W = w.W

@@ -269,6 +269,24 @@ int rwkv7_decode_step(const rsu_dims *dims, float *S, const void *q, const void 
                       float *y, rsu_stream_t stream);
 
 /* ------------------------------------------------------------------------
+ * RWKV7 on the per-window int8 state, two records per token (LeapQuant App. A:
+ * the same treatment as a DeltaProduct token with two sub-steps). A window of W
+ * tokens buffers 2W records; token pos writes record 2 pos = the erase
+ * (gate w, key kappa, value 0 - S_{t-1}^T (a * kappa)) and record 2 pos + 1 = the
+ * write (gate 1, key k, value v), and returns y = S_t^T q read by eq. 9 over the
+ * window-start (Z, row_absmax) and the records:
+ *   Kbuf [B,H,2W,d] in qkv_dtype, Ubuf [B,H,2W,d] fp32, Gbuf [B,H,2W,d_k] fp32.
+ * At pos = W-1 the token's records are appended as well and S_W (eq. 4 over all
+ * 2W records) is requantized into Z and row_absmax in place, by a second launch on
+ * the same stream. 1 <= W <= 16, 0 <= pos < W. Inputs as for rwkv7_decode_step;
+ * codes, scales and other rules as for the per-row int8 window.
+ * ---------------------------------------------------------------------- */
+int rwkv7_q8_window(const rsu_dims *dims, int W, int pos, int8_t *Z, float *row_absmax,
+                    void *Kbuf, float *Ubuf, float *Gbuf, const void *q, const void *k,
+                    const void *v, const void *kappa, const float *w, const float *a,
+                    float *y, rsu_stream_t stream);
+
+/* ------------------------------------------------------------------------
  * Measurement helper (not part of the recurrence): dst[i] = src[i] for
  * n fp32 elements, with the same 128-bit non-temporal access pattern and grid
  * shape (64 KiB per workgroup) as the dense step. n must be a multiple of 4.

@@ -65,6 +65,7 @@ _SIGS = {
     "kda_log_step_slots": [_DP, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
     "rwkv6_decode_step": [_DP, _P, _P, _P, _P, _P, _P, _P],
     "rwkv7_decode_step": [_DP, _P, _P, _P, _P, _P, _P, _P, _P, _P],
+    "rwkv7_q8_window": [_DP, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
     "rwkv6_log_append": [_DP, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
     "rwkv6_log_merge": [_DP, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
     "rwkv6_log_step_slots": [_DP, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
@@ -273,6 +274,25 @@ def rwkv7_decode_step(S, q, k, v, kappa, w, a, y):
     _need(y, "y", torch.float32, (dims.B, dims.H, D))
     _call("rwkv7_decode_step", ctypes.byref(dims), _ptr(S), _ptr(q), _ptr(k), _ptr(v), _ptr(kappa), _ptr(w),
           _ptr(a), _ptr(y), _stream())
+    return y
+
+
+def rwkv7_q8_window(W, pos, Z, row_absmax, Kbuf, Ubuf, Gbuf, q, k, v, kappa, w, a, y):
+    """Token pos of a window of W on the int8 state with two records per token (records
+    2 pos and 2 pos + 1; at pos == W - 1 the state is requantized from all 2W records)."""
+    dims = _dims(q, k, v)
+    B, H = dims.B, dims.H
+    _need(Z, "Z", torch.int8, (B, H, D, D))
+    _need(row_absmax, "row_absmax", torch.float32, (B, H, D))
+    _need(Kbuf, "Kbuf", q.dtype, (B, H, 2 * W, D))
+    _need(Ubuf, "Ubuf", torch.float32, (B, H, 2 * W, D))
+    _need(Gbuf, "Gbuf", torch.float32, (B, H, 2 * W, D))
+    _need(kappa, "kappa", q.dtype, (B, H, D))
+    _need(w, "w", torch.float32, (B, H, D))
+    _need(a, "a", torch.float32, (B, H, D))
+    _need(y, "y", torch.float32, (B, H, D))
+    _call("rwkv7_q8_window", ctypes.byref(dims), int(W), int(pos), _ptr(Z), _ptr(row_absmax), _ptr(Kbuf),
+          _ptr(Ubuf), _ptr(Gbuf), _ptr(q), _ptr(k), _ptr(v), _ptr(kappa), _ptr(w), _ptr(a), _ptr(y), _stream())
     return y
 
 

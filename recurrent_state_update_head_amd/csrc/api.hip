@@ -327,6 +327,31 @@ int rwkv7_decode_step(const rsu_dims* dims, float* S, const void* q, const void*
                     fn);
 }
 
+int rwkv7_q8_window(const rsu_dims* dims, int W, int pos, int8_t* Z, float* row_absmax, void* Kbuf, float* Ubuf,
+                    float* Gbuf, const void* q, const void* k, const void* v, const void* kappa, const float* w,
+                    const float* a, float* y, rsu_stream_t stream) {
+    const char* fn = "rwkv7_q8_window";
+    int heads = 0;
+    if (int rc = check_dims(dims, &heads, fn)) return rc;
+    if (W < 1 || W > 16) return fail(RSU_E_RANGE, "%s: W=%d outside [1, 16] (two records per token)", fn, W);
+    if (pos < 0 || pos >= W) return fail(RSU_E_RANGE, "%s: pos=%d outside [0, W=%d)", fn, pos, W);
+    if (heads == 0) return RSU_OK;
+    if (int rc = check_ptrs({{Z, "Z"}, {row_absmax, "row_absmax"}, {Kbuf, "Kbuf"}, {Ubuf, "Ubuf"}, {Gbuf, "Gbuf"},
+                             {q, "q"}, {k, "k"}, {v, "v"}, {kappa, "kappa"}, {w, "w"}, {a, "a"}, {y, "y"}}, fn))
+        return rc;
+    rsu::WindowArgs wa;
+    wa.W = W;
+    wa.pos = pos;
+    wa.Z = Z;
+    wa.A = row_absmax;
+    wa.Kbuf = Kbuf;
+    wa.Ubuf = Ubuf;
+    wa.Gbuf = Gbuf;
+    return launched(rsu::launch_rwkv7_q8_window(step_args(heads, nullptr, q, k, v, w, nullptr, y), wa, kappa, a,
+                                                dims->qkv_dtype == RSU_BF16, stream),
+                    fn);
+}
+
 int rwkv6_log_append(const rsu_dims* dims, int C, int L, const float* Sbase, float* lbar, void* Klog,
                      void* Ulog, float* Lam, const void* q, const void* k, const void* v, const float* w,
                      float* y, rsu_stream_t stream) {

@@ -48,6 +48,10 @@ hipError_t launch_copy(const float* src, float* dst, int64_t n, hipStream_t stre
 hipError_t launch_q8_quantize(int heads, const float* S, int8_t* Z, float* A, hipStream_t stream);
 hipError_t launch_q8_window(const StepArgs& a, const WindowArgs& w, bool per_key, bool bf16,
                             hipStream_t stream);
+// RWKV7 on the int8 window, two records per token (W <= 16; Kbuf, Ubuf, Gbuf hold 2W
+// records per head, Gbuf per key): gate = w, kappa in the input dtype, erase [heads, 128]
+hipError_t launch_rwkv7_q8_window(const StepArgs& a, const WindowArgs& w, const void* kappa, const float* erase,
+                                  bool bf16, hipStream_t stream);
 // LeapQuant's boundary format (GDN or KDA, bf16 keys, W <= 16): payload, per-column absmax,
 // per-row smoothing scales, fp16 token pairs [heads][4][128], and the window's records.
 struct LqArgs {

@@ -308,6 +308,85 @@ __device__ __forceinline__ uint32_t code_byte(float w) {
     return static_cast<uint32_t>(min(max(bits, lo), hi)) & 0xffu;
 }
 
+// S_W of eq. 4 from the staged window, requantized in place: the record sum is a
+// [128 x kWmax] . [kWmax x 128] contraction per head, done on the matrix cores as its
+// transpose with v_mfma_f32_16x16x4f32 (A from lane l is A[l%16][l/16], B is B[l/16][l%16],
+// result i of lane l is D[4(l/16)+i][l%16]). Wave w owns key rows 32w .. 32w+31 as two bands
+// of 16 (B = decayed keys KE, one row per lane l%16); value-column tile ct (A = corrections
+// Us) takes the columns 8m + ct, m = 0..15, so that lane l reads the corrections of columns
+// 8(l%16) .. +7 with two 128-bit LDS loads and ends up holding the 32 consecutive columns
+// 32(l/16) .. +31 of its row: result i of tile ct is column 32(l/16) + 8i + ct. All operands
+// of a band are loaded before its MFMAs. Rows of KE / Us past the last record are zero;
+// zcoef[r] = a_r / 127 Gamma_{1:W, r}; Zs holds the old codes (row stride kZsStride) and
+// receives the new ones; the rows leave from there as whole 128-byte rows.
+template <int kWmax>
+__device__ __forceinline__ void form_and_requantize(const float* KE, const float* Us, uint32_t* Zs,
+                                                    const float* zcoef, float* __restrict__ Ah,
+                                                    uint32_t* __restrict__ Zh, int wave, int lane) {
+    constexpr int kSteps = kWmax / 4;
+    const int lr = lane & 15, lq = lane >> 4;
+    f32x4 ua[kSteps][2];
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s) {
+        const float* src = Us + (4 * s + lq) * kD + 8 * lr;
+        ua[s][0] = *reinterpret_cast<const f32x4*>(src);
+        ua[s][1] = *reinterpret_cast<const f32x4*>(src + 4);
+    }
+    for (int a = 0; a < 2; ++a) {  // one 16-row band at a time: 8 accumulators live
+        const int row = 16 * (2 * wave + a) + lr;
+        float eb[kSteps];
+#pragma unroll
+        for (int s = 0; s < kSteps; ++s)
+            eb[s] = KE[(4 * s + lq) * kD + row];
+        // old codes of columns 32 lq .. +31: dword d holds columns 32 lq + 4d .. +3
+        uint32_t zo[8];
+#pragma unroll
+        for (int d = 0; d < 8; ++d) zo[d] = Zs[row * kZsStride + 8 * lq + d];
+        const float zc = zcoef[row];
+        f32x4 acc[8];
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                acc[ct][i] = static_cast<float>(static_cast<int8_t>((zo[2 * i + ct / 4] >> (8 * (ct % 4))) & 0xffu)) * zc;
+#pragma unroll
+        for (int s = 0; s < kSteps; ++s) {
+#pragma unroll
+            for (int ct = 0; ct < 8; ++ct)
+                acc[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(ua[s][ct / 4][ct % 4], eb[s], acc[ct], 0, 0, 0);
+        }
+        // per-row absmax: 32 values in this lane, then the 4 lanes l, l^16, l^32, l^48
+        float m = 0.f;
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct)
+            m = fmaxf(m, fmaxf(fmaxf(fabsf(acc[ct].x), fabsf(acc[ct].y)),
+                               fmaxf(fabsf(acc[ct].z), fabsf(acc[ct].w))));
+        m = max_xor16(m);
+        float m0, m1;
+        swap32(m, m0, m1);
+        m = fmaxf(m0, m1);
+        const float sc = m > 0.f ? __fdiv_rn(127.f, m) : 0.f;
+        if (lq == 0) Ah[row] = m;
+        // the new codes replace the old ones in Zs (this lane read exactly these words)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh)
+                Zs[row * kZsStride + 8 * lq + 2 * i + hh] =
+                    code_byte(acc[4 * hh + 0][i] * sc) | (code_byte(acc[4 * hh + 1][i] * sc) << 8) |
+                    (code_byte(acc[4 * hh + 2][i] * sc) << 16) | (code_byte(acc[4 * hh + 3][i] * sc) << 24);
+    }
+    // the wave's 32 rows (32w .. 32w+31, 4 KiB of codes) leave as whole 128-byte rows
+    wave_lds_sync();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int row = 32 * wave + 8 * i + (lane >> 3), d0 = 4 * (lane & 7);
+        const uint32_t* src = Zs + row * kZsStride + d0;
+        const u32x4 w4 = {src[0], src[1], src[2], src[3]};
+        __builtin_nontemporal_store(w4, reinterpret_cast<u32x4*>(Zh + row * (kD / 4) + d0));
+    }
+}
+
 // ---- the last step of the window (pos = W - 1): the step itself, then S_W of eq. 4
 // formed from the codes and all W records, and requantized in place.
 template <bool kPerKey, int kWmax, typename T>
@@ -464,77 +543,225 @@ __global__ __launch_bounds__(kThreads) void q8_boundary_kernel(
     __syncthreads();
 
     // ---- S_W = Gamma_{1:W} S^_0 + sum_j Gamma_{j+1:W} k_j u_j^T, requantized.
-    // The record sum is a [128 x kWmax] . [kWmax x 128] contraction per head, done on the
-    // matrix cores as its transpose with v_mfma_f32_16x16x4f32 (A from lane l is
-    // A[l%16][l/16], B is B[l/16][l%16], result i of lane l is D[4(l/16)+i][l%16]).
-    // Wave w owns key rows 32w .. 32w+31 as two bands of 16 (B = decayed keys, one
-    // row per lane l%16); value-column tile ct (A = corrections) takes the columns
-    // 8m + ct, m = 0..15, so that lane l reads the corrections of columns
-    // 8(l%16) .. +7 with two 128-bit LDS loads and ends up holding the 32
-    // consecutive columns 32(l/16) .. +31 of its row: result i of tile ct is column
-    // 32(l/16) + 8i + ct. All operands of a band are loaded before its MFMAs.
-    constexpr int kSteps = kWmax / 4;
-    const int lr = lane & 15, lq = lane >> 4;
-    f32x4 ua[kSteps][2];
+    form_and_requantize<kWmax>(KE, Us, Zs, zcoef, A + vec_off, Zh, wave, lane);
+}
+
+// ---- RWKV7 on the per-window int8 state, two records per token (LeapQuant, App. A: an
+// erase sub-step with gate w, key kappa and read vector a * kappa, then a write with gate 1
+// and key k). Record 2t = (w_t, kappa_t, u_e = 0 - S_{t-1}^T (a_t * kappa_t)), record 2t+1 =
+// (1, k_t, v_t). Token t reads S_{t-1} (eq. 4 over its 2t records) along a_t * kappa_t and,
+// for the output, along w_t * q_t:  y = S_{t-1}^T (w_t q_t) + u_e (kappa_t . q_t) + v_t (k_t . q_t).
+// Both reads are one sweep with the per-key step's layout (records in registers, 16-lane
+// groups for their coefficients, row-owners for their corrections); a record's decay is the
+// product of the later records' gates (the read vectors carry the token's own factors).
+// Every token, the last one too, appends its two records; at the end of the window a
+// second launch requantizes S_W from all 2W records.
+constexpr int kRwkv7Rec = 32;  // records per window: two per token, W <= 16
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void rwkv7_q8_step_kernel(
+    int W, int pos, const int8_t* __restrict__ Z, const float* __restrict__ A, T* __restrict__ Kbuf,
+    float* __restrict__ Ubuf, float* __restrict__ Gbuf, const T* __restrict__ q, const T* __restrict__ k,
+    const T* __restrict__ v, const T* __restrict__ kappa, const float* __restrict__ w,
+    const float* __restrict__ erase, float* __restrict__ y) {
+    extern __shared__ __align__(16) float gs_lds[];   // the records' gates [2 pos][128]
+    __shared__ f32x2 rowv[kD];            // a_r/127 Gamma_{1:t-1} (a_r kappa_r, w_r q_r)
+    __shared__ f32x2 coef[kRwkv7Rec];     // per record (E_j . a kappa, E_j . w q)
+    __shared__ f32x2 red[4][kD];          // per-wave column partials
+    __shared__ f32x2 kq_part[2];          // (kappa . q, k . q) of the two waves that hold rows
+    constexpr int kKSlots = kRwkv7Rec / 16, kUSlots = kRwkv7Rec / 8;
+
+    const int h = head_of_block(blockIdx.x, gridDim.x), tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
+    const int c4 = lane & 31, ro = lane >> 5, owner = 2 * wave + ro;
+    const int grp = tid >> 4, ch = tid & 15;
+    const size_t vec_off = static_cast<size_t>(h) * kD;
+    const size_t rec0 = static_cast<size_t>(h) * 2 * W * kD;
+    const int r = tid & (kD - 1);
+    const bool first = tid < kD;
+    const int nrec = 2 * pos;
+
+    // ---- loads: records, gates, inputs, then the codes
+    Raw8<T> kc[kKSlots];
 #pragma unroll
-    for (int s = 0; s < kSteps; ++s) {
-        const float* src = Us + (4 * s + lq) * kD + 8 * lr;
-        ua[s][0] = *reinterpret_cast<const f32x4*>(src);
-        ua[s][1] = *reinterpret_cast<const f32x4*>(src + 4);
+    for (int s = 0; s < kKSlots; ++s) {
+        const int j = grp + 16 * s;
+        if (16 * s < nrec) kc[s].load(Kbuf + rec0 + static_cast<size_t>(j < nrec ? j : 0) * kD + 8 * ch);
     }
-    for (int a = 0; a < 2; ++a) {  // one 16-row band at a time: 8 accumulators live
-        const int row = 16 * (2 * wave + a) + lr;
-        float eb[kSteps];
+    f32x4 ur[kUSlots];
 #pragma unroll
-        for (int s = 0; s < kSteps; ++s)
-            eb[s] = KE[(4 * s + lq) * kD + row];
-        // old codes of columns 32 lq .. +31: dword d holds columns 32 lq + 4d .. +3
-        uint32_t zo[8];
+    for (int m = 0; m < kUSlots; ++m) {
+        const int j = owner + 8 * m;
+        ur[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (8 * m < nrec)
+            ur[m] = *reinterpret_cast<const f32x4*>(Ubuf + rec0 + static_cast<size_t>(j < nrec ? j : 0) * kD + 4 * c4);
+    }
+    Stager<float, kRwkv7Rec * kD> sg;
+    sg.load(Gbuf + rec0, nrec * kD, tid);
+    Raw8<T> cch, qch;  // kappa and q of the lane's 8 keys
+    cch.load(kappa + vec_off + 8 * ch);
+    qch.load(q + vec_off + 8 * ch);
+    const f32x4 w_lo = *reinterpret_cast<const f32x4*>(w + vec_off + 8 * ch);
+    const f32x4 w_hi = *reinterpret_cast<const f32x4*>(w + vec_off + 8 * ch + 4);
+    const f32x4 e_lo = *reinterpret_cast<const f32x4*>(erase + vec_off + 8 * ch);
+    const f32x4 e_hi = *reinterpret_cast<const f32x4*>(erase + vec_off + 8 * ch + 4);
+    const float kr = load_in(k, vec_off + r), qr = load_in(q, vec_off + r), cr = load_in(kappa, vec_off + r);
+    const float wr = w[vec_off + r], er = erase[vec_off + r];
+    const float ar = A[vec_off + r];
+    const float vr = load_in(v, vec_off + r);
+    const uint32_t* Zh = reinterpret_cast<const uint32_t*>(Z + static_cast<size_t>(h) * kD * kD);
+    uint32_t zw[kRowsPerThread];
 #pragma unroll
-        for (int d = 0; d < 8; ++d) zo[d] = Zs[row * kZsStride + 8 * lq + d];
-        const float zc = zcoef[row];
-        f32x4 acc[8];
+    for (int it = 0; it < kRowsPerThread; ++it)
+        zw[it] = __builtin_nontemporal_load(Zh + q8_row(it, wave, ro) * (kD / 4) + c4);
+
+    sg.store(gs_lds, tid);
+    __syncthreads();
+
+    // ---- decays: Gs = product of the gates of the records after record grp + 16 s, per key of
+    // the lane's 8; Gall = product of all record gates at row r
+    float Gs[kKSlots][8];
 #pragma unroll
-        for (int ct = 0; ct < 8; ++ct)
+    for (int s = 0; s < kKSlots; ++s) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                acc[ct][i] = static_cast<float>(static_cast<int8_t>((zo[2 * i + ct / 4] >> (8 * (ct % 4))) & 0xffu)) * zc;
+        for (int e = 0; e < 8; ++e) Gs[s][e] = 1.f;
+        if (16 * s >= nrec) continue;
+        for (int i = nrec - 1; i > grp + 16 * s; --i) {
+            const f32x4 lo = *reinterpret_cast<const f32x4*>(gs_lds + i * kD + 8 * ch);
+            const f32x4 hi = *reinterpret_cast<const f32x4*>(gs_lds + i * kD + 8 * ch + 4);
 #pragma unroll
-        for (int s = 0; s < kSteps; ++s) {
-#pragma unroll
-            for (int ct = 0; ct < 8; ++ct)
-                acc[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(ua[s][ct / 4][ct % 4], eb[s], acc[ct], 0, 0, 0);
+            for (int e = 0; e < 4; ++e) {
+                Gs[s][e] *= lo[e];
+                Gs[s][e + 4] *= hi[e];
+            }
         }
-        // per-row absmax: 32 values in this lane, then the 4 lanes l, l^16, l^32, l^48
-        float m = 0.f;
-#pragma unroll
-        for (int ct = 0; ct < 8; ++ct)
-            m = fmaxf(m, fmaxf(fmaxf(fabsf(acc[ct].x), fabsf(acc[ct].y)),
-                               fmaxf(fabsf(acc[ct].z), fabsf(acc[ct].w))));
-        m = max_xor16(m);
-        float m0, m1;
-        swap32(m, m0, m1);
-        m = fmaxf(m0, m1);
-        const float sc = m > 0.f ? __fdiv_rn(127.f, m) : 0.f;
-        if (lq == 0) A[vec_off + row] = m;
-        // the new codes replace the old ones in Zs (this lane read exactly these words)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int hh = 0; hh < 2; ++hh)
-                Zs[row * kZsStride + 8 * lq + 2 * i + hh] =
-                    code_byte(acc[4 * hh + 0][i] * sc) | (code_byte(acc[4 * hh + 1][i] * sc) << 8) |
-                    (code_byte(acc[4 * hh + 2][i] * sc) << 16) | (code_byte(acc[4 * hh + 3][i] * sc) << 24);
     }
-    // the wave's 32 rows (32w .. 32w+31, 4 KiB of codes) leave as whole 128-byte rows
-    wave_lds_sync();
+    float Gall = 1.f;
+    for (int i = nrec - 1; i >= 0; --i) Gall *= gs_lds[i * kD + r];
+
+    // ---- record coefficients against both read vectors, over the 16 lanes of each group
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int row = 32 * wave + 8 * i + (lane >> 3), d0 = 4 * (lane & 7);
-        const uint32_t* src = Zs + row * kZsStride + d0;
-        const u32x4 w4 = {src[0], src[1], src[2], src[3]};
-        __builtin_nontemporal_store(w4, reinterpret_cast<u32x4*>(Zh + row * (kD / 4) + d0));
+    for (int s = 0; s < kKSlots; ++s) {
+        if (16 * s >= nrec) continue;
+        const int j = grp + 16 * s;
+        float c1 = 0.f, c2 = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float ej = kc[s][e] * Gs[s][e];
+            const float x1 = (e < 4 ? e_lo[e] : e_hi[e - 4]) * cch[e];
+            const float x2 = (e < 4 ? w_lo[e] : w_hi[e - 4]) * qch[e];
+            c1 += ej * x1;
+            c2 += ej * x2;
+        }
+        c1 = row16_sum(c1);
+        c2 = row16_sum(c2);
+        if (ch == 0 && j < nrec) coef[j] = f32x2{c1, c2};
     }
+    if (first) {
+        const float c0 = ar * (1.f / 127.f) * Gall;  // a_r/127 Gamma_{1:t-1} at row r
+        rowv[r] = f32x2{c0 * (er * cr), c0 * (wr * qr)};
+        const float cq = wave_sum(cr * qr);
+        const float kq = wave_sum(kr * qr);
+        if (lane == 0) kq_part[wave] = f32x2{cq, kq};
+    }
+    __syncthreads();
+
+    // ---- one sweep of the int8 tile for both read vectors, plus the records
+    f32x4 p1 = {0.f, 0.f, 0.f, 0.f}, p2 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int it = 0; it < kRowsPerThread; ++it) {
+        const f32x2 rv = rowv[q8_row(it, wave, ro)];
+        const f32x4 zf = unpack_i8x4(zw[it]);
+        p1 += zf * rv.x;
+        p2 += zf * rv.y;
+    }
+#pragma unroll
+    for (int m = 0; m < kUSlots; ++m) {
+        if (8 * m >= nrec) continue;
+        const int j = owner + 8 * m;
+        const f32x2 c = j < nrec ? coef[j] : f32x2{0.f, 0.f};
+        p1 += ur[m] * c.x;
+        p2 += ur[m] * c.y;
+    }
+    p1 = f32x4{add_xor32(p1.x), add_xor32(p1.y), add_xor32(p1.z), add_xor32(p1.w)};
+    p2 = f32x4{add_xor32(p2.x), add_xor32(p2.y), add_xor32(p2.z), add_xor32(p2.w)};
+    if (ro == 0) {
+        red[wave][4 * c4 + 0] = f32x2{p1.x, p2.x};
+        red[wave][4 * c4 + 1] = f32x2{p1.y, p2.y};
+        red[wave][4 * c4 + 2] = f32x2{p1.z, p2.z};
+        red[wave][4 * c4 + 3] = f32x2{p1.w, p2.w};
+    }
+    __syncthreads();
+
+    // ---- the erase value, the output, and the token's two records (thread -> column c == r)
+    if (first) {
+        const int c = tid;
+        const f32x2 acc = red[0][c] + red[1][c] + red[2][c] + red[3][c];
+        const f32x2 kq = kq_part[0] + kq_part[1];
+        const float ue = 0.f - acc.x;
+        y[vec_off + c] = acc.y + ue * kq.x + vr * kq.y;
+        const size_t re = rec0 + static_cast<size_t>(nrec) * kD, rw = re + kD;
+        store_in(Kbuf, re + c, cr);
+        Ubuf[re + c] = ue;
+        Gbuf[re + c] = wr;
+        store_in(Kbuf, rw + c, kr);
+        Ubuf[rw + c] = vr;
+        Gbuf[rw + c] = 1.f;
+    }
+}
+
+// ---- requantization of S_W = Gamma_{1:W} S^_0 + sum_j Gamma_{j+1:W} k_j u_j^T from nrec
+// buffered records and no current step (the window's last records are already appended).
+template <typename T>
+__global__ __launch_bounds__(kThreads) void q8_requant_kernel(int nrec, int rec_stride, int8_t* __restrict__ Z,
+                                                              float* __restrict__ A, const T* __restrict__ Kbuf,
+                                                              const float* __restrict__ Ubuf,
+                                                              const float* __restrict__ Gbuf) {
+    extern __shared__ __align__(16) float dyn_lds[];
+    __shared__ float zcoef[kD];
+    float* KE = dyn_lds;
+    float* Us = KE + kRwkv7Rec * kD;
+    float* Gs = Us + kRwkv7Rec * kD;
+    uint32_t* Zs = reinterpret_cast<uint32_t*>(Gs + kRwkv7Rec * kD);
+
+    const int h = head_of_block(blockIdx.x, gridDim.x), tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
+    const int c4 = lane & 31, ro = lane >> 5;
+    const int r = tid & (kD - 1);
+    const bool first = tid < kD;
+    const size_t vec_off = static_cast<size_t>(h) * kD;
+    const size_t rec0 = static_cast<size_t>(h) * rec_stride * kD;
+    uint32_t* Zh = reinterpret_cast<uint32_t*>(Z + static_cast<size_t>(h) * kD * kD);
+
+    Stager<T, kRwkv7Rec * kD> sk;
+    Stager<float, kRwkv7Rec * kD> su;
+    Stager<float, kRwkv7Rec * kD> sg;
+    sk.load(Kbuf + rec0, nrec * kD, tid);
+    su.load(Ubuf + rec0, nrec * kD, tid);
+    sg.load(Gbuf + rec0, nrec * kD, tid);
+    const float ar = A[vec_off + r];
+    uint32_t zw[kRowsPerThread];
+#pragma unroll
+    for (int it = 0; it < kRowsPerThread; ++it)
+        zw[it] = __builtin_nontemporal_load(Zh + q8_row(it, wave, ro) * (kD / 4) + c4);
+    sk.store(KE, tid);
+    su.store(Us, tid);
+    sg.store(Gs, tid);
+    for (int i = nrec * kD + tid; i < kRwkv7Rec * kD; i += kThreads) Us[i] = 0.f;
+#pragma unroll
+    for (int it = 0; it < kRowsPerThread; ++it) Zs[q8_row(it, wave, ro) * kZsStride + c4] = zw[it];
+    __syncthreads();
+    if (first) {  // thread r walks key row r from the newest record
+        float G = 1.f;
+        for (int j = nrec - 1; j >= 0; --j) {
+            KE[j * kD + r] *= G;
+            G *= Gs[j * kD + r];
+        }
+        for (int j = nrec; j < kRwkv7Rec; ++j) KE[j * kD + r] = 0.f;
+        zcoef[r] = ar * (1.f / 127.f) * G;
+    }
+    __syncthreads();
+    form_and_requantize<kRwkv7Rec>(KE, Us, Zs, zcoef, A + vec_off, Zh, wave, lane);
 }
 
 // Three bf16 parts of an fp32 value: hi = bf16(x), mid = bf16(x - hi), lo = bf16(x - hi - mid).
@@ -796,6 +1023,31 @@ static hipError_t launch_window_t(const StepArgs& a, const WindowArgs& w, hipStr
                          : launch_boundary_kernel<kPerKey, kMaxW, T>(a, w, stream);
     return w.W <= 16 ? launch_step_kernel<kPerKey, 16, T>(a, w, stream)
                      : launch_step_kernel<kPerKey, kMaxW, T>(a, w, stream);
+}
+
+template <typename T>
+static hipError_t launch_rwkv7_window_t(const StepArgs& a, const WindowArgs& w, const void* kappa,
+                                        const float* erase, hipStream_t stream) {
+    hipLaunchKernelGGL(rwkv7_q8_step_kernel<T>, dim3(a.heads), dim3(kThreads), sizeof(float) * 2 * w.pos * kD,
+                       stream, w.W, w.pos, w.Z, w.A, static_cast<T*>(w.Kbuf), w.Ubuf, w.Gbuf,
+                       static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v),
+                       static_cast<const T*>(kappa), a.gate, erase, a.y);
+    if (hipError_t e = hipGetLastError()) return e;
+    if (w.pos < w.W - 1) return hipSuccess;
+    const int floats = boundary_lds_floats(kRwkv7Rec, true);
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(q8_requant_kernel<T>),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                       static_cast<int>(sizeof(float) * floats));
+    if (attr != hipSuccess) return attr;
+    hipLaunchKernelGGL(q8_requant_kernel<T>, dim3(a.heads), dim3(kThreads), sizeof(float) * floats, stream,
+                       2 * w.W, 2 * w.W, w.Z, w.A, static_cast<const T*>(w.Kbuf), w.Ubuf, w.Gbuf);
+    return hipGetLastError();
+}
+
+hipError_t launch_rwkv7_q8_window(const StepArgs& a, const WindowArgs& w, const void* kappa, const float* erase,
+                                  bool bf16, hipStream_t stream) {
+    return bf16 ? launch_rwkv7_window_t<bf16_t>(a, w, kappa, erase, stream)
+                : launch_rwkv7_window_t<float>(a, w, kappa, erase, stream);
 }
 
 hipError_t launch_q8_window(const StepArgs& a, const WindowArgs& w, bool per_key, bool bf16,

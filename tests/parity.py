@@ -330,6 +330,14 @@ def run_lq(w: wl.Workload, n_iter: int = 1, n_iter0: int = 8, sample: int | None
 
 def new_window_buffers(w: wl.Workload):
     B, H, W = w.B, w.H, w.W
+    if w.variant == "rwkv7":   # two records per token, per-key gates
+        return {
+            "Z": torch.zeros(B, H, 128, 128, device=DEV, dtype=torch.int8),
+            "A": torch.zeros(B, H, 128, device=DEV),
+            "Kbuf": torch.zeros(B, H, 2 * W, 128, device=DEV, dtype=qkv_dtype(w)),
+            "Ubuf": torch.zeros(B, H, 2 * W, 128, device=DEV),
+            "Gbuf": torch.zeros(B, H, 2 * W, 128, device=DEV),
+        }
     return {
         "Z": torch.zeros(B, H, 128, 128, device=DEV, dtype=torch.int8),
         "A": torch.zeros(B, H, 128, device=DEV),
@@ -341,6 +349,10 @@ def new_window_buffers(w: wl.Workload):
 
 def window_step(w: wl.Workload, pos: int, buf, d, y):
     m = rsu()
+    if w.variant == "rwkv7":
+        m.rwkv7_q8_window(w.W, pos, buf["Z"], buf["A"], buf["Kbuf"], buf["Ubuf"], buf["Gbuf"], d["q"], d["k"],
+                          d["v"], d["kappa"], d["gate"], d["a"], y)
+        return
     fn = m.kda_q8_window if w.per_key_gate else m.gdn_q8_window
     fn(w.W, pos, buf["Z"], buf["A"], buf["Kbuf"], buf["Ubuf"], buf["Gbuf"], d["q"], d["k"], d["v"],
        d["gate"], d["beta"], y)
@@ -373,12 +385,16 @@ def run_window(w: wl.Workload, sample: int | None = None, steps: int | None = No
     for t in range(steps):
         pos = t % W
         if pos == 0:
-            ref = oracle.WindowState(take(buf["Z"], hd, (128, 128)), take(buf["A"], hd, (128,)),
-                                     W, w.per_key_gate)
+            Zs, As = take(buf["Z"], hd, (128, 128)), take(buf["A"], hd, (128,))
+            ref = oracle.Rwkv7WindowState(Zs, As, W) if w.variant == "rwkv7" else \
+                oracle.WindowState(Zs, As, W, w.per_key_gate)
         x, d = dev_inputs(w, t)
         window_step(w, pos, buf, d, y)
+        args = host_slice(x, heads)
+        if w.variant == "rwkv7":
+            args = args[:4] + (x["kappa"][heads], x["a"][heads])
         if pos == W - 1:
-            y_ref, _, wcode = ref.step(*host_slice(x, heads), want_boundary=True)
+            y_ref, _, wcode = ref.step(*args, want_boundary=True)
             Zg = take(buf["Z"], hd, (128, 128)).astype(np.int32)
             ag = take(buf["A"], hd, (128,)).astype(np.float64)
             aref = ref.a.astype(np.float64)
@@ -391,6 +407,6 @@ def run_window(w: wl.Workload, sample: int | None = None, steps: int | None = No
             st["z_flips_outside_band"] += int((flips & ~near_tie).sum())
             st["boundaries"] += 1
         else:
-            y_ref = ref.step(*host_slice(x, heads))
+            y_ref = ref.step(*args)
         st["y"] = max(st["y"], rel_err(take(y, hd, (128,)), y_ref))
     return st

@@ -79,6 +79,9 @@ WORKLOADS = {
     9: Workload(9, "kda_lq_window_b128_h32_w16", "kda", "lq_window", 128, 32, 256, "bf16", 0.80, 1.0,
                 W=16, outliers=True),
     10: Workload(10, "rwkv7_dense_b128_h32_bf16", "rwkv7", "dense", 128, 32, 32, "bf16", 0.80, 1.0),
+    # RWKV7 on the int8 window, two records per token (with the int8 workload's outliers)
+    11: Workload(11, "rwkv7_q8_window_b128_h32_w16", "rwkv7", "q8_window", 128, 32, 256, "bf16", 0.80, 1.0,
+                 W=16, outliers=True),
     7: Workload(7, "rwkv6_dense_b128_h32_bf16", "rwkv6", "dense", 128, 32, 32, "bf16", 0.80, 1.0),
     8: Workload(8, "rwkv6_log_b128_h32_m4", "rwkv6", "log", 128, 32, 128, "bf16", 0.80, 1.0, M=4),
 }
