@@ -25,6 +25,9 @@ Readings taken where the pages are silent (stated once here, used everywhere):
     against the rounded tokens, so the stored pieces add up to the reconstruction;
   * the smoothing floor is 1e-6 on c; c and B are stored in fp32;
   * codes round half to even and are clamped to [-127, 127]; B_j = 0 gives Z = 0.
+  * at 4 bits (the page uses r = 8 tokens there) the same recipe with codes in [-7, 7]
+    and dequant(Z, B)_ij = Z_ij B_j / 7 (the /127 convention at 4 bits); on the device two
+    codes share a byte, the even column in the low nibble.
 """
 from __future__ import annotations
 
@@ -32,6 +35,12 @@ import numpy as np
 
 R_TOKENS = 4
 C_FLOOR = 1e-6
+QMAX8, QMAX4 = 127, 7
+
+
+def qmax_of(bits: int) -> int:
+    """Largest code of the symmetric format: 127 at 8 bits, 7 at 4 bits."""
+    return (1 << (bits - 1)) - 1
 
 
 def walsh_start(d: int = 128, r: int = R_TOKENS) -> np.ndarray:
@@ -71,8 +80,9 @@ def to_fp16(x: np.ndarray) -> np.ndarray:
     return np.asarray(x, dtype=np.float64).astype(np.float16).astype(np.float64)
 
 
-def smooth_quantize(S: np.ndarray, K16: np.ndarray, U16: np.ndarray):
-    """Residual, smoothing and per-value-channel int8 (LeapQuant sec. 3.4, eq. 7).
+def smooth_quantize(S: np.ndarray, K16: np.ndarray, U16: np.ndarray, qmax: int = QMAX8):
+    """Residual, smoothing and per-value-channel int8 (LeapQuant sec. 3.4, eq. 7); qmax = 7
+    gives the 4-bit codes.
 
     Returns Z (int8), B (fp32 values in fp64), c (fp32 values in fp64) and w, the
     exact pre-rounding code values (for the tie band of parity checks)."""
@@ -83,27 +93,46 @@ def smooth_quantize(S: np.ndarray, K16: np.ndarray, U16: np.ndarray):
     B = np.max(np.abs(X), axis=0).astype(np.float32).astype(np.float64)
     w = np.zeros_like(X)
     nz = B > 0
-    w[:, nz] = X[:, nz] * 127.0 / B[nz][None, :]
-    Z = np.clip(np.rint(w), -127, 127).astype(np.int8)
+    w[:, nz] = X[:, nz] * float(qmax) / B[nz][None, :]
+    Z = np.clip(np.rint(w), -qmax, qmax).astype(np.int8)
     return Z, B, c, w
 
 
-def boundary(S: np.ndarray, V0: np.ndarray, n_iter: int) -> dict:
-    """The whole boundary: fit, fp16 tokens, residual, smoothing, payload."""
+def boundary(S: np.ndarray, V0: np.ndarray, n_iter: int, qmax: int = QMAX8) -> dict:
+    """The whole boundary: fit (r = the columns of V0), fp16 tokens, residual, smoothing,
+    payload."""
     K, U = fit(S, V0, n_iter)
     K16, U16 = to_fp16(K), to_fp16(U)
-    Z, B, c, w = smooth_quantize(S, K16, U16)
+    Z, B, c, w = smooth_quantize(S, K16, U16, qmax)
     return {"K": K, "U": U, "K16": K16, "U16": U16, "Z": Z, "B": B, "c": c, "w": w}
 
 
-def represent(Z, B, c, K16, U16) -> np.ndarray:
+def represent(Z, B, c, K16, U16, qmax: int = QMAX8) -> np.ndarray:
     """The state a window starts from: C dequant(Z, B) + Kt Ut^T (eq. 7 at l = 0)."""
     Zf = np.asarray(Z, dtype=np.float64)
-    return np.asarray(c, np.float64)[:, None] * (Zf * (np.asarray(B, np.float64) / 127.0)[None, :]) + \
+    return np.asarray(c, np.float64)[:, None] * (Zf * (np.asarray(B, np.float64) / float(qmax))[None, :]) + \
         np.asarray(K16, np.float64) @ np.asarray(U16, np.float64).T
 
 
-def bytes_per_element(d: int = 128, r: int = R_TOKENS) -> float:
-    """Stored bytes per state element at a boundary: int8 payload, fp32 B and c,
-    fp16 token pairs (LeapQuant sec. 4.3)."""
-    return (d * d * 1 + d * 4 + d * 4 + 2 * r * d * 2) / (d * d)
+def bytes_per_element(d: int = 128, r: int = R_TOKENS, bits: int = 8) -> float:
+    """Stored bytes per state element at a boundary: the payload, fp32 B and c, fp16
+    token pairs (LeapQuant sec. 4.3)."""
+    return (d * d * bits / 8 + d * 4 + d * 4 + 2 * r * d * 2) / (d * d)
+
+
+def pack_nibbles(Z: np.ndarray) -> np.ndarray:
+    """4-bit codes [..., d] in [-7, 7] -> bytes [..., d / 2]: column 2m in the low nibble,
+    2m + 1 in the high nibble, each a 4-bit two's complement."""
+    z = np.asarray(Z, dtype=np.int64) & 0xF
+    return (z[..., 0::2] | (z[..., 1::2] << 4)).astype(np.uint8)
+
+
+def unpack_nibbles(P: np.ndarray) -> np.ndarray:
+    """Inverse of pack_nibbles."""
+    p = np.asarray(P, dtype=np.int64)
+    lo, hi = p & 0xF, (p >> 4) & 0xF
+    lo = np.where(lo >= 8, lo - 16, lo)
+    hi = np.where(hi >= 8, hi - 16, hi)
+    out = np.empty(p.shape[:-1] + (2 * p.shape[-1],), dtype=np.int8)
+    out[..., 0::2], out[..., 1::2] = lo, hi
+    return out

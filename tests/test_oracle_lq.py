@@ -196,3 +196,103 @@ def test_boundary_bytes_per_element_match_the_page():
     bpe = lq.bytes_per_element(f["dk"], f["r"])
     assert round(bpe, 2) == f["bytes_per_element_printed"]
     assert round(f["fp32_bytes_per_element"] / bpe, 1) == f["reduction_printed"]
+
+
+# ---------------------------------------------------------------- 4 bits, r = 8 tokens
+# (LeapQuant sec. 4.1 uses r = 8 compensator tokens at 4 bits; codes in [-7, 7], /7)
+
+def _gapped8(d=128, noise=0.01, rng=RNG):
+    sig = np.array([12.0, 10.0, 9.0, 8.0, 6.0, 5.0, 4.0, 3.0])
+    A = np.linalg.qr(rng.standard_normal((d, d)))[0]
+    Bm = np.linalg.qr(rng.standard_normal((d, d)))[0]
+    return (A[:, :8] * sig) @ Bm[:, :8].T + noise * rng.standard_normal((d, d))
+
+
+def test_eight_token_fit_converges_to_the_truncated_svd():
+    S = _gapped8()
+    V0 = lq.walsh_start(r=8)
+    np.testing.assert_allclose(V0.T @ V0, np.eye(8), atol=1e-15)
+    K, U = lq.fit(S, V0, 80)
+    u, s, vt = np.linalg.svd(S)
+    np.testing.assert_allclose(K @ U.T, (u[:, :8] * s[:8]) @ vt[:8], atol=1e-9)
+    np.testing.assert_allclose(np.linalg.norm(S - K @ U.T), np.sqrt(np.sum(s[8:] ** 2)), rtol=1e-9)
+
+
+def test_4bit_representation_error_is_bounded_by_half_a_step():
+    S = _gapped8(noise=0.05)
+    out = lq.boundary(S, lq.walsh_start(r=8), 2, qmax=lq.QMAX4)
+    assert out["Z"].min() >= -7 and out["Z"].max() <= 7
+    S0 = lq.represent(out["Z"], out["B"], out["c"], out["K16"], out["U16"], qmax=lq.QMAX4)
+    step = out["c"][:, None] * out["B"][None, :] / 7.0
+    assert np.all(np.abs(S0 - S) <= 0.5 * step * (1 + 1e-6) + 1e-15)
+
+
+def test_4bit_without_tokens_is_a_per_column_int4_quantizer():
+    """r = 0: codes rne(X_ij * 7 / B_j) on the smoothed state, written out column by column."""
+    S = RNG.standard_normal((128, 128)) * 0.02
+    zero = np.zeros((128, 0))
+    Z, Bq, c, _ = lq.smooth_quantize(S, zero, zero, qmax=lq.QMAX4)
+    X = S / c[:, None]
+    for j in range(128):
+        B = float(np.float32(np.abs(X[:, j]).max()))
+        assert Bq[j] == B
+        for i in range(0, 128, 7):
+            x = X[i, j] * 7.0 / B
+            f = np.floor(x)
+            r = f + 1 if (x - f > 0.5 or (x - f == 0.5 and f % 2 == 1)) else f
+            assert Z[i, j] == max(-7, min(7, int(r)))
+
+
+def test_4bit_ties_round_to_even():
+    """c = 1 by construction (row mean |R| = 1); column 0 on the half grid with absmax 7."""
+    S = np.zeros((128, 128))
+    t = np.concatenate([[7.0], ((np.arange(127) % 15) - 7) + 0.5])
+    t[t > 7] = 6.5
+    S[:, 0] = t
+    S[:, 1] = 128.0 - np.abs(t)
+    zero = np.zeros((128, 0))
+    Z, B, c, w = lq.smooth_quantize(S, zero, zero, qmax=lq.QMAX4)
+    np.testing.assert_array_equal(c, 1.0)
+    assert B[0] == 7.0
+    np.testing.assert_array_equal(w[:, 0], t)
+    halves = t[1:]
+    even = np.where(np.floor(halves) % 2 == 0, np.floor(halves), np.ceil(halves))
+    np.testing.assert_array_equal(Z[1:, 0], even.astype(np.int8))
+
+
+def test_nibble_packing_layout_and_round_trip():
+    Z = np.array([[-7, 7, -1, 0, 3, -3, 1, -8 + 1]], dtype=np.int8)
+    P = lq.pack_nibbles(Z)
+    # column 0 in the low nibble, column 1 in the high nibble, two's complement
+    np.testing.assert_array_equal(P[0], [0x79, 0x0F, 0xD3, 0x9 << 4 | 0x1])
+    np.testing.assert_array_equal(lq.unpack_nibbles(P), Z)
+    R = RNG.integers(-7, 8, size=(5, 128)).astype(np.int8)
+    np.testing.assert_array_equal(lq.unpack_nibbles(lq.pack_nibbles(R)), R)
+
+
+def test_eq10_readout_at_4_bits_with_8_tokens_equals_dense_decoding():
+    d, W = 128, 4
+    S = _gapped8(noise=0.05)
+    rep = lq.boundary(S, lq.walsh_start(r=8), 1, qmax=lq.QMAX4)
+    S0 = lq.represent(rep["Z"], rep["B"], rep["c"], rep["K16"], rep["U16"], qmax=lq.QMAX4)
+    Sd = S0[None].copy()
+    recs = []
+    for _ in range(W):
+        q = RNG.standard_normal((1, d))
+        k = RNG.standard_normal((1, d))
+        k /= np.linalg.norm(k)
+        v = RNG.standard_normal((1, d))
+        g = np.array([RNG.uniform(0.9, 0.999)])
+        b = np.array([RNG.uniform(0.0, 1.0)])
+        y_dense = oracle.dense_step(Sd, q, k, v, g, b)[0]
+        gam_all = np.prod([r[2] for r in recs]) * g[0]
+
+        def read(x):
+            out = (rep["B"] / 7.0) * (rep["Z"].astype(np.float64).T @ (rep["c"] * gam_all * x))
+            out += rep["U16"] @ (rep["K16"].T @ (gam_all * x))
+            for j, (kj, uj, _) in enumerate(recs):
+                out += uj * (kj @ (np.prod([r[2] for r in recs[j + 1:]]) * g[0] * x))
+            return out
+        u = b[0] * (v[0] - read(k[0]))
+        np.testing.assert_allclose(read(q[0]) + u * (k[0] @ q[0]), y_dense, rtol=0, atol=1e-11)
+        recs.append((k[0], u, g[0]))
