@@ -33,39 +33,43 @@ __device__ __forceinline__ f32x4 unpack_codes(uint32_t w) {
                  static_cast<float>(static_cast<int8_t>(w >> 24))};
 }
 
-// Code byte of w = x * (127 / B): round half to even with one fp32 add (the low mantissa
-// bits of w + 1.5 * 2^23 are the integer), then clamp the bits to the codes -127 .. 127.
-__device__ __forceinline__ uint32_t lq_code(float w) {
-    constexpr float kMagic = 12582912.0f;
-    const int bits = __float_as_int(w + kMagic);
-    return static_cast<uint32_t>(min(max(bits, 0x4B400000 - 127), 0x4B400000 + 127)) & 0xffu;
-}
 
 // ---------------------------------------------------------------- the refit
 // The refit holds the state in registers: lane l of wave w owns the 4 columns of unit
 // uu = 8 w + (l & 7) (columns 4 uu .. 4 uu + 3) in the 16 rows 8 it + (l >> 3). Products
 // with V sum over the 8 column lanes of a row (DPP) and then over the 4 waves (LDS);
 // products with S^T and the per-column absmax sum over the 8 row lanes of a column
-// group inside the wave.
+// group inside the wave. kT tokens (4 at 8 bits, 8 at 4 bits) are kT / 4 f32x4 per row
+// or column of V, Y, W, Kr and Ur (token t of entry i in element t % 4 of chunk t / 4).
 //
-// LDS of the refit, in floats. A region of kRefitRegionFloats holds the staged codes
-// (128 rows of kCodeStride words) and V, Y, Kr, Ur [128] x f32x4 (token t of row or
-// column i in element t of entry i), the per-wave partials Yp [4][128] x f32x4 (also the
-// per-wave row sums of |R|) and the row factors 1 / c [128]. W [128] x f32x4, the start
-// vectors and the S^T Y products, lies outside the region: the boundary writes it
+// LDS of the refit, in floats. A region of kRegionFloats holds the staged codes (128 rows
+// of kCodeStride words) and V, Y, Kr, Ur [128 x kT], the per-wave partials Yp [4][128 x kT]
+// (also the per-wave row sums of |R|) and the row factors 1 / c [128]. W [128 x kT], the
+// start vectors and the S^T Y products, lies outside the region: the boundary writes it
 // before its state region (which the refit region reuses) is free.
-constexpr int kCodeStride = 40;  // 16-byte rows; rows 8 apart in banks
-constexpr int kRefitRegionFloats = kD * kCodeStride + 4 * 4 * kD + 4 * 4 * kD + kD;
-constexpr int kRefitQuantizeFloats = kRefitRegionFloats + 4 * kD;
+template <int kT, int kBits>
+struct RefitCfg {
+    static_assert((kT == 4 || kT == 8) && (kBits == 8 || kBits == 4), "4 or 8 tokens, 8- or 4-bit codes");
+    static constexpr int kC = kT / 4;                        // f32x4 chunks of a token vector
+    static constexpr int kQmax = kBits == 8 ? 127 : 7;       // largest code
+    static constexpr int kRowWords = kD * kBits / 32;        // 32 (8-bit) or 16 (4-bit) words per row
+    static constexpr int kCodeStride = kBits == 8 ? 40 : 20; // staged row stride: 16-byte rows, 8 rows span the banks
+    static constexpr int kRegionFloats = kD * kCodeStride + 4 * kT * kD + 4 * kT * kD + kD;
+    static constexpr int kWFloats = kT * kD;
+};
 
+template <int kT, int kBits>
 struct RefitLds {
+    using Cfg = RefitCfg<kT, kBits>;
+    static constexpr int kC = Cfg::kC;
     uint32_t* codes;
     f32x4 *V, *Y, *Kr, *Ur, *Yp, *W;
     float* ic;
     __device__ RefitLds(float* region, float* w_area)
         : codes(reinterpret_cast<uint32_t*>(region)),
-          V(reinterpret_cast<f32x4*>(region + kD * kCodeStride)), Y(V + kD), Kr(Y + kD), Ur(Kr + kD),
-          Yp(Ur + kD), W(reinterpret_cast<f32x4*>(w_area)), ic(reinterpret_cast<float*>(Yp + 4 * kD)) {}
+          V(reinterpret_cast<f32x4*>(region + kD * Cfg::kCodeStride)), Y(V + kD * kC), Kr(Y + kD * kC),
+          Ur(Kr + kD * kC), Yp(Ur + kD * kC), W(reinterpret_cast<f32x4*>(w_area)),
+          ic(reinterpret_cast<float*>(Yp + 4 * kD * kC)) {}
     __device__ float* Ap() const { return reinterpret_cast<float*>(Yp); }
 };
 
@@ -96,13 +100,35 @@ __device__ __forceinline__ float max_row_lanes(float x) {
     return fmaxf(a, b);
 }
 
-// W -> V: modified Gram-Schmidt over the 4 columns in order (wave 0; lane l holds rows
+// Code of w = x * (qmax / B): round half to even with one fp32 add (the low mantissa bits
+// of w + 1.5 * 2^23 are the integer), clamped to [-qmax, qmax], as a byte (8-bit) or as a
+// two's complement nibble (4-bit).
+template <int kBits>
+__device__ __forceinline__ uint32_t lq_code_t(float w) {
+    constexpr float kMagic = 12582912.0f;
+    constexpr int kQ = kBits == 8 ? 127 : 7;
+    const int bits = __float_as_int(w + kMagic);
+    return static_cast<uint32_t>(min(max(bits, 0x4B400000 - kQ), 0x4B400000 + kQ)) & (kBits == 8 ? 0xffu : 0xfu);
+}
+
+// W -> V: modified Gram-Schmidt over the kT columns in order (wave 0; lane l holds rows
 // 2l and 2l + 1); a column with zero norm after the projections stays zero.
-__device__ __forceinline__ void refit_mgs(const RefitLds& L, int wave, int lane) {
+template <int kT, int kBits>
+__device__ __forceinline__ void refit_mgs(const RefitLds<kT, kBits>& L, int wave, int lane) {
+    constexpr int kC = kT / 4;
     if (wave == 0) {
-        f32x4 a = L.W[2 * lane], b = L.W[2 * lane + 1];
+        float a[kT], b[kT];
 #pragma unroll
-        for (int t = 0; t < kTok; ++t) {
+        for (int h = 0; h < kC; ++h) {
+            const f32x4 wa = L.W[(2 * lane) * kC + h], wb = L.W[(2 * lane + 1) * kC + h];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                a[4 * h + e] = wa[e];
+                b[4 * h + e] = wb[e];
+            }
+        }
+#pragma unroll
+        for (int t = 0; t < kT; ++t) {
 #pragma unroll
             for (int g = 0; g < t; ++g) {
                 const float d = wave_sum(a[g] * a[t] + b[g] * b[t]);
@@ -114,52 +140,96 @@ __device__ __forceinline__ void refit_mgs(const RefitLds& L, int wave, int lane)
             a[t] *= inv;
             b[t] *= inv;
         }
-        L.V[2 * lane] = a;
-        L.V[2 * lane + 1] = b;
+#pragma unroll
+        for (int h = 0; h < kC; ++h) {
+            L.V[(2 * lane) * kC + h] = f32x4{a[4 * h], a[4 * h + 1], a[4 * h + 2], a[4 * h + 3]};
+            L.V[(2 * lane + 1) * kC + h] = f32x4{b[4 * h], b[4 * h + 1], b[4 * h + 2], b[4 * h + 3]};
+        }
     }
     __syncthreads();
 }
 
 // Y = S V
-__device__ __forceinline__ void refit_sv(const RefitLds& L, const f32x4 (&s)[16], int wave, int lane, int tid) {
+template <int kT, int kBits>
+__device__ __forceinline__ void refit_sv(const RefitLds<kT, kBits>& L, const f32x4 (&s)[16], int wave, int lane,
+                                         int tid) {
+    constexpr int kC = kT / 4;
     const int uu = 8 * wave + (lane & 7), ro = lane >> 3;
-    const f32x4 v0 = L.V[4 * uu], v1 = L.V[4 * uu + 1], v2 = L.V[4 * uu + 2], v3 = L.V[4 * uu + 3];
+    f32x4 vc[4][kC];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int h = 0; h < kC; ++h) vc[e][h] = L.V[(4 * uu + e) * kC + h];
 #pragma unroll
     for (int it = 0; it < 16; ++it) {
-        const f32x4 p = sum_col_lanes(axpy(s[it].w, v3, axpy(s[it].z, v2, axpy(s[it].y, v1, s[it].x * v0))));
-        if ((lane & 7) == 0) L.Yp[wave * kD + 8 * it + ro] = p;
+#pragma unroll
+        for (int h = 0; h < kC; ++h) {
+            const f32x4 p = sum_col_lanes(axpy(s[it].w, vc[3][h], axpy(s[it].z, vc[2][h],
+                                                 axpy(s[it].y, vc[1][h], s[it].x * vc[0][h]))));
+            if ((lane & 7) == 0) L.Yp[(wave * kD + 8 * it + ro) * kC + h] = p;
+        }
     }
     __syncthreads();
-    if (tid < kD) L.Y[tid] = (L.Yp[tid] + L.Yp[kD + tid]) + (L.Yp[2 * kD + tid] + L.Yp[3 * kD + tid]);
+    if (tid < kD)
+#pragma unroll
+        for (int h = 0; h < kC; ++h)
+            L.Y[tid * kC + h] = (L.Yp[tid * kC + h] + L.Yp[(kD + tid) * kC + h]) +
+                                (L.Yp[(2 * kD + tid) * kC + h] + L.Yp[(3 * kD + tid) * kC + h]);
     __syncthreads();
 }
 
 // W = S^T Y
-__device__ __forceinline__ void refit_sty(const RefitLds& L, const f32x4 (&s)[16], int wave, int lane) {
+template <int kT, int kBits>
+__device__ __forceinline__ void refit_sty(const RefitLds<kT, kBits>& L, const f32x4 (&s)[16], int wave, int lane) {
+    constexpr int kC = kT / 4;
     const int uu = 8 * wave + (lane & 7), ro = lane >> 3;
-    f32x4 acc[4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    f32x4 acc[4][kC];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int h = 0; h < kC; ++h) acc[e][h] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int it = 0; it < 16; ++it) {
-        const f32x4 yv = L.Y[8 * it + ro];
-        acc[0] = axpy(s[it].x, yv, acc[0]);
-        acc[1] = axpy(s[it].y, yv, acc[1]);
-        acc[2] = axpy(s[it].z, yv, acc[2]);
-        acc[3] = axpy(s[it].w, yv, acc[3]);
+#pragma unroll
+        for (int h = 0; h < kC; ++h) {
+            const f32x4 yv = L.Y[(8 * it + ro) * kC + h];
+            acc[0][h] = axpy(s[it].x, yv, acc[0][h]);
+            acc[1][h] = axpy(s[it].y, yv, acc[1][h]);
+            acc[2][h] = axpy(s[it].z, yv, acc[2][h]);
+            acc[3][h] = axpy(s[it].w, yv, acc[3][h]);
+        }
     }
 #pragma unroll
-    for (int e = 0; e < 4; ++e) acc[e] = sum_row_lanes(acc[e]);
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int h = 0; h < kC; ++h) acc[e][h] = sum_row_lanes(acc[e][h]);
     if (ro == 0)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) L.W[4 * uu + e] = acc[e];
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+            for (int h = 0; h < kC; ++h) L.W[(4 * uu + e) * kC + h] = acc[e][h];
     __syncthreads();
 }
 
+// k . u over the kT tokens of one row (k) and one column (u)
+template <int kC>
+__device__ __forceinline__ float tok_dot(const f32x4 (&k)[kC], const f32x4 (&u)[kC]) {
+    float d = k[0].x * u[0].x + k[0].y * u[0].y + k[0].z * u[0].z + k[0].w * u[0].w;
+#pragma unroll
+    for (int h = 1; h < kC; ++h) d += k[h].x * u[h].x + k[h].y * u[h].y + k[h].z * u[h].z + k[h].w * u[h].w;
+    return d;
+}
+
 // The refit of one head. On entry s holds the lane's part of the state and W the start
-// vectors; every thread of the workgroup calls it. Writes Z, B, c and the fp16 tokens.
-__device__ __forceinline__ void lq_refit(const RefitLds& L, f32x4 (&s)[16], int n_iter, int tid,
+// vectors; every thread of the workgroup calls it. Writes the codes (Zh: the head's
+// payload as 32-bit words), B, c and the fp16 tokens [kT][128].
+template <int kT, int kBits>
+__device__ __forceinline__ void lq_refit(const RefitLds<kT, kBits>& L, f32x4 (&s)[16], int n_iter, int tid,
                                          uint32_t* __restrict__ Zh, float* __restrict__ Bh,
                                          float* __restrict__ Ch, half_t* __restrict__ Kh,
                                          half_t* __restrict__ Uh) {
+    using Cfg = RefitCfg<kT, kBits>;
+    constexpr int kC = Cfg::kC;
     const int wave = tid >> 6, lane = tid & 63;
     const int uu = 8 * wave + (lane & 7), ro = lane >> 3;
     refit_mgs(L, wave, lane);
@@ -172,33 +242,45 @@ __device__ __forceinline__ void lq_refit(const RefitLds& L, f32x4 (&s)[16], int 
 
     // fp16 tokens (stored), and their exact fp32 values for the residual
     if (tid < kD) {
-        const f32x4 kv = L.Y[tid], uv = L.V[tid];
-        f32x4 kr, ur;
 #pragma unroll
-        for (int t = 0; t < kTok; ++t) {
-            const half_t kh = static_cast<half_t>(kv[t]);
-            const half_t uh = static_cast<half_t>(uv[t]);
-            kr[t] = static_cast<float>(kh);
-            ur[t] = static_cast<float>(uh);
-            Kh[t * kD + tid] = kh;
-            Uh[t * kD + tid] = uh;
+        for (int h = 0; h < kC; ++h) {
+            const f32x4 kv = L.Y[tid * kC + h], uv = L.V[tid * kC + h];
+            f32x4 kr, ur;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const half_t kh = static_cast<half_t>(kv[e]);
+                const half_t uh = static_cast<half_t>(uv[e]);
+                kr[e] = static_cast<float>(kh);
+                ur[e] = static_cast<float>(uh);
+                Kh[(4 * h + e) * kD + tid] = kh;
+                Uh[(4 * h + e) * kD + tid] = uh;
+            }
+            L.Kr[tid * kC + h] = kr;
+            L.Ur[tid * kC + h] = ur;
         }
-        L.Kr[tid] = kr;
-        L.Ur[tid] = ur;
     }
     __syncthreads();
 
     // residual R = S - Kt Ut^T in registers, and each row's sum of |R|
     {
-        const f32x4 u0 = L.Ur[4 * uu], u1 = L.Ur[4 * uu + 1], u2 = L.Ur[4 * uu + 2], u3 = L.Ur[4 * uu + 3];
+        f32x4 u0[kC], u1[kC], u2[kC], u3[kC];
+#pragma unroll
+        for (int h = 0; h < kC; ++h) {
+            u0[h] = L.Ur[(4 * uu) * kC + h];
+            u1[h] = L.Ur[(4 * uu + 1) * kC + h];
+            u2[h] = L.Ur[(4 * uu + 2) * kC + h];
+            u3[h] = L.Ur[(4 * uu + 3) * kC + h];
+        }
         float* Ap = L.Ap();
 #pragma unroll
         for (int it = 0; it < 16; ++it) {
-            const f32x4 kr = L.Kr[8 * it + ro];
-            s[it].x -= kr.x * u0.x + kr.y * u0.y + kr.z * u0.z + kr.w * u0.w;
-            s[it].y -= kr.x * u1.x + kr.y * u1.y + kr.z * u1.z + kr.w * u1.w;
-            s[it].z -= kr.x * u2.x + kr.y * u2.y + kr.z * u2.z + kr.w * u2.w;
-            s[it].w -= kr.x * u3.x + kr.y * u3.y + kr.z * u3.z + kr.w * u3.w;
+            f32x4 kr[kC];
+#pragma unroll
+            for (int h = 0; h < kC; ++h) kr[h] = L.Kr[(8 * it + ro) * kC + h];
+            s[it].x -= tok_dot<kC>(kr, u0);
+            s[it].y -= tok_dot<kC>(kr, u1);
+            s[it].z -= tok_dot<kC>(kr, u2);
+            s[it].w -= tok_dot<kC>(kr, u3);
             const float a = sum_col_lanes((fabsf(s[it].x) + fabsf(s[it].y)) + (fabsf(s[it].z) + fabsf(s[it].w)));
             if ((lane & 7) == 0) Ap[wave * kD + 8 * it + ro] = a;
         }
@@ -212,7 +294,7 @@ __device__ __forceinline__ void lq_refit(const RefitLds& L, f32x4 (&s)[16], int 
         __syncthreads();
     }
 
-    // X = R / c, the per-value-channel absmax B and the code scale 127 / B
+    // X = R / c, the per-value-channel absmax B and the code scale qmax / B
     f32x4 m = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int it = 0; it < 16; ++it) {
@@ -223,32 +305,44 @@ __device__ __forceinline__ void lq_refit(const RefitLds& L, f32x4 (&s)[16], int 
     m = f32x4{max_row_lanes(m.x), max_row_lanes(m.y), max_row_lanes(m.z), max_row_lanes(m.w)};
     f32x4 sc;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) sc[e] = m[e] > 0.f ? __fdiv_rn(127.f, m[e]) : 0.f;
+    for (int e = 0; e < 4; ++e) sc[e] = m[e] > 0.f ? __fdiv_rn(static_cast<float>(Cfg::kQmax), m[e]) : 0.f;
     if (ro == 0) *reinterpret_cast<f32x4*>(Bh + 4 * uu) = m;
 
-    // codes: one word per row and unit, staged so that whole rows leave together
+    // codes of the lane's unit in each of its rows, staged so that whole rows leave together
+    if constexpr (kBits == 8) {
 #pragma unroll
-    for (int it = 0; it < 16; ++it)
-        L.codes[(8 * it + ro) * kCodeStride + uu] = lq_code(s[it].x * sc.x) | (lq_code(s[it].y * sc.y) << 8) |
-                                                    (lq_code(s[it].z * sc.z) << 16) |
-                                                    (lq_code(s[it].w * sc.w) << 24);
+        for (int it = 0; it < 16; ++it)
+            L.codes[(8 * it + ro) * Cfg::kCodeStride + uu] =
+                lq_code_t<8>(s[it].x * sc.x) | (lq_code_t<8>(s[it].y * sc.y) << 8) |
+                (lq_code_t<8>(s[it].z * sc.z) << 16) | (lq_code_t<8>(s[it].w * sc.w) << 24);
+    } else {  // four nibbles: half of the row's word for columns 8 (uu / 2) .. +7
+        uint16_t* c16 = reinterpret_cast<uint16_t*>(L.codes);
+#pragma unroll
+        for (int it = 0; it < 16; ++it)
+            c16[(8 * it + ro) * 2 * Cfg::kCodeStride + uu] = static_cast<uint16_t>(
+                lq_code_t<4>(s[it].x * sc.x) | (lq_code_t<4>(s[it].y * sc.y) << 4) |
+                (lq_code_t<4>(s[it].z * sc.z) << 8) | (lq_code_t<4>(s[it].w * sc.w) << 12));
+    }
     __syncthreads();
+    constexpr int kQuads = Cfg::kRowWords / 4;  // 16-byte pieces per row
 #pragma unroll
-    for (int mm = 0; mm < 4; ++mm) {
+    for (int mm = 0; mm < kD * kQuads / kThreads; ++mm) {
         const int qd = tid + kThreads * mm;
-        const int row = qd >> 3, d = 4 * (qd & 7);  // words d .. d+3 of the row's 32
-        const u32x4 w4 = *reinterpret_cast<const u32x4*>(L.codes + row * kCodeStride + d);
-        __builtin_nontemporal_store(w4, reinterpret_cast<u32x4*>(Zh + row * (kD / 4) + d));
+        const int row = qd / kQuads, d = 4 * (qd % kQuads);
+        const u32x4 w4 = *reinterpret_cast<const u32x4*>(L.codes + row * Cfg::kCodeStride + d);
+        __builtin_nontemporal_store(w4, reinterpret_cast<u32x4*>(Zh + row * Cfg::kRowWords + d));
     }
 }
 
 // ---------------------------------------------------------------- conversion of a plain state
+template <int kT, int kBits>
 __global__ __launch_bounds__(kThreads) void lq_quantize_kernel(const float* __restrict__ S, int n_iter,
-                                                               int8_t* __restrict__ Z, float* __restrict__ B,
+                                                               uint32_t* __restrict__ Z, float* __restrict__ B,
                                                                float* __restrict__ Cs, half_t* __restrict__ Kc,
                                                                half_t* __restrict__ Uc) {
+    using Cfg = RefitCfg<kT, kBits>;
     extern __shared__ __align__(16) float lds[];
-    const RefitLds L(lds, lds + kRefitRegionFloats);
+    const RefitLds<kT, kBits> L(lds, lds + Cfg::kRegionFloats);
     const int h = head_of_block(blockIdx.x, gridDim.x), tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
     const int uu = 8 * wave + (lane & 7), ro = lane >> 3;
@@ -256,17 +350,20 @@ __global__ __launch_bounds__(kThreads) void lq_quantize_kernel(const float* __re
     f32x4 s[16];
 #pragma unroll
     for (int it = 0; it < 16; ++it) s[it] = stream_load(Sh + (8 * it + ro) * kD + 4 * uu);
-    if (tid < kD) {  // the first 4 Walsh columns: (-1)^popcount(i & t) / sqrt(128)
+    if (tid < kD) {  // the first kT Walsh columns: (-1)^popcount(i & t) / sqrt(128)
         constexpr float sq = 0.08838834764831845f;
-        f32x4 w;
 #pragma unroll
-        for (int t = 0; t < kTok; ++t) w[t] = (__builtin_popcount(tid & t) & 1) ? -sq : sq;
-        L.W[tid] = w;
+        for (int hh = 0; hh < Cfg::kC; ++hh) {
+            f32x4 w;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) w[e] = (__builtin_popcount(tid & (4 * hh + e)) & 1) ? -sq : sq;
+            L.W[tid * Cfg::kC + hh] = w;
+        }
     }
     __syncthreads();
     const size_t vo = static_cast<size_t>(h) * kD;
-    lq_refit(L, s, n_iter, tid, reinterpret_cast<uint32_t*>(Z + vo * kD), B + vo, Cs + vo,
-             Kc + vo * kTok, Uc + vo * kTok);
+    lq_refit(L, s, n_iter, tid, Z + static_cast<size_t>(h) * kD * Cfg::kRowWords, B + vo, Cs + vo,
+             Kc + vo * kT, Uc + vo * kT);
 }
 
 // ---------------------------------------------------------------- in-window step
@@ -478,7 +575,7 @@ constexpr int kZsStride = kD / 4 + 1;
 constexpr int kStepFloats = 2 * kD * 4 + 3 * 2 * kD * 4 + kD * kZsStride + 2 * kTok * kD + 4 * kD * 2 + kD * 2;
 constexpr int kLqBoundaryFloats = kD * kD + 4 * kD + kD;
 static_assert(kStepFloats <= kD * kD, "the step-phase arrays must lie inside the shared region");
-static_assert(kRefitRegionFloats <= kD * kD, "the refit's arrays must lie inside the shared region");
+static_assert(RefitCfg<4, 8>::kRegionFloats <= kD * kD, "the refit's arrays must lie inside the shared region");
 
 // The state in transit: row r in 16-byte units, unit u stored at u ^ f(r) with
 // f(r) = (r & 7) ^ ((r & 1) << 3), so that the MFMA-layout writes and the refit-layout
@@ -524,7 +621,7 @@ __global__ __launch_bounds__(kThreads) void lq_boundary_kernel(
     f32x2* red = reinterpret_cast<f32x2*>(Utok + kTok * kD);       // [4][128]
     f32x2* recp = red + 4 * kD;                                     // [128]
     // refit views (its region overlaps every step-phase array above; W and bscs do not)
-    const RefitLds L(dyn_lds, dyn_lds + kD * kD);
+    const RefitLds<4, 8> L(dyn_lds, dyn_lds + kD * kD);
     float* bscs = dyn_lds + kD * kD + 4 * kD;   // B / 127 of the old payload
 
     const int h = head_of_block(blockIdx.x, gridDim.x), tid = threadIdx.x;
@@ -771,7 +868,7 @@ __global__ __launch_bounds__(kThreads) void lq_boundary_kda_kernel(
     float* Kt4 = reinterpret_cast<float*>(Zs + kD * kZsStride);    // [4][128] Gamma_{1:W} Kt
     float* Ut4 = Kt4 + kTok * kD;                                   // [4][128] Ut
     f32x2* red = reinterpret_cast<f32x2*>(Ut4 + kTok * kD);        // [4][128]
-    const RefitLds L(dyn_lds, dyn_lds + kD * kD);
+    const RefitLds<4, 8> L(dyn_lds, dyn_lds + kD * kD);
     float* bscs = dyn_lds + kD * kD + 4 * kD;                       // B / 127 of the old payload
 
     const int h = head_of_block(blockIdx.x, gridDim.x), tid = threadIdx.x;
@@ -978,10 +1075,13 @@ static hipError_t set_lds(const void* fn, int floats) {
 
 hipError_t launch_lq_quantize(int heads, const float* S, int n_iter, int8_t* Z, float* B, float* C,
                               void* Kc, void* Uc, hipStream_t stream) {
-    static const hipError_t attr = set_lds(reinterpret_cast<const void*>(lq_quantize_kernel), kRefitQuantizeFloats);
+    using Cfg = RefitCfg<4, 8>;
+    constexpr int floats = Cfg::kRegionFloats + Cfg::kWFloats;
+    static const hipError_t attr = set_lds(reinterpret_cast<const void*>(lq_quantize_kernel<4, 8>), floats);
     if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL(lq_quantize_kernel, dim3(heads), dim3(kThreads), sizeof(float) * kRefitQuantizeFloats, stream,
-                       S, n_iter, Z, B, C, static_cast<half_t*>(Kc), static_cast<half_t*>(Uc));
+    hipLaunchKernelGGL((lq_quantize_kernel<4, 8>), dim3(heads), dim3(kThreads), sizeof(float) * floats, stream,
+                       S, n_iter, reinterpret_cast<uint32_t*>(Z), B, C, static_cast<half_t*>(Kc),
+                       static_cast<half_t*>(Uc));
     return hipGetLastError();
 }
 
