@@ -193,6 +193,18 @@ int gdn_lq_window(const rsu_dims *dims, int W, int pos, int n_iter, int8_t *Z,
                   float *col_absmax, float *row_smooth, void *Kc, void *Uc, void *Kbuf,
                   float *Ubuf, float *Gbuf, const void *q, const void *k, const void *v,
                   const float *alpha, const float *beta, float *y, rsu_stream_t stream);
+/* The same format at 4 bits with r = 8 tokens (LeapQuant sec. 4.1 fits 8 tokens at
+ * 4 bits), GDN: codes in [-7, 7] with dequant Z_ij * col_absmax_j / 7, two per byte
+ * (column 2m in the low nibble, 2m + 1 in the high nibble, two's complement):
+ *   Z [B,H,d_k,d_v/2] bytes, Kc, Uc [B,H,8,d] fp16; col_absmax, row_smooth as above.
+ * The fit starts from the first 8 Walsh columns; other rules as for gdn_lq_window. */
+int gdn_lq4_quantize(const rsu_dims *dims, const float *S, int n_iter, void *Z,
+                     float *col_absmax, float *row_smooth, void *Kc, void *Uc,
+                     rsu_stream_t stream);
+int gdn_lq4_window(const rsu_dims *dims, int W, int pos, int n_iter, void *Z,
+                   float *col_absmax, float *row_smooth, void *Kc, void *Uc, void *Kbuf,
+                   float *Ubuf, float *Gbuf, const void *q, const void *k, const void *v,
+                   const float *alpha, const float *beta, float *y, rsu_stream_t stream);
 int kda_lq_quantize(const rsu_dims *dims, const float *S, int n_iter, int8_t *Z,
                     float *col_absmax, float *row_smooth, void *Kc, void *Uc,
                     rsu_stream_t stream);

@@ -60,6 +60,8 @@ _SIGS = {
     "gdn_lq_quantize": [_DP, _P, _I, _P, _P, _P, _P, _P, _P],
     "gdn_lq_window": [_DP, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
     "kda_lq_quantize": [_DP, _P, _I, _P, _P, _P, _P, _P, _P],
+    "gdn_lq4_quantize": [_DP, _P, _I, _P, _P, _P, _P, _P, _P],
+    "gdn_lq4_window": [_DP, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
     "kda_lq_window": [_DP, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
     "gdn_log_step_slots": [_DP, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
     "kda_log_step_slots": [_DP, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
@@ -335,20 +337,24 @@ def rwkv6_log_step_slots(C, L, Sbase, lbar, Klog, Ulog, Lam, q, k, v, w, y):
     return _rwkv6_log("rwkv6_log_step_slots", C, L, Sbase, lbar, Klog, Ulog, Lam, q, k, v, w, y)
 
 
-def _lq_state(B, H, Z, col_absmax, row_smooth, Kc, Uc):
-    _need(Z, "Z", torch.int8, (B, H, D, D))
+def _lq_state(B, H, Z, col_absmax, row_smooth, Kc, Uc, four_bit=False):
+    if four_bit:
+        _need(Z, "Z", torch.uint8, (B, H, D, D // 2))
+    else:
+        _need(Z, "Z", torch.int8, (B, H, D, D))
     _need(col_absmax, "col_absmax", torch.float32, (B, H, D))
     _need(row_smooth, "row_smooth", torch.float32, (B, H, D))
-    _need(Kc, "Kc", torch.float16, (B, H, 4, D))
-    _need(Uc, "Uc", torch.float16, (B, H, 4, D))
+    r = 8 if four_bit else 4
+    _need(Kc, "Kc", torch.float16, (B, H, r, D))
+    _need(Uc, "Uc", torch.float16, (B, H, r, D))
 
 
-def _lq_quantize(name, S, n_iter, Z, col_absmax, row_smooth, Kc, Uc):
+def _lq_quantize(name, S, n_iter, Z, col_absmax, row_smooth, Kc, Uc, four_bit=False):
     if S.dim() != 4:
         raise ValueError("S must be [B, H, 128, 128]")
     B, H = S.shape[0], S.shape[1]
     _need(S, "S", torch.float32, (B, H, D, D))
-    _lq_state(B, H, Z, col_absmax, row_smooth, Kc, Uc)
+    _lq_state(B, H, Z, col_absmax, row_smooth, Kc, Uc, four_bit)
     dims = _Dims(B, H, D, D, RSU_F32)
     _call(name, ctypes.byref(dims), _ptr(S), int(n_iter), _ptr(Z), _ptr(col_absmax),
           _ptr(row_smooth), _ptr(Kc), _ptr(Uc), _stream())
@@ -366,10 +372,10 @@ def kda_lq_quantize(S, n_iter, Z, col_absmax, row_smooth, Kc, Uc):
 
 
 def _lq_window(name, per_key, W, pos, n_iter, Z, col_absmax, row_smooth, Kc, Uc, Kbuf, Ubuf, Gbuf, q, k, v,
-               gate, beta, y):
+               gate, beta, y, four_bit=False):
     dims = _dims(q, k, v)
     B, H = dims.B, dims.H
-    _lq_state(B, H, Z, col_absmax, row_smooth, Kc, Uc)
+    _lq_state(B, H, Z, col_absmax, row_smooth, Kc, Uc, four_bit)
     _need(Kbuf, "Kbuf", q.dtype, (B, H, W, D))
     _need(Ubuf, "Ubuf", torch.float32, (B, H, W, D))
     _need(Gbuf, "Gbuf", torch.float32, (B, H, W, D) if per_key else (B, H, W))
@@ -385,6 +391,18 @@ def gdn_lq_window(W, pos, n_iter, Z, col_absmax, row_smooth, Kc, Uc, Kbuf, Ubuf,
     """One decode step in LeapQuant's format (eq. 10 readout; at pos = W - 1 the refit)."""
     return _lq_window("gdn_lq_window", False, W, pos, n_iter, Z, col_absmax, row_smooth, Kc, Uc, Kbuf, Ubuf,
                       Gbuf, q, k, v, alpha, beta, y)
+
+
+def gdn_lq4_quantize(S, n_iter, Z, col_absmax, row_smooth, Kc, Uc):
+    """Convert fp32 states into LeapQuant's format at 4 bits with 8 tokens (Z: uint8
+    [B, H, 128, 64] packed nibbles; Kc, Uc: fp16 [B, H, 8, 128])."""
+    _lq_quantize("gdn_lq4_quantize", S, n_iter, Z, col_absmax, row_smooth, Kc, Uc, four_bit=True)
+
+
+def gdn_lq4_window(W, pos, n_iter, Z, col_absmax, row_smooth, Kc, Uc, Kbuf, Ubuf, Gbuf, q, k, v, alpha, beta, y):
+    """One decode step in the 4-bit, 8-token format (eq. 10; at pos = W - 1 the refit)."""
+    return _lq_window("gdn_lq4_window", False, W, pos, n_iter, Z, col_absmax, row_smooth, Kc, Uc, Kbuf, Ubuf,
+                      Gbuf, q, k, v, alpha, beta, y, four_bit=True)
 
 
 def kda_lq_window(W, pos, n_iter, Z, col_absmax, row_smooth, Kc, Uc, Kbuf, Ubuf, Gbuf, q, k, v, d, beta, y):

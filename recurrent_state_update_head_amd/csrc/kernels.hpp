@@ -69,6 +69,11 @@ struct LqArgs {
 hipError_t launch_lq_quantize(int heads, const float* S, int n_iter, int8_t* Z, float* B, float* C,
                               void* Kc, void* Uc, hipStream_t stream);
 hipError_t launch_lq_window(const StepArgs& a, const LqArgs& w, bool per_key, hipStream_t stream);
+// The same format at 4 bits with 8 tokens (GDN): Z [heads, 128, 64] packed nibbles,
+// Kc, Uc [heads, 8, 128] fp16.
+hipError_t launch_lq4_quantize(int heads, const float* S, int n_iter, void* Z, float* B, float* C, void* Kc,
+                               void* Uc, hipStream_t stream);
+hipError_t launch_lq4_window(const StepArgs& a, const LqArgs& w, hipStream_t stream);
 
 // mode: 0 append, 1 merge, 2 per-slot live lengths
 hipError_t launch_log(const StepArgs& a, const LogArgs& l, int mode, bool per_key, bool bf16,

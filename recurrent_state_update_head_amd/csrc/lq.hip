@@ -1067,6 +1067,429 @@ __global__ __launch_bounds__(kThreads) void lq_boundary_kda_kernel(
     lq_refit(L, s, n_iter, tid, Zh, Bcol + vec_off, Csm + vec_off, Kc + tok0, Uc + tok0);
 }
 
+// ---------------------------------------------------------------- 4 bits, 8 tokens
+// LeapQuant at 4 bits (sec. 4.1 fits r = 8 tokens there): codes in [-7, 7], two per byte
+// (the even column in the low nibble), dequant Z B / 7, 8 KiB of payload per head. The
+// int4 sweep has its own layout: lane l of wave w owns the 32-bit word of 8 columns
+// 8 (l & 15) .. +7 in the rows 16 it + 4 w + (l >> 4), it = 0..7; a word's 4 row lanes
+// (l, l^16, l^32, l^48) combine by lane swaps, the 4 waves through LDS. Record and token
+// terms are added per value column: thread c + 128 h (h = 0, 1) adds records 8h .. 8h+7
+// and tokens 4h .. 4h+3 of column c.
+constexpr int kTok4 = 8;
+constexpr int kRow4 = kD / 8;  // 32-bit words of a 4-bit row
+
+__device__ __forceinline__ int lq4_row(int it, int wave, int rl) { return 16 * it + 4 * wave + rl; }
+
+// the 8 signed nibbles of a word, column order
+__device__ __forceinline__ void unpack_nibbles8(uint32_t w, float (&z)[8]) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) z[e] = static_cast<float>(static_cast<int>(w << (28 - 4 * e)) >> 28);
+}
+
+__global__ __launch_bounds__(kThreads) void lq4_step_kernel(
+    int W, int pos, const uint32_t* __restrict__ Z, const float* __restrict__ Bcol, const float* __restrict__ Csm,
+    const half_t* __restrict__ Kc, const half_t* __restrict__ Uc, bf16_t* __restrict__ Kbuf,
+    float* __restrict__ Ubuf, float* __restrict__ Gbuf, const bf16_t* __restrict__ q,
+    const bf16_t* __restrict__ k, const bf16_t* __restrict__ v, const float* __restrict__ gate,
+    const float* __restrict__ beta, float* __restrict__ y) {
+    __shared__ f32x2 rowv[kD];
+    __shared__ f32x2 coef[16];
+    __shared__ f32x2 ctok[kTok4];
+    __shared__ f32x2 red[4][kD];
+    __shared__ f32x2 recp[kD];
+    __shared__ float kq_part[2];
+
+    const int h = head_of_block(blockIdx.x, gridDim.x), tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
+    const int c16 = lane & 15, rl = lane >> 4;
+    const int grp = tid >> 4, ch = tid & 15;
+    const int cc = tid & (kD - 1), half = tid >> 7;
+    const bool first = tid < kD;
+    const size_t vec_off = static_cast<size_t>(h) * kD;
+    const size_t rec0 = static_cast<size_t>(h) * W * kD;
+    const size_t tok0 = static_cast<size_t>(h) * kTok4 * kD;
+
+    // ---- loads: record keys (group grp) and values (column cc), tokens, inputs, codes
+    uint32_t kc[4] = {0u, 0u, 0u, 0u};
+    if (0 < pos) {
+        const uint4 x = *reinterpret_cast<const uint4*>(Kbuf + rec0 + static_cast<size_t>(grp < pos ? grp : 0) * kD + 8 * ch);
+        kc[0] = x.x; kc[1] = x.y; kc[2] = x.z; kc[3] = x.w;
+    }
+    float ucol[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const int j = 8 * half + e;
+        ucol[e] = j < pos ? Ubuf[rec0 + static_cast<size_t>(j) * kD + cc] : 0.f;
+    }
+    uint4 ktw = {0u, 0u, 0u, 0u};
+    if (first) ktw = *reinterpret_cast<const uint4*>(Kc + tok0 + (grp & 7) * kD + 8 * ch);
+    half_t utv[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) utv[e] = Uc[tok0 + (4 * half + e) * kD + cc];
+    const float g_lane = lane < pos ? Gbuf[static_cast<size_t>(h) * W + lane] : 1.f;
+    const uint4 kchw = *reinterpret_cast<const uint4*>(k + vec_off + 8 * ch);
+    const uint4 qchw = *reinterpret_cast<const uint4*>(q + vec_off + 8 * ch);
+    const float kr = load_in(k, vec_off + cc), qr = load_in(q, vec_off + cc);
+    const float gr = gate[h];
+    const float cr = Csm[vec_off + cc];
+    const float bcc = Bcol[vec_off + cc];
+    const float vr = load_in(v, vec_off + cc);
+    const float bt = beta[h];
+    const uint32_t* Zh = Z + static_cast<size_t>(h) * kD * kRow4;
+    uint32_t zw[8];
+#pragma unroll
+    for (int it = 0; it < 8; ++it) zw[it] = __builtin_nontemporal_load(Zh + lq4_row(it, wave, rl) * kRow4 + c16);
+
+    // ---- decays (newest gate first): after record grp, and over the whole window so far
+    float Gg = 1.f, Gall = 1.f;
+    for (int i = pos - 1; i >= 0; --i) {
+        const float gi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, g_lane), i));
+        Gg = i > grp ? Gg * gi : Gg;
+        Gall *= gi;
+    }
+    const uint32_t kcw[4] = {kchw.x, kchw.y, kchw.z, kchw.w};
+    const uint32_t qcw[4] = {qchw.x, qchw.y, qchw.z, qchw.w};
+    auto bfe = [](const uint32_t (&w)[4], int e) {
+        return (e & 1) ? __uint_as_float(w[e >> 1] & 0xffff0000u) : __uint_as_float(w[e >> 1] << 16);
+    };
+    if (0 < pos) {
+        float ck = 0.f, cq = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float ej = bfe(kc, e) * (Gg * gr);
+            ck += ej * bfe(kcw, e);
+            cq += ej * bfe(qcw, e);
+        }
+        ck = row16_sum(ck);
+        cq = row16_sum(cq);
+        if (ch == 0 && grp < pos) coef[grp] = f32x2{ck, cq};
+    }
+    if (first) {  // groups 0..7: the tokens, decayed by every gate of the window
+        const half_t* kt = reinterpret_cast<const half_t*>(&ktw);
+        float ck = 0.f, cq = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float ej = static_cast<float>(kt[e]) * (Gall * gr);
+            ck += ej * bfe(kcw, e);
+            cq += ej * bfe(qcw, e);
+        }
+        ck = row16_sum(ck);
+        cq = row16_sum(cq);
+        if (ch == 0) ctok[grp] = f32x2{ck, cq};
+        const float c0 = cr * Gall * gr;  // c_r Gamma_{1:l} at row r
+        rowv[cc] = f32x2{c0 * kr, c0 * qr};
+        const float kq = wave_sum(kr * qr);
+        if (lane == 0) kq_part[wave] = kq;
+    }
+    __syncthreads();
+
+    // ---- payload sweep over the lane's 8 words; the 4 row lanes, then the waves
+    float p1[8], p2[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) p1[e] = p2[e] = 0.f;
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+        const f32x2 rv = rowv[lq4_row(it, wave, rl)];
+        float z[8];
+        unpack_nibbles8(zw[it], z);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            p1[e] += z[e] * rv.x;
+            p2[e] += z[e] * rv.y;
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        p1[e] = add_xor32(add_xor16(p1[e]));
+        p2[e] = add_xor32(add_xor16(p2[e]));
+    }
+    if (rl == 0)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) red[wave][8 * c16 + e] = f32x2{p1[e], p2[e]};
+    // record and token terms of column cc
+    f32x2 rp = {0.f, 0.f};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const int j = 8 * half + e;
+        if (j < pos) rp += coef[j] * ucol[e];
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) rp += ctok[4 * half + e] * static_cast<float>(utv[e]);
+    if (half == 1) recp[cc] = rp;
+    __syncthreads();
+
+    if (first) {
+        const int c = cc;
+        f32x2 acc = (red[0][c] + red[1][c] + red[2][c] + red[3][c]) * (bcc * (1.f / 7.f));
+        acc += rp + recp[c];
+        const float kq = kq_part[0] + kq_part[1];
+        const float u = bt * (vr - acc.x);
+        y[vec_off + c] = acc.y + u * kq;
+        const size_t rec = rec0 + static_cast<size_t>(pos) * kD;
+        Ubuf[rec + c] = u;
+        store_in(Kbuf, rec + c, kr);
+        if (c == 0) Gbuf[static_cast<size_t>(h) * W + pos] = gr;
+    }
+}
+
+// The window's last step at 4 bits: the step as above, then S_W on the matrix cores as in
+// the 8-bit boundary (payload init from the staged nibbles, the records' two bf16 MFMAs per
+// tile, the 8 tokens' two fp32 MFMAs), through LDS into the refit's layout, and the 8-token
+// refit with 4-bit codes. One region of dynamic LDS serves the step arrays, the state in
+// transit and the refit's arrays in turn; after it lie W (the old Ut, 8 tokens) and the old
+// payload's B / 7.
+constexpr int kZs4Stride = kRow4 + 1;
+constexpr int kStep4Floats = 2 * kD * 4 + 3 * 2 * kD * 4 + kD * kZs4Stride + 2 * kTok4 * kD + 4 * kD * 2 + kD * 2;
+constexpr int kLq4BoundaryFloats = kD * kD + kTok4 * kD + kD;
+static_assert(kStep4Floats <= kD * kD, "the step-phase arrays must lie inside the shared region");
+static_assert(RefitCfg<8, 4>::kRegionFloats <= kD * kD, "the refit's arrays must lie inside the shared region");
+
+__global__ __launch_bounds__(kThreads) void lq4_boundary_kernel(
+    int W, int pos, int n_iter, uint32_t* __restrict__ Z, float* __restrict__ Bcol, float* __restrict__ Csm,
+    half_t* __restrict__ Kc, half_t* __restrict__ Uc, const bf16_t* __restrict__ Kbuf,
+    const float* __restrict__ Ubuf, const float* __restrict__ Gbuf, const bf16_t* __restrict__ q,
+    const bf16_t* __restrict__ k, const bf16_t* __restrict__ v, const float* __restrict__ gate,
+    const float* __restrict__ beta, float* __restrict__ y) {
+    constexpr int kRec = 16;
+    extern __shared__ __align__(16) float dyn_lds[];
+    __shared__ f32x2 rowv[kD];
+    __shared__ f32x2 coef[kRec];
+    __shared__ f32x2 ctok[kTok4];
+    __shared__ float kq_part[2];
+    __shared__ float zcoef[kD];
+    __shared__ float gam[kRec];
+
+    u32x4* Kt = reinterpret_cast<u32x4*>(dyn_lds);                 // [2][128] keys, 8 records per word
+    u32x4* Ut = Kt + 2 * kD;                                        // [3][2][128] scaled values, 3 parts
+    uint32_t* Zs = reinterpret_cast<uint32_t*>(Ut + 3 * 2 * kD);   // [128][17] the old codes
+    float* Ktok = reinterpret_cast<float*>(Zs + kD * kZs4Stride);  // [8][128]
+    float* Utok = Ktok + kTok4 * kD;                                // [8][128], scaled by Gamma_{1:W}
+    f32x2* red = reinterpret_cast<f32x2*>(Utok + kTok4 * kD);      // [4][128]
+    f32x2* recp = red + 4 * kD;                                     // [128]
+    const RefitLds<kTok4, 4> L(dyn_lds, dyn_lds + kD * kD);
+    float* bscs = dyn_lds + kD * kD + kTok4 * kD;                   // B / 7 of the old payload
+
+    const int h = head_of_block(blockIdx.x, gridDim.x), tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
+    const int c16 = lane & 15, rl = lane >> 4;
+    const int grp = tid >> 4, ch = tid & 15;
+    const int cc = tid & (kD - 1), half = tid >> 7;
+    const bool first = tid < kD;
+    const size_t vec_off = static_cast<size_t>(h) * kD;
+    const size_t rec0 = static_cast<size_t>(h) * W * kD;
+    const size_t tok0 = static_cast<size_t>(h) * kTok4 * kD;
+    uint32_t* Zh = Z + static_cast<size_t>(h) * kD * kRow4;
+
+    // ---- loads
+    uint32_t kcr[4] = {0u, 0u, 0u, 0u};
+    if (0 < pos) {
+        const uint4 x = *reinterpret_cast<const uint4*>(Kbuf + rec0 + static_cast<size_t>(grp < pos ? grp : 0) * kD + 8 * ch);
+        kcr[0] = x.x; kcr[1] = x.y; kcr[2] = x.z; kcr[3] = x.w;
+    }
+    float ucol[8];
+    uint32_t kcol[4];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const int j = 8 * half + e;
+        const size_t at = rec0 + static_cast<size_t>(j < pos ? j : 0) * kD + cc;
+        ucol[e] = j < pos ? Ubuf[at] : 0.f;
+        const uint32_t kb = j < pos ? static_cast<uint32_t>(Kbuf[at]) : 0u;
+        kcol[e >> 1] = (e & 1) ? (kcol[e >> 1] | (kb << 16)) : kb;
+    }
+    uint4 ktw = {0u, 0u, 0u, 0u};
+    if (first) ktw = *reinterpret_cast<const uint4*>(Kc + tok0 + (grp & 7) * kD + 8 * ch);
+    half_t tokv[kTok4];  // token t at row / column cc (threads < 128: keys; threads >= 128: values)
+#pragma unroll
+    for (int t = 0; t < kTok4; ++t) tokv[t] = (first ? Kc : Uc)[tok0 + t * kD + cc];
+    const float g_lane = lane < pos ? Gbuf[static_cast<size_t>(h) * W + lane] : 1.f;
+    const uint4 kchw = *reinterpret_cast<const uint4*>(k + vec_off + 8 * ch);
+    const uint4 qchw = *reinterpret_cast<const uint4*>(q + vec_off + 8 * ch);
+    const float kr = load_in(k, vec_off + cc), qr = load_in(q, vec_off + cc);
+    const float gr = gate[h];
+    const float cr = Csm[vec_off + cc];
+    const float bcc = Bcol[vec_off + cc];
+    const float vr = load_in(v, vec_off + cc);
+    const float bt = beta[h];
+    uint32_t zw[8];
+#pragma unroll
+    for (int it = 0; it < 8; ++it) zw[it] = __builtin_nontemporal_load(Zh + lq4_row(it, wave, rl) * kRow4 + c16);
+
+    // ---- gate products (newest first): after record grp, after record = lane, all
+    float Gg = 1.f, Gl = 1.f, Gall = 1.f;
+    for (int i = pos - 1; i >= 0; --i) {
+        const float gi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, g_lane), i));
+        Gg = i > grp ? Gg * gi : Gg;
+        Gl = i > lane ? Gl * gi : Gl;
+        Gall *= gi;
+    }
+    const float gam_all = Gall * gr;  // Gamma_{1:W}
+    if (wave == 0 && lane < kRec) gam[lane] = lane < pos ? Gl * gr : 1.f;
+    const uint32_t kcw[4] = {kchw.x, kchw.y, kchw.z, kchw.w};
+    const uint32_t qcw[4] = {qchw.x, qchw.y, qchw.z, qchw.w};
+    auto bfe = [](const uint32_t (&w)[4], int e) {
+        return (e & 1) ? __uint_as_float(w[e >> 1] & 0xffff0000u) : __uint_as_float(w[e >> 1] << 16);
+    };
+    if (0 < pos) {
+        float ck = 0.f, cq = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float ej = bfe(kcr, e) * (Gg * gr);
+            ck += ej * bfe(kcw, e);
+            cq += ej * bfe(qcw, e);
+        }
+        ck = row16_sum(ck);
+        cq = row16_sum(cq);
+        if (ch == 0 && grp < pos) coef[grp] = f32x2{ck, cq};
+    }
+    if (first) {
+        const half_t* kt = reinterpret_cast<const half_t*>(&ktw);
+        float ck = 0.f, cq = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float ej = static_cast<float>(kt[e]) * gam_all;
+            ck += ej * bfe(kcw, e);
+            cq += ej * bfe(qcw, e);
+        }
+        ck = row16_sum(ck);
+        cq = row16_sum(cq);
+        if (ch == 0) ctok[grp] = f32x2{ck, cq};
+        const float c0 = cr * gam_all;
+        rowv[cc] = f32x2{c0 * kr, c0 * qr};
+        zcoef[cc] = c0;
+        const float kq = wave_sum(kr * qr);
+        if (lane == 0) kq_part[wave] = kq;
+    } else {
+        bscs[cc] = bcc * (1.f / 7.f);
+    }
+    // token operands of the contraction, and the unscaled values as the refit's start
+#pragma unroll
+    for (int t = 0; t < kTok4; ++t) {
+        const float x = static_cast<float>(tokv[t]);
+        if (first) Ktok[t * kD + cc] = x;
+        else Utok[t * kD + cc] = x * gam_all;
+    }
+    if (!first)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+            L.W[cc * 2 + hh] = f32x4{static_cast<float>(tokv[4 * hh]), static_cast<float>(tokv[4 * hh + 1]),
+                                     static_cast<float>(tokv[4 * hh + 2]), static_cast<float>(tokv[4 * hh + 3])};
+    Kt[half * kD + cc] = u32x4{kcol[0], kcol[1], kcol[2], kcol[3]};
+    __syncthreads();
+
+    // ---- payload sweep; record and token terms per column; scaled records staged for the MFMA
+    float p1[8], p2[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) p1[e] = p2[e] = 0.f;
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+        const f32x2 rv = rowv[lq4_row(it, wave, rl)];
+        float z[8];
+        unpack_nibbles8(zw[it], z);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            p1[e] += z[e] * rv.x;
+            p2[e] += z[e] * rv.y;
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        p1[e] = add_xor32(add_xor16(p1[e]));
+        p2[e] = add_xor32(add_xor16(p2[e]));
+    }
+    if (rl == 0)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) red[wave * kD + 8 * c16 + e] = f32x2{p1[e], p2[e]};
+    f32x2 rp = {0.f, 0.f};
+    u32x4 part[3];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const int j = 8 * half + e;
+        const f32x2 c = j < pos ? coef[j] : f32x2{0.f, 0.f};
+        rp += c * ucol[e];
+        uint32_t hi, mid, lo;
+        split3_bf16(gam[j] * ucol[e], hi, mid, lo);
+        const int sh = 16 * (e & 1);
+        part[0][e >> 1] = (e & 1) ? (part[0][e >> 1] | (hi << sh)) : hi;
+        part[1][e >> 1] = (e & 1) ? (part[1][e >> 1] | (mid << sh)) : mid;
+        part[2][e >> 1] = (e & 1) ? (part[2][e >> 1] | (lo << sh)) : lo;
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {  // tokens 4 half .. +3 of column cc (L.W holds their unscaled values)
+        const f32x4 ut = L.W[cc * 2 + half];
+        rp += ctok[4 * half + e] * ut[e];
+    }
+#pragma unroll
+    for (int pp = 0; pp < 3; ++pp) Ut[(pp * 2 + half) * kD + cc] = part[pp];
+    if (half == 1) recp[cc] = rp;
+#pragma unroll
+    for (int it = 0; it < 8; ++it) Zs[lq4_row(it, wave, rl) * kZs4Stride + c16] = zw[it];
+    __syncthreads();
+
+    // ---- correction and output; the current record joins the contraction operands
+    if (first) {
+        const int c = cc;
+        f32x2 acc = (red[c] + red[kD + c] + red[2 * kD + c] + red[3 * kD + c]) * bscs[c];
+        acc += rp + recp[c];
+        const float kq = kq_part[0] + kq_part[1];
+        const float u = bt * (vr - acc.x);
+        y[vec_off + c] = acc.y + u * kq;
+        uint32_t uh, um, ul;
+        split3_bf16(u, uh, um, ul);
+        reinterpret_cast<uint16_t*>(&Ut[(0 * 2 + (pos >> 3)) * kD + c])[pos & 7] = static_cast<uint16_t>(uh);
+        reinterpret_cast<uint16_t*>(&Ut[(1 * 2 + (pos >> 3)) * kD + c])[pos & 7] = static_cast<uint16_t>(um);
+        reinterpret_cast<uint16_t*>(&Ut[(2 * 2 + (pos >> 3)) * kD + c])[pos & 7] = static_cast<uint16_t>(ul);
+        reinterpret_cast<uint16_t*>(&Kt[(pos >> 3) * kD + c])[pos & 7] = static_cast<uint16_t>(__float_as_uint(kr) >> 16);
+    }
+    __syncthreads();
+
+    // ---- S_W on the matrix cores (result layout of v_mfma_f32_16x16x{32_bf16,4f32}: lane l
+    // holds key row 32w + 16a + l%16 and value columns 16ct + 4(l/16) .. +3 of tile ct)
+    const int lr = lane & 15, lq = lane >> 4, blk = lq & 1;
+    f32x4 acc[2][8];
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+        const int row = 16 * (2 * wave + a) + lr;
+        const bf16x8 bv = __builtin_bit_cast(bf16x8, Kt[blk * kD + row]);
+        const float zc = zcoef[row];
+        const float bk0 = Ktok[lq * kD + row], bk1 = Ktok[(4 + lq) * kD + row];
+        const uint16_t* z16 = reinterpret_cast<const uint16_t*>(Zs + row * kZs4Stride);
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct) {
+            const f32x4 bs = *reinterpret_cast<const f32x4*>(bscs + 16 * ct + 4 * lq);
+            const uint32_t zz = z16[4 * ct + lq];  // the 4 nibbles of columns 16ct + 4lq .. +3
+            const f32x4 zf = {static_cast<float>(static_cast<int>(zz << 28) >> 28),
+                              static_cast<float>(static_cast<int>(zz << 24) >> 28),
+                              static_cast<float>(static_cast<int>(zz << 20) >> 28),
+                              static_cast<float>(static_cast<int>(zz << 16) >> 28)};
+            acc[a][ct] = zf * (bs * zc);
+            const int col = 16 * ct + lr;
+            const bf16x8 a1 = __builtin_bit_cast(bf16x8, Ut[((lq < 2 ? 0 : 1) * 2 + blk) * kD + col]);
+            const u32x4 lo = Ut[(2 * 2 + blk) * kD + col];
+            const bf16x8 a2 = __builtin_bit_cast(bf16x8, lq < 2 ? lo : u32x4{0u, 0u, 0u, 0u});
+            acc[a][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, bv, acc[a][ct], 0, 0, 0);
+            acc[a][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a2, bv, acc[a][ct], 0, 0, 0);
+            acc[a][ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(Utok[lq * kD + col], bk0, acc[a][ct], 0, 0, 0);
+            acc[a][ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(Utok[(4 + lq) * kD + col], bk1, acc[a][ct], 0, 0, 0);
+        }
+    }
+    __syncthreads();  // every read of the step-phase arrays is done: the region holds S
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+        const int row = 16 * (2 * wave + a) + lr;
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct) state_unit(dyn_lds, row, 4 * ct + lq) = acc[a][ct];
+    }
+    __syncthreads();
+    f32x4 s[16];
+    {
+        const int uu = 8 * wave + (lane & 7), rr = lane >> 3;
+#pragma unroll
+        for (int it = 0; it < 16; ++it) s[it] = state_unit(dyn_lds, 8 * it + rr, uu);
+    }
+    __syncthreads();  // the region is free for the refit's arrays
+    lq_refit(L, s, n_iter, tid, Zh, Bcol + vec_off, Csm + vec_off, Kc + tok0, Uc + tok0);
+}
+
 // ---------------------------------------------------------------- launchers
 static hipError_t set_lds(const void* fn, int floats) {
     return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -1115,6 +1538,37 @@ hipError_t launch_lq_window(const StepArgs& a, const LqArgs& w, bool per_key, hi
                            w.C, static_cast<const half_t*>(w.Kc), static_cast<const half_t*>(w.Uc),
                            static_cast<bf16_t*>(w.Kbuf), w.Ubuf, w.Gbuf, static_cast<const bf16_t*>(a.q),
                            static_cast<const bf16_t*>(a.k), static_cast<const bf16_t*>(a.v), a.gate, a.beta, a.y);
+    return hipGetLastError();
+}
+
+hipError_t launch_lq4_quantize(int heads, const float* S, int n_iter, void* Z, float* B, float* C, void* Kc,
+                               void* Uc, hipStream_t stream) {
+    using Cfg = RefitCfg<kTok4, 4>;
+    constexpr int floats = Cfg::kRegionFloats + Cfg::kWFloats;
+    static const hipError_t attr = set_lds(reinterpret_cast<const void*>(lq_quantize_kernel<kTok4, 4>), floats);
+    if (attr != hipSuccess) return attr;
+    hipLaunchKernelGGL((lq_quantize_kernel<kTok4, 4>), dim3(heads), dim3(kThreads), sizeof(float) * floats, stream,
+                       S, n_iter, static_cast<uint32_t*>(Z), B, C, static_cast<half_t*>(Kc),
+                       static_cast<half_t*>(Uc));
+    return hipGetLastError();
+}
+
+hipError_t launch_lq4_window(const StepArgs& a, const LqArgs& w, hipStream_t stream) {
+    if (w.pos == w.W - 1) {
+        static const hipError_t attr = set_lds(reinterpret_cast<const void*>(lq4_boundary_kernel), kLq4BoundaryFloats);
+        if (attr != hipSuccess) return attr;
+        hipLaunchKernelGGL(lq4_boundary_kernel, dim3(a.heads), dim3(kThreads), sizeof(float) * kLq4BoundaryFloats,
+                           stream, w.W, w.pos, w.n_iter, reinterpret_cast<uint32_t*>(w.Z), w.B, w.C,
+                           static_cast<half_t*>(w.Kc), static_cast<half_t*>(w.Uc),
+                           static_cast<const bf16_t*>(w.Kbuf), w.Ubuf, w.Gbuf, static_cast<const bf16_t*>(a.q),
+                           static_cast<const bf16_t*>(a.k), static_cast<const bf16_t*>(a.v), a.gate, a.beta, a.y);
+        return hipGetLastError();
+    }
+    hipLaunchKernelGGL(lq4_step_kernel, dim3(a.heads), dim3(kThreads), 0, stream, w.W, w.pos,
+                       reinterpret_cast<const uint32_t*>(w.Z), w.B, w.C, static_cast<const half_t*>(w.Kc),
+                       static_cast<const half_t*>(w.Uc), static_cast<bf16_t*>(w.Kbuf), w.Ubuf, w.Gbuf,
+                       static_cast<const bf16_t*>(a.q), static_cast<const bf16_t*>(a.k),
+                       static_cast<const bf16_t*>(a.v), a.gate, a.beta, a.y);
     return hipGetLastError();
 }
 

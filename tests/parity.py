@@ -221,12 +221,14 @@ def run_log_slots(w: wl.Workload, sample: int | None = None, steps: int | None =
 
 def new_lq_buffers(w: wl.Workload):
     B, H, W = w.B, w.H, w.W
+    r = 8 if w.bits == 4 else 4
     return {
-        "Z": torch.zeros(B, H, 128, 128, device=DEV, dtype=torch.int8),
+        "Z": (torch.zeros(B, H, 128, 64, device=DEV, dtype=torch.uint8) if w.bits == 4 else
+              torch.zeros(B, H, 128, 128, device=DEV, dtype=torch.int8)),
         "B": torch.zeros(B, H, 128, device=DEV),
         "C": torch.zeros(B, H, 128, device=DEV),
-        "Kc": torch.zeros(B, H, 4, 128, device=DEV, dtype=torch.float16),
-        "Uc": torch.zeros(B, H, 4, 128, device=DEV, dtype=torch.float16),
+        "Kc": torch.zeros(B, H, r, 128, device=DEV, dtype=torch.float16),
+        "Uc": torch.zeros(B, H, r, 128, device=DEV, dtype=torch.float16),
         "Kbuf": torch.zeros(B, H, W, 128, device=DEV, dtype=qkv_dtype(w)),
         "Ubuf": torch.zeros(B, H, W, 128, device=DEV),
         "Gbuf": torch.zeros((B, H, W, 128) if w.per_key_gate else (B, H, W), device=DEV),
@@ -234,16 +236,22 @@ def new_lq_buffers(w: wl.Workload):
 
 
 def lq_host(buf, hd):
-    """The GPU's representation of the sampled heads: Z, B, c, and the tokens as [n, 128, 4]."""
-    Z = take(buf["Z"], hd, (128, 128)).astype(np.int64)
+    """The GPU's representation of the sampled heads: Z, B, c, and the tokens as [n, 128, r]
+    (4-bit codes unpacked from their nibbles)."""
+    from oracle import lq as lqo
+    if buf["Z"].dtype == torch.uint8:
+        Z = lqo.unpack_nibbles(take(buf["Z"], hd, (128, 64))).astype(np.int64)
+    else:
+        Z = take(buf["Z"], hd, (128, 128)).astype(np.int64)
+    r = buf["Kc"].shape[2]
     Bc = take(buf["B"], hd, (128,)).astype(np.float64)
     C = take(buf["C"], hd, (128,)).astype(np.float64)
-    K16 = np.transpose(take(buf["Kc"].float(), hd, (4, 128)), (0, 2, 1)).astype(np.float64)
-    U16 = np.transpose(take(buf["Uc"].float(), hd, (4, 128)), (0, 2, 1)).astype(np.float64)
+    K16 = np.transpose(take(buf["Kc"].float(), hd, (r, 128)), (0, 2, 1)).astype(np.float64)
+    U16 = np.transpose(take(buf["Uc"].float(), hd, (r, 128)), (0, 2, 1)).astype(np.float64)
     return Z, Bc, C, K16, U16
 
 
-def check_lq_refit(S_ref, V0, n_iter, rep, err, tie_band=1e-3, mat_rel=1e-6):
+def check_lq_refit(S_ref, V0, n_iter, rep, err, tie_band=1e-3, mat_rel=1e-6, qmax=127):
     """Teacher-forced check of one refit.
 
     Tokens: against the oracle's fit of the same state from the same start (the
@@ -275,14 +283,14 @@ def check_lq_refit(S_ref, V0, n_iter, rep, err, tie_band=1e-3, mat_rel=1e-6):
         err["B"] = max(err["B"], float(np.max(np.abs(Bc[i] - B_ref) / np.maximum(xmag, 1e-300))))
         nz = Bc[i] > 0
         w = np.zeros_like(X)
-        w[:, nz] = X[:, nz] * 127.0 / Bc[i][nz][None, :]
-        Zr = np.clip(np.rint(w), -127, 127).astype(np.int64)
+        w[:, nz] = X[:, nz] * float(qmax) / Bc[i][nz][None, :]
+        Zr = np.clip(np.rint(w), -qmax, qmax).astype(np.int64)
         dz = np.abs(Z[i] - Zr)
         err["z_maxdiff"] = max(err["z_maxdiff"], int(dz.max()))
         flips = dz > 0
         err["z_flips"] += int(flips.sum())
         band = np.full_like(w, tie_band)
-        band[:, nz] += mat_rel * 127.0 * (mag[:, nz] / C[i][:, None]) / Bc[i][nz][None, :]
+        band[:, nz] += mat_rel * float(qmax) * (mag[:, nz] / C[i][:, None]) / Bc[i][nz][None, :]
         near = np.abs(np.abs(w - np.floor(w)) - 0.5) < band
         err["z_flips_outside_band"] += int((flips & ~near).sum())
 
@@ -303,17 +311,21 @@ def run_lq(w: wl.Workload, n_iter: int = 1, n_iter0: int = 8, sample: int | None
     Sd = torch.from_numpy(S0).to(DEV).view(B, H, 128, 128)
     quantize = m.kda_lq_quantize if w.per_key_gate else m.gdn_lq_quantize
     window = m.kda_lq_window if w.per_key_gate else m.gdn_lq_window
+    if w.bits == 4:
+        quantize, window = m.gdn_lq4_quantize, m.gdn_lq4_window
+    qmax = lqo.QMAX4 if w.bits == 4 else lqo.QMAX8
+    r = 8 if w.bits == 4 else 4
     quantize(Sd, n_iter0, buf["Z"], buf["B"], buf["C"], buf["Kc"], buf["Uc"])
     err = {"y": 0.0, "tok": 0.0, "tok_k": 0.0, "tok_u": 0.0, "c": 0.0, "B": 0.0, "z_maxdiff": 0,
            "z_flips": 0, "z_flips_outside_band": 0, "boundaries": 0}
     S_ref = S0[heads].astype(np.float64)
     del Sd, S0
-    walsh = np.broadcast_to(lqo.walsh_start(), (len(heads), 128, 4))
-    check_lq_refit(S_ref, walsh, n_iter0, lq_host(buf, hd), err)
+    walsh = np.broadcast_to(lqo.walsh_start(r=r), (len(heads), 128, r))
+    check_lq_refit(S_ref, walsh, n_iter0, lq_host(buf, hd), err, qmax=qmax)
     y = torch.empty(B, H, 128, device=DEV)
     for t0 in range(0, steps, W):
         rep = lq_host(buf, hd)
-        S = np.stack([lqo.represent(rep[0][i], rep[1][i], rep[2][i], rep[3][i], rep[4][i])
+        S = np.stack([lqo.represent(rep[0][i], rep[1][i], rep[2][i], rep[3][i], rep[4][i], qmax=qmax)
                       for i in range(len(heads))])
         n = min(W, steps - t0)
         for pos in range(n):
@@ -323,7 +335,7 @@ def run_lq(w: wl.Workload, n_iter: int = 1, n_iter0: int = 8, sample: int | None
             y_ref = oracle.dense_step(S, *host_slice(x, heads))
             err["y"] = max(err["y"], rel_err(take(y, hd, (128,)), y_ref))
         if n == W:
-            check_lq_refit(S, rep[4], n_iter, lq_host(buf, hd), err)
+            check_lq_refit(S, rep[4], n_iter, lq_host(buf, hd), err, qmax=qmax)
             err["boundaries"] += 1
     return err
 

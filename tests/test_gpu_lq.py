@@ -52,6 +52,19 @@ def test_lq_kda_b128_h32_full_size_sampled():
     _check(run_lq(w, n_iter=1, sample=64, steps=48), w.name)
 
 
+@pytest.mark.parametrize("W,B,H,n_iter", [(16, 2, 5, 1), (16, 3, 4, 2), (5, 2, 3, 1), (1, 2, 2, 0)])
+def test_lq4_windows_small(W, B, H, n_iter):
+    """4-bit codes (two per byte, /7) with 8 tokens (LeapQuant sec. 4.1)."""
+    w = wl.custom(wl.WORKLOADS[12], B=B, H=H, W=W, steps=2 * W + min(W, 3))
+    _check(run_lq(w, n_iter=n_iter), f"4-bit W={W} B={B} H={H} n_iter={n_iter}")
+
+
+def test_lq4_b256_h48_full_size_sampled():
+    w = wl.WORKLOADS[12]
+    say(f"[lq] {w.name}: full size, 64 sampled heads, 48 steps")
+    _check(run_lq(w, n_iter=1, sample=64, steps=48), w.name)
+
+
 @pytest.mark.parametrize("n_iter0", [0, 3])
 def test_lq_quantize_start_iterations(n_iter0):
     w = wl.custom(wl.WORKLOADS[6], B=2, H=3, W=16, steps=0)

@@ -49,6 +49,7 @@ class Workload:
     W: int = 0            # window length of the int8 path
     M: int = 0            # merge interval of the base+log path (capacity C = M - 1)
     outliers: bool = False
+    bits: int = 8         # code width of the LeapQuant window format (8, or 4 with 8 tokens)
 
     @property
     def heads(self) -> int:
@@ -75,6 +76,9 @@ WORKLOADS = {
                 0.90, 0.999, W=16, outliers=True),
     # RWKV6 at the shape of DeltaLog's kernel study (Table 3: 32 heads of 128 x 128, M = 4),
     # batch 128 as in its interval sweep; per-key decays drawn like KDA's gates
+    # LeapQuant's format at 4 bits with 8 tokens on the int8 workload's inputs (same seed as 4)
+    12: Workload(4, "gdn_lq4_window_b256_h48_w16", "gdn", "lq_window", 256, 48, 256, "bf16", 0.90, 0.999,
+                 W=16, outliers=True, bits=4),
     # LeapQuant's format with KDA gates on the KDA workload's shape (same outliers as 4)
     9: Workload(9, "kda_lq_window_b128_h32_w16", "kda", "lq_window", 128, 32, 256, "bf16", 0.80, 1.0,
                 W=16, outliers=True),
