@@ -40,7 +40,7 @@ KERNEL_SOURCES = {
 }
 
 WORKLOAD_BY_FLAG = {"gdn": 2, "gdn_small": 1, "kda": 3, "q8": 4, "log": 5, "lq": 6, "rwkv6": 7,
-                    "rwkv6_log": 8, "kda_lq": 9, "rwkv7": 10, "rwkv7_q8": 11}
+                    "rwkv6_log": 8, "kda_lq": 9, "rwkv7": 10, "rwkv7_q8": 11, "lq4": 12}
 LQ_TOKENS = 4
 
 
@@ -101,7 +101,8 @@ def lq_step_bytes_per_head(w: wl.Workload, pos: int) -> int:
     gdim = d if w.per_key_gate else 1
     rec = d * _in_bytes(w) + 4 * d + 4 * gdim
     inputs = 3 * d * _in_bytes(w) + 4 * gdim + 4
-    rep = d * d + 4 * d + 4 * d + 2 * LQ_TOKENS * d * 2
+    r = 8 if w.bits == 4 else LQ_TOKENS
+    rep = d * d * w.bits // 8 + 4 * d + 4 * d + 2 * r * d * 2
     rd = rep + pos * rec + inputs
     wr = 4 * d + (rep if pos == w.W - 1 else rec)
     return rd + wr
@@ -284,17 +285,20 @@ def run_gpu(w: wl.Workload, steps: int, warmup: int, slots: bool = False, n_iter
             state["t"] += 1
     elif w.path == "lq_window":
         W = w.W
-        Z = torch.empty(B, H, 128, 128, device=dev, dtype=torch.int8)
+        four = w.bits == 4
+        Z = (torch.empty(B, H, 128, 64, device=dev, dtype=torch.uint8) if four else
+             torch.empty(B, H, 128, 128, device=dev, dtype=torch.int8))
         Bc = torch.empty(B, H, 128, device=dev)
         Cs = torch.empty(B, H, 128, device=dev)
-        Kc = torch.empty(B, H, LQ_TOKENS, 128, device=dev, dtype=torch.float16)
+        Kc = torch.empty(B, H, 8 if four else LQ_TOKENS, 128, device=dev, dtype=torch.float16)
         Uc = torch.empty_like(Kc)
-        (rsu.kda_lq_quantize if kda else rsu.gdn_lq_quantize)(S0, 8, Z, Bc, Cs, Kc, Uc)
+        quant = rsu.gdn_lq4_quantize if four else (rsu.kda_lq_quantize if kda else rsu.gdn_lq_quantize)
+        quant(S0, 8, Z, Bc, Cs, Kc, Uc)
         del S0
         Kb = torch.zeros(B, H, W, 128, device=dev, dtype=x["q"].dtype)
         Ub = torch.zeros(B, H, W, 128, device=dev)
         Gb = torch.zeros((B, H, W, 128) if kda else (B, H, W), device=dev)
-        win = rsu.kda_lq_window if kda else rsu.gdn_lq_window
+        win = rsu.gdn_lq4_window if four else (rsu.kda_lq_window if kda else rsu.gdn_lq_window)
 
         def step():
             t = state["t"]
@@ -479,8 +483,9 @@ def main():
         "dtype": "f32",
         "data": "synthetic (seeded; shapes and distributions of the workload)",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "dk": 128, "dv": 128,
-                   "qkv": w.qkv, "state": {"q8_window": "int8+f32 scales",
-                                            "lq_window": "int8+f32 scales+4 fp16 token pairs"}.get(w.path, "f32"),
+                   "qkv": w.qkv, "state": ("int4+f32 scales+8 fp16 token pairs" if w.bits == 4 else
+                                            {"q8_window": "int8+f32 scales",
+                                             "lq_window": "int8+f32 scales+4 fp16 token pairs"}.get(w.path, "f32")),
                    "W": w.W or None, "M": w.M or None, "gates": w.variant,
                    "log_phases": ("per-slot (mixed)" if args.slots else "batch-uniform") if w.path == "log" else None,
                    "refit_iterations": args.n_iter if w.path == "lq_window" else None},
