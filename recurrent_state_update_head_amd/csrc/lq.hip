@@ -80,16 +80,14 @@ __device__ __forceinline__ float sum_col_lanes(float x) {
     x += dpp<kDppXor2>(x);
     return x + dpp<kDppHalfMirror>(x);
 }
-__device__ __forceinline__ f32x4 sum_col_lanes(f32x4 x) {
-    return f32x4{sum_col_lanes(x.x), sum_col_lanes(x.y), sum_col_lanes(x.z), sum_col_lanes(x.w)};
-}
 
-// y + a x element by element, written without a splat of a: the refit's state is
-// invariant across the fit's iterations, and splats of it would be hoisted out of the
+// y + a x and a x element by element, written without a splat of a: the refit's state
+// is invariant across the fit's iterations, and splats of it would be hoisted out of the
 // loop as four registers each.
 __device__ __forceinline__ f32x4 axpy(float a, f32x4 x, f32x4 y) {
     return f32x4{fmaf(a, x.x, y.x), fmaf(a, x.y, y.y), fmaf(a, x.z, y.z), fmaf(a, x.w, y.w)};
 }
+__device__ __forceinline__ f32x4 scale(float a, f32x4 x) { return f32x4{a * x.x, a * x.y, a * x.z, a * x.w}; }
 
 __device__ __forceinline__ float max_row_lanes(float x) {
     x = fmaxf(x, dpp<kDppRor8>(x));
@@ -149,25 +147,46 @@ __device__ __forceinline__ void refit_mgs(const RefitLds<kT, kBits>& L, int wave
     __syncthreads();
 }
 
-// Y = S V
+// Y = S V. A lane's kT partial sums for one row (its 4 columns against the kT columns of
+// V) are summed over the row's 8 lanes by a transposing butterfly: at each of the lane
+// exchanges i^1, i^2 and i^7 (the last one within each group of 8) a lane keeps half of its
+// values and adds the partner's copy of that half, so the 8 lanes end with one token each
+// after kT/2 + kT/4 + 1 adds instead of 3 kT. For the halves to match, lane bits b0..b2 give
+// each lane its own token order: value i holds token i ^ sv_token_perm (at 4 tokens the last
+// exchange is a plain sum, and lanes l and l^7 hold the same token).
+template <int kT>
+__device__ __forceinline__ int sv_token_perm(int lane) {
+    const int b0 = lane & 1, b1 = (lane >> 1) & 1, b2 = (lane >> 2) & 1;
+    return (kT / 2) * (b0 ^ b2) + (kT / 4) * (b1 ^ b2) + (kT == 8 ? b2 : 0);
+}
+
 template <int kT, int kBits>
 __device__ __forceinline__ void refit_sv(const RefitLds<kT, kBits>& L, const f32x4 (&s)[16], int wave, int lane,
                                          int tid) {
     constexpr int kC = kT / 4;
     const int uu = 8 * wave + (lane & 7), ro = lane >> 3;
-    f32x4 vc[4][kC];
+    const int tp = sv_token_perm<kT>(lane);
+    const float* Vf = reinterpret_cast<const float*>(L.V);
+    float vp[4][kT];
 #pragma unroll
     for (int e = 0; e < 4; ++e)
 #pragma unroll
-        for (int h = 0; h < kC; ++h) vc[e][h] = L.V[(4 * uu + e) * kC + h];
+        for (int i = 0; i < kT; ++i) vp[e][i] = Vf[(4 * uu + e) * kT + (i ^ tp)];
+    float* Ypf = reinterpret_cast<float*>(L.Yp);
 #pragma unroll
     for (int it = 0; it < 16; ++it) {
+        float p[kT];
 #pragma unroll
-        for (int h = 0; h < kC; ++h) {
-            const f32x4 p = sum_col_lanes(axpy(s[it].w, vc[3][h], axpy(s[it].z, vc[2][h],
-                                                 axpy(s[it].y, vc[1][h], s[it].x * vc[0][h]))));
-            if ((lane & 7) == 0) L.Yp[(wave * kD + 8 * it + ro) * kC + h] = p;
-        }
+        for (int i = 0; i < kT; ++i)
+            p[i] = fmaf(s[it].w, vp[3][i], fmaf(s[it].z, vp[2][i], fmaf(s[it].y, vp[1][i], s[it].x * vp[0][i])));
+        float q[kT / 2];
+#pragma unroll
+        for (int i = 0; i < kT / 2; ++i) q[i] = p[i] + dpp<kDppXor1>(p[i + kT / 2]);
+        float r[kT / 4];
+#pragma unroll
+        for (int i = 0; i < kT / 4; ++i) r[i] = q[i] + dpp<kDppXor2>(q[i + kT / 4]);
+        const float t = r[0] + dpp<kDppHalfMirror>(r[kT / 4 - 1]);
+        Ypf[(wave * kD + 8 * it + ro) * kT + tp] = t;
     }
     __syncthreads();
     if (tid < kD)
@@ -178,11 +197,30 @@ __device__ __forceinline__ void refit_sv(const RefitLds<kT, kBits>& L, const f32
     __syncthreads();
 }
 
-// W = S^T Y
+// Sums of x and y over lane pairs (l, l^16) (pair16) or (l, l^32) (pair32) with one lane
+// swap: lanes whose bit 4 (bit 5) is clear get the sum of x, the others the sum of y.
+__device__ __forceinline__ float add_pair16(float x, float y) {
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+    const unsigned p0 = p[0], p1 = p[1];
+    return __uint_as_float(p0) + __uint_as_float(p1);
+}
+__device__ __forceinline__ float add_pair32(float x, float y) {
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+    const unsigned p0 = p[0], p1 = p[1];
+    return __uint_as_float(p0) + __uint_as_float(p1);
+}
+
+// W = S^T Y. A lane's 4 kT partial sums (its 4 columns against the kT columns of Y, over its
+// 16 rows) are summed over the 8 row lanes of the column group by a transposing butterfly:
+// over lane^8 (row_ror:8) the two token halves, then over lane^16 and lane^32 the column
+// pairs (e, e+2) and (e, e+1) with the swaps above. A lane with bit 3 set reads Y's token
+// halves in swapped order so that the first exchange pairs equal tokens. The lane ends with
+// tokens kT/2 b3 .. +kT/2-1 of column 4 uu + 2 b4 + b5.
 template <int kT, int kBits>
 __device__ __forceinline__ void refit_sty(const RefitLds<kT, kBits>& L, const f32x4 (&s)[16], int wave, int lane) {
-    constexpr int kC = kT / 4;
+    constexpr int kC = kT / 4, kJ = kT / 2;
     const int uu = 8 * wave + (lane & 7), ro = lane >> 3;
+    const int b3 = ro & 1, b4 = (ro >> 1) & 1, b5 = ro >> 2;
     f32x4 acc[4][kC];
 #pragma unroll
     for (int e = 0; e < 4; ++e)
@@ -192,22 +230,38 @@ __device__ __forceinline__ void refit_sty(const RefitLds<kT, kBits>& L, const f3
     for (int it = 0; it < 16; ++it) {
 #pragma unroll
         for (int h = 0; h < kC; ++h) {
-            const f32x4 yv = L.Y[(8 * it + ro) * kC + h];
+            f32x4 yv;
+            if constexpr (kT == 8) {
+                yv = L.Y[(8 * it + ro) * kC + (h ^ b3)];
+            } else {
+                const f32x2* Y2 = reinterpret_cast<const f32x2*>(L.Y);
+                const f32x2 lo = Y2[(8 * it + ro) * 2 + b3], hi = Y2[(8 * it + ro) * 2 + (b3 ^ 1)];
+                yv = f32x4{lo.x, lo.y, hi.x, hi.y};
+            }
             acc[0][h] = axpy(s[it].x, yv, acc[0][h]);
             acc[1][h] = axpy(s[it].y, yv, acc[1][h]);
             acc[2][h] = axpy(s[it].z, yv, acc[2][h]);
             acc[3][h] = axpy(s[it].w, yv, acc[3][h]);
         }
     }
+    float ra[4][kJ];
 #pragma unroll
     for (int e = 0; e < 4; ++e)
 #pragma unroll
-        for (int h = 0; h < kC; ++h) acc[e][h] = sum_row_lanes(acc[e][h]);
-    if (ro == 0)
+        for (int j = 0; j < kJ; ++j)
+            ra[e][j] = acc[e][0][j] + dpp<kDppRor8>(kT == 8 ? acc[e][kC - 1][j] : acc[e][0][(j + 2) & 3]);
+    float rb[2][kJ];
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
+    for (int e = 0; e < 2; ++e)
 #pragma unroll
-            for (int h = 0; h < kC; ++h) L.W[(4 * uu + e) * kC + h] = acc[e][h];
+        for (int j = 0; j < kJ; ++j) rb[e][j] = add_pair16(ra[e][j], ra[e + 2][j]);
+    float* Wf = reinterpret_cast<float*>(L.W) + (4 * uu + 2 * b4 + b5) * kT + kJ * b3;
+    if constexpr (kT == 8) {
+        *reinterpret_cast<f32x4*>(Wf) = f32x4{add_pair32(rb[0][0], rb[1][0]), add_pair32(rb[0][1], rb[1][1]),
+                                               add_pair32(rb[0][2], rb[1][2]), add_pair32(rb[0][3], rb[1][3])};
+    } else {
+        *reinterpret_cast<f32x2*>(Wf) = f32x2{add_pair32(rb[0][0], rb[1][0]), add_pair32(rb[0][1], rb[1][1])};
+    }
     __syncthreads();
 }
 
