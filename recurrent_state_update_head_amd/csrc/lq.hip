@@ -99,14 +99,16 @@ __device__ __forceinline__ float max_row_lanes(float x) {
 }
 
 // Code of w = x * (qmax / B): round half to even with one fp32 add (the low mantissa bits
-// of w + 1.5 * 2^23 are the integer), clamped to [-qmax, qmax], as a byte (8-bit) or as a
-// two's complement nibble (4-bit).
+// of w + 1.5 * 2^23 are the integer), clamped to [-qmax, qmax]; the code is the low byte
+// (8-bit) or the low nibble (4-bit, two's complement) of the returned bits. The add is not
+// contracted with the product that forms w: the code is decided on w rounded to fp32.
 template <int kBits>
 __device__ __forceinline__ uint32_t lq_code_t(float w) {
+#pragma clang fp contract(off)
     constexpr float kMagic = 12582912.0f;
     constexpr int kQ = kBits == 8 ? 127 : 7;
     const int bits = __float_as_int(w + kMagic);
-    return static_cast<uint32_t>(min(max(bits, 0x4B400000 - kQ), 0x4B400000 + kQ)) & (kBits == 8 ? 0xffu : 0xfu);
+    return static_cast<uint32_t>(min(max(bits, 0x4B400000 - kQ), 0x4B400000 + kQ));
 }
 
 // W -> V: modified Gram-Schmidt over the kT columns in order (wave 0; lane l holds rows
@@ -367,15 +369,15 @@ __device__ __forceinline__ void lq_refit(const RefitLds<kT, kBits>& L, f32x4 (&s
 #pragma unroll
         for (int it = 0; it < 16; ++it)
             L.codes[(8 * it + ro) * Cfg::kCodeStride + uu] =
-                lq_code_t<8>(s[it].x * sc.x) | (lq_code_t<8>(s[it].y * sc.y) << 8) |
-                (lq_code_t<8>(s[it].z * sc.z) << 16) | (lq_code_t<8>(s[it].w * sc.w) << 24);
+                pack_low_bytes(lq_code_t<8>(s[it].x * sc.x), lq_code_t<8>(s[it].y * sc.y),
+                               lq_code_t<8>(s[it].z * sc.z), lq_code_t<8>(s[it].w * sc.w));
     } else {  // four nibbles: half of the row's word for columns 8 (uu / 2) .. +7
         uint16_t* c16 = reinterpret_cast<uint16_t*>(L.codes);
 #pragma unroll
         for (int it = 0; it < 16; ++it)
             c16[(8 * it + ro) * 2 * Cfg::kCodeStride + uu] = static_cast<uint16_t>(
-                lq_code_t<4>(s[it].x * sc.x) | (lq_code_t<4>(s[it].y * sc.y) << 4) |
-                (lq_code_t<4>(s[it].z * sc.z) << 8) | (lq_code_t<4>(s[it].w * sc.w) << 12));
+                (lq_code_t<4>(s[it].x * sc.x) & 0xfu) | ((lq_code_t<4>(s[it].y * sc.y) & 0xfu) << 4) |
+                ((lq_code_t<4>(s[it].z * sc.z) & 0xfu) << 8) | ((lq_code_t<4>(s[it].w * sc.w) & 0xfu) << 12));
     }
     __syncthreads();
     constexpr int kQuads = Cfg::kRowWords / 4;  // 16-byte pieces per row

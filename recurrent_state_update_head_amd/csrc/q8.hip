@@ -300,12 +300,19 @@ __host__ __device__ constexpr int boundary_lds_floats(int wmax, bool per_key) {
 
 // Round-half-to-even of |w| <= 2^22 to an integer with one fp32 add: the sum's
 // low mantissa bits are the integer. The code byte is the low byte of the sum's
-// bits after clamping those bits to the codes of -127 .. 127.
-__device__ __forceinline__ uint32_t code_byte(float w) {
+// bits after clamping those bits to the codes of -127 .. 127. The add is kept apart
+// from the product that forms w (no contraction into an FMA): the code is decided on
+// w rounded to fp32, as the quantizer of a plain state decides it.
+__device__ __forceinline__ uint32_t code_bits(float w) {
+#pragma clang fp contract(off)
     constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23
     const int bits = __float_as_int(w + kMagic);
     const int lo = 0x4B400000 - 127, hi = 0x4B400000 + 127;
-    return static_cast<uint32_t>(min(max(bits, lo), hi)) & 0xffu;
+    return static_cast<uint32_t>(min(max(bits, lo), hi));
+}
+// Codes of a, b, c, d (a in the low byte) as one word.
+__device__ __forceinline__ uint32_t code_word(float a, float b, float c, float d) {
+    return pack_low_bytes(code_bits(a), code_bits(b), code_bits(c), code_bits(d));
 }
 
 // S_W of eq. 4 from the staged window, requantized in place: the record sum is a
@@ -373,8 +380,8 @@ __device__ __forceinline__ void form_and_requantize(const float* KE, const float
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh)
                 Zs[row * kZsStride + 8 * lq + 2 * i + hh] =
-                    code_byte(acc[4 * hh + 0][i] * sc) | (code_byte(acc[4 * hh + 1][i] * sc) << 8) |
-                    (code_byte(acc[4 * hh + 2][i] * sc) << 16) | (code_byte(acc[4 * hh + 3][i] * sc) << 24);
+                    code_word(acc[4 * hh + 0][i] * sc, acc[4 * hh + 1][i] * sc, acc[4 * hh + 2][i] * sc,
+                              acc[4 * hh + 3][i] * sc);
     }
     // the wave's 32 rows (32w .. 32w+31, 4 KiB of codes) leave as whole 128-byte rows
     wave_lds_sync();
@@ -787,7 +794,10 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 // keys, then the lo part): the products are exact and accumulate in fp32, so the
 // result matches an fp32 contraction up to rounding order, at a quarter of the
 // matrix-core time of v_mfma_f32_16x16x4f32. Operand layout (checked on gfx950):
-// lane l supplies A[l%16][8(l/16) + e] and B[8(l/16) + e][l%16], e = 0..7.
+// lane l supplies A[l%16][8(l/16) + e] and B[8(l/16) + e][l%16], e = 0..7. (A
+// v_mfma_f32_16x16x16_bf16 for the lo parts alone would skip the zero half of the
+// second product, but chained onto the same accumulator after the x32 product it
+// gave wrong sums with this toolchain.)
 // Records are staged transposed, as 16-byte words of 8 consecutive records:
 // Kt[b][row] (keys of records 8b .. 8b+7 at a key row) and Ut[part][b][column].
 __global__ __launch_bounds__(kThreads) void q8_boundary_bf16_kernel(
@@ -963,9 +973,8 @@ __global__ __launch_bounds__(kThreads) void q8_boundary_bf16_kernel(
         if (lq == 0) A[vec_off + row] = m;
 #pragma unroll
         for (int ct = 0; ct < 8; ++ct)
-            Zs[row * kZsStride + 4 * ct + lq] = code_byte(acc[ct].x * sc) | (code_byte(acc[ct].y * sc) << 8) |
-                                                (code_byte(acc[ct].z * sc) << 16) |
-                                                (code_byte(acc[ct].w * sc) << 24);
+            Zs[row * kZsStride + 4 * ct + lq] = code_word(acc[ct].x * sc, acc[ct].y * sc, acc[ct].z * sc,
+                                                          acc[ct].w * sc);
     }
     wave_lds_sync();
 #pragma unroll

@@ -130,6 +130,25 @@ def test_lq_validation(lib):
     assert qz(ctypes.byref(d16), GOOD, 2, GOOD, GOOD, ODD, GOOD, GOOD, None) == E_ALIGN
 
 
+def test_lq4_validation(lib):
+    w = lib.gdn_lq4_window
+    w.restype = ctypes.c_int
+    d16 = Dims(2, 3, 128, 128, 1)
+    args = [GOOD] * 14
+    assert w(ctypes.byref(Dims(2, 3, 128, 128, 0)), 16, 0, 1, *args, None) == E_DTYPE  # bf16 only
+    assert w(ctypes.byref(d16), 17, 0, 1, *args, None) == E_RANGE
+    assert w(ctypes.byref(d16), 16, 16, 1, *args, None) == E_RANGE
+    assert w(ctypes.byref(d16), 16, 3, -1, *args, None) == E_RANGE
+    assert w(ctypes.byref(d16), 16, 3, 1, None, *([GOOD] * 13), None) == E_NULL
+    assert w(ctypes.byref(d16), 16, 3, 1, ODD, *([GOOD] * 13), None) == E_ALIGN
+    assert w(ctypes.byref(Dims(0, 3, 128, 128, 1)), 16, 3, 1, *([None] * 14), None) == RSU_OK
+    qz = lib.gdn_lq4_quantize
+    qz.restype = ctypes.c_int
+    assert qz(ctypes.byref(d16), GOOD, 99, *([GOOD] * 5), None) == E_RANGE
+    assert qz(ctypes.byref(d16), GOOD, 2, GOOD, GOOD, ODD, GOOD, GOOD, None) == E_ALIGN
+    assert qz(ctypes.byref(Dims(2, 3, 128, 64, 1)), GOOD, 2, *([GOOD] * 5), None) == E_DIMS
+
+
 def test_copy_validation(lib):
     c = lib.rsu_copy_f32
     c.restype = ctypes.c_int

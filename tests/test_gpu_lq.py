@@ -59,6 +59,30 @@ def test_lq4_windows_small(W, B, H, n_iter):
     _check(run_lq(w, n_iter=n_iter), f"4-bit W={W} B={B} H={H} n_iter={n_iter}")
 
 
+@pytest.mark.parametrize("n_iter0", [0, 3])
+def test_lq4_quantize_start_iterations(n_iter0):
+    w = wl.custom(wl.WORKLOADS[12], B=3, H=11, W=16, steps=0)
+    _check(run_lq(w, n_iter0=n_iter0, steps=0), f"4-bit quantize n_iter0={n_iter0}", boundaries=False)
+
+
+def test_lq4_ragged_batch():
+    """100 heads: the head order's last group of 32 is cut short."""
+    w = wl.custom(wl.WORKLOADS[12], B=10, H=10, W=16, steps=35)
+    _check(run_lq(w, n_iter=1), "4-bit B=10 H=10")
+
+
+def test_lq4_zero_state_gives_zero_tokens_and_payload():
+    m = rsu()
+    S = torch.zeros(1, 2, 128, 128, device=DEV)
+    w = wl.custom(wl.WORKLOADS[12], B=1, H=2, W=16)
+    buf = new_lq_buffers(w)
+    buf["C"].fill_(7.0)
+    buf["Z"].fill_(0x5A)
+    m.gdn_lq4_quantize(S, 4, buf["Z"], buf["B"], buf["C"], buf["Kc"], buf["Uc"])
+    assert not buf["Z"].any() and not buf["B"].any() and not buf["Kc"].any()
+    np.testing.assert_array_equal(buf["C"].cpu().numpy(), np.float32(1e-6))
+
+
 def test_lq4_b256_h48_full_size_sampled():
     w = wl.WORKLOADS[12]
     say(f"[lq] {w.name}: full size, 64 sampled heads, 48 steps")
