@@ -1,0 +1,13 @@
+// Packing of quantized codes, shared by the int8 and LeapQuant requantizers.
+#pragma once
+
+#include <cstdint>
+
+namespace rsu {
+
+// The low bytes of a, b, c, d as one word (a in byte 0): two byte permutes and an or.
+__device__ __forceinline__ uint32_t pack_low_bytes(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+    return __builtin_amdgcn_perm(b, a, 0x0c0c0400u) | __builtin_amdgcn_perm(d, c, 0x04000c0cu);
+}
+
+}  // namespace rsu

@@ -15,6 +15,7 @@
 // (c_i = max(sqrt(mean_j |R_ij|), 1e-6)) and quantized per value channel.
 #include "kernels.hpp"
 #include "rsu_device.hpp"
+#include "codes.hpp"
 
 namespace rsu {
 

@@ -18,6 +18,7 @@
 // two full rows (256 contiguous bytes).
 #include "kernels.hpp"
 #include "rsu_device.hpp"
+#include "codes.hpp"
 
 namespace rsu {
 

@@ -204,11 +204,6 @@ __device__ __forceinline__ float half_wave_max(float x) {
 // Sum over all 64 lanes of a wave (result in every lane).
 __device__ __forceinline__ float wave_sum(float x) { return add_xor32(add_xor16(row16_sum(x))); }
 
-// The low bytes of a, b, c, d as one word (a in byte 0): two byte permutes and an or.
-__device__ __forceinline__ uint32_t pack_low_bytes(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
-    return __builtin_amdgcn_perm(b, a, 0x0c0c0400u) | __builtin_amdgcn_perm(d, c, 0x04000c0cu);
-}
-
 // Sum over the lanes that differ only in lane bits 3..5 (the 8 row lanes of a
 // column group in the fp32-state layout).
 __device__ __forceinline__ float sum_row_lanes(float x) {
