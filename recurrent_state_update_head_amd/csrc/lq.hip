@@ -703,8 +703,10 @@ __global__ __launch_bounds__(kThreads) void lq_boundary_kernel(
     for (int e = 0; e < 8; ++e) {
         const int j = 8 * half + e;
         const size_t at = rec0 + static_cast<size_t>(j < pos ? j : 0) * kD + cc;
-        ucol[e] = j < pos ? Ubuf[at] : 0.f;
-        const uint32_t kb = j < pos ? static_cast<uint32_t>(Kbuf[at]) : 0u;
+        const float ul = Ubuf[at];  // unconditional: at is clamped to slot 0 (in bounds), the value dropped for j >= pos
+        const uint32_t kl = static_cast<uint32_t>(Kbuf[at]);
+        ucol[e] = j < pos ? ul : 0.f;
+        const uint32_t kb = j < pos ? kl : 0u;
         kcol[e >> 1] = (e & 1) ? (kcol[e >> 1] | (kb << 16)) : kb;
     }
     uint4 ktw = {0u, 0u, 0u, 0u};
@@ -1137,10 +1139,43 @@ constexpr int kRow4 = kD / 8;  // 32-bit words of a 4-bit row
 
 __device__ __forceinline__ int lq4_row(int it, int wave, int rl) { return 16 * it + 4 * wave + rl; }
 
-// the 8 signed nibbles of a word, column order
-__device__ __forceinline__ void unpack_nibbles8(uint32_t w, float (&z)[8]) {
+// Payload sweep of the 4-bit steps: the lane's 8 code words (rows lq4_row(it, wave, l >> 4),
+// value columns 8 (l & 15) .. +7) against the two read vectors, whose rowv entries are the read
+// vectors times 1/16. A code is read as the signed high nibble of a byte, i.e. as 16 z with one
+// sign-extending byte conversion (the even columns from w << 4, the odd ones from w), so the
+// products equal z times the unscaled entries exactly. The 4 row lanes l, l^16, l^32, l^48 are
+// summed by two lane swaps that halve the live values: lanes with bit 4 set keep columns 4..7 of
+// the eight, lanes with bit 5 set the upper pair of their four. Each lane stores {p1, p2} of its two
+// columns 4 b4 + 2 b5 + (0, 1) into red_w (the wave's [128] partials).
+__device__ __forceinline__ void sweep4(const uint32_t (&zw)[8], const f32x2* rowv, int wave, int lane,
+                                       f32x2* red_w) {
+    const int c16 = lane & 15, rl = lane >> 4;
+    float p1[8], p2[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) z[e] = static_cast<float>(static_cast<int>(w << (28 - 4 * e)) >> 28);
+    for (int e = 0; e < 8; ++e) p1[e] = p2[e] = 0.f;
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+        const f32x2 rv = rowv[lq4_row(it, wave, rl)];
+        const uint32_t ev = (zw[it] << 4) & 0xF0F0F0F0u, od = zw[it] & 0xF0F0F0F0u;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float ze = static_cast<float>(static_cast<int8_t>(ev >> (8 * j)));
+            const float zo = static_cast<float>(static_cast<int8_t>(od >> (8 * j)));
+            p1[2 * j] = fmaf(ze, rv.x, p1[2 * j]);
+            p2[2 * j] = fmaf(ze, rv.y, p2[2 * j]);
+            p1[2 * j + 1] = fmaf(zo, rv.x, p1[2 * j + 1]);
+            p2[2 * j + 1] = fmaf(zo, rv.y, p2[2 * j + 1]);
+        }
+    }
+    float q1[4], q2[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        q1[e] = add_pair16(p1[e], p1[e + 4]);
+        q2[e] = add_pair16(p2[e], p2[e + 4]);
+    }
+    const int b4 = (lane >> 4) & 1, b5 = lane >> 5;
+    *reinterpret_cast<f32x4*>(red_w + 8 * c16 + 4 * b4 + 2 * b5) =
+        f32x4{add_pair32(q1[0], q1[2]), add_pair32(q2[0], q2[2]), add_pair32(q1[1], q1[3]), add_pair32(q2[1], q2[3])};
 }
 
 __global__ __launch_bounds__(kThreads) void lq4_step_kernel(
@@ -1176,7 +1211,8 @@ __global__ __launch_bounds__(kThreads) void lq4_step_kernel(
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
         const int j = 8 * half + e;
-        ucol[e] = j < pos ? Ubuf[rec0 + static_cast<size_t>(j) * kD + cc] : 0.f;
+        const float ul = Ubuf[rec0 + static_cast<size_t>(j < pos ? j : 0) * kD + cc];  // slot clamped to 0: in bounds, no branch
+        ucol[e] = j < pos ? ul : 0.f;
     }
     uint4 ktw = {0u, 0u, 0u, 0u};
     if (first) ktw = *reinterpret_cast<const uint4*>(Kc + tok0 + (grp & 7) * kD + 8 * ch);
@@ -1234,35 +1270,14 @@ __global__ __launch_bounds__(kThreads) void lq4_step_kernel(
         cq = row16_sum(cq);
         if (ch == 0) ctok[grp] = f32x2{ck, cq};
         const float c0 = cr * Gall * gr;  // c_r Gamma_{1:l} at row r
-        rowv[cc] = f32x2{c0 * kr, c0 * qr};
+        rowv[cc] = f32x2{c0 * kr, c0 * qr} * 0.0625f;  // times 1/16: see sweep4
         const float kq = wave_sum(kr * qr);
         if (lane == 0) kq_part[wave] = kq;
     }
     __syncthreads();
 
     // ---- payload sweep over the lane's 8 words; the 4 row lanes, then the waves
-    float p1[8], p2[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) p1[e] = p2[e] = 0.f;
-#pragma unroll
-    for (int it = 0; it < 8; ++it) {
-        const f32x2 rv = rowv[lq4_row(it, wave, rl)];
-        float z[8];
-        unpack_nibbles8(zw[it], z);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            p1[e] += z[e] * rv.x;
-            p2[e] += z[e] * rv.y;
-        }
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        p1[e] = add_xor32(add_xor16(p1[e]));
-        p2[e] = add_xor32(add_xor16(p2[e]));
-    }
-    if (rl == 0)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) red[wave][8 * c16 + e] = f32x2{p1[e], p2[e]};
+    sweep4(zw, rowv, wave, lane, red[wave]);
     // record and token terms of column cc
     f32x2 rp = {0.f, 0.f};
 #pragma unroll
@@ -1349,8 +1364,10 @@ __global__ __launch_bounds__(kThreads) void lq4_boundary_kernel(
     for (int e = 0; e < 8; ++e) {
         const int j = 8 * half + e;
         const size_t at = rec0 + static_cast<size_t>(j < pos ? j : 0) * kD + cc;
-        ucol[e] = j < pos ? Ubuf[at] : 0.f;
-        const uint32_t kb = j < pos ? static_cast<uint32_t>(Kbuf[at]) : 0u;
+        const float ul = Ubuf[at];  // unconditional: at is clamped to slot 0 (in bounds), the value dropped for j >= pos
+        const uint32_t kl = static_cast<uint32_t>(Kbuf[at]);
+        ucol[e] = j < pos ? ul : 0.f;
+        const uint32_t kb = j < pos ? kl : 0u;
         kcol[e >> 1] = (e & 1) ? (kcol[e >> 1] | (kb << 16)) : kb;
     }
     uint4 ktw = {0u, 0u, 0u, 0u};
@@ -1411,7 +1428,7 @@ __global__ __launch_bounds__(kThreads) void lq4_boundary_kernel(
         cq = row16_sum(cq);
         if (ch == 0) ctok[grp] = f32x2{ck, cq};
         const float c0 = cr * gam_all;
-        rowv[cc] = f32x2{c0 * kr, c0 * qr};
+        rowv[cc] = f32x2{c0 * kr, c0 * qr} * 0.0625f;  // times 1/16: see sweep4
         zcoef[cc] = c0;
         const float kq = wave_sum(kr * qr);
         if (lane == 0) kq_part[wave] = kq;
@@ -1434,28 +1451,7 @@ __global__ __launch_bounds__(kThreads) void lq4_boundary_kernel(
     __syncthreads();
 
     // ---- payload sweep; record and token terms per column; scaled records staged for the MFMA
-    float p1[8], p2[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) p1[e] = p2[e] = 0.f;
-#pragma unroll
-    for (int it = 0; it < 8; ++it) {
-        const f32x2 rv = rowv[lq4_row(it, wave, rl)];
-        float z[8];
-        unpack_nibbles8(zw[it], z);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            p1[e] += z[e] * rv.x;
-            p2[e] += z[e] * rv.y;
-        }
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        p1[e] = add_xor32(add_xor16(p1[e]));
-        p2[e] = add_xor32(add_xor16(p2[e]));
-    }
-    if (rl == 0)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) red[wave * kD + 8 * c16 + e] = f32x2{p1[e], p2[e]};
+    sweep4(zw, rowv, wave, lane, red + wave * kD);
     f32x2 rp = {0.f, 0.f};
     u32x4 part[3];
 #pragma unroll

@@ -836,8 +836,10 @@ __global__ __launch_bounds__(kThreads) void q8_boundary_bf16_kernel(
     for (int e = 0; e < 8; ++e) {
         const int j = 8 * half + e;
         const size_t at = rec0 + static_cast<size_t>(j < pos ? j : 0) * kD + cc;
-        ucol[e] = j < pos ? Ubuf[at] : 0.f;
-        const uint32_t kb = j < pos ? static_cast<uint32_t>(Kbuf[at]) : 0u;
+        const float ul = Ubuf[at];  // unconditional: at is clamped to slot 0 (in bounds), the value dropped for j >= pos
+        const uint32_t kl = static_cast<uint32_t>(Kbuf[at]);
+        ucol[e] = j < pos ? ul : 0.f;
+        const uint32_t kb = j < pos ? kl : 0u;
         kcol[e >> 1] = (e & 1) ? (kcol[e >> 1] | (kb << 16)) : kb;
     }
     const float g_lane = lane < pos ? Gbuf[static_cast<size_t>(h) * W + lane] : 1.f;
