@@ -21,6 +21,9 @@ FLAGS = [
     "-Wall",
     # no packed fp32 instructions anywhere in the device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in ordinary VGPRs: the LeapQuant boundaries need no AGPR block
+    # beside the refit's registers, which keeps three of their workgroups on a CU
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-I", os.path.join(ROOT, "include"),
 ]
 

@@ -623,22 +623,50 @@ __global__ __launch_bounds__(kThreads) void lq_step_kernel(
 // staged transposed for the bf16-split MFMA), with the payload terms scaled by B and c
 // and the token pairs added; then S_W is formed on the matrix cores (payload init, the
 // records' two bf16 MFMAs per tile, the tokens' one fp32 MFMA per tile), passed through
-// LDS into the refit's register layout, and refitted. The first kD * kD floats of
-// dynamic LDS are one region used three times: the step and the contraction operands,
-// then the state on its way between the two register layouts, then the refit's arrays.
-// After it lie W (the old Ut, the refit's start) and the old payload's B / 127.
+// LDS into the refit's register layout, and refitted. The first floats of dynamic LDS are
+// one region used three times: the step and the contraction operands, then the state on
+// its way between the two register layouts (half of it at a time), then the refit's arrays.
+// After it lie W (the old Ut, the refit's start) and the old payload's B / 127. The region
+// is sized to the largest of the three (44 KB of LDS in all), so that three workgroups
+// share a CU.
 constexpr int kZsStride = kD / 4 + 1;
 // floats of the step-phase region: Kt (4 KB), Ut (12 KB), Zs, Ktok, Utok, red, recp
 constexpr int kStepFloats = 2 * kD * 4 + 3 * 2 * kD * 4 + kD * kZsStride + 2 * kTok * kD + 4 * kD * 2 + kD * 2;
-constexpr int kLqBoundaryFloats = kD * kD + 4 * kD + kD;
-static_assert(kStepFloats <= kD * kD, "the step-phase arrays must lie inside the shared region");
-static_assert(RefitCfg<4, 8>::kRegionFloats <= kD * kD, "the refit's arrays must lie inside the shared region");
+constexpr int cmax3(int a, int b, int c) { return a > b ? (a > c ? a : c) : (b > c ? b : c); }
+constexpr int kTransitFloats = kD * kD / 2;  // half the state in transit
+constexpr int kLqRegionFloats = cmax3(kStepFloats, kTransitFloats, RefitCfg<4, 8>::kRegionFloats);
+constexpr int kLqBoundaryFloats = kLqRegionFloats + 4 * kD + kD;
+static_assert(kLqRegionFloats % 4 == 0, "W after the region must be 16-byte aligned");
 
 // The state in transit: row r in 16-byte units, unit u stored at u ^ f(r) with
 // f(r) = (r & 7) ^ ((r & 1) << 3), so that the MFMA-layout writes and the refit-layout
 // reads both spread over the banks.
 __device__ __forceinline__ f32x4& state_unit(float* base, int r, int u) {
     return reinterpret_cast<f32x4*>(base + r * kD)[u ^ ((r & 7) ^ ((r & 1) << 3))];
+}
+
+// S from the MFMA result layout (wave w holds rows 32w .. 32w+31: acc[a][ct] is row
+// 16(2w + a) + (l & 15), columns 16ct + 4(l >> 4) .. +3) to the refit's layout (s[it] is row
+// 8it + (l >> 3), columns 4uu .. +3), through a buffer of half the state at base: rows
+// 0 .. 63 (written by waves 0 and 1) first, then rows 64 .. 127. Every thread calls it.
+__device__ __forceinline__ void state_to_refit(float* base, const f32x4 (&acc)[2][8], f32x4 (&s)[16], int wave,
+                                               int lane) {
+    const int lr = lane & 15, lq = lane >> 4;
+    const int uu = 8 * wave + (lane & 7), rr = lane >> 3;
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+        if ((wave >> 1) == hf) {
+#pragma unroll
+            for (int a = 0; a < 2; ++a)
+#pragma unroll
+                for (int ct = 0; ct < 8; ++ct)
+                    state_unit(base, 16 * (2 * (wave & 1) + a) + lr, 4 * ct + lq) = acc[a][ct];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int it = 0; it < 8; ++it) s[8 * hf + it] = state_unit(base, 8 * it + rr, uu);
+        __syncthreads();
+    }
 }
 
 __device__ __forceinline__ void split3_bf16(float x, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
@@ -678,8 +706,8 @@ __global__ __launch_bounds__(kThreads) void lq_boundary_kernel(
     f32x2* red = reinterpret_cast<f32x2*>(Utok + kTok * kD);       // [4][128]
     f32x2* recp = red + 4 * kD;                                     // [128]
     // refit views (its region overlaps every step-phase array above; W and bscs do not)
-    const RefitLds<4, 8> L(dyn_lds, dyn_lds + kD * kD);
-    float* bscs = dyn_lds + kD * kD + 4 * kD;   // B / 127 of the old payload
+    const RefitLds<4, 8> L(dyn_lds, dyn_lds + kLqRegionFloats);
+    float* bscs = dyn_lds + kLqRegionFloats + 4 * kD;   // B / 127 of the old payload
 
     const int h = head_of_block(blockIdx.x, gridDim.x), tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
@@ -871,21 +899,9 @@ __global__ __launch_bounds__(kThreads) void lq_boundary_kernel(
             acc[a][ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(Utok[lq * kD + col], bk, acc[a][ct], 0, 0, 0);
         }
     }
-    __syncthreads();  // every read of the step-phase arrays is done: the region holds S
-#pragma unroll
-    for (int a = 0; a < 2; ++a) {
-        const int row = 16 * (2 * wave + a) + lr;
-#pragma unroll
-        for (int ct = 0; ct < 8; ++ct) state_unit(dyn_lds, row, 4 * ct + lq) = acc[a][ct];
-    }
-    __syncthreads();
+    __syncthreads();  // every read of the step-phase arrays is done: the region holds S in halves
     f32x4 s[16];
-    {
-        const int uu = 8 * wave + (lane & 7), rr = lane >> 3;
-#pragma unroll
-        for (int it = 0; it < 16; ++it) s[it] = state_unit(dyn_lds, 8 * it + rr, uu);
-    }
-    __syncthreads();  // the region is free for the refit's arrays
+    state_to_refit(dyn_lds, acc, s, wave, lane);  // ends with a barrier: the region is free for the refit
     lq_refit(L, s, n_iter, tid, Zh, Bcol + vec_off, Csm + vec_off, Kc + tok0, Uc + tok0);
 }
 
@@ -905,6 +921,7 @@ constexpr int kKdaRec = 16;
 // token values [4][128], red [4][128] x 2
 constexpr int kKdaStepFloats = 3 * kKdaRec * kD + kD * kZsStride + 2 * kTok * kD + 4 * kD * 2;
 static_assert(kKdaStepFloats <= kD * kD, "the step-phase arrays must lie inside the shared region");
+constexpr int kLqKdaBoundaryFloats = kD * kD + 4 * kD + kD;
 
 __global__ __launch_bounds__(kThreads) void lq_boundary_kda_kernel(
     int W, int pos, int n_iter, int8_t* __restrict__ Z, float* __restrict__ Bcol, float* __restrict__ Csm,
@@ -929,6 +946,7 @@ __global__ __launch_bounds__(kThreads) void lq_boundary_kda_kernel(
     f32x2* red = reinterpret_cast<f32x2*>(Ut4 + kTok * kD);        // [4][128]
     const RefitLds<4, 8> L(dyn_lds, dyn_lds + kD * kD);
     float* bscs = dyn_lds + kD * kD + 4 * kD;                       // B / 127 of the old payload
+    // (the whole state passes through LDS at once here: the step-phase arrays take 48.5 KB)
 
     const int h = head_of_block(blockIdx.x, gridDim.x), tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
@@ -1308,13 +1326,13 @@ __global__ __launch_bounds__(kThreads) void lq4_step_kernel(
 // the 8-bit boundary (payload init from the staged nibbles, the records' two bf16 MFMAs per
 // tile, the 8 tokens' two fp32 MFMAs), through LDS into the refit's layout, and the 8-token
 // refit with 4-bit codes. One region of dynamic LDS serves the step arrays, the state in
-// transit and the refit's arrays in turn; after it lie W (the old Ut, 8 tokens) and the old
-// payload's B / 7.
+// transit (half of it at a time) and the refit's arrays in turn; after it lie W (the old Ut,
+// 8 tokens) and the old payload's B / 7: 47 KB in all, three workgroups per CU.
 constexpr int kZs4Stride = kRow4 + 1;
 constexpr int kStep4Floats = 2 * kD * 4 + 3 * 2 * kD * 4 + kD * kZs4Stride + 2 * kTok4 * kD + 4 * kD * 2 + kD * 2;
-constexpr int kLq4BoundaryFloats = kD * kD + kTok4 * kD + kD;
-static_assert(kStep4Floats <= kD * kD, "the step-phase arrays must lie inside the shared region");
-static_assert(RefitCfg<8, 4>::kRegionFloats <= kD * kD, "the refit's arrays must lie inside the shared region");
+constexpr int kLq4RegionFloats = cmax3(kStep4Floats, kTransitFloats, RefitCfg<8, 4>::kRegionFloats);
+constexpr int kLq4BoundaryFloats = kLq4RegionFloats + kTok4 * kD + kD;
+static_assert(kLq4RegionFloats % 4 == 0, "W after the region must be 16-byte aligned");
 
 __global__ __launch_bounds__(kThreads) void lq4_boundary_kernel(
     int W, int pos, int n_iter, uint32_t* __restrict__ Z, float* __restrict__ Bcol, float* __restrict__ Csm,
@@ -1338,8 +1356,8 @@ __global__ __launch_bounds__(kThreads) void lq4_boundary_kernel(
     float* Utok = Ktok + kTok4 * kD;                                // [8][128], scaled by Gamma_{1:W}
     f32x2* red = reinterpret_cast<f32x2*>(Utok + kTok4 * kD);      // [4][128]
     f32x2* recp = red + 4 * kD;                                     // [128]
-    const RefitLds<kTok4, 4> L(dyn_lds, dyn_lds + kD * kD);
-    float* bscs = dyn_lds + kD * kD + kTok4 * kD;                   // B / 7 of the old payload
+    const RefitLds<kTok4, 4> L(dyn_lds, dyn_lds + kLq4RegionFloats);
+    float* bscs = dyn_lds + kLq4RegionFloats + kTok4 * kD;          // B / 7 of the old payload
 
     const int h = head_of_block(blockIdx.x, gridDim.x), tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
@@ -1525,21 +1543,9 @@ __global__ __launch_bounds__(kThreads) void lq4_boundary_kernel(
             acc[a][ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(Utok[(4 + lq) * kD + col], bk1, acc[a][ct], 0, 0, 0);
         }
     }
-    __syncthreads();  // every read of the step-phase arrays is done: the region holds S
-#pragma unroll
-    for (int a = 0; a < 2; ++a) {
-        const int row = 16 * (2 * wave + a) + lr;
-#pragma unroll
-        for (int ct = 0; ct < 8; ++ct) state_unit(dyn_lds, row, 4 * ct + lq) = acc[a][ct];
-    }
-    __syncthreads();
+    __syncthreads();  // every read of the step-phase arrays is done: the region holds S in halves
     f32x4 s[16];
-    {
-        const int uu = 8 * wave + (lane & 7), rr = lane >> 3;
-#pragma unroll
-        for (int it = 0; it < 16; ++it) s[it] = state_unit(dyn_lds, 8 * it + rr, uu);
-    }
-    __syncthreads();  // the region is free for the refit's arrays
+    state_to_refit(dyn_lds, acc, s, wave, lane);  // ends with a barrier: the region is free for the refit
     lq_refit(L, s, n_iter, tid, Zh, Bcol + vec_off, Csm + vec_off, Kc + tok0, Uc + tok0);
 }
 
@@ -1564,10 +1570,10 @@ hipError_t launch_lq_quantize(int heads, const float* S, int n_iter, int8_t* Z, 
 hipError_t launch_lq_window(const StepArgs& a, const LqArgs& w, bool per_key, hipStream_t stream) {
     if (w.pos == w.W - 1) {
         static const hipError_t attr_gdn = set_lds(reinterpret_cast<const void*>(lq_boundary_kernel), kLqBoundaryFloats);
-        static const hipError_t attr_kda = set_lds(reinterpret_cast<const void*>(lq_boundary_kda_kernel), kLqBoundaryFloats);
+        static const hipError_t attr_kda = set_lds(reinterpret_cast<const void*>(lq_boundary_kda_kernel), kLqKdaBoundaryFloats);
         if (hipError_t e = per_key ? attr_kda : attr_gdn) return e;
         if (per_key)
-            hipLaunchKernelGGL(lq_boundary_kda_kernel, dim3(a.heads), dim3(kThreads), sizeof(float) * kLqBoundaryFloats,
+            hipLaunchKernelGGL(lq_boundary_kda_kernel, dim3(a.heads), dim3(kThreads), sizeof(float) * kLqKdaBoundaryFloats,
                                stream, w.W, w.pos, w.n_iter, w.Z, w.B, w.C, static_cast<half_t*>(w.Kc),
                                static_cast<half_t*>(w.Uc), static_cast<const bf16_t*>(w.Kbuf), w.Ubuf, w.Gbuf,
                                static_cast<const bf16_t*>(a.q), static_cast<const bf16_t*>(a.k),
