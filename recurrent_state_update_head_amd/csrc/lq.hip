@@ -645,29 +645,37 @@ __device__ __forceinline__ f32x4& state_unit(float* base, int r, int u) {
     return reinterpret_cast<f32x4*>(base + r * kD)[u ^ ((r & 7) ^ ((r & 1) << 3))];
 }
 
-// S from the MFMA result layout (wave w holds rows 32w .. 32w+31: acc[a][ct] is row
-// 16(2w + a) + (l & 15), columns 16ct + 4(l >> 4) .. +3) to the refit's layout (s[it] is row
-// 8it + (l >> 3), columns 4uu .. +3), through a buffer of half the state at base: rows
-// 0 .. 63 (written by waves 0 and 1) first, then rows 64 .. 127. Every thread calls it.
-__device__ __forceinline__ void state_to_refit(float* base, const f32x4 (&acc)[2][8], f32x4 (&s)[16], int wave,
-                                               int lane) {
-    const int lr = lane & 15, lq = lane >> 4;
+// S from an MFMA result layout, in which wave w holds rows 32w .. 32w+31, to the refit's
+// layout (s[it] is row 8it + (l >> 3), columns 4uu .. +3), through a buffer of half the
+// state at base: rows 0 .. 63 (written by waves 0 and 1) first, then rows 64 .. 127.
+// write(base, r0) stores the wave's 32 rows as rows r0 .. r0+31 of the buffer. Every thread
+// calls it; it ends with a barrier.
+template <typename Write>
+__device__ __forceinline__ void state_to_refit(float* base, Write write, f32x4 (&s)[16], int wave, int lane) {
     const int uu = 8 * wave + (lane & 7), rr = lane >> 3;
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
-        if ((wave >> 1) == hf) {
-#pragma unroll
-            for (int a = 0; a < 2; ++a)
-#pragma unroll
-                for (int ct = 0; ct < 8; ++ct)
-                    state_unit(base, 16 * (2 * (wave & 1) + a) + lr, 4 * ct + lq) = acc[a][ct];
-        }
+        if ((wave >> 1) == hf) write(base, 32 * (wave & 1));
         __syncthreads();
 #pragma unroll
         for (int it = 0; it < 8; ++it) s[8 * hf + it] = state_unit(base, 8 * it + rr, uu);
         __syncthreads();
     }
 }
+
+// The writer of the GDN boundaries' layout: acc[a][ct] is row 16(2w + a) + (l & 15),
+// columns 16ct + 4(l >> 4) .. +3.
+struct TileRows {
+    const f32x4 (&acc)[2][8];
+    int lane;
+    __device__ void operator()(float* base, int r0) const {
+        const int lr = lane & 15, lq = lane >> 4;
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+            for (int ct = 0; ct < 8; ++ct) state_unit(base, r0 + 16 * a + lr, 4 * ct + lq) = acc[a][ct];
+    }
+};
 
 __device__ __forceinline__ void split3_bf16(float x, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
     const __bf16 a = static_cast<__bf16>(x);
@@ -901,7 +909,7 @@ __global__ __launch_bounds__(kThreads) void lq_boundary_kernel(
     }
     __syncthreads();  // every read of the step-phase arrays is done: the region holds S in halves
     f32x4 s[16];
-    state_to_refit(dyn_lds, acc, s, wave, lane);  // ends with a barrier: the region is free for the refit
+    state_to_refit(dyn_lds, TileRows{acc, lane}, s, wave, lane);  // then the region is free for the refit
     lq_refit(L, s, n_iter, tid, Zh, Bcol + vec_off, Csm + vec_off, Kc + tok0, Uc + tok0);
 }
 
@@ -920,8 +928,13 @@ constexpr int kKdaRec = 16;
 // floats of the step-phase arrays: KE, Us, Gs [16][128], Zs, decayed token keys and
 // token values [4][128], red [4][128] x 2
 constexpr int kKdaStepFloats = 3 * kKdaRec * kD + kD * kZsStride + 2 * kTok * kD + 4 * kD * 2;
-static_assert(kKdaStepFloats <= kD * kD, "the step-phase arrays must lie inside the shared region");
-constexpr int kLqKdaBoundaryFloats = kD * kD + 4 * kD + kD;
+// W (the refit's start) is written once the step arrays are dead, right after the refit's
+// region; B / 127 of the old payload follows the step arrays. 50 KB in all: three workgroups
+// per CU.
+constexpr int kKdaWOffset = RefitCfg<4, 8>::kRegionFloats;
+static_assert(kKdaWOffset >= kTransitFloats && kKdaWOffset + 4 * kD <= kKdaStepFloats,
+              "W must lie inside the step region, clear of the half state and the refit's arrays");
+constexpr int kLqKdaBoundaryFloats = kKdaStepFloats + kD;
 
 __global__ __launch_bounds__(kThreads) void lq_boundary_kda_kernel(
     int W, int pos, int n_iter, int8_t* __restrict__ Z, float* __restrict__ Bcol, float* __restrict__ Csm,
@@ -944,9 +957,8 @@ __global__ __launch_bounds__(kThreads) void lq_boundary_kda_kernel(
     float* Kt4 = reinterpret_cast<float*>(Zs + kD * kZsStride);    // [4][128] Gamma_{1:W} Kt
     float* Ut4 = Kt4 + kTok * kD;                                   // [4][128] Ut
     f32x2* red = reinterpret_cast<f32x2*>(Ut4 + kTok * kD);        // [4][128]
-    const RefitLds<4, 8> L(dyn_lds, dyn_lds + kD * kD);
-    float* bscs = dyn_lds + kD * kD + 4 * kD;                       // B / 127 of the old payload
-    // (the whole state passes through LDS at once here: the step-phase arrays take 48.5 KB)
+    const RefitLds<4, 8> L(dyn_lds, dyn_lds + kKdaWOffset);
+    float* bscs = dyn_lds + kKdaStepFloats;                         // B / 127 of the old payload
 
     const int h = head_of_block(blockIdx.x, gridDim.x), tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
@@ -1008,8 +1020,6 @@ __global__ __launch_bounds__(kThreads) void lq_boundary_kda_kernel(
     } else {
 #pragma unroll
         for (int t = 0; t < kTok; ++t) Ut4[t * kD + r] = static_cast<float>(tokv[t]);
-        L.W[r] = f32x4{static_cast<float>(tokv[0]), static_cast<float>(tokv[1]), static_cast<float>(tokv[2]),
-                       static_cast<float>(tokv[3])};
         bscs[r] = bcc * (1.f / 127.f);
     }
     __syncthreads();
@@ -1122,25 +1132,23 @@ __global__ __launch_bounds__(kThreads) void lq_boundary_kda_kernel(
         for (int ct = 0; ct < 8; ++ct)
             acc[a][ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(utk[ct / 4][ct % 4], kb, acc[a][ct], 0, 0, 0);
     }
-    __syncthreads();  // every read of the step-phase arrays is done: the region holds S
+    __syncthreads();  // every read of the step-phase arrays is done: the region holds S in halves, and W
+    if (!first)
+        L.W[r] = f32x4{static_cast<float>(tokv[0]), static_cast<float>(tokv[1]), static_cast<float>(tokv[2]),
+                       static_cast<float>(tokv[3])};
+    // this layout: acc[a][ct][i] is row 16(2w + a) + (l & 15), column 32(l >> 4) + 8i + ct
+    auto write = [&](float* base, int r0) {
 #pragma unroll
-    for (int a = 0; a < 2; ++a) {
-        const int row = 16 * (2 * wave + a) + lr;
+        for (int a = 0; a < 2; ++a)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int hh = 0; hh < 2; ++hh)
-                state_unit(dyn_lds, row, 8 * lq + 2 * i + hh) =
-                    f32x4{acc[a][4 * hh][i], acc[a][4 * hh + 1][i], acc[a][4 * hh + 2][i], acc[a][4 * hh + 3][i]};
-    }
-    __syncthreads();
+                for (int hh = 0; hh < 2; ++hh)
+                    state_unit(base, r0 + 16 * a + lr, 8 * lq + 2 * i + hh) =
+                        f32x4{acc[a][4 * hh][i], acc[a][4 * hh + 1][i], acc[a][4 * hh + 2][i], acc[a][4 * hh + 3][i]};
+    };
     f32x4 s[16];
-    {
-        const int uu = 8 * wave + (lane & 7), rr = lane >> 3;
-#pragma unroll
-        for (int it = 0; it < 16; ++it) s[it] = state_unit(dyn_lds, 8 * it + rr, uu);
-    }
-    __syncthreads();  // the region is free for the refit's arrays
+    state_to_refit(dyn_lds, write, s, wave, lane);  // then the region is free for the refit
     lq_refit(L, s, n_iter, tid, Zh, Bcol + vec_off, Csm + vec_off, Kc + tok0, Uc + tok0);
 }
 
@@ -1545,7 +1553,7 @@ __global__ __launch_bounds__(kThreads) void lq4_boundary_kernel(
     }
     __syncthreads();  // every read of the step-phase arrays is done: the region holds S in halves
     f32x4 s[16];
-    state_to_refit(dyn_lds, acc, s, wave, lane);  // ends with a barrier: the region is free for the refit
+    state_to_refit(dyn_lds, TileRows{acc, lane}, s, wave, lane);  // then the region is free for the refit
     lq_refit(L, s, n_iter, tid, Zh, Bcol + vec_off, Csm + vec_off, Kc + tok0, Uc + tok0);
 }
 
