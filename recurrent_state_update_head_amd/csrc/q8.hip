@@ -290,14 +290,13 @@ __global__ __launch_bounds__(kThreads) void q8_step_kernel(
 
 // Dynamic LDS of the boundary step, in 32-bit words, for windows of up to kWmax records:
 // KE[kWmax][128] (record keys, turned in place into the decayed keys E; zero after the
-// last record), Us[kWmax][128] (record corrections; zero after the last), Gs[kWmax][128]
-// (record gates, KDA only) and Zs[128][kZsStride] (the codes re-laid out for the
-// MFMA tiles, then the new codes on their way out; the padded row stride spreads the
-// LDS banks).
+// last record), Us[kWmax][128] (record corrections; zero after the last) and
+// Zs[128][kZsStride] (the codes re-laid out for the MFMA tiles, then the new codes on
+// their way out; the padded row stride spreads the LDS banks). Per-key record gates are
+// not staged: each key row's gates go from HBM straight into the registers of the thread
+// that walks that row.
 constexpr int kZsStride = kD / 4 + 1;
-__host__ __device__ constexpr int boundary_lds_floats(int wmax, bool per_key) {
-    return (2 + (per_key ? 1 : 0)) * wmax * kD + kD * kZsStride;
-}
+__host__ __device__ constexpr int boundary_lds_floats(int wmax) { return 2 * wmax * kD + kD * kZsStride; }
 
 // Round-half-to-even of |w| <= 2^22 to an integer with one fp32 add: the sum's
 // low mantissa bits are the integer. The code byte is the low byte of the sum's
@@ -419,8 +418,7 @@ __global__ __launch_bounds__(kThreads) void q8_boundary_kernel(
     const size_t rec0 = static_cast<size_t>(h) * W * kD;
     float* KE = dyn_lds;
     float* Us = KE + kWmax * kD;
-    float* Gs = Us + kWmax * kD;
-    uint32_t* Zs = reinterpret_cast<uint32_t*>(Gs + (kPerKey ? kWmax * kD : 0));
+    uint32_t* Zs = reinterpret_cast<uint32_t*>(Us + kWmax * kD);
 
     // ---- every load of the step is issued here: records and inputs first, then the
     // codes, so that the key-side preparation below only waits for the former while
@@ -430,12 +428,17 @@ __global__ __launch_bounds__(kThreads) void q8_boundary_kernel(
     Stager<float, kMaxW * kD> su;
     sk.load(Kbuf + rec0, pos * kD, tid);
     su.load(Ubuf + rec0, pos * kD, tid);
-    Stager<float, kPerKey ? kMaxW * kD : 8> sg;
-    float g_rec = 1.f;
-    if constexpr (kPerKey) sg.load(Gbuf + rec0, pos * kD, tid);
-    else if (tid < pos) g_rec = Gbuf[static_cast<size_t>(h) * W + tid];
     const int r = tid & (kD - 1);
     const bool first = tid < kD;
+    float g_rec = 1.f;
+    float grow[kPerKey ? kWmax : 1];  // per-key gates of key row r, records 0 .. kWmax-1 (slot clamped)
+    if constexpr (kPerKey) {
+        if (first)
+#pragma unroll
+            for (int j = 0; j < kWmax; ++j) grow[j] = Gbuf[rec0 + static_cast<size_t>(j < pos ? j : 0) * kD + r];
+    } else if (tid < pos) {
+        g_rec = Gbuf[static_cast<size_t>(h) * W + tid];
+    }
     const float kr = load_in(k, vec_off + r), qr = load_in(q, vec_off + r);
     const float gr = kPerKey ? gate[vec_off + r] : gate[h];
     const float ar = A[vec_off + r];
@@ -461,7 +464,6 @@ __global__ __launch_bounds__(kThreads) void q8_boundary_kernel(
     }
     sk.store(KE, tid);
     su.store(Us, tid);
-    if constexpr (kPerKey) sg.store(Gs, tid);
     for (int i = W * kD + tid; i < kWmax * kD; i += kThreads) Us[i] = 0.f;  // rows after the last record
     __syncthreads();
 
@@ -474,9 +476,12 @@ __global__ __launch_bounds__(kThreads) void q8_boundary_kernel(
         // thread r < 128 walks the records of key row r backwards
         G = 1.f;
         if (first) {
-            for (int j = pos - 1; j >= 0; --j) {
-                KE[j * kD + r] *= G * gr;
-                G *= Gs[j * kD + r];
+#pragma unroll
+            for (int j = kWmax - 1; j >= 0; --j) {
+                if (j < pos) {
+                    KE[j * kD + r] *= G * gr;
+                    G *= grow[j];
+                }
             }
         }
     }
@@ -729,8 +734,7 @@ __global__ __launch_bounds__(kThreads) void q8_requant_kernel(int nrec, int rec_
     __shared__ float zcoef[kD];
     float* KE = dyn_lds;
     float* Us = KE + kRwkv7Rec * kD;
-    float* Gs = Us + kRwkv7Rec * kD;
-    uint32_t* Zs = reinterpret_cast<uint32_t*>(Gs + kRwkv7Rec * kD);
+    uint32_t* Zs = reinterpret_cast<uint32_t*>(Us + kRwkv7Rec * kD);
 
     const int h = head_of_block(blockIdx.x, gridDim.x), tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
@@ -743,10 +747,12 @@ __global__ __launch_bounds__(kThreads) void q8_requant_kernel(int nrec, int rec_
 
     Stager<T, kRwkv7Rec * kD> sk;
     Stager<float, kRwkv7Rec * kD> su;
-    Stager<float, kRwkv7Rec * kD> sg;
     sk.load(Kbuf + rec0, nrec * kD, tid);
     su.load(Ubuf + rec0, nrec * kD, tid);
-    sg.load(Gbuf + rec0, nrec * kD, tid);
+    float grow[kRwkv7Rec];  // the gates of key row r, records 0 .. 31 (slot clamped)
+    if (first)
+#pragma unroll
+        for (int j = 0; j < kRwkv7Rec; ++j) grow[j] = Gbuf[rec0 + static_cast<size_t>(j < nrec ? j : 0) * kD + r];
     const float ar = A[vec_off + r];
     uint32_t zw[kRowsPerThread];
 #pragma unroll
@@ -754,16 +760,18 @@ __global__ __launch_bounds__(kThreads) void q8_requant_kernel(int nrec, int rec_
         zw[it] = __builtin_nontemporal_load(Zh + q8_row(it, wave, ro) * (kD / 4) + c4);
     sk.store(KE, tid);
     su.store(Us, tid);
-    sg.store(Gs, tid);
     for (int i = nrec * kD + tid; i < kRwkv7Rec * kD; i += kThreads) Us[i] = 0.f;
 #pragma unroll
     for (int it = 0; it < kRowsPerThread; ++it) Zs[q8_row(it, wave, ro) * kZsStride + c4] = zw[it];
     __syncthreads();
     if (first) {  // thread r walks key row r from the newest record
         float G = 1.f;
-        for (int j = nrec - 1; j >= 0; --j) {
-            KE[j * kD + r] *= G;
-            G *= Gs[j * kD + r];
+#pragma unroll
+        for (int j = kRwkv7Rec - 1; j >= 0; --j) {
+            if (j < nrec) {
+                KE[j * kD + r] *= G;
+                G *= grow[j];
+            }
         }
         for (int j = nrec; j < kRwkv7Rec; ++j) KE[j * kD + r] = 0.f;
         zcoef[r] = ar * (1.f / 127.f) * G;
@@ -1006,11 +1014,11 @@ static hipError_t launch_step_kernel(const StepArgs& a, const WindowArgs& w, hip
 
 template <bool kPerKey, int kWmax, typename T>
 static hipError_t launch_boundary_kernel(const StepArgs& a, const WindowArgs& w, hipStream_t stream) {
-    const size_t lds = sizeof(float) * boundary_lds_floats(kWmax, kPerKey);
+    const size_t lds = sizeof(float) * boundary_lds_floats(kWmax);
     static const hipError_t attr = hipFuncSetAttribute(
         reinterpret_cast<const void*>(q8_boundary_kernel<kPerKey, kWmax, T>),
         hipFuncAttributeMaxDynamicSharedMemorySize,
-        static_cast<int>(sizeof(float) * boundary_lds_floats(kWmax, kPerKey)));
+        static_cast<int>(sizeof(float) * boundary_lds_floats(kWmax)));
     if (attr != hipSuccess) return attr;
     hipLaunchKernelGGL((q8_boundary_kernel<kPerKey, kWmax, T>), dim3(a.heads), dim3(kThreads), lds, stream,
                        w.W, w.pos, w.Z, w.A, static_cast<const T*>(w.Kbuf), w.Ubuf, w.Gbuf,
@@ -1046,7 +1054,7 @@ static hipError_t launch_rwkv7_window_t(const StepArgs& a, const WindowArgs& w, 
                        static_cast<const T*>(kappa), a.gate, erase, a.y);
     if (hipError_t e = hipGetLastError()) return e;
     if (w.pos < w.W - 1) return hipSuccess;
-    const int floats = boundary_lds_floats(kRwkv7Rec, true);
+    const int floats = boundary_lds_floats(kRwkv7Rec);
     static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(q8_requant_kernel<T>),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize,
                                                        static_cast<int>(sizeof(float) * floats));
