@@ -29,7 +29,7 @@ DK = 128
 DV = 128
 
 # tensor tags of the substreams
-_TAG_S0, _TAG_Q, _TAG_K, _TAG_V, _TAG_GATE, _TAG_BETA, _TAG_OUTLIER, _TAG_KAPPA, _TAG_A = range(9)
+_TAG_S0, _TAG_Q, _TAG_K, _TAG_V, _TAG_GATE, _TAG_BETA, _TAG_OUTLIER, _TAG_KAPPA, _TAG_A, _TAG_OMEGA = range(10)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -38,7 +38,7 @@ class Workload:
     name: str
     variant: str          # "gdn" (scalar gate alpha), "kda" (per-key gate d), "rwkv6" (per-key decay w,
                           # no delta read) or "rwkv7" (per-key decay w, erase along kappa read with a * kappa)
-    path: str             # "dense", "q8_window", "lq_window" or "log"
+    path: str             # "dense", "q8_window", "lq_window", "log" or "stepq"
     B: int
     H: int
     steps: int
@@ -88,6 +88,10 @@ WORKLOADS = {
                  W=16, outliers=True),
     7: Workload(7, "rwkv6_dense_b128_h32_bf16", "rwkv6", "dense", 128, 32, 32, "bf16", 0.80, 1.0),
     8: Workload(8, "rwkv6_log_b128_h32_m4", "rwkv6", "log", 128, 32, 128, "bf16", 0.80, 1.0, M=4),
+    # STEPQuant-style per-step packed state (4-bit codes, fp16 row and column factors) at the
+    # dense GDN workload's serving shape, with the int8 workload's row and column outliers
+    13: Workload(13, "gdn_stepq_b256_h48_bf16", "gdn", "stepq", 256, 48, 16, "bf16", 0.90, 0.999,
+                 outliers=True, bits=4),
 }
 
 
@@ -188,6 +192,15 @@ def step_inputs(wl: Workload, t: int) -> dict:
                                             .astype(np.float64)))
         out["a"] = _rng(wl, _TAG_A, t).random((n, DK), dtype=f32)
     return out
+
+
+def row_influence(wl: Workload) -> np.ndarray:
+    """Row influence scores omega [B*H, 128] fp32 of the packed-state workload: log-normal,
+    exp(1.08 N(0, 1)), whose 90th/10th percentile ratio, exp(2 * 1.2816 * 1.08) = 15.9, is the
+    per-head median ratio the STEPQuant notes report (15.95). They stand in for calibration."""
+    n = wl.heads
+    z = _rng(wl, _TAG_OMEGA, 0).standard_normal((n, DK), dtype=np.float32).astype(np.float64)
+    return np.exp(1.08 * z).astype(np.float32)
 
 
 def sample_heads(wl: Workload, count: int, seed: int = 7) -> np.ndarray:
