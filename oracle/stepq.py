@@ -12,8 +12,10 @@ kernel decodes the packed state, applies the delta update, reads y_t = X_t^T q_t
 packs X_t again.
 
 Readings taken where the notes are silent or their text is lost (stated once here):
-  * row influence weights: w_i = omega_i^gamma with gamma = 0.25, divided by their geometric
-    mean over the head's 128 rows; omega (the calibrated row influence scores) is an input;
+  * row influence weights: the notes compress omega with the exponent gamma = 0.25 and say
+    that this makes w_i proportional to omega_i^(1/8); read as the power gamma of the RMS read
+    weight sqrt(omega_i): w_i = omega_i^(gamma / 2), divided by their geometric mean over the
+    head's 128 rows; omega (the calibrated row influence scores) is an input;
   * row factor: r_i = sqrt(m_i / w_i) with m_i = mean_j |X_ij| (the notes' formula did not
     survive extraction; they describe it as SmoothQuant's fractional-power balance of the
     row's magnitude against its influence, read here as SmoothQuant's square root), rounded
@@ -42,8 +44,9 @@ def to_fp16(x) -> np.ndarray:
 
 
 def row_weights(omega: np.ndarray) -> np.ndarray:
-    """w_i = omega_i^gamma over its geometric mean along the last axis (the head's rows)."""
-    p = np.asarray(omega, dtype=np.float64) ** GAMMA
+    """w_i = sqrt(omega_i)^gamma = omega_i^(1/8) over its geometric mean along the last axis
+    (the head's rows)."""
+    p = np.sqrt(np.asarray(omega, dtype=np.float64)) ** GAMMA
     return p / np.exp(np.mean(np.log(p), axis=-1, keepdims=True))
 
 

@@ -4,12 +4,13 @@ the mathematics fix.
 The column factor is the closed-form weighted least squares the notes state (checked
 against numpy's least-squares solver on the square-root-weighted system, and by
 optimality: no perturbation of c_j lowers the weighted error, and the fitted factors never
-do worse than the range-setting factor a_j / qmax); the row weights are omega^(1/4) with
-geometric mean 1; scaling X by 4 doubles r and c and keeps every code (the square-root
-row factor); hand-built ties round to even; zero rows and zero columns give zero codes and
-factors; with a huge code range the packed state reproduces X; and a decode step equals
-the dense step from the decoded state. A slip such as dropping w^2 from the fit, swapping
-the row and column roles, or taking m_i over the wrong axis fails at least one of them.
+do worse than the range-setting factor a_j / qmax); the row weights are omega^(1/8) (what
+the notes say the exponent 0.25 amounts to) with geometric mean 1; scaling X by 4 doubles
+r and c and keeps every code (the square-root row factor); hand-built ties round to even;
+zero rows and zero columns give zero codes and factors; with a huge code range the packed
+state reproduces X; and a decode step equals the dense step from the decoded state. A slip
+such as dropping w^2 from the fit, swapping the row and column roles, or taking m_i over
+the wrong axis fails at least one of them.
 """
 import numpy as np
 import pytest
@@ -32,11 +33,11 @@ def _omega(rng, d=128):
     return np.exp(rng.standard_normal(d) * 1.08)
 
 
-def test_row_weights_have_unit_geometric_mean_and_the_quarter_power():
+def test_row_weights_have_unit_geometric_mean_and_the_eighth_power():
     om = _omega(RNG)
     w = stepq.row_weights(om)
     assert abs(np.exp(np.mean(np.log(w))) - 1.0) < 1e-12
-    ratio = w / om ** 0.25
+    ratio = w / om ** 0.125
     np.testing.assert_allclose(ratio, ratio[0], rtol=1e-12)
     np.testing.assert_allclose(stepq.row_weights(np.full(128, 3.7)), 1.0, rtol=1e-12)
 
