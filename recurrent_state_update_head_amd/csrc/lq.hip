@@ -16,6 +16,7 @@
 #include "kernels.hpp"
 #include "rsu_device.hpp"
 #include "codes.hpp"
+#include "swaps.hpp"
 
 namespace rsu {
 
@@ -200,18 +201,6 @@ __device__ __forceinline__ void refit_sv(const RefitLds<kT, kBits>& L, const f32
     __syncthreads();
 }
 
-// Sums of x and y over lane pairs (l, l^16) (pair16) or (l, l^32) (pair32) with one lane
-// swap: lanes whose bit 4 (bit 5) is clear get the sum of x, the others the sum of y.
-__device__ __forceinline__ float add_pair16(float x, float y) {
-    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(y), false, false);
-    const unsigned p0 = p[0], p1 = p[1];
-    return __uint_as_float(p0) + __uint_as_float(p1);
-}
-__device__ __forceinline__ float add_pair32(float x, float y) {
-    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false, false);
-    const unsigned p0 = p[0], p1 = p[1];
-    return __uint_as_float(p0) + __uint_as_float(p1);
-}
 
 // W = S^T Y. A lane's 4 kT partial sums (its 4 columns against the kT columns of Y, over its
 // 16 rows) are summed over the 8 row lanes of the column group by a transposing butterfly:
