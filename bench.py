@@ -40,7 +40,8 @@ KERNEL_SOURCES = {
 }
 
 WORKLOAD_BY_FLAG = {"gdn": 2, "gdn_small": 1, "kda": 3, "q8": 4, "log": 5, "lq": 6, "rwkv6": 7,
-                    "rwkv6_log": 8, "kda_lq": 9, "rwkv7": 10, "rwkv7_q8": 11, "lq4": 12}
+                    "rwkv6_log": 8, "kda_lq": 9, "rwkv7": 10, "rwkv7_q8": 11, "lq4": 12,
+                    "stepq": 13}
 LQ_TOKENS = 4
 
 
@@ -108,6 +109,15 @@ def lq_step_bytes_per_head(w: wl.Workload, pos: int) -> int:
     return rd + wr
 
 
+def stepq_bytes_per_head(w: wl.Workload) -> int:
+    """Packed-state step: the 4-bit codes and the fp16 row and column factors read and
+    written, the fp32 row influence scores read, the step inputs, y."""
+    d = wl.DK
+    gate = 4 * d if w.per_key_gate else 4
+    packed = d * d // 2 + 2 * d + 2 * d
+    return 2 * packed + 4 * d + 3 * d * _in_bytes(w) + gate + _beta_bytes(w) + 4 * d
+
+
 def log_step_bytes_per_head(w: wl.Workload, L: int) -> int:
     """Base+log step with L live entries: base read, L entries read, lbar, inputs,
     y, and either the entry + lbar write (append) or the base + lbar write (merge).
@@ -143,6 +153,8 @@ def cycle_bytes_per_head(w: wl.Workload) -> float:
     """Average algorithmic bytes per head-update over one window / merge cycle."""
     if w.path == "dense":
         return float(dense_bytes_per_head(w))
+    if w.path == "stepq":
+        return float(stepq_bytes_per_head(w))
     if w.path == "q8_window":
         return sum(window_step_bytes_per_head(w, p) for p in range(w.W)) / w.W
     if w.path == "lq_window":
@@ -221,7 +233,7 @@ def run_gpu(w: wl.Workload, steps: int, warmup: int, slots: bool = False, n_iter
     import recurrent_state_update_head_amd as rsu
     dev = "cuda"
     B, H = w.B, w.H
-    n_inputs = {"dense": w.steps, "q8_window": w.W, "lq_window": w.W, "log": w.M}[w.path]
+    n_inputs = {"dense": w.steps, "stepq": w.steps, "q8_window": w.W, "lq_window": w.W, "log": w.M}[w.path]
     n_inputs = min(n_inputs, max(1, w.steps))
     x = _dev_inputs(w, n_inputs, torch, dev)
     y = torch.empty(B, H, 128, device=dev)
@@ -250,6 +262,19 @@ def run_gpu(w: wl.Workload, steps: int, warmup: int, slots: bool = False, n_iter
         def step():
             i = state["t"] % n_inputs
             fn(S, x["q"][i], x["k"][i], x["v"][i], x["gate"][i], x["beta"][i], y)
+            state["t"] += 1
+    elif w.path == "stepq":
+        Z = torch.empty(B, H, 128, 64, device=dev, dtype=torch.uint8)
+        R = torch.empty(B, H, 128, device=dev, dtype=torch.float16)
+        Cf = torch.empty(B, H, 128, device=dev, dtype=torch.float16)
+        om = torch.from_numpy(wl.row_influence(w)).to(dev).view(B, H, 128)
+        rsu.stepq_pack(S0, om, Z, R, Cf)
+        del S0
+        fn = rsu.kda_stepq_step if kda else rsu.gdn_stepq_step
+
+        def step():
+            i = state["t"] % n_inputs
+            fn(Z, R, Cf, om, x["q"][i], x["k"][i], x["v"][i], x["gate"][i], x["beta"][i], y)
             state["t"] += 1
     elif w.path == "q8_window" and w.variant == "rwkv7":
         W = w.W
@@ -352,7 +377,7 @@ def run_gpu(w: wl.Workload, steps: int, warmup: int, slots: bool = False, n_iter
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     phases = None
-    if w.path != "dense":
+    if w.path not in ("dense", "stepq"):
         # one untimed pass over whole cycles with an event between consecutive launches:
         # average launch time per window position / per live log length
         cyc = w.W if w.path in ("q8_window", "lq_window") else w.M
@@ -424,7 +449,7 @@ def override_workload(w: wl.Workload, args) -> wl.Workload:
     """Apply the command-line overrides; the workload's name records them."""
     ch = {}
     if args.variant and args.variant != w.variant:
-        if w.path not in ("dense", "log") and args.variant != "kda":
+        if w.path not in ("dense", "log", "stepq") and args.variant != "kda":
             raise SystemExit(f"--variant {args.variant} does not apply to the {w.path} workload")
         per_key = args.variant in ("kda", "rwkv6")
         ch.update(variant=args.variant, gate_lo=0.8 if per_key else 0.9, gate_hi=1.0 if per_key else 0.999)
@@ -442,7 +467,8 @@ def override_workload(w: wl.Workload, args) -> wl.Workload:
         return w
     w2 = wl.custom(w, **ch)
     var = w2.variant
-    tail = {"dense": "", "q8_window": f"_w{w2.W}", "lq_window": f"_w{w2.W}", "log": f"_m{w2.M}"}[w2.path]
+    tail = {"dense": "", "stepq": "", "q8_window": f"_w{w2.W}", "lq_window": f"_w{w2.W}",
+            "log": f"_m{w2.M}"}[w2.path]
     path = w2.path
     name = f"{var}_{path}_b{w2.B}_h{w2.H}{tail}" + ("_slots" if args.slots else "")
     return wl.custom(w2, name=name)
@@ -476,7 +502,7 @@ def main():
 
     w = wl.WORKLOADS[WORKLOAD_BY_FLAG[args.workload]]
     w = override_workload(w, args)
-    cycle = {"dense": 1, "q8_window": w.W, "lq_window": w.W, "log": w.M}[w.path]
+    cycle = {"dense": 1, "stepq": 1, "q8_window": w.W, "lq_window": w.W, "log": w.M}[w.path]
     steps = args.steps if args.steps is not None else 256
     steps = max(cycle, (steps + cycle - 1) // cycle * cycle)   # whole windows / cycles
     warmup = args.warmup if args.warmup is not None else 2 * cycle
@@ -503,7 +529,8 @@ def main():
         "dtype": "f32",
         "data": "synthetic (seeded; shapes and distributions of the workload)",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "dk": 128, "dv": 128,
-                   "qkv": w.qkv, "state": ("int4+f32 scales+8 fp16 token pairs" if w.bits == 4 else
+                   "qkv": w.qkv, "state": ("int4+fp16 row and column factors" if w.path == "stepq" else
+                                           "int4+f32 scales+8 fp16 token pairs" if w.bits == 4 else
                                             {"q8_window": "int8+f32 scales",
                                              "lq_window": "int8+f32 scales+4 fp16 token pairs"}.get(w.path, "f32")),
                    "W": w.W or None, "M": w.M or None, "gates": w.variant,

@@ -299,6 +299,39 @@ int rwkv7_q8_window(const rsu_dims *dims, int W, int pos, int8_t *Z, float *row_
                     float *y, rsu_stream_t stream);
 
 /* ------------------------------------------------------------------------
+ * STEPQuant's per-step packed state (STEPQuant notes, the section on the
+ * key-row-aware dual-axis fit, and the section on one decode step in SGLang):
+ * element (i, j) of a head's state is R_i C_j z_ij with fp16 key-row factors R,
+ * fp16 value-column factors C and 4-bit codes z in [-7, 7], refitted from the new
+ * state after every decode step.
+ *   Z     [B,H,d_k,d_v/2] bytes, two's complement nibbles, value column 2m in the
+ *         low nibble of byte m, 2m + 1 in the high nibble
+ *   R, C  [B,H,d] fp16
+ *   omega [B,H,d_k] fp32 row influence scores (> 0), read only
+ * The packing of a state X: w_i = omega_i^(1/8) over its geometric mean in the head
+ * (the notes' compression exponent 0.25 on sqrt(omega)); R_i = fp16(sqrt(m_i / w_i))
+ * with m_i = mean_j |X_ij|; a_j = max_i |X_ij / R_i|; z_ij = X_ij / R_i * 7 / a_j
+ * rounded half to even and clamped to [-7, 7] (0 where R_i or a_j is 0); C_j = fp16
+ * of the weighted least squares sum_i w_i^2 R_i z_ij X_ij / sum_i w_i^2 R_i^2 z_ij^2
+ * (0 for a column without nonzero codes). The row factor's formula is a reading
+ * (the notes name SmoothQuant's fractional power; its square root is taken).
+ *
+ * stepq_pack: packs fp32 states S [B,H,d,d] (only read); dims->qkv_dtype is not used.
+ * gdn_stepq_step / kda_stepq_step: one decode step on the packed state in place:
+ *   X = R C z, then the dense step of gdn_decode_step / kda_decode_step on X (y
+ *   read from the updated state), then X_t packed into Z, R, C.
+ * Other rules as for the dense step; calls that share Z, R, C must not overlap.
+ * ---------------------------------------------------------------------- */
+int stepq_pack(const rsu_dims *dims, const float *S, const float *omega, void *Z, void *R,
+               void *C, rsu_stream_t stream);
+int gdn_stepq_step(const rsu_dims *dims, void *Z, void *R, void *C, const float *omega,
+                   const void *q, const void *k, const void *v, const float *alpha,
+                   const float *beta, float *y, rsu_stream_t stream);
+int kda_stepq_step(const rsu_dims *dims, void *Z, void *R, void *C, const float *omega,
+                   const void *q, const void *k, const void *v, const float *d,
+                   const float *beta, float *y, rsu_stream_t stream);
+
+/* ------------------------------------------------------------------------
  * Measurement helper (not part of the recurrence): dst[i] = src[i] for
  * n fp32 elements, with the same 128-bit non-temporal access pattern and grid
  * shape (64 KiB per workgroup) as the dense step. n must be a multiple of 4.

@@ -71,6 +71,9 @@ _SIGS = {
     "rwkv6_log_append": [_DP, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
     "rwkv6_log_merge": [_DP, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
     "rwkv6_log_step_slots": [_DP, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
+    "stepq_pack": [_DP, _P, _P, _P, _P, _P, _P],
+    "gdn_stepq_step": [_DP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
+    "kda_stepq_step": [_DP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
     "rsu_copy_f32": [_P, _P, ctypes.c_int64, _P],
 }
 for _name, _args in _SIGS.items():
@@ -409,6 +412,45 @@ def kda_lq_window(W, pos, n_iter, Z, col_absmax, row_smooth, Kc, Uc, Kbuf, Ubuf,
     """The same step with KDA's per-key gate d (Gbuf holds [B, H, W, 128] gates)."""
     return _lq_window("kda_lq_window", True, W, pos, n_iter, Z, col_absmax, row_smooth, Kc, Uc, Kbuf, Ubuf,
                       Gbuf, q, k, v, d, beta, y)
+
+
+def _stepq_state(B, H, Z, R, C, omega):
+    _need(Z, "Z", torch.uint8, (B, H, D, D // 2))
+    _need(R, "R", torch.float16, (B, H, D))
+    _need(C, "C", torch.float16, (B, H, D))
+    _need(omega, "omega", torch.float32, (B, H, D))
+
+
+def stepq_pack(S, omega, Z, R, C):
+    """Pack fp32 states into STEPQuant's dual-axis format: element (i, j) = R_i C_j z_ij
+    (Z: uint8 [B, H, 128, 64], two signed 4-bit codes per byte, the even value column in
+    the low nibble; R, C: fp16 [B, H, 128]; omega: the row influence scores)."""
+    if S.dim() != 4:
+        raise ValueError("S must be [B, H, 128, 128]")
+    B, H = S.shape[0], S.shape[1]
+    _need(S, "S", torch.float32, (B, H, D, D))
+    _stepq_state(B, H, Z, R, C, omega)
+    dims = _Dims(B, H, D, D, RSU_F32)
+    _call("stepq_pack", ctypes.byref(dims), _ptr(S), _ptr(omega), _ptr(Z), _ptr(R), _ptr(C), _stream())
+
+
+def _stepq_step(name, per_key, Z, R, C, omega, q, k, v, gate, beta, y):
+    dims = _dims(q, k, v)
+    _stepq_state(dims.B, dims.H, Z, R, C, omega)
+    _step_common(dims, gate, beta, y, per_key, "d" if per_key else "alpha")
+    _call(name, ctypes.byref(dims), _ptr(Z), _ptr(R), _ptr(C), _ptr(omega), _ptr(q), _ptr(k), _ptr(v),
+          _ptr(gate), _ptr(beta), _ptr(y), _stream())
+    return y
+
+
+def gdn_stepq_step(Z, R, C, omega, q, k, v, alpha, beta, y):
+    """One GDN decode step on the packed state: decode, update, read out y, pack again."""
+    return _stepq_step("gdn_stepq_step", False, Z, R, C, omega, q, k, v, alpha, beta, y)
+
+
+def kda_stepq_step(Z, R, C, omega, q, k, v, d, beta, y):
+    """The same step with KDA's per-key gate d."""
+    return _stepq_step("kda_stepq_step", True, Z, R, C, omega, q, k, v, d, beta, y)
 
 
 def copy_f32(src: torch.Tensor, dst: torch.Tensor):

@@ -210,6 +210,20 @@ int lq_window_common(const char* fn, Kind m, const rsu_dims* dims, int W, int po
     return launched(rsu::launch_lq_window(a, w, m == Kind::kda, stream), fn);
 }
 
+int stepq_step_common(const char* fn, Kind m, const rsu_dims* dims, void* Z, void* R, void* C, const float* omega,
+                      const void* q, const void* k, const void* v, const float* gate, const float* beta, float* y,
+                      rsu_stream_t stream) {
+    int heads = 0;
+    if (int rc = check_dims(dims, &heads, fn)) return rc;
+    if (heads == 0) return RSU_OK;
+    if (int rc = check_ptrs({{Z, "Z"}, {R, "R"}, {C, "C"}, {omega, "omega"}, {q, "q"}, {k, "k"}, {v, "v"},
+                             {gate, gate_name(m)}, {beta, "beta"}, {y, "y"}}, fn))
+        return rc;
+    return launched(rsu::launch_sq_step(step_args(heads, nullptr, q, k, v, gate, beta, y), Z, R, C, omega,
+                                        m == Kind::kda, dims->qkv_dtype == RSU_BF16, stream),
+                    fn);
+}
+
 }  // namespace
 
 extern "C" {
@@ -405,6 +419,28 @@ int rsu_copy_f32(const float* src, float* dst, int64_t n, rsu_stream_t stream) {
     if (n == 0) return RSU_OK;
     if (int rc = check_ptrs({{src, "src"}, {dst, "dst"}}, "rsu_copy_f32")) return rc;
     return launched(rsu::launch_copy(src, dst, n, stream), "rsu_copy_f32");
+}
+
+int stepq_pack(const rsu_dims* dims, const float* S, const float* omega, void* Z, void* R, void* C,
+               rsu_stream_t stream) {
+    const char* fn = "stepq_pack";
+    int heads = 0;
+    if (int rc = check_dims(dims, &heads, fn)) return rc;
+    if (heads == 0) return RSU_OK;
+    if (int rc = check_ptrs({{S, "S"}, {omega, "omega"}, {Z, "Z"}, {R, "R"}, {C, "C"}}, fn)) return rc;
+    return launched(rsu::launch_sq_pack(heads, S, omega, Z, R, C, stream), fn);
+}
+
+int gdn_stepq_step(const rsu_dims* dims, void* Z, void* R, void* C, const float* omega, const void* q,
+                   const void* k, const void* v, const float* alpha, const float* beta, float* y,
+                   rsu_stream_t stream) {
+    return stepq_step_common("gdn_stepq_step", Kind::gdn, dims, Z, R, C, omega, q, k, v, alpha, beta, y, stream);
+}
+
+int kda_stepq_step(const rsu_dims* dims, void* Z, void* R, void* C, const float* omega, const void* q,
+                   const void* k, const void* v, const float* d, const float* beta, float* y,
+                   rsu_stream_t stream) {
+    return stepq_step_common("kda_stepq_step", Kind::kda, dims, Z, R, C, omega, q, k, v, d, beta, y, stream);
 }
 
 }  // extern "C"

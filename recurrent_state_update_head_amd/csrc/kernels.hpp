@@ -75,6 +75,14 @@ hipError_t launch_lq4_quantize(int heads, const float* S, int n_iter, void* Z, f
                                void* Uc, hipStream_t stream);
 hipError_t launch_lq4_window(const StepArgs& a, const LqArgs& w, hipStream_t stream);
 
+// STEPQuant's packed state (4-bit codes with fp16 key-row and value-column factors):
+// Z [heads, 128, 16] words of 8 signed nibbles, R [heads, 128] and C [heads, 128] fp16,
+// omega [heads, 128] row influence scores.
+hipError_t launch_sq_pack(int heads, const float* S, const float* omega, void* Z, void* R, void* C,
+                          hipStream_t stream);
+hipError_t launch_sq_step(const StepArgs& a, void* Z, void* R, void* C, const float* omega, bool per_key, bool bf16,
+                          hipStream_t stream);
+
 // mode: 0 append, 1 merge, 2 per-slot live lengths
 hipError_t launch_log(const StepArgs& a, const LogArgs& l, int mode, bool per_key, bool bf16,
                       hipStream_t stream);

@@ -1,0 +1,333 @@
+// stepq.hip -- the per-step packed state of the STEPQuant notes (the key-row-aware dual-axis
+// fit): element (i, j) of a head's 128 x 128 state is r_i c_j z_ij, with fp16 key-row factors
+// r_i, fp16 value-column factors c_j and 4-bit codes z_ij (two per byte, the even value column
+// in the low nibble), and the state is packed again after every decode step.
+//
+// The packing of a state X (one workgroup per head):
+//   w_i = omega_i^(1/8) / (their geometric mean over the head's rows)   (row influence weights;
+//         the compression exponent 0.25 applied to the RMS read weight sqrt(omega_i))
+//   r_i = fp16(sqrt(m_i / w_i)),  m_i = mean_j |X_ij|                   (0 for a zero row)
+//   a_j = max_i |X_ij / r_i|,  z_ij = clamp(rne(X_ij / r_i * 7 / a_j), -7, 7)   (0 if a_j = 0)
+//   c_j = fp16(sum_i w_i^2 r_i z_ij X_ij / sum_i w_i^2 r_i^2 z_ij^2)    (weighted least squares)
+// and a decode step decodes X_{t-1}, applies the dense update (decayed delta read, rank-one
+// write, y = X_t^T q from the updated state) and packs X_t, all in registers: the packed state
+// is read once and written once per step.
+//
+// Thread layout (as in the 4-bit LeapQuant sweep): lane l of wave w owns the code word of
+// value columns 8(l & 15) .. +7 in the key rows 16 it + 4 w + (l >> 4), it = 0..7, and keeps
+// those 64 elements of X in registers. Row sums run over the 16 lanes of a DPP row; column
+// sums over the 4 row lanes (two lane swaps) and then the 4 waves through LDS.
+#include "kernels.hpp"
+#include "rsu_device.hpp"
+#include "codes.hpp"
+#include "swaps.hpp"
+
+namespace rsu {
+
+typedef _Float16 half_t;
+
+namespace {
+
+constexpr float kSqQmax = 7.f;
+
+__device__ __forceinline__ int sq_row(int it, int wave, int rl) { return 16 * it + 4 * wave + rl; }
+
+// Workgroup-shared arrays of the packing.
+struct SqLds {
+    float w[kD];          // w_i
+    float wsq[kD];        // w_i^2
+    float r[kD];          // r_i (the fp16 value)
+    float ir[kD];         // 1 / r_i, 0 for a zero row
+    float sc[kD];         // 7 / a_j, 0 for a zero column
+    f32x2 red[4][kD];     // per-wave column partials
+    float lgw[4];         // per-wave sums of log(omega^(1/4))
+};
+
+// Row influence weights from omega [128] (threads < 128 hold row tid): w_i and w_i^2 into L.
+// Every thread calls it; it ends with a barrier.
+__device__ __forceinline__ void sq_row_weights(SqLds& L, const float* __restrict__ omega_h, int tid) {
+    const int wave = tid >> 6, lane = tid & 63;
+    float p = 1.f;
+    if (tid < kD) {
+        p = sqrtf(sqrtf(sqrtf(omega_h[tid])));  // omega^(1/8)
+        const float s = wave_sum(logf(p));
+        if (lane == 0) L.lgw[wave] = s;
+    }
+    __syncthreads();
+    if (tid < kD) {
+        const float g = expf((L.lgw[0] + L.lgw[1]) * (1.f / kD));  // geometric mean of omega^(1/4)
+        const float w = p / g;
+        L.w[tid] = w;
+        L.wsq[tid] = w * w;
+    }
+    __syncthreads();
+}
+
+// The codes of 8 elements (column order) as one word of 8 signed nibbles, u = X / r.
+__device__ __forceinline__ uint32_t sq_code_word(const float (&u)[8], const float (&s)[8]) {
+#pragma clang fp contract(off)
+    uint32_t w = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const int bits = __float_as_int(u[e] * s[e] + 12582912.0f);  // rne with one fp32 add
+        w |= (static_cast<uint32_t>(min(max(bits, 0x4B400000 - 7), 0x4B400000 + 7)) & 0xfu) << (4 * e);
+    }
+    return w;
+}
+
+// Packs the lane's 64 elements x (rows sq_row(it, wave, l >> 4), columns 8 (l & 15) + e):
+// row factors, column ranges, codes (stored), weighted least squares column factors.
+// L.w and L.wsq must hold the row weights. Every thread calls it.
+__device__ __forceinline__ void sq_pack(SqLds& L, const float (&x)[8][8], int tid, uint32_t* __restrict__ Zh,
+                                        half_t* __restrict__ Rh, half_t* __restrict__ Ch) {
+    const int wave = tid >> 6, lane = tid & 63;
+    const int c16 = lane & 15, rl = lane >> 4;
+    const int b4 = (lane >> 4) & 1, b5 = lane >> 5;
+
+    // ---- r_i from the row means (the 16 lanes of a DPP row hold one key row)
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+        float a = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) a += fabsf(x[it][e]);
+        a = row16_sum(a);
+        if (c16 == 0) {
+            const int row = sq_row(it, wave, rl);
+            const float m = a * (1.f / kD);
+            const half_t rh = static_cast<half_t>(sqrtf(m / L.w[row]));
+            const float r = static_cast<float>(rh);
+            L.r[row] = r;
+            L.ir[row] = r > 0.f ? 1.f / r : 0.f;
+            Rh[row] = rh;
+        }
+    }
+    __syncthreads();
+
+    // ---- column ranges a_j = max_i |X_ij / r_i|: the lane's 8 rows, its 4 row lanes, the 4 waves
+    float ir[8];
+#pragma unroll
+    for (int it = 0; it < 8; ++it) ir[it] = L.ir[sq_row(it, wave, rl)];
+    {
+        float m[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            m[e] = 0.f;
+#pragma unroll
+            for (int it = 0; it < 8; ++it) m[e] = fmaxf(m[e], fabsf(x[it][e] * ir[it]));
+        }
+        float q[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) q[e] = max_pair16(m[e], m[e + 4]);      // column e + 4 b4
+        const float m0 = max_pair32(q[0], q[2]), m1 = max_pair32(q[1], q[3]);  // columns + 2 b5, + 1
+        float* redf = reinterpret_cast<float*>(L.red);
+        *reinterpret_cast<f32x2*>(redf + wave * kD + 8 * c16 + 4 * b4 + 2 * b5) = f32x2{m0, m1};
+    }
+    __syncthreads();
+    if (tid < kD) {
+        const float* redf = reinterpret_cast<const float*>(L.red);
+        const float a = fmaxf(fmaxf(redf[tid], redf[kD + tid]), fmaxf(redf[2 * kD + tid], redf[3 * kD + tid]));
+        L.sc[tid] = a > 0.f ? __fdiv_rn(kSqQmax, a) : 0.f;
+    }
+    __syncthreads();
+
+    // ---- codes (stored), and the least-squares sums of the lane's columns
+    float s[8];
+    {
+        const f32x4 s0 = *reinterpret_cast<const f32x4*>(L.sc + 8 * c16);
+        const f32x4 s1 = *reinterpret_cast<const f32x4*>(L.sc + 8 * c16 + 4);
+        s[0] = s0.x; s[1] = s0.y; s[2] = s0.z; s[3] = s0.w;
+        s[4] = s1.x; s[5] = s1.y; s[6] = s1.z; s[7] = s1.w;
+    }
+    float num[8], den[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) num[e] = den[e] = 0.f;
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+        const int row = sq_row(it, wave, rl);
+        float u[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) u[e] = x[it][e] * ir[it];
+        const uint32_t word = sq_code_word(u, s);
+        Zh[row * (kD / 8) + c16] = word;
+        const float wr = L.wsq[row] * L.r[row];       // w_i^2 r_i
+        const float wrr = wr * L.r[row];              // w_i^2 r_i^2
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float z = static_cast<float>(static_cast<int>(word << (28 - 4 * e)) >> 28);
+            num[e] = fmaf(wr * z, x[it][e], num[e]);
+            den[e] = fmaf(wrr * z, z, den[e]);
+        }
+    }
+    {
+        float qn[4], qd[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            qn[e] = add_pair16(num[e], num[e + 4]);
+            qd[e] = add_pair16(den[e], den[e + 4]);
+        }
+        *reinterpret_cast<f32x4*>(L.red[wave] + 8 * c16 + 4 * b4 + 2 * b5) =
+            f32x4{add_pair32(qn[0], qn[2]), add_pair32(qd[0], qd[2]), add_pair32(qn[1], qn[3]),
+                  add_pair32(qd[1], qd[3])};
+    }
+    __syncthreads();
+    if (tid < kD) {
+        const f32x2 t = (L.red[0][tid] + L.red[1][tid]) + (L.red[2][tid] + L.red[3][tid]);
+        Ch[tid] = static_cast<half_t>(t.y > 0.f ? t.x / t.y : 0.f);
+    }
+}
+
+// ---- a plain fp32 state [heads, 128, 128] into the packed format
+__global__ __launch_bounds__(kThreads) void sq_pack_kernel(const float* __restrict__ S,
+                                                           const float* __restrict__ omega,
+                                                           uint32_t* __restrict__ Z, half_t* __restrict__ R,
+                                                           half_t* __restrict__ C) {
+    __shared__ SqLds L;
+    const int h = head_of_block(blockIdx.x, gridDim.x), tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
+    const int c16 = lane & 15, rl = lane >> 4;
+    const float* Sh = S + static_cast<size_t>(h) * kD * kD;
+    float x[8][8];
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+        const float* src = Sh + sq_row(it, wave, rl) * kD + 8 * c16;
+        const f32x4 a = stream_load(src), b = stream_load(src + 4);
+        x[it][0] = a.x; x[it][1] = a.y; x[it][2] = a.z; x[it][3] = a.w;
+        x[it][4] = b.x; x[it][5] = b.y; x[it][6] = b.z; x[it][7] = b.w;
+    }
+    sq_row_weights(L, omega + static_cast<size_t>(h) * kD, tid);
+    sq_pack(L, x, tid, Z + static_cast<size_t>(h) * kD * (kD / 8), R + static_cast<size_t>(h) * kD,
+            C + static_cast<size_t>(h) * kD);
+}
+
+// ---- one decode step on the packed state, in place
+template <bool kPerKey, typename T>
+__global__ __launch_bounds__(kThreads) void sq_step_kernel(uint32_t* __restrict__ Z, half_t* __restrict__ R,
+                                                           half_t* __restrict__ C, const float* __restrict__ omega,
+                                                           const T* __restrict__ q, const T* __restrict__ k,
+                                                           const T* __restrict__ v, const float* __restrict__ gate,
+                                                           const float* __restrict__ beta, float* __restrict__ y) {
+    __shared__ SqLds L;
+    __shared__ f32x4 rowv[kD];   // (r g k, r g q, r g, k) of key row i
+    __shared__ float ucol[kD];   // u_j
+    __shared__ float kq_part[2];
+    const int h = head_of_block(blockIdx.x, gridDim.x), tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
+    const int c16 = lane & 15, rl = lane >> 4;
+    const int b4 = (lane >> 4) & 1, b5 = lane >> 5;
+    const size_t vec_off = static_cast<size_t>(h) * kD;
+    uint32_t* Zh = Z + static_cast<size_t>(h) * kD * (kD / 8);
+
+    // ---- loads: the lane's code words and column factors, the key-side inputs of row tid
+    uint32_t zw[8];
+#pragma unroll
+    for (int it = 0; it < 8; ++it) zw[it] = __builtin_nontemporal_load(Zh + sq_row(it, wave, rl) * (kD / 8) + c16);
+    const uint4 cw = *reinterpret_cast<const uint4*>(C + vec_off + 8 * c16);
+    float kr = 0.f, qr = 0.f, gr = 1.f, rr = 0.f, vr = 0.f;
+    if (tid < kD) {
+        kr = load_in(k, vec_off + tid);
+        qr = load_in(q, vec_off + tid);
+        gr = kPerKey ? gate[vec_off + tid] : gate[h];
+        rr = static_cast<float>(R[vec_off + tid]);
+        vr = load_in(v, vec_off + tid);
+    }
+    const float bt = beta[h];
+    if (tid < kD) {
+        const float rg = rr * gr;
+        rowv[tid] = f32x4{rg * kr, rg * qr, rg, kr};
+        const float kq = wave_sum(kr * qr);
+        if (lane == 0) kq_part[wave] = kq;
+    }
+    sq_row_weights(L, omega + vec_off, tid);  // (its barriers also publish rowv)
+
+    // ---- decode X_{t-1} = r c z (the column factor applied here, the row factor through rowv),
+    // and the two column sums of the old state: p = X^T (g k), o = X^T (g q)
+    float cz[8][8];
+    float cc[8];
+    {
+        const half_t* ch = reinterpret_cast<const half_t*>(&cw);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) cc[e] = static_cast<float>(ch[e]) * 0.0625f;  // the codes come as 16 z
+    }
+    float p[8], o[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) p[e] = o[e] = 0.f;
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+        const f32x4 rv = rowv[sq_row(it, wave, rl)];
+        const uint32_t ev = (zw[it] << 4) & 0xF0F0F0F0u, od = zw[it] & 0xF0F0F0F0u;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            cz[it][2 * j] = static_cast<float>(static_cast<int8_t>(ev >> (8 * j))) * cc[2 * j];
+            cz[it][2 * j + 1] = static_cast<float>(static_cast<int8_t>(od >> (8 * j))) * cc[2 * j + 1];
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            p[e] = fmaf(cz[it][e], rv.x, p[e]);
+            o[e] = fmaf(cz[it][e], rv.y, o[e]);
+        }
+    }
+    {
+        float qp[4], qo[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            qp[e] = add_pair16(p[e], p[e + 4]);
+            qo[e] = add_pair16(o[e], o[e + 4]);
+        }
+        *reinterpret_cast<f32x4*>(L.red[wave] + 8 * c16 + 4 * b4 + 2 * b5) =
+            f32x4{add_pair32(qp[0], qp[2]), add_pair32(qo[0], qo[2]), add_pair32(qp[1], qp[3]),
+                  add_pair32(qo[1], qo[3])};
+    }
+    __syncthreads();
+    if (tid < kD) {  // column tid: correction, output
+        const f32x2 t = (L.red[0][tid] + L.red[1][tid]) + (L.red[2][tid] + L.red[3][tid]);
+        const float u = bt * (vr - t.x);
+        y[vec_off + tid] = t.y + u * (kq_part[0] + kq_part[1]);
+        ucol[tid] = u;
+    }
+    __syncthreads();
+
+    // ---- X_t = Diag(g) X_{t-1} + k u^T in registers, then packed
+    float uc[8];
+    {
+        const f32x4 u0 = *reinterpret_cast<const f32x4*>(ucol + 8 * c16);
+        const f32x4 u1 = *reinterpret_cast<const f32x4*>(ucol + 8 * c16 + 4);
+        uc[0] = u0.x; uc[1] = u0.y; uc[2] = u0.z; uc[3] = u0.w;
+        uc[4] = u1.x; uc[5] = u1.y; uc[6] = u1.z; uc[7] = u1.w;
+    }
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+        const f32x4 rv = rowv[sq_row(it, wave, rl)];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) cz[it][e] = fmaf(rv.z, cz[it][e], rv.w * uc[e]);
+    }
+    sq_pack(L, cz, tid, Zh, R + vec_off, C + vec_off);
+}
+
+}  // namespace
+
+hipError_t launch_sq_pack(int heads, const float* S, const float* omega, void* Z, void* R, void* C,
+                          hipStream_t stream) {
+    hipLaunchKernelGGL(sq_pack_kernel, dim3(heads), dim3(kThreads), 0, stream, S, omega,
+                       static_cast<uint32_t*>(Z), static_cast<half_t*>(R), static_cast<half_t*>(C));
+    return hipGetLastError();
+}
+
+hipError_t launch_sq_step(const StepArgs& a, void* Z, void* R, void* C, const float* omega, bool per_key, bool bf16,
+                          hipStream_t stream) {
+    auto go = [&](auto kernel, auto tag) {
+        using T = decltype(tag);
+        hipLaunchKernelGGL(kernel, dim3(a.heads), dim3(kThreads), 0, stream, static_cast<uint32_t*>(Z),
+                           static_cast<half_t*>(R), static_cast<half_t*>(C), omega, static_cast<const T*>(a.q),
+                           static_cast<const T*>(a.k), static_cast<const T*>(a.v), a.gate, a.beta, a.y);
+    };
+    if (per_key) {
+        if (bf16) go(sq_step_kernel<true, bf16_t>, bf16_t{});
+        else go(sq_step_kernel<true, float>, float{});
+    } else {
+        if (bf16) go(sq_step_kernel<false, bf16_t>, bf16_t{});
+        else go(sq_step_kernel<false, float>, float{});
+    }
+    return hipGetLastError();
+}
+
+}  // namespace rsu

@@ -422,3 +422,122 @@ def run_window(w: wl.Workload, sample: int | None = None, steps: int | None = No
             y_ref = ref.step(*args)
         st["y"] = max(st["y"], rel_err(take(y, hd, (128,)), y_ref))
     return st
+
+
+def new_stepq_buffers(w: wl.Workload):
+    B, H = w.B, w.H
+    return {
+        "Z": torch.zeros(B, H, 128, 64, device=DEV, dtype=torch.uint8),
+        "R": torch.zeros(B, H, 128, device=DEV, dtype=torch.float16),
+        "C": torch.zeros(B, H, 128, device=DEV, dtype=torch.float16),
+    }
+
+
+def stepq_host(buf, hd):
+    """The GPU's packed state of the sampled heads: codes [n, 128, 128], R, C (fp64)."""
+    from oracle import lq as lqo
+    z = lqo.unpack_nibbles(take(buf["Z"], hd, (128, 64))).astype(np.int64)
+    r = take(buf["R"].float(), hd, (128,)).astype(np.float64)
+    c = take(buf["C"].float(), hd, (128,)).astype(np.float64)
+    return z, r, c
+
+
+def _fp16_rounding_ok(got, exact, rel_band):
+    """got == fp16(exact), or exact lies within rel_band * |exact| of the midpoint between
+    got and fp16(exact) (a tie the GPU's fp32 arithmetic may round either way). Returns the
+    masks (off: wrong outside the band, tie: differs inside it)."""
+    from oracle import stepq as sqo
+    ref = sqo.to_fp16(exact)
+    diff = got != ref
+    near = np.abs(exact - 0.5 * (got + ref)) <= rel_band * np.abs(exact)
+    return diff & ~near, diff & near
+
+
+def check_stepq_pack(X, mag, omega, rep, err, tie_band=1e-4, mat_rel=1e-6, rel_band=2e-5):
+    """Teacher-forced check of the packing of the fp64 states X [n, 128, 128].
+
+    mag bounds the magnitude the GPU's fp32 X was formed from (|X| itself for a packed
+    input state; |g X_prev| + |k u^T| after a step): the GPU's elements carry errors of
+    about mat_rel * mag. Row factors: the GPU's R is the fp16 rounding of the exact
+    sqrt(m_i / w_i), except within a relative band of a rounding midpoint. Codes:
+    recomputed from the GPU's own R; a code may differ by 1 only within tie_band (plus
+    mat_rel * mag in code units) of a tie. Column factors: recomputed in fp64 from the
+    GPU's own R and codes; the GPU's C is their fp16 rounding up to a band at midpoints."""
+    from oracle import stepq as sqo
+    z, r, c = rep
+    W = sqo.row_weights(omega)
+    qmax = sqo.QMAX4
+    for i in range(X.shape[0]):
+        p = sqo.pack(X[i], W[i])
+        m = np.mean(np.abs(X[i]), axis=1)
+        band_r = rel_band + mat_rel * np.mean(mag[i], axis=1) / np.maximum(m, 1e-300)
+        off, tie = _fp16_rounding_ok(r[i], p["r_pre"], band_r)
+        err["r_off"] += int(off.sum())
+        err["r_ties"] += int(tie.sum())
+        live = r[i] > 0
+        U = np.zeros_like(X[i])
+        U[live] = X[i][live] / r[i][live][:, None]
+        a = np.max(np.abs(U), axis=0)
+        cols = a > 0
+        code = np.zeros_like(U)
+        code[:, cols] = U[:, cols] * (qmax / a[cols])[None, :]
+        Zr = np.clip(np.rint(code), -qmax, qmax).astype(np.int64)
+        dz = np.abs(z[i] - Zr)
+        err["z_maxdiff"] = max(err["z_maxdiff"], int(dz.max()))
+        flips = dz > 0
+        err["z_flips"] += int(flips.sum())
+        band = np.full_like(code, tie_band)
+        rr = np.where(live, r[i], np.inf)[:, None]
+        band[:, cols] += mat_rel * qmax * (mag[i][:, cols] / rr) / a[cols][None, :]
+        near = np.abs(np.abs(code - np.floor(code)) - 0.5) < band
+        err["z_flips_outside_band"] += int((flips & ~near).sum())
+        zf = z[i].astype(np.float64)
+        cp = sqo.column_factors(X[i], r[i], zf, W[i])
+        wr = (W[i] ** 2 * r[i])[:, None]
+        num_abs = np.sum(wr * np.abs(zf) * mag[i], axis=0)
+        num = np.abs(np.sum(wr * zf * X[i], axis=0))
+        band_c = rel_band + mat_rel * num_abs / np.maximum(num, 1e-300)
+        off, tie = _fp16_rounding_ok(c[i], cp, band_c)
+        err["c_off"] += int(off.sum())
+        err["c_ties"] += int(tie.sum())
+        err["rows"] += X.shape[1]
+
+
+def run_stepq(w: wl.Workload, sample: int | None = None, steps: int | None = None, S0=None, om=None):
+    """The packed state on the GPU against the oracle, teacher-forced per step: the packing
+    of the initial state, then for every step the output against the dense step from the
+    GPU's packed state before it, and the packing of the resulting state."""
+    from oracle import stepq as sqo
+    m = rsu()
+    B, H = w.B, w.H
+    steps = w.steps if steps is None else steps
+    if S0 is None:
+        S0 = wl.initial_state(w)
+    if om is None:
+        om = wl.row_influence(w)
+    heads = np.arange(w.heads) if sample is None else wl.sample_heads(w, sample)
+    hd = torch.from_numpy(heads).to(DEV)
+    buf = new_stepq_buffers(w)
+    omega = torch.from_numpy(om).to(DEV).view(B, H, 128)
+    Sd = torch.from_numpy(S0).to(DEV).view(B, H, 128, 128)
+    m.stepq_pack(Sd, omega, buf["Z"], buf["R"], buf["C"])
+    err = {"y": 0.0, "r_off": 0, "r_ties": 0, "z_maxdiff": 0, "z_flips": 0, "z_flips_outside_band": 0,
+           "c_off": 0, "c_ties": 0, "rows": 0, "steps": 0}
+    X0 = S0[heads].astype(np.float64)
+    del Sd, S0
+    om_s = om[heads].astype(np.float64)
+    check_stepq_pack(X0, np.abs(X0), om_s, stepq_host(buf, hd), err)
+    step = m.kda_stepq_step if w.per_key_gate else m.gdn_stepq_step
+    y = torch.empty(B, H, 128, device=DEV)
+    for t in range(steps):
+        z, r, c = stepq_host(buf, hd)
+        x, d = dev_inputs(w, t)
+        step(buf["Z"], buf["R"], buf["C"], omega, d["q"], d["k"], d["v"], d["gate"], d["beta"], y)
+        q, k, v, g, b = host_slice(x, heads)
+        y_ref, _, Xt = sqo.step(z, r, c, om_s, q, k, v, g, b)
+        err["y"] = max(err["y"], rel_err(take(y, hd, (128,)), y_ref))
+        Xp = sqo.decode(z, r, c)
+        gX = Xp * (np.asarray(g, np.float64)[:, :, None] if g.ndim == 2 else np.asarray(g, np.float64)[:, None, None])
+        check_stepq_pack(Xt, np.abs(gX) + np.abs(Xt - gX), om_s, stepq_host(buf, hd), err)
+        err["steps"] += 1
+    return err

@@ -17,8 +17,8 @@ RSU_OK, E_NULL, E_DIMS, E_DTYPE, E_ALIGN, E_RANGE = 0, -1, -2, -3, -4, -5
 @pytest.fixture(scope="module")
 def lib():
     if not os.path.exists(LIB):
-        from recurrent_state_update_head_amd import _build
-        _build.build()
+        import __graft_entry__
+        __graft_entry__.build()
     return ctypes.CDLL(LIB)
 
 
@@ -147,6 +147,30 @@ def test_lq4_validation(lib):
     assert qz(ctypes.byref(d16), GOOD, 99, *([GOOD] * 5), None) == E_RANGE
     assert qz(ctypes.byref(d16), GOOD, 2, GOOD, GOOD, ODD, GOOD, GOOD, None) == E_ALIGN
     assert qz(ctypes.byref(Dims(2, 3, 128, 64, 1)), GOOD, 2, *([GOOD] * 5), None) == E_DIMS
+
+
+def test_stepq_validation(lib):
+    d32 = Dims(2, 3, 128, 128, 0)
+    pk = lib.stepq_pack
+    pk.restype = ctypes.c_int
+    assert pk(ctypes.byref(d32), GOOD, None, GOOD, GOOD, GOOD, None) == E_NULL
+    assert "omega is NULL" in _last(lib)
+    assert pk(ctypes.byref(d32), GOOD, GOOD, GOOD, ODD, GOOD, None) == E_ALIGN
+    assert pk(ctypes.byref(Dims(2, 3, 64, 128, 0)), *([GOOD] * 5), None) == E_DIMS
+    assert pk(ctypes.byref(Dims(0, 3, 128, 128, 0)), *([None] * 5), None) == RSU_OK
+    for name, gname in (("gdn_stepq_step", "alpha"), ("kda_stepq_step", "d")):
+        f = getattr(lib, name)
+        f.restype = ctypes.c_int
+        args = [GOOD] * 10
+        assert f(ctypes.byref(Dims(2, 3, 128, 128, 7)), *args, None) == E_DTYPE
+        bad = list(args)
+        bad[7] = None
+        assert f(ctypes.byref(d32), *bad, None) == E_NULL
+        assert f"{gname} is NULL" in _last(lib)
+        bad[7] = ODD
+        assert f(ctypes.byref(d32), *bad, None) == E_ALIGN
+        assert f(ctypes.byref(Dims(-1, 3, 128, 128, 1)), *args, None) == E_DIMS
+        assert f(ctypes.byref(Dims(2, 0, 128, 128, 1)), *([None] * 10), None) == RSU_OK
 
 
 def test_copy_validation(lib):

@@ -104,3 +104,22 @@ def test_graph_leapquant_window(bits):
 
     _check_rounds(block, _twin(bufs), _twin(bufs), torch.zeros(w.B, w.H, 128, device=DEV),
                   torch.zeros(w.B, w.H, 128, device=DEV))
+
+
+def test_graph_stepq():
+    """Four packed-state steps per block (decode, update, readout, repack)."""
+    from parity import new_stepq_buffers
+    m = rsu()
+    w = wl.custom(wl.WORKLOADS[13], B=2, H=5)
+    bufs = new_stepq_buffers(w)
+    S0 = torch.from_numpy(wl.initial_state(w)).to(DEV).view(w.B, w.H, 128, 128)
+    om = torch.from_numpy(wl.row_influence(w)).to(DEV).view(w.B, w.H, 128)
+    m.stepq_pack(S0, om, bufs["Z"], bufs["R"], bufs["C"])
+    ins = [dev_inputs(w, t)[1] for t in range(4)]
+
+    def block(b, y):
+        for d in ins:
+            m.gdn_stepq_step(b["Z"], b["R"], b["C"], om, d["q"], d["k"], d["v"], d["gate"], d["beta"], y)
+
+    _check_rounds(block, _twin(bufs), _twin(bufs), torch.zeros(w.B, w.H, 128, device=DEV),
+                  torch.zeros(w.B, w.H, 128, device=DEV))

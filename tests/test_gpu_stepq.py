@@ -1,0 +1,115 @@
+"""STEPQuant's per-step packed state on the GPU (stepq_pack, gdn_stepq_step,
+kda_stepq_step through the C ABI) against the fp64 oracle, teacher-forced per step.
+
+Every step's output must match the dense step from the GPU's packed state before it to
+the fp32 tolerance. Every packing (of the initial state and after each step) is checked
+piece by piece: row factors are the fp16 rounding of the exact sqrt(m_i / w_i), codes are
+recomputed from the GPU's row factors, column factors are the fp16 rounding of the
+weighted least squares recomputed from the GPU's codes; a difference is allowed only
+within a narrow band of a rounding tie (fp32 arithmetic on the GPU against fp64), and
+such ties must stay rare.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads as wl
+from parity import DEV, TOL_F32, new_stepq_buffers, rsu, run_stepq, say, stepq_host
+
+pytestmark = pytest.mark.gpu
+
+BASE = wl.WORKLOADS[13]
+
+
+def _kda(base, **kw):
+    return wl.custom(base, variant="kda", gate_lo=0.8, gate_hi=1.0, **kw)
+
+
+def _assert_ok(err, tol=TOL_F32):
+    say(err)
+    assert err["y"] < tol
+    assert err["r_off"] == 0
+    assert err["c_off"] == 0
+    assert err["z_maxdiff"] <= 1
+    assert err["z_flips_outside_band"] == 0
+    assert err["r_ties"] + err["c_ties"] <= max(2, err["rows"] // 100)
+
+
+@pytest.mark.parametrize("variant", ["gdn", "kda"])
+@pytest.mark.parametrize("qkv", ["f32", "bf16"])
+def test_stepq_small_all_heads(variant, qkv):
+    w = wl.custom(BASE, B=3, H=5, qkv=qkv)
+    if variant == "kda":
+        w = _kda(w)
+    say(f"stepq {variant} {qkv} B=3 H=5")
+    _assert_ok(run_stepq(w, steps=6))
+
+
+def test_stepq_ragged_grid():
+    """100 heads: three whole groups of the XCD head map and a ragged tail."""
+    w = wl.custom(BASE, B=10, H=10)
+    say("stepq gdn B=10 H=10")
+    _assert_ok(run_stepq(w, steps=3))
+
+
+def test_stepq_full_size_sampled():
+    say(f"stepq {BASE.name} sampled")
+    _assert_ok(run_stepq(BASE, sample=16, steps=3))
+
+
+def test_stepq_kda_full_size_sampled():
+    w = _kda(BASE, B=128, H=32)
+    say("stepq kda B=128 H=32 sampled")
+    _assert_ok(run_stepq(w, sample=12, steps=2))
+
+
+def test_stepq_uniform_influence():
+    """omega constant over the rows: every w_i = 1."""
+    w = wl.custom(BASE, B=2, H=3)
+    say("stepq uniform omega")
+    _assert_ok(run_stepq(w, steps=3, om=np.full((w.heads, 128), 3.5, np.float32)))
+
+
+def test_stepq_zero_state():
+    """A zero state packs to zero codes and factors; the first step then writes k (beta v)^T."""
+    w = wl.custom(BASE, B=2, H=3)
+    S0 = np.zeros((w.heads, 128, 128), np.float32)
+    m = rsu()
+    buf = new_stepq_buffers(w)
+    m.stepq_pack(torch.from_numpy(S0).to(DEV).view(w.B, w.H, 128, 128),
+                 torch.from_numpy(wl.row_influence(w)).to(DEV).view(w.B, w.H, 128), buf["Z"], buf["R"], buf["C"])
+    z, r, c = stepq_host(buf, torch.arange(w.heads, device=DEV))
+    assert not z.any() and not r.any() and not c.any()
+    say("stepq zero state")
+    _assert_ok(run_stepq(w, steps=2, S0=S0))
+
+
+def test_stepq_zero_rows_and_columns():
+    w = wl.custom(BASE, B=2, H=3)
+    S0 = wl.initial_state(w)
+    S0[:, 7, :] = 0.0
+    S0[:, :, 40] = 0.0
+    S0[1, :, :] = 0.0
+    say("stepq zero rows and columns")
+    m = rsu()
+    buf = new_stepq_buffers(w)
+    m.stepq_pack(torch.from_numpy(S0).to(DEV).view(w.B, w.H, 128, 128),
+                 torch.from_numpy(wl.row_influence(w)).to(DEV).view(w.B, w.H, 128), buf["Z"], buf["R"], buf["C"])
+    z, r, c = stepq_host(buf, torch.arange(w.heads, device=DEV))
+    assert not r[:, 7].any() and not z[:, 7, :].any()
+    assert not c[:, 40].any() and not z[:, :, 40].any()
+    assert not z[1].any() and not r[1].any() and not c[1].any()
+    _assert_ok(run_stepq(w, steps=2, S0=S0))
+
+
+def test_stepq_empty_batch():
+    m = rsu()
+    w = wl.custom(BASE, B=0, H=4)
+    buf = new_stepq_buffers(w)
+    om = torch.ones(0, 4, 128, device=DEV)
+    q = torch.zeros(0, 4, 128, device=DEV, dtype=torch.bfloat16)
+    y = torch.zeros(0, 4, 128, device=DEV)
+    m.stepq_pack(torch.zeros(0, 4, 128, 128, device=DEV), om, buf["Z"], buf["R"], buf["C"])
+    m.gdn_stepq_step(buf["Z"], buf["R"], buf["C"], om, q, q, q, torch.zeros(0, 4, device=DEV),
+                     torch.zeros(0, 4, device=DEV), y)
+    torch.cuda.synchronize()
