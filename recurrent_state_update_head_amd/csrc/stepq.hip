@@ -34,17 +34,17 @@ __device__ __forceinline__ int sq_row(int it, int wave, int rl) { return 16 * it
 
 // Workgroup-shared arrays of the packing.
 struct SqLds {
-    float w[kD];          // w_i
+    float iw[kD];         // 1 / w_i
     float wsq[kD];        // w_i^2
-    float r[kD];          // r_i (the fp16 value)
     float ir[kD];         // 1 / r_i, 0 for a zero row
+    float wrr[kD];        // w_i^2 r_i^2
     float sc[kD];         // 7 / a_j, 0 for a zero column
     f32x2 red[4][kD];     // per-wave column partials
-    float lgw[4];         // per-wave sums of log(omega^(1/4))
+    float lgw[4];         // per-wave sums of log(omega^(1/8))
 };
 
-// Row influence weights from omega [128] (threads < 128 hold row tid): w_i and w_i^2 into L.
-// Every thread calls it; it ends with a barrier.
+// Row influence weights from omega [128] (threads < 128 hold row tid): 1 / w_i and w_i^2 into
+// L. Every thread calls it; it ends with a barrier.
 __device__ __forceinline__ void sq_row_weights(SqLds& L, const float* __restrict__ omega_h, int tid) {
     const int wave = tid >> 6, lane = tid & 63;
     float p = 1.f;
@@ -55,65 +55,68 @@ __device__ __forceinline__ void sq_row_weights(SqLds& L, const float* __restrict
     }
     __syncthreads();
     if (tid < kD) {
-        const float g = expf((L.lgw[0] + L.lgw[1]) * (1.f / kD));  // geometric mean of omega^(1/4)
+        const float g = expf((L.lgw[0] + L.lgw[1]) * (1.f / kD));  // their geometric mean
         const float w = p / g;
-        L.w[tid] = w;
+        L.iw[tid] = 1.f / w;
         L.wsq[tid] = w * w;
     }
     __syncthreads();
 }
 
-// The codes of 8 elements (column order) as one word of 8 signed nibbles, u = X / r.
-__device__ __forceinline__ uint32_t sq_code_word(const float (&u)[8], const float (&s)[8]) {
-#pragma clang fp contract(off)
-    uint32_t w = 0;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const int bits = __float_as_int(u[e] * s[e] + 12582912.0f);  // rne with one fp32 add
-        w |= (static_cast<uint32_t>(min(max(bits, 0x4B400000 - 7), 0x4B400000 + 7)) & 0xfu) << (4 * e);
-    }
-    return w;
-}
+constexpr float kRne = 12582912.0f;      // 1.5 * 2^23: adding it rounds to an integer (half to even)
+constexpr int kRneBits = 0x4B400000;     // its bit pattern; bits - kRneBits is that integer
 
 // Packs the lane's 64 elements x (rows sq_row(it, wave, l >> 4), columns 8 (l & 15) + e):
 // row factors, column ranges, codes (stored), weighted least squares column factors.
-// L.w and L.wsq must hold the row weights. Every thread calls it.
-__device__ __forceinline__ void sq_pack(SqLds& L, const float (&x)[8][8], int tid, uint32_t* __restrict__ Zh,
+// Overwrites x with u = x / r. L.iw and L.wsq must hold the row weights. Every thread calls it.
+__device__ __forceinline__ void sq_pack(SqLds& L, float (&x)[8][8], int tid, uint32_t* __restrict__ Zh,
                                         half_t* __restrict__ Rh, half_t* __restrict__ Ch) {
     const int wave = tid >> 6, lane = tid & 63;
     const int c16 = lane & 15, rl = lane >> 4;
     const int b4 = (lane >> 4) & 1, b5 = lane >> 5;
 
-    // ---- r_i from the row means (the 16 lanes of a DPP row hold one key row)
+    // ---- r_i from the row means: the 16 lanes of a DPP row hold the lane's 8 key rows; lane
+    // c16 then takes row c16 & 7 (lanes 8..15 repeat it)
+    {
+        float a[8];
 #pragma unroll
-    for (int it = 0; it < 8; ++it) {
-        float a = 0.f;
+        for (int it = 0; it < 8; ++it) {
+            float t = 0.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) a += fabsf(x[it][e]);
-        a = row16_sum(a);
-        if (c16 == 0) {
-            const int row = sq_row(it, wave, rl);
-            const float m = a * (1.f / kD);
-            const half_t rh = static_cast<half_t>(sqrtf(m / L.w[row]));
-            const float r = static_cast<float>(rh);
-            L.r[row] = r;
+            for (int e = 0; e < 8; ++e) t += fabsf(x[it][e]);
+            a[it] = row16_sum(t);
+        }
+        float s1[4], s2[2];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) s1[j] = (c16 & 1) ? a[2 * j + 1] : a[2 * j];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) s2[j] = (c16 & 2) ? s1[2 * j + 1] : s1[2 * j];
+        const float sum = (c16 & 4) ? s2[1] : s2[0];
+        const int row = sq_row(c16 & 7, wave, rl);
+        const half_t rh = static_cast<half_t>(sqrtf(sum * (1.f / kD) * L.iw[row]));
+        const float r = static_cast<float>(rh);
+        if (c16 < 8) {
             L.ir[row] = r > 0.f ? 1.f / r : 0.f;
+            L.wrr[row] = L.wsq[row] * r * r;
             Rh[row] = rh;
         }
     }
     __syncthreads();
 
-    // ---- column ranges a_j = max_i |X_ij / r_i|: the lane's 8 rows, its 4 row lanes, the 4 waves
-    float ir[8];
-#pragma unroll
-    for (int it = 0; it < 8; ++it) ir[it] = L.ir[sq_row(it, wave, rl)];
+    // ---- u = x / r in place, and the column ranges a_j = max_i |u_ij|: the lane's 8 rows, its
+    // 4 row lanes, the 4 waves
     {
         float m[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            m[e] = 0.f;
+        for (int e = 0; e < 8; ++e) m[e] = 0.f;
 #pragma unroll
-            for (int it = 0; it < 8; ++it) m[e] = fmaxf(m[e], fabsf(x[it][e] * ir[it]));
+        for (int it = 0; it < 8; ++it) {
+            const float ir = L.ir[sq_row(it, wave, rl)];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                x[it][e] *= ir;
+                m[e] = fmaxf(m[e], fabsf(x[it][e]));
+            }
         }
         float q[4];
 #pragma unroll
@@ -130,7 +133,8 @@ __device__ __forceinline__ void sq_pack(SqLds& L, const float (&x)[8][8], int ti
     }
     __syncthreads();
 
-    // ---- codes (stored), and the least-squares sums of the lane's columns
+    // ---- codes (stored), and the least-squares sums of the lane's columns. With u = x / r,
+    // sum_i w^2 r z x = sum_i (w^2 r^2) z u.
     float s[8];
     {
         const f32x4 s0 = *reinterpret_cast<const f32x4*>(L.sc + 8 * c16);
@@ -144,19 +148,24 @@ __device__ __forceinline__ void sq_pack(SqLds& L, const float (&x)[8][8], int ti
 #pragma unroll
     for (int it = 0; it < 8; ++it) {
         const int row = sq_row(it, wave, rl);
-        float u[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) u[e] = x[it][e] * ir[it];
-        const uint32_t word = sq_code_word(u, s);
-        Zh[row * (kD / 8) + c16] = word;
-        const float wr = L.wsq[row] * L.r[row];       // w_i^2 r_i
-        const float wrr = wr * L.r[row];              // w_i^2 r_i^2
+        const float W = L.wrr[row];
+        uint32_t bits[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const float z = static_cast<float>(static_cast<int>(word << (28 - 4 * e)) >> 28);
-            num[e] = fmaf(wr * z, x[it][e], num[e]);
-            den[e] = fmaf(wrr * z, z, den[e]);
+            // the code rne(u s) from the exact product (one rounding), clamped to [-7, 7]
+            const int b = __float_as_int(__builtin_fmaf(x[it][e], s[e], kRne));
+            const int c = min(max(b, kRneBits - 7), kRneBits + 7);
+            bits[e] = static_cast<uint32_t>(c);
+            const float z = __int_as_float(c) - kRne;
+            const float t = W * z;
+            num[e] = fmaf(t, x[it][e], num[e]);
+            den[e] = fmaf(t, z, den[e]);
         }
+        // low bytes hold the codes' two's complement; nibbles of the even columns from E, the
+        // odd ones from O shifted into the high nibbles
+        const uint32_t E = pack_low_bytes(bits[0], bits[2], bits[4], bits[6]);
+        const uint32_t O = pack_low_bytes(bits[1], bits[3], bits[5], bits[7]);
+        Zh[row * (kD / 8) + c16] = (E & 0x0F0F0F0Fu) | ((O << 4) & 0xF0F0F0F0u);
     }
     {
         float qn[4], qd[4];
