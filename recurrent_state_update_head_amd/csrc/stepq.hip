@@ -39,32 +39,34 @@ struct SqLds {
     float ir[kD];         // 1 / r_i, 0 for a zero row
     float wrr[kD];        // w_i^2 r_i^2
     float sc[kD];         // 7 / a_j, 0 for a zero column
+    half_t rh[kD];        // r_i, stored coalesced after the row phase
     f32x2 red[4][kD];     // per-wave column partials
-    float lgw[4];         // per-wave sums of log(omega^(1/8))
+    float lgw[4];         // per-wave sums of log2(omega^(1/8))
 };
 
 // Row influence weights from omega [128] (threads < 128 hold row tid): 1 / w_i and w_i^2 into
-// L. Every thread calls it; it ends with a barrier.
+// L, with w_i = omega_i^(1/8) / (their geometric mean) = 2^(l_i - mean(l)), l_i = log2(omega_i) / 8.
+// Every thread calls it; it ends with a barrier.
 __device__ __forceinline__ void sq_row_weights(SqLds& L, const float* __restrict__ omega_h, int tid) {
     const int wave = tid >> 6, lane = tid & 63;
-    float p = 1.f;
+    float l = 0.f;
     if (tid < kD) {
-        p = sqrtf(sqrtf(sqrtf(omega_h[tid])));  // omega^(1/8)
-        const float s = wave_sum(logf(p));
+        l = __log2f(omega_h[tid]) * 0.125f;
+        const float s = wave_sum(l);
         if (lane == 0) L.lgw[wave] = s;
     }
     __syncthreads();
     if (tid < kD) {
-        const float g = expf((L.lgw[0] + L.lgw[1]) * (1.f / kD));  // their geometric mean
-        const float w = p / g;
-        L.iw[tid] = 1.f / w;
-        L.wsq[tid] = w * w;
+        const float d = l - (L.lgw[0] + L.lgw[1]) * (1.f / kD);  // log2 w_i
+        L.iw[tid] = exp2f(-d);
+        L.wsq[tid] = exp2f(2.f * d);
     }
     __syncthreads();
 }
 
-constexpr float kRne = 12582912.0f;      // 1.5 * 2^23: adding it rounds to an integer (half to even)
-constexpr int kRneBits = 0x4B400000;     // its bit pattern; bits - kRneBits is that integer
+// 1.5 * 2^23: adding it rounds to an integer (half to even); for integers in [-7, 7] the low
+// byte of the sum's bits is that integer's two's complement
+constexpr float kRne = 12582912.0f;
 
 // Packs the lane's 64 elements x (rows sq_row(it, wave, l >> 4), columns 8 (l & 15) + e):
 // row factors, column ranges, codes (stored), weighted least squares column factors.
@@ -98,10 +100,11 @@ __device__ __forceinline__ void sq_pack(SqLds& L, float (&x)[8][8], int tid, uin
         if (c16 < 8) {
             L.ir[row] = r > 0.f ? 1.f / r : 0.f;
             L.wrr[row] = L.wsq[row] * r * r;
-            Rh[row] = rh;
+            L.rh[row] = rh;
         }
     }
     __syncthreads();
+    if (tid < kD) Rh[tid] = L.rh[tid];
 
     // ---- u = x / r in place, and the column ranges a_j = max_i |u_ij|: the lane's 8 rows, its
     // 4 row lanes, the 4 waves
@@ -129,7 +132,9 @@ __device__ __forceinline__ void sq_pack(SqLds& L, float (&x)[8][8], int tid, uin
     if (tid < kD) {
         const float* redf = reinterpret_cast<const float*>(L.red);
         const float a = fmaxf(fmaxf(redf[tid], redf[kD + tid]), fmaxf(redf[2 * kD + tid], redf[3 * kD + tid]));
-        L.sc[tid] = a > 0.f ? __fdiv_rn(kSqQmax, a) : 0.f;
+        // capped so that |u| s stays below 7.5 even where 7 / a overflows (a subnormal range):
+        // every code then rounds into [-7, 7] with no clamp
+        L.sc[tid] = a > 0.f ? fminf(__fdiv_rn(kSqQmax, a), 3.402823466e38f) : 0.f;
     }
     __syncthreads();
 
@@ -152,11 +157,11 @@ __device__ __forceinline__ void sq_pack(SqLds& L, float (&x)[8][8], int tid, uin
         uint32_t bits[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            // the code rne(u s) from the exact product (one rounding), clamped to [-7, 7]
-            const int b = __float_as_int(__builtin_fmaf(x[it][e], s[e], kRne));
-            const int c = min(max(b, kRneBits - 7), kRneBits + 7);
-            bits[e] = static_cast<uint32_t>(c);
-            const float z = __int_as_float(c) - kRne;
+            // the code rne(u s) from the exact product (one rounding); |u| <= a_j and s_j is
+            // 7 / a_j rounded, so |u s| <= 7 (1 + 2^-23) and the code lies in [-7, 7]
+            const float f = __builtin_fmaf(x[it][e], s[e], kRne);
+            bits[e] = static_cast<uint32_t>(__float_as_int(f));
+            const float z = f - kRne;
             const float t = W * z;
             num[e] = fmaf(t, x[it][e], num[e]);
             den[e] = fmaf(t, z, den[e]);
