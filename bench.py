@@ -228,7 +228,8 @@ def copy_ceiling(torch, rsu, nbytes: int, reps: int = 10) -> float:
     return 2 * n * 4 / sec / 1e9
 
 
-def run_gpu(w: wl.Workload, steps: int, warmup: int, slots: bool = False, n_iter: int = 1, graph: bool = False):
+def run_gpu(w: wl.Workload, steps: int, warmup: int, slots: bool = False, n_iter: int = 1, graph: bool = False,
+            split: bool = False):
     import torch
     import recurrent_state_update_head_amd as rsu
     dev = "cuda"
@@ -271,11 +272,49 @@ def run_gpu(w: wl.Workload, steps: int, warmup: int, slots: bool = False, n_iter
         rsu.stepq_pack(S0, om, Z, R, Cf)
         del S0
         fn = rsu.kda_stepq_step if kda else rsu.gdn_stepq_step
+        if split:
+            # the readout on this stream, the repack on a second one ordered by events (the
+            # next readout waits for it): nothing else runs here to hide the repack behind
+            readout = rsu.kda_stepq_readout if kda else rsu.gdn_stepq_readout
+            repack = rsu.kda_stepq_repack if kda else rsu.gdn_stepq_repack
+            u = torch.empty(B, H, 128, device=dev)
+            side = torch.cuda.Stream()
+            main = torch.cuda.current_stream()
 
-        def step():
-            i = state["t"] % n_inputs
-            fn(Z, R, Cf, om, x["q"][i], x["k"][i], x["v"][i], x["gate"][i], x["beta"][i], y)
-            state["t"] += 1
+            def step():
+                i = state["t"] % n_inputs
+                readout(Z, R, Cf, x["q"][i], x["k"][i], x["v"][i], x["gate"][i], x["beta"][i], u, y)
+                r1 = torch.cuda.Event()
+                r1.record(main)
+                with torch.cuda.stream(side):
+                    side.wait_event(r1)
+                    repack(Z, R, Cf, om, x["k"][i], x["gate"][i], u)
+                    p1 = torch.cuda.Event()
+                    p1.record(side)
+                main.wait_event(p1)
+                state["t"] += 1
+
+            def split_phases(reps=32):
+                """Each half alone, launched back to back on one stream (the readout only reads the
+                packed state; repeated repacks keep stepping it): average launch times."""
+                out = {}
+                for key, call in (("readout_us", lambda: readout(Z, R, Cf, x["q"][0], x["k"][0], x["v"][0],
+                                                                   x["gate"][0], x["beta"][0], u, y)),
+                                  ("repack_us", lambda: repack(Z, R, Cf, om, x["k"][0], x["gate"][0], u))):
+                    call()
+                    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    a.record(main)
+                    for _ in range(reps):
+                        call()
+                    b.record(main)
+                    torch.cuda.synchronize()
+                    out[key] = round(a.elapsed_time(b) * 1e3 / reps, 2)
+                return out
+        else:
+            def step():
+                i = state["t"] % n_inputs
+                fn(Z, R, Cf, om, x["q"][i], x["k"][i], x["v"][i], x["gate"][i], x["beta"][i], y)
+                state["t"] += 1
     elif w.path == "q8_window" and w.variant == "rwkv7":
         W = w.W
         Z = torch.empty(B, H, 128, 128, device=dev, dtype=torch.int8)
@@ -418,6 +457,8 @@ def run_gpu(w: wl.Workload, steps: int, warmup: int, slots: bool = False, n_iter
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
     gpu_sec = e0.elapsed_time(e1) / 1e3
+    if split:
+        phases = split_phases()
     ceiling = copy_ceiling(torch, rsu, 4 * B * H * 128 * 128) if w.path == "dense" else None
     return gpu_sec, wall, ceiling, phases
 
@@ -491,6 +532,8 @@ def main():
     ap.add_argument("--M", type=int, default=None, help="log path: merge interval (1..64)")
     ap.add_argument("--n-iter", type=int, default=1,
                     help="lq path: subspace iterations per boundary refit (warm-started)")
+    ap.add_argument("--split", action="store_true",
+                    help="stepq path: the readout and the repack as two launches on two streams")
     ap.add_argument("--slots", action="store_true",
                     help="log path: per-slot live lengths, every head at its own cycle point")
     args = ap.parse_args()
@@ -508,7 +551,9 @@ def main():
     warmup = args.warmup if args.warmup is not None else 2 * cycle
     warmup = (warmup + cycle - 1) // cycle * cycle
 
-    gpu_sec, wall, ceiling, phases = run_gpu(w, steps, warmup, args.slots, args.n_iter, args.graph)
+    if args.split and (w.path != "stepq" or args.graph):
+        raise SystemExit("--split applies to the stepq workload, without --graph")
+    gpu_sec, wall, ceiling, phases = run_gpu(w, steps, warmup, args.slots, args.n_iter, args.graph, args.split)
     heads = w.heads
     per_head = slots_bytes_per_head(w) if args.slots else cycle_bytes_per_head(w)
     launch_sec = gpu_sec / steps
@@ -542,7 +587,8 @@ def main():
         "hbm_copy_ceiling": ({"achieved": ceiling, "unit": "GB/s", "frac": ceiling / PEAK_HBM_GBS}
                              if ceiling else None),
         "wall_s_timed_region": wall,
-        "timing": "the K steps captured as one HIP graph, replayed once" if args.graph else "eager launches",
+        "timing": ("the K steps captured as one HIP graph, replayed once" if args.graph else
+                   "eager launches, readout and repack on two streams" if args.split else "eager launches"),
     }
     if phases:
         out["phases"] = phases

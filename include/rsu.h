@@ -330,6 +330,28 @@ int gdn_stepq_step(const rsu_dims *dims, void *Z, void *R, void *C, const float 
 int kda_stepq_step(const rsu_dims *dims, void *Z, void *R, void *C, const float *omega,
                    const void *q, const void *k, const void *v, const float *d,
                    const float *beta, float *y, rsu_stream_t stream);
+/* The same step in two launches, as the notes run it in SGLang: the readout first
+ * (decode, update, y), the dual-axis repack on another stream behind the rest of the
+ * model, done before the next read of the state.
+ * gdn_stepq_readout / kda_stepq_readout: decode X = R C z, the correction
+ *   u = beta (v - X^T (g k)) and y = X_t^T q; writes u [B,H,d_v] fp32 (caller-owned) and
+ *   y; Z, R, C are only read.
+ * gdn_stepq_repack / kda_stepq_repack: X_t = Diag(g) X + k u^T from the same packed
+ *   state and the readout's u, packed into Z, R, C in place (k in dims->qkv_dtype).
+ * The pair repeats the fused step's arithmetic: y, u and the new Z, R, C equal those
+ * of gdn_stepq_step / kda_stepq_step bit for bit. The caller orders them (the repack
+ * after its readout, the next readout after the repack; e.g. with HIP events across
+ * two streams). Other rules as for the fused step. */
+int gdn_stepq_readout(const rsu_dims *dims, const void *Z, const void *R, const void *C,
+                      const void *q, const void *k, const void *v, const float *alpha,
+                      const float *beta, float *u, float *y, rsu_stream_t stream);
+int kda_stepq_readout(const rsu_dims *dims, const void *Z, const void *R, const void *C,
+                      const void *q, const void *k, const void *v, const float *d,
+                      const float *beta, float *u, float *y, rsu_stream_t stream);
+int gdn_stepq_repack(const rsu_dims *dims, void *Z, void *R, void *C, const float *omega,
+                     const void *k, const float *alpha, const float *u, rsu_stream_t stream);
+int kda_stepq_repack(const rsu_dims *dims, void *Z, void *R, void *C, const float *omega,
+                     const void *k, const float *d, const float *u, rsu_stream_t stream);
 
 /* ------------------------------------------------------------------------
  * Measurement helper (not part of the recurrence): dst[i] = src[i] for

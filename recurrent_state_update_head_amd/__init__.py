@@ -74,6 +74,10 @@ _SIGS = {
     "stepq_pack": [_DP, _P, _P, _P, _P, _P, _P],
     "gdn_stepq_step": [_DP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
     "kda_stepq_step": [_DP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
+    "gdn_stepq_readout": [_DP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
+    "kda_stepq_readout": [_DP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
+    "gdn_stepq_repack": [_DP, _P, _P, _P, _P, _P, _P, _P, _P],
+    "kda_stepq_repack": [_DP, _P, _P, _P, _P, _P, _P, _P, _P],
     "rsu_copy_f32": [_P, _P, ctypes.c_int64, _P],
 }
 for _name, _args in _SIGS.items():
@@ -451,6 +455,51 @@ def gdn_stepq_step(Z, R, C, omega, q, k, v, alpha, beta, y):
 def kda_stepq_step(Z, R, C, omega, q, k, v, d, beta, y):
     """The same step with KDA's per-key gate d."""
     return _stepq_step("kda_stepq_step", True, Z, R, C, omega, q, k, v, d, beta, y)
+
+
+def _stepq_readout(name, per_key, Z, R, C, q, k, v, gate, beta, u, y):
+    dims = _dims(q, k, v)
+    B, H = dims.B, dims.H
+    _need(Z, "Z", torch.uint8, (B, H, D, D // 2))
+    _need(R, "R", torch.float16, (B, H, D))
+    _need(C, "C", torch.float16, (B, H, D))
+    _need(u, "u", torch.float32, (B, H, D))
+    _step_common(dims, gate, beta, y, per_key, "d" if per_key else "alpha")
+    _call(name, ctypes.byref(dims), _ptr(Z), _ptr(R), _ptr(C), _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(beta),
+          _ptr(u), _ptr(y), _stream())
+    return y
+
+
+def gdn_stepq_readout(Z, R, C, q, k, v, alpha, beta, u, y):
+    """The readout half of a packed-state step: writes the correction u and y; the packed
+    state is only read. gdn_stepq_repack with the same u completes the step."""
+    return _stepq_readout("gdn_stepq_readout", False, Z, R, C, q, k, v, alpha, beta, u, y)
+
+
+def kda_stepq_readout(Z, R, C, q, k, v, d, beta, u, y):
+    return _stepq_readout("kda_stepq_readout", True, Z, R, C, q, k, v, d, beta, u, y)
+
+
+def _stepq_repack(name, per_key, Z, R, C, omega, k, gate, u):
+    if k.dim() != 3 or k.shape[-1] != D or k.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError(f"k must be a float32 or bfloat16 [B, H, {D}] tensor")
+    B, H = int(k.shape[0]), int(k.shape[1])
+    _need(k, "k", k.dtype, (B, H, D))
+    _stepq_state(B, H, Z, R, C, omega)
+    _need(gate, "d" if per_key else "alpha", torch.float32, _gate_shape(B, H, per_key))
+    _need(u, "u", torch.float32, (B, H, D))
+    dims = _Dims(B, H, D, D, RSU_BF16 if k.dtype == torch.bfloat16 else RSU_F32)
+    _call(name, ctypes.byref(dims), _ptr(Z), _ptr(R), _ptr(C), _ptr(omega), _ptr(k), _ptr(gate), _ptr(u), _stream())
+
+
+def gdn_stepq_repack(Z, R, C, omega, k, alpha, u):
+    """The repack half: X_t = alpha X + k u^T from the packed state and the readout's u, packed
+    in place (may run on another stream, ordered after its readout and before the next)."""
+    _stepq_repack("gdn_stepq_repack", False, Z, R, C, omega, k, alpha, u)
+
+
+def kda_stepq_repack(Z, R, C, omega, k, d, u):
+    _stepq_repack("kda_stepq_repack", True, Z, R, C, omega, k, d, u)
 
 
 def copy_f32(src: torch.Tensor, dst: torch.Tensor):

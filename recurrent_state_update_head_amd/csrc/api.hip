@@ -219,8 +219,37 @@ int stepq_step_common(const char* fn, Kind m, const rsu_dims* dims, void* Z, voi
     if (int rc = check_ptrs({{Z, "Z"}, {R, "R"}, {C, "C"}, {omega, "omega"}, {q, "q"}, {k, "k"}, {v, "v"},
                              {gate, gate_name(m)}, {beta, "beta"}, {y, "y"}}, fn))
         return rc;
-    return launched(rsu::launch_sq_step(step_args(heads, nullptr, q, k, v, gate, beta, y), Z, R, C, omega,
-                                        m == Kind::kda, dims->qkv_dtype == RSU_BF16, stream),
+    return launched(rsu::launch_sq_step(step_args(heads, nullptr, q, k, v, gate, beta, y), 0, Z, R, C, omega,
+                                        nullptr, m == Kind::kda, dims->qkv_dtype == RSU_BF16, stream),
+                    fn);
+}
+
+int stepq_readout_common(const char* fn, Kind m, const rsu_dims* dims, const void* Z, const void* R, const void* C,
+                         const void* q, const void* k, const void* v, const float* gate, const float* beta,
+                         float* u, float* y, rsu_stream_t stream) {
+    int heads = 0;
+    if (int rc = check_dims(dims, &heads, fn)) return rc;
+    if (heads == 0) return RSU_OK;
+    if (int rc = check_ptrs({{Z, "Z"}, {R, "R"}, {C, "C"}, {q, "q"}, {k, "k"}, {v, "v"}, {gate, gate_name(m)},
+                             {beta, "beta"}, {u, "u"}, {y, "y"}}, fn))
+        return rc;
+    return launched(rsu::launch_sq_step(step_args(heads, nullptr, q, k, v, gate, beta, y), 1, const_cast<void*>(Z),
+                                        const_cast<void*>(R), const_cast<void*>(C), nullptr, u, m == Kind::kda,
+                                        dims->qkv_dtype == RSU_BF16, stream),
+                    fn);
+}
+
+int stepq_repack_common(const char* fn, Kind m, const rsu_dims* dims, void* Z, void* R, void* C, const float* omega,
+                        const void* k, const float* gate, const float* u, rsu_stream_t stream) {
+    int heads = 0;
+    if (int rc = check_dims(dims, &heads, fn)) return rc;
+    if (heads == 0) return RSU_OK;
+    if (int rc = check_ptrs({{Z, "Z"}, {R, "R"}, {C, "C"}, {omega, "omega"}, {k, "k"}, {gate, gate_name(m)},
+                             {u, "u"}}, fn))
+        return rc;
+    return launched(rsu::launch_sq_step(step_args(heads, nullptr, nullptr, k, nullptr, gate, nullptr, nullptr), 2, Z,
+                                        R, C, omega, const_cast<float*>(u), m == Kind::kda,
+                                        dims->qkv_dtype == RSU_BF16, stream),
                     fn);
 }
 
@@ -441,6 +470,28 @@ int kda_stepq_step(const rsu_dims* dims, void* Z, void* R, void* C, const float*
                    const void* k, const void* v, const float* d, const float* beta, float* y,
                    rsu_stream_t stream) {
     return stepq_step_common("kda_stepq_step", Kind::kda, dims, Z, R, C, omega, q, k, v, d, beta, y, stream);
+}
+
+int gdn_stepq_readout(const rsu_dims* dims, const void* Z, const void* R, const void* C, const void* q,
+                      const void* k, const void* v, const float* alpha, const float* beta, float* u, float* y,
+                      rsu_stream_t stream) {
+    return stepq_readout_common("gdn_stepq_readout", Kind::gdn, dims, Z, R, C, q, k, v, alpha, beta, u, y, stream);
+}
+
+int kda_stepq_readout(const rsu_dims* dims, const void* Z, const void* R, const void* C, const void* q,
+                      const void* k, const void* v, const float* d, const float* beta, float* u, float* y,
+                      rsu_stream_t stream) {
+    return stepq_readout_common("kda_stepq_readout", Kind::kda, dims, Z, R, C, q, k, v, d, beta, u, y, stream);
+}
+
+int gdn_stepq_repack(const rsu_dims* dims, void* Z, void* R, void* C, const float* omega, const void* k,
+                     const float* alpha, const float* u, rsu_stream_t stream) {
+    return stepq_repack_common("gdn_stepq_repack", Kind::gdn, dims, Z, R, C, omega, k, alpha, u, stream);
+}
+
+int kda_stepq_repack(const rsu_dims* dims, void* Z, void* R, void* C, const float* omega, const void* k,
+                     const float* d, const float* u, rsu_stream_t stream) {
+    return stepq_repack_common("kda_stepq_repack", Kind::kda, dims, Z, R, C, omega, k, d, u, stream);
 }
 
 }  // extern "C"

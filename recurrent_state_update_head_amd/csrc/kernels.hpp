@@ -80,8 +80,10 @@ hipError_t launch_lq4_window(const StepArgs& a, const LqArgs& w, hipStream_t str
 // omega [heads, 128] row influence scores.
 hipError_t launch_sq_pack(int heads, const float* S, const float* omega, void* Z, void* R, void* C,
                           hipStream_t stream);
-hipError_t launch_sq_step(const StepArgs& a, void* Z, void* R, void* C, const float* omega, bool per_key, bool bf16,
-                          hipStream_t stream);
+// mode: 0 the fused step, 1 the readout alone (writes u [heads, 128] and y; Z, R, C only read),
+// 2 the repack alone (reads u; q, v, beta, y unused)
+hipError_t launch_sq_step(const StepArgs& a, int mode, void* Z, void* R, void* C, const float* omega, float* u,
+                          bool per_key, bool bf16, hipStream_t stream);
 
 // mode: 0 append, 1 merge, 2 per-slot live lengths
 hipError_t launch_log(const StepArgs& a, const LogArgs& l, int mode, bool per_key, bool bf16,

@@ -17,6 +17,8 @@
 // value columns 8(l & 15) .. +7 in the key rows 16 it + 4 w + (l >> 4), it = 0..7, and keeps
 // those 64 elements of X in registers. Row sums run over the 16 lanes of a DPP row; column
 // sums over the 4 row lanes (two lane swaps) and then the 4 waves through LDS.
+#include <type_traits>
+
 #include "kernels.hpp"
 #include "rsu_device.hpp"
 #include "codes.hpp"
@@ -213,13 +215,21 @@ __global__ __launch_bounds__(kThreads) void sq_pack_kernel(const float* __restri
             C + static_cast<size_t>(h) * kD);
 }
 
-// ---- one decode step on the packed state, in place
-template <bool kPerKey, typename T>
+// ---- one decode step on the packed state, in place (kMode = kSqFused), or the same step in two
+// launches: the readout (decode, both column sums, u and y; the packed state is only read) and the
+// repack (decode again, X_t = Diag(g) X_{t-1} + k u^T, pack), which a caller may run on a second
+// stream behind other work. The two launches repeat the fused step's arithmetic operation for
+// operation, so their y, u and packed state equal the fused step's bit for bit.
+constexpr int kSqFused = 0, kSqReadout = 1, kSqRepack = 2;
+
+template <int kMode, bool kPerKey, typename T>
 __global__ __launch_bounds__(kThreads) void sq_step_kernel(uint32_t* __restrict__ Z, half_t* __restrict__ R,
                                                            half_t* __restrict__ C, const float* __restrict__ omega,
                                                            const T* __restrict__ q, const T* __restrict__ k,
                                                            const T* __restrict__ v, const float* __restrict__ gate,
-                                                           const float* __restrict__ beta, float* __restrict__ y) {
+                                                           const float* __restrict__ beta, float* __restrict__ u_io,
+                                                           float* __restrict__ y) {
+    constexpr bool kRead = kMode != kSqRepack, kPack = kMode != kSqReadout;
     __shared__ SqLds L;
     __shared__ f32x4 rowv[kD];   // (r g k, r g q, r g, k) of key row i
     __shared__ float ucol[kD];   // u_j
@@ -239,19 +249,28 @@ __global__ __launch_bounds__(kThreads) void sq_step_kernel(uint32_t* __restrict_
     float kr = 0.f, qr = 0.f, gr = 1.f, rr = 0.f, vr = 0.f;
     if (tid < kD) {
         kr = load_in(k, vec_off + tid);
-        qr = load_in(q, vec_off + tid);
         gr = kPerKey ? gate[vec_off + tid] : gate[h];
         rr = static_cast<float>(R[vec_off + tid]);
-        vr = load_in(v, vec_off + tid);
+        if constexpr (kRead) {
+            qr = load_in(q, vec_off + tid);
+            vr = load_in(v, vec_off + tid);
+        } else {
+            ucol[tid] = u_io[vec_off + tid];
+        }
     }
-    const float bt = beta[h];
+    const float bt = kRead ? beta[h] : 0.f;
     if (tid < kD) {
         const float rg = rr * gr;
         rowv[tid] = f32x4{rg * kr, rg * qr, rg, kr};
-        const float kq = wave_sum(kr * qr);
-        if (lane == 0) kq_part[wave] = kq;
+        if constexpr (kRead) {
+            const float kq = wave_sum(kr * qr);
+            if (lane == 0) kq_part[wave] = kq;
+        }
     }
-    sq_row_weights(L, omega + vec_off, tid);  // (its barriers also publish rowv)
+    if constexpr (kPack)
+        sq_row_weights(L, omega + vec_off, tid);  // (its barriers also publish rowv and ucol)
+    else
+        __syncthreads();
 
     // ---- decode X_{t-1} = r c z (the column factor applied here, the row factor through rowv),
     // and the two column sums of the old state: p = X^T (g k), o = X^T (g q)
@@ -274,31 +293,39 @@ __global__ __launch_bounds__(kThreads) void sq_step_kernel(uint32_t* __restrict_
             cz[it][2 * j] = static_cast<float>(static_cast<int8_t>(ev >> (8 * j))) * cc[2 * j];
             cz[it][2 * j + 1] = static_cast<float>(static_cast<int8_t>(od >> (8 * j))) * cc[2 * j + 1];
         }
+        if constexpr (kRead) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            p[e] = fmaf(cz[it][e], rv.x, p[e]);
-            o[e] = fmaf(cz[it][e], rv.y, o[e]);
+            for (int e = 0; e < 8; ++e) {
+                p[e] = fmaf(cz[it][e], rv.x, p[e]);
+                o[e] = fmaf(cz[it][e], rv.y, o[e]);
+            }
         }
     }
-    {
-        float qp[4], qo[4];
+    if constexpr (kRead) {
+        {
+            float qp[4], qo[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            qp[e] = add_pair16(p[e], p[e + 4]);
-            qo[e] = add_pair16(o[e], o[e + 4]);
+            for (int e = 0; e < 4; ++e) {
+                qp[e] = add_pair16(p[e], p[e + 4]);
+                qo[e] = add_pair16(o[e], o[e + 4]);
+            }
+            *reinterpret_cast<f32x4*>(L.red[wave] + 8 * c16 + 4 * b4 + 2 * b5) =
+                f32x4{add_pair32(qp[0], qp[2]), add_pair32(qo[0], qo[2]), add_pair32(qp[1], qp[3]),
+                      add_pair32(qo[1], qo[3])};
         }
-        *reinterpret_cast<f32x4*>(L.red[wave] + 8 * c16 + 4 * b4 + 2 * b5) =
-            f32x4{add_pair32(qp[0], qp[2]), add_pair32(qo[0], qo[2]), add_pair32(qp[1], qp[3]),
-                  add_pair32(qo[1], qo[3])};
+        __syncthreads();
+        if (tid < kD) {  // column tid: correction, output
+            const f32x2 t = (L.red[0][tid] + L.red[1][tid]) + (L.red[2][tid] + L.red[3][tid]);
+            const float u = bt * (vr - t.x);
+            y[vec_off + tid] = t.y + u * (kq_part[0] + kq_part[1]);
+            if constexpr (kMode == kSqReadout)
+                u_io[vec_off + tid] = u;
+            else
+                ucol[tid] = u;
+        }
+        if constexpr (kMode == kSqReadout) return;
+        __syncthreads();
     }
-    __syncthreads();
-    if (tid < kD) {  // column tid: correction, output
-        const f32x2 t = (L.red[0][tid] + L.red[1][tid]) + (L.red[2][tid] + L.red[3][tid]);
-        const float u = bt * (vr - t.x);
-        y[vec_off + tid] = t.y + u * (kq_part[0] + kq_part[1]);
-        ucol[tid] = u;
-    }
-    __syncthreads();
 
     // ---- X_t = Diag(g) X_{t-1} + k u^T in registers, then packed
     float uc[8];
@@ -326,21 +353,27 @@ hipError_t launch_sq_pack(int heads, const float* S, const float* omega, void* Z
     return hipGetLastError();
 }
 
-hipError_t launch_sq_step(const StepArgs& a, void* Z, void* R, void* C, const float* omega, bool per_key, bool bf16,
-                          hipStream_t stream) {
+hipError_t launch_sq_step(const StepArgs& a, int mode, void* Z, void* R, void* C, const float* omega, float* u,
+                          bool per_key, bool bf16, hipStream_t stream) {
     auto go = [&](auto kernel, auto tag) {
         using T = decltype(tag);
         hipLaunchKernelGGL(kernel, dim3(a.heads), dim3(kThreads), 0, stream, static_cast<uint32_t*>(Z),
                            static_cast<half_t*>(R), static_cast<half_t*>(C), omega, static_cast<const T*>(a.q),
-                           static_cast<const T*>(a.k), static_cast<const T*>(a.v), a.gate, a.beta, a.y);
+                           static_cast<const T*>(a.k), static_cast<const T*>(a.v), a.gate, a.beta, u, a.y);
     };
-    if (per_key) {
-        if (bf16) go(sq_step_kernel<true, bf16_t>, bf16_t{});
-        else go(sq_step_kernel<true, float>, float{});
-    } else {
-        if (bf16) go(sq_step_kernel<false, bf16_t>, bf16_t{});
-        else go(sq_step_kernel<false, float>, float{});
-    }
+    auto by_mode = [&](auto mode_tag) {
+        constexpr int M = decltype(mode_tag)::value;
+        if (per_key) {
+            if (bf16) go(sq_step_kernel<M, true, bf16_t>, bf16_t{});
+            else go(sq_step_kernel<M, true, float>, float{});
+        } else {
+            if (bf16) go(sq_step_kernel<M, false, bf16_t>, bf16_t{});
+            else go(sq_step_kernel<M, false, float>, float{});
+        }
+    };
+    if (mode == kSqReadout) by_mode(std::integral_constant<int, kSqReadout>{});
+    else if (mode == kSqRepack) by_mode(std::integral_constant<int, kSqRepack>{});
+    else by_mode(std::integral_constant<int, kSqFused>{});
     return hipGetLastError();
 }
 

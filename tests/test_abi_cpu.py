@@ -173,6 +173,40 @@ def test_stepq_validation(lib):
         assert f(ctypes.byref(Dims(2, 0, 128, 128, 1)), *([None] * 10), None) == RSU_OK
 
 
+def test_stepq_split_validation(lib):
+    d32 = Dims(2, 3, 128, 128, 0)
+    for name, gname in (("gdn_stepq_readout", "alpha"), ("kda_stepq_readout", "d")):
+        f = getattr(lib, name)
+        f.restype = ctypes.c_int
+        args = [GOOD] * 10
+        bad = list(args)
+        bad[8] = None
+        assert f(ctypes.byref(d32), *bad, None) == E_NULL
+        assert "u is NULL" in _last(lib)
+        bad[8] = ODD
+        assert f(ctypes.byref(d32), *bad, None) == E_ALIGN
+        bad = list(args)
+        bad[6] = None
+        assert f(ctypes.byref(d32), *bad, None) == E_NULL
+        assert f"{gname} is NULL" in _last(lib)
+        assert f(ctypes.byref(Dims(2, 3, 128, 128, 9)), *args, None) == E_DTYPE
+        assert f(ctypes.byref(Dims(0, 3, 128, 128, 1)), *([None] * 10), None) == RSU_OK
+    for name, gname in (("gdn_stepq_repack", "alpha"), ("kda_stepq_repack", "d")):
+        f = getattr(lib, name)
+        f.restype = ctypes.c_int
+        args = [GOOD] * 7
+        for i, n in enumerate(("Z", "R", "C", "omega", "k", gname, "u")):
+            bad = list(args)
+            bad[i] = None
+            assert f(ctypes.byref(d32), *bad, None) == E_NULL
+            assert f"{n} is NULL" in _last(lib)
+        bad = list(args)
+        bad[6] = ODD
+        assert f(ctypes.byref(d32), *bad, None) == E_ALIGN
+        assert f(ctypes.byref(Dims(2, 3, 128, 96, 0)), *args, None) == E_DIMS
+        assert f(ctypes.byref(Dims(2, 0, 128, 128, 0)), *([None] * 7), None) == RSU_OK
+
+
 def test_copy_validation(lib):
     c = lib.rsu_copy_f32
     c.restype = ctypes.c_int

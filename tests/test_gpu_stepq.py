@@ -113,3 +113,48 @@ def test_stepq_empty_batch():
     m.gdn_stepq_step(buf["Z"], buf["R"], buf["C"], om, q, q, q, torch.zeros(0, 4, device=DEV),
                      torch.zeros(0, 4, device=DEV), y)
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("variant", ["gdn", "kda"])
+@pytest.mark.parametrize("shape", [(4, 6), (256, 48)])
+def test_stepq_split_equals_fused(variant, shape):
+    """The readout on the caller's stream and the repack on a second stream (ordered with
+    events, as a caller would overlap it with other work) give y and the new packed state of
+    the fused step bit for bit, step after step."""
+    from parity import dev_inputs
+    m = rsu()
+    w = wl.custom(BASE, B=shape[0], H=shape[1])
+    if variant == "kda":
+        w = _kda(w)
+    say(f"stepq split {variant} B={w.B} H={w.H}")
+    S0 = torch.from_numpy(wl.initial_state(w)).to(DEV).view(w.B, w.H, 128, 128)
+    om = torch.from_numpy(wl.row_influence(w)).to(DEV).view(w.B, w.H, 128)
+    a, b = new_stepq_buffers(w), new_stepq_buffers(w)
+    m.stepq_pack(S0, om, a["Z"], a["R"], a["C"])
+    del S0
+    for n in a:
+        b[n].copy_(a[n])
+    fused = m.kda_stepq_step if variant == "kda" else m.gdn_stepq_step
+    readout = m.kda_stepq_readout if variant == "kda" else m.gdn_stepq_readout
+    repack = m.kda_stepq_repack if variant == "kda" else m.gdn_stepq_repack
+    ya = torch.zeros(w.B, w.H, 128, device=DEV)
+    yb = torch.zeros_like(ya)
+    u = torch.zeros_like(ya)
+    side = torch.cuda.Stream()
+    main = torch.cuda.current_stream()
+    for t in range(4):
+        d = dev_inputs(w, t)[1]
+        fused(a["Z"], a["R"], a["C"], om, d["q"], d["k"], d["v"], d["gate"], d["beta"], ya)
+        readout(b["Z"], b["R"], b["C"], d["q"], d["k"], d["v"], d["gate"], d["beta"], u, yb)
+        done_read = torch.cuda.Event()
+        done_read.record(main)
+        with torch.cuda.stream(side):
+            side.wait_event(done_read)
+            repack(b["Z"], b["R"], b["C"], om, d["k"], d["gate"], u)
+            done_pack = torch.cuda.Event()
+            done_pack.record(side)
+        main.wait_event(done_pack)
+        torch.cuda.synchronize()
+        assert torch.equal(ya, yb), f"step {t}: y differs"
+        for n in a:
+            assert torch.equal(a[n], b[n]), f"step {t}: {n} differs"
