@@ -7,11 +7,12 @@
 //   w_i = omega_i^(1/8) / (their geometric mean over the head's rows)   (row influence weights;
 //         the compression exponent 0.25 applied to the RMS read weight sqrt(omega_i))
 //   r_i = fp16(sqrt(m_i / w_i)),  m_i = mean_j |X_ij|                   (0 for a zero row)
-//   a_j = max_i |X_ij / r_i|,  z_ij = clamp(rne(X_ij / r_i * 7 / a_j), -7, 7)   (0 if a_j = 0)
+//   a_j = max_i |X_ij / r_i|,  z_ij = rne(X_ij / r_i * 7 / a_j) in [-7, 7]    (0 if a_j = 0)
 //   c_j = fp16(sum_i w_i^2 r_i z_ij X_ij / sum_i w_i^2 r_i^2 z_ij^2)    (weighted least squares)
 // and a decode step decodes X_{t-1}, applies the dense update (decayed delta read, rank-one
 // write, y = X_t^T q from the updated state) and packs X_t, all in registers: the packed state
-// is read once and written once per step.
+// is read once and written once per step. The same kernel also runs the step as two launches,
+// the readout and then the repack, for callers that hide the repack on a second stream.
 //
 // Thread layout (as in the 4-bit LeapQuant sweep): lane l of wave w owns the code word of
 // value columns 8(l & 15) .. +7 in the key rows 16 it + 4 w + (l >> 4), it = 0..7, and keeps
