@@ -44,27 +44,21 @@ struct SqLds {
     float sc[kD];         // 7 / a_j, 0 for a zero column
     half_t rh[kD];        // r_i, stored coalesced after the row phase
     f32x2 red[4][kD];     // per-wave column partials
-    float lgw[4];         // per-wave sums of log2(omega^(1/8))
 };
 
-// Row influence weights from omega [128] (threads < 128 hold row tid): 1 / w_i and w_i^2 into
+// Row influence weights from omega [128]: threads < 128 write 1 / w_i and w_i^2 of row tid into
 // L, with w_i = omega_i^(1/8) / (their geometric mean) = 2^(l_i - mean(l)), l_i = log2(omega_i) / 8.
-// Every thread calls it; it ends with a barrier.
+// Each of the two waves reads all 128 scores, so the mean needs no exchange between waves; the
+// caller's next barrier publishes the weights.
 __device__ __forceinline__ void sq_row_weights(SqLds& L, const float* __restrict__ omega_h, int tid) {
-    const int wave = tid >> 6, lane = tid & 63;
-    float l = 0.f;
     if (tid < kD) {
-        l = __log2f(omega_h[tid]) * 0.125f;
-        const float s = wave_sum(l);
-        if (lane == 0) L.lgw[wave] = s;
-    }
-    __syncthreads();
-    if (tid < kD) {
-        const float d = l - (L.lgw[0] + L.lgw[1]) * (1.f / kD);  // log2 w_i
+        const int lane = tid & 63;
+        const float l0 = __log2f(omega_h[lane]) * 0.125f, l1 = __log2f(omega_h[lane + 64]) * 0.125f;
+        const float mean = wave_sum(l0 + l1) * (1.f / kD);
+        const float d = (tid < 64 ? l0 : l1) - mean;  // log2 w_i
         L.iw[tid] = exp2f(-d);
         L.wsq[tid] = exp2f(2.f * d);
     }
-    __syncthreads();
 }
 
 // 1.5 * 2^23: adding it rounds to an integer (half to even); for integers in [-7, 7] the low
@@ -73,7 +67,8 @@ constexpr float kRne = 12582912.0f;
 
 // Packs the lane's 64 elements x (rows sq_row(it, wave, l >> 4), columns 8 (l & 15) + e):
 // row factors, column ranges, codes (stored), weighted least squares column factors.
-// Overwrites x with u = x / r. L.iw and L.wsq must hold the row weights. Every thread calls it.
+// Overwrites x with u = x / r. L.iw and L.wsq must hold the row weights (published by a barrier).
+// Every thread calls it.
 __device__ __forceinline__ void sq_pack(SqLds& L, float (&x)[8][8], int tid, uint32_t* __restrict__ Zh,
                                         half_t* __restrict__ Rh, half_t* __restrict__ Ch) {
     const int wave = tid >> 6, lane = tid & 63;
@@ -212,6 +207,7 @@ __global__ __launch_bounds__(kThreads) void sq_pack_kernel(const float* __restri
         x[it][4] = b.x; x[it][5] = b.y; x[it][6] = b.z; x[it][7] = b.w;
     }
     sq_row_weights(L, omega + static_cast<size_t>(h) * kD, tid);
+    __syncthreads();
     sq_pack(L, x, tid, Z + static_cast<size_t>(h) * kD * (kD / 8), R + static_cast<size_t>(h) * kD,
             C + static_cast<size_t>(h) * kD);
 }
@@ -268,10 +264,8 @@ __global__ __launch_bounds__(kThreads) void sq_step_kernel(uint32_t* __restrict_
             if (lane == 0) kq_part[wave] = kq;
         }
     }
-    if constexpr (kPack)
-        sq_row_weights(L, omega + vec_off, tid);  // (its barriers also publish rowv and ucol)
-    else
-        __syncthreads();
+    if constexpr (kPack) sq_row_weights(L, omega + vec_off, tid);
+    __syncthreads();  // publishes rowv, the row weights and (repack) ucol
 
     // ---- decode X_{t-1} = r c z (the column factor applied here, the row factor through rowv),
     // and the two column sums of the old state: p = X^T (g k), o = X^T (g q)

@@ -70,6 +70,16 @@ def test_stepq_uniform_influence():
     _assert_ok(run_stepq(w, steps=3, om=np.full((w.heads, 128), 3.5, np.float32)))
 
 
+def test_stepq_extreme_influence_spread():
+    """omega log-uniform over 24 decades (w over 6): the row weights' log2 / exp2 path and the
+    fp16 factors stay within the oracle's bars."""
+    w = wl.custom(BASE, B=2, H=3)
+    rng = np.random.default_rng(17)
+    om = (10.0 ** rng.uniform(-12, 12, size=(w.heads, 128))).astype(np.float32)
+    say("stepq extreme omega")
+    _assert_ok(run_stepq(w, steps=3, om=om))
+
+
 def test_stepq_zero_state():
     """A zero state packs to zero codes and factors; the first step then writes k (beta v)^T."""
     w = wl.custom(BASE, B=2, H=3)
