@@ -540,7 +540,7 @@ def main():
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(this build has no multi-GPU path).", file=sys.stderr)
+              "(the library has no multi-GPU path).", file=sys.stderr)
         sys.exit(2)
 
     w = wl.WORKLOADS[WORKLOAD_BY_FLAG[args.workload]]
