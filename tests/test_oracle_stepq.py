@@ -165,3 +165,28 @@ def test_fit_lowers_the_weighted_error_against_per_row_scaling(seed):
     zr = np.clip(np.rint(X / s[:, None]), -7, 7)
     e_row = float(np.sum((w ** 2)[:, None] * (X - s[:, None] * zr) ** 2))
     assert e_dual < e_row
+
+
+def test_column_and_row_permutations_and_sign_are_equivariant():
+    """Permuting value columns permutes codes and column factors; permuting key rows together
+    with their influence scores permutes codes and row factors; negating X negates the codes.
+    A row/column mix-up in the fit breaks at least one of these."""
+    rng = np.random.default_rng(7)
+    X = _state(rng)
+    om = _omega(rng)
+    w = stepq.row_weights(om)
+    p = stepq.pack(X, w)
+    pc = rng.permutation(128)
+    q = stepq.pack(X[:, pc], w)
+    np.testing.assert_array_equal(q["z"], p["z"][:, pc])
+    np.testing.assert_array_equal(q["c"], p["c"][pc])
+    np.testing.assert_array_equal(q["r"], p["r"])
+    pr = rng.permutation(128)
+    q = stepq.pack(X[pr], stepq.row_weights(om[pr]))
+    np.testing.assert_array_equal(q["z"], p["z"][pr])
+    np.testing.assert_array_equal(q["r"], p["r"][pr])
+    np.testing.assert_allclose(q["c"], p["c"], rtol=0, atol=0)
+    n = stepq.pack(-X, w)
+    np.testing.assert_array_equal(n["z"], -p["z"])
+    np.testing.assert_array_equal(n["r"], p["r"])
+    np.testing.assert_array_equal(n["c"], p["c"])
