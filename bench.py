@@ -431,6 +431,20 @@ def run_gpu(w: wl.Workload, steps: int, warmup: int, slots: bool = False, n_iter
             per[i % cyc] += evs[i].elapsed_time(evs[i + 1]) * 1e3 / 4
         key = "pos" if w.path in ("q8_window", "lq_window") else ("step" if slots else "L")
         phases = {f"{key}{i}_us": round(t, 2) for i, t in enumerate(per)}
+    # one untimed pass with an event between consecutive launches: the distribution of step
+    # times (whole cycles for the window and log paths, so that every position is included)
+    cyc = {"q8_window": w.W, "lq_window": w.W, "log": w.M}.get(w.path, 1)
+    n_dist = max(cyc, min(steps, 64) // cyc * cyc)
+    evd = [torch.cuda.Event(enable_timing=True) for _ in range(n_dist + 1)]
+    evd[0].record(stream)
+    for e in evd[1:]:
+        step()
+        e.record(stream)
+    torch.cuda.synchronize()
+    per_step = np.array([evd[i].elapsed_time(evd[i + 1]) * 1e3 for i in range(n_dist)])
+    dist = {"n": n_dist, "median_us": round(float(np.median(per_step)), 2),
+            "p10_us": round(float(np.percentile(per_step, 10)), 2),
+            "p90_us": round(float(np.percentile(per_step, 90)), 2)}
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     if graph:
         # the K steps' launches captured once (capturing runs nothing; the host-side step
@@ -460,7 +474,7 @@ def run_gpu(w: wl.Workload, steps: int, warmup: int, slots: bool = False, n_iter
     if split:
         phases = split_phases()
     ceiling = copy_ceiling(torch, rsu, 4 * B * H * 128 * 128) if w.path == "dense" else None
-    return gpu_sec, wall, ceiling, phases
+    return gpu_sec, wall, ceiling, phases, dist
 
 
 # ----------------------------------------------------------------- CPU baseline (oracle)
@@ -553,7 +567,7 @@ def main():
 
     if args.split and (w.path != "stepq" or args.graph):
         raise SystemExit("--split applies to the stepq workload, without --graph")
-    gpu_sec, wall, ceiling, phases = run_gpu(w, steps, warmup, args.slots, args.n_iter, args.graph, args.split)
+    gpu_sec, wall, ceiling, phases, dist = run_gpu(w, steps, warmup, args.slots, args.n_iter, args.graph, args.split)
     heads = w.heads
     per_head = slots_bytes_per_head(w) if args.slots else cycle_bytes_per_head(w)
     launch_sec = gpu_sec / steps
@@ -590,6 +604,7 @@ def main():
         "timing": ("the K steps captured as one HIP graph, replayed once" if args.graph else
                    "eager launches, readout and repack on two streams" if args.split else "eager launches"),
     }
+    out["step_time_distribution"] = dist
     if phases:
         out["phases"] = phases
     if not args.no_cpu_baseline and w is wl.WORKLOADS[WORKLOAD_BY_FLAG["gdn"]]:
