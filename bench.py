@@ -479,6 +479,17 @@ def run_gpu(w: wl.Workload, steps: int, warmup: int, slots: bool = False, n_iter
 
 # ----------------------------------------------------------------- CPU baseline (oracle)
 
+def _cpu_model() -> str | None:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def run_cpu_baseline(w: wl.Workload, budget_s: float = 10.0, max_steps: int = 4096):
     """The fp64 oracle (as it stands) on the host cores: every head of the workload,
     consecutive steps (cycling the workload's distinct step inputs) until the
@@ -495,7 +506,8 @@ def run_cpu_baseline(w: wl.Workload, budget_s: float = 10.0, max_steps: int = 40
         t_total += time.perf_counter() - t0
         n_steps += 1
     return {"value": w.heads * n_steps / t_total, "unit": "head-updates/s",
-            "cores": oracle.num_threads(), "kind": "oracle",
+            "cores": oracle.num_threads(), "kind": "oracle", "cpu_model": _cpu_model(),
+            "host_cpus": os.cpu_count(),
             "sample": f"all {w.heads} heads x {n_steps} consecutive steps of the same workload "
                       f"(fp64 oracle, {t_total:.1f} s of compute)"}
 
