@@ -18,7 +18,9 @@ dense step (LeapQuant sec. 3.1, App. A; STEPQuant notes, Proposition 1)
   * error recursion E_t = D E_{t-1} - beta k (E_{t-1}^T (g k))^T + eps_t (LeapQuant eq. 8)
 quantizer: hand-built ties (round half to even), absmax maps to +-127, zero rows
 window path: equals the explicit dequantize / dense steps / requantize schedule
-  (eq. 4 unrolls eq. 3); the eq. 9 readout computed independently
+  (eq. 4 unrolls eq. 3); the eq. 9 readout computed independently; on an exactly
+  representable state (the identity-quantizer case) the first window is dense decoding;
+  the per-window error stays below the per-step error (the page's trend)
 log path: equals eager decoding at every step (DeltaLog eq. 7 and closure), M = 1
   reduces to eager, slot reset
 tiny cases: the fp64 oracle agrees with exact rational brute force, and the
@@ -405,3 +407,47 @@ def test_exact_window_matches_fp64_window_oracle():
             nb += 1
             np.testing.assert_array_equal(ws.Z[0], np.array(Zx))
             np.testing.assert_allclose(ws.a[0], np.array(ax, dtype=float), rtol=1e-7)
+
+
+@pytest.mark.parametrize("per_key", [False, True])
+def test_window_with_an_exactly_representable_state_is_dense(per_key):
+    """The identity-quantizer case: rows whose absmax is 127 * 2^e and whose entries are
+    integer multiples of 2^e quantize exactly (the scale 127 / a = 2^-e is exact), so until
+    the first requantization the window path must reproduce dense decoding from S_0. A slip
+    in the readout's scale (/128 for /127, the scale applied twice, a wrong row) breaks it."""
+    rng = np.random.default_rng(31)
+    nh, dk, dv, W = 4, 128, 128, 8
+    codes = rng.integers(-127, 128, size=(nh, dk, dv)).astype(np.float64)
+    codes[:, :, 0] = np.where(rng.random((nh, dk)) < 0.5, 127.0, -127.0)   # absmax 127 in every row
+    e = rng.integers(-12, -4, size=(nh, dk, 1)).astype(np.float64)
+    S0 = codes * 2.0 ** e
+    Z, a = oracle.q8_quantize(S0)
+    np.testing.assert_array_equal(Z.astype(np.float64), codes)
+    np.testing.assert_array_equal(oracle.dequant(Z, a), S0)
+    ws = oracle.WindowState(Z, a, W, per_key)
+    S = S0.copy()
+    for _ in range(W - 1):
+        q, k, v, g, b = _inputs(nh, dk, dv, per_key, rng)
+        y_w = ws.step(q, k, v, g, b)
+        y_d = oracle.dense_step(S, q, k, v, g, b)
+        np.testing.assert_allclose(y_w, y_d, rtol=0, atol=1e-12 * np.abs(y_d).max())
+
+
+def test_window_error_is_below_per_step_error():
+    """LeapQuant's point about windows: against the fp32-exact trajectory, quantizing once per
+    window of 16 leaves less output error than quantizing after every step (W = 1), because
+    rounding enters 16 times less often. A trend the page reports, checked on one seeded run."""
+    rng = np.random.default_rng(8)
+    nh, dk, dv, T = 6, 128, 128, 64
+    S0 = rng.standard_normal((nh, dk, dv)) * 0.02
+    S0[:, 3, :] *= 50
+    steps = [_inputs(nh, dk, dv, False, rng) for _ in range(T)]
+    S = S0.copy()
+    ref = [oracle.dense_step(S, *x) for x in steps]
+    err = {}
+    for W in (1, 16):
+        Z, a = oracle.q8_quantize(S0)
+        ws = oracle.WindowState(Z, a, W, False)
+        e = [np.linalg.norm(ws.step(*x) - r) / np.linalg.norm(r) for x, r in zip(steps, ref)]
+        err[W] = float(np.mean(e))
+    assert err[16] < err[1]
