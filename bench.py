@@ -490,26 +490,94 @@ def _cpu_model() -> str | None:
     return None
 
 
-def run_cpu_baseline(w: wl.Workload, budget_s: float = 10.0, max_steps: int = 4096):
-    """The fp64 oracle (as it stands) on the host cores: every head of the workload,
-    consecutive steps (cycling the workload's distinct step inputs) until the
-    time budget is spent."""
+def run_cpu_baseline(w: wl.Workload, budget_s: float = 10.0, max_steps: int = 4096, slots: bool = False,
+                     n_iter: int = 1):
+    """The fp64 oracle (as it stands) of the workload's own path on the host cores: consecutive
+    steps (cycling the workload's distinct step inputs) until the time budget is spent, on all
+    heads for the dense steps and on the first 512 heads where the oracle loops over heads in
+    Python (LeapQuant's refit, the packed state) or keeps per-window records. Only the oracle
+    calls are timed."""
     import oracle
     oracle.build(force=False)
-    S = wl.initial_state(w).astype(np.float64)
-    inputs = [wl.step_inputs(w, t) for t in range(w.steps)]
+    n = w.heads if w.path == "dense" else min(w.heads, 512)
+    S = wl.initial_state(w)[:n].astype(np.float64)
+    cache = {}
+
+    def inputs(t):
+        i = t % max(1, w.steps)
+        if i not in cache:
+            x = wl.step_inputs(w, i)
+            cache[i] = {name: a[:n] for name, a in x.items()}
+        return cache[i]
+
+    step = None
+    if w.path == "dense":
+        if w.variant == "rwkv6":
+            def step(x): oracle.rwkv6_step(S, x["q"], x["k"], x["v"], x["gate"])  # noqa: E704
+        elif w.variant == "rwkv7":
+            def step(x): oracle.rwkv7_step(S, x["q"], x["k"], x["v"], x["gate"], x["kappa"], x["a"])  # noqa: E704
+        else:
+            def step(x): oracle.dense_step(S, x["q"], x["k"], x["v"], x["gate"], x["beta"])  # noqa: E704
+    elif w.path == "q8_window":
+        Z, a = oracle.q8_quantize(S)
+        if w.variant == "rwkv7":
+            ws = oracle.Rwkv7WindowState(Z, a, w.W)
+
+            def step(x): ws.step(x["q"], x["k"], x["v"], x["gate"], x["kappa"], x["a"])  # noqa: E704
+        else:
+            ws = oracle.WindowState(Z, a, w.W, w.per_key_gate)
+
+            def step(x): ws.step(x["q"], x["k"], x["v"], x["gate"], x["beta"])  # noqa: E704
+    elif w.path == "log":
+        ls = oracle.LogState(S, w.M - 1, w.per_key_gate, rwkv6=w.variant == "rwkv6")
+        Ls = slot_lengths(w)[:n].copy() if slots else None
+
+        def step(x):
+            if slots:
+                ls.step_slots(Ls, x["q"], x["k"], x["v"], x["gate"], x.get("beta"))
+            else:
+                ls.step(x["q"], x["k"], x["v"], x["gate"], x.get("beta"))
+    elif w.path == "lq_window":
+        from oracle import lq
+        qmax = lq.qmax_of(w.bits)
+        r = 8 if w.bits == 4 else LQ_TOKENS
+        reps = [lq.boundary(S[i], lq.walsh_start(r=r), 8, qmax) for i in range(n)]
+        st = {"pos": 0, "S": None}
+
+        def step(x):
+            if st["pos"] == 0:
+                st["S"] = np.stack([lq.represent(p["Z"], p["B"], p["c"], p["K16"], p["U16"], qmax) for p in reps])
+            oracle.dense_step(st["S"], x["q"], x["k"], x["v"], x["gate"], x["beta"])
+            st["pos"] += 1
+            if st["pos"] == w.W:
+                for i in range(n):
+                    reps[i] = lq.boundary(st["S"][i], reps[i]["U"], n_iter, qmax)
+                st["pos"] = 0
+    elif w.path == "stepq":
+        from oracle import stepq
+        om = wl.row_influence(w)[:n].astype(np.float64)
+        wts = stepq.row_weights(om)
+        packs = [stepq.pack(S[i], wts[i]) for i in range(n)]
+        st = {"z": np.stack([p["z"] for p in packs]), "r": np.stack([p["r"] for p in packs]),
+              "c": np.stack([p["c"] for p in packs])}
+
+        def step(x):
+            _, new, _ = stepq.step(st["z"], st["r"], st["c"], om, x["q"], x["k"], x["v"], x["gate"], x["beta"])
+            st["z"] = np.stack([p["z"] for p in new])
+            st["r"] = np.stack([p["r"] for p in new])
+            st["c"] = np.stack([p["c"] for p in new])
     n_steps, t_total = 0, 0.0
     while n_steps < max_steps and t_total < budget_s:
-        x = inputs[n_steps % len(inputs)]
+        x = inputs(n_steps)
         t0 = time.perf_counter()
-        oracle.dense_step(S, x["q"], x["k"], x["v"], x["gate"], x["beta"])
+        step(x)
         t_total += time.perf_counter() - t0
         n_steps += 1
-    return {"value": w.heads * n_steps / t_total, "unit": "head-updates/s",
+    sample = f"{'all' if n == w.heads else 'the first'} {n} of {w.heads} heads x {n_steps} consecutive steps " \
+             f"of the same workload (fp64 oracle of this path, {t_total:.1f} s of compute)"
+    return {"value": n * n_steps / t_total, "unit": "head-updates/s",
             "cores": oracle.num_threads(), "kind": "oracle", "cpu_model": _cpu_model(),
-            "host_cpus": os.cpu_count(),
-            "sample": f"all {w.heads} heads x {n_steps} consecutive steps of the same workload "
-                      f"(fp64 oracle, {t_total:.1f} s of compute)"}
+            "host_cpus": os.cpu_count(), "sample": sample}
 
 
 def override_workload(w: wl.Workload, args) -> wl.Workload:
@@ -619,8 +687,8 @@ def main():
     out["step_time_distribution"] = dist
     if phases:
         out["phases"] = phases
-    if not args.no_cpu_baseline and w is wl.WORKLOADS[WORKLOAD_BY_FLAG["gdn"]]:
-        out["cpu_baseline"] = run_cpu_baseline(w)
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = run_cpu_baseline(w, slots=args.slots, n_iter=args.n_iter)
     print(json.dumps(out), flush=True)
 
 
