@@ -28,6 +28,7 @@
 namespace rsu {
 
 typedef _Float16 half_t;
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 
 namespace {
 
@@ -61,6 +62,24 @@ __device__ __forceinline__ void sq_row_weights(SqLds& L, const float* __restrict
     }
 }
 
+// Three bf16 parts of an fp32 value (hi = bf16(x), mid = bf16(x - hi), lo = bf16(x - hi - mid);
+// both differences are exact in fp32): hi + mid + lo equals x to about 2^-24 |x|.
+__device__ __forceinline__ void sq_split3(float x, uint16_t& hi, uint16_t& mid, uint16_t& lo) {
+    const __bf16 h = static_cast<__bf16>(x);
+    const float r1 = x - static_cast<float>(h);
+    const __bf16 m = static_cast<__bf16>(r1);
+    const __bf16 l = static_cast<__bf16>(r1 - static_cast<float>(m));
+    hi = __builtin_bit_cast(uint16_t, h);
+    mid = __builtin_bit_cast(uint16_t, m);
+    lo = __builtin_bit_cast(uint16_t, l);
+}
+
+// c ? x : y as one bitfield insert on the values' bits.
+__device__ __forceinline__ float bit_select(int c, float x, float y) {
+    const uint32_t m = c ? 0xffffffffu : 0u;
+    return __uint_as_float((__float_as_uint(x) & m) | (__float_as_uint(y) & ~m));
+}
+
 // 1.5 * 2^23: adding it rounds to an integer (half to even); for integers in [-7, 7] the low
 // byte of the sum's bits is that integer's two's complement
 constexpr float kRne = 12582912.0f;
@@ -86,12 +105,14 @@ __device__ __forceinline__ void sq_pack(SqLds& L, float (&x)[8][8], int tid, uin
             for (int e = 0; e < 8; ++e) t += fabsf(x[it][e]);
             a[it] = row16_sum(t);
         }
+        // a[c16 & 7] by three rounds of bitwise selects (written as selects, the compiler turns
+        // them into an index into a private array, which lives in scratch memory)
         float s1[4], s2[2];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) s1[j] = (c16 & 1) ? a[2 * j + 1] : a[2 * j];
+        for (int j = 0; j < 4; ++j) s1[j] = bit_select(c16 & 1, a[2 * j + 1], a[2 * j]);
 #pragma unroll
-        for (int j = 0; j < 2; ++j) s2[j] = (c16 & 2) ? s1[2 * j + 1] : s1[2 * j];
-        const float sum = (c16 & 4) ? s2[1] : s2[0];
+        for (int j = 0; j < 2; ++j) s2[j] = bit_select(c16 & 2, s1[2 * j + 1], s1[2 * j]);
+        const float sum = bit_select(c16 & 4, s2[1], s2[0]);
         const int row = sq_row(c16 & 7, wave, rl);
         const half_t rh = static_cast<half_t>(sqrtf(sum * (1.f / kD) * L.iw[row]));
         const float r = static_cast<float>(rh);
@@ -228,9 +249,17 @@ __global__ __launch_bounds__(kThreads) void sq_step_kernel(uint32_t* __restrict_
                                                            float* __restrict__ y) {
     constexpr bool kRead = kMode != kSqRepack, kPack = kMode != kSqReadout;
     __shared__ SqLds L;
-    __shared__ f32x4 rowv[kD];   // (r g k, r g q, r g, k) of key row i
+    __shared__ f32x2 rowv[kD];   // (r g, k) of key row i
     __shared__ float ucol[kD];   // u_j
     __shared__ float kq_part[2];
+    // The column sums p = X^T (g k) and o = X^T (g q) run on the matrix cores: per value column
+    // e of a lane, one v_mfma_f32_16x16x32_bf16 with B = the lane's 8 codes of that column (as
+    // 16 z, exact in bf16; k = 8 rl + it indexes the wave's 32 rows) and A = the read vectors
+    // r g k and r g q of those rows, each in three bf16 parts (rows m = 0..2 and 4..6 of A; the
+    // products are exact and accumulate in fp32). apart[3 v + part][wave][rl] holds the 8 bf16
+    // of rows lq_row(it = 0..7) that lane (m, rl) supplies.
+    __shared__ uint4 apart[6][4][4];
+    __shared__ f32x4 redpo[2][4][kD / 4];  // per-wave column sums of the old state: p, o
     const int h = head_of_block(blockIdx.x, gridDim.x), tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
     const int c16 = lane & 15, rl = lane >> 4;
@@ -258,7 +287,20 @@ __global__ __launch_bounds__(kThreads) void sq_step_kernel(uint32_t* __restrict_
     const float bt = kRead ? beta[h] : 0.f;
     if (tid < kD) {
         const float rg = rr * gr;
-        rowv[tid] = f32x4{rg * kr, rg * qr, rg, kr};
+        rowv[tid] = f32x2{rg, kr};
+        if constexpr (kRead) {
+            const int it = tid >> 4, w = (tid >> 2) & 3, r4 = tid & 3;  // tid = sq_row(it, w, r4)
+            uint16_t* ap = reinterpret_cast<uint16_t*>(apart);
+            uint16_t hi, mid, lo;
+            sq_split3(rg * kr, hi, mid, lo);
+            ap[((0 * 4 + w) * 4 + r4) * 8 + it] = hi;
+            ap[((1 * 4 + w) * 4 + r4) * 8 + it] = mid;
+            ap[((2 * 4 + w) * 4 + r4) * 8 + it] = lo;
+            sq_split3(rg * qr, hi, mid, lo);
+            ap[((3 * 4 + w) * 4 + r4) * 8 + it] = hi;
+            ap[((4 * 4 + w) * 4 + r4) * 8 + it] = mid;
+            ap[((5 * 4 + w) * 4 + r4) * 8 + it] = lo;
+        }
         if constexpr (kRead) {
             const float kq = wave_sum(kr * qr);
             if (lane == 0) kq_part[wave] = kq;
@@ -267,52 +309,56 @@ __global__ __launch_bounds__(kThreads) void sq_step_kernel(uint32_t* __restrict_
     if constexpr (kPack) sq_row_weights(L, omega + vec_off, tid);
     __syncthreads();  // publishes rowv, the row weights and (repack) ucol
 
-    // ---- decode X_{t-1} = r c z (the column factor applied here, the row factor through rowv),
-    // and the two column sums of the old state: p = X^T (g k), o = X^T (g q)
-    float cz[8][8];
+    // ---- the codes as floats 16 z, the two column sums of the old state p = X^T (g k) and
+    // o = X^T (g q) on the matrix cores (c / 16 applied to each column's sum), and the decoded
+    // X_{t-1} = r c z (the column factor applied here, the row factor with the gate in rowv)
     float cc[8];
     {
         const half_t* ch = reinterpret_cast<const half_t*>(&cw);
 #pragma unroll
         for (int e = 0; e < 8; ++e) cc[e] = static_cast<float>(ch[e]) * 0.0625f;  // the codes come as 16 z
     }
-    float p[8], o[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) p[e] = o[e] = 0.f;
+    float zf[8][8];  // 16 z
 #pragma unroll
     for (int it = 0; it < 8; ++it) {
-        const f32x4 rv = rowv[sq_row(it, wave, rl)];
         const uint32_t ev = (zw[it] << 4) & 0xF0F0F0F0u, od = zw[it] & 0xF0F0F0F0u;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            cz[it][2 * j] = static_cast<float>(static_cast<int8_t>(ev >> (8 * j))) * cc[2 * j];
-            cz[it][2 * j + 1] = static_cast<float>(static_cast<int8_t>(od >> (8 * j))) * cc[2 * j + 1];
-        }
-        if constexpr (kRead) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                p[e] = fmaf(cz[it][e], rv.x, p[e]);
-                o[e] = fmaf(cz[it][e], rv.y, o[e]);
-            }
+            zf[it][2 * j] = static_cast<float>(static_cast<int8_t>(ev >> (8 * j)));
+            zf[it][2 * j + 1] = static_cast<float>(static_cast<int8_t>(od >> (8 * j)));
         }
     }
     if constexpr (kRead) {
-        {
-            float qp[4], qo[4];
+        // lane (m = l & 15, rl): A row m is part m % 4 of read vector m / 4 (m % 4 == 3 and m >= 8: zero)
+        const int m = c16, am = (m >> 2) * 3 + (m & 3);
+        const bool live = m < 8 && (m & 3) != 3;
+        const uint4 aw = live ? apart[am][wave][rl] : uint4{0u, 0u, 0u, 0u};
+        const bf16x8_t av = __builtin_bit_cast(bf16x8_t, aw);
+        float part[8];  // lane rl = 0: p of column 8 c16 + e; rl = 1: o; others unused
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                qp[e] = add_pair16(p[e], p[e + 4]);
-                qo[e] = add_pair16(o[e], o[e + 4]);
-            }
-            *reinterpret_cast<f32x4*>(L.red[wave] + 8 * c16 + 4 * b4 + 2 * b5) =
-                f32x4{add_pair32(qp[0], qp[2]), add_pair32(qo[0], qo[2]), add_pair32(qp[1], qp[3]),
-                      add_pair32(qo[1], qo[3])};
+        for (int e = 0; e < 8; ++e) {
+            uint4 bw;
+            bw.x = __builtin_amdgcn_perm(__float_as_uint(zf[1][e]), __float_as_uint(zf[0][e]), 0x07060302u);
+            bw.y = __builtin_amdgcn_perm(__float_as_uint(zf[3][e]), __float_as_uint(zf[2][e]), 0x07060302u);
+            bw.z = __builtin_amdgcn_perm(__float_as_uint(zf[5][e]), __float_as_uint(zf[4][e]), 0x07060302u);
+            bw.w = __builtin_amdgcn_perm(__float_as_uint(zf[7][e]), __float_as_uint(zf[6][e]), 0x07060302u);
+            const f32x4 d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8_t, bw),
+                                                                    f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+            part[e] = (d.x + d.y + d.z) * cc[e];
+        }
+        if (rl < 2) {
+            f32x4* dst = redpo[rl][wave] + 2 * c16;
+            dst[0] = f32x4{part[0], part[1], part[2], part[3]};
+            dst[1] = f32x4{part[4], part[5], part[6], part[7]};
         }
         __syncthreads();
         if (tid < kD) {  // column tid: correction, output
-            const f32x2 t = (L.red[0][tid] + L.red[1][tid]) + (L.red[2][tid] + L.red[3][tid]);
-            const float u = bt * (vr - t.x);
-            y[vec_off + tid] = t.y + u * (kq_part[0] + kq_part[1]);
+            const float* rp = reinterpret_cast<const float*>(redpo[0]);
+            const float* ro = reinterpret_cast<const float*>(redpo[1]);
+            const float pt = (rp[tid] + rp[kD + tid]) + (rp[2 * kD + tid] + rp[3 * kD + tid]);
+            const float ot = (ro[tid] + ro[kD + tid]) + (ro[2 * kD + tid] + ro[3 * kD + tid]);
+            const float u = bt * (vr - pt);
+            y[vec_off + tid] = ot + u * (kq_part[0] + kq_part[1]);
             if constexpr (kMode == kSqReadout)
                 u_io[vec_off + tid] = u;
             else
@@ -321,6 +367,11 @@ __global__ __launch_bounds__(kThreads) void sq_step_kernel(uint32_t* __restrict_
         if constexpr (kMode == kSqReadout) return;
         __syncthreads();
     }
+    float cz[8][8];
+#pragma unroll
+    for (int it = 0; it < 8; ++it)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) cz[it][e] = zf[it][e] * cc[e];
 
     // ---- X_t = Diag(g) X_{t-1} + k u^T in registers, then packed
     float uc[8];
@@ -332,9 +383,9 @@ __global__ __launch_bounds__(kThreads) void sq_step_kernel(uint32_t* __restrict_
     }
 #pragma unroll
     for (int it = 0; it < 8; ++it) {
-        const f32x4 rv = rowv[sq_row(it, wave, rl)];
+        const f32x2 rv = rowv[sq_row(it, wave, rl)];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) cz[it][e] = fmaf(rv.z, cz[it][e], rv.w * uc[e]);
+        for (int e = 0; e < 8; ++e) cz[it][e] = fmaf(rv.x, cz[it][e], rv.y * uc[e]);
     }
     sq_pack(L, cz, tid, Zh, R + vec_off, C + vec_off);
 }
