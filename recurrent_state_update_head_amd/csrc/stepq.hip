@@ -263,7 +263,6 @@ __global__ __launch_bounds__(kThreads) void sq_step_kernel(uint32_t* __restrict_
     const int h = head_of_block(blockIdx.x, gridDim.x), tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
     const int c16 = lane & 15, rl = lane >> 4;
-    const int b4 = (lane >> 4) & 1, b5 = lane >> 5;
     const size_t vec_off = static_cast<size_t>(h) * kD;
     uint32_t* Zh = Z + static_cast<size_t>(h) * kD * (kD / 8);
 
