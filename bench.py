@@ -12,8 +12,12 @@ Prints ONE JSON line on stdout:
   value = state head-updates per second (B*H*K / timed seconds),
   roofline = algorithmic HBM bytes per launch / average launch time vs 8 TB/s,
   cpu_baseline = the fp64 oracle timed on the host cores on a bounded sample.
-Other workloads (--workload kda|q8|log|gdn_small) report the same fields for
-their own kernels; they are measurements, not the headline line.
+Other workloads (--workload kda|q8|log|lq|kda_lq|lq4|rwkv6|rwkv6_log|rwkv7|rwkv7_q8|
+stepq|gdn_small) report the same fields for their own kernels, with the CPU baseline
+timing the oracle of their own path; they are measurements, not the headline line.
+Per-launch timing of window positions / log lengths goes to "phases", a launch-by-launch
+pass to "step_time_distribution"; --graph replays the timed steps as one HIP graph and
+--split (stepq) runs the readout and the repack on two streams.
 """
 from __future__ import annotations
 
