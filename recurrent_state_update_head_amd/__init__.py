@@ -15,7 +15,9 @@ Shapes (B requests, H heads, d = 128):
   Klog [B,H,C,d] (q dtype), Ulog [B,H,C,d] fp32, Lam [B,H,C] or [B,H,C,d] fp32,
   lbar [B,H] or [B,H,d] fp32, per-slot live lengths L [B,H] int32
   LeapQuant format: Z [B,H,d,d] int8, col_absmax [B,H,d] fp32, row_smooth [B,H,d] fp32,
-  Kc, Uc [B,H,4,d] fp16
+  Kc, Uc [B,H,4,d] fp16 (4 bits: Z [B,H,d,d/2] uint8 nibbles, Kc, Uc [B,H,8,d] fp16)
+  STEPQuant packed state: Z [B,H,d,d/2] uint8 nibbles, R, C [B,H,d] fp16, omega [B,H,d] fp32,
+  u [B,H,d] fp32 (the readout's correction, consumed by the repack)
 """
 from __future__ import annotations
 
