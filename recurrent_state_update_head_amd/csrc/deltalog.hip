@@ -77,7 +77,13 @@ __global__ __launch_bounds__(kThreads) void log_step_kernel(
     constexpr bool merge = kMode == kMergeMode || kMode == kSlotMerge;
     int L = L_uniform;
     if constexpr (kSlots) {
-        L = min(max(Lslot[h], 0), C);
+        // One thread reads the live length and the workgroup takes it from LDS: Lslot[h]
+        // is advanced below by thread 0, so no other thread may read it from memory
+        // after that write (the barrier orders the one read before the one write).
+        __shared__ int L_head;
+        if (tid == 0) L_head = min(max(Lslot[h], 0), C);
+        __syncthreads();
+        L = L_head;
         if (kMode == kSlotAppend && L == C) return;  // merged by the second pass
         if (kMode == kSlotMerge && L < C) {          // appended by the first pass
             if (tid == 0) Lslot[h] = L + 1;
@@ -122,7 +128,7 @@ __global__ __launch_bounds__(kThreads) void log_step_kernel(
     float* Sh = Sbase + static_cast<size_t>(h) * kD * kD;
     f32x4 s[kRowsPerThread];
 #pragma unroll
-    for (int it = 0; it < kRowsPerThread; ++it) s[it] = stream_load(Sh + (it * 8 + ro) * kD + col);
+    for (int it = 0; it < kRowsPerThread; ++it) s[it] = stream_load(Sh + (row_block(it, wave) * 8 + ro) * kD + col);
 
     land(0);
     for (int m0 = kChunk; m0 < L; m0 += kChunk) {
@@ -195,7 +201,7 @@ __global__ __launch_bounds__(kThreads) void log_step_kernel(
     f32x4 p1 = {0.f, 0.f, 0.f, 0.f}, p2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int it = 0; it < kRowsPerThread; ++it) {
-        const f32x4 rv = row_vec[it * 8 + ro];
+        const f32x4 rv = row_vec[row_block(it, wave) * 8 + ro];
         if constexpr (kDelta) p1 += s[it] * rv.x;
         p2 += s[it] * rv.y;
     }
@@ -218,7 +224,7 @@ __global__ __launch_bounds__(kThreads) void log_step_kernel(
     // ---- merge (eq. 6): Sbar <- D(lbar') Sbar + sum_m D(lbar'-Lam_m) K_m U_m^T + k b^T
 #pragma unroll
     for (int it = 0; it < kRowsPerThread; ++it) {
-        const f32x4 rv = row_vec[it * 8 + ro];
+        const f32x4 rv = row_vec[row_block(it, wave) * 8 + ro];
         s[it] = s[it] * rv.w + rv.z * b;
     }
     for (int m0 = 0; m0 < L; m0 += 4) {
@@ -229,12 +235,12 @@ __global__ __launch_bounds__(kThreads) void log_step_kernel(
                                 : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int it = 0; it < kRowsPerThread; ++it) {
-            const f32x4 e = *reinterpret_cast<const f32x4*>(kd + (it * 8 + ro) * Cp + m0);
+            const f32x4 e = *reinterpret_cast<const f32x4*>(kd + (row_block(it, wave) * 8 + ro) * Cp + m0);
             s[it] += u[0] * e.x + u[1] * e.y + u[2] * e.z + u[3] * e.w;
         }
     }
 #pragma unroll
-    for (int it = 0; it < kRowsPerThread; ++it) stream_store(Sh + (it * 8 + ro) * kD + col, s[it]);
+    for (int it = 0; it < kRowsPerThread; ++it) stream_store(Sh + (row_block(it, wave) * 8 + ro) * kD + col, s[it]);
 }
 
 template <bool kPerKey, bool kDelta, int kMode, typename T>
