@@ -2,9 +2,10 @@
 the C ABI, run the fp64 oracle on the same inputs (all heads, or sampled heads
 at full size), and measure the error as the pages' tolerances define it.
 
-Error metric: for every (head, step), the norm-wise relative error
-||x_gpu - x_ref||_2 / ||x_ref||_2 over the head's output vector (or state
-matrix); the maximum over heads and steps is compared with the tolerance.
+Error metric: for every (head, step), two relative errors over the head's output
+vector (or state matrix): the norm-wise ||x_gpu - x_ref||_2 / ||x_ref||_2 and the
+element-wise max|x_gpu - x_ref| / max|x_ref|. The larger of the two, maximised over
+heads and steps, is compared with the tolerance.
 """
 from __future__ import annotations
 
@@ -52,13 +53,22 @@ def host_slice(x: dict, heads: np.ndarray):
     return tuple(x[n][heads] for n in ("q", "k", "v", "gate", "beta"))
 
 
-def rel_err(gpu: np.ndarray, ref: np.ndarray) -> float:
-    """max over leading index of ||gpu - ref|| / ||ref|| over the trailing axes."""
+def rel_err_parts(gpu: np.ndarray, ref: np.ndarray) -> tuple[float, float]:
+    """Both error figures over the trailing axes, maximised over the leading index (one
+    head's vector or state matrix at one step): the norm-wise ||gpu - ref||_2 / ||ref||_2
+    and the element-wise max|gpu - ref| / max|ref|."""
     g = gpu.reshape(gpu.shape[0], -1).astype(np.float64)
     r = ref.reshape(ref.shape[0], -1).astype(np.float64)
-    num = np.linalg.norm(g - r, axis=1)
-    den = np.linalg.norm(r, axis=1)
-    return float(np.max(num / np.maximum(den, 1e-300)))
+    d = g - r
+    norm = np.linalg.norm(d, axis=1) / np.maximum(np.linalg.norm(r, axis=1), 1e-300)
+    elem = np.max(np.abs(d), axis=1) / np.maximum(np.max(np.abs(r), axis=1), 1e-300)
+    return float(np.max(norm)), float(np.max(elem))
+
+
+def rel_err(gpu: np.ndarray, ref: np.ndarray) -> float:
+    """The larger of the two figures of rel_err_parts: every tolerance bounds both the
+    norm-wise error of a head's vector or matrix and its worst single element."""
+    return max(rel_err_parts(gpu, ref))
 
 
 def take(t: torch.Tensor, heads_dev: torch.Tensor, inner) -> np.ndarray:

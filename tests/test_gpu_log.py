@@ -2,7 +2,7 @@
 base + log steps, which equal eager decoding (a pinned oracle property), and
 against the GPU's own eager dense step.
 
-Tolerance: 1e-5 norm-wise relative error for outputs, merged bases and logged
+Tolerance: 1e-5 relative error (norm-wise and element-wise) for outputs, merged bases and logged
 value factors; logged keys are copied bit-exactly; log-decays within 1e-5."""
 import numpy as np
 import pytest
@@ -38,6 +38,16 @@ def test_log_b256_h48_full_size_sampled():
     w = wl.WORKLOADS[5]
     say(f"[log] {w.name}: full size, 64 sampled heads, {w.steps} steps")
     _check(run_log(w, sample=64), w.name)
+
+
+@pytest.mark.parametrize("M", [4, 8])
+def test_kda_log_b128_h32_full_grid_sampled(M):
+    """KDA gates on the base + log path over the full grid of the KDA workload (B=128,
+    H=32, 4,096 heads, the XCD-grouped head order of every full block), three cycles and
+    two steps into the fourth, 64 sampled heads."""
+    w = wl.custom(wl.WORKLOADS[5], B=128, H=32, M=M, steps=3 * M + 2, variant="kda", gate_lo=0.8, gate_hi=1.0)
+    say(f"[log] kda B=128 H=32 M={M}: full grid, 64 sampled heads, {w.steps} steps")
+    _check(run_log(w, sample=64), f"kda log b128 h32 m{M}")
 
 
 @pytest.mark.parametrize("variant", ["gdn", "kda"])

@@ -3,7 +3,7 @@
 Bars: the initial quantization of an fp32 state is bit-exact (both sides take the
 code decision in fp32 from identical inputs); inside a window the outputs are
 within 1e-4 norm-wise relative error of the oracle teacher-forced from the GPU's
-window-start state; at each boundary the requantized codes differ by at most
+window-start state (norm-wise and element-wise); at each boundary the requantized codes differ by at most
 1 LSB, and only where the exact code lies within 1e-3 LSB of a rounding tie;
 row scales within 1e-5 relative."""
 import numpy as np
@@ -54,6 +54,25 @@ def test_window_small_all_heads(variant, W, B, H):
                   variant=variant, gate_lo=0.8 if variant == "kda" else 0.9,
                   gate_hi=1.0 if variant == "kda" else 0.999)
     _check(run_window(w), f"{variant} W={W} B={B} H={H}")
+
+
+@pytest.mark.parametrize("variant,W,qkv", [("gdn", 24, "bf16"), ("gdn", 32, "f32"), ("kda", 24, "f32"),
+                                            ("kda", 32, "bf16"), ("gdn", 17, "bf16")])
+def test_window_long_windows_all_heads(variant, W, qkv):
+    """Windows of 17 to 32 tokens, the lengths served by the 32-record instantiations of
+    the step and of the boundary (bf16 GDN keys take the generic boundary there)."""
+    w = wl.custom(wl.WORKLOADS[4], B=2, H=3, W=W, qkv=qkv, steps=2 * W + 3, variant=variant,
+                  gate_lo=0.8 if variant == "kda" else 0.9, gate_hi=1.0 if variant == "kda" else 0.999)
+    _check(run_window(w), f"{variant} W={W} B=2 H=3 {qkv}")
+
+
+def test_kda_window_b128_h32_full_grid_sampled():
+    """KDA gates on the int8 window over the full grid of the KDA workload (B=128, H=32,
+    4,096 heads, the XCD-grouped head order of every full block), W=16, three windows and
+    two steps into the fourth, 64 sampled heads."""
+    w = wl.custom(wl.WORKLOADS[4], B=128, H=32, steps=3 * 16 + 2, variant="kda", gate_lo=0.8, gate_hi=1.0)
+    say(f"[q8] kda B=128 H=32 W=16: full grid, 64 sampled heads, {w.steps} steps")
+    _check(run_window(w, sample=64), "kda q8 window b128 h32 w16")
 
 
 def test_window_f32_inputs():
