@@ -11,6 +11,9 @@ kernel (gate, k-read, correction, rank-one update, readout) over all B*H heads.
 Prints ONE JSON line on stdout:
   value = state head-updates per second (B*H*K / timed seconds),
   roofline = algorithmic HBM bytes per launch / average launch time vs 8 TB/s,
+  hbm_ceiling = read-only and write-only stream rates of the same tile pattern over the
+    state's size, and the step time they imply (bytes read / R + bytes written / W),
+  other_configs = GPU-only lines of the KDA, int8-window and base+log workloads,
   cpu_baseline = the fp64 oracle timed on the host cores on a bounded sample.
 Other workloads (--workload kda|q8|log|lq|kda_lq|lq4|rwkv6|rwkv6_log|rwkv7|rwkv7_q8|
 stepq|gdn_small) report the same fields for their own kernels, with the CPU baseline
@@ -213,27 +216,57 @@ def _dev_inputs(w, steps, torch, dev):
     return {n: torch.stack(v) for n, v in out.items()}
 
 
-def copy_ceiling(torch, rsu, nbytes: int, reps: int = 10) -> float:
-    """Read+write GB/s of the copy probe over a buffer of nbytes (counting both directions)."""
-    n = nbytes // 4 // 16384 * 16384
-    src = torch.empty(n, device="cuda").uniform_()
+def dense_rw_bytes_per_head(w: wl.Workload) -> tuple[int, int]:
+    """(bytes read, bytes written) of one dense step per head: the state both ways, the
+    inputs read, y written."""
+    total = dense_bytes_per_head(w)
+    written = 4 * wl.DK * wl.DK + 4 * wl.DK
+    return total - written, written
+
+
+def _time_calls(torch, call, reps: int = 10, trials: int = 3) -> float:
+    """Median over trials of the average launch time (s) of `reps` back-to-back calls, with
+    HIP events on the stream the calls launch on (torch's current stream)."""
+    stream = torch.cuda.current_stream()
+    call()
+    torch.cuda.synchronize()
+    out = []
+    for _ in range(trials):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            call()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        out.append(e0.elapsed_time(e1) / 1e3 / reps)
+    return float(np.median(out))
+
+
+def hbm_ceiling(torch, rsu, tiles: int, read_bytes: float, write_bytes: float, step_sec: float) -> dict:
+    """The HBM read rate R and write rate W of streams with the dense step's tile pattern
+    over `tiles` 64 KiB tiles (the size of the step's state), and the time a step that
+    reads read_bytes and writes write_bytes would take at those rates one after the
+    other: read_bytes / R + write_bytes / W. A copy into a second buffer is reported
+    beside them; it is not a bound of the in-place step."""
+    src = torch.empty(tiles, 128, 128, device="cuda").uniform_()
+    sums = torch.empty(tiles, 128, device="cuda")
     dst = torch.empty_like(src)
-    for _ in range(2):
-        rsu.copy_f32(src, dst)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(reps):
-        rsu.copy_f32(src, dst)
-    e1.record()
-    torch.cuda.synchronize()
-    sec = e0.elapsed_time(e1) / 1e3 / reps
-    del src, dst
-    return 2 * n * 4 / sec / 1e9
+    nbytes = tiles * 128 * 128 * 4
+    t_r = _time_calls(torch, lambda: rsu.read_f32(src, sums))
+    t_w = _time_calls(torch, lambda: rsu.fill_f32(dst, 0.5))
+    t_c = _time_calls(torch, lambda: rsu.copy_f32(src, dst))
+    del src, sums, dst
+    R, W = nbytes / t_r, nbytes / t_w
+    ceil_sec = read_bytes / R + write_bytes / W
+    return {"read_GBps": R / 1e9, "write_GBps": W / 1e9, "copy_GBps": 2 * nbytes / t_c / 1e9,
+            "bytes_read_per_step": read_bytes, "bytes_written_per_step": write_bytes,
+            "ceiling_us": ceil_sec * 1e6, "step_us": step_sec * 1e6, "frac_of_ceiling": ceil_sec / step_sec,
+            "ceiling_GBps": (read_bytes + write_bytes) / ceil_sec / 1e9,
+            "probes": "rsu_read_f32 / rsu_fill_f32 / rsu_copy_f32 over the state's size, same tile pattern"}
 
 
 def run_gpu(w: wl.Workload, steps: int, warmup: int, slots: bool = False, n_iter: int = 1, graph: bool = False,
-            split: bool = False):
+            split: bool = False, measure_ceiling: bool = True):
     import torch
     import recurrent_state_update_head_amd as rsu
     dev = "cuda"
@@ -477,8 +510,36 @@ def run_gpu(w: wl.Workload, steps: int, warmup: int, slots: bool = False, n_iter
     gpu_sec = e0.elapsed_time(e1) / 1e3
     if split:
         phases = split_phases()
-    ceiling = copy_ceiling(torch, rsu, 4 * B * H * 128 * 128) if w.path == "dense" else None
+    ceiling = None
+    if w.path == "dense" and measure_ceiling:
+        rb, wb = dense_rw_bytes_per_head(w)
+        ceiling = hbm_ceiling(torch, rsu, w.heads, rb * w.heads, wb * w.heads, gpu_sec / steps)
     return gpu_sec, wall, ceiling, phases, dist
+
+
+# ----------------------------------------------------------------- the other workloads
+
+# The other workloads of the default line, with their timed and warm-up steps (whole windows
+# and whole merge cycles): the dense KDA step, the int8 window and the base + log cycle.
+OTHER_CONFIGS = ((3, 32, 4), (4, 64, 16), (5, 64, 16))
+
+
+def run_other_configs() -> dict:
+    """GPU-only measurements of the other workloads, each over whole windows / cycles, in the
+    same process as the headline line (no CPU baseline): time per step, head-updates/s and
+    algorithmic GB/s against the HBM peak."""
+    out = {}
+    for cid, steps, warmup in OTHER_CONFIGS:
+        w = wl.WORKLOADS[cid]
+        gpu_sec, _, _, _, dist = run_gpu(w, steps, warmup, measure_ceiling=False)
+        per_head = cycle_bytes_per_head(w)
+        launch = gpu_sec / steps
+        gbs = per_head * w.heads / launch / 1e9
+        out[w.name] = {"ms_per_step": launch * 1e3, "value": w.heads / launch, "unit": "head-updates/s",
+                       "steps": steps, "warmup": warmup, "algorithmic_bytes_per_head_update": per_head,
+                       "achieved_GBps": gbs, "frac": gbs / PEAK_HBM_GBS,
+                       "median_step_us": dist["median_us"]}
+    return out
 
 
 # ----------------------------------------------------------------- CPU baseline (oracle)
@@ -634,6 +695,8 @@ def main():
                     help="stepq path: the readout and the repack as two launches on two streams")
     ap.add_argument("--slots", action="store_true",
                     help="log path: per-slot live lengths, every head at its own cycle point")
+    ap.add_argument("--no-other-configs", action="store_true",
+                    help="default workload: skip the GPU-only lines of the KDA, int8-window and base+log workloads")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -657,6 +720,9 @@ def main():
     launch_sec = gpu_sec / steps
     achieved = per_head * heads / launch_sec / 1e9
     traffic = counter_traffic(per_head * heads) if w is wl.WORKLOADS[2] else None
+    others = None
+    if w is wl.WORKLOADS[2] and not args.no_other_configs and not args.graph:
+        others = run_other_configs()
 
     out = {
         "metric": METRIC,
@@ -681,9 +747,11 @@ def main():
                    "refit_iterations": args.n_iter if w.path == "lq_window" else None},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
+                     "traffic_source": (f"{os.path.relpath(PROFILE_COUNTERS, ROOT)}: rocprofv3 FETCH_SIZE and "
+                                        "WRITE_SIZE of this kernel source (hash-checked), scaled by the stream "
+                                        "probes; not measured in this run" if traffic is not None else None),
                      "algorithmic_bytes_per_launch": per_head * heads},
-        "hbm_copy_ceiling": ({"achieved": ceiling, "unit": "GB/s", "frac": ceiling / PEAK_HBM_GBS}
-                             if ceiling else None),
+        "hbm_ceiling": ceiling,
         "wall_s_timed_region": wall,
         "timing": ("the K steps captured as one HIP graph, replayed once" if args.graph else
                    "eager launches, readout and repack on two streams" if args.split else "eager launches"),
@@ -691,6 +759,8 @@ def main():
     out["step_time_distribution"] = dist
     if phases:
         out["phases"] = phases
+    if others:
+        out["other_configs"] = others
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = run_cpu_baseline(w, slots=args.slots, n_iter=args.n_iter)
     print(json.dumps(out), flush=True)

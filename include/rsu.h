@@ -361,6 +361,18 @@ int kda_stepq_repack(const rsu_dims *dims, void *Z, void *R, void *C, const floa
  * ---------------------------------------------------------------------- */
 int rsu_copy_f32(const float *src, float *dst, int64_t n, rsu_stream_t stream);
 
+/* Measurement helpers (not part of the recurrence): a read-only and a write-only stream
+ * over `tiles` whole 128 x 128 fp32 tiles (64 KiB each), with the same 128-bit
+ * non-temporal access pattern, tile order and grid shape as the dense step. Their rates
+ * are the HBM read and write rates that bound a step that reads each tile once and writes
+ * it once.
+ * rsu_read_f32: reads src [tiles,128,128] and writes the column sums of each tile to
+ *   col_sums [tiles,128] (512 B written per 64 KiB read).
+ * rsu_fill_f32: sets every element of dst [tiles,128,128] to value.
+ * 0 <= tiles <= 2^31 - 1; pointers 16-byte aligned; errors as above. */
+int rsu_read_f32(const float *src, float *col_sums, int64_t tiles, rsu_stream_t stream);
+int rsu_fill_f32(float *dst, float value, int64_t tiles, rsu_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

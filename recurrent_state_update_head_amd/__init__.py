@@ -81,6 +81,8 @@ _SIGS = {
     "gdn_stepq_repack": [_DP, _P, _P, _P, _P, _P, _P, _P, _P],
     "kda_stepq_repack": [_DP, _P, _P, _P, _P, _P, _P, _P, _P],
     "rsu_copy_f32": [_P, _P, ctypes.c_int64, _P],
+    "rsu_read_f32": [_P, _P, ctypes.c_int64, _P],
+    "rsu_fill_f32": [_P, ctypes.c_float, ctypes.c_int64, _P],
 }
 for _name, _args in _SIGS.items():
     getattr(_lib, _name).argtypes = _args
@@ -509,6 +511,25 @@ def copy_f32(src: torch.Tensor, dst: torch.Tensor):
     _need(src, "src", torch.float32, src.shape)
     _need(dst, "dst", torch.float32, src.shape)
     _call("rsu_copy_f32", _ptr(src), _ptr(dst), src.numel(), _stream())
+
+
+def read_f32(src: torch.Tensor, col_sums: torch.Tensor):
+    """Read-only stream over whole 128 x 128 fp32 tiles with the dense step's access pattern:
+    src [..., 128, 128], col_sums [..., 128] <- the column sums of every tile."""
+    if src.dim() < 2 or tuple(src.shape[-2:]) != (D, D):
+        raise ValueError(f"src must be [..., {D}, {D}], got {tuple(src.shape)}")
+    _need(src, "src", torch.float32, src.shape)
+    _need(col_sums, "col_sums", torch.float32, tuple(src.shape[:-1]))
+    _call("rsu_read_f32", _ptr(src), _ptr(col_sums), src.numel() // (D * D), _stream())
+
+
+def fill_f32(dst: torch.Tensor, value: float):
+    """Write-only stream over whole 128 x 128 fp32 tiles with the dense step's access
+    pattern: every element of dst [..., 128, 128] <- value."""
+    if dst.dim() < 2 or tuple(dst.shape[-2:]) != (D, D):
+        raise ValueError(f"dst must be [..., {D}, {D}], got {tuple(dst.shape)}")
+    _need(dst, "dst", torch.float32, dst.shape)
+    _call("rsu_fill_f32", _ptr(dst), ctypes.c_float(value), dst.numel() // (D * D), _stream())
 
 
 def raw_library() -> ctypes.CDLL:

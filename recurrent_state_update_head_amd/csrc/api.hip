@@ -450,6 +450,22 @@ int rsu_copy_f32(const float* src, float* dst, int64_t n, rsu_stream_t stream) {
     return launched(rsu::launch_copy(src, dst, n, stream), "rsu_copy_f32");
 }
 
+int rsu_read_f32(const float* src, float* col_sums, int64_t tiles, rsu_stream_t stream) {
+    g_err[0] = '\0';
+    if (tiles < 0 || tiles > 0x7fffffffLL) return fail(RSU_E_DIMS, "rsu_read_f32: tiles=%lld out of range", (long long)tiles);
+    if (tiles == 0) return RSU_OK;
+    if (int rc = check_ptrs({{src, "src"}, {col_sums, "col_sums"}}, "rsu_read_f32")) return rc;
+    return launched(rsu::launch_read_probe(src, col_sums, static_cast<int>(tiles), stream), "rsu_read_f32");
+}
+
+int rsu_fill_f32(float* dst, float value, int64_t tiles, rsu_stream_t stream) {
+    g_err[0] = '\0';
+    if (tiles < 0 || tiles > 0x7fffffffLL) return fail(RSU_E_DIMS, "rsu_fill_f32: tiles=%lld out of range", (long long)tiles);
+    if (tiles == 0) return RSU_OK;
+    if (int rc = check_ptrs({{dst, "dst"}}, "rsu_fill_f32")) return rc;
+    return launched(rsu::launch_write_probe(dst, value, static_cast<int>(tiles), stream), "rsu_fill_f32");
+}
+
 int stepq_pack(const rsu_dims* dims, const float* S, const float* omega, void* Z, void* R, void* C,
                rsu_stream_t stream) {
     const char* fn = "stepq_pack";

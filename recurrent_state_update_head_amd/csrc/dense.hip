@@ -45,7 +45,7 @@ __global__ __launch_bounds__(kThreads) void dense_step_kernel(
     f32x4 s[kRowsPerThread];
 #pragma unroll
     for (int it = 0; it < kRowsPerThread; ++it)
-        s[it] = stream_load(Sh + (it * 8 + ro) * kD + col);
+        s[it] = stream_load(Sh + (row_block(it, wave) * 8 + ro) * kD + col);
 
     row_vec[wave][2 * lane] = f32x4{g2.x * k2.x, g2.x * q2.x, k2.x, g2.x};
     row_vec[wave][2 * lane + 1] = f32x4{g2.y * k2.y, g2.y * q2.y, k2.y, g2.y};
@@ -56,7 +56,7 @@ __global__ __launch_bounds__(kThreads) void dense_step_kernel(
     f32x4 p = {0.f, 0.f, 0.f, 0.f}, r = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int it = 0; it < kRowsPerThread; ++it) {
-        const f32x4 rv = row_vec[wave][it * 8 + ro];
+        const f32x4 rv = row_vec[wave][row_block(it, wave) * 8 + ro];
         if constexpr (kDelta) p += s[it] * rv.x;
         r += s[it] * rv.y;
     }
@@ -68,9 +68,9 @@ __global__ __launch_bounds__(kThreads) void dense_step_kernel(
 
 #pragma unroll
     for (int it = 0; it < kRowsPerThread; ++it) {
-        const f32x4 rv = row_vec[wave][it * 8 + ro];
+        const f32x4 rv = row_vec[wave][row_block(it, wave) * 8 + ro];
         const float g = kPerKey ? rv.w : alpha;
-        stream_store(Sh + (it * 8 + ro) * kD + col, s[it] * g + rv.z * u);
+        stream_store(Sh + (row_block(it, wave) * 8 + ro) * kD + col, s[it] * g + rv.z * u);
     }
 }
 
@@ -106,7 +106,7 @@ __global__ __launch_bounds__(kThreads) void rwkv7_step_kernel(
     f32x4 s[kRowsPerThread];
 #pragma unroll
     for (int it = 0; it < kRowsPerThread; ++it)
-        s[it] = stream_load(Sh + (it * 8 + ro) * kD + col);
+        s[it] = stream_load(Sh + (row_block(it, wave) * 8 + ro) * kD + col);
 
     row_vec[wave][2 * lane] = f32x4{a2.x * c2.x, w2.x * q2.x, c2.x, w2.x};
     row_vec[wave][2 * lane + 1] = f32x4{a2.y * c2.y, w2.y * q2.y, c2.y, w2.y};
@@ -119,7 +119,7 @@ __global__ __launch_bounds__(kThreads) void rwkv7_step_kernel(
     f32x4 p = {0.f, 0.f, 0.f, 0.f}, r = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int it = 0; it < kRowsPerThread; ++it) {
-        const f32x4 rv = row_vec[wave][it * 8 + ro];
+        const f32x4 rv = row_vec[wave][row_block(it, wave) * 8 + ro];
         p += s[it] * rv.x;
         r += s[it] * rv.y;
     }
@@ -131,8 +131,8 @@ __global__ __launch_bounds__(kThreads) void rwkv7_step_kernel(
 
 #pragma unroll
     for (int it = 0; it < kRowsPerThread; ++it) {
-        const f32x4 rv = row_vec[wave][it * 8 + ro];
-        stream_store(Sh + (it * 8 + ro) * kD + col, s[it] * rv.w + rv.z * u + krow[wave][it * 8 + ro] * vv);
+        const f32x4 rv = row_vec[wave][row_block(it, wave) * 8 + ro];
+        stream_store(Sh + (row_block(it, wave) * 8 + ro) * kD + col, s[it] * rv.w + rv.z * u + krow[wave][row_block(it, wave) * 8 + ro] * vv);
     }
 }
 
@@ -146,15 +146,46 @@ __global__ __launch_bounds__(kThreads) void copy_kernel(const float* __restrict_
     if (base + kD * kD <= n) {
         f32x4 s[kRowsPerThread];
 #pragma unroll
-        for (int it = 0; it < kRowsPerThread; ++it) s[it] = stream_load(src + base + it * 8 * kD + off);
+        for (int it = 0; it < kRowsPerThread; ++it) s[it] = stream_load(src + base + row_block(it, wave) * 8 * kD + off);
 #pragma unroll
-        for (int it = 0; it < kRowsPerThread; ++it) stream_store(dst + base + it * 8 * kD + off, s[it]);
+        for (int it = 0; it < kRowsPerThread; ++it) stream_store(dst + base + row_block(it, wave) * 8 * kD + off, s[it]);
     } else {
         for (int it = 0; it < kRowsPerThread; ++it) {
             const int64_t i = base + it * 8 * kD + off;
             if (i + 4 <= n) stream_store(dst + i, stream_load(src + i));
         }
     }
+}
+
+// Read-only and write-only streams over whole 128 x 128 fp32 tiles, with the dense step's
+// tile pattern, head order and cache policy: the HBM read and write rates that bound a step
+// which reads every tile once and writes it once. The read probe writes each tile's 128
+// column sums (512 B per 64 KiB read) so that its loads cannot be dropped.
+__global__ __launch_bounds__(kThreads) void read_probe_kernel(const float* __restrict__ src,
+                                                              float* __restrict__ sums) {
+    const int64_t tile = head_of_block(blockIdx.x, gridDim.x);
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
+    const int col = wave * 32 + (lane & 7) * 4;
+    const float* t = src + tile * kD * kD + (lane >> 3) * kD + col;
+    f32x4 s[kRowsPerThread];
+#pragma unroll
+    for (int it = 0; it < kRowsPerThread; ++it) s[it] = stream_load(t + row_block(it, wave) * 8 * kD);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int it = 0; it < kRowsPerThread; ++it) acc += s[it];
+    acc = sum_row_lanes(acc);
+    if ((lane >> 3) == 0) *reinterpret_cast<f32x4*>(sums + tile * kD + col) = acc;
+}
+
+__global__ __launch_bounds__(kThreads) void write_probe_kernel(float* __restrict__ dst, float value) {
+    const int64_t tile = head_of_block(blockIdx.x, gridDim.x);
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
+    float* t = dst + tile * kD * kD + (lane >> 3) * kD + wave * 32 + (lane & 7) * 4;
+#pragma unroll
+    for (int it = 0; it < kRowsPerThread; ++it)
+        stream_store(t + row_block(it, wave) * 8 * kD, f32x4{value, value, value, value});
 }
 
 template <bool kPerKey, bool kDelta, typename T>
@@ -194,6 +225,16 @@ hipError_t launch_copy(const float* src, float* dst, int64_t n, hipStream_t stre
     const int64_t blocks = (n + kD * kD - 1) / (kD * kD);
     hipLaunchKernelGGL(copy_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, stream,
                        src, dst, n);
+    return hipGetLastError();
+}
+
+hipError_t launch_read_probe(const float* src, float* sums, int tiles, hipStream_t stream) {
+    hipLaunchKernelGGL(read_probe_kernel, dim3(tiles), dim3(kThreads), 0, stream, src, sums);
+    return hipGetLastError();
+}
+
+hipError_t launch_write_probe(float* dst, float value, int tiles, hipStream_t stream) {
+    hipLaunchKernelGGL(write_probe_kernel, dim3(tiles), dim3(kThreads), 0, stream, dst, value);
     return hipGetLastError();
 }
 

@@ -45,6 +45,8 @@ hipError_t launch_rwkv6(const StepArgs& a, bool bf16, hipStream_t stream);
 hipError_t launch_rwkv7(const StepArgs& a, const void* kappa, const float* erase_rate, bool bf16,
                         hipStream_t stream);
 hipError_t launch_copy(const float* src, float* dst, int64_t n, hipStream_t stream);
+hipError_t launch_read_probe(const float* src, float* sums, int tiles, hipStream_t stream);
+hipError_t launch_write_probe(float* dst, float value, int tiles, hipStream_t stream);
 hipError_t launch_q8_quantize(int heads, const float* S, int8_t* Z, float* A, hipStream_t stream);
 hipError_t launch_q8_window(const StepArgs& a, const WindowArgs& w, bool per_key, bool bf16,
                             hipStream_t stream);

@@ -140,6 +140,12 @@ __device__ __forceinline__ int head_of_block(int bid, int nblk) {
     return bid / grp * grp + (bid % kXcds) * kXcdRun + (bid / kXcds) % kXcdRun;
 }
 
+// Row block (8 key rows, 4 KiB of fp32 state) that a wave of the fp32-state layout
+// visits at iteration it: the four waves of a head start at row blocks 0, 4, 8 and 12,
+// so the first loads of a workgroup cover four 4 KiB regions of the head instead of one.
+// Measured on MI355X: the dense step 1% faster than with every wave starting at row 0.
+__device__ __forceinline__ int row_block(int it, int wave) { return (it + 4 * wave) & 15; }
+
 // ---- cross-lane reductions on the VALU (DPP and permlane swaps; no LDS round trip)
 // Lane layouts checked on gfx950: quad_perm 0xB1 / 0x4E exchange lanes i^1 / i^2,
 // row_ror:8 exchanges i^8 inside each row of 16 lanes, row_ror:4 rotates a row by

@@ -216,6 +216,25 @@ def test_copy_validation(lib):
     assert c(None, None, 0, None) == RSU_OK
 
 
+def test_stream_probe_validation(lib):
+    r = lib.rsu_read_f32
+    r.restype = ctypes.c_int
+    r.argtypes = [P, P, ctypes.c_int64, P]
+    w = lib.rsu_fill_f32
+    w.restype = ctypes.c_int
+    w.argtypes = [P, ctypes.c_float, ctypes.c_int64, P]
+    assert r(GOOD, GOOD, -1, None) == E_DIMS
+    assert r(GOOD, GOOD, 1 << 31, None) == E_DIMS
+    assert r(GOOD, None, 4, None) == E_NULL
+    assert "col_sums is NULL" in _last(lib)
+    assert r(ODD, GOOD, 4, None) == E_ALIGN
+    assert r(None, None, 0, None) == RSU_OK
+    assert w(None, 1.0, 4, None) == E_NULL
+    assert w(ODD, 1.0, 4, None) == E_ALIGN
+    assert w(GOOD, 1.0, -2, None) == E_DIMS
+    assert w(None, 1.0, 0, None) == RSU_OK
+
+
 def test_rwkv6_validation(lib):
     f = lib.rwkv6_decode_step
     f.restype = ctypes.c_int
