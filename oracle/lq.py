@@ -21,6 +21,9 @@ Readings taken where the pages are silent (stated once here, used everywhere):
     MGS is modified Gram-Schmidt over the columns in order, a zero column stays zero;
   * the start is the previous window's Ut (orthonormalized); the first fit, from a
     plain state, starts from the first r Walsh (Sylvester-Hadamard) columns;
+  * parity unpinned: the page gives the objective and names power iteration, not the
+    solver; the pins fix the limit of the iteration (the truncated SVD), not the tokens
+    that one warm-started iteration per boundary leaves;
   * Kt and Ut are rounded to fp16 (round to nearest even) and the residual is taken
     against the rounded tokens, so the stored pieces add up to the reconstruction;
   * the smoothing floor is 1e-6 on c; c and B are stored in fp32;

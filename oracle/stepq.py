@@ -19,7 +19,8 @@ Readings taken where the notes are silent or their text is lost (stated once her
   * row factor: r_i = sqrt(m_i / w_i) with m_i = mean_j |X_ij| (the notes' formula did not
     survive extraction; they describe it as SmoothQuant's fractional-power balance of the
     row's magnitude against its influence, read here as SmoothQuant's square root), rounded
-    to fp16; a row with m_i = 0 gets r_i = 0 and zero codes;
+    to fp16; a row with m_i = 0 gets r_i = 0 and zero codes. Parity unpinned: the pins fix
+    what follows from any row factor, not this exponent;
   * codes of one uniform width (qmax = 7, i.e. 4 bits: the calibrated per-unit width tables
     and the fp16 pivot rows come from data and are not built): with the column range
     a_j = max_i |X_ij| / r_i over the rows with r_i > 0, z_ij = clamp(rne(X_ij / r_i * qmax /
