@@ -194,14 +194,13 @@ __global__ __launch_bounds__(kThreads) void q8_step_kernel(
     float Gs[kKSlots][kPerKey ? 8 : 1];
     float Gall = 1.f;
     if constexpr (!kPerKey) {
+        // suffix scan over the record lanes (g = 1 from record pos on): the product of the
+        // gates after each record, gathered for the records of this lane's groups
+        const float Sfx = suffix_prod<kWmax>(g_lane, lane);
+        const float E = suffix_prod_excl<kWmax>(Sfx, lane);
 #pragma unroll
-        for (int s = 0; s < kKSlots; ++s) Gs[s][0] = 1.f;
-        for (int i = pos - 1; i >= 0; --i) {
-            const float gi = lane_value(g_lane, i);
-#pragma unroll
-            for (int s = 0; s < kKSlots; ++s) Gs[s][0] = i > grp + 16 * s ? Gs[s][0] * gi : Gs[s][0];
-            Gall *= gi;
-        }
+        for (int s = 0; s < kKSlots; ++s) Gs[s][0] = lane_gather(E, grp + 16 * s);
+        Gall = lane_value(Sfx, 0);
     } else {
 #pragma unroll
         for (int s = 0; s < kKSlots; ++s) {
@@ -315,6 +314,20 @@ __device__ __forceinline__ uint32_t code_word(float a, float b, float c, float d
     return pack_low_bytes(code_bits(a), code_bits(b), code_bits(c), code_bits(d));
 }
 
+// The same without the clamp, for values w = x * fp32(127 / m) with |x| <= m, m the absmax
+// of the row the x belong to: |w| <= m fp32(127 / m) <= 127 (1 + 2^-24) rounds to at most
+// 127, so the integer is already a code (m = 0 gives w = 0). Non-finite rows give
+// unspecified codes.
+__device__ __forceinline__ uint32_t code_bits_in_range(float w) {
+#pragma clang fp contract(off)
+    constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23
+    return static_cast<uint32_t>(__float_as_int(w + kMagic));
+}
+__device__ __forceinline__ uint32_t code_word_in_range(float a, float b, float c, float d) {
+    return pack_low_bytes(code_bits_in_range(a), code_bits_in_range(b), code_bits_in_range(c),
+                          code_bits_in_range(d));
+}
+
 // S_W of eq. 4 from the staged window, requantized in place: the record sum is a
 // [128 x kWmax] . [kWmax x 128] contraction per head, done on the matrix cores as its
 // transpose with v_mfma_f32_16x16x4f32 (A from lane l is A[l%16][l/16], B is B[l/16][l%16],
@@ -380,8 +393,8 @@ __device__ __forceinline__ void form_and_requantize(const float* KE, const float
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh)
                 Zs[row * kZsStride + 8 * lq + 2 * i + hh] =
-                    code_word(acc[4 * hh + 0][i] * sc, acc[4 * hh + 1][i] * sc, acc[4 * hh + 2][i] * sc,
-                              acc[4 * hh + 3][i] * sc);
+                    code_word_in_range(acc[4 * hh + 0][i] * sc, acc[4 * hh + 1][i] * sc,
+                                       acc[4 * hh + 2][i] * sc, acc[4 * hh + 3][i] * sc);
     }
     // the wave's 32 rows (32w .. 32w+31, 4 KiB of codes) leave as whole 128-byte rows
     wave_lds_sync();
@@ -794,6 +807,20 @@ __device__ __forceinline__ void split3_bf16(float x, uint32_t& hi, uint32_t& mid
 }
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// bf16(x0) | bf16(x1) << 16, both rounded to nearest even (one conversion instruction).
+__device__ __forceinline__ uint32_t pk_bf16(float x0, float x1) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{x0, x1}), bf16x2));
+}
+// split3_bf16 of two values at once, each part as a packed pair (x0 in the low half).
+__device__ __forceinline__ void split3_bf16x2(float x0, float x1, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
+    hi = pk_bf16(x0, x1);
+    const float r0 = x0 - __uint_as_float(hi << 16), r1 = x1 - __uint_as_float(hi & 0xffff0000u);
+    mid = pk_bf16(r0, r1);
+    const float s0 = r0 - __uint_as_float(mid << 16), s1 = r1 - __uint_as_float(mid & 0xffff0000u);
+    lo = pk_bf16(s0, s1);
+}
 
 // ---- the last step of the window for scalar gates (GDN), bf16 keys and W <= 16.
 // The decay of record j is a scalar, so it moves onto the correction:
@@ -865,14 +892,13 @@ __global__ __launch_bounds__(kThreads) void q8_boundary_bf16_kernel(
     for (int it = 0; it < kRowsPerThread; ++it)
         zw[it] = __builtin_nontemporal_load(Zh + q8_row(it, wave, ro) * (kD / 4) + c4);
 
-    // ---- gate products (newest first): for record grp, for record = lane, and all
-    float Gg = 1.f, Gl = 1.f, Gall = 1.f;
-    for (int i = pos - 1; i >= 0; --i) {
-        const float gi = lane_value(g_lane, i);
-        Gg = i > grp ? Gg * gi : Gg;
-        Gl = i > lane ? Gl * gi : Gl;
-        Gall *= gi;
-    }
+    // ---- gate products by a suffix scan over the record lanes (g = 1 past the last
+    // record): Gl = the product of the gates after record `lane`, Gg the same for record
+    // grp, Gall the product of all record gates
+    const float Sfx = suffix_prod<kRec>(g_lane, lane);
+    const float Gl = suffix_prod_excl<kRec>(Sfx, lane);
+    const float Gg = lane_gather(Gl, grp);
+    const float Gall = lane_value(Sfx, 0);
     if (wave == 0 && lane < kRec) gam[lane] = lane < pos ? Gl * gr : 1.f;
     if (0 < pos) {
         float ck = 0.f, cq = 0.f;
@@ -904,6 +930,9 @@ __global__ __launch_bounds__(kThreads) void q8_boundary_bf16_kernel(
         const f32x4 zf = unpack_i8x4(zw[it]);
         p1 += zf * rv.x;
         p2 += zf * rv.y;
+        // decode a few words at a time: decoding all 64 codes ahead of their products
+        // would hold them in 64 registers
+        if ((it & 3) == 3) __builtin_amdgcn_sched_barrier(0);
     }
     f32x2 rp = {0.f, 0.f};
     u32x4 part[3];
@@ -912,12 +941,15 @@ __global__ __launch_bounds__(kThreads) void q8_boundary_bf16_kernel(
         const int j = 8 * half + e;
         const f32x2 c = j < pos ? coef[j] : f32x2{0.f, 0.f};
         rp += c * ucol[e];
+    }
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+        const int j = 8 * half + e;
         uint32_t hi, mid, lo;
-        split3_bf16(gam[j] * ucol[e], hi, mid, lo);
-        const int sh = 16 * (e & 1);
-        part[0][e >> 1] = (e & 1) ? (part[0][e >> 1] | (hi << sh)) : hi;
-        part[1][e >> 1] = (e & 1) ? (part[1][e >> 1] | (mid << sh)) : mid;
-        part[2][e >> 1] = (e & 1) ? (part[2][e >> 1] | (lo << sh)) : lo;
+        split3_bf16x2(gam[j] * ucol[e], gam[j + 1] * ucol[e + 1], hi, mid, lo);
+        part[0][e >> 1] = hi;
+        part[1][e >> 1] = mid;
+        part[2][e >> 1] = lo;
     }
 #pragma unroll
     for (int pp = 0; pp < 3; ++pp) Ut[pp][half][cc] = part[pp];
@@ -958,6 +990,9 @@ __global__ __launch_bounds__(kThreads) void q8_boundary_bf16_kernel(
     for (int a = 0; a < 2; ++a) {
         const int row = 16 * (2 * wave + a) + lr;
         const bf16x8 bv = __builtin_bit_cast(bf16x8, Kt[blk][row]);
+        // the lo parts fill only half of the second product's depth: the lanes of the other
+        // half (lq >= 2) supply zero keys, so whatever they read as corrections drops out
+        const bf16x8 bv_lo = lq < 2 ? bv : __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
         const float zc = zcoef[row];
         f32x4 acc[8];
 #pragma unroll
@@ -966,10 +1001,9 @@ __global__ __launch_bounds__(kThreads) void q8_boundary_bf16_kernel(
         for (int ct = 0; ct < 8; ++ct) {
             const int col = 16 * ct + lr;
             const bf16x8 a1 = __builtin_bit_cast(bf16x8, Ut[lq < 2 ? 0 : 1][blk][col]);
-            const u32x4 lo = Ut[2][blk][col];
-            const bf16x8 a2 = __builtin_bit_cast(bf16x8, lq < 2 ? lo : u32x4{0u, 0u, 0u, 0u});
+            const bf16x8 a2 = __builtin_bit_cast(bf16x8, Ut[2][blk][col]);
             acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, bv, acc[ct], 0, 0, 0);
-            acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a2, bv, acc[ct], 0, 0, 0);
+            acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a2, bv_lo, acc[ct], 0, 0, 0);
         }
         float m = 0.f;
 #pragma unroll
@@ -984,8 +1018,8 @@ __global__ __launch_bounds__(kThreads) void q8_boundary_bf16_kernel(
         if (lq == 0) A[vec_off + row] = m;
 #pragma unroll
         for (int ct = 0; ct < 8; ++ct)
-            Zs[row * kZsStride + 4 * ct + lq] = code_word(acc[ct].x * sc, acc[ct].y * sc, acc[ct].z * sc,
-                                                          acc[ct].w * sc);
+            Zs[row * kZsStride + 4 * ct + lq] = code_word_in_range(acc[ct].x * sc, acc[ct].y * sc,
+                                                                   acc[ct].z * sc, acc[ct].w * sc);
     }
     wave_lds_sync();
 #pragma unroll

@@ -191,6 +191,35 @@ __device__ __forceinline__ float max_xor16(float x) {
     return fmaxf(a, b);
 }
 
+// Value of x in lane (src mod 64) of the same wave, for each lane's own src (a lane
+// permute through the LDS crossbar; no LDS memory is used). The permute reads nothing
+// from lanes that are switched off, so it must run with the whole wave active: it is
+// never placed under a lane-dependent condition.
+__device__ __forceinline__ float lane_gather(float x, int src) {
+    return __int_as_float(__builtin_amdgcn_ds_bpermute(src << 2, __float_as_int(x)));
+}
+
+// Suffix products over lanes 0..kN-1 of a wave (kN a power of two, at most 32): lane
+// l < kN gets x_l x_{l+1} ... x_{kN-1}; lanes past kN keep x. Every permute runs with the
+// whole wave; the range check selects the factor after it.
+template <int kN>
+__device__ __forceinline__ float suffix_prod(float x, int lane) {
+#pragma unroll
+    for (int d = 1; d < kN; d <<= 1) {
+        const float o = lane_gather(x, lane + d);
+        x *= lane + d < kN ? o : 1.f;
+    }
+    return x;
+}
+
+// Exclusive suffix products of the same: lane l < kN gets x_{l+1} ... x_{kN-1} (1 for
+// l = kN - 1), from the inclusive ones.
+template <int kN>
+__device__ __forceinline__ float suffix_prod_excl(float incl, int lane) {
+    const float o = lane_gather(incl, lane + 1);
+    return lane + 1 < kN ? o : 1.f;
+}
+
 // Sum over the 16 lanes of each DPP row (result in every lane of the row).
 __device__ __forceinline__ float row16_sum(float x) {
     x += dpp<kDppXor1>(x);
