@@ -1154,59 +1154,43 @@ constexpr int kRow4 = kD / 8;  // 32-bit words of a 4-bit row
 
 __device__ __forceinline__ int lq4_row(int it, int wave, int rl) { return 16 * it + 4 * wave + rl; }
 
-// Payload sweep of the 4-bit steps on the matrix cores: the lane's 8 code words (rows
-// lq4_row(it, wave, l >> 4), value columns 8 (l & 15) .. +7) against the two read vectors, whose
-// entries are the read vectors times 1/16. A code is read as the signed high nibble of a byte, i.e.
-// as 16 z with one sign-extending byte conversion (the even columns from w << 4, the odd ones from
-// w), exact in bf16. For each of its 8 value columns e a lane supplies those codes of its 8 rows as
-// the B operand of one v_mfma_f32_16x16x32_bf16 (K = 8 (l >> 4) + it runs over the wave's 32 rows
-// exactly as the lane layout holds them); the A operand holds the two read vectors of those rows in
-// three bf16 parts each (rows 0..2 and 4..6 of A), staged once per workgroup by sq4_stage_parts, so
-// that the products are exact and accumulate in fp32. Result rows 0..2 (lanes with l >> 4 = 0) sum to
-// the first read vector's partial of column 8 (l & 15) + e, rows 4..6 (l >> 4 = 1) to the second's;
-// those lanes store them into red_w (the wave's [128] partials {p1, p2}).
-__device__ __forceinline__ void sq4_stage_parts(uint4 (*apart)[4][4], int row, f32x2 rv) {
-    const int it = row >> 4, w = (row >> 2) & 3, r4 = row & 3;  // row = lq4_row(it, w, r4)
-    uint16_t* ap = reinterpret_cast<uint16_t*>(apart);
-    uint32_t hi, mid, lo;
-    split3_bf16(rv.x, hi, mid, lo);
-    ap[((0 * 4 + w) * 4 + r4) * 8 + it] = static_cast<uint16_t>(hi);
-    ap[((1 * 4 + w) * 4 + r4) * 8 + it] = static_cast<uint16_t>(mid);
-    ap[((2 * 4 + w) * 4 + r4) * 8 + it] = static_cast<uint16_t>(lo);
-    split3_bf16(rv.y, hi, mid, lo);
-    ap[((3 * 4 + w) * 4 + r4) * 8 + it] = static_cast<uint16_t>(hi);
-    ap[((4 * 4 + w) * 4 + r4) * 8 + it] = static_cast<uint16_t>(mid);
-    ap[((5 * 4 + w) * 4 + r4) * 8 + it] = static_cast<uint16_t>(lo);
-}
-
-__device__ __forceinline__ void sweep4(const uint32_t (&zw)[8], const uint4 (*apart)[4][4], int wave, int lane,
+// Payload sweep of the 4-bit steps: the lane's 8 code words (rows lq4_row(it, wave, l >> 4),
+// value columns 8 (l & 15) .. +7) against the two read vectors, whose rowv entries are the read
+// vectors times 1/16. A code is read as the signed high nibble of a byte, i.e. as 16 z with one
+// sign-extending byte conversion (the even columns from w << 4, the odd ones from w), so the
+// products equal z times the unscaled entries exactly. The 4 row lanes l, l^16, l^32, l^48 are
+// summed by two lane swaps that halve the live values: lanes with bit 4 set keep columns 4..7 of
+// the eight, lanes with bit 5 set the upper pair of their four. Each lane stores {p1, p2} of its two
+// columns 4 b4 + 2 b5 + (0, 1) into red_w (the wave's [128] partials).
+__device__ __forceinline__ void sweep4(const uint32_t (&zw)[8], const f32x2* rowv, int wave, int lane,
                                        f32x2* red_w) {
     const int c16 = lane & 15, rl = lane >> 4;
-    const int am = (c16 >> 2) * 3 + (c16 & 3);
-    const bool live = c16 < 8 && (c16 & 3) != 3;
-    const bf16x8 av = __builtin_bit_cast(bf16x8, live ? apart[am][wave][rl] : uint4{0u, 0u, 0u, 0u});
-    float zf[8][8];  // 16 z of rows it, columns e
+    float p1[8], p2[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) p1[e] = p2[e] = 0.f;
 #pragma unroll
     for (int it = 0; it < 8; ++it) {
+        const f32x2 rv = rowv[lq4_row(it, wave, rl)];
         const uint32_t ev = (zw[it] << 4) & 0xF0F0F0F0u, od = zw[it] & 0xF0F0F0F0u;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            zf[it][2 * j] = static_cast<float>(static_cast<int8_t>(ev >> (8 * j)));
-            zf[it][2 * j + 1] = static_cast<float>(static_cast<int8_t>(od >> (8 * j)));
+            const float ze = static_cast<float>(static_cast<int8_t>(ev >> (8 * j)));
+            const float zo = static_cast<float>(static_cast<int8_t>(od >> (8 * j)));
+            p1[2 * j] = fmaf(ze, rv.x, p1[2 * j]);
+            p2[2 * j] = fmaf(ze, rv.y, p2[2 * j]);
+            p1[2 * j + 1] = fmaf(zo, rv.x, p1[2 * j + 1]);
+            p2[2 * j + 1] = fmaf(zo, rv.y, p2[2 * j + 1]);
         }
     }
-    float* rf = reinterpret_cast<float*>(red_w);
+    float q1[4], q2[4];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        uint4 bw;
-        bw.x = __builtin_amdgcn_perm(__float_as_uint(zf[1][e]), __float_as_uint(zf[0][e]), 0x07060302u);
-        bw.y = __builtin_amdgcn_perm(__float_as_uint(zf[3][e]), __float_as_uint(zf[2][e]), 0x07060302u);
-        bw.z = __builtin_amdgcn_perm(__float_as_uint(zf[5][e]), __float_as_uint(zf[4][e]), 0x07060302u);
-        bw.w = __builtin_amdgcn_perm(__float_as_uint(zf[7][e]), __float_as_uint(zf[6][e]), 0x07060302u);
-        const f32x4 d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, bw),
-                                                                f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-        if (rl < 2) rf[2 * (8 * c16 + e) + rl] = d.x + d.y + d.z;
+    for (int e = 0; e < 4; ++e) {
+        q1[e] = add_pair16(p1[e], p1[e + 4]);
+        q2[e] = add_pair16(p2[e], p2[e + 4]);
     }
+    const int b4 = (lane >> 4) & 1, b5 = lane >> 5;
+    *reinterpret_cast<f32x4*>(red_w + 8 * c16 + 4 * b4 + 2 * b5) =
+        f32x4{add_pair32(q1[0], q1[2]), add_pair32(q2[0], q2[2]), add_pair32(q1[1], q1[3]), add_pair32(q2[1], q2[3])};
 }
 
 __global__ __launch_bounds__(kThreads) void lq4_step_kernel(
@@ -1215,7 +1199,7 @@ __global__ __launch_bounds__(kThreads) void lq4_step_kernel(
     float* __restrict__ Ubuf, float* __restrict__ Gbuf, const bf16_t* __restrict__ q,
     const bf16_t* __restrict__ k, const bf16_t* __restrict__ v, const float* __restrict__ gate,
     const float* __restrict__ beta, float* __restrict__ y) {
-    __shared__ uint4 apart[6][4][4];  // the read vectors in three bf16 parts: see sweep4
+    __shared__ f32x2 rowv[kD];
     __shared__ f32x2 coef[16];
     __shared__ f32x2 ctok[kTok4];
     __shared__ f32x2 red[4][kD];
@@ -1301,14 +1285,14 @@ __global__ __launch_bounds__(kThreads) void lq4_step_kernel(
         cq = row16_sum(cq);
         if (ch == 0) ctok[grp] = f32x2{ck, cq};
         const float c0 = cr * Gall * gr;  // c_r Gamma_{1:l} at row r
-        sq4_stage_parts(apart, cc, f32x2{c0 * kr, c0 * qr} * 0.0625f);  // times 1/16: see sweep4
+        rowv[cc] = f32x2{c0 * kr, c0 * qr} * 0.0625f;  // times 1/16: see sweep4
         const float kq = wave_sum(kr * qr);
         if (lane == 0) kq_part[wave] = kq;
     }
     __syncthreads();
 
     // ---- payload sweep over the lane's 8 words; the 4 row lanes, then the waves
-    sweep4(zw, apart, wave, lane, red[wave]);
+    sweep4(zw, rowv, wave, lane, red[wave]);
     // record and token terms of column cc
     f32x2 rp = {0.f, 0.f};
 #pragma unroll
@@ -1355,7 +1339,7 @@ __global__ __launch_bounds__(kThreads) void lq4_boundary_kernel(
     const float* __restrict__ beta, float* __restrict__ y) {
     constexpr int kRec = 16;
     extern __shared__ __align__(16) float dyn_lds[];
-    __shared__ uint4 apart[6][4][4];  // the read vectors in three bf16 parts: see sweep4
+    __shared__ f32x2 rowv[kD];
     __shared__ f32x2 coef[kRec];
     __shared__ f32x2 ctok[kTok4];
     __shared__ float kq_part[2];
@@ -1459,7 +1443,7 @@ __global__ __launch_bounds__(kThreads) void lq4_boundary_kernel(
         cq = row16_sum(cq);
         if (ch == 0) ctok[grp] = f32x2{ck, cq};
         const float c0 = cr * gam_all;
-        sq4_stage_parts(apart, cc, f32x2{c0 * kr, c0 * qr} * 0.0625f);  // times 1/16: see sweep4
+        rowv[cc] = f32x2{c0 * kr, c0 * qr} * 0.0625f;  // times 1/16: see sweep4
         zcoef[cc] = c0;
         const float kq = wave_sum(kr * qr);
         if (lane == 0) kq_part[wave] = kq;
@@ -1482,7 +1466,7 @@ __global__ __launch_bounds__(kThreads) void lq4_boundary_kernel(
     __syncthreads();
 
     // ---- payload sweep; record and token terms per column; scaled records staged for the MFMA
-    sweep4(zw, apart, wave, lane, red + wave * kD);
+    sweep4(zw, rowv, wave, lane, red + wave * kD);
     f32x2 rp = {0.f, 0.f};
     u32x4 part[3];
 #pragma unroll
