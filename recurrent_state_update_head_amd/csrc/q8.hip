@@ -115,6 +115,41 @@ __device__ __forceinline__ float lane_value(float x, int i) {
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), i));
 }
 
+// Per-key decays of a window's staged record keys, over all 256 threads of the workgroup:
+// thread t takes key row t >> 1 and the records of one half, j = (t & 1) kHalf + e, so the
+// two halves of a row sit in neighbouring lanes. load() issues the loads of the half's gates
+// (records j >= n count as 1); apply() turns KE[j][row] into extra * (the product of the
+// row's gates of the records after j) * KE[j][row] for every record j < n and returns the
+// product of the gates of all n records at the row (in both lanes of the row).
+template <int kHalf>
+struct KeyDecays {
+    float g[kHalf];
+    __device__ __forceinline__ void load(const float* __restrict__ G, int n, int tid) {
+        const int row = tid >> 1, j0 = (tid & 1) * kHalf;
+#pragma unroll
+        for (int e = 0; e < kHalf; ++e) {
+            const int j = j0 + e;
+            const float gj = G[static_cast<size_t>(j < n ? j : 0) * kD + row];  // slot clamped: in bounds
+            g[e] = j < n ? gj : 1.f;
+        }
+    }
+    __device__ __forceinline__ float apply(float* KE, int n, float extra, int tid) const {
+        const int row = tid >> 1, upper = tid & 1, j0 = upper * kHalf;
+        float mine = 1.f;
+#pragma unroll
+        for (int e = 0; e < kHalf; ++e) mine *= g[e];
+        const float other = dpp<kDppXor1>(mine);      // the partner lane's half
+        float s = extra * (upper ? 1.f : other);     // decay from the records after this half
+#pragma unroll
+        for (int e = kHalf - 1; e >= 0; --e) {
+            const int j = j0 + e;
+            if (j < n) KE[j * kD + row] *= s;
+            s *= g[e];
+        }
+        return mine * other;
+    }
+};
+
 // ---- one step inside the window (pos < W - 1): read S_{l-1} in both directions and
 // append this step's record. The records never pass through LDS: the 16 lanes of a
 // DPP row hold 8 keys each of one record and reduce its coefficients
@@ -345,13 +380,6 @@ __device__ __forceinline__ void form_and_requantize(const float* KE, const float
                                                     uint32_t* __restrict__ Zh, int wave, int lane) {
     constexpr int kSteps = kWmax / 4;
     const int lr = lane & 15, lq = lane >> 4;
-    f32x4 ua[kSteps][2];
-#pragma unroll
-    for (int s = 0; s < kSteps; ++s) {
-        const float* src = Us + (4 * s + lq) * kD + 8 * lr;
-        ua[s][0] = *reinterpret_cast<const f32x4*>(src);
-        ua[s][1] = *reinterpret_cast<const f32x4*>(src + 4);
-    }
     for (int a = 0; a < 2; ++a) {  // one 16-row band at a time: 8 accumulators live
         const int row = 16 * (2 * wave + a) + lr;
         float eb[kSteps];
@@ -369,11 +397,16 @@ __device__ __forceinline__ void form_and_requantize(const float* KE, const float
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 acc[ct][i] = static_cast<float>(static_cast<int8_t>((zo[2 * i + ct / 4] >> (8 * (ct % 4))) & 0xffu)) * zc;
+        // the corrections of four records at a time (loaded again for the second band: holding
+        // them across both bands would take 16 kWmax registers)
 #pragma unroll
         for (int s = 0; s < kSteps; ++s) {
+            const float* src = Us + (4 * s + lq) * kD + 8 * lr;
+            const f32x4 ua[2] = {*reinterpret_cast<const f32x4*>(src), *reinterpret_cast<const f32x4*>(src + 4)};
 #pragma unroll
             for (int ct = 0; ct < 8; ++ct)
-                acc[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(ua[s][ct / 4][ct % 4], eb[s], acc[ct], 0, 0, 0);
+                acc[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(ua[ct / 4][ct % 4], eb[s], acc[ct], 0, 0, 0);
+            if (s % 2 == 1) __builtin_amdgcn_sched_barrier(0);
         }
         // per-row absmax: 32 values in this lane, then the 4 lanes l, l^16, l^32, l^48
         float m = 0.f;
@@ -417,6 +450,7 @@ __global__ __launch_bounds__(kThreads) void q8_boundary_kernel(
     const float* __restrict__ beta, float* __restrict__ y) {
     extern __shared__ __align__(16) float dyn_lds[];
     __shared__ float gsuf[kMaxW + 1];     // GDN: gate products after each record; [kMaxW]: all
+    __shared__ float gtot[kPerKey ? kD : 1];  // KDA: the product of all record gates per key row
     __shared__ f32x2 rowv[kD];            // a_r/127 Gamma_{1:l} (k_r, q_r)
     __shared__ f32x2 kq_row[kD];          // (k_r, q_r)
     __shared__ f32x2 coef[kMaxW];         // per record (E_j . k, E_j . q)
@@ -444,11 +478,11 @@ __global__ __launch_bounds__(kThreads) void q8_boundary_kernel(
     const int r = tid & (kD - 1);
     const bool first = tid < kD;
     float g_rec = 1.f;
-    float grow[kPerKey ? kWmax : 1];  // per-key gates of key row r, records 0 .. kWmax-1 (slot clamped)
+    KeyDecays<kPerKey ? kWmax / 2 : 1> kdec;   // per-key gates: row tid >> 1, half tid & 1
+    float g_half_row = 1.f;                      // the current gate at that row
     if constexpr (kPerKey) {
-        if (first)
-#pragma unroll
-            for (int j = 0; j < kWmax; ++j) grow[j] = Gbuf[rec0 + static_cast<size_t>(j < pos ? j : 0) * kD + r];
+        kdec.load(Gbuf + rec0, pos, tid);
+        g_half_row = gate[vec_off + (tid >> 1)];
     } else if (tid < pos) {
         g_rec = Gbuf[static_cast<size_t>(h) * W + tid];
     }
@@ -481,34 +515,27 @@ __global__ __launch_bounds__(kThreads) void q8_boundary_kernel(
     __syncthreads();
 
     // ---- decayed keys E_j = Gamma_{j+1:l} k_j in place; the current key is row pos
-    float G;  // product of all record gates at row r
     if constexpr (!kPerKey) {
         for (int i = tid; i < pos * kD; i += kThreads) KE[i] *= gsuf[i >> 7] * gr;
-        G = gsuf[kMaxW];
     } else {
-        // thread r < 128 walks the records of key row r backwards
-        G = 1.f;
-        if (first) {
-#pragma unroll
-            for (int j = kWmax - 1; j >= 0; --j) {
-                if (j < pos) {
-                    KE[j * kD + r] *= G * gr;
-                    G *= grow[j];
-                }
-            }
-        }
+        // both halves of each key row's records at once; gtot: the product of the row's gates
+        const float G = kdec.apply(KE, pos, g_half_row, tid);
+        if ((tid & 1) == 0) gtot[tid >> 1] = G;
     }
     if (first) {
-        const float c0 = ar * (1.f / 127.f) * G * gr;  // a_r/127 Gamma_{1:l} at row r
-        rowv[r] = f32x2{c0 * kr, c0 * qr};
         kq_row[r] = f32x2{kr, qr};
         const float kq = wave_sum(kr * qr);
         if (lane == 0) kq_part[wave] = kq;
-        zcoef[r] = c0;
         KE[pos * kD + r] = kr;  // the current record: no decay after it
         for (int j = pos + 1; j < kWmax; ++j) KE[j * kD + r] = 0.f;
     }
     __syncthreads();
+    if (first) {
+        const float G = kPerKey ? gtot[r] : gsuf[kMaxW];  // product of all record gates at row r
+        const float c0 = ar * (1.f / 127.f) * G * gr;   // a_r/127 Gamma_{1:l} at row r
+        rowv[r] = f32x2{c0 * kr, c0 * qr};
+        zcoef[r] = c0;
+    }
 
     // ---- record coefficients: the 16 lanes of a DPP row reduce one record (8 rows each)
     {
@@ -762,11 +789,9 @@ __global__ __launch_bounds__(kThreads) void q8_requant_kernel(int nrec, int rec_
     Stager<float, kRwkv7Rec * kD> su;
     sk.load(Kbuf + rec0, nrec * kD, tid);
     su.load(Ubuf + rec0, nrec * kD, tid);
-    float grow[kRwkv7Rec];  // the gates of key row r, records 0 .. 31 (slot clamped)
-    if (first)
-#pragma unroll
-        for (int j = 0; j < kRwkv7Rec; ++j) grow[j] = Gbuf[rec0 + static_cast<size_t>(j < nrec ? j : 0) * kD + r];
-    const float ar = A[vec_off + r];
+    KeyDecays<kRwkv7Rec / 2> kdec;  // the gates of key row tid >> 1, half tid & 1
+    kdec.load(Gbuf + rec0, nrec, tid);
+    const float ar_half_row = A[vec_off + (tid >> 1)];
     uint32_t zw[kRowsPerThread];
 #pragma unroll
     for (int it = 0; it < kRowsPerThread; ++it)
@@ -777,18 +802,12 @@ __global__ __launch_bounds__(kThreads) void q8_requant_kernel(int nrec, int rec_
 #pragma unroll
     for (int it = 0; it < kRowsPerThread; ++it) Zs[q8_row(it, wave, ro) * kZsStride + c4] = zw[it];
     __syncthreads();
-    if (first) {  // thread r walks key row r from the newest record
-        float G = 1.f;
-#pragma unroll
-        for (int j = kRwkv7Rec - 1; j >= 0; --j) {
-            if (j < nrec) {
-                KE[j * kD + r] *= G;
-                G *= grow[j];
-            }
-        }
-        for (int j = nrec; j < kRwkv7Rec; ++j) KE[j * kD + r] = 0.f;
-        zcoef[r] = ar * (1.f / 127.f) * G;
+    {   // both halves of each key row's records at once
+        const float G = kdec.apply(KE, nrec, 1.f, tid);
+        if ((tid & 1) == 0) zcoef[tid >> 1] = ar_half_row * (1.f / 127.f) * G;
     }
+    if (first)
+        for (int j = nrec; j < kRwkv7Rec; ++j) KE[j * kD + r] = 0.f;
     __syncthreads();
     form_and_requantize<kRwkv7Rec>(KE, Us, Zs, zcoef, A + vec_off, Zh, wave, lane);
 }
