@@ -54,6 +54,9 @@ def _load():
         lib.oracle_rwkv7_step.argtypes = [I64, I, I, P, P, P, P, P, P, P, P]
         lib.oracle_rwkv7_q8_window_step.argtypes = [I64, I, I, I, I, P, P, P, P, P, P, P, P, P, P, P, P, P,
                                                     P]
+        lib.oracle_deltaproduct_step.argtypes = [I64, I, I, I, P, P, P, P, P, P, P]
+        lib.oracle_deltaproduct_q8_window_step.argtypes = [I64, I, I, I, I, I, P, P, P, P, P, P, P, P,
+                                                           P, P, P, P, P]
         lib.oracle_rwkv6_log_step.argtypes = [I64, I, I, I, I, P, P, P, P, P, P, P, P, P, P]
         lib.oracle_rwkv6_log_step_slots.argtypes = [I64, I, I, I, P, P, P, P, P, P, P, P, P, P, P]
         lib.oracle_num_threads.argtypes = []
@@ -61,7 +64,8 @@ def _load():
         for f in (lib.oracle_dense_step, lib.oracle_q8_quantize, lib.oracle_q8_window_step,
                   lib.oracle_log_step, lib.oracle_log_step_slots, lib.oracle_rwkv6_step,
                   lib.oracle_rwkv6_log_step, lib.oracle_rwkv6_log_step_slots, lib.oracle_rwkv7_step,
-                  lib.oracle_rwkv7_q8_window_step):
+                  lib.oracle_rwkv7_q8_window_step, lib.oracle_deltaproduct_step,
+                  lib.oracle_deltaproduct_q8_window_step):
             f.restype = None
         _lib = lib
     return _lib
@@ -123,6 +127,27 @@ def rwkv7_step(S: np.ndarray, q, k, v, w, kappa, a) -> np.ndarray:
     y = np.empty((nh, dv))
     _load().oracle_rwkv7_step(nh, dk, dv, _ptr(S), _ptr(q), _ptr(k), _ptr(v), _ptr(w), _ptr(kappa), _ptr(a),
                               _ptr(y))
+    return y
+
+
+def _check_dp_inputs(nh, dk, dv, q, k, v, alpha, beta):
+    n = k.shape[1] if k.ndim == 3 else 0
+    assert n >= 1 and q.shape == (nh, dk) and k.shape == (nh, n, dk) and v.shape == (nh, n, dv)
+    assert alpha.shape == (nh,) and beta.shape == (nh, n)
+    return n
+
+
+def deltaproduct_step(S: np.ndarray, q, k, v, alpha, beta) -> np.ndarray:
+    """One DeltaProduct token (n delta-rule sub-steps, the scalar gate in the first) on fp64
+    states S[nh, dk, dv] (updated in place): k [nh, n, dk], v [nh, n, dv], alpha [nh],
+    beta [nh, n]. Returns y[nh, dv] read after the last sub-step."""
+    assert S.dtype == np.float64 and S.flags.c_contiguous
+    nh, dk, dv = S.shape
+    q, k, v, alpha, beta = map(_f64, (q, k, v, alpha, beta))
+    n = _check_dp_inputs(nh, dk, dv, q, k, v, alpha, beta)
+    y = np.empty((nh, dv))
+    _load().oracle_deltaproduct_step(nh, dk, dv, n, _ptr(S), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
+                                     _ptr(beta), _ptr(y))
     return y
 
 
@@ -209,6 +234,40 @@ class Rwkv7WindowState:
         _load().oracle_rwkv7_q8_window_step(
             nh, dk, dv, self.W, self.pos, _ptr(self.Z), _ptr(self.a), _ptr(self.G), _ptr(self.K),
             _ptr(self.U), _ptr(q), _ptr(k), _ptr(v), _ptr(w), _ptr(kappa), _ptr(erase), _ptr(y),
+            _ptr(Sw) if Sw is not None else None, _ptr(wq) if wq is not None else None)
+        self.pos = 0 if boundary else self.pos + 1
+        if boundary:
+            self.G[:] = 0
+            self.K[:] = 0
+            self.U[:] = 0
+        return (y, Sw, wq) if (boundary and want_boundary) else y
+
+
+class DeltaProductWindowState:
+    """DeltaProduct on the int8 window representation: window-start (Z, a) plus n records per
+    token (one per delta-rule sub-step; LeapQuant App. A), nW records per window."""
+
+    def __init__(self, Z: np.ndarray, a: np.ndarray, W: int, n: int):
+        nh, dk, dv = Z.shape
+        self.Z = np.ascontiguousarray(Z, dtype=np.int8).copy()
+        self.a = np.ascontiguousarray(a, dtype=np.float32).copy()
+        self.W, self.n = W, n
+        self.G = np.zeros((nh, n * W))
+        self.K = np.zeros((nh, n * W, dk))
+        self.U = np.zeros((nh, n * W, dv))
+        self.pos = 0
+
+    def step(self, q, k, v, alpha, beta, want_boundary: bool = False):
+        nh, dk, dv = self.Z.shape
+        q, k, v, alpha, beta = map(_f64, (q, k, v, alpha, beta))
+        assert _check_dp_inputs(nh, dk, dv, q, k, v, alpha, beta) == self.n
+        y = np.empty((nh, dv))
+        boundary = self.pos == self.W - 1
+        Sw = np.empty((nh, dk, dv)) if (boundary and want_boundary) else None
+        wq = np.empty((nh, dk, dv)) if (boundary and want_boundary) else None
+        _load().oracle_deltaproduct_q8_window_step(
+            nh, dk, dv, self.n, self.W, self.pos, _ptr(self.Z), _ptr(self.a), _ptr(self.G), _ptr(self.K),
+            _ptr(self.U), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(y),
             _ptr(Sw) if Sw is not None else None, _ptr(wq) if wq is not None else None)
         self.pos = 0 if boundary else self.pos + 1
         if boundary:

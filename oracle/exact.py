@@ -197,6 +197,74 @@ def rwkv7_explicit_run(S0: Mat, inputs, W: int):
     return ys, bounds
 
 
+def deltaproduct_householder(S: Mat, ks, vs, alpha: F, betas) -> Mat:
+    """A DeltaProduct token as the product of its generalized Householder sub-steps
+    (LeapQuant App. A, Table 4; each sub-step the left-hand side of the GDN expansion):
+    S <- (I - b_n k_n k_n^T)(... ((I - b_1 k_1 k_1^T) alpha S + b_1 k_1 v_1^T) ...) + b_n k_n v_n^T."""
+    dk = len(S)
+    for s, (k, v, b) in enumerate(zip(ks, vs, betas)):
+        S = householder_step(S, k, v, [alpha if s == 0 else F(1)] * dk, b)
+    return S
+
+
+def deltaproduct_window_run(S0: Mat, inputs, W: int):
+    """DeltaProduct on the per-window representation with exact arithmetic: one record per
+    sub-step (gate alpha for the first, 1 for the others; u = beta (v - (d S_cur)^T k)), the
+    state materialized by eq. 4 from the window-start state and the records, requantized at
+    every window end. inputs: (q, ks, vs, alpha, betas) per token. Returns (ys, boundaries)."""
+    dk, dv = len(S0), len(S0[0])
+    Z, a = quantize(S0)
+    ys, bounds = [], []
+    recs = []          # (scalar gate, key, u)
+
+    def mat(base):
+        out = []
+        for i in range(dk):
+            g = F(1)
+            for (gr, _, _) in recs:
+                g *= gr
+            row = [g * base[i][j] for j in range(dv)]
+            for m, (_, km, um) in enumerate(recs):
+                c = km[i]
+                for (gr, _, _) in recs[m + 1:]:
+                    c *= gr
+                for j in range(dv):
+                    row[j] += c * um[j]
+            out.append(row)
+        return out
+
+    for t, (q, ks, vs, alpha, betas) in enumerate(inputs):
+        base = dequant(Z, a)
+        for s, (k, v, b) in enumerate(zip(ks, vs, betas)):
+            d = alpha if s == 0 else F(1)
+            S = mat(base)
+            u = [b * (v[j] - sum(d * S[i][j] * k[i] for i in range(dk))) for j in range(dv)]
+            recs.append((d, list(k), u))
+        S = mat(base)
+        ys.append([sum(S[i][j] * q[i] for i in range(dk)) for j in range(dv)])
+        if (t + 1) % W == 0:
+            Z, a = quantize(S)
+            bounds.append((Z, a))
+            recs = []
+    return ys, bounds
+
+
+def deltaproduct_explicit_run(S0: Mat, inputs, W: int):
+    """Dequantize at each window start, run DeltaProduct tokens as products of Householder
+    sub-steps, requantize at its end."""
+    Z, a = quantize(S0)
+    ys, bounds = [], []
+    S = dequant(Z, a)
+    for t, (q, ks, vs, alpha, betas) in enumerate(inputs):
+        S = deltaproduct_householder(S, ks, vs, alpha, betas)
+        ys.append([sum(S[i][j] * q[i] for i in range(len(S))) for j in range(len(S[0]))])
+        if (t + 1) % W == 0:
+            Z, a = quantize(S)
+            bounds.append((Z, a))
+            S = dequant(Z, a)
+    return ys, bounds
+
+
 def log_run(S0: Mat, inputs, M: int, delta: bool = True):
     """Base + log (DeltaLog Alg. 1, eqs. 4-7) with decays as exact gate products:
     D(lbar) is the product of the gates since the last merge and D(lbar - Lam_m) the

@@ -148,6 +148,55 @@ void oracle_rwkv7_step(int64_t nh, int dk, int dv, double *S, const double *q, c
 }
 
 /*
+ * One DeltaProduct token with n delta-rule sub-steps (LeapQuant, App. A: Table 4 lists
+ * DeltaProduct as n sub-steps of eq. 1 per token). Sub-step i (0-based) has its own key
+ * k_i, value v_i and strength beta_i; the token's scalar gate alpha decays the state once,
+ * in the first sub-step:
+ *   S' = d_i S,  d_0 = alpha, d_i = 1 for i > 0      decay
+ *   u_i = beta_i (v_i - S'^T k_i)                      read along k_i from the decayed state
+ *   S  = S' + k_i u_i^T                                rank-one delta write
+ * and after the n sub-steps y = S^T q.
+ * k[nh][n][dk], v[nh][n][dv], beta[nh][n], alpha[nh].
+ */
+void oracle_deltaproduct_step(int64_t nh, int dk, int dv, int n, double *S, const double *q,
+                              const double *k, const double *v, const double *alpha,
+                              const double *beta, double *y)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t h = 0; h < nh; ++h) {
+        double *Sh = S + (size_t)h * dk * dv;
+        const double *qh = q + (size_t)h * dk;
+        double *yh = y + (size_t)h * dv;
+        double *u = (double *)malloc(sizeof(double) * dv);
+        for (int s = 0; s < n; ++s) {
+            const double *ks = k + ((size_t)h * n + s) * dk;
+            const double *vs = v + ((size_t)h * n + s) * dv;
+            const double bs = beta[(size_t)h * n + s];
+            const double d = s == 0 ? alpha[h] : 1.0;
+            for (int i = 0; i < dk; ++i)
+                for (int j = 0; j < dv; ++j)
+                    Sh[IDX2(i, j, dv)] *= d;
+            for (int j = 0; j < dv; ++j) {
+                double p = 0.0;
+                for (int i = 0; i < dk; ++i)
+                    p += Sh[IDX2(i, j, dv)] * ks[i];
+                u[j] = bs * (vs[j] - p);
+            }
+            for (int i = 0; i < dk; ++i)
+                for (int j = 0; j < dv; ++j)
+                    Sh[IDX2(i, j, dv)] += ks[i] * u[j];
+        }
+        for (int j = 0; j < dv; ++j) {
+            double acc = 0.0;
+            for (int i = 0; i < dk; ++i)
+                acc += Sh[IDX2(i, j, dv)] * qh[i];
+            yh[j] = acc;
+        }
+        free(u);
+    }
+}
+
+/*
  * Symmetric per-key-row int8 quantizer (STEPQuant notes, the uniform per-row
  * absmax baseline; LeapQuant, App. B.3, the /127 convention).
  *   a_i = max_j |S_ij|          stored as fp32
@@ -351,6 +400,70 @@ void oracle_rwkv7_q8_window_step(int64_t nh, int dk, int dv, int W, int pos, int
             Kh[IDX2(rw, i, dk)] = kh[i];
         }
         window_materialize(dk, dv, 1, rw + 1, S0, Gh, Kh, Uh, St);      /* S_t */
+        for (int j = 0; j < dv; ++j) {
+            double acc = 0.0;
+            for (int i = 0; i < dk; ++i)
+                acc += St[IDX2(i, j, dv)] * qh[i];
+            yh[j] = acc;
+        }
+        if (pos == W - 1) {
+            if (Sw_out)
+                memcpy(Sw_out + (size_t)h * dk * dv, St, sizeof(double) * dk * dv);
+            oracle_q8_quantize(dk, dv, St, Zh, ah, w_out ? w_out + (size_t)h * dk * dv : NULL);
+        }
+        free(S0);
+        free(St);
+    }
+}
+
+/*
+ * One DeltaProduct token on the per-window int8 state (LeapQuant, sec. 3.2 and App. A:
+ * each of the n sub-steps is one buffered record, as the page does for a token with two
+ * sub-steps). A window of W tokens buffers nW records with scalar gates alpha_t, 1, .., 1
+ * per token. Token pos (0-based) owns records n pos .. n pos + n - 1; sub-step s:
+ *   S_cur = eq. 4 over the records before n pos + s
+ *   u_s = beta_s (v_s - (d_s S_cur)^T k_s),  d_0 = alpha, d_s = 1     record (d_s, k_s, u_s)
+ * then y = S_t^T q with S_t = eq. 4 over all the token's records; at the last token
+ * (pos = W-1) S_W is quantized into the next window's (Z, a).
+ * Records: G[nh][nW], K[nh][nW][dk], U[nh][nW][dv]; k[nh][n][dk], v[nh][n][dv], beta[nh][n].
+ */
+void oracle_deltaproduct_q8_window_step(int64_t nh, int dk, int dv, int n, int W, int pos,
+                                        int8_t *Z, float *a, double *G, double *K, double *U,
+                                        const double *q, const double *k, const double *v,
+                                        const double *alpha, const double *beta, double *y,
+                                        double *Sw_out, double *w_out)
+{
+    const int R = n * W;
+#pragma omp parallel for schedule(static)
+    for (int64_t h = 0; h < nh; ++h) {
+        int8_t *Zh = Z + (size_t)h * dk * dv;
+        float *ah = a + (size_t)h * dk;
+        double *Gh = G + (size_t)h * R;
+        double *Kh = K + (size_t)h * R * dk;
+        double *Uh = U + (size_t)h * R * dv;
+        const double *qh = q + (size_t)h * dk;
+        double *yh = y + (size_t)h * dv;
+
+        double *S0 = (double *)malloc(sizeof(double) * dk * dv);
+        double *St = (double *)malloc(sizeof(double) * dk * dv);
+        dequant_head(dk, dv, Zh, ah, S0);
+        for (int s = 0; s < n; ++s) {
+            const int rec = n * pos + s;
+            const double *ks = k + ((size_t)h * n + s) * dk;
+            const double *vs = v + ((size_t)h * n + s) * dv;
+            const double d = s == 0 ? alpha[h] : 1.0;
+            Gh[rec] = d;
+            for (int i = 0; i < dk; ++i)
+                Kh[IDX2(rec, i, dk)] = ks[i];
+            window_materialize(dk, dv, 0, rec, S0, Gh, Kh, Uh, St);
+            for (int j = 0; j < dv; ++j) {
+                double p = 0.0;
+                for (int i = 0; i < dk; ++i)
+                    p += d * St[IDX2(i, j, dv)] * ks[i];
+                Uh[IDX2(rec, j, dv)] = beta[(size_t)h * n + s] * (vs[j] - p);
+            }
+        }
+        window_materialize(dk, dv, 0, n * pos + n, S0, Gh, Kh, Uh, St);
         for (int j = 0; j < dv; ++j) {
             double acc = 0.0;
             for (int i = 0; i < dk; ++i)
