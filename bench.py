@@ -16,7 +16,7 @@ Prints ONE JSON line on stdout:
   other_configs = GPU-only lines of the KDA, int8-window and base+log workloads,
   cpu_baseline = the fp64 oracle timed on the host cores on a bounded sample.
 Other workloads (--workload kda|q8|log|lq|kda_lq|lq4|rwkv6|rwkv6_log|rwkv7|rwkv7_q8|
-stepq|gdn_small) report the same fields for their own kernels, with the CPU baseline
+stepq|dp|dp_q8|gdn_small) report the same fields for their own kernels, with the CPU baseline
 timing the oracle of their own path; they are measurements, not the headline line.
 Per-launch timing of window positions / log lengths goes to "phases", a launch-by-launch
 pass to "step_time_distribution"; --graph replays the timed steps as one HIP graph and
@@ -48,7 +48,7 @@ KERNEL_SOURCES = {
 
 WORKLOAD_BY_FLAG = {"gdn": 2, "gdn_small": 1, "kda": 3, "q8": 4, "log": 5, "lq": 6, "rwkv6": 7,
                     "rwkv6_log": 8, "kda_lq": 9, "rwkv7": 10, "rwkv7_q8": 11, "lq4": 12,
-                    "stepq": 13}
+                    "stepq": 13, "dp": 14, "dp_q8": 15}
 LQ_TOKENS = 4
 
 
@@ -66,6 +66,8 @@ def dense_bytes_per_head(w: wl.Workload) -> int:
     """State read + write (fp32), q/k/v in their dtype, gate, beta, y (fp32)."""
     d = wl.DK
     gate = 4 * d if w.per_key_gate else 4
+    if w.variant == "deltaproduct":   # n keys, n values and n betas per token
+        return 2 * 4 * d * d + (1 + 2 * w.n) * d * _in_bytes(w) + gate + 4 * w.n + 4 * d
     extra = d * _in_bytes(w) + 4 * d if w.variant == "rwkv7" else 0     # RWKV7's kappa and erase rate a
     return 2 * 4 * d * d + 3 * d * _in_bytes(w) + gate + _beta_bytes(w) + 4 * d + extra
 
@@ -80,6 +82,8 @@ def window_step_bytes_per_head(w: wl.Workload, pos: int) -> int:
     inputs = 3 * d * _in_bytes(w) + 4 * gdim + 4
     if w.variant == "rwkv7":
         return rwkv7_window_step_bytes_per_head(w, pos)
+    if w.variant == "deltaproduct":
+        return dp_window_step_bytes_per_head(w, pos)
     rd = d * d + 4 * d + pos * rec + inputs
     wr = 4 * d + ((d * d + 4 * d) if pos == w.W - 1 else rec)
     return rd + wr
@@ -97,6 +101,23 @@ def rwkv7_window_step_bytes_per_head(w: wl.Workload, pos: int) -> int:
     wr = 4 * d + 2 * rec
     if pos == w.W - 1:
         rd += d * d + 4 * d + 2 * w.W * rec
+        wr += d * d + 4 * d
+    return rd + wr
+
+
+def dp_window_step_bytes_per_head(w: wl.Workload, pos: int) -> int:
+    """DeltaProduct on the int8 window, one record per sub-step (key in the input dtype, value
+    fp32, scalar gate fp32): the step reads codes + row scales, its n pos records, q, the n
+    keys, values and betas and alpha, and writes y and its n records; at the last token a
+    second pass reads the codes, scales and all nW records and writes the requantized codes
+    and scales."""
+    d, n = wl.DK, w.n
+    rec = d * _in_bytes(w) + 4 * d + 4
+    inputs = (1 + 2 * n) * d * _in_bytes(w) + 4 + 4 * n
+    rd = d * d + 4 * d + n * pos * rec + inputs
+    wr = 4 * d + n * rec
+    if pos == w.W - 1:
+        rd += d * d + 4 * d + n * w.W * rec
         wr += d * d + 4 * d
     return rd + wr
 
@@ -204,15 +225,17 @@ def _dev_inputs(w, steps, torch, dev):
     dt = torch.bfloat16 if w.qkv == "bf16" else torch.float32
     B, H = w.B, w.H
     names = ("q", "k", "v", "gate", "beta") + (("kappa", "a") if w.variant == "rwkv7" else ())
+    sub = (w.n,) if w.variant == "deltaproduct" else ()   # DeltaProduct: per-sub-step k, v, beta
     out = {n: [] for n in names}
     for t in range(steps):
         x = wl.step_inputs(w, t)
         for n in ("q", "k", "v") + (("kappa",) if w.variant == "rwkv7" else ()):
-            out[n].append(torch.from_numpy(x[n]).to(dev).to(dt).view(B, H, 128))
+            shape = (B, H) + (sub if n in ("k", "v") else ()) + (128,)
+            out[n].append(torch.from_numpy(x[n]).to(dev).to(dt).view(shape))
         if w.variant == "rwkv7":
             out["a"].append(torch.from_numpy(x["a"]).to(dev).view(B, H, 128))
         out["gate"].append(torch.from_numpy(x["gate"]).to(dev).view((B, H, 128) if w.per_key_gate else (B, H)))
-        out["beta"].append(torch.from_numpy(x["beta"]).to(dev).view(B, H))
+        out["beta"].append(torch.from_numpy(x["beta"]).to(dev).view((B, H) + sub))
     return {n: torch.stack(v) for n, v in out.items()}
 
 
@@ -285,6 +308,13 @@ def run_gpu(w: wl.Workload, steps: int, warmup: int, slots: bool = False, n_iter
         def step():
             i = state["t"] % n_inputs
             rsu.rwkv7_decode_step(S, x["q"][i], x["k"][i], x["v"][i], x["kappa"][i], x["gate"][i], x["a"][i], y)
+            state["t"] += 1
+    elif w.path == "dense" and w.variant == "deltaproduct":
+        S = S0
+
+        def step():
+            i = state["t"] % n_inputs
+            rsu.deltaproduct_decode_step(S, x["q"][i], x["k"][i], x["v"][i], x["gate"][i], x["beta"][i], y)
             state["t"] += 1
     elif w.path == "dense" and w.variant == "rwkv6":
         S = S0
@@ -367,6 +397,22 @@ def run_gpu(w: wl.Workload, steps: int, warmup: int, slots: bool = False, n_iter
             i = t % n_inputs
             rsu.rwkv7_q8_window(W, t % W, Z, A, Kb, Ub, Gb, x["q"][i], x["k"][i], x["v"][i], x["kappa"][i],
                                 x["gate"][i], x["a"][i], y)
+            state["t"] += 1
+    elif w.path == "q8_window" and w.variant == "deltaproduct":
+        W, R = w.W, w.n * w.W
+        Z = torch.empty(B, H, 128, 128, device=dev, dtype=torch.int8)
+        A = torch.empty(B, H, 128, device=dev)
+        rsu.q8_quantize(S0, Z, A)
+        del S0
+        Kb = torch.zeros(B, H, R, 128, device=dev, dtype=x["q"].dtype)
+        Ub = torch.zeros(B, H, R, 128, device=dev)
+        Gb = torch.zeros(B, H, R, device=dev)
+
+        def step():
+            t = state["t"]
+            i = t % n_inputs
+            rsu.deltaproduct_q8_window(W, t % W, Z, A, Kb, Ub, Gb, x["q"][i], x["k"][i], x["v"][i], x["gate"][i],
+                                       x["beta"][i], y)
             state["t"] += 1
     elif w.path == "q8_window":
         W = w.W
@@ -581,6 +627,8 @@ def run_cpu_baseline(w: wl.Workload, budget_s: float = 10.0, max_steps: int = 40
             def step(x): oracle.rwkv6_step(S, x["q"], x["k"], x["v"], x["gate"])  # noqa: E704
         elif w.variant == "rwkv7":
             def step(x): oracle.rwkv7_step(S, x["q"], x["k"], x["v"], x["gate"], x["kappa"], x["a"])  # noqa: E704
+        elif w.variant == "deltaproduct":
+            def step(x): oracle.deltaproduct_step(S, x["q"], x["k"], x["v"], x["gate"], x["beta"])  # noqa: E704
         else:
             def step(x): oracle.dense_step(S, x["q"], x["k"], x["v"], x["gate"], x["beta"])  # noqa: E704
     elif w.path == "q8_window":
@@ -589,6 +637,10 @@ def run_cpu_baseline(w: wl.Workload, budget_s: float = 10.0, max_steps: int = 40
             ws = oracle.Rwkv7WindowState(Z, a, w.W)
 
             def step(x): ws.step(x["q"], x["k"], x["v"], x["gate"], x["kappa"], x["a"])  # noqa: E704
+        elif w.variant == "deltaproduct":
+            ws = oracle.DeltaProductWindowState(Z, a, w.W, w.n)
+
+            def step(x): ws.step(x["q"], x["k"], x["v"], x["gate"], x["beta"])  # noqa: E704
         else:
             ws = oracle.WindowState(Z, a, w.W, w.per_key_gate)
 

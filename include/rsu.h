@@ -299,6 +299,35 @@ int rwkv7_q8_window(const rsu_dims *dims, int W, int pos, int8_t *Z, float *row_
                     float *y, rsu_stream_t stream);
 
 /* ------------------------------------------------------------------------
+ * DeltaProduct (LeapQuant App. A, Table 4: n delta-rule sub-steps of eq. 1 per
+ * token). Sub-step i (0-based) has its own key k_i, value v_i and strength
+ * beta_i; the token's scalar gate alpha decays the state once, in the first
+ * sub-step; the output is read after the last:
+ *     S' = d_i S (d_0 = alpha, d_i = 1 for i > 0),  u_i = beta_i (v_i - S'^T k_i),
+ *     S  = S' + k_i u_i^T,   and after the n sub-steps  y = S^T q.
+ * q [B,H,d_k], k [B,H,n,d_k], v [B,H,n,d_v] in qkv_dtype; alpha [B,H], beta [B,H,n]
+ * fp32; 1 <= n <= 4 (else RSU_E_RANGE). With n = 1 this is gdn_decode_step.
+ *
+ * deltaproduct_decode_step: the dense fp32 state S [B,H,d_k,d_v], read once and
+ *   written once, in place (every read of the token comes from the old state).
+ * deltaproduct_q8_window: the per-row int8 window of gdn_q8_window with one record
+ *   per sub-step (LeapQuant App. A treats a token with two sub-steps the same way):
+ *   token pos writes records n pos .. n pos + n - 1 with gates alpha, 1, .., 1:
+ *   Kbuf [B,H,nW,d_k] in qkv_dtype, Ubuf [B,H,nW,d_v] fp32, Gbuf [B,H,nW] fp32.
+ *   At pos = W-1 the token's records are appended as well and S_W (eq. 4 over all
+ *   nW records) is requantized into Z and row_absmax in place by a second launch
+ *   on the same stream. 1 <= W, n W <= 32, 0 <= pos < W. Codes, scales and other
+ *   rules as for the int8 window.
+ * ---------------------------------------------------------------------- */
+int deltaproduct_decode_step(const rsu_dims *dims, int n, float *S, const void *q,
+                             const void *k, const void *v, const float *alpha,
+                             const float *beta, float *y, rsu_stream_t stream);
+int deltaproduct_q8_window(const rsu_dims *dims, int n, int W, int pos, int8_t *Z,
+                           float *row_absmax, void *Kbuf, float *Ubuf, float *Gbuf,
+                           const void *q, const void *k, const void *v, const float *alpha,
+                           const float *beta, float *y, rsu_stream_t stream);
+
+/* ------------------------------------------------------------------------
  * STEPQuant's per-step packed state (STEPQuant notes, the section on the
  * key-row-aware dual-axis fit, and the section on one decode step in SGLang):
  * element (i, j) of a head's state is R_i C_j z_ij with fp16 key-row factors R,

@@ -18,6 +18,8 @@ Shapes (B requests, H heads, d = 128):
   Kc, Uc [B,H,4,d] fp16 (4 bits: Z [B,H,d,d/2] uint8 nibbles, Kc, Uc [B,H,8,d] fp16)
   STEPQuant packed state: Z [B,H,d,d/2] uint8 nibbles, R, C [B,H,d] fp16, omega [B,H,d] fp32,
   u [B,H,d] fp32 (the readout's correction, consumed by the repack)
+  DeltaProduct (n sub-steps per token): k, v [B,H,n,d], alpha [B,H], beta [B,H,n] fp32;
+  on the int8 window Kbuf [B,H,nW,d] (q dtype), Ubuf [B,H,nW,d] fp32, Gbuf [B,H,nW] fp32
 """
 from __future__ import annotations
 
@@ -80,6 +82,8 @@ _SIGS = {
     "kda_stepq_readout": [_DP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
     "gdn_stepq_repack": [_DP, _P, _P, _P, _P, _P, _P, _P, _P],
     "kda_stepq_repack": [_DP, _P, _P, _P, _P, _P, _P, _P, _P],
+    "deltaproduct_decode_step": [_DP, _I, _P, _P, _P, _P, _P, _P, _P, _P],
+    "deltaproduct_q8_window": [_DP, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
     "rsu_copy_f32": [_P, _P, ctypes.c_int64, _P],
     "rsu_read_f32": [_P, _P, ctypes.c_int64, _P],
     "rsu_fill_f32": [_P, ctypes.c_float, ctypes.c_int64, _P],
@@ -306,6 +310,53 @@ def rwkv7_q8_window(W, pos, Z, row_absmax, Kbuf, Ubuf, Gbuf, q, k, v, kappa, w, 
     _need(y, "y", torch.float32, (B, H, D))
     _call("rwkv7_q8_window", ctypes.byref(dims), int(W), int(pos), _ptr(Z), _ptr(row_absmax), _ptr(Kbuf),
           _ptr(Ubuf), _ptr(Gbuf), _ptr(q), _ptr(k), _ptr(v), _ptr(kappa), _ptr(w), _ptr(a), _ptr(y), _stream())
+    return y
+
+
+def _dp_dims(q, k, v, alpha, beta):
+    """rsu_dims and n of a DeltaProduct call: q [B,H,d], k, v [B,H,n,d] in q's dtype,
+    alpha [B,H], beta [B,H,n] fp32."""
+    if q.dim() != 3 or q.shape[-1] != D:
+        raise ValueError(f"q must be [B, H, {D}], got {tuple(q.shape)}")
+    if q.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError(f"q, k, v must be float32 or bfloat16, got {q.dtype}")
+    B, H = int(q.shape[0]), int(q.shape[1])
+    if k.dim() != 4:
+        raise ValueError(f"k must be [B, H, n, {D}], got {tuple(k.shape)}")
+    n = int(k.shape[2])
+    _need(q, "q", q.dtype, (B, H, D))
+    _need(k, "k", q.dtype, (B, H, n, D))
+    _need(v, "v", q.dtype, (B, H, n, D))
+    _need(alpha, "alpha", torch.float32, (B, H))
+    _need(beta, "beta", torch.float32, (B, H, n))
+    return _Dims(B, H, D, D, RSU_BF16 if q.dtype == torch.bfloat16 else RSU_F32), n
+
+
+def deltaproduct_decode_step(S, q, k, v, alpha, beta, y):
+    """One DeltaProduct token of n = k.shape[2] delta-rule sub-steps on the dense state S
+    [B,H,d,d] (in place); y [B,H,d] is read after the last sub-step."""
+    dims, n = _dp_dims(q, k, v, alpha, beta)
+    _need(S, "S", torch.float32, (dims.B, dims.H, D, D))
+    _need(y, "y", torch.float32, (dims.B, dims.H, D))
+    _call("deltaproduct_decode_step", ctypes.byref(dims), n, _ptr(S), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
+          _ptr(beta), _ptr(y), _stream())
+    return y
+
+
+def deltaproduct_q8_window(W, pos, Z, row_absmax, Kbuf, Ubuf, Gbuf, q, k, v, alpha, beta, y):
+    """Token pos of a window of W on the int8 state with one record per sub-step (records
+    n pos .. n pos + n - 1; at pos == W - 1 the state is requantized from all n W records).
+    Kbuf [B,H,nW,d] in q's dtype, Ubuf [B,H,nW,d] fp32, Gbuf [B,H,nW] fp32."""
+    dims, n = _dp_dims(q, k, v, alpha, beta)
+    B, H = dims.B, dims.H
+    _need(Z, "Z", torch.int8, (B, H, D, D))
+    _need(row_absmax, "row_absmax", torch.float32, (B, H, D))
+    _need(Kbuf, "Kbuf", q.dtype, (B, H, n * W, D))
+    _need(Ubuf, "Ubuf", torch.float32, (B, H, n * W, D))
+    _need(Gbuf, "Gbuf", torch.float32, (B, H, n * W))
+    _need(y, "y", torch.float32, (B, H, D))
+    _call("deltaproduct_q8_window", ctypes.byref(dims), n, int(W), int(pos), _ptr(Z), _ptr(row_absmax), _ptr(Kbuf),
+          _ptr(Ubuf), _ptr(Gbuf), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(y), _stream())
     return y
 
 

@@ -441,6 +441,47 @@ int rwkv6_log_step_slots(const rsu_dims* dims, int C, int* L, float* Sbase, floa
                       k, v, w, nullptr, y, stream);
 }
 
+int deltaproduct_decode_step(const rsu_dims* dims, int n, float* S, const void* q, const void* k, const void* v,
+                             const float* alpha, const float* beta, float* y, rsu_stream_t stream) {
+    const char* fn = "deltaproduct_decode_step";
+    int heads = 0;
+    if (int rc = check_dims(dims, &heads, fn)) return rc;
+    if (n < 1 || n > 4) return fail(RSU_E_RANGE, "%s: n=%d outside [1, 4]", fn, n);
+    if (heads == 0) return RSU_OK;
+    if (int rc = check_ptrs({{S, "S"}, {q, "q"}, {k, "k"}, {v, "v"}, {alpha, "alpha"}, {beta, "beta"}, {y, "y"}}, fn))
+        return rc;
+    return launched(rsu::launch_deltaproduct(step_args(heads, S, q, k, v, alpha, beta, y), n,
+                                             dims->qkv_dtype == RSU_BF16, stream),
+                    fn);
+}
+
+int deltaproduct_q8_window(const rsu_dims* dims, int n, int W, int pos, int8_t* Z, float* row_absmax, void* Kbuf,
+                           float* Ubuf, float* Gbuf, const void* q, const void* k, const void* v, const float* alpha,
+                           const float* beta, float* y, rsu_stream_t stream) {
+    const char* fn = "deltaproduct_q8_window";
+    int heads = 0;
+    if (int rc = check_dims(dims, &heads, fn)) return rc;
+    if (n < 1 || n > 4) return fail(RSU_E_RANGE, "%s: n=%d outside [1, 4]", fn, n);
+    if (W < 1 || n * W > rsu::kMaxW)
+        return fail(RSU_E_RANGE, "%s: W=%d with n=%d: need 1 <= W and n W <= %d", fn, W, n, rsu::kMaxW);
+    if (pos < 0 || pos >= W) return fail(RSU_E_RANGE, "%s: pos=%d outside [0, W=%d)", fn, pos, W);
+    if (heads == 0) return RSU_OK;
+    if (int rc = check_ptrs({{Z, "Z"}, {row_absmax, "row_absmax"}, {Kbuf, "Kbuf"}, {Ubuf, "Ubuf"}, {Gbuf, "Gbuf"},
+                             {q, "q"}, {k, "k"}, {v, "v"}, {alpha, "alpha"}, {beta, "beta"}, {y, "y"}}, fn))
+        return rc;
+    rsu::WindowArgs wa;
+    wa.W = W;
+    wa.pos = pos;
+    wa.Z = Z;
+    wa.A = row_absmax;
+    wa.Kbuf = Kbuf;
+    wa.Ubuf = Ubuf;
+    wa.Gbuf = Gbuf;
+    return launched(rsu::launch_dp_q8_window(step_args(heads, nullptr, q, k, v, alpha, beta, y), wa, n,
+                                             dims->qkv_dtype == RSU_BF16, stream),
+                    fn);
+}
+
 int rsu_copy_f32(const float* src, float* dst, int64_t n, rsu_stream_t stream) {
     g_err[0] = '\0';
     if (n < 0 || n % 4 != 0) return fail(RSU_E_DIMS, "rsu_copy_f32: n=%lld must be a multiple of 4", (long long)n);

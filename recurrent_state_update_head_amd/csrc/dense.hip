@@ -136,6 +136,105 @@ __global__ __launch_bounds__(kThreads) void rwkv7_step_kernel(
     }
 }
 
+// DeltaProduct (LeapQuant, App. A, Table 4: n delta-rule sub-steps of eq. 1 per token),
+// each sub-step with its own key k_i, value v_i and strength beta_i, the scalar gate alpha
+// decaying the state once, in the first. Every read of the token comes from the old state:
+// with P_i = S^T k_i and R = S^T q,
+//   u_i = beta_i (v_i - alpha P_i - sum_{m<i} u_m (k_m . k_i)),
+//   S <- alpha S + sum_i k_i u_i^T,   y = alpha R + sum_i u_i (k_i . q),
+// so the state is swept once for kN + 1 column sums and crosses HBM once in and once out.
+template <int kN, typename T>
+__global__ __launch_bounds__(kThreads) void deltaproduct_step_kernel(
+    float* __restrict__ S, const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    const float* __restrict__ alpha, const float* __restrict__ beta, float* __restrict__ y) {
+    // per wave, per key row: the kN keys and q (each wave stages its own copy)
+    __shared__ float rowk[kThreads / 64][kN + 1][kD];
+
+    const int h = head_of_block(blockIdx.x, gridDim.x);
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
+    const int ro = lane >> 3;
+    const int col = wave * 32 + (lane & 7) * 4;
+    const size_t vec_off = static_cast<size_t>(h) * kD;
+    const size_t key_off = static_cast<size_t>(h) * kN * kD;
+
+    f32x2 kk[kN];
+#pragma unroll
+    for (int i = 0; i < kN; ++i) kk[i] = load2_in(k, key_off + i * kD + 2 * lane);
+    const f32x2 q2 = load2_in(q, vec_off + 2 * lane);
+    const float al = alpha[h];
+
+    float* Sh = S + static_cast<size_t>(h) * kD * kD;
+    f32x4 s[kRowsPerThread];
+#pragma unroll
+    for (int it = 0; it < kRowsPerThread; ++it)
+        s[it] = stream_load(Sh + (row_block(it, wave) * 8 + ro) * kD + col);
+
+#pragma unroll
+    for (int i = 0; i < kN; ++i) {
+        rowk[wave][i][2 * lane] = kk[i].x;
+        rowk[wave][i][2 * lane + 1] = kk[i].y;
+    }
+    rowk[wave][kN][2 * lane] = q2.x;
+    rowk[wave][kN][2 * lane + 1] = q2.y;
+    // the key-key and key-query dot products, wave-uniform (kept in scalar registers)
+    float kq[kN], kkd[kN][kN];
+#pragma unroll
+    for (int i = 0; i < kN; ++i) {
+        kq[i] = uniform(wave_sum(kk[i].x * q2.x + kk[i].y * q2.y));
+#pragma unroll
+        for (int m = 0; m < i; ++m) kkd[m][i] = uniform(wave_sum(kk[m].x * kk[i].x + kk[m].y * kk[i].y));
+    }
+    wave_lds_sync();
+
+    // kN + 1 column sums over this thread's 16 rows, then over the 8 row lanes
+    f32x4 P[kN + 1];
+#pragma unroll
+    for (int i = 0; i <= kN; ++i) P[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int it = 0; it < kRowsPerThread; ++it) {
+        const int row = row_block(it, wave) * 8 + ro;
+#pragma unroll
+        for (int i = 0; i <= kN; ++i) P[i] += s[it] * rowk[wave][i][row];
+    }
+#pragma unroll
+    for (int i = 0; i <= kN; ++i) P[i] = sum_row_lanes(P[i]);
+
+    // the sub-steps' corrections, in order (values and strengths loaded only now: held
+    // through the sweep they would take 5 kN more registers)
+    __builtin_amdgcn_sched_barrier(0);
+    f32x4 vv[kN];
+    float bt[kN];
+#pragma unroll
+    for (int i = 0; i < kN; ++i) {
+        vv[i] = load4_in(v, key_off + i * kD + col);
+        bt[i] = beta[static_cast<size_t>(h) * kN + i];
+    }
+    f32x4 u[kN];
+#pragma unroll
+    for (int i = 0; i < kN; ++i) {
+        f32x4 p = al * P[i];
+#pragma unroll
+        for (int m = 0; m < i; ++m) p += u[m] * kkd[m][i];
+        u[i] = bt[i] * (vv[i] - p);
+    }
+    if (ro == 0) {
+        f32x4 o = al * P[kN];
+#pragma unroll
+        for (int i = 0; i < kN; ++i) o += u[i] * kq[i];
+        *reinterpret_cast<f32x4*>(y + vec_off + col) = o;
+    }
+
+#pragma unroll
+    for (int it = 0; it < kRowsPerThread; ++it) {
+        const int row = row_block(it, wave) * 8 + ro;
+        f32x4 x = s[it] * al;
+#pragma unroll
+        for (int i = 0; i < kN; ++i) x += rowk[wave][i][row] * u[i];
+        stream_store(Sh + row * kD + col, x);
+    }
+}
+
 // Read+write copy with the same access pattern, for the practical HBM ceiling.
 __global__ __launch_bounds__(kThreads) void copy_kernel(const float* __restrict__ src,
                                                         float* __restrict__ dst, int64_t n) {
@@ -219,6 +318,28 @@ hipError_t launch_rwkv7(const StepArgs& a, const void* kappa, const float* erase
                            static_cast<const float*>(a.v), static_cast<const float*>(kappa), a.gate, erase_rate,
                            a.y);
     return hipGetLastError();
+}
+
+template <int kN, typename T>
+static hipError_t launch_dp_t(const StepArgs& a, hipStream_t stream) {
+    hipLaunchKernelGGL((deltaproduct_step_kernel<kN, T>), dim3(a.heads), dim3(kThreads), 0, stream, a.S,
+                       static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v),
+                       a.gate, a.beta, a.y);
+    return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t launch_dp_n(const StepArgs& a, int n, hipStream_t stream) {
+    switch (n) {
+        case 1: return launch_dp_t<1, T>(a, stream);
+        case 2: return launch_dp_t<2, T>(a, stream);
+        case 3: return launch_dp_t<3, T>(a, stream);
+        default: return launch_dp_t<4, T>(a, stream);
+    }
+}
+
+hipError_t launch_deltaproduct(const StepArgs& a, int n, bool bf16, hipStream_t stream) {
+    return bf16 ? launch_dp_n<bf16_t>(a, n, stream) : launch_dp_n<float>(a, n, stream);
 }
 
 hipError_t launch_copy(const float* src, float* dst, int64_t n, hipStream_t stream) {

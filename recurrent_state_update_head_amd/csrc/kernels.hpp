@@ -44,6 +44,9 @@ hipError_t launch_rwkv6(const StepArgs& a, bool bf16, hipStream_t stream);
 // kappa [heads, 128] in the input dtype, erase_rate [heads, 128] fp32; beta unused)
 hipError_t launch_rwkv7(const StepArgs& a, const void* kappa, const float* erase_rate, bool bf16,
                         hipStream_t stream);
+// DeltaProduct with n sub-steps (1 <= n <= 4): k, v [heads, n, 128] in the input dtype, gate = alpha
+// [heads], beta [heads, n]
+hipError_t launch_deltaproduct(const StepArgs& a, int n, bool bf16, hipStream_t stream);
 hipError_t launch_copy(const float* src, float* dst, int64_t n, hipStream_t stream);
 hipError_t launch_read_probe(const float* src, float* sums, int tiles, hipStream_t stream);
 hipError_t launch_write_probe(float* dst, float value, int tiles, hipStream_t stream);
@@ -54,6 +57,10 @@ hipError_t launch_q8_window(const StepArgs& a, const WindowArgs& w, bool per_key
 // records per head, Gbuf per key): gate = w, kappa in the input dtype, erase [heads, 128]
 hipError_t launch_rwkv7_q8_window(const StepArgs& a, const WindowArgs& w, const void* kappa, const float* erase,
                                   bool bf16, hipStream_t stream);
+// DeltaProduct on the int8 window, one record per sub-step (n records per token, n W <= 32):
+// k, v [heads, n, 128] in the input dtype, gate = alpha [heads], beta [heads, n]; Kbuf [heads, nW, 128],
+// Ubuf [heads, nW, 128], Gbuf [heads, nW] scalar gates. At pos = W - 1 a second launch requantizes.
+hipError_t launch_dp_q8_window(const StepArgs& a, const WindowArgs& w, int n, bool bf16, hipStream_t stream);
 // LeapQuant's boundary format (GDN or KDA, bf16 keys, W <= 16): payload, per-column absmax,
 // per-row smoothing scales, fp16 token pairs [heads][4][128], and the window's records.
 struct LqArgs {

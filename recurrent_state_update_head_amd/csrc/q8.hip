@@ -763,9 +763,178 @@ __global__ __launch_bounds__(kThreads) void rwkv7_q8_step_kernel(
     }
 }
 
+// ---- DeltaProduct on the per-window int8 state (LeapQuant, sec. 3.2 with App. A: each of a
+// token's kN delta-rule sub-steps is one buffered record; gate alpha for the first, 1 for the
+// others; key k_i; correction u_i). Token pos reads S_{t-1} (eq. 4 over the kN pos earlier
+// records) along its kN keys and along q, all in one sweep; with P_i = S_{t-1}^T k_i and
+// R = S_{t-1}^T q,
+//   u_i = beta_i (v_i - alpha P_i - sum_{m<i} u_m (k_m . k_i)),   y = alpha R + sum_i u_i (k_i . q),
+// then appends its kN records; at the end of the window a second launch requantizes S_W from
+// all kN W records. The records' gates are scalars, so their decays come from a suffix scan
+// across the record lanes. Layouts as in the RWKV7 step: record keys in 16-lane groups for
+// their coefficients, record corrections in the registers of the row-owners.
+template <int kN, typename T>
+__global__ __launch_bounds__(kThreads) void dp_q8_step_kernel(
+    int W, int pos, const int8_t* __restrict__ Z, const float* __restrict__ A, T* __restrict__ Kbuf,
+    float* __restrict__ Ubuf, float* __restrict__ Gbuf, const T* __restrict__ q, const T* __restrict__ k,
+    const T* __restrict__ v, const float* __restrict__ alpha, const float* __restrict__ beta,
+    float* __restrict__ y) {
+    constexpr int kRec = kRwkv7Rec;       // record slots (kN W <= 32)
+    constexpr int kX = kN + 1;            // read vectors: the kN keys, then q
+    constexpr int kKSlots = kRec / 16, kUSlots = kRec / 8;
+    __shared__ float rowv[kX][kD];        // a_r/127 Gamma_{1:t-1} x_r
+    __shared__ float coef[kRec][kX];      // per record, (Gamma_{j+1:t-1} k_j) . x
+    __shared__ float red[4][kX][kD];      // per-wave column partials
+    __shared__ float dots[2][kX][kX];     // [wave][m][i]: partial k_m . x_i, m < i, of the two row waves
+
+    const int h = head_of_block(blockIdx.x, gridDim.x), tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
+    const int c4 = lane & 31, ro = lane >> 5, owner = 2 * wave + ro;
+    const int grp = tid >> 4, ch = tid & 15;
+    const size_t vec_off = static_cast<size_t>(h) * kD;
+    const size_t key_off = static_cast<size_t>(h) * kN * kD;
+    const int R = kN * W;                          // record slots per head
+    const size_t rec0 = static_cast<size_t>(h) * R * kD;
+    const int r = tid & (kD - 1);
+    const bool first = tid < kD;
+    const int nrec = kN * pos;
+
+    // ---- loads: records, gates, inputs, then the codes
+    Raw8<T> kc[kKSlots];
+#pragma unroll
+    for (int s = 0; s < kKSlots; ++s) {
+        const int j = grp + 16 * s;
+        if (16 * s < nrec) kc[s].load(Kbuf + rec0 + static_cast<size_t>(j < nrec ? j : 0) * kD + 8 * ch);
+    }
+    f32x4 ur[kUSlots];
+#pragma unroll
+    for (int m = 0; m < kUSlots; ++m) {
+        const int j = owner + 8 * m;
+        ur[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (8 * m < nrec)
+            ur[m] = *reinterpret_cast<const f32x4*>(Ubuf + rec0 + static_cast<size_t>(j < nrec ? j : 0) * kD + 4 * c4);
+    }
+    const float g_lane = lane < nrec ? Gbuf[static_cast<size_t>(h) * R + lane] : 1.f;
+    Raw8<T> xch[kX];  // the lane's 8 key rows of every read vector
+#pragma unroll
+    for (int i = 0; i < kN; ++i) xch[i].load(k + key_off + i * kD + 8 * ch);
+    xch[kN].load(q + vec_off + 8 * ch);
+    float xr[kX];     // key row r of every read vector
+#pragma unroll
+    for (int i = 0; i < kN; ++i) xr[i] = load_in(k, key_off + i * kD + r);
+    xr[kN] = load_in(q, vec_off + r);
+    const float ar = A[vec_off + r];
+    const float al = alpha[h];
+    const uint32_t* Zh = reinterpret_cast<const uint32_t*>(Z + static_cast<size_t>(h) * kD * kD);
+    uint32_t zw[kRowsPerThread];
+#pragma unroll
+    for (int it = 0; it < kRowsPerThread; ++it)
+        zw[it] = __builtin_nontemporal_load(Zh + q8_row(it, wave, ro) * (kD / 4) + c4);
+
+    // ---- decays: products of the gates after each record (g = 1 from record nrec on)
+    const float Sfx = suffix_prod<kRec>(g_lane, lane);
+    const float E = suffix_prod_excl<kRec>(Sfx, lane);
+    float Gs[kKSlots];
+#pragma unroll
+    for (int s = 0; s < kKSlots; ++s) Gs[s] = lane_gather(E, grp + 16 * s);
+    const float Gall = lane_value(Sfx, 0);
+
+    // ---- record coefficients against every read vector, over the 16 lanes of each group
+#pragma unroll
+    for (int s = 0; s < kKSlots; ++s) {
+        if (16 * s >= nrec) continue;
+        const int j = grp + 16 * s;
+        float c[kX];
+#pragma unroll
+        for (int i = 0; i < kX; ++i) c[i] = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float ej = kc[s][e] * Gs[s];
+#pragma unroll
+            for (int i = 0; i < kX; ++i) c[i] += ej * xch[i][e];
+        }
+#pragma unroll
+        for (int i = 0; i < kX; ++i) c[i] = row16_sum(c[i]);
+        if (ch == 0 && j < nrec)
+#pragma unroll
+            for (int i = 0; i < kX; ++i) coef[j][i] = c[i];
+    }
+    if (first) {
+        const float c0 = ar * (1.f / 127.f) * Gall;  // a_r/127 Gamma_{1:t-1} at row r
+#pragma unroll
+        for (int i = 0; i < kX; ++i) rowv[i][r] = c0 * xr[i];
+#pragma unroll
+        for (int m = 0; m < kN; ++m)
+#pragma unroll
+            for (int i = m + 1; i < kX; ++i) {
+                const float d = wave_sum(xr[m] * xr[i]);
+                if (lane == 0) dots[wave][m][i] = d;
+            }
+    }
+    __syncthreads();
+
+    // ---- one sweep of the int8 tile for every read vector, plus the records
+    f32x4 P[kX];
+#pragma unroll
+    for (int i = 0; i < kX; ++i) P[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int it = 0; it < kRowsPerThread; ++it) {
+        const int row = q8_row(it, wave, ro);
+        const f32x4 zf = unpack_i8x4(zw[it]);
+#pragma unroll
+        for (int i = 0; i < kX; ++i) P[i] += zf * rowv[i][row];
+        if ((it & 3) == 3) __builtin_amdgcn_sched_barrier(0);  // decode a few words at a time
+    }
+#pragma unroll
+    for (int m = 0; m < kUSlots; ++m) {
+        if (8 * m >= nrec) continue;
+        const int j = owner + 8 * m;
+        if (j < nrec)
+#pragma unroll
+            for (int i = 0; i < kX; ++i) P[i] += ur[m] * coef[j][i];
+    }
+#pragma unroll
+    for (int i = 0; i < kX; ++i) {
+        P[i] = f32x4{add_xor32(P[i].x), add_xor32(P[i].y), add_xor32(P[i].z), add_xor32(P[i].w)};
+        if (ro == 0) *reinterpret_cast<f32x4*>(&red[wave][i][4 * c4]) = P[i];
+    }
+    __syncthreads();
+
+    // ---- the sub-steps' corrections in order, the output, and the token's records
+    // (thread -> value column c == key row r)
+    if (first) {
+        const int c = tid;
+        float Pc[kX];
+#pragma unroll
+        for (int i = 0; i < kX; ++i) Pc[i] = red[0][i][c] + red[1][i][c] + red[2][i][c] + red[3][i][c];
+        float u[kN];
+#pragma unroll
+        for (int i = 0; i < kN; ++i) {
+            float p = al * Pc[i];
+#pragma unroll
+            for (int m = 0; m < i; ++m) p += u[m] * (dots[0][m][i] + dots[1][m][i]);
+            u[i] = beta[static_cast<size_t>(h) * kN + i] * (load_in(v, key_off + i * kD + c) - p);
+        }
+        float o = al * Pc[kN];
+#pragma unroll
+        for (int i = 0; i < kN; ++i) o += u[i] * (dots[0][i][kN] + dots[1][i][kN]);
+        y[vec_off + c] = o;
+#pragma unroll
+        for (int i = 0; i < kN; ++i) {
+            const size_t rec = rec0 + static_cast<size_t>(nrec + i) * kD;
+            Ubuf[rec + c] = u[i];
+            store_in(Kbuf, rec + c, xr[i]);
+        }
+        if (c < kN) Gbuf[static_cast<size_t>(h) * R + nrec + c] = c == 0 ? al : 1.f;
+    }
+}
+
+
 // ---- requantization of S_W = Gamma_{1:W} S^_0 + sum_j Gamma_{j+1:W} k_j u_j^T from nrec
 // buffered records and no current step (the window's last records are already appended).
-template <typename T>
+// kPerKey: per-key record gates Gbuf [heads, rec_stride, 128] (RWKV7), else one scalar gate per
+// record, Gbuf [heads, rec_stride] (DeltaProduct sub-steps).
+template <bool kPerKey, typename T>
 __global__ __launch_bounds__(kThreads) void q8_requant_kernel(int nrec, int rec_stride, int8_t* __restrict__ Z,
                                                               float* __restrict__ A, const T* __restrict__ Kbuf,
                                                               const float* __restrict__ Ubuf,
@@ -789,9 +958,14 @@ __global__ __launch_bounds__(kThreads) void q8_requant_kernel(int nrec, int rec_
     Stager<float, kRwkv7Rec * kD> su;
     sk.load(Kbuf + rec0, nrec * kD, tid);
     su.load(Ubuf + rec0, nrec * kD, tid);
-    KeyDecays<kRwkv7Rec / 2> kdec;  // the gates of key row tid >> 1, half tid & 1
-    kdec.load(Gbuf + rec0, nrec, tid);
+    KeyDecays<kPerKey ? kRwkv7Rec / 2 : 1> kdec;  // per-key gates of key row tid >> 1, half tid & 1
+    float g_lane = 1.f;                             // scalar gates: lane j holds the gate of record j
+    if constexpr (kPerKey) kdec.load(Gbuf + rec0, nrec, tid);
+    else if (lane < nrec) g_lane = Gbuf[static_cast<size_t>(h) * rec_stride + lane];
     const float ar_half_row = A[vec_off + (tid >> 1)];
+    const float ar = A[vec_off + r];
+    (void)ar_half_row;
+    (void)ar;
     uint32_t zw[kRowsPerThread];
 #pragma unroll
     for (int it = 0; it < kRowsPerThread; ++it)
@@ -802,9 +976,14 @@ __global__ __launch_bounds__(kThreads) void q8_requant_kernel(int nrec, int rec_
 #pragma unroll
     for (int it = 0; it < kRowsPerThread; ++it) Zs[q8_row(it, wave, ro) * kZsStride + c4] = zw[it];
     __syncthreads();
-    {   // both halves of each key row's records at once
+    if constexpr (kPerKey) {  // both halves of each key row's records at once
         const float G = kdec.apply(KE, nrec, 1.f, tid);
         if ((tid & 1) == 0) zcoef[tid >> 1] = ar_half_row * (1.f / 127.f) * G;
+    } else {                  // the scalar decays from a suffix scan over the record lanes
+        const float Sfx = suffix_prod<kRwkv7Rec>(g_lane, lane);
+        const float E = suffix_prod_excl<kRwkv7Rec>(Sfx, lane);
+        for (int i = tid; i < nrec * kD; i += kThreads) KE[i] *= lane_gather(E, i >> 7);
+        if (first) zcoef[r] = ar * (1.f / 127.f) * lane_value(Sfx, 0);
     }
     if (first)
         for (int j = nrec; j < kRwkv7Rec; ++j) KE[j * kD + r] = 0.f;
@@ -1108,13 +1287,44 @@ static hipError_t launch_rwkv7_window_t(const StepArgs& a, const WindowArgs& w, 
     if (hipError_t e = hipGetLastError()) return e;
     if (w.pos < w.W - 1) return hipSuccess;
     const int floats = boundary_lds_floats(kRwkv7Rec);
-    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(q8_requant_kernel<T>),
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(q8_requant_kernel<true, T>),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize,
                                                        static_cast<int>(sizeof(float) * floats));
     if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL(q8_requant_kernel<T>, dim3(a.heads), dim3(kThreads), sizeof(float) * floats, stream,
+    hipLaunchKernelGGL((q8_requant_kernel<true, T>), dim3(a.heads), dim3(kThreads), sizeof(float) * floats, stream,
                        2 * w.W, 2 * w.W, w.Z, w.A, static_cast<const T*>(w.Kbuf), w.Ubuf, w.Gbuf);
     return hipGetLastError();
+}
+
+template <int kN, typename T>
+static hipError_t launch_dp_window_t(const StepArgs& a, const WindowArgs& w, hipStream_t stream) {
+    hipLaunchKernelGGL((dp_q8_step_kernel<kN, T>), dim3(a.heads), dim3(kThreads), 0, stream, w.W, w.pos, w.Z, w.A,
+                       static_cast<T*>(w.Kbuf), w.Ubuf, w.Gbuf, static_cast<const T*>(a.q),
+                       static_cast<const T*>(a.k), static_cast<const T*>(a.v), a.gate, a.beta, a.y);
+    if (hipError_t e = hipGetLastError()) return e;
+    if (w.pos < w.W - 1) return hipSuccess;
+    const int floats = boundary_lds_floats(kRwkv7Rec);
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(q8_requant_kernel<false, T>),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                       static_cast<int>(sizeof(float) * floats));
+    if (attr != hipSuccess) return attr;
+    hipLaunchKernelGGL((q8_requant_kernel<false, T>), dim3(a.heads), dim3(kThreads), sizeof(float) * floats, stream,
+                       kN * w.W, kN * w.W, w.Z, w.A, static_cast<const T*>(w.Kbuf), w.Ubuf, w.Gbuf);
+    return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t launch_dp_window_n(const StepArgs& a, const WindowArgs& w, int n, hipStream_t stream) {
+    switch (n) {
+        case 1: return launch_dp_window_t<1, T>(a, w, stream);
+        case 2: return launch_dp_window_t<2, T>(a, w, stream);
+        case 3: return launch_dp_window_t<3, T>(a, w, stream);
+        default: return launch_dp_window_t<4, T>(a, w, stream);
+    }
+}
+
+hipError_t launch_dp_q8_window(const StepArgs& a, const WindowArgs& w, int n, bool bf16, hipStream_t stream) {
+    return bf16 ? launch_dp_window_n<bf16_t>(a, w, n, stream) : launch_dp_window_n<float>(a, w, n, stream);
 }
 
 hipError_t launch_rwkv7_q8_window(const StepArgs& a, const WindowArgs& w, const void* kappa, const float* erase,

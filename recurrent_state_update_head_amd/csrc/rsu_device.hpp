@@ -236,6 +236,11 @@ __device__ __forceinline__ float half_wave_max(float x) {
     x = fmaxf(x, dpp<kDppRor4>(x));
     return max_xor16(x);
 }
+// A value that is the same in every lane, moved to a scalar register.
+__device__ __forceinline__ float uniform(float x) {
+    return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(x)));
+}
+
 // Sum over all 64 lanes of a wave (result in every lane).
 __device__ __forceinline__ float wave_sum(float x) { return add_xor32(add_xor16(row16_sum(x))); }
 

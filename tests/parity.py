@@ -40,9 +40,12 @@ def dev_inputs(w: wl.Workload, t: int):
     """Host inputs of step t (fp32 numpy) and their device tensors in the workload dtype."""
     x = wl.step_inputs(w, t)
     B, H, dt = w.B, w.H, qkv_dtype(w)
-    d = {n: torch.from_numpy(x[n]).to(DEV).to(dt).view(B, H, 128) for n in ("q", "k", "v")}
+    sub = (w.n,) if w.variant == "deltaproduct" else ()   # DeltaProduct: one key, value, beta per sub-step
+    d = {"q": torch.from_numpy(x["q"]).to(DEV).to(dt).view(B, H, 128)}
+    for n in ("k", "v"):
+        d[n] = torch.from_numpy(x[n]).to(DEV).to(dt).view((B, H) + sub + (128,))
     d["gate"] = torch.from_numpy(x["gate"]).to(DEV).view((B, H, 128) if w.per_key_gate else (B, H))
-    d["beta"] = torch.from_numpy(x["beta"]).to(DEV).view(B, H)
+    d["beta"] = torch.from_numpy(x["beta"]).to(DEV).view((B, H) + sub)
     if "kappa" in x:
         d["kappa"] = torch.from_numpy(x["kappa"]).to(DEV).to(dt).view(B, H, 128)
         d["a"] = torch.from_numpy(x["a"]).to(DEV).view(B, H, 128)
@@ -96,6 +99,9 @@ def run_dense(w: wl.Workload, sample: int | None = None):
         elif w.variant == "rwkv7":
             m.rwkv7_decode_step(S, d["q"], d["k"], d["v"], d["kappa"], d["gate"], d["a"], y)
             y_ref = oracle.rwkv7_step(S_ref, *host_slice(x, heads)[:4], x["kappa"][heads], x["a"][heads])
+        elif w.variant == "deltaproduct":
+            m.deltaproduct_decode_step(S, d["q"], d["k"], d["v"], d["gate"], d["beta"], y)
+            y_ref = oracle.deltaproduct_step(S_ref, *host_slice(x, heads))
         else:
             fn(S, d["q"], d["k"], d["v"], d["gate"], d["beta"], y)
             y_ref = oracle.dense_step(S_ref, *host_slice(x, heads))
@@ -360,6 +366,15 @@ def new_window_buffers(w: wl.Workload):
             "Ubuf": torch.zeros(B, H, 2 * W, 128, device=DEV),
             "Gbuf": torch.zeros(B, H, 2 * W, 128, device=DEV),
         }
+    if w.variant == "deltaproduct":   # one record per sub-step, scalar gates
+        R = w.n * W
+        return {
+            "Z": torch.zeros(B, H, 128, 128, device=DEV, dtype=torch.int8),
+            "A": torch.zeros(B, H, 128, device=DEV),
+            "Kbuf": torch.zeros(B, H, R, 128, device=DEV, dtype=qkv_dtype(w)),
+            "Ubuf": torch.zeros(B, H, R, 128, device=DEV),
+            "Gbuf": torch.zeros(B, H, R, device=DEV),
+        }
     return {
         "Z": torch.zeros(B, H, 128, 128, device=DEV, dtype=torch.int8),
         "A": torch.zeros(B, H, 128, device=DEV),
@@ -374,6 +389,10 @@ def window_step(w: wl.Workload, pos: int, buf, d, y):
     if w.variant == "rwkv7":
         m.rwkv7_q8_window(w.W, pos, buf["Z"], buf["A"], buf["Kbuf"], buf["Ubuf"], buf["Gbuf"], d["q"], d["k"],
                           d["v"], d["kappa"], d["gate"], d["a"], y)
+        return
+    if w.variant == "deltaproduct":
+        m.deltaproduct_q8_window(w.W, pos, buf["Z"], buf["A"], buf["Kbuf"], buf["Ubuf"], buf["Gbuf"], d["q"],
+                                 d["k"], d["v"], d["gate"], d["beta"], y)
         return
     fn = m.kda_q8_window if w.per_key_gate else m.gdn_q8_window
     fn(w.W, pos, buf["Z"], buf["A"], buf["Kbuf"], buf["Ubuf"], buf["Gbuf"], d["q"], d["k"], d["v"],
@@ -408,8 +427,12 @@ def run_window(w: wl.Workload, sample: int | None = None, steps: int | None = No
         pos = t % W
         if pos == 0:
             Zs, As = take(buf["Z"], hd, (128, 128)), take(buf["A"], hd, (128,))
-            ref = oracle.Rwkv7WindowState(Zs, As, W) if w.variant == "rwkv7" else \
-                oracle.WindowState(Zs, As, W, w.per_key_gate)
+            if w.variant == "rwkv7":
+                ref = oracle.Rwkv7WindowState(Zs, As, W)
+            elif w.variant == "deltaproduct":
+                ref = oracle.DeltaProductWindowState(Zs, As, W, w.n)
+            else:
+                ref = oracle.WindowState(Zs, As, W, w.per_key_gate)
         x, d = dev_inputs(w, t)
         window_step(w, pos, buf, d, y)
         args = host_slice(x, heads)

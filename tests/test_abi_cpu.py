@@ -235,6 +235,30 @@ def test_stream_probe_validation(lib):
     assert w(None, 1.0, 0, None) == RSU_OK
 
 
+def test_deltaproduct_validation(lib):
+    f = lib.deltaproduct_decode_step
+    f.restype = ctypes.c_int
+    d = Dims(2, 3, 128, 128, 1)
+    args = [GOOD] * 7                                          # S, q, k, v, alpha, beta, y
+    assert f(ctypes.byref(d), 0, *args, None) == E_RANGE
+    assert f(ctypes.byref(d), 5, *args, None) == E_RANGE
+    assert f(ctypes.byref(d), 2, GOOD, GOOD, GOOD, GOOD, GOOD, None, GOOD, None) == E_NULL
+    assert "beta is NULL" in _last(lib)
+    assert f(ctypes.byref(d), 2, GOOD, GOOD, ODD, GOOD, GOOD, GOOD, GOOD, None) == E_ALIGN
+    assert f(ctypes.byref(Dims(0, 3, 128, 128, 1)), 2, *([None] * 7), None) == RSU_OK
+    w = lib.deltaproduct_q8_window
+    w.restype = ctypes.c_int
+    wargs = [GOOD] * 11                                        # Z .. y
+    assert w(ctypes.byref(d), 2, 17, 0, *wargs, None) == E_RANGE   # n W > 32
+    assert w(ctypes.byref(d), 4, 9, 0, *wargs, None) == E_RANGE
+    assert w(ctypes.byref(d), 2, 16, 16, *wargs, None) == E_RANGE  # pos >= W
+    assert w(ctypes.byref(d), 2, 0, 0, *wargs, None) == E_RANGE
+    assert w(ctypes.byref(d), 0, 8, 0, *wargs, None) == E_RANGE
+    assert w(ctypes.byref(d), 2, 16, 3, *([GOOD] * 4), None, *([GOOD] * 6), None) == E_NULL
+    assert "Gbuf is NULL" in _last(lib)
+    assert w(ctypes.byref(Dims(2, 0, 128, 128, 1)), 2, 16, 3, *([None] * 11), None) == RSU_OK
+
+
 def test_rwkv6_validation(lib):
     f = lib.rwkv6_decode_step
     f.restype = ctypes.c_int

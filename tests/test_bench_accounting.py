@@ -101,3 +101,18 @@ def test_log_cycle_bytes_follow_the_traffic_model(variant, M):
     L = bench.slot_lengths(w2)
     per = [bench.log_step_bytes_per_head(w2, int(x)) for x in L]
     assert bench.slots_bytes_per_head(w2) == pytest.approx(sum(per) / len(per), rel=1e-15)
+
+
+def test_deltaproduct_bytes():
+    """DeltaProduct with n = 2 (bf16): the dense step moves the state both ways plus q, two keys,
+    two values (bf16), alpha, two betas and y; with n = 1 it is the GDN step's accounting. On
+    the window each sub-step is a 772-byte record (bf16 key, fp32 value, fp32 scalar gate)."""
+    w = wl.WORKLOADS[14]
+    assert bench.dense_bytes_per_head(w) == 131072 + 5 * 256 + 4 + 8 + 512
+    assert bench.dense_bytes_per_head(wl.custom(w, n=1)) == bench.dense_bytes_per_head(wl.WORKLOADS[2])
+    ww = wl.WORKLOADS[15]
+    rec = 256 + 512 + 4
+    inputs = 5 * 256 + 4 + 8
+    assert bench.window_step_bytes_per_head(ww, 3) == 16384 + 512 + 6 * rec + inputs + 512 + 2 * rec
+    last = bench.window_step_bytes_per_head(ww, 15)
+    assert last == (16384 + 512 + 30 * rec + inputs + 512 + 2 * rec) + (16384 + 512 + 32 * rec) + (16384 + 512)

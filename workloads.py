@@ -29,7 +29,8 @@ DK = 128
 DV = 128
 
 # tensor tags of the substreams
-_TAG_S0, _TAG_Q, _TAG_K, _TAG_V, _TAG_GATE, _TAG_BETA, _TAG_OUTLIER, _TAG_KAPPA, _TAG_A, _TAG_OMEGA = range(10)
+(_TAG_S0, _TAG_Q, _TAG_K, _TAG_V, _TAG_GATE, _TAG_BETA, _TAG_OUTLIER, _TAG_KAPPA, _TAG_A, _TAG_OMEGA,
+ _TAG_SUB_K, _TAG_SUB_V, _TAG_SUB_BETA) = range(13)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -37,7 +38,8 @@ class Workload:
     cid: int
     name: str
     variant: str          # "gdn" (scalar gate alpha), "kda" (per-key gate d), "rwkv6" (per-key decay w,
-                          # no delta read) or "rwkv7" (per-key decay w, erase along kappa read with a * kappa)
+                          # no delta read), "rwkv7" (per-key decay w, erase along kappa read with a * kappa)
+                          # or "deltaproduct" (n delta-rule sub-steps per token, scalar gate alpha)
     path: str             # "dense", "q8_window", "lq_window", "log" or "stepq"
     B: int
     H: int
@@ -50,6 +52,7 @@ class Workload:
     M: int = 0            # merge interval of the base+log path (capacity C = M - 1)
     outliers: bool = False
     bits: int = 8         # code width of the LeapQuant window format (8, or 4 with 8 tokens)
+    n: int = 1            # DeltaProduct: delta-rule sub-steps per token
 
     @property
     def heads(self) -> int:
@@ -92,6 +95,12 @@ WORKLOADS = {
     # dense GDN workload's serving shape, with the int8 workload's row and column outliers
     13: Workload(13, "gdn_stepq_b256_h48_bf16", "gdn", "stepq", 256, 48, 16, "bf16", 0.90, 0.999,
                  outliers=True, bits=4),
+    # DeltaProduct with two sub-steps per token (LeapQuant App. A, Table 4) at the dense GDN
+    # workload's serving shape, and on the int8 window (one record per sub-step, 32 per window)
+    14: Workload(14, "deltaproduct_dense_b256_h48_n2_bf16", "deltaproduct", "dense", 256, 48, 16, "bf16",
+                 0.90, 0.999, n=2),
+    15: Workload(15, "deltaproduct_q8_window_b256_h48_n2_w16", "deltaproduct", "q8_window", 256, 48, 256,
+                 "bf16", 0.90, 0.999, W=16, outliers=True, n=2),
 }
 
 
@@ -174,7 +183,9 @@ def step_inputs(wl: Workload, t: int) -> dict:
     v: N(0,1) in the input dtype. gate: alpha ~ U(lo, hi) per head [B*H] for
     GDN, d ~ U(lo, hi) per key channel [B*H, 128] for KDA. beta ~ U(0, 1) [B*H].
     RWKV7 also draws its removal key kappa (N(0,1), L2-normalised, input dtype) and its
-    per-key erase rate a ~ U(0, 1) [B*H, 128]. All arrays are fp32.
+    per-key erase rate a ~ U(0, 1) [B*H, 128]. DeltaProduct draws a key, a value and a
+    strength per sub-step the same way (k [B*H, n, 128], v [B*H, n, 128], beta [B*H, n]).
+    All arrays are fp32.
     """
     n = wl.heads
     f32 = np.float32
@@ -191,6 +202,18 @@ def step_inputs(wl: Workload, t: int) -> dict:
         out["kappa"] = _cast(wl, _unit_rows(_rng(wl, _TAG_KAPPA, t).standard_normal((n, DK), dtype=f32)
                                             .astype(np.float64)))
         out["a"] = _rng(wl, _TAG_A, t).random((n, DK), dtype=f32)
+    if wl.variant == "deltaproduct":
+        # sub-step 0 takes the draws above; sub-steps 1 .. n-1 draw their own key, value and
+        # strength the same way: k [heads, n, d_k], v [heads, n, d_v], beta [heads, n]
+        ks, vs, bs = [k], [v], [beta]
+        for i in range(1, wl.n):
+            ks.append(_cast(wl, _unit_rows(_rng(wl, _TAG_SUB_K, wl.n * t + i).standard_normal((n, DK), dtype=f32)
+                                           .astype(np.float64))))
+            vs.append(_cast(wl, _rng(wl, _TAG_SUB_V, wl.n * t + i).standard_normal((n, DV), dtype=f32)))
+            bs.append(_rng(wl, _TAG_SUB_BETA, wl.n * t + i).random((n,), dtype=f32))
+        out["k"] = np.ascontiguousarray(np.stack(ks, axis=1))
+        out["v"] = np.ascontiguousarray(np.stack(vs, axis=1))
+        out["beta"] = np.ascontiguousarray(np.stack(bs, axis=1))
     return out
 
 
