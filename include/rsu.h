@@ -21,6 +21,7 @@
  *           contiguous, row-major and 16-byte aligned. The library never
  *           allocates, frees or synchronises; each call enqueues its kernels on
  *           `stream` (NULL = the null stream) and returns without waiting.
+ *           (The one exception is rsu_debug_metadata_counts, a checking call.)
  * Shapes.   B requests x H heads. d_k and d_v must both be 128. B*H == 0 is a
  *           valid empty batch: nothing is launched and 0 is returned.
  * Inputs.   q, k [B,H,d_k] and v [B,H,d_v] are fp32 or bf16 (dims->qkv_dtype).
@@ -56,7 +57,8 @@ enum rsu_status {
     RSU_E_DTYPE = -3,     /* qkv_dtype not RSU_F32 / RSU_BF16 */
     RSU_E_ALIGN = -4,     /* a pointer is not 16-byte aligned */
     RSU_E_RANGE = -5,     /* W / pos / C / L out of range */
-    RSU_E_HIP = -6        /* the kernel launch failed */
+    RSU_E_HIP = -6,       /* the kernel launch failed */
+    RSU_E_UNSUPPORTED = -7 /* the call needs a build option this library lacks */
 };
 
 typedef struct rsu_dims {
@@ -401,6 +403,20 @@ int rsu_copy_f32(const float *src, float *dst, int64_t n, rsu_stream_t stream);
  * 0 <= tiles <= 2^31 - 1; pointers 16-byte aligned; errors as above. */
 int rsu_read_f32(const float *src, float *col_sums, int64_t tiles, rsu_stream_t stream);
 int rsu_fill_f32(float *dst, float value, int64_t tiles, rsu_stream_t stream);
+
+/* Checking build only: the log's single-writer rule (DeltaLog, sec. 3.3 and the caption
+ * of Fig. 5: one writer per head commits K_log[L], Lam_log[L], lbar and L).
+ * A library built with RSU_CHECK_METADATA counts, per head (heads 0 .. 65535), every
+ * element of log metadata its log kernels write (all *_log_append, *_log_merge and
+ * *_log_step_slots entry points). This call waits for `stream`, copies the counters of
+ * heads 0 .. heads-1 to the HOST array counts [heads][8] (uint32; columns: K_log row
+ * elements, Lam elements, lbar elements, L, U_log row elements, then three unused), and
+ * clears every counter. One step writes, per head: an append 128 K_log, 128 U_log
+ * and 128 (KDA, RWKV6) or 1 (GDN) Lam and lbar elements; a merge only lbar (same count);
+ * a per-slot step also writes L once. Unlike the other calls it synchronises.
+ * Errors: RSU_E_NULL (counts), RSU_E_RANGE (heads outside 0 .. 65536),
+ * RSU_E_UNSUPPORTED (an ordinary build, which keeps no counters), RSU_E_HIP. */
+int rsu_debug_metadata_counts(uint32_t *counts, int64_t heads, rsu_stream_t stream);
 
 #ifdef __cplusplus
 }

@@ -41,7 +41,6 @@ class RsuError(RuntimeError):
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built; run `python -m recurrent_state_update_head_amd._build`")
 
-_lib = ctypes.CDLL(LIB_PATH)
 
 
 class _Dims(ctypes.Structure):
@@ -87,12 +86,22 @@ _SIGS = {
     "rsu_copy_f32": [_P, _P, ctypes.c_int64, _P],
     "rsu_read_f32": [_P, _P, ctypes.c_int64, _P],
     "rsu_fill_f32": [_P, ctypes.c_float, ctypes.c_int64, _P],
+    "rsu_debug_metadata_counts": [_P, ctypes.c_int64, _P],
 }
-for _name, _args in _SIGS.items():
-    getattr(_lib, _name).argtypes = _args
-    getattr(_lib, _name).restype = ctypes.c_int
-_lib.rsu_abi_version.restype = ctypes.c_int
-_lib.rsu_last_error.restype = ctypes.c_char_p
+
+
+def _open(path: str) -> ctypes.CDLL:
+    """Load one build of the library and declare its entry points' signatures."""
+    lib = ctypes.CDLL(path)
+    for name, args in _SIGS.items():
+        getattr(lib, name).argtypes = args
+        getattr(lib, name).restype = ctypes.c_int
+    lib.rsu_abi_version.restype = ctypes.c_int
+    lib.rsu_last_error.restype = ctypes.c_char_p
+    return lib
+
+
+_lib = _open(LIB_PATH)
 
 
 def abi_version() -> int:
@@ -581,6 +590,17 @@ def fill_f32(dst: torch.Tensor, value: float):
         raise ValueError(f"dst must be [..., {D}, {D}], got {tuple(dst.shape)}")
     _need(dst, "dst", torch.float32, dst.shape)
     _call("rsu_fill_f32", _ptr(dst), ctypes.c_float(value), dst.numel() // (D * D), _stream())
+
+
+def debug_metadata_counts(heads: int):
+    """Per-head metadata write counts of the log kernels since the last read (the checking
+    build only; the ordinary build raises RsuError): a numpy uint32 array [heads, 8] with
+    columns K_log elements, Lam elements, lbar elements, L, U_log elements. Waits for
+    torch's current stream and clears the counters."""
+    import numpy as np
+    out = np.zeros((heads, 8), dtype=np.uint32)
+    _call("rsu_debug_metadata_counts", out.ctypes.data_as(ctypes.c_void_p), heads, _stream())
+    return out
 
 
 def raw_library() -> ctypes.CDLL:

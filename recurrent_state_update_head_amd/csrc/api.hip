@@ -1,6 +1,6 @@
 // api.hip -- the extern "C" entry points declared in include/rsu.h: argument
 // validation, error reporting, kernel dispatch. Nothing here allocates memory
-// or synchronises the device.
+// or synchronises the device (except the checking build's counter read-back).
 #include <stdarg.h>
 #include <stdio.h>
 
@@ -505,6 +505,19 @@ int rsu_fill_f32(float* dst, float value, int64_t tiles, rsu_stream_t stream) {
     if (tiles == 0) return RSU_OK;
     if (int rc = check_ptrs({{dst, "dst"}}, "rsu_fill_f32")) return rc;
     return launched(rsu::launch_write_probe(dst, value, static_cast<int>(tiles), stream), "rsu_fill_f32");
+}
+
+int rsu_debug_metadata_counts(uint32_t* counts, int64_t heads, rsu_stream_t stream) {
+    const char* fn = "rsu_debug_metadata_counts";
+    g_err[0] = '\0';
+    if (!counts) return fail(RSU_E_NULL, "%s: counts is NULL", fn);
+    if (heads < 0 || heads > rsu::kMetaCheckHeads)
+        return fail(RSU_E_RANGE, "%s: heads=%lld outside 0..%d", fn, (long long)heads, rsu::kMetaCheckHeads);
+    const hipError_t e = rsu::read_metadata_counts(counts, heads, stream);
+    if (e == hipErrorNotSupported)
+        return fail(RSU_E_UNSUPPORTED, "%s: this library was built without RSU_CHECK_METADATA", fn);
+    if (e != hipSuccess) return fail(RSU_E_HIP, "%s: %s", fn, hipGetErrorString(e));
+    return RSU_OK;
 }
 
 int stepq_pack(const rsu_dims* dims, const float* S, const float* omega, void* Z, void* R, void* C,

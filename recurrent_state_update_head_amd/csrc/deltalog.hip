@@ -34,6 +34,30 @@ namespace rsu {
 // first chunk is issued before the base tile, so short logs cost one round trip.
 constexpr int kChunk = 16;
 
+// Metadata write counts (DeltaLog sec. 3.3: one writer per head commits K_log[L],
+// Lam_log[L], lbar and L). A build with RSU_CHECK_METADATA defined adds one to a per-head
+// counter for every element of those it writes (and of U_log[L]), so a test can check
+// that each is written exactly once per step; the ordinary build counts nothing.
+#ifdef RSU_CHECK_METADATA
+__device__ unsigned meta_writes[kMetaCheckHeads * kMetaKinds];
+__device__ __forceinline__ void meta_count(int h, int kind, unsigned n) {
+    if (h < kMetaCheckHeads) atomicAdd(&meta_writes[h * kMetaKinds + kind], n);
+}
+
+hipError_t read_metadata_counts(unsigned* host, int64_t heads, hipStream_t stream) {
+    void* dev = nullptr;
+    if (hipError_t e = hipGetSymbolAddress(&dev, HIP_SYMBOL(meta_writes))) return e;
+    if (hipError_t e = hipStreamSynchronize(stream)) return e;
+    const size_t bytes = sizeof(unsigned) * kMetaKinds * static_cast<size_t>(heads);
+    if (hipError_t e = hipMemcpy(host, dev, bytes, hipMemcpyDeviceToHost)) return e;
+    return hipMemset(dev, 0, sizeof(unsigned) * kMetaKinds * kMetaCheckHeads);
+}
+#else
+__device__ __forceinline__ void meta_count(int, int, unsigned) {}
+
+hipError_t read_metadata_counts(unsigned*, int64_t, hipStream_t) { return hipErrorNotSupported; }
+#endif
+
 // Dynamic LDS of a step, in 32-bit words, for n staged entries (n = L for the
 // batch-uniform calls, n = C for the per-slot call): Ek[n][128] (K_m, turned in
 // place into exp(lbar' - Lam_m) K_m), Us[n][128] (U_m), Ls[n][128] (KDA) or Ls[n]
@@ -86,7 +110,10 @@ __global__ __launch_bounds__(kThreads) void log_step_kernel(
         L = L_head;
         if (kMode == kSlotAppend && L == C) return;  // merged by the second pass
         if (kMode == kSlotMerge && L < C) {          // appended by the first pass
-            if (tid == 0) Lslot[h] = L + 1;
+            if (tid == 0) {
+                Lslot[h] = L + 1;
+                meta_count(h, kMetaL, 1);
+            }
             return;
         }
     }
@@ -181,20 +208,25 @@ __global__ __launch_bounds__(kThreads) void log_step_kernel(
     // metadata: one writer per element (all reads of lbar / Lam / Lslot are done)
     if (first) {
         if (merge) {
-            if (kPerKey) lbar[vec_off + r] = 0.f;
-            else if (r == 0) lbar[h] = 0.f;
+            if (kPerKey || r == 0) {
+                lbar[kPerKey ? vec_off + r : h] = 0.f;
+                meta_count(h, kMetaLbar, 1);
+            }
         } else {
             const size_t ent = static_cast<size_t>(h) * C + L;
             store_in(Klog, ent * kD + r, kr);
-            if (kPerKey) {
-                Lam[ent * kD + r] = lb_new;
-                lbar[vec_off + r] = lb_new;
-            } else if (r == 0) {
-                Lam[ent] = lb_new;
-                lbar[h] = lb_new;
+            meta_count(h, kMetaK, 1);
+            if (kPerKey || r == 0) {
+                Lam[kPerKey ? ent * kD + r : ent] = lb_new;
+                lbar[kPerKey ? vec_off + r : h] = lb_new;
+                meta_count(h, kMetaLam, 1);
+                meta_count(h, kMetaLbar, 1);
             }
         }
-        if (kMode == kSlotMerge && tid == 0) Lslot[h] = 0;
+        if (kMode == kSlotMerge && tid == 0) {
+            Lslot[h] = 0;
+            meta_count(h, kMetaL, 1);
+        }
     }
 
     // ---- sweep of the base for both read vectors, plus the log entries
@@ -217,7 +249,10 @@ __global__ __launch_bounds__(kThreads) void log_step_kernel(
     const f32x4 b = kDelta ? bt * (vv - p1) : vv;
     if (ro == 0) {
         *reinterpret_cast<f32x4*>(y + vec_off + col) = p2 + b * kq;
-        if (!merge) store4_in(Ulog, ent0 + static_cast<size_t>(L) * kD + col, b);
+        if (!merge) {
+            store4_in(Ulog, ent0 + static_cast<size_t>(L) * kD + col, b);
+            meta_count(h, kMetaU, 4);
+        }
     }
     if (!merge) return;
 

@@ -47,6 +47,13 @@ hipError_t launch_rwkv7(const StepArgs& a, const void* kappa, const float* erase
 // DeltaProduct with n sub-steps (1 <= n <= 4): k, v [heads, n, 128] in the input dtype, gate = alpha
 // [heads], beta [heads, n]
 hipError_t launch_deltaproduct(const StepArgs& a, int n, bool bf16, hipStream_t stream);
+// Per-head metadata write counters of the log kernels, kept only by a build with
+// RSU_CHECK_METADATA defined (kinds: K_log row, Lam entry, lbar, L, U_log row elements).
+constexpr int kMetaCheckHeads = 1 << 16, kMetaKinds = 8;
+enum MetaKind { kMetaK = 0, kMetaLam = 1, kMetaLbar = 2, kMetaL = 3, kMetaU = 4 };
+// Copies the counters of the first `heads` heads to host memory after the stream's work
+// has finished, then clears all counters; hipErrorNotSupported in the ordinary build.
+hipError_t read_metadata_counts(unsigned* host, int64_t heads, hipStream_t stream);
 hipError_t launch_copy(const float* src, float* dst, int64_t n, hipStream_t stream);
 hipError_t launch_read_probe(const float* src, float* sums, int tiles, hipStream_t stream);
 hipError_t launch_write_probe(float* dst, float value, int tiles, hipStream_t stream);

@@ -11,7 +11,8 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "rsu.h")
 LIB = os.path.join(ROOT, "recurrent_state_update_head_amd", "librsu.so")
 
-RSU_OK, E_NULL, E_DIMS, E_DTYPE, E_ALIGN, E_RANGE = 0, -1, -2, -3, -4, -5
+RSU_OK, E_NULL, E_DIMS, E_DTYPE, E_ALIGN, E_RANGE, E_UNSUPPORTED = 0, -1, -2, -3, -4, -5, -7
+CHECK_LIB = os.path.join(ROOT, "recurrent_state_update_head_amd", "librsu_check.so")
 
 
 @pytest.fixture(scope="module")
@@ -297,3 +298,24 @@ def test_rwkv7_validation(lib):
     assert f(ctypes.byref(d), GOOD, GOOD, GOOD, GOOD, GOOD, ODD, GOOD, GOOD, None) == E_ALIGN
     assert f(ctypes.byref(Dims(2, 3, 128, 128, 5)), *([GOOD] * 8), None) == E_DTYPE
     assert f(ctypes.byref(Dims(0, 3, 128, 128, 1)), *([None] * 8), None) == RSU_OK
+
+
+def test_checking_build_exports_the_same_symbols(lib):
+    if not os.path.exists(CHECK_LIB):
+        import __graft_entry__
+        __graft_entry__.build()
+    chk = ctypes.CDLL(CHECK_LIB)
+    for n in declared_functions():
+        assert hasattr(chk, n), n
+
+
+def test_metadata_counts_need_the_checking_build(lib):
+    f = lib.rsu_debug_metadata_counts
+    f.restype = ctypes.c_int
+    f.argtypes = [P, ctypes.c_int64, P]
+    buf = (ctypes.c_uint32 * 32)()
+    assert f(None, 4, None) == E_NULL
+    assert f(ctypes.cast(buf, P), -1, None) == E_RANGE
+    assert f(ctypes.cast(buf, P), 65537, None) == E_RANGE
+    assert f(ctypes.cast(buf, P), 4, None) == E_UNSUPPORTED
+    assert "RSU_CHECK_METADATA" in _last(lib)
