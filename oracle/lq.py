@@ -31,6 +31,12 @@ Readings taken where the pages are silent (stated once here, used everywhere):
   * at 4 bits (the page uses r = 8 tokens there) the same recipe with codes in [-7, 7]
     and dequant(Z, B)_ij = Z_ij B_j / 7 (the /127 convention at 4 bits); on the device two
     codes share a byte, the even column in the low nibble.
+  * at 6 bits (sec. 4.1 evaluates a 6-bit group but gives a token count only for 4 bits,
+    so the default r = 4 holds) codes in [-31, 31] and dequant Z B / 31. The page prints
+    no packing; the device stores a row of 128 codes in 96 bytes: bytes 0..63 hold the
+    high parts z >> 2 (floor division by 4, a 4-bit two's complement in [-8, 7]) in the
+    4-bit layout, bytes 64..95 the low parts z & 3, four per byte, column 4b + i in bits
+    2i .. 2i+1 of byte 64 + b (pack6 / unpack6 below).
 """
 from __future__ import annotations
 
@@ -38,11 +44,11 @@ import numpy as np
 
 R_TOKENS = 4
 C_FLOOR = 1e-6
-QMAX8, QMAX4 = 127, 7
+QMAX8, QMAX6, QMAX4 = 127, 31, 7
 
 
 def qmax_of(bits: int) -> int:
-    """Largest code of the symmetric format: 127 at 8 bits, 7 at 4 bits."""
+    """Largest code of the symmetric format: 127 at 8 bits, 31 at 6 bits, 7 at 4 bits."""
     return (1 << (bits - 1)) - 1
 
 
@@ -139,3 +145,26 @@ def unpack_nibbles(P: np.ndarray) -> np.ndarray:
     out = np.empty(p.shape[:-1] + (2 * p.shape[-1],), dtype=np.int8)
     out[..., 0::2], out[..., 1::2] = lo, hi
     return out
+
+
+def pack6(Z: np.ndarray) -> np.ndarray:
+    """6-bit codes [..., d] in [-31, 31] -> bytes [..., 3 d / 4]: the high parts z >> 2 as
+    nibbles (pack_nibbles), then the low parts z & 3, four per byte, column 4b + i in bits
+    2i .. 2i+1 of byte b of the second part."""
+    z = np.asarray(Z, dtype=np.int64)
+    hi = pack_nibbles(z >> 2)
+    lo = z & 3
+    lo_bytes = lo[..., 0::4] | (lo[..., 1::4] << 2) | (lo[..., 2::4] << 4) | (lo[..., 3::4] << 6)
+    return np.concatenate([hi, lo_bytes.astype(np.uint8)], axis=-1)
+
+
+def unpack6(P: np.ndarray) -> np.ndarray:
+    """Inverse of pack6."""
+    p = np.asarray(P, dtype=np.int64)
+    d = p.shape[-1] * 4 // 3
+    hi = unpack_nibbles(p[..., :d // 2]).astype(np.int64)
+    lb = p[..., d // 2:]
+    lo = np.empty(p.shape[:-1] + (d,), dtype=np.int64)
+    for i in range(4):
+        lo[..., i::4] = (lb >> (2 * i)) & 3
+    return (4 * hi + lo).astype(np.int8)

@@ -296,3 +296,95 @@ def test_eq10_readout_at_4_bits_with_8_tokens_equals_dense_decoding():
         u = b[0] * (v[0] - read(k[0]))
         np.testing.assert_allclose(read(q[0]) + u * (k[0] @ q[0]), y_dense, rtol=0, atol=1e-11)
         recs.append((k[0], u, g[0]))
+
+
+# ---------------------------------------------------------------- 6 bits, r = 4 tokens
+# (LeapQuant sec. 4.1 and Table 1 evaluate a 6-bit group; codes in [-31, 31], /31; the
+# token count stays at the default r = 4, since only 4 bits is given r = 8)
+
+def test_6bit_representation_error_is_bounded_by_half_a_step():
+    S = _gapped(noise=0.05)
+    out = lq.boundary(S, lq.walsh_start(), 2, qmax=lq.QMAX6)
+    assert out["Z"].min() >= -31 and out["Z"].max() <= 31
+    assert np.abs(out["Z"]).max() == 31
+    S0 = lq.represent(out["Z"], out["B"], out["c"], out["K16"], out["U16"], qmax=lq.QMAX6)
+    step = out["c"][:, None] * out["B"][None, :] / 31.0
+    assert np.all(np.abs(S0 - S) <= 0.5 * step * (1 + 1e-6) + 1e-15)
+    # finer than the 4-bit grid on the same state, coarser than the 8-bit one
+    err = {b: np.linalg.norm(lq.represent(*(lambda o: (o["Z"], o["B"], o["c"], o["K16"], o["U16"]))(
+        lq.boundary(S, lq.walsh_start(), 2, qmax=lq.qmax_of(b))), qmax=lq.qmax_of(b)) - S) for b in (4, 6, 8)}
+    assert err[8] < err[6] < err[4]
+
+
+def test_6bit_without_tokens_is_a_per_column_int6_quantizer():
+    """r = 0: codes rne(X_ij * 31 / B_j) on the smoothed state, written out column by column."""
+    S = RNG.standard_normal((128, 128)) * 0.02
+    zero = np.zeros((128, 0))
+    Z, Bq, c, _ = lq.smooth_quantize(S, zero, zero, qmax=lq.QMAX6)
+    X = S / c[:, None]
+    for j in range(0, 128, 3):
+        B = float(np.float32(np.abs(X[:, j]).max()))
+        assert Bq[j] == B
+        for i in range(0, 128, 5):
+            x = X[i, j] * 31.0 / B
+            f = np.floor(x)
+            r = f + 1 if (x - f > 0.5 or (x - f == 0.5 and f % 2 == 1)) else f
+            assert Z[i, j] == max(-31, min(31, int(r)))
+
+
+def test_6bit_ties_round_to_even():
+    """c = 1 by construction (row mean |R| = 1); column 0 on the half grid with absmax 31."""
+    S = np.zeros((128, 128))
+    t = np.concatenate([[31.0], ((np.arange(127) % 62) - 31) + 0.5])
+    S[:, 0] = t
+    S[:, 1] = 128.0 - np.abs(t)
+    zero = np.zeros((128, 0))
+    Z, B, c, w = lq.smooth_quantize(S, zero, zero, qmax=lq.QMAX6)
+    np.testing.assert_array_equal(c, 1.0)
+    assert B[0] == 31.0
+    np.testing.assert_array_equal(w[:, 0], t)
+    halves = t[1:]
+    even = np.where(np.floor(halves) % 2 == 0, np.floor(halves), np.ceil(halves))
+    np.testing.assert_array_equal(Z[1:, 0], even.astype(np.int8))
+
+
+def test_6bit_packing_layout_and_round_trip():
+    Z = np.zeros((1, 128), dtype=np.int8)
+    Z[0, :4] = [-31, 31, -1, 5]   # = 4 (-8) + 1, 4 (7) + 3, 4 (-1) + 3, 4 (1) + 1
+    P = lq.pack6(Z)
+    assert P.shape == (1, 96) and P.dtype == np.uint8
+    # high parts as nibbles (column 0 low), then the low parts four per byte (column 0 lowest)
+    np.testing.assert_array_equal(P[0, :2], [0x78, 0x1F])
+    assert P[0, 64] == 0b01_11_11_01
+    assert not P[0, 2:64].any() and not P[0, 65:].any()
+    np.testing.assert_array_equal(lq.unpack6(P), Z)
+    R = RNG.integers(-31, 32, size=(5, 128)).astype(np.int8)
+    np.testing.assert_array_equal(lq.unpack6(lq.pack6(R)), R)
+
+
+def test_eq10_readout_at_6_bits_equals_dense_decoding():
+    d, W = 128, 4
+    S = _gapped(noise=0.05)
+    rep = lq.boundary(S, lq.walsh_start(), 1, qmax=lq.QMAX6)
+    S0 = lq.represent(rep["Z"], rep["B"], rep["c"], rep["K16"], rep["U16"], qmax=lq.QMAX6)
+    Sd = S0[None].copy()
+    recs = []
+    for _ in range(W):
+        q = RNG.standard_normal((1, d))
+        k = RNG.standard_normal((1, d))
+        k /= np.linalg.norm(k)
+        v = RNG.standard_normal((1, d))
+        g = np.array([RNG.uniform(0.9, 0.999)])
+        b = np.array([RNG.uniform(0.0, 1.0)])
+        y_dense = oracle.dense_step(Sd, q, k, v, g, b)[0]
+        gam_all = np.prod([r[2] for r in recs]) * g[0]
+
+        def read(x):
+            out = (rep["B"] / 31.0) * (rep["Z"].astype(np.float64).T @ (rep["c"] * gam_all * x))
+            out += rep["U16"] @ (rep["K16"].T @ (gam_all * x))
+            for j, (kj, uj, _) in enumerate(recs):
+                out += uj * (kj @ (np.prod([r[2] for r in recs[j + 1:]]) * g[0] * x))
+            return out
+        u = b[0] * (v[0] - read(k[0]))
+        np.testing.assert_allclose(read(q[0]) + u * (k[0] @ q[0]), y_dense, rtol=0, atol=1e-11)
+        recs.append((k[0], u, g[0]))

@@ -51,7 +51,7 @@ class Workload:
     W: int = 0            # window length of the int8 path
     M: int = 0            # merge interval of the base+log path (capacity C = M - 1)
     outliers: bool = False
-    bits: int = 8         # code width of the LeapQuant window format (8, or 4 with 8 tokens)
+    bits: int = 8         # code width of the LeapQuant window format (8, 6, or 4 with 8 tokens)
     n: int = 1            # DeltaProduct: delta-rule sub-steps per token
 
     @property
@@ -82,6 +82,9 @@ WORKLOADS = {
     # LeapQuant's format at 4 bits with 8 tokens on the int8 workload's inputs (same seed as 4)
     12: Workload(4, "gdn_lq4_window_b256_h48_w16", "gdn", "lq_window", 256, 48, 256, "bf16", 0.90, 0.999,
                  W=16, outliers=True, bits=4),
+    # LeapQuant's format at 6 bits (4 tokens) on the int8 workload's inputs (same seed as 4)
+    16: Workload(4, "gdn_lq6_window_b256_h48_w16", "gdn", "lq_window", 256, 48, 256, "bf16", 0.90, 0.999,
+                 W=16, outliers=True, bits=6),
     # LeapQuant's format with KDA gates on the KDA workload's shape (same outliers as 4)
     9: Workload(9, "kda_lq_window_b128_h32_w16", "kda", "lq_window", 128, 32, 256, "bf16", 0.80, 1.0,
                 W=16, outliers=True),
