@@ -48,7 +48,7 @@ KERNEL_SOURCES = {
 
 WORKLOAD_BY_FLAG = {"gdn": 2, "gdn_small": 1, "kda": 3, "q8": 4, "log": 5, "lq": 6, "rwkv6": 7,
                     "rwkv6_log": 8, "kda_lq": 9, "rwkv7": 10, "rwkv7_q8": 11, "lq4": 12,
-                    "stepq": 13, "dp": 14, "dp_q8": 15}
+                    "stepq": 13, "dp": 14, "dp_q8": 15, "lq6": 16}
 LQ_TOKENS = 4
 
 
@@ -433,19 +433,21 @@ def run_gpu(w: wl.Workload, steps: int, warmup: int, slots: bool = False, n_iter
     elif w.path == "lq_window":
         W = w.W
         four = w.bits == 4
-        Z = (torch.empty(B, H, 128, 64, device=dev, dtype=torch.uint8) if four else
+        Z = (torch.empty(B, H, 128, 128 * w.bits // 8, device=dev, dtype=torch.uint8) if w.bits != 8 else
              torch.empty(B, H, 128, 128, device=dev, dtype=torch.int8))
         Bc = torch.empty(B, H, 128, device=dev)
         Cs = torch.empty(B, H, 128, device=dev)
         Kc = torch.empty(B, H, 8 if four else LQ_TOKENS, 128, device=dev, dtype=torch.float16)
         Uc = torch.empty_like(Kc)
-        quant = rsu.gdn_lq4_quantize if four else (rsu.kda_lq_quantize if kda else rsu.gdn_lq_quantize)
+        quant = {4: rsu.gdn_lq4_quantize, 6: rsu.gdn_lq6_quantize}.get(
+            w.bits, rsu.kda_lq_quantize if kda else rsu.gdn_lq_quantize)
         quant(S0, 8, Z, Bc, Cs, Kc, Uc)
         del S0
         Kb = torch.zeros(B, H, W, 128, device=dev, dtype=x["q"].dtype)
         Ub = torch.zeros(B, H, W, 128, device=dev)
         Gb = torch.zeros((B, H, W, 128) if kda else (B, H, W), device=dev)
-        win = rsu.gdn_lq4_window if four else (rsu.kda_lq_window if kda else rsu.gdn_lq_window)
+        win = {4: rsu.gdn_lq4_window, 6: rsu.gdn_lq6_window}.get(
+            w.bits, rsu.kda_lq_window if kda else rsu.gdn_lq_window)
 
         def step():
             t = state["t"]
@@ -792,6 +794,7 @@ def main():
         "config": {"workload": w.name, "B": w.B, "H": w.H, "dk": 128, "dv": 128,
                    "qkv": w.qkv, "state": ("int4+fp16 row and column factors" if w.path == "stepq" else
                                            "int4+f32 scales+8 fp16 token pairs" if w.bits == 4 else
+                                           "int6+f32 scales+4 fp16 token pairs" if w.bits == 6 else
                                             {"q8_window": "int8+f32 scales",
                                              "lq_window": "int8+f32 scales+4 fp16 token pairs"}.get(w.path, "f32")),
                    "W": w.W or None, "M": w.M or None, "gates": w.variant,

@@ -207,6 +207,20 @@ int gdn_lq4_window(const rsu_dims *dims, int W, int pos, int n_iter, void *Z,
                    float *col_absmax, float *row_smooth, void *Kc, void *Uc, void *Kbuf,
                    float *Ubuf, float *Gbuf, const void *q, const void *k, const void *v,
                    const float *alpha, const float *beta, float *y, rsu_stream_t stream);
+/* The same format at 6 bits (LeapQuant sec. 4.1 and Table 1 evaluate a 6-bit group; the
+ * token count stays r = 4), GDN: codes in [-31, 31] with dequant Z_ij * col_absmax_j / 31.
+ * Row i of a head's payload is 96 bytes: bytes 0..63 hold the high parts z >> 2 (floor
+ * division, 4-bit two's complement) two per byte as in gdn_lq4_window, bytes 64..95 the
+ * low parts z & 3 four per byte, column 4b + m in bits 2m .. 2m+1 of byte 64 + b:
+ *   Z [B,H,d_k,96] bytes, Kc, Uc [B,H,4,d] fp16; col_absmax, row_smooth as above.
+ * The fit starts from the first 4 Walsh columns; other rules as for gdn_lq_window. */
+int gdn_lq6_quantize(const rsu_dims *dims, const float *S, int n_iter, void *Z,
+                     float *col_absmax, float *row_smooth, void *Kc, void *Uc,
+                     rsu_stream_t stream);
+int gdn_lq6_window(const rsu_dims *dims, int W, int pos, int n_iter, void *Z,
+                   float *col_absmax, float *row_smooth, void *Kc, void *Uc, void *Kbuf,
+                   float *Ubuf, float *Gbuf, const void *q, const void *k, const void *v,
+                   const float *alpha, const float *beta, float *y, rsu_stream_t stream);
 int kda_lq_quantize(const rsu_dims *dims, const float *S, int n_iter, int8_t *Z,
                     float *col_absmax, float *row_smooth, void *Kc, void *Uc,
                     rsu_stream_t stream);

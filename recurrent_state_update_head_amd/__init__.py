@@ -15,7 +15,8 @@ Shapes (B requests, H heads, d = 128):
   Klog [B,H,C,d] (q dtype), Ulog [B,H,C,d] fp32, Lam [B,H,C] or [B,H,C,d] fp32,
   lbar [B,H] or [B,H,d] fp32, per-slot live lengths L [B,H] int32
   LeapQuant format: Z [B,H,d,d] int8, col_absmax [B,H,d] fp32, row_smooth [B,H,d] fp32,
-  Kc, Uc [B,H,4,d] fp16 (4 bits: Z [B,H,d,d/2] uint8 nibbles, Kc, Uc [B,H,8,d] fp16)
+  Kc, Uc [B,H,4,d] fp16 (4 bits: Z [B,H,d,d/2] uint8 nibbles, Kc, Uc [B,H,8,d] fp16;
+  6 bits: Z [B,H,d,3d/4] uint8, high-part nibbles then low 2-bit parts, Kc, Uc [B,H,4,d])
   STEPQuant packed state: Z [B,H,d,d/2] uint8 nibbles, R, C [B,H,d] fp16, omega [B,H,d] fp32,
   u [B,H,d] fp32 (the readout's correction, consumed by the repack)
   DeltaProduct (n sub-steps per token): k, v [B,H,n,d], alpha [B,H], beta [B,H,n] fp32;
@@ -65,6 +66,8 @@ _SIGS = {
     "kda_lq_quantize": [_DP, _P, _I, _P, _P, _P, _P, _P, _P],
     "gdn_lq4_quantize": [_DP, _P, _I, _P, _P, _P, _P, _P, _P],
     "gdn_lq4_window": [_DP, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
+    "gdn_lq6_quantize": [_DP, _P, _I, _P, _P, _P, _P, _P, _P],
+    "gdn_lq6_window": [_DP, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
     "kda_lq_window": [_DP, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
     "gdn_log_step_slots": [_DP, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
     "kda_log_step_slots": [_DP, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
@@ -408,24 +411,24 @@ def rwkv6_log_step_slots(C, L, Sbase, lbar, Klog, Ulog, Lam, q, k, v, w, y):
     return _rwkv6_log("rwkv6_log_step_slots", C, L, Sbase, lbar, Klog, Ulog, Lam, q, k, v, w, y)
 
 
-def _lq_state(B, H, Z, col_absmax, row_smooth, Kc, Uc, four_bit=False):
-    if four_bit:
-        _need(Z, "Z", torch.uint8, (B, H, D, D // 2))
-    else:
+def _lq_state(B, H, Z, col_absmax, row_smooth, Kc, Uc, bits=8):
+    if bits == 8:
         _need(Z, "Z", torch.int8, (B, H, D, D))
+    else:
+        _need(Z, "Z", torch.uint8, (B, H, D, D * bits // 8))
     _need(col_absmax, "col_absmax", torch.float32, (B, H, D))
     _need(row_smooth, "row_smooth", torch.float32, (B, H, D))
-    r = 8 if four_bit else 4
+    r = 8 if bits == 4 else 4
     _need(Kc, "Kc", torch.float16, (B, H, r, D))
     _need(Uc, "Uc", torch.float16, (B, H, r, D))
 
 
-def _lq_quantize(name, S, n_iter, Z, col_absmax, row_smooth, Kc, Uc, four_bit=False):
+def _lq_quantize(name, S, n_iter, Z, col_absmax, row_smooth, Kc, Uc, bits=8):
     if S.dim() != 4:
         raise ValueError("S must be [B, H, 128, 128]")
     B, H = S.shape[0], S.shape[1]
     _need(S, "S", torch.float32, (B, H, D, D))
-    _lq_state(B, H, Z, col_absmax, row_smooth, Kc, Uc, four_bit)
+    _lq_state(B, H, Z, col_absmax, row_smooth, Kc, Uc, bits)
     dims = _Dims(B, H, D, D, RSU_F32)
     _call(name, ctypes.byref(dims), _ptr(S), int(n_iter), _ptr(Z), _ptr(col_absmax),
           _ptr(row_smooth), _ptr(Kc), _ptr(Uc), _stream())
@@ -443,10 +446,10 @@ def kda_lq_quantize(S, n_iter, Z, col_absmax, row_smooth, Kc, Uc):
 
 
 def _lq_window(name, per_key, W, pos, n_iter, Z, col_absmax, row_smooth, Kc, Uc, Kbuf, Ubuf, Gbuf, q, k, v,
-               gate, beta, y, four_bit=False):
+               gate, beta, y, bits=8):
     dims = _dims(q, k, v)
     B, H = dims.B, dims.H
-    _lq_state(B, H, Z, col_absmax, row_smooth, Kc, Uc, four_bit)
+    _lq_state(B, H, Z, col_absmax, row_smooth, Kc, Uc, bits)
     _need(Kbuf, "Kbuf", q.dtype, (B, H, W, D))
     _need(Ubuf, "Ubuf", torch.float32, (B, H, W, D))
     _need(Gbuf, "Gbuf", torch.float32, (B, H, W, D) if per_key else (B, H, W))
@@ -467,13 +470,26 @@ def gdn_lq_window(W, pos, n_iter, Z, col_absmax, row_smooth, Kc, Uc, Kbuf, Ubuf,
 def gdn_lq4_quantize(S, n_iter, Z, col_absmax, row_smooth, Kc, Uc):
     """Convert fp32 states into LeapQuant's format at 4 bits with 8 tokens (Z: uint8
     [B, H, 128, 64] packed nibbles; Kc, Uc: fp16 [B, H, 8, 128])."""
-    _lq_quantize("gdn_lq4_quantize", S, n_iter, Z, col_absmax, row_smooth, Kc, Uc, four_bit=True)
+    _lq_quantize("gdn_lq4_quantize", S, n_iter, Z, col_absmax, row_smooth, Kc, Uc, bits=4)
 
 
 def gdn_lq4_window(W, pos, n_iter, Z, col_absmax, row_smooth, Kc, Uc, Kbuf, Ubuf, Gbuf, q, k, v, alpha, beta, y):
     """One decode step in the 4-bit, 8-token format (eq. 10; at pos = W - 1 the refit)."""
     return _lq_window("gdn_lq4_window", False, W, pos, n_iter, Z, col_absmax, row_smooth, Kc, Uc, Kbuf, Ubuf,
-                      Gbuf, q, k, v, alpha, beta, y, four_bit=True)
+                      Gbuf, q, k, v, alpha, beta, y, bits=4)
+
+
+def gdn_lq6_quantize(S, n_iter, Z, col_absmax, row_smooth, Kc, Uc):
+    """Convert fp32 states into LeapQuant's format at 6 bits with 4 tokens (Z: uint8
+    [B, H, 128, 96], per row the high parts as nibbles then the low 2-bit parts; Kc, Uc:
+    fp16 [B, H, 4, 128])."""
+    _lq_quantize("gdn_lq6_quantize", S, n_iter, Z, col_absmax, row_smooth, Kc, Uc, bits=6)
+
+
+def gdn_lq6_window(W, pos, n_iter, Z, col_absmax, row_smooth, Kc, Uc, Kbuf, Ubuf, Gbuf, q, k, v, alpha, beta, y):
+    """One decode step in the 6-bit, 4-token format (eq. 10; at pos = W - 1 the refit)."""
+    return _lq_window("gdn_lq6_window", False, W, pos, n_iter, Z, col_absmax, row_smooth, Kc, Uc, Kbuf, Ubuf,
+                      Gbuf, q, k, v, alpha, beta, y, bits=6)
 
 
 def kda_lq_window(W, pos, n_iter, Z, col_absmax, row_smooth, Kc, Uc, Kbuf, Ubuf, Gbuf, q, k, v, d, beta, y):

@@ -165,8 +165,8 @@ int lq_quantize_common(const char* fn, const rsu_dims* dims, const float* S, int
     return launched(rsu::launch_lq_quantize(heads, S, n_iter, Z, col_absmax, row_smooth, Kc, Uc, stream), fn);
 }
 
-int lq4_quantize_common(const char* fn, const rsu_dims* dims, const float* S, int n_iter, void* Z, float* col_absmax,
-                        float* row_smooth, void* Kc, void* Uc, rsu_stream_t stream) {
+int lq_low_quantize_common(const char* fn, int bits, const rsu_dims* dims, const float* S, int n_iter, void* Z,
+                           float* col_absmax, float* row_smooth, void* Kc, void* Uc, rsu_stream_t stream) {
     int heads = 0;
     if (int rc = check_dims(dims, &heads, fn)) return rc;
     if (n_iter < 0 || n_iter > 64) return fail(RSU_E_RANGE, "%s: n_iter=%d outside [0, 64]", fn, n_iter);
@@ -174,13 +174,14 @@ int lq4_quantize_common(const char* fn, const rsu_dims* dims, const float* S, in
     if (int rc = check_ptrs({{S, "S"}, {Z, "Z"}, {col_absmax, "col_absmax"}, {row_smooth, "row_smooth"},
                              {Kc, "Kc"}, {Uc, "Uc"}}, fn))
         return rc;
-    return launched(rsu::launch_lq4_quantize(heads, S, n_iter, Z, col_absmax, row_smooth, Kc, Uc, stream), fn);
+    return launched(rsu::launch_lq_low_quantize(bits, heads, S, n_iter, Z, col_absmax, row_smooth, Kc, Uc, stream),
+                    fn);
 }
 
 int lq_window_common(const char* fn, Kind m, const rsu_dims* dims, int W, int pos, int n_iter, int8_t* Z,
                      float* col_absmax, float* row_smooth, void* Kc, void* Uc, void* Kbuf, float* Ubuf,
                      float* Gbuf, const void* q, const void* k, const void* v, const float* gate,
-                     const float* beta, float* y, rsu_stream_t stream, bool four_bit = false) {
+                     const float* beta, float* y, rsu_stream_t stream, int bits = 8) {
     int heads = 0;
     if (int rc = check_dims(dims, &heads, fn)) return rc;
     if (dims->qkv_dtype != RSU_BF16)
@@ -206,7 +207,7 @@ int lq_window_common(const char* fn, Kind m, const rsu_dims* dims, int W, int po
     w.Ubuf = Ubuf;
     w.Gbuf = Gbuf;
     const rsu::StepArgs a = step_args(heads, nullptr, q, k, v, gate, beta, y);
-    if (four_bit) return launched(rsu::launch_lq4_window(a, w, stream), fn);
+    if (bits != 8) return launched(rsu::launch_lq_low_window(bits, a, w, stream), fn);
     return launched(rsu::launch_lq_window(a, w, m == Kind::kda, stream), fn);
 }
 
@@ -335,14 +336,26 @@ int kda_lq_quantize(const rsu_dims* dims, const float* S, int n_iter, int8_t* Z,
 
 int gdn_lq4_quantize(const rsu_dims* dims, const float* S, int n_iter, void* Z, float* col_absmax, float* row_smooth,
                      void* Kc, void* Uc, rsu_stream_t stream) {
-    return lq4_quantize_common("gdn_lq4_quantize", dims, S, n_iter, Z, col_absmax, row_smooth, Kc, Uc, stream);
+    return lq_low_quantize_common("gdn_lq4_quantize", 4, dims, S, n_iter, Z, col_absmax, row_smooth, Kc, Uc, stream);
+}
+
+int gdn_lq6_quantize(const rsu_dims* dims, const float* S, int n_iter, void* Z, float* col_absmax, float* row_smooth,
+                     void* Kc, void* Uc, rsu_stream_t stream) {
+    return lq_low_quantize_common("gdn_lq6_quantize", 6, dims, S, n_iter, Z, col_absmax, row_smooth, Kc, Uc, stream);
+}
+
+int gdn_lq6_window(const rsu_dims* dims, int W, int pos, int n_iter, void* Z, float* col_absmax, float* row_smooth,
+                   void* Kc, void* Uc, void* Kbuf, float* Ubuf, float* Gbuf, const void* q, const void* k,
+                   const void* v, const float* alpha, const float* beta, float* y, rsu_stream_t stream) {
+    return lq_window_common("gdn_lq6_window", Kind::gdn, dims, W, pos, n_iter, static_cast<int8_t*>(Z), col_absmax,
+                            row_smooth, Kc, Uc, Kbuf, Ubuf, Gbuf, q, k, v, alpha, beta, y, stream, 6);
 }
 
 int gdn_lq4_window(const rsu_dims* dims, int W, int pos, int n_iter, void* Z, float* col_absmax, float* row_smooth,
                    void* Kc, void* Uc, void* Kbuf, float* Ubuf, float* Gbuf, const void* q, const void* k,
                    const void* v, const float* alpha, const float* beta, float* y, rsu_stream_t stream) {
     return lq_window_common("gdn_lq4_window", Kind::gdn, dims, W, pos, n_iter, static_cast<int8_t*>(Z), col_absmax,
-                            row_smooth, Kc, Uc, Kbuf, Ubuf, Gbuf, q, k, v, alpha, beta, y, stream, true);
+                            row_smooth, Kc, Uc, Kbuf, Ubuf, Gbuf, q, k, v, alpha, beta, y, stream, 4);
 }
 
 int gdn_lq_window(const rsu_dims* dims, int W, int pos, int n_iter, int8_t* Z, float* col_absmax,

@@ -51,11 +51,12 @@ __device__ __forceinline__ f32x4 unpack_codes(uint32_t w) {
 // before its state region (which the refit region reuses) is free.
 template <int kT, int kBits>
 struct RefitCfg {
-    static_assert((kT == 4 || kT == 8) && (kBits == 8 || kBits == 4), "4 or 8 tokens, 8- or 4-bit codes");
+    static_assert((kT == 4 || kT == 8) && (kBits == 8 || kBits == 6 || kBits == 4), "4 or 8 tokens, 8-, 6- or 4-bit codes");
     static constexpr int kC = kT / 4;                        // f32x4 chunks of a token vector
-    static constexpr int kQmax = kBits == 8 ? 127 : 7;       // largest code
-    static constexpr int kRowWords = kD * kBits / 32;        // 32 (8-bit) or 16 (4-bit) words per row
-    static constexpr int kCodeStride = kBits == 8 ? 40 : 20; // staged row stride: 16-byte rows, 8 rows span the banks
+    static constexpr int kQmax = (1 << (kBits - 1)) - 1;     // largest code: 127, 31 or 7
+    static constexpr int kRowWords = kD * kBits / 32;        // 32 (8-bit), 24 (6-bit) or 16 (4-bit) words per row
+    // staged row stride: 16-byte rows, 8 rows span the banks
+    static constexpr int kCodeStride = kBits == 8 ? 40 : kBits == 6 ? 28 : 20;
     static constexpr int kRegionFloats = kD * kCodeStride + 4 * kT * kD + 4 * kT * kD + kD;
     static constexpr int kWFloats = kT * kD;
 };
@@ -101,14 +102,16 @@ __device__ __forceinline__ float max_row_lanes(float x) {
 }
 
 // Code of w = x * (qmax / B): round half to even with one fp32 add (the low mantissa bits
-// of w + 1.5 * 2^23 are the integer), clamped to [-qmax, qmax]; the code is the low byte
-// (8-bit) or the low nibble (4-bit, two's complement) of the returned bits. The add is not
-// contracted with the product that forms w: the code is decided on w rounded to fp32.
+// of w + 1.5 * 2^23 are the integer), clamped to [-qmax, qmax]; the returned bits are
+// 0x4B400000 + z, so the code's two's complement is in the low bits: the low byte (8-bit),
+// the low nibble (4-bit), or the high part z >> 2 in bits 2..5 and the low part z & 3 in
+// bits 0..1 (6-bit). The add is not contracted with the product that forms w: the code is
+// decided on w rounded to fp32.
 template <int kBits>
 __device__ __forceinline__ uint32_t lq_code_t(float w) {
 #pragma clang fp contract(off)
     constexpr float kMagic = 12582912.0f;
-    constexpr int kQ = kBits == 8 ? 127 : 7;
+    constexpr int kQ = (1 << (kBits - 1)) - 1;
     const int bits = __float_as_int(w + kMagic);
     return static_cast<uint32_t>(min(max(bits, 0x4B400000 - kQ), 0x4B400000 + kQ));
 }
@@ -361,13 +364,26 @@ __device__ __forceinline__ void lq_refit(const RefitLds<kT, kBits>& L, f32x4 (&s
             L.codes[(8 * it + ro) * Cfg::kCodeStride + uu] =
                 pack_low_bytes(lq_code_t<8>(s[it].x * sc.x), lq_code_t<8>(s[it].y * sc.y),
                                lq_code_t<8>(s[it].z * sc.z), lq_code_t<8>(s[it].w * sc.w));
-    } else {  // four nibbles: half of the row's word for columns 8 (uu / 2) .. +7
+    } else if constexpr (kBits == 4) {  // four nibbles: half of the row's word for columns 8 (uu / 2) .. +7
         uint16_t* c16 = reinterpret_cast<uint16_t*>(L.codes);
 #pragma unroll
         for (int it = 0; it < 16; ++it)
             c16[(8 * it + ro) * 2 * Cfg::kCodeStride + uu] = static_cast<uint16_t>(
                 (lq_code_t<4>(s[it].x * sc.x) & 0xfu) | ((lq_code_t<4>(s[it].y * sc.y) & 0xfu) << 4) |
                 ((lq_code_t<4>(s[it].z * sc.z) & 0xfu) << 8) | ((lq_code_t<4>(s[it].w * sc.w) & 0xfu) << 12));
+    } else {  // the four high parts as nibbles (bytes 0..63 of the row), the low parts in byte 64 + uu
+        uint16_t* c16 = reinterpret_cast<uint16_t*>(L.codes);
+        uint8_t* c8 = reinterpret_cast<uint8_t*>(L.codes);
+#pragma unroll
+        for (int it = 0; it < 16; ++it) {
+            const int row = 8 * it + ro;
+            const uint32_t z0 = lq_code_t<6>(s[it].x * sc.x), z1 = lq_code_t<6>(s[it].y * sc.y);
+            const uint32_t z2 = lq_code_t<6>(s[it].z * sc.z), z3 = lq_code_t<6>(s[it].w * sc.w);
+            c16[row * 2 * Cfg::kCodeStride + uu] = static_cast<uint16_t>(
+                ((z0 >> 2) & 0xfu) | (((z1 >> 2) & 0xfu) << 4) | (((z2 >> 2) & 0xfu) << 8) | (((z3 >> 2) & 0xfu) << 12));
+            c8[row * 4 * Cfg::kCodeStride + 64 + uu] =
+                static_cast<uint8_t>((z0 & 3u) | ((z1 & 3u) << 2) | ((z2 & 3u) << 4) | ((z3 & 3u) << 6));
+        }
     }
     __syncthreads();
     constexpr int kQuads = Cfg::kRowWords / 4;  // 16-byte pieces per row
@@ -1141,37 +1157,61 @@ __global__ __launch_bounds__(kThreads) void lq_boundary_kda_kernel(
     lq_refit(L, s, n_iter, tid, Zh, Bcol + vec_off, Csm + vec_off, Kc + tok0, Uc + tok0);
 }
 
-// ---------------------------------------------------------------- 4 bits, 8 tokens
+// ---------------------------------------------------------------- 4 and 6 bits
 // LeapQuant at 4 bits (sec. 4.1 fits r = 8 tokens there): codes in [-7, 7], two per byte
-// (the even column in the low nibble), dequant Z B / 7, 8 KiB of payload per head. The
-// int4 sweep has its own layout: lane l of wave w owns the 32-bit word of 8 columns
-// 8 (l & 15) .. +7 in the rows 16 it + 4 w + (l >> 4), it = 0..7; a word's 4 row lanes
-// (l, l^16, l^32, l^48) combine by lane swaps, the 4 waves through LDS. Record and token
-// terms are added per value column: thread c + 128 h (h = 0, 1) adds records 8h .. 8h+7
-// and tokens 4h .. 4h+3 of column c.
-constexpr int kTok4 = 8;
-constexpr int kRow4 = kD / 8;  // 32-bit words of a 4-bit row
+// (the even column in the low nibble), dequant Z B / 7, 8 KiB of payload per head.
+// At 6 bits (r = 4 tokens): codes in [-31, 31], dequant Z B / 31, a row of 96 bytes: the
+// high parts z >> 2 as nibbles in the 4-bit layout (bytes 0..63), then the low parts z & 3,
+// four per byte, column 4b + i in bits 2i .. 2i+1 of byte 64 + b; 12 KiB per head.
+// The low-bit sweep has its own layout: lane l of wave w owns the 32-bit nibble word of 8
+// columns 8 (l & 15) .. +7 (and at 6 bits their 16 bits of low parts) in the rows
+// 16 it + 4 w + (l >> 4), it = 0..7; a word's 4 row lanes (l, l^16, l^32, l^48) combine by
+// lane swaps, the 4 waves through LDS. Record and token terms are added per value column:
+// thread c + 128 h (h = 0, 1) adds records 8h .. 8h+7 and the h-th half of the tokens.
+template <int kBits>
+struct LowBits {
+    static_assert(kBits == 4 || kBits == 6, "4- or 6-bit codes");
+    static constexpr int kT = kBits == 4 ? 8 : 4;           // compensator tokens
+    static constexpr int kTh = kT / 2;                       // tokens per column thread
+    static constexpr int kC = kT / 4;                        // f32x4 chunks of a token vector
+    static constexpr int kQmax = (1 << (kBits - 1)) - 1;     // 7 or 31
+    static constexpr int kRowWords = kD * kBits / 32;        // 16 or 24 words per row
+    static constexpr int kZsStride = kRowWords + 1;          // staged row stride of the boundary
+    // the sweep multiplies by 16 z (4 bits) or 4 z (6 bits): the read vectors carry the inverse
+    static constexpr float kReadScale = kBits == 4 ? 0.0625f : 0.25f;
+};
 
-__device__ __forceinline__ int lq4_row(int it, int wave, int rl) { return 16 * it + 4 * wave + rl; }
+__device__ __forceinline__ int low_row(int it, int wave, int rl) { return 16 * it + 4 * wave + rl; }
 
-// Payload sweep of the 4-bit steps: the lane's 8 code words (rows lq4_row(it, wave, l >> 4),
+// Payload sweep of the low-bit steps: the lane's 8 code words (rows low_row(it, wave, l >> 4),
 // value columns 8 (l & 15) .. +7) against the two read vectors, whose rowv entries are the read
-// vectors times 1/16. A code is read as the signed high nibble of a byte, i.e. as 16 z with one
-// sign-extending byte conversion (the even columns from w << 4, the odd ones from w), so the
-// products equal z times the unscaled entries exactly. The 4 row lanes l, l^16, l^32, l^48 are
+// vectors times kReadScale. A 4-bit code is read as the signed high nibble of a byte, i.e. as
+// 16 z with one sign-extending byte conversion (the even columns from w << 4, the odd ones from
+// w). At 6 bits the nibble is the high part and the low part z & 3 goes into bits 2..3 of the
+// same byte, which then reads 16 (z >> 2) + 4 (z & 3) = 4 z. Either way the products equal z
+// times the unscaled entries exactly. The 4 row lanes l, l^16, l^32, l^48 are
 // summed by two lane swaps that halve the live values: lanes with bit 4 set keep columns 4..7 of
 // the eight, lanes with bit 5 set the upper pair of their four. Each lane stores {p1, p2} of its two
 // columns 4 b4 + 2 b5 + (0, 1) into red_w (the wave's [128] partials).
-__device__ __forceinline__ void sweep4(const uint32_t (&zw)[8], const f32x2* rowv, int wave, int lane,
-                                       f32x2* red_w) {
+template <int kBits>
+__device__ __forceinline__ void sweep_low(const uint32_t (&zw)[8], const uint32_t (&zl)[8], const f32x2* rowv,
+                                          int wave, int lane, f32x2* red_w) {
     const int c16 = lane & 15, rl = lane >> 4;
     float p1[8], p2[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) p1[e] = p2[e] = 0.f;
 #pragma unroll
     for (int it = 0; it < 8; ++it) {
-        const f32x2 rv = rowv[lq4_row(it, wave, rl)];
-        const uint32_t ev = (zw[it] << 4) & 0xF0F0F0F0u, od = zw[it] & 0xF0F0F0F0u;
+        const f32x2 rv = rowv[low_row(it, wave, rl)];
+        uint32_t ev = (zw[it] << 4) & 0xF0F0F0F0u, od = zw[it] & 0xF0F0F0F0u;
+        if constexpr (kBits == 6) {
+            // the 8 low parts (column e in bits 2e) spread to one nibble per byte: byte j holds
+            // column 2j in bits 0..1 and column 2j + 1 in bits 2..3
+            uint32_t sp = (zl[it] | (zl[it] << 8)) & 0x00FF00FFu;
+            sp = (sp | (sp << 4)) & 0x0F0F0F0Fu;
+            ev |= (sp << 2) & 0x0C0C0C0Cu;
+            od |= sp & 0x0C0C0C0Cu;
+        }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const float ze = static_cast<float>(static_cast<int8_t>(ev >> (8 * j)));
@@ -1193,7 +1233,8 @@ __device__ __forceinline__ void sweep4(const uint32_t (&zw)[8], const f32x2* row
         f32x4{add_pair32(q1[0], q1[2]), add_pair32(q2[0], q2[2]), add_pair32(q1[1], q1[3]), add_pair32(q2[1], q2[3])};
 }
 
-__global__ __launch_bounds__(kThreads) void lq4_step_kernel(
+template <int kBits>
+__global__ __launch_bounds__(kThreads) void lq_low_step_kernel(
     int W, int pos, const uint32_t* __restrict__ Z, const float* __restrict__ Bcol, const float* __restrict__ Csm,
     const half_t* __restrict__ Kc, const half_t* __restrict__ Uc, bf16_t* __restrict__ Kbuf,
     float* __restrict__ Ubuf, float* __restrict__ Gbuf, const bf16_t* __restrict__ q,
@@ -1201,7 +1242,9 @@ __global__ __launch_bounds__(kThreads) void lq4_step_kernel(
     const float* __restrict__ beta, float* __restrict__ y) {
     __shared__ f32x2 rowv[kD];
     __shared__ f32x2 coef[16];
-    __shared__ f32x2 ctok[kTok4];
+    using Cfg = LowBits<kBits>;
+    constexpr int kT = Cfg::kT, kTh = Cfg::kTh;
+    __shared__ f32x2 ctok[kT];
     __shared__ f32x2 red[4][kD];
     __shared__ f32x2 recp[kD];
     __shared__ float kq_part[2];
@@ -1214,7 +1257,7 @@ __global__ __launch_bounds__(kThreads) void lq4_step_kernel(
     const bool first = tid < kD;
     const size_t vec_off = static_cast<size_t>(h) * kD;
     const size_t rec0 = static_cast<size_t>(h) * W * kD;
-    const size_t tok0 = static_cast<size_t>(h) * kTok4 * kD;
+    const size_t tok0 = static_cast<size_t>(h) * kT * kD;
 
     // ---- loads: record keys (group grp) and values (column cc), tokens, inputs, codes
     uint32_t kc[4] = {0u, 0u, 0u, 0u};
@@ -1230,10 +1273,10 @@ __global__ __launch_bounds__(kThreads) void lq4_step_kernel(
         ucol[e] = j < pos ? ul : 0.f;
     }
     uint4 ktw = {0u, 0u, 0u, 0u};
-    if (first) ktw = *reinterpret_cast<const uint4*>(Kc + tok0 + (grp & 7) * kD + 8 * ch);
-    half_t utv[4];
+    if (first) ktw = *reinterpret_cast<const uint4*>(Kc + tok0 + (grp & (kT - 1)) * kD + 8 * ch);
+    half_t utv[kTh];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) utv[e] = Uc[tok0 + (4 * half + e) * kD + cc];
+    for (int e = 0; e < kTh; ++e) utv[e] = Uc[tok0 + (kTh * half + e) * kD + cc];
     const float g_lane = lane < pos ? Gbuf[static_cast<size_t>(h) * W + lane] : 1.f;
     const uint4 kchw = *reinterpret_cast<const uint4*>(k + vec_off + 8 * ch);
     const uint4 qchw = *reinterpret_cast<const uint4*>(q + vec_off + 8 * ch);
@@ -1243,10 +1286,17 @@ __global__ __launch_bounds__(kThreads) void lq4_step_kernel(
     const float bcc = Bcol[vec_off + cc];
     const float vr = load_in(v, vec_off + cc);
     const float bt = beta[h];
-    const uint32_t* Zh = Z + static_cast<size_t>(h) * kD * kRow4;
-    uint32_t zw[8];
+    const uint32_t* Zh = Z + static_cast<size_t>(h) * kD * Cfg::kRowWords;
+    uint32_t zw[8], zl[8];
 #pragma unroll
-    for (int it = 0; it < 8; ++it) zw[it] = __builtin_nontemporal_load(Zh + lq4_row(it, wave, rl) * kRow4 + c16);
+    for (int it = 0; it < 8; ++it) {
+        const uint32_t* zrow = Zh + low_row(it, wave, rl) * Cfg::kRowWords;
+        zw[it] = __builtin_nontemporal_load(zrow + c16);
+        if constexpr (kBits == 6)  // the low parts: bytes 64 + 2 c16, +1 of the row
+            zl[it] = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(zrow + 16) + c16);
+        else
+            zl[it] = 0u;
+    }
 
     // ---- decays (newest gate first): after record grp, and over the whole window so far
     float Gg = 1.f, Gall = 1.f;
@@ -1272,7 +1322,7 @@ __global__ __launch_bounds__(kThreads) void lq4_step_kernel(
         cq = row16_sum(cq);
         if (ch == 0 && grp < pos) coef[grp] = f32x2{ck, cq};
     }
-    if (first) {  // groups 0..7: the tokens, decayed by every gate of the window
+    if (first) {  // groups 0..kT-1: the tokens, decayed by every gate of the window
         const half_t* kt = reinterpret_cast<const half_t*>(&ktw);
         float ck = 0.f, cq = 0.f;
 #pragma unroll
@@ -1283,16 +1333,16 @@ __global__ __launch_bounds__(kThreads) void lq4_step_kernel(
         }
         ck = row16_sum(ck);
         cq = row16_sum(cq);
-        if (ch == 0) ctok[grp] = f32x2{ck, cq};
+        if (ch == 0 && grp < kT) ctok[grp] = f32x2{ck, cq};
         const float c0 = cr * Gall * gr;  // c_r Gamma_{1:l} at row r
-        rowv[cc] = f32x2{c0 * kr, c0 * qr} * 0.0625f;  // times 1/16: see sweep4
+        rowv[cc] = f32x2{c0 * kr, c0 * qr} * Cfg::kReadScale;  // see sweep_low
         const float kq = wave_sum(kr * qr);
         if (lane == 0) kq_part[wave] = kq;
     }
     __syncthreads();
 
     // ---- payload sweep over the lane's 8 words; the 4 row lanes, then the waves
-    sweep4(zw, rowv, wave, lane, red[wave]);
+    sweep_low<kBits>(zw, zl, rowv, wave, lane, red[wave]);
     // record and token terms of column cc
     f32x2 rp = {0.f, 0.f};
 #pragma unroll
@@ -1301,13 +1351,13 @@ __global__ __launch_bounds__(kThreads) void lq4_step_kernel(
         if (j < pos) rp += coef[j] * ucol[e];
     }
 #pragma unroll
-    for (int e = 0; e < 4; ++e) rp += ctok[4 * half + e] * static_cast<float>(utv[e]);
+    for (int e = 0; e < kTh; ++e) rp += ctok[kTh * half + e] * static_cast<float>(utv[e]);
     if (half == 1) recp[cc] = rp;
     __syncthreads();
 
     if (first) {
         const int c = cc;
-        f32x2 acc = (red[0][c] + red[1][c] + red[2][c] + red[3][c]) * (bcc * (1.f / 7.f));
+        f32x2 acc = (red[0][c] + red[1][c] + red[2][c] + red[3][c]) * (bcc * (1.f / Cfg::kQmax));
         acc += rp + recp[c];
         const float kq = kq_part[0] + kq_part[1];
         const float u = bt * (vr - acc.x);
@@ -1319,42 +1369,49 @@ __global__ __launch_bounds__(kThreads) void lq4_step_kernel(
     }
 }
 
-// The window's last step at 4 bits: the step as above, then S_W on the matrix cores as in
-// the 8-bit boundary (payload init from the staged nibbles, the records' two bf16 MFMAs per
-// tile, the 8 tokens' two fp32 MFMAs), through LDS into the refit's layout, and the 8-token
-// refit with 4-bit codes. One region of dynamic LDS serves the step arrays, the state in
-// transit (half of it at a time) and the refit's arrays in turn; after it lie W (the old Ut,
-// 8 tokens) and the old payload's B / 7: 47 KB in all, three workgroups per CU.
-constexpr int kZs4Stride = kRow4 + 1;
-constexpr int kStep4Floats = 2 * kD * 4 + 3 * 2 * kD * 4 + kD * kZs4Stride + 2 * kTok4 * kD + 4 * kD * 2 + kD * 2;
-constexpr int kLq4RegionFloats = cmax3(kStep4Floats, kTransitFloats, RefitCfg<8, 4>::kRegionFloats);
-constexpr int kLq4BoundaryFloats = kLq4RegionFloats + kTok4 * kD + kD;
-static_assert(kLq4RegionFloats % 4 == 0, "W after the region must be 16-byte aligned");
+// The window's last step at 4 or 6 bits: the step as above, then S_W on the matrix cores as
+// in the 8-bit boundary (payload init from the staged codes, the records' two bf16 MFMAs per
+// tile, the tokens' fp32 MFMAs, one per 4 tokens), through LDS into the refit's layout, and
+// the refit with low-bit codes. One region of dynamic LDS serves the step arrays, the state
+// in transit (half of it at a time) and the refit's arrays in turn; after it lie W (the old
+// Ut) and the old payload's B / qmax: 47 KB (4 bits) or 40 KB (6 bits) in all.
+template <int kBits>
+struct LowBitsLds {
+    using Cfg = LowBits<kBits>;
+    static constexpr int kStep = 2 * kD * 4 + 3 * 2 * kD * 4 + kD * Cfg::kZsStride + 2 * Cfg::kT * kD + 4 * kD * 2 + kD * 2;
+    static constexpr int kRegion = cmax3(kStep, kTransitFloats, RefitCfg<Cfg::kT, kBits>::kRegionFloats);
+    static constexpr int kBoundary = kRegion + Cfg::kT * kD + kD;
+    static_assert(kRegion % 4 == 0, "W after the region must be 16-byte aligned");
+};
 
-__global__ __launch_bounds__(kThreads) void lq4_boundary_kernel(
+template <int kBits>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void lq_low_boundary_kernel(
     int W, int pos, int n_iter, uint32_t* __restrict__ Z, float* __restrict__ Bcol, float* __restrict__ Csm,
     half_t* __restrict__ Kc, half_t* __restrict__ Uc, const bf16_t* __restrict__ Kbuf,
     const float* __restrict__ Ubuf, const float* __restrict__ Gbuf, const bf16_t* __restrict__ q,
     const bf16_t* __restrict__ k, const bf16_t* __restrict__ v, const float* __restrict__ gate,
     const float* __restrict__ beta, float* __restrict__ y) {
+    using Cfg = LowBits<kBits>;
+    constexpr int kT = Cfg::kT, kTh = Cfg::kTh, kC = Cfg::kC, kZsStride = Cfg::kZsStride;
+    constexpr int kRegion = LowBitsLds<kBits>::kRegion;
     constexpr int kRec = 16;
     extern __shared__ __align__(16) float dyn_lds[];
     __shared__ f32x2 rowv[kD];
     __shared__ f32x2 coef[kRec];
-    __shared__ f32x2 ctok[kTok4];
+    __shared__ f32x2 ctok[kT];
     __shared__ float kq_part[2];
     __shared__ float zcoef[kD];
     __shared__ float gam[kRec];
 
     u32x4* Kt = reinterpret_cast<u32x4*>(dyn_lds);                 // [2][128] keys, 8 records per word
     u32x4* Ut = Kt + 2 * kD;                                        // [3][2][128] scaled values, 3 parts
-    uint32_t* Zs = reinterpret_cast<uint32_t*>(Ut + 3 * 2 * kD);   // [128][17] the old codes
-    float* Ktok = reinterpret_cast<float*>(Zs + kD * kZs4Stride);  // [8][128]
-    float* Utok = Ktok + kTok4 * kD;                                // [8][128], scaled by Gamma_{1:W}
-    f32x2* red = reinterpret_cast<f32x2*>(Utok + kTok4 * kD);      // [4][128]
+    uint32_t* Zs = reinterpret_cast<uint32_t*>(Ut + 3 * 2 * kD);   // [128][kZsStride] the old codes
+    float* Ktok = reinterpret_cast<float*>(Zs + kD * kZsStride);   // [kT][128]
+    float* Utok = Ktok + kT * kD;                                   // [kT][128], scaled by Gamma_{1:W}
+    f32x2* red = reinterpret_cast<f32x2*>(Utok + kT * kD);         // [4][128]
     f32x2* recp = red + 4 * kD;                                     // [128]
-    const RefitLds<kTok4, 4> L(dyn_lds, dyn_lds + kLq4RegionFloats);
-    float* bscs = dyn_lds + kLq4RegionFloats + kTok4 * kD;          // B / 7 of the old payload
+    const RefitLds<kT, kBits> L(dyn_lds, dyn_lds + kRegion);
+    float* bscs = dyn_lds + kRegion + kT * kD;                      // B / qmax of the old payload
 
     const int h = head_of_block(blockIdx.x, gridDim.x), tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
@@ -1364,8 +1421,8 @@ __global__ __launch_bounds__(kThreads) void lq4_boundary_kernel(
     const bool first = tid < kD;
     const size_t vec_off = static_cast<size_t>(h) * kD;
     const size_t rec0 = static_cast<size_t>(h) * W * kD;
-    const size_t tok0 = static_cast<size_t>(h) * kTok4 * kD;
-    uint32_t* Zh = Z + static_cast<size_t>(h) * kD * kRow4;
+    const size_t tok0 = static_cast<size_t>(h) * kT * kD;
+    uint32_t* Zh = Z + static_cast<size_t>(h) * kD * Cfg::kRowWords;
 
     // ---- loads
     uint32_t kcr[4] = {0u, 0u, 0u, 0u};
@@ -1386,10 +1443,10 @@ __global__ __launch_bounds__(kThreads) void lq4_boundary_kernel(
         kcol[e >> 1] = (e & 1) ? (kcol[e >> 1] | (kb << 16)) : kb;
     }
     uint4 ktw = {0u, 0u, 0u, 0u};
-    if (first) ktw = *reinterpret_cast<const uint4*>(Kc + tok0 + (grp & 7) * kD + 8 * ch);
-    half_t tokv[kTok4];  // token t at row / column cc (threads < 128: keys; threads >= 128: values)
+    if (first) ktw = *reinterpret_cast<const uint4*>(Kc + tok0 + (grp & (kT - 1)) * kD + 8 * ch);
+    half_t tokv[kT];  // token t at row / column cc (threads < 128: keys; threads >= 128: values)
 #pragma unroll
-    for (int t = 0; t < kTok4; ++t) tokv[t] = (first ? Kc : Uc)[tok0 + t * kD + cc];
+    for (int t = 0; t < kT; ++t) tokv[t] = (first ? Kc : Uc)[tok0 + t * kD + cc];
     const float g_lane = lane < pos ? Gbuf[static_cast<size_t>(h) * W + lane] : 1.f;
     const uint4 kchw = *reinterpret_cast<const uint4*>(k + vec_off + 8 * ch);
     const uint4 qchw = *reinterpret_cast<const uint4*>(q + vec_off + 8 * ch);
@@ -1399,9 +1456,16 @@ __global__ __launch_bounds__(kThreads) void lq4_boundary_kernel(
     const float bcc = Bcol[vec_off + cc];
     const float vr = load_in(v, vec_off + cc);
     const float bt = beta[h];
-    uint32_t zw[8];
+    uint32_t zw[8], zl[8];
 #pragma unroll
-    for (int it = 0; it < 8; ++it) zw[it] = __builtin_nontemporal_load(Zh + lq4_row(it, wave, rl) * kRow4 + c16);
+    for (int it = 0; it < 8; ++it) {
+        const uint32_t* zrow = Zh + low_row(it, wave, rl) * Cfg::kRowWords;
+        zw[it] = __builtin_nontemporal_load(zrow + c16);
+        if constexpr (kBits == 6)  // the low parts: bytes 64 + 2 c16, +1 of the row
+            zl[it] = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(zrow + 16) + c16);
+        else
+            zl[it] = 0u;
+    }
 
     // ---- gate products (newest first): after record grp, after record = lane, all
     float Gg = 1.f, Gl = 1.f, Gall = 1.f;
@@ -1441,32 +1505,32 @@ __global__ __launch_bounds__(kThreads) void lq4_boundary_kernel(
         }
         ck = row16_sum(ck);
         cq = row16_sum(cq);
-        if (ch == 0) ctok[grp] = f32x2{ck, cq};
+        if (ch == 0 && grp < kT) ctok[grp] = f32x2{ck, cq};
         const float c0 = cr * gam_all;
-        rowv[cc] = f32x2{c0 * kr, c0 * qr} * 0.0625f;  // times 1/16: see sweep4
+        rowv[cc] = f32x2{c0 * kr, c0 * qr} * Cfg::kReadScale;  // see sweep_low
         zcoef[cc] = c0;
         const float kq = wave_sum(kr * qr);
         if (lane == 0) kq_part[wave] = kq;
     } else {
-        bscs[cc] = bcc * (1.f / 7.f);
+        bscs[cc] = bcc * (1.f / Cfg::kQmax);
     }
     // token operands of the contraction, and the unscaled values as the refit's start
 #pragma unroll
-    for (int t = 0; t < kTok4; ++t) {
+    for (int t = 0; t < kT; ++t) {
         const float x = static_cast<float>(tokv[t]);
         if (first) Ktok[t * kD + cc] = x;
         else Utok[t * kD + cc] = x * gam_all;
     }
     if (!first)
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
-            L.W[cc * 2 + hh] = f32x4{static_cast<float>(tokv[4 * hh]), static_cast<float>(tokv[4 * hh + 1]),
+        for (int hh = 0; hh < kC; ++hh)
+            L.W[cc * kC + hh] = f32x4{static_cast<float>(tokv[4 * hh]), static_cast<float>(tokv[4 * hh + 1]),
                                      static_cast<float>(tokv[4 * hh + 2]), static_cast<float>(tokv[4 * hh + 3])};
     Kt[half * kD + cc] = u32x4{kcol[0], kcol[1], kcol[2], kcol[3]};
     __syncthreads();
 
     // ---- payload sweep; record and token terms per column; scaled records staged for the MFMA
-    sweep4(zw, rowv, wave, lane, red + wave * kD);
+    sweep_low<kBits>(zw, zl, rowv, wave, lane, red + wave * kD);
     f32x2 rp = {0.f, 0.f};
     u32x4 part[3];
 #pragma unroll
@@ -1482,15 +1546,19 @@ __global__ __launch_bounds__(kThreads) void lq4_boundary_kernel(
         part[2][e >> 1] = (e & 1) ? (part[2][e >> 1] | (lo << sh)) : lo;
     }
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {  // tokens 4 half .. +3 of column cc (L.W holds their unscaled values)
-        const f32x4 ut = L.W[cc * 2 + half];
-        rp += ctok[4 * half + e] * ut[e];
+    for (int e = 0; e < kTh; ++e) {  // tokens kTh half .. +kTh-1 of column cc (L.W holds their unscaled values)
+        const int t = kTh * half + e;
+        rp += ctok[t] * L.W[cc * kC + (t >> 2)][t & 3];
     }
 #pragma unroll
     for (int pp = 0; pp < 3; ++pp) Ut[(pp * 2 + half) * kD + cc] = part[pp];
     if (half == 1) recp[cc] = rp;
 #pragma unroll
-    for (int it = 0; it < 8; ++it) Zs[lq4_row(it, wave, rl) * kZs4Stride + c16] = zw[it];
+    for (int it = 0; it < 8; ++it) {
+        uint32_t* zs_row = Zs + low_row(it, wave, rl) * kZsStride;
+        zs_row[c16] = zw[it];
+        if constexpr (kBits == 6) reinterpret_cast<uint16_t*>(zs_row + 16)[c16] = static_cast<uint16_t>(zl[it]);
+    }
     __syncthreads();
 
     // ---- correction and output; the current record joins the contraction operands
@@ -1519,16 +1587,26 @@ __global__ __launch_bounds__(kThreads) void lq4_boundary_kernel(
         const int row = 16 * (2 * wave + a) + lr;
         const bf16x8 bv = __builtin_bit_cast(bf16x8, Kt[blk * kD + row]);
         const float zc = zcoef[row];
-        const float bk0 = Ktok[lq * kD + row], bk1 = Ktok[(4 + lq) * kD + row];
-        const uint16_t* z16 = reinterpret_cast<const uint16_t*>(Zs + row * kZs4Stride);
+        const float bk0 = Ktok[lq * kD + row], bk1 = kT == 8 ? Ktok[(4 + lq) * kD + row] : 0.f;
+        const uint16_t* z16 = reinterpret_cast<const uint16_t*>(Zs + row * kZsStride);
+        const uint8_t* z8lo = reinterpret_cast<const uint8_t*>(Zs + row * kZsStride + 16);
 #pragma unroll
         for (int ct = 0; ct < 8; ++ct) {
             const f32x4 bs = *reinterpret_cast<const f32x4*>(bscs + 16 * ct + 4 * lq);
             const uint32_t zz = z16[4 * ct + lq];  // the 4 nibbles of columns 16ct + 4lq .. +3
-            const f32x4 zf = {static_cast<float>(static_cast<int>(zz << 28) >> 28),
-                              static_cast<float>(static_cast<int>(zz << 24) >> 28),
-                              static_cast<float>(static_cast<int>(zz << 20) >> 28),
-                              static_cast<float>(static_cast<int>(zz << 16) >> 28)};
+            f32x4 zf;
+            if constexpr (kBits == 4) {
+                zf = f32x4{static_cast<float>(static_cast<int>(zz << 28) >> 28),
+                           static_cast<float>(static_cast<int>(zz << 24) >> 28),
+                           static_cast<float>(static_cast<int>(zz << 20) >> 28),
+                           static_cast<float>(static_cast<int>(zz << 16) >> 28)};
+            } else {  // 4 (z >> 2) + (z & 3), the low parts of the same 4 columns in one byte
+                const uint32_t zb = z8lo[4 * ct + lq];
+                zf = f32x4{static_cast<float>(4 * (static_cast<int>(zz << 28) >> 28) + static_cast<int>(zb & 3u)),
+                           static_cast<float>(4 * (static_cast<int>(zz << 24) >> 28) + static_cast<int>((zb >> 2) & 3u)),
+                           static_cast<float>(4 * (static_cast<int>(zz << 20) >> 28) + static_cast<int>((zb >> 4) & 3u)),
+                           static_cast<float>(4 * (static_cast<int>(zz << 16) >> 28) + static_cast<int>(zb >> 6))};
+            }
             acc[a][ct] = zf * (bs * zc);
             const int col = 16 * ct + lr;
             const bf16x8 a1 = __builtin_bit_cast(bf16x8, Ut[((lq < 2 ? 0 : 1) * 2 + blk) * kD + col]);
@@ -1537,7 +1615,8 @@ __global__ __launch_bounds__(kThreads) void lq4_boundary_kernel(
             acc[a][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, bv, acc[a][ct], 0, 0, 0);
             acc[a][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a2, bv, acc[a][ct], 0, 0, 0);
             acc[a][ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(Utok[lq * kD + col], bk0, acc[a][ct], 0, 0, 0);
-            acc[a][ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(Utok[(4 + lq) * kD + col], bk1, acc[a][ct], 0, 0, 0);
+            if constexpr (kT == 8)
+                acc[a][ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(Utok[(4 + lq) * kD + col], bk1, acc[a][ct], 0, 0, 0);
         }
     }
     __syncthreads();  // every read of the step-phase arrays is done: the region holds S in halves
@@ -1597,35 +1676,50 @@ hipError_t launch_lq_window(const StepArgs& a, const LqArgs& w, bool per_key, hi
     return hipGetLastError();
 }
 
-hipError_t launch_lq4_quantize(int heads, const float* S, int n_iter, void* Z, float* B, float* C, void* Kc,
-                               void* Uc, hipStream_t stream) {
-    using Cfg = RefitCfg<kTok4, 4>;
+template <int kBits>
+static hipError_t launch_low_quantize(int heads, const float* S, int n_iter, void* Z, float* B, float* C, void* Kc,
+                                      void* Uc, hipStream_t stream) {
+    constexpr int kT = LowBits<kBits>::kT;
+    using Cfg = RefitCfg<kT, kBits>;
     constexpr int floats = Cfg::kRegionFloats + Cfg::kWFloats;
-    static const hipError_t attr = set_lds(reinterpret_cast<const void*>(lq_quantize_kernel<kTok4, 4>), floats);
+    static const hipError_t attr = set_lds(reinterpret_cast<const void*>(lq_quantize_kernel<kT, kBits>), floats);
     if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL((lq_quantize_kernel<kTok4, 4>), dim3(heads), dim3(kThreads), sizeof(float) * floats, stream,
+    hipLaunchKernelGGL((lq_quantize_kernel<kT, kBits>), dim3(heads), dim3(kThreads), sizeof(float) * floats, stream,
                        S, n_iter, static_cast<uint32_t*>(Z), B, C, static_cast<half_t*>(Kc),
                        static_cast<half_t*>(Uc));
     return hipGetLastError();
 }
 
-hipError_t launch_lq4_window(const StepArgs& a, const LqArgs& w, hipStream_t stream) {
+template <int kBits>
+static hipError_t launch_low_window(const StepArgs& a, const LqArgs& w, hipStream_t stream) {
     if (w.pos == w.W - 1) {
-        static const hipError_t attr = set_lds(reinterpret_cast<const void*>(lq4_boundary_kernel), kLq4BoundaryFloats);
+        constexpr auto kernel = lq_low_boundary_kernel<kBits>;
+        constexpr int floats = LowBitsLds<kBits>::kBoundary;
+        static const hipError_t attr = set_lds(reinterpret_cast<const void*>(kernel), floats);
         if (attr != hipSuccess) return attr;
-        hipLaunchKernelGGL(lq4_boundary_kernel, dim3(a.heads), dim3(kThreads), sizeof(float) * kLq4BoundaryFloats,
+        hipLaunchKernelGGL(kernel, dim3(a.heads), dim3(kThreads), sizeof(float) * floats,
                            stream, w.W, w.pos, w.n_iter, reinterpret_cast<uint32_t*>(w.Z), w.B, w.C,
                            static_cast<half_t*>(w.Kc), static_cast<half_t*>(w.Uc),
                            static_cast<const bf16_t*>(w.Kbuf), w.Ubuf, w.Gbuf, static_cast<const bf16_t*>(a.q),
                            static_cast<const bf16_t*>(a.k), static_cast<const bf16_t*>(a.v), a.gate, a.beta, a.y);
         return hipGetLastError();
     }
-    hipLaunchKernelGGL(lq4_step_kernel, dim3(a.heads), dim3(kThreads), 0, stream, w.W, w.pos,
+    hipLaunchKernelGGL(lq_low_step_kernel<kBits>, dim3(a.heads), dim3(kThreads), 0, stream, w.W, w.pos,
                        reinterpret_cast<const uint32_t*>(w.Z), w.B, w.C, static_cast<const half_t*>(w.Kc),
                        static_cast<const half_t*>(w.Uc), static_cast<bf16_t*>(w.Kbuf), w.Ubuf, w.Gbuf,
                        static_cast<const bf16_t*>(a.q), static_cast<const bf16_t*>(a.k),
                        static_cast<const bf16_t*>(a.v), a.gate, a.beta, a.y);
     return hipGetLastError();
+}
+
+hipError_t launch_lq_low_quantize(int bits, int heads, const float* S, int n_iter, void* Z, float* B, float* C,
+                                  void* Kc, void* Uc, hipStream_t stream) {
+    return bits == 4 ? launch_low_quantize<4>(heads, S, n_iter, Z, B, C, Kc, Uc, stream)
+                     : launch_low_quantize<6>(heads, S, n_iter, Z, B, C, Kc, Uc, stream);
+}
+
+hipError_t launch_lq_low_window(int bits, const StepArgs& a, const LqArgs& w, hipStream_t stream) {
+    return bits == 4 ? launch_low_window<4>(a, w, stream) : launch_low_window<6>(a, w, stream);
 }
 
 }  // namespace rsu

@@ -239,7 +239,7 @@ def new_lq_buffers(w: wl.Workload):
     B, H, W = w.B, w.H, w.W
     r = 8 if w.bits == 4 else 4
     return {
-        "Z": (torch.zeros(B, H, 128, 64, device=DEV, dtype=torch.uint8) if w.bits == 4 else
+        "Z": (torch.zeros(B, H, 128, 128 * w.bits // 8, device=DEV, dtype=torch.uint8) if w.bits != 8 else
               torch.zeros(B, H, 128, 128, device=DEV, dtype=torch.int8)),
         "B": torch.zeros(B, H, 128, device=DEV),
         "C": torch.zeros(B, H, 128, device=DEV),
@@ -253,9 +253,11 @@ def new_lq_buffers(w: wl.Workload):
 
 def lq_host(buf, hd):
     """The GPU's representation of the sampled heads: Z, B, c, and the tokens as [n, 128, r]
-    (4-bit codes unpacked from their nibbles)."""
+    (4-bit codes unpacked from their nibbles, 6-bit codes from their two parts)."""
     from oracle import lq as lqo
-    if buf["Z"].dtype == torch.uint8:
+    if buf["Z"].dtype == torch.uint8 and buf["Z"].shape[-1] == 96:
+        Z = lqo.unpack6(take(buf["Z"], hd, (128, 96))).astype(np.int64)
+    elif buf["Z"].dtype == torch.uint8:
         Z = lqo.unpack_nibbles(take(buf["Z"], hd, (128, 64))).astype(np.int64)
     else:
         Z = take(buf["Z"], hd, (128, 128)).astype(np.int64)
@@ -329,7 +331,9 @@ def run_lq(w: wl.Workload, n_iter: int = 1, n_iter0: int = 8, sample: int | None
     window = m.kda_lq_window if w.per_key_gate else m.gdn_lq_window
     if w.bits == 4:
         quantize, window = m.gdn_lq4_quantize, m.gdn_lq4_window
-    qmax = lqo.QMAX4 if w.bits == 4 else lqo.QMAX8
+    if w.bits == 6:
+        quantize, window = m.gdn_lq6_quantize, m.gdn_lq6_window
+    qmax = lqo.qmax_of(w.bits)
     r = 8 if w.bits == 4 else 4
     quantize(Sd, n_iter0, buf["Z"], buf["B"], buf["C"], buf["Kc"], buf["Uc"])
     err = {"y": 0.0, "tok": 0.0, "tok_k": 0.0, "tok_u": 0.0, "c": 0.0, "B": 0.0, "z_maxdiff": 0,

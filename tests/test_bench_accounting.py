@@ -116,3 +116,17 @@ def test_deltaproduct_bytes():
     assert bench.window_step_bytes_per_head(ww, 3) == 16384 + 512 + 6 * rec + inputs + 512 + 2 * rec
     last = bench.window_step_bytes_per_head(ww, 15)
     assert last == (16384 + 512 + 30 * rec + inputs + 512 + 2 * rec) + (16384 + 512 + 32 * rec) + (16384 + 512)
+
+
+def test_lq_low_bit_representation_bytes():
+    """LeapQuant's boundary representation per head: the payload (16384, 12288 or 8192
+    bytes at 8, 6 or 4 bits), fp32 B and c (512 each) and r fp16 token pairs (r = 4, 4, 8).
+    A step at pos 0 reads it with the inputs (3 bf16 vectors, alpha, beta) and writes y and
+    one record (bf16 key, fp32 value, fp32 gate)."""
+    rec = 256 + 512 + 4
+    inputs = 3 * 256 + 4 + 4
+    for cid, payload, r in ((6, 16384, 4), (16, 12288, 4), (12, 8192, 8)):
+        w = wl.WORKLOADS[cid]
+        rep = payload + 512 + 512 + 2 * r * 128 * 2
+        assert bench.lq_step_bytes_per_head(w, 0) == rep + inputs + 512 + rec
+        assert bench.lq_step_bytes_per_head(w, w.W - 1) == rep + (w.W - 1) * rec + inputs + 512 + rep

@@ -89,6 +89,68 @@ def test_lq4_b256_h48_full_size_sampled():
     _check(run_lq(w, n_iter=1, sample=64, steps=48), w.name)
 
 
+@pytest.mark.parametrize("W,B,H,n_iter", [(16, 2, 5, 1), (16, 3, 4, 2), (5, 2, 3, 1), (1, 2, 2, 0)])
+def test_lq6_windows_small(W, B, H, n_iter):
+    """6-bit codes (high parts as nibbles, low 2-bit parts four per byte, /31) with 4 tokens."""
+    w = wl.custom(wl.WORKLOADS[16], B=B, H=H, W=W, steps=2 * W + min(W, 3))
+    _check(run_lq(w, n_iter=n_iter), f"6-bit W={W} B={B} H={H} n_iter={n_iter}")
+
+
+@pytest.mark.parametrize("n_iter0", [0, 3])
+def test_lq6_quantize_start_iterations(n_iter0):
+    w = wl.custom(wl.WORKLOADS[16], B=3, H=11, W=16, steps=0)
+    _check(run_lq(w, n_iter0=n_iter0, steps=0), f"6-bit quantize n_iter0={n_iter0}", boundaries=False)
+
+
+def test_lq6_ragged_batch():
+    """100 heads: the head order's last group of 32 is cut short."""
+    w = wl.custom(wl.WORKLOADS[16], B=10, H=10, W=16, steps=35)
+    _check(run_lq(w, n_iter=1), "6-bit B=10 H=10")
+
+
+def test_lq6_zero_state_gives_zero_tokens_and_payload():
+    m = rsu()
+    S = torch.zeros(1, 2, 128, 128, device=DEV)
+    w = wl.custom(wl.WORKLOADS[16], B=1, H=2, W=16)
+    buf = new_lq_buffers(w)
+    buf["C"].fill_(7.0)
+    buf["Z"].fill_(0x5A)
+    m.gdn_lq6_quantize(S, 4, buf["Z"], buf["B"], buf["C"], buf["Kc"], buf["Uc"])
+    assert not buf["Z"].any() and not buf["B"].any() and not buf["Kc"].any()
+    np.testing.assert_array_equal(buf["C"].cpu().numpy(), np.float32(1e-6))
+
+
+def test_lq6_extreme_codes_round_trip():
+    """A state whose smoothed residual puts codes at -31, 31 and every value between in each
+    column: the payload's two parts decode to the oracle's codes exactly."""
+    m = rsu()
+    from oracle import lq as lqo
+    rng = np.random.default_rng(61)
+    S = (rng.standard_normal((2, 3, 128, 128)) * 0.02).astype(np.float32)
+    S[..., 5, :] *= 40.0   # a heavy row the smoothing scales down
+    Sd = torch.from_numpy(S).to(DEV)
+    w = wl.custom(wl.WORKLOADS[16], B=2, H=3, W=16)
+    buf = new_lq_buffers(w)
+    m.gdn_lq6_quantize(Sd, 2, buf["Z"], buf["B"], buf["C"], buf["Kc"], buf["Uc"])
+    hd = torch.arange(6, device=DEV)
+    rep = lq_host(buf, hd)
+    assert (np.abs(rep[0]).max(axis=1) == 31).all()          # each column's absmax code
+    assert set(np.unique(rep[0]).tolist()) == set(range(-31, 32))  # every code, both signs
+    err = {"tok": 0.0, "tok_k": 0.0, "tok_u": 0.0, "c": 0.0, "B": 0.0, "z_maxdiff": 0, "z_flips": 0,
+           "z_flips_outside_band": 0}
+    from parity import check_lq_refit
+    check_lq_refit(S.reshape(6, 128, 128).astype(np.float64), np.broadcast_to(lqo.walsh_start(), (6, 128, 4)),
+                   2, rep, err, qmax=31)
+    say(f"[lq] 6-bit extremes: {err}")
+    assert err["z_maxdiff"] <= 1 and err["z_flips_outside_band"] == 0
+
+
+def test_lq6_b256_h48_full_size_sampled():
+    w = wl.WORKLOADS[16]
+    say(f"[lq] {w.name}: full size, 64 sampled heads, 48 steps")
+    _check(run_lq(w, n_iter=1, sample=64, steps=48), w.name)
+
+
 @pytest.mark.parametrize("n_iter0", [0, 3])
 def test_lq_quantize_start_iterations(n_iter0):
     w = wl.custom(wl.WORKLOADS[6], B=2, H=3, W=16, steps=0)
