@@ -48,7 +48,7 @@ KERNEL_SOURCES = {
 
 WORKLOAD_BY_FLAG = {"gdn": 2, "gdn_small": 1, "kda": 3, "q8": 4, "log": 5, "lq": 6, "rwkv6": 7,
                     "rwkv6_log": 8, "kda_lq": 9, "rwkv7": 10, "rwkv7_q8": 11, "lq4": 12,
-                    "stepq": 13, "dp": 14, "dp_q8": 15, "lq6": 16}
+                    "stepq": 13, "dp": 14, "dp_q8": 15, "lq6": 16, "kda_lq4": 17, "kda_lq6": 18}
 LQ_TOKENS = 4
 
 
@@ -439,15 +439,15 @@ def run_gpu(w: wl.Workload, steps: int, warmup: int, slots: bool = False, n_iter
         Cs = torch.empty(B, H, 128, device=dev)
         Kc = torch.empty(B, H, 8 if four else LQ_TOKENS, 128, device=dev, dtype=torch.float16)
         Uc = torch.empty_like(Kc)
-        quant = {4: rsu.gdn_lq4_quantize, 6: rsu.gdn_lq6_quantize}.get(
-            w.bits, rsu.kda_lq_quantize if kda else rsu.gdn_lq_quantize)
+        quant = ({4: rsu.kda_lq4_quantize, 6: rsu.kda_lq6_quantize, 8: rsu.kda_lq_quantize} if kda else
+                 {4: rsu.gdn_lq4_quantize, 6: rsu.gdn_lq6_quantize, 8: rsu.gdn_lq_quantize})[w.bits]
         quant(S0, 8, Z, Bc, Cs, Kc, Uc)
         del S0
         Kb = torch.zeros(B, H, W, 128, device=dev, dtype=x["q"].dtype)
         Ub = torch.zeros(B, H, W, 128, device=dev)
         Gb = torch.zeros((B, H, W, 128) if kda else (B, H, W), device=dev)
-        win = {4: rsu.gdn_lq4_window, 6: rsu.gdn_lq6_window}.get(
-            w.bits, rsu.kda_lq_window if kda else rsu.gdn_lq_window)
+        win = ({4: rsu.kda_lq4_window, 6: rsu.kda_lq6_window, 8: rsu.kda_lq_window} if kda else
+               {4: rsu.gdn_lq4_window, 6: rsu.gdn_lq6_window, 8: rsu.gdn_lq_window})[w.bits]
 
         def step():
             t = state["t"]

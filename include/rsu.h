@@ -221,6 +221,25 @@ int gdn_lq6_window(const rsu_dims *dims, int W, int pos, int n_iter, void *Z,
                    float *col_absmax, float *row_smooth, void *Kc, void *Uc, void *Kbuf,
                    float *Ubuf, float *Gbuf, const void *q, const void *k, const void *v,
                    const float *alpha, const float *beta, float *y, rsu_stream_t stream);
+/* KDA at 4 and 6 bits (LeapQuant sec. 4.2 evaluates both widths on a KDA model): the
+ * formats of gdn_lq4_window / gdn_lq6_window with the per-key gate d [B,H,d_k] and
+ * Gbuf [B,H,W,d_k], as kda_lq_window is to gdn_lq_window. kda_lq4_quantize and
+ * kda_lq6_quantize are the conversions of gdn_lq4_quantize / gdn_lq6_quantize (the
+ * format does not depend on the gates). Rules as for gdn_lq_window. */
+int kda_lq4_quantize(const rsu_dims *dims, const float *S, int n_iter, void *Z,
+                     float *col_absmax, float *row_smooth, void *Kc, void *Uc,
+                     rsu_stream_t stream);
+int kda_lq4_window(const rsu_dims *dims, int W, int pos, int n_iter, void *Z,
+                   float *col_absmax, float *row_smooth, void *Kc, void *Uc, void *Kbuf,
+                   float *Ubuf, float *Gbuf, const void *q, const void *k, const void *v,
+                   const float *d, const float *beta, float *y, rsu_stream_t stream);
+int kda_lq6_quantize(const rsu_dims *dims, const float *S, int n_iter, void *Z,
+                     float *col_absmax, float *row_smooth, void *Kc, void *Uc,
+                     rsu_stream_t stream);
+int kda_lq6_window(const rsu_dims *dims, int W, int pos, int n_iter, void *Z,
+                   float *col_absmax, float *row_smooth, void *Kc, void *Uc, void *Kbuf,
+                   float *Ubuf, float *Gbuf, const void *q, const void *k, const void *v,
+                   const float *d, const float *beta, float *y, rsu_stream_t stream);
 int kda_lq_quantize(const rsu_dims *dims, const float *S, int n_iter, int8_t *Z,
                     float *col_absmax, float *row_smooth, void *Kc, void *Uc,
                     rsu_stream_t stream);

@@ -67,6 +67,10 @@ _SIGS = {
     "gdn_lq4_quantize": [_DP, _P, _I, _P, _P, _P, _P, _P, _P],
     "gdn_lq4_window": [_DP, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
     "gdn_lq6_quantize": [_DP, _P, _I, _P, _P, _P, _P, _P, _P],
+    "kda_lq4_quantize": [_DP, _P, _I, _P, _P, _P, _P, _P, _P],
+    "kda_lq6_quantize": [_DP, _P, _I, _P, _P, _P, _P, _P, _P],
+    "kda_lq4_window": [_DP, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
+    "kda_lq6_window": [_DP, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
     "gdn_lq6_window": [_DP, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
     "kda_lq_window": [_DP, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
     "gdn_log_step_slots": [_DP, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
@@ -490,6 +494,28 @@ def gdn_lq6_window(W, pos, n_iter, Z, col_absmax, row_smooth, Kc, Uc, Kbuf, Ubuf
     """One decode step in the 6-bit, 4-token format (eq. 10; at pos = W - 1 the refit)."""
     return _lq_window("gdn_lq6_window", False, W, pos, n_iter, Z, col_absmax, row_smooth, Kc, Uc, Kbuf, Ubuf,
                       Gbuf, q, k, v, alpha, beta, y, bits=6)
+
+
+def kda_lq4_quantize(S, n_iter, Z, col_absmax, row_smooth, Kc, Uc):
+    """The 4-bit conversion for KDA states (the format does not depend on the gates)."""
+    _lq_quantize("kda_lq4_quantize", S, n_iter, Z, col_absmax, row_smooth, Kc, Uc, bits=4)
+
+
+def kda_lq6_quantize(S, n_iter, Z, col_absmax, row_smooth, Kc, Uc):
+    """The 6-bit conversion for KDA states (the format does not depend on the gates)."""
+    _lq_quantize("kda_lq6_quantize", S, n_iter, Z, col_absmax, row_smooth, Kc, Uc, bits=6)
+
+
+def kda_lq4_window(W, pos, n_iter, Z, col_absmax, row_smooth, Kc, Uc, Kbuf, Ubuf, Gbuf, q, k, v, d, beta, y):
+    """The 4-bit, 8-token step with KDA's per-key gate d (Gbuf holds [B, H, W, 128] gates)."""
+    return _lq_window("kda_lq4_window", True, W, pos, n_iter, Z, col_absmax, row_smooth, Kc, Uc, Kbuf, Ubuf,
+                      Gbuf, q, k, v, d, beta, y, bits=4)
+
+
+def kda_lq6_window(W, pos, n_iter, Z, col_absmax, row_smooth, Kc, Uc, Kbuf, Ubuf, Gbuf, q, k, v, d, beta, y):
+    """The 6-bit, 4-token step with KDA's per-key gate d (Gbuf holds [B, H, W, 128] gates)."""
+    return _lq_window("kda_lq6_window", True, W, pos, n_iter, Z, col_absmax, row_smooth, Kc, Uc, Kbuf, Ubuf,
+                      Gbuf, q, k, v, d, beta, y, bits=6)
 
 
 def kda_lq_window(W, pos, n_iter, Z, col_absmax, row_smooth, Kc, Uc, Kbuf, Ubuf, Gbuf, q, k, v, d, beta, y):

@@ -207,7 +207,7 @@ int lq_window_common(const char* fn, Kind m, const rsu_dims* dims, int W, int po
     w.Ubuf = Ubuf;
     w.Gbuf = Gbuf;
     const rsu::StepArgs a = step_args(heads, nullptr, q, k, v, gate, beta, y);
-    if (bits != 8) return launched(rsu::launch_lq_low_window(bits, a, w, stream), fn);
+    if (bits != 8) return launched(rsu::launch_lq_low_window(bits, a, w, m == Kind::kda, stream), fn);
     return launched(rsu::launch_lq_window(a, w, m == Kind::kda, stream), fn);
 }
 
@@ -342,6 +342,30 @@ int gdn_lq4_quantize(const rsu_dims* dims, const float* S, int n_iter, void* Z, 
 int gdn_lq6_quantize(const rsu_dims* dims, const float* S, int n_iter, void* Z, float* col_absmax, float* row_smooth,
                      void* Kc, void* Uc, rsu_stream_t stream) {
     return lq_low_quantize_common("gdn_lq6_quantize", 6, dims, S, n_iter, Z, col_absmax, row_smooth, Kc, Uc, stream);
+}
+
+int kda_lq4_quantize(const rsu_dims* dims, const float* S, int n_iter, void* Z, float* col_absmax, float* row_smooth,
+                     void* Kc, void* Uc, rsu_stream_t stream) {
+    return lq_low_quantize_common("kda_lq4_quantize", 4, dims, S, n_iter, Z, col_absmax, row_smooth, Kc, Uc, stream);
+}
+
+int kda_lq6_quantize(const rsu_dims* dims, const float* S, int n_iter, void* Z, float* col_absmax, float* row_smooth,
+                     void* Kc, void* Uc, rsu_stream_t stream) {
+    return lq_low_quantize_common("kda_lq6_quantize", 6, dims, S, n_iter, Z, col_absmax, row_smooth, Kc, Uc, stream);
+}
+
+int kda_lq4_window(const rsu_dims* dims, int W, int pos, int n_iter, void* Z, float* col_absmax, float* row_smooth,
+                   void* Kc, void* Uc, void* Kbuf, float* Ubuf, float* Gbuf, const void* q, const void* k,
+                   const void* v, const float* d, const float* beta, float* y, rsu_stream_t stream) {
+    return lq_window_common("kda_lq4_window", Kind::kda, dims, W, pos, n_iter, static_cast<int8_t*>(Z), col_absmax,
+                            row_smooth, Kc, Uc, Kbuf, Ubuf, Gbuf, q, k, v, d, beta, y, stream, 4);
+}
+
+int kda_lq6_window(const rsu_dims* dims, int W, int pos, int n_iter, void* Z, float* col_absmax, float* row_smooth,
+                   void* Kc, void* Uc, void* Kbuf, float* Ubuf, float* Gbuf, const void* q, const void* k,
+                   const void* v, const float* d, const float* beta, float* y, rsu_stream_t stream) {
+    return lq_window_common("kda_lq6_window", Kind::kda, dims, W, pos, n_iter, static_cast<int8_t*>(Z), col_absmax,
+                            row_smooth, Kc, Uc, Kbuf, Ubuf, Gbuf, q, k, v, d, beta, y, stream, 6);
 }
 
 int gdn_lq6_window(const rsu_dims* dims, int W, int pos, int n_iter, void* Z, float* col_absmax, float* row_smooth,

@@ -85,12 +85,12 @@ struct LqArgs {
 hipError_t launch_lq_quantize(int heads, const float* S, int n_iter, int8_t* Z, float* B, float* C,
                               void* Kc, void* Uc, hipStream_t stream);
 hipError_t launch_lq_window(const StepArgs& a, const LqArgs& w, bool per_key, hipStream_t stream);
-// The same format at low bit widths (GDN): bits = 4 with 8 tokens, Z [heads, 128, 64] packed
+// The same format at low bit widths (GDN, or KDA with per_key): bits = 4 with 8 tokens, Z [heads, 128, 64] packed
 // nibbles, Kc, Uc [heads, 8, 128] fp16; bits = 6 with 4 tokens, Z [heads, 128, 96] bytes (the
 // high parts as nibbles, then the low 2-bit parts), Kc, Uc [heads, 4, 128] fp16.
 hipError_t launch_lq_low_quantize(int bits, int heads, const float* S, int n_iter, void* Z, float* B, float* C,
                                   void* Kc, void* Uc, hipStream_t stream);
-hipError_t launch_lq_low_window(int bits, const StepArgs& a, const LqArgs& w, hipStream_t stream);
+hipError_t launch_lq_low_window(int bits, const StepArgs& a, const LqArgs& w, bool per_key, hipStream_t stream);
 
 // STEPQuant's packed state (4-bit codes with fp16 key-row and value-column factors):
 // Z [heads, 128, 16] words of 8 signed nibbles, R [heads, 128] and C [heads, 128] fp16,

@@ -1233,13 +1233,17 @@ __device__ __forceinline__ void sweep_low(const uint32_t (&zw)[8], const uint32_
         f32x4{add_pair32(q1[0], q1[2]), add_pair32(q2[0], q2[2]), add_pair32(q1[1], q1[3]), add_pair32(q2[1], q2[3])};
 }
 
-template <int kBits>
+// With per-key gates (KDA) the records' gates are staged in LDS and each lane forms the
+// decay products of its 8 keys as in the 8-bit step; the read vectors take the decay of
+// their own row.
+template <int kBits, bool kPerKey>
 __global__ __launch_bounds__(kThreads) void lq_low_step_kernel(
     int W, int pos, const uint32_t* __restrict__ Z, const float* __restrict__ Bcol, const float* __restrict__ Csm,
     const half_t* __restrict__ Kc, const half_t* __restrict__ Uc, bf16_t* __restrict__ Kbuf,
     float* __restrict__ Ubuf, float* __restrict__ Gbuf, const bf16_t* __restrict__ q,
     const bf16_t* __restrict__ k, const bf16_t* __restrict__ v, const float* __restrict__ gate,
     const float* __restrict__ beta, float* __restrict__ y) {
+    extern __shared__ __align__(16) float gs_lds[];   // KDA: the records' gates [pos][128]
     __shared__ f32x2 rowv[kD];
     __shared__ f32x2 coef[16];
     using Cfg = LowBits<kBits>;
@@ -1277,11 +1281,19 @@ __global__ __launch_bounds__(kThreads) void lq_low_step_kernel(
     half_t utv[kTh];
 #pragma unroll
     for (int e = 0; e < kTh; ++e) utv[e] = Uc[tok0 + (kTh * half + e) * kD + cc];
-    const float g_lane = lane < pos ? Gbuf[static_cast<size_t>(h) * W + lane] : 1.f;
+    float g_lane = 1.f;  // GDN: lane i holds the gate of record i
+    Stager<float, kPerKey ? 16 * kD : 8> sg;
+    if constexpr (kPerKey) sg.load(Gbuf + rec0, pos * kD, tid);
+    else if (lane < pos) g_lane = Gbuf[static_cast<size_t>(h) * W + lane];
     const uint4 kchw = *reinterpret_cast<const uint4*>(k + vec_off + 8 * ch);
     const uint4 qchw = *reinterpret_cast<const uint4*>(q + vec_off + 8 * ch);
+    f32x4 gch_lo = {1.f, 1.f, 1.f, 1.f}, gch_hi = {1.f, 1.f, 1.f, 1.f};  // KDA: current gates of the 8 keys
+    if constexpr (kPerKey) {
+        gch_lo = *reinterpret_cast<const f32x4*>(gate + vec_off + 8 * ch);
+        gch_hi = *reinterpret_cast<const f32x4*>(gate + vec_off + 8 * ch + 4);
+    }
     const float kr = load_in(k, vec_off + cc), qr = load_in(q, vec_off + cc);
-    const float gr = gate[h];
+    const float gr = kPerKey ? gate[vec_off + cc] : gate[h];
     const float cr = Csm[vec_off + cc];
     const float bcc = Bcol[vec_off + cc];
     const float vr = load_in(v, vec_off + cc);
@@ -1298,13 +1310,37 @@ __global__ __launch_bounds__(kThreads) void lq_low_step_kernel(
             zl[it] = 0u;
     }
 
-    // ---- decays (newest gate first): after record grp, and over the whole window so far
+    // ---- decays (newest gate first): after record grp, and over the whole window so far.
+    // Per key (KDA): Ge[e] after record grp and Gt[e] over the window for the lane's 8 keys,
+    // Gall for row cc; the current gate comes on top of each.
     float Gg = 1.f, Gall = 1.f;
-    for (int i = pos - 1; i >= 0; --i) {
-        const float gi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, g_lane), i));
-        Gg = i > grp ? Gg * gi : Gg;
-        Gall *= gi;
+    float Ge[kPerKey ? 8 : 1], Gt[kPerKey ? 8 : 1];
+    if constexpr (!kPerKey) {
+        for (int i = pos - 1; i >= 0; --i) {
+            const float gi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, g_lane), i));
+            Gg = i > grp ? Gg * gi : Gg;
+            Gall *= gi;
+        }
+    } else {
+        sg.store(gs_lds, tid);
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < 8; ++e) Ge[e] = Gt[e] = 1.f;
+        for (int i = pos - 1; i >= 0; --i) {
+            const f32x4 lo = *reinterpret_cast<const f32x4*>(gs_lds + i * kD + 8 * ch);
+            const f32x4 hi = *reinterpret_cast<const f32x4*>(gs_lds + i * kD + 8 * ch + 4);
+            const bool after = i > grp;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                Gt[e] *= lo[e];
+                Gt[e + 4] *= hi[e];
+                Ge[e] = after ? Ge[e] * lo[e] : Ge[e];
+                Ge[e + 4] = after ? Ge[e + 4] * hi[e] : Ge[e + 4];
+            }
+        }
+        for (int i = pos - 1; i >= 0; --i) Gall *= gs_lds[i * kD + cc];
     }
+    auto gcur = [&](int e) { return e < 4 ? gch_lo[e] : gch_hi[e - 4]; };
     const uint32_t kcw[4] = {kchw.x, kchw.y, kchw.z, kchw.w};
     const uint32_t qcw[4] = {qchw.x, qchw.y, qchw.z, qchw.w};
     auto bfe = [](const uint32_t (&w)[4], int e) {
@@ -1314,7 +1350,7 @@ __global__ __launch_bounds__(kThreads) void lq_low_step_kernel(
         float ck = 0.f, cq = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const float ej = bfe(kc, e) * (Gg * gr);
+            const float ej = bfe(kc, e) * (kPerKey ? Ge[e] * gcur(e) : Gg * gr);
             ck += ej * bfe(kcw, e);
             cq += ej * bfe(qcw, e);
         }
@@ -1327,7 +1363,7 @@ __global__ __launch_bounds__(kThreads) void lq_low_step_kernel(
         float ck = 0.f, cq = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const float ej = static_cast<float>(kt[e]) * (Gall * gr);
+            const float ej = static_cast<float>(kt[e]) * (kPerKey ? Gt[e] * gcur(e) : Gall * gr);
             ck += ej * bfe(kcw, e);
             cq += ej * bfe(qcw, e);
         }
@@ -1365,7 +1401,8 @@ __global__ __launch_bounds__(kThreads) void lq_low_step_kernel(
         const size_t rec = rec0 + static_cast<size_t>(pos) * kD;
         Ubuf[rec + c] = u;
         store_in(Kbuf, rec + c, kr);
-        if (c == 0) Gbuf[static_cast<size_t>(h) * W + pos] = gr;
+        if (kPerKey) Gbuf[rec + c] = gr;
+        else if (c == 0) Gbuf[static_cast<size_t>(h) * W + pos] = gr;
     }
 }
 
@@ -1625,6 +1662,242 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     lq_refit(L, s, n_iter, tid, Zh, Bcol + vec_off, Csm + vec_off, Kc + tok0, Uc + tok0);
 }
 
+// ---------------------------------------------------------------- 4 and 6 bits, per-key gates
+// KDA's boundary at low bit widths: the step as in the 8-bit KDA boundary (records, their
+// gates and keys staged in LDS as fp32, the decayed keys formed by one thread per key row
+// walking the records backwards) with the low-bit payload sweep; the record and token terms
+// are added per value column after the sweep. S_W forms on the matrix cores in fp32 in the
+// 8-bit KDA boundary's operand layout (the payload init decodes the staged low-bit codes of
+// columns 32 (l / 16) + 8 i + ct), passes through LDS into the refit's layout and is refitted
+// with low-bit codes. W (the refit's start) lies after the refit's arrays and the half state
+// in transit, inside the step arrays (written once they are dead); B / qmax of the old
+// payload follows both.
+template <int kBits>
+struct LowKdaLds {
+    using Cfg = LowBits<kBits>;
+    static constexpr int kStep = 3 * kKdaRec * kD + kD * Cfg::kZsStride + 2 * Cfg::kT * kD + 4 * kD * 2;
+    static constexpr int kRefit = RefitCfg<Cfg::kT, kBits>::kRegionFloats;
+    static constexpr int kW = kRefit > kTransitFloats ? kRefit : kTransitFloats;
+    static constexpr int kBscs = kStep > kW + Cfg::kT * kD ? kStep : kW + Cfg::kT * kD;
+    static constexpr int kTotal = kBscs + kD;
+    static_assert(kW % 4 == 0 && (3 * kKdaRec * kD + kD * Cfg::kZsStride + 2 * Cfg::kT * kD) % 2 == 0,
+                  "W must be 16-byte and red 8-byte aligned");
+};
+
+template <int kBits>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void lq_low_boundary_kda_kernel(
+    int W, int pos, int n_iter, uint32_t* __restrict__ Z, float* __restrict__ Bcol, float* __restrict__ Csm,
+    half_t* __restrict__ Kc, half_t* __restrict__ Uc, const bf16_t* __restrict__ Kbuf,
+    const float* __restrict__ Ubuf, const float* __restrict__ Gbuf, const bf16_t* __restrict__ q,
+    const bf16_t* __restrict__ k, const bf16_t* __restrict__ v, const float* __restrict__ gate,
+    const float* __restrict__ beta, float* __restrict__ y) {
+    using Cfg = LowBits<kBits>;
+    using Lds = LowKdaLds<kBits>;
+    constexpr int kT = Cfg::kT, kC = Cfg::kC, kZsStride = Cfg::kZsStride;
+    extern __shared__ __align__(16) float dyn_lds[];
+    __shared__ f32x2 rowv[kD];       // c_r Gamma_{1:W,r} (k_r, q_r) kReadScale
+    __shared__ f32x2 kq_row[kD];     // (k_r, q_r)
+    __shared__ f32x2 coef[kKdaRec];  // per record (E_j . k, E_j . q)
+    __shared__ f32x2 ctok[kT];       // per token ((Gamma Kt_t) . k, (Gamma Kt_t) . q)
+    __shared__ float kq_part[2];
+    __shared__ float zcoef[kD];      // c_r Gamma_{1:W,r}
+
+    float* KE = dyn_lds;                                            // [16][128]
+    float* Us = KE + kKdaRec * kD;                                  // [16][128]
+    float* Gs = Us + kKdaRec * kD;                                  // [16][128]
+    uint32_t* Zs = reinterpret_cast<uint32_t*>(Gs + kKdaRec * kD);  // [128][kZsStride]
+    float* Ktk = reinterpret_cast<float*>(Zs + kD * kZsStride);    // [kT][128] Gamma_{1:W} Kt
+    float* Utk = Ktk + kT * kD;                                     // [kT][128] Ut
+    f32x2* red = reinterpret_cast<f32x2*>(Utk + kT * kD);          // [4][128]
+    const RefitLds<kT, kBits> L(dyn_lds, dyn_lds + Lds::kW);
+    float* bscs = dyn_lds + Lds::kBscs;                             // B / qmax of the old payload
+
+    const int h = head_of_block(blockIdx.x, gridDim.x), tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
+    const int c16 = lane & 15, rl = lane >> 4;
+    const int r = tid & (kD - 1);
+    const bool first = tid < kD;
+    const size_t vec_off = static_cast<size_t>(h) * kD;
+    const size_t rec0 = static_cast<size_t>(h) * W * kD;
+    const size_t tok0 = static_cast<size_t>(h) * kT * kD;
+    uint32_t* Zh = Z + static_cast<size_t>(h) * kD * Cfg::kRowWords;
+
+    // ---- loads: records, gates, tokens and inputs first, then the codes
+    Stager<bf16_t, kKdaRec * kD> sk;
+    Stager<float, kKdaRec * kD> su;
+    Stager<float, kKdaRec * kD> sg;
+    sk.load(Kbuf + rec0, pos * kD, tid);
+    su.load(Ubuf + rec0, pos * kD, tid);
+    sg.load(Gbuf + rec0, pos * kD, tid);
+    half_t tokv[kT];  // token t at row / column r (threads < 128: keys; threads >= 128: values)
+#pragma unroll
+    for (int t = 0; t < kT; ++t) tokv[t] = (first ? Kc : Uc)[tok0 + t * kD + r];
+    const float kr = load_in(k, vec_off + r), qr = load_in(q, vec_off + r);
+    const float gr = gate[vec_off + r];
+    const float cr = Csm[vec_off + r];
+    const float bcc = Bcol[vec_off + r];
+    const float vr = load_in(v, vec_off + r);
+    const float bt = beta[h];
+    uint32_t zw[8], zl[8];
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+        const uint32_t* zrow = Zh + low_row(it, wave, rl) * Cfg::kRowWords;
+        zw[it] = __builtin_nontemporal_load(zrow + c16);
+        if constexpr (kBits == 6)
+            zl[it] = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(zrow + 16) + c16);
+        else
+            zl[it] = 0u;
+    }
+
+    sk.store(KE, tid);
+    su.store(Us, tid);
+    sg.store(Gs, tid);
+    for (int i = pos * kD + tid; i < kKdaRec * kD; i += kThreads) Us[i] = 0.f;  // rows pos .. 15
+    __syncthreads();
+
+    // ---- decayed keys in place (thread r < 128 walks key row r from the newest record),
+    // read vectors, token keys with the whole window's decay; token values from threads >= 128
+    if (first) {
+        float G = 1.f;
+        for (int j = pos - 1; j >= 0; --j) {
+            KE[j * kD + r] *= G * gr;
+            G *= Gs[j * kD + r];
+        }
+        const float gam = G * gr;  // Gamma_{1:W} at row r
+        const float c0 = cr * gam;
+        rowv[r] = f32x2{c0 * kr, c0 * qr} * Cfg::kReadScale;  // see sweep_low
+        kq_row[r] = f32x2{kr, qr};
+        zcoef[r] = c0;
+        KE[pos * kD + r] = kr;  // the current record: no decay after it
+        for (int j = pos + 1; j < kKdaRec; ++j) KE[j * kD + r] = 0.f;
+#pragma unroll
+        for (int t = 0; t < kT; ++t) Ktk[t * kD + r] = static_cast<float>(tokv[t]) * gam;
+        const float kq = wave_sum(kr * qr);
+        if (lane == 0) kq_part[wave] = kq;
+    } else {
+#pragma unroll
+        for (int t = 0; t < kT; ++t) Utk[t * kD + r] = static_cast<float>(tokv[t]);
+        bscs[r] = bcc * (1.f / Cfg::kQmax);
+    }
+    __syncthreads();
+
+    // ---- record and token coefficients: the 16 lanes of a DPP row reduce one (8 rows each)
+    {
+        const int chunk = tid & 15, j = tid >> 4;
+        auto dot8 = [&](const float* e) {
+            const f32x4 e0 = *reinterpret_cast<const f32x4*>(e + 8 * chunk);
+            const f32x4 e1 = *reinterpret_cast<const f32x4*>(e + 8 * chunk + 4);
+            const f32x2* kqr = kq_row + 8 * chunk;
+            f32x2 c = e0.x * kqr[0] + e0.y * kqr[1] + e0.z * kqr[2] + e0.w * kqr[3] + e1.x * kqr[4] +
+                      e1.y * kqr[5] + e1.z * kqr[6] + e1.w * kqr[7];
+            return f32x2{row16_sum(c.x), row16_sum(c.y)};
+        };
+        const f32x2 c = dot8(KE + (j < pos ? j : 0) * kD);
+        if (chunk == 0 && j < pos) coef[j] = c;
+        if (j < kT) {  // the first kT groups again (whole waves): the tokens
+            const f32x2 ct = dot8(Ktk + j * kD);
+            if (chunk == 0) ctok[j] = ct;
+        }
+    }
+    __syncthreads();
+
+    // ---- payload sweep; the codes staged for the payload init
+    sweep_low<kBits>(zw, zl, rowv, wave, lane, red + wave * kD);
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+        uint32_t* zs_row = Zs + low_row(it, wave, rl) * kZsStride;
+        zs_row[c16] = zw[it];
+        if constexpr (kBits == 6) reinterpret_cast<uint16_t*>(zs_row + 16)[c16] = static_cast<uint16_t>(zl[it]);
+    }
+    __syncthreads();
+
+    // ---- correction and output with the record and token terms of column c; u of this step
+    // becomes row pos of Us
+    if (first) {
+        const int c = tid;
+        f32x2 acc = (red[c] + red[kD + c] + red[2 * kD + c] + red[3 * kD + c]) * bscs[c];
+        for (int j = 0; j < pos; ++j) acc += coef[j] * Us[j * kD + c];
+#pragma unroll
+        for (int t = 0; t < kT; ++t) acc += ctok[t] * Utk[t * kD + c];
+        const float kq = kq_part[0] + kq_part[1];
+        const float u = bt * (vr - acc.x);
+        y[vec_off + c] = acc.y + u * kq;
+        Us[pos * kD + c] = u;
+    }
+    __syncthreads();
+
+    // ---- S_W on the matrix cores, both 16-row bands of the wave held in registers
+    const int lr = lane & 15, lq = lane >> 4;
+    f32x4 ua[kKdaRec / 4][2];
+#pragma unroll
+    for (int s4 = 0; s4 < kKdaRec / 4; ++s4) {
+        const float* src = Us + (4 * s4 + lq) * kD + 8 * lr;
+        ua[s4][0] = *reinterpret_cast<const f32x4*>(src);
+        ua[s4][1] = *reinterpret_cast<const f32x4*>(src + 4);
+    }
+    f32x4 utk[kC][2];
+#pragma unroll
+    for (int g = 0; g < kC; ++g) {
+        utk[g][0] = *reinterpret_cast<const f32x4*>(Utk + (4 * g + lq) * kD + 8 * lr);
+        utk[g][1] = *reinterpret_cast<const f32x4*>(Utk + (4 * g + lq) * kD + 8 * lr + 4);
+    }
+    f32x4 acc[2][8];
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+        const int row = 16 * (2 * wave + a) + lr;
+        float eb[kKdaRec / 4], kb[kC];
+#pragma unroll
+        for (int s4 = 0; s4 < kKdaRec / 4; ++s4) eb[s4] = KE[(4 * s4 + lq) * kD + row];
+#pragma unroll
+        for (int g = 0; g < kC; ++g) kb[g] = Ktk[(4 * g + lq) * kD + row];
+        const float zc = zcoef[row];
+        const uint32_t* zs_row = Zs + row * kZsStride;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {  // columns 32 lq + 8 i + ct: nibble word 4 lq + i, nibble ct
+            const uint32_t zn = zs_row[4 * lq + i];
+            const uint32_t zlo = kBits == 6 ? reinterpret_cast<const uint16_t*>(zs_row + 16)[4 * lq + i] : 0u;
+            const f32x4 b0 = *reinterpret_cast<const f32x4*>(bscs + 32 * lq + 8 * i);
+            const f32x4 b1 = *reinterpret_cast<const f32x4*>(bscs + 32 * lq + 8 * i + 4);
+#pragma unroll
+            for (int ct = 0; ct < 8; ++ct) {
+                int z = static_cast<int>(zn << (28 - 4 * ct)) >> 28;
+                if constexpr (kBits == 6) z = 4 * z + static_cast<int>((zlo >> (2 * ct)) & 3u);
+                acc[a][ct][i] = static_cast<float>(z) * ((ct < 4 ? b0[ct] : b1[ct - 4]) * zc);
+            }
+        }
+#pragma unroll
+        for (int s4 = 0; s4 < kKdaRec / 4; ++s4)
+#pragma unroll
+            for (int ct = 0; ct < 8; ++ct)
+                acc[a][ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(ua[s4][ct / 4][ct % 4], eb[s4], acc[a][ct], 0, 0, 0);
+#pragma unroll
+        for (int g = 0; g < kC; ++g)
+#pragma unroll
+            for (int ct = 0; ct < 8; ++ct)
+                acc[a][ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(utk[g][ct / 4][ct % 4], kb[g], acc[a][ct], 0, 0, 0);
+    }
+    __syncthreads();  // every read of the step-phase arrays is done: the region holds S in halves, and W
+    if (!first)
+#pragma unroll
+        for (int hh = 0; hh < kC; ++hh)
+            L.W[r * kC + hh] = f32x4{static_cast<float>(tokv[4 * hh]), static_cast<float>(tokv[4 * hh + 1]),
+                                     static_cast<float>(tokv[4 * hh + 2]), static_cast<float>(tokv[4 * hh + 3])};
+    // this layout: acc[a][ct][i] is row 16(2w + a) + (l & 15), column 32(l >> 4) + 8i + ct
+    auto write = [&](float* base, int r0) {
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh)
+                    state_unit(base, r0 + 16 * a + lr, 8 * lq + 2 * i + hh) =
+                        f32x4{acc[a][4 * hh][i], acc[a][4 * hh + 1][i], acc[a][4 * hh + 2][i], acc[a][4 * hh + 3][i]};
+    };
+    f32x4 s[16];
+    state_to_refit(dyn_lds, write, s, wave, lane);  // then the region is free for the refit
+    lq_refit(L, s, n_iter, tid, Zh, Bcol + vec_off, Csm + vec_off, Kc + tok0, Uc + tok0);
+}
+
 // ---------------------------------------------------------------- launchers
 static hipError_t set_lds(const void* fn, int floats) {
     return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -1690,11 +1963,11 @@ static hipError_t launch_low_quantize(int heads, const float* S, int n_iter, voi
     return hipGetLastError();
 }
 
-template <int kBits>
+template <int kBits, bool kPerKey>
 static hipError_t launch_low_window(const StepArgs& a, const LqArgs& w, hipStream_t stream) {
     if (w.pos == w.W - 1) {
-        constexpr auto kernel = lq_low_boundary_kernel<kBits>;
-        constexpr int floats = LowBitsLds<kBits>::kBoundary;
+        constexpr auto kernel = kPerKey ? lq_low_boundary_kda_kernel<kBits> : lq_low_boundary_kernel<kBits>;
+        constexpr int floats = kPerKey ? LowKdaLds<kBits>::kTotal : LowBitsLds<kBits>::kBoundary;
         static const hipError_t attr = set_lds(reinterpret_cast<const void*>(kernel), floats);
         if (attr != hipSuccess) return attr;
         hipLaunchKernelGGL(kernel, dim3(a.heads), dim3(kThreads), sizeof(float) * floats,
@@ -1704,7 +1977,8 @@ static hipError_t launch_low_window(const StepArgs& a, const LqArgs& w, hipStrea
                            static_cast<const bf16_t*>(a.k), static_cast<const bf16_t*>(a.v), a.gate, a.beta, a.y);
         return hipGetLastError();
     }
-    hipLaunchKernelGGL(lq_low_step_kernel<kBits>, dim3(a.heads), dim3(kThreads), 0, stream, w.W, w.pos,
+    hipLaunchKernelGGL((lq_low_step_kernel<kBits, kPerKey>), dim3(a.heads), dim3(kThreads),
+                       kPerKey ? sizeof(float) * w.pos * kD : 0, stream, w.W, w.pos,
                        reinterpret_cast<const uint32_t*>(w.Z), w.B, w.C, static_cast<const half_t*>(w.Kc),
                        static_cast<const half_t*>(w.Uc), static_cast<bf16_t*>(w.Kbuf), w.Ubuf, w.Gbuf,
                        static_cast<const bf16_t*>(a.q), static_cast<const bf16_t*>(a.k),
@@ -1718,8 +1992,9 @@ hipError_t launch_lq_low_quantize(int bits, int heads, const float* S, int n_ite
                      : launch_low_quantize<6>(heads, S, n_iter, Z, B, C, Kc, Uc, stream);
 }
 
-hipError_t launch_lq_low_window(int bits, const StepArgs& a, const LqArgs& w, hipStream_t stream) {
-    return bits == 4 ? launch_low_window<4>(a, w, stream) : launch_low_window<6>(a, w, stream);
+hipError_t launch_lq_low_window(int bits, const StepArgs& a, const LqArgs& w, bool per_key, hipStream_t stream) {
+    if (per_key) return bits == 4 ? launch_low_window<4, true>(a, w, stream) : launch_low_window<6, true>(a, w, stream);
+    return bits == 4 ? launch_low_window<4, false>(a, w, stream) : launch_low_window<6, false>(a, w, stream);
 }
 
 }  // namespace rsu

@@ -330,9 +330,11 @@ def run_lq(w: wl.Workload, n_iter: int = 1, n_iter0: int = 8, sample: int | None
     quantize = m.kda_lq_quantize if w.per_key_gate else m.gdn_lq_quantize
     window = m.kda_lq_window if w.per_key_gate else m.gdn_lq_window
     if w.bits == 4:
-        quantize, window = m.gdn_lq4_quantize, m.gdn_lq4_window
+        quantize, window = ((m.kda_lq4_quantize, m.kda_lq4_window) if w.per_key_gate else
+                            (m.gdn_lq4_quantize, m.gdn_lq4_window))
     if w.bits == 6:
-        quantize, window = m.gdn_lq6_quantize, m.gdn_lq6_window
+        quantize, window = ((m.kda_lq6_quantize, m.kda_lq6_window) if w.per_key_gate else
+                            (m.gdn_lq6_quantize, m.gdn_lq6_window))
     qmax = lqo.qmax_of(w.bits)
     r = 8 if w.bits == 4 else 4
     quantize(Sd, n_iter0, buf["Z"], buf["B"], buf["C"], buf["Kc"], buf["Uc"])

@@ -151,6 +151,23 @@ def test_lq6_b256_h48_full_size_sampled():
     _check(run_lq(w, n_iter=1, sample=64, steps=48), w.name)
 
 
+@pytest.mark.parametrize("cid", [17, 18])
+@pytest.mark.parametrize("W,B,H,n_iter", [(16, 2, 5, 1), (16, 3, 4, 2), (7, 2, 3, 1), (1, 2, 2, 0)])
+def test_lq_low_bit_kda_windows_small(cid, W, B, H, n_iter):
+    """KDA's per-key gates at 4 bits (8 tokens) and 6 bits (4 tokens)."""
+    w = wl.custom(wl.WORKLOADS[cid], B=B, H=H, W=W, steps=2 * W + min(W, 3))
+    _check(run_lq(w, n_iter=n_iter), f"kda {w.bits}-bit W={W} B={B} H={H} n_iter={n_iter}")
+
+
+@pytest.mark.parametrize("cid", [17, 18])
+def test_lq_low_bit_kda_b128_h32_full_size_sampled(cid):
+    """The KDA LeapQuant workloads at 4 and 6 bits (B=128, H=32, W=16), 64 sampled heads,
+    3 windows."""
+    w = wl.WORKLOADS[cid]
+    say(f"[lq] {w.name}: full size, 64 sampled heads, 48 steps")
+    _check(run_lq(w, n_iter=1, sample=64, steps=48), w.name)
+
+
 @pytest.mark.parametrize("n_iter0", [0, 3])
 def test_lq_quantize_start_iterations(n_iter0):
     w = wl.custom(wl.WORKLOADS[6], B=2, H=3, W=16, steps=0)

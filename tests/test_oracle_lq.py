@@ -158,14 +158,18 @@ def test_eq10_readout_equals_dense_decoding_from_the_represented_state():
         recs.append((k[0], u, g[0]))
 
 
-def test_eq10_readout_with_per_key_decays_equals_dense_kda_decoding():
+@pytest.mark.parametrize("bits,r", [(8, 4), (6, 4), (4, 8)])
+def test_eq10_readout_with_per_key_decays_equals_dense_kda_decoding(bits, r):
     """Eq. 10 with KDA's per-key gates: Gamma is diagonal over the key rows, so it scales
     the read vector row by row (payload and token keys alike) and each record's key;
-    term by term this equals dense KDA decoding from the represented state."""
+    term by term this equals dense KDA decoding from the represented state (at each code
+    width: /127 with 4 tokens, /31 with 4, /7 with 8)."""
     d, W = 128, 5
-    S = _gapped(noise=0.05)
-    rep = lq.boundary(S, lq.walsh_start(), 1)
-    S0 = lq.represent(rep["Z"], rep["B"], rep["c"], rep["K16"], rep["U16"])
+    qmax = lq.qmax_of(bits)
+    S = _gapped(noise=0.05) if r == 4 else _gapped8(noise=0.05)
+    rep = lq.boundary(S, lq.walsh_start(r=r), 1, qmax=qmax)
+    assert np.abs(rep["Z"]).max() == qmax
+    S0 = lq.represent(rep["Z"], rep["B"], rep["c"], rep["K16"], rep["U16"], qmax=qmax)
     Sd = S0[None].copy()
     recs = []
     for t in range(W):
@@ -176,13 +180,13 @@ def test_eq10_readout_with_per_key_decays_equals_dense_kda_decoding():
         g = RNG.uniform(0.8, 1.0, (1, d))
         b = np.array([RNG.uniform(0.0, 1.0)])
         y_dense = oracle.dense_step(Sd, q, k, v, g, b)[0]
-        gam_all = np.prod([r[2] for r in recs] + [g[0]], axis=0)          # per key row
+        gam_all = np.prod([rr[2] for rr in recs] + [g[0]], axis=0)        # per key row
 
         def read(x):
-            out = (rep["B"] / 127.0) * (rep["Z"].astype(np.float64).T @ (rep["c"] * gam_all * x))
+            out = (rep["B"] / float(qmax)) * (rep["Z"].astype(np.float64).T @ (rep["c"] * gam_all * x))
             out += rep["U16"] @ (rep["K16"].T @ (gam_all * x))
             for j, (kj, uj, _) in enumerate(recs):
-                dec = np.prod([r[2] for r in recs[j + 1:]] + [g[0]], axis=0)
+                dec = np.prod([rr[2] for rr in recs[j + 1:]] + [g[0]], axis=0)
                 out += uj * (kj @ (dec * x))
             return out
         p = read(k[0])

@@ -85,6 +85,11 @@ WORKLOADS = {
     # LeapQuant's format at 6 bits (4 tokens) on the int8 workload's inputs (same seed as 4)
     16: Workload(4, "gdn_lq6_window_b256_h48_w16", "gdn", "lq_window", 256, 48, 256, "bf16", 0.90, 0.999,
                  W=16, outliers=True, bits=6),
+    # LeapQuant's format at 4 and 6 bits with KDA gates on the KDA workload's shape (same seed as 9)
+    17: Workload(9, "kda_lq4_window_b128_h32_w16", "kda", "lq_window", 128, 32, 256, "bf16", 0.80, 1.0,
+                 W=16, outliers=True, bits=4),
+    18: Workload(9, "kda_lq6_window_b128_h32_w16", "kda", "lq_window", 128, 32, 256, "bf16", 0.80, 1.0,
+                 W=16, outliers=True, bits=6),
     # LeapQuant's format with KDA gates on the KDA workload's shape (same outliers as 4)
     9: Workload(9, "kda_lq_window_b128_h32_w16", "kda", "lq_window", 128, 32, 256, "bf16", 0.80, 1.0,
                 W=16, outliers=True),
