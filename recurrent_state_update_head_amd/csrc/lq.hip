@@ -37,18 +37,8 @@ __device__ __forceinline__ f32x4 unpack_codes(uint32_t w) {
 
 
 // ---------------------------------------------------------------- the refit
-// The refit holds the state in registers: lane l of wave w owns the 4 columns of unit
-// uu = 8 w + (l & 7) (columns 4 uu .. 4 uu + 3) in the 16 rows 8 it + (l >> 3). Products
-// with V sum over the 8 column lanes of a row (DPP) and then over the 4 waves (LDS);
-// products with S^T and the per-column absmax sum over the 8 row lanes of a column
-// group inside the wave. kT tokens (4 at 8 bits, 8 at 4 bits) are kT / 4 f32x4 per row
-// or column of V, Y, W, Kr and Ur (token t of entry i in element t % 4 of chunk t / 4).
-//
-// LDS of the refit, in floats. A region of kRegionFloats holds the staged codes (128 rows
-// of kCodeStride words) and V, Y, Kr, Ur [128 x kT], the per-wave partials Yp [4][128 x kT]
-// (also the per-wave row sums of |R|) and the row factors 1 / c [128]. W [128 x kT], the
-// start vectors and the S^T Y products, lies outside the region: the boundary writes it
-// before its state region (which the refit region reuses) is free.
+// Sizes of the fitted format: kT tokens (4 at 8 and 6 bits, 8 at 4 bits), codes of kBits bits,
+// and the LDS staging of the code rows (whole rows leave the workgroup together).
 template <int kT, int kBits>
 struct RefitCfg {
     static_assert((kT == 4 || kT == 8) && (kBits == 8 || kBits == 6 || kBits == 4), "4 or 8 tokens, 8-, 6- or 4-bit codes");
@@ -57,32 +47,7 @@ struct RefitCfg {
     static constexpr int kRowWords = kD * kBits / 32;        // 32 (8-bit), 24 (6-bit) or 16 (4-bit) words per row
     // staged row stride: 16-byte rows, 8 rows span the banks
     static constexpr int kCodeStride = kBits == 8 ? 40 : kBits == 6 ? 28 : 20;
-    static constexpr int kRegionFloats = kD * kCodeStride + 4 * kT * kD + 4 * kT * kD + kD;
-    static constexpr int kWFloats = kT * kD;
 };
-
-template <int kT, int kBits>
-struct RefitLds {
-    using Cfg = RefitCfg<kT, kBits>;
-    static constexpr int kC = Cfg::kC;
-    uint32_t* codes;
-    f32x4 *V, *Y, *Kr, *Ur, *Yp, *W;
-    float* ic;
-    __device__ RefitLds(float* region, float* w_area)
-        : codes(reinterpret_cast<uint32_t*>(region)),
-          V(reinterpret_cast<f32x4*>(region + kD * Cfg::kCodeStride)), Y(V + kD * kC), Kr(Y + kD * kC),
-          Ur(Kr + kD * kC), Yp(Ur + kD * kC), W(reinterpret_cast<f32x4*>(w_area)),
-          ic(reinterpret_cast<float*>(Yp + 4 * kD * kC)) {}
-    __device__ float* Ap() const { return reinterpret_cast<float*>(Yp); }
-};
-
-// Sum over the 8 lanes that differ in lane bits 0..2 (quad sums, then the mirrored
-// quad inside each half-row of 8 lanes).
-__device__ __forceinline__ float sum_col_lanes(float x) {
-    x += dpp<kDppXor1>(x);
-    x += dpp<kDppXor2>(x);
-    return x + dpp<kDppHalfMirror>(x);
-}
 
 // y + a x and a x element by element, written without a splat of a: the refit's state
 // is invariant across the fit's iterations, and splats of it would be hoisted out of the
@@ -91,15 +56,6 @@ __device__ __forceinline__ f32x4 axpy(float a, f32x4 x, f32x4 y) {
     return f32x4{fmaf(a, x.x, y.x), fmaf(a, x.y, y.y), fmaf(a, x.z, y.z), fmaf(a, x.w, y.w)};
 }
 __device__ __forceinline__ f32x4 scale(float a, f32x4 x) { return f32x4{a * x.x, a * x.y, a * x.z, a * x.w}; }
-
-__device__ __forceinline__ float max_row_lanes(float x) {
-    x = fmaxf(x, dpp<kDppRor8>(x));
-    float a, b;
-    swap16(x, a, b);
-    x = fmaxf(a, b);
-    swap32(x, a, b);
-    return fmaxf(a, b);
-}
 
 // Code of w = x * (qmax / B): round half to even with one fp32 add (the low mantissa bits
 // of w + 1.5 * 2^23 are the integer), clamped to [-qmax, qmax]; the returned bits are
@@ -114,318 +70,6 @@ __device__ __forceinline__ uint32_t lq_code_t(float w) {
     constexpr int kQ = (1 << (kBits - 1)) - 1;
     const int bits = __float_as_int(w + kMagic);
     return static_cast<uint32_t>(min(max(bits, 0x4B400000 - kQ), 0x4B400000 + kQ));
-}
-
-// W -> V: modified Gram-Schmidt over the kT columns in order (wave 0; lane l holds rows
-// 2l and 2l + 1); a column with zero norm after the projections stays zero.
-template <int kT, int kBits>
-__device__ __forceinline__ void refit_mgs(const RefitLds<kT, kBits>& L, int wave, int lane) {
-    constexpr int kC = kT / 4;
-    if (wave == 0) {
-        float a[kT], b[kT];
-#pragma unroll
-        for (int h = 0; h < kC; ++h) {
-            const f32x4 wa = L.W[(2 * lane) * kC + h], wb = L.W[(2 * lane + 1) * kC + h];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                a[4 * h + e] = wa[e];
-                b[4 * h + e] = wb[e];
-            }
-        }
-#pragma unroll
-        for (int t = 0; t < kT; ++t) {
-#pragma unroll
-            for (int g = 0; g < t; ++g) {
-                const float d = wave_sum(a[g] * a[t] + b[g] * b[t]);
-                a[t] -= d * a[g];
-                b[t] -= d * b[g];
-            }
-            const float n2 = wave_sum(a[t] * a[t] + b[t] * b[t]);
-            const float inv = n2 > 0.f ? 1.f / sqrtf(n2) : 0.f;
-            a[t] *= inv;
-            b[t] *= inv;
-        }
-#pragma unroll
-        for (int h = 0; h < kC; ++h) {
-            L.V[(2 * lane) * kC + h] = f32x4{a[4 * h], a[4 * h + 1], a[4 * h + 2], a[4 * h + 3]};
-            L.V[(2 * lane + 1) * kC + h] = f32x4{b[4 * h], b[4 * h + 1], b[4 * h + 2], b[4 * h + 3]};
-        }
-    }
-    __syncthreads();
-}
-
-// Y = S V. A lane's kT partial sums for one row (its 4 columns against the kT columns of
-// V) are summed over the row's 8 lanes by a transposing butterfly: at each of the lane
-// exchanges i^1, i^2 and i^7 (the last one within each group of 8) a lane keeps half of its
-// values and adds the partner's copy of that half, so the 8 lanes end with one token each
-// after kT/2 + kT/4 + 1 adds instead of 3 kT. For the halves to match, lane bits b0..b2 give
-// each lane its own token order: value i holds token i ^ sv_token_perm (at 4 tokens the last
-// exchange is a plain sum, and lanes l and l^7 hold the same token).
-template <int kT>
-__device__ __forceinline__ int sv_token_perm(int lane) {
-    const int b0 = lane & 1, b1 = (lane >> 1) & 1, b2 = (lane >> 2) & 1;
-    return (kT / 2) * (b0 ^ b2) + (kT / 4) * (b1 ^ b2) + (kT == 8 ? b2 : 0);
-}
-
-template <int kT, int kBits>
-__device__ __forceinline__ void refit_sv(const RefitLds<kT, kBits>& L, const f32x4 (&s)[16], int wave, int lane,
-                                         int tid) {
-    constexpr int kC = kT / 4;
-    const int uu = 8 * wave + (lane & 7), ro = lane >> 3;
-    const int tp = sv_token_perm<kT>(lane);
-    const float* Vf = reinterpret_cast<const float*>(L.V);
-    float vp[4][kT];
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-#pragma unroll
-        for (int i = 0; i < kT; ++i) vp[e][i] = Vf[(4 * uu + e) * kT + (i ^ tp)];
-    float* Ypf = reinterpret_cast<float*>(L.Yp);
-#pragma unroll
-    for (int it = 0; it < 16; ++it) {
-        float p[kT];
-#pragma unroll
-        for (int i = 0; i < kT; ++i)
-            p[i] = fmaf(s[it].w, vp[3][i], fmaf(s[it].z, vp[2][i], fmaf(s[it].y, vp[1][i], s[it].x * vp[0][i])));
-        float q[kT / 2];
-#pragma unroll
-        for (int i = 0; i < kT / 2; ++i) q[i] = p[i] + dpp<kDppXor1>(p[i + kT / 2]);
-        float r[kT / 4];
-#pragma unroll
-        for (int i = 0; i < kT / 4; ++i) r[i] = q[i] + dpp<kDppXor2>(q[i + kT / 4]);
-        const float t = r[0] + dpp<kDppHalfMirror>(r[kT / 4 - 1]);
-        Ypf[(wave * kD + 8 * it + ro) * kT + tp] = t;
-    }
-    __syncthreads();
-    if (tid < kD)
-#pragma unroll
-        for (int h = 0; h < kC; ++h)
-            L.Y[tid * kC + h] = (L.Yp[tid * kC + h] + L.Yp[(kD + tid) * kC + h]) +
-                                (L.Yp[(2 * kD + tid) * kC + h] + L.Yp[(3 * kD + tid) * kC + h]);
-    __syncthreads();
-}
-
-
-// W = S^T Y. A lane's 4 kT partial sums (its 4 columns against the kT columns of Y, over its
-// 16 rows) are summed over the 8 row lanes of the column group by a transposing butterfly:
-// over lane^8 (row_ror:8) the two token halves, then over lane^16 and lane^32 the column
-// pairs (e, e+2) and (e, e+1) with the swaps above. A lane with bit 3 set reads Y's token
-// halves in swapped order so that the first exchange pairs equal tokens. The lane ends with
-// tokens kT/2 b3 .. +kT/2-1 of column 4 uu + 2 b4 + b5.
-template <int kT, int kBits>
-__device__ __forceinline__ void refit_sty(const RefitLds<kT, kBits>& L, const f32x4 (&s)[16], int wave, int lane) {
-    constexpr int kC = kT / 4, kJ = kT / 2;
-    const int uu = 8 * wave + (lane & 7), ro = lane >> 3;
-    const int b3 = ro & 1, b4 = (ro >> 1) & 1, b5 = ro >> 2;
-    f32x4 acc[4][kC];
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-#pragma unroll
-        for (int h = 0; h < kC; ++h) acc[e][h] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int it = 0; it < 16; ++it) {
-#pragma unroll
-        for (int h = 0; h < kC; ++h) {
-            f32x4 yv;
-            if constexpr (kT == 8) {
-                yv = L.Y[(8 * it + ro) * kC + (h ^ b3)];
-            } else {
-                const f32x2* Y2 = reinterpret_cast<const f32x2*>(L.Y);
-                const f32x2 lo = Y2[(8 * it + ro) * 2 + b3], hi = Y2[(8 * it + ro) * 2 + (b3 ^ 1)];
-                yv = f32x4{lo.x, lo.y, hi.x, hi.y};
-            }
-            acc[0][h] = axpy(s[it].x, yv, acc[0][h]);
-            acc[1][h] = axpy(s[it].y, yv, acc[1][h]);
-            acc[2][h] = axpy(s[it].z, yv, acc[2][h]);
-            acc[3][h] = axpy(s[it].w, yv, acc[3][h]);
-        }
-    }
-    float ra[4][kJ];
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-#pragma unroll
-        for (int j = 0; j < kJ; ++j)
-            ra[e][j] = acc[e][0][j] + dpp<kDppRor8>(kT == 8 ? acc[e][kC - 1][j] : acc[e][0][(j + 2) & 3]);
-    float rb[2][kJ];
-#pragma unroll
-    for (int e = 0; e < 2; ++e)
-#pragma unroll
-        for (int j = 0; j < kJ; ++j) rb[e][j] = add_pair16(ra[e][j], ra[e + 2][j]);
-    float* Wf = reinterpret_cast<float*>(L.W) + (4 * uu + 2 * b4 + b5) * kT + kJ * b3;
-    if constexpr (kT == 8) {
-        *reinterpret_cast<f32x4*>(Wf) = f32x4{add_pair32(rb[0][0], rb[1][0]), add_pair32(rb[0][1], rb[1][1]),
-                                               add_pair32(rb[0][2], rb[1][2]), add_pair32(rb[0][3], rb[1][3])};
-    } else {
-        *reinterpret_cast<f32x2*>(Wf) = f32x2{add_pair32(rb[0][0], rb[1][0]), add_pair32(rb[0][1], rb[1][1])};
-    }
-    __syncthreads();
-}
-
-// k . u over the kT tokens of one row (k) and one column (u)
-template <int kC>
-__device__ __forceinline__ float tok_dot(const f32x4 (&k)[kC], const f32x4 (&u)[kC]) {
-    float d = k[0].x * u[0].x + k[0].y * u[0].y + k[0].z * u[0].z + k[0].w * u[0].w;
-#pragma unroll
-    for (int h = 1; h < kC; ++h) d += k[h].x * u[h].x + k[h].y * u[h].y + k[h].z * u[h].z + k[h].w * u[h].w;
-    return d;
-}
-
-// The refit of one head. On entry s holds the lane's part of the state and W the start
-// vectors; every thread of the workgroup calls it. Writes the codes (Zh: the head's
-// payload as 32-bit words), B, c and the fp16 tokens [kT][128].
-template <int kT, int kBits>
-__device__ __forceinline__ void lq_refit(const RefitLds<kT, kBits>& L, f32x4 (&s)[16], int n_iter, int tid,
-                                         uint32_t* __restrict__ Zh, float* __restrict__ Bh,
-                                         float* __restrict__ Ch, half_t* __restrict__ Kh,
-                                         half_t* __restrict__ Uh) {
-    using Cfg = RefitCfg<kT, kBits>;
-    constexpr int kC = Cfg::kC;
-    const int wave = tid >> 6, lane = tid & 63;
-    const int uu = 8 * wave + (lane & 7), ro = lane >> 3;
-    refit_mgs(L, wave, lane);
-    for (int it = 0; it < n_iter; ++it) {
-        refit_sv(L, s, wave, lane, tid);
-        refit_sty(L, s, wave, lane);
-        refit_mgs(L, wave, lane);
-    }
-    refit_sv(L, s, wave, lane, tid);  // Kt = S V
-
-    // fp16 tokens (stored), and their exact fp32 values for the residual
-    if (tid < kD) {
-#pragma unroll
-        for (int h = 0; h < kC; ++h) {
-            const f32x4 kv = L.Y[tid * kC + h], uv = L.V[tid * kC + h];
-            f32x4 kr, ur;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const half_t kh = static_cast<half_t>(kv[e]);
-                const half_t uh = static_cast<half_t>(uv[e]);
-                kr[e] = static_cast<float>(kh);
-                ur[e] = static_cast<float>(uh);
-                Kh[(4 * h + e) * kD + tid] = kh;
-                Uh[(4 * h + e) * kD + tid] = uh;
-            }
-            L.Kr[tid * kC + h] = kr;
-            L.Ur[tid * kC + h] = ur;
-        }
-    }
-    __syncthreads();
-
-    // residual R = S - Kt Ut^T in registers, and each row's sum of |R|
-    {
-        f32x4 u0[kC], u1[kC], u2[kC], u3[kC];
-#pragma unroll
-        for (int h = 0; h < kC; ++h) {
-            u0[h] = L.Ur[(4 * uu) * kC + h];
-            u1[h] = L.Ur[(4 * uu + 1) * kC + h];
-            u2[h] = L.Ur[(4 * uu + 2) * kC + h];
-            u3[h] = L.Ur[(4 * uu + 3) * kC + h];
-        }
-        float* Ap = L.Ap();
-#pragma unroll
-        for (int it = 0; it < 16; ++it) {
-            f32x4 kr[kC];
-#pragma unroll
-            for (int h = 0; h < kC; ++h) kr[h] = L.Kr[(8 * it + ro) * kC + h];
-            s[it].x -= tok_dot<kC>(kr, u0);
-            s[it].y -= tok_dot<kC>(kr, u1);
-            s[it].z -= tok_dot<kC>(kr, u2);
-            s[it].w -= tok_dot<kC>(kr, u3);
-            const float a = sum_col_lanes((fabsf(s[it].x) + fabsf(s[it].y)) + (fabsf(s[it].z) + fabsf(s[it].w)));
-            if ((lane & 7) == 0) Ap[wave * kD + 8 * it + ro] = a;
-        }
-        __syncthreads();
-        if (tid < kD) {
-            const float asum = (Ap[tid] + Ap[kD + tid]) + (Ap[2 * kD + tid] + Ap[3 * kD + tid]);
-            const float cs = fmaxf(sqrtf(asum * (1.f / kD)), kSmoothFloor);
-            Ch[tid] = cs;
-            L.ic[tid] = 1.f / cs;
-        }
-        __syncthreads();
-    }
-
-    // X = R / c, the per-value-channel absmax B and the code scale qmax / B
-    f32x4 m = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int it = 0; it < 16; ++it) {
-        s[it] *= L.ic[8 * it + ro];
-        m = f32x4{fmaxf(m.x, fabsf(s[it].x)), fmaxf(m.y, fabsf(s[it].y)), fmaxf(m.z, fabsf(s[it].z)),
-                  fmaxf(m.w, fabsf(s[it].w))};
-    }
-    m = f32x4{max_row_lanes(m.x), max_row_lanes(m.y), max_row_lanes(m.z), max_row_lanes(m.w)};
-    f32x4 sc;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) sc[e] = m[e] > 0.f ? __fdiv_rn(static_cast<float>(Cfg::kQmax), m[e]) : 0.f;
-    if (ro == 0) *reinterpret_cast<f32x4*>(Bh + 4 * uu) = m;
-
-    // codes of the lane's unit in each of its rows, staged so that whole rows leave together
-    if constexpr (kBits == 8) {
-#pragma unroll
-        for (int it = 0; it < 16; ++it)
-            L.codes[(8 * it + ro) * Cfg::kCodeStride + uu] =
-                pack_low_bytes(lq_code_t<8>(s[it].x * sc.x), lq_code_t<8>(s[it].y * sc.y),
-                               lq_code_t<8>(s[it].z * sc.z), lq_code_t<8>(s[it].w * sc.w));
-    } else if constexpr (kBits == 4) {  // four nibbles: half of the row's word for columns 8 (uu / 2) .. +7
-        uint16_t* c16 = reinterpret_cast<uint16_t*>(L.codes);
-#pragma unroll
-        for (int it = 0; it < 16; ++it)
-            c16[(8 * it + ro) * 2 * Cfg::kCodeStride + uu] = static_cast<uint16_t>(
-                (lq_code_t<4>(s[it].x * sc.x) & 0xfu) | ((lq_code_t<4>(s[it].y * sc.y) & 0xfu) << 4) |
-                ((lq_code_t<4>(s[it].z * sc.z) & 0xfu) << 8) | ((lq_code_t<4>(s[it].w * sc.w) & 0xfu) << 12));
-    } else {  // the four high parts as nibbles (bytes 0..63 of the row), the low parts in byte 64 + uu
-        uint16_t* c16 = reinterpret_cast<uint16_t*>(L.codes);
-        uint8_t* c8 = reinterpret_cast<uint8_t*>(L.codes);
-#pragma unroll
-        for (int it = 0; it < 16; ++it) {
-            const int row = 8 * it + ro;
-            const uint32_t z0 = lq_code_t<6>(s[it].x * sc.x), z1 = lq_code_t<6>(s[it].y * sc.y);
-            const uint32_t z2 = lq_code_t<6>(s[it].z * sc.z), z3 = lq_code_t<6>(s[it].w * sc.w);
-            c16[row * 2 * Cfg::kCodeStride + uu] = static_cast<uint16_t>(
-                ((z0 >> 2) & 0xfu) | (((z1 >> 2) & 0xfu) << 4) | (((z2 >> 2) & 0xfu) << 8) | (((z3 >> 2) & 0xfu) << 12));
-            c8[row * 4 * Cfg::kCodeStride + 64 + uu] =
-                static_cast<uint8_t>((z0 & 3u) | ((z1 & 3u) << 2) | ((z2 & 3u) << 4) | ((z3 & 3u) << 6));
-        }
-    }
-    __syncthreads();
-    constexpr int kQuads = Cfg::kRowWords / 4;  // 16-byte pieces per row
-#pragma unroll
-    for (int mm = 0; mm < kD * kQuads / kThreads; ++mm) {
-        const int qd = tid + kThreads * mm;
-        const int row = qd / kQuads, d = 4 * (qd % kQuads);
-        const u32x4 w4 = *reinterpret_cast<const u32x4*>(L.codes + row * Cfg::kCodeStride + d);
-        __builtin_nontemporal_store(w4, reinterpret_cast<u32x4*>(Zh + row * Cfg::kRowWords + d));
-    }
-}
-
-// ---------------------------------------------------------------- conversion of a plain state
-template <int kT, int kBits>
-__global__ __launch_bounds__(kThreads) void lq_quantize_kernel(const float* __restrict__ S, int n_iter,
-                                                               uint32_t* __restrict__ Z, float* __restrict__ B,
-                                                               float* __restrict__ Cs, half_t* __restrict__ Kc,
-                                                               half_t* __restrict__ Uc) {
-    using Cfg = RefitCfg<kT, kBits>;
-    extern __shared__ __align__(16) float lds[];
-    const RefitLds<kT, kBits> L(lds, lds + Cfg::kRegionFloats);
-    const int h = head_of_block(blockIdx.x, gridDim.x), tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63;
-    const int uu = 8 * wave + (lane & 7), ro = lane >> 3;
-    const float* Sh = S + static_cast<size_t>(h) * kD * kD;
-    f32x4 s[16];
-#pragma unroll
-    for (int it = 0; it < 16; ++it) s[it] = stream_load(Sh + (8 * it + ro) * kD + 4 * uu);
-    if (tid < kD) {  // the first kT Walsh columns: (-1)^popcount(i & t) / sqrt(128)
-        constexpr float sq = 0.08838834764831845f;
-#pragma unroll
-        for (int hh = 0; hh < Cfg::kC; ++hh) {
-            f32x4 w;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) w[e] = (__builtin_popcount(tid & (4 * hh + e)) & 1) ? -sq : sq;
-            L.W[tid * Cfg::kC + hh] = w;
-        }
-    }
-    __syncthreads();
-    const size_t vo = static_cast<size_t>(h) * kD;
-    lq_refit(L, s, n_iter, tid, Z + static_cast<size_t>(h) * kD * Cfg::kRowWords, B + vo, Cs + vo,
-             Kc + vo * kT, Uc + vo * kT);
 }
 
 // ---------------------------------------------------------------- in-window step
@@ -638,38 +282,20 @@ constexpr int kZsStride = kD / 4 + 1;
 // floats of the step-phase region: Kt (4 KB), Ut (12 KB), Zs, Ktok, Utok, red, recp
 constexpr int kStepFloats = 2 * kD * 4 + 3 * 2 * kD * 4 + kD * kZsStride + 2 * kTok * kD + 4 * kD * 2 + kD * 2;
 constexpr int cmax3(int a, int b, int c) { return a > b ? (a > c ? a : c) : (b > c ? b : c); }
-constexpr int kTransitFloats = kD * kD / 2;  // half the state in transit
-constexpr int kLqRegionFloats = cmax3(kStepFloats, kTransitFloats, RefitCfg<4, 8>::kRegionFloats);
+constexpr int kTransitFloats = kD * kD / 2;  // half the state in LDS during S^T Y
+constexpr int kLqRegionFloats = kStepFloats > kTransitFloats + 2 * 4 * kD ? kStepFloats : kTransitFloats + 2 * 4 * kD;
 constexpr int kLqBoundaryFloats = kLqRegionFloats + 4 * kD + kD;
 static_assert(kLqRegionFloats % 4 == 0, "W after the region must be 16-byte aligned");
 
-// The state in transit: row r in 16-byte units, unit u stored at u ^ f(r) with
-// f(r) = (r & 7) ^ ((r & 1) << 3), so that the MFMA-layout writes and the refit-layout
-// reads both spread over the banks.
+// The half state in LDS during S^T Y: row r in 16-byte units, unit u stored at u ^ f(r) with
+// f(r) = (r & 7) ^ ((r & 1) << 3), so that the tile-layout writes and the 16-row slice reads
+// both spread over the banks.
 __device__ __forceinline__ f32x4& state_unit(float* base, int r, int u) {
     return reinterpret_cast<f32x4*>(base + r * kD)[u ^ ((r & 7) ^ ((r & 1) << 3))];
 }
 
-// S from an MFMA result layout, in which wave w holds rows 32w .. 32w+31, to the refit's
-// layout (s[it] is row 8it + (l >> 3), columns 4uu .. +3), through a buffer of half the
-// state at base: rows 0 .. 63 (written by waves 0 and 1) first, then rows 64 .. 127.
-// write(base, r0) stores the wave's 32 rows as rows r0 .. r0+31 of the buffer. Every thread
-// calls it; it ends with a barrier.
-template <typename Write>
-__device__ __forceinline__ void state_to_refit(float* base, Write write, f32x4 (&s)[16], int wave, int lane) {
-    const int uu = 8 * wave + (lane & 7), rr = lane >> 3;
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-        if ((wave >> 1) == hf) write(base, 32 * (wave & 1));
-        __syncthreads();
-#pragma unroll
-        for (int it = 0; it < 8; ++it) s[8 * hf + it] = state_unit(base, 8 * it + rr, uu);
-        __syncthreads();
-    }
-}
-
-// The writer of the GDN boundaries' layout: acc[a][ct] is row 16(2w + a) + (l & 15),
-// columns 16ct + 4(l >> 4) .. +3.
+// The writer of the tile layout: acc[a][ct] is row 16(2w + a) + (l & 15), columns
+// 16ct + 4(l >> 4) .. +3; stores the wave's 32 rows as rows r0 .. r0+31 of the buffer.
 struct TileRows {
     const f32x4 (&acc)[2][8];
     int lane;
@@ -681,6 +307,355 @@ struct TileRows {
             for (int ct = 0; ct < 8; ++ct) state_unit(base, r0 + 16 * a + lr, 4 * ct + lq) = acc[a][ct];
     }
 };
+
+// ---------------------------------------------------------------- the refit in the MFMA tile layout
+// The boundaries form S_W on the matrix cores in a tile layout: lane l of wave w holds, in tile
+// ct of band a, key row 16(2w + a) + (l & 15) and value columns 16ct + 4(l >> 4) .. +3. This refit
+// keeps the state there (64 fp32 registers):
+//  * S V (the fit's Y, and the new key tokens) on v_mfma_f32_4x4x1_16b_f32. A block of 4 lanes
+//    (4b .. 4b+3) holds 4 consecutive rows of the same columns, so one state element per lane is
+//    the block's A operand and V of that column, one token per lane, its B operand; register i of
+//    lane 4b + j accumulates row i of the block, token j. The 4 lane groups (l >> 4) end with partial
+//    sums over their columns, added by two transposing lane swaps.
+//  * S^T Y sums over the rows, which lie along the 16 lanes of a DPP row here, so the state passes
+//    through LDS in two halves of 32 KB into slices of 16 rows by 4 columns per lane, where a
+//    column's rows sum over 8 lanes (as in the register layout of the plain-state conversion).
+//  * The residual S - Kt Ut^T on v_mfma_f32_16x16x4f32, whose result layout is the tile layout: A
+//    the negated value tokens of 16 columns, B the key tokens of 16 rows, 4 tokens per instruction.
+//  * The smoothing sum of a row stays in the 4 lanes that hold it; the column absmax reduces over
+//    the 16 lanes of a DPP row, then over the 4 waves through LDS.
+// LDS (floats): part A (32 KB) holds the half state during S^T Y, then the staged code rows, the
+// rounded tokens Kr, Ur [128][kT], the per-wave column maxima [4][128] and the code scales [128];
+// then V^T [kT][128] and Y [128][kT] (also the new key tokens). W [128][kT] (the fit's start and
+// the S^T Y result) lies outside the region.
+template <int kT, int kBits>
+struct TileRefitLds {
+    using Cfg = RefitCfg<kT, kBits>;
+    static constexpr int kA = kTransitFloats;
+    static constexpr int kRegionFloats = kA + 2 * kT * kD;
+    static constexpr int kWFloats = kT * kD;
+    static_assert(kD * Cfg::kCodeStride + 2 * kT * kD + 4 * kD + kD <= kA, "part A holds the code rows and the small arrays");
+    float* half;
+    uint32_t* codes;
+    float *Kr, *Ur, *cmax, *sc, *VT, *Y;
+    f32x4* W;
+    __device__ TileRefitLds(float* region, float* w_area)
+        : half(region), codes(reinterpret_cast<uint32_t*>(region)), Kr(region + kD * Cfg::kCodeStride),
+          Ur(Kr + kT * kD), cmax(Ur + kT * kD), sc(cmax + 4 * kD), VT(region + kA), Y(VT + kT * kD),
+          W(reinterpret_cast<f32x4*>(w_area)) {}
+};
+
+// Max over the 16 lanes of each DPP row of non-negative floats, compared as their bit patterns
+// (integer max takes the DPP operand directly; a float max would first quiet each operand).
+template <int kCtrl>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t x) {
+    return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), kCtrl, 0xF, 0xF, false));
+}
+__device__ __forceinline__ uint32_t row16_max_bits(uint32_t x) {
+    x = max(x, dpp_u<kDppXor1>(x));
+    x = max(x, dpp_u<kDppXor2>(x));
+    x = max(x, dpp_u<kDppRor8>(x));
+    return max(x, dpp_u<kDppRor4>(x));
+}
+
+// W -> V^T: modified Gram-Schmidt over the kT columns of W in order (one wave, lane l holding
+// rows 2l and 2l + 1; the wave rotates with the workgroup so that the serial work does not
+// always fall on the same SIMD); a column with zero norm after the projections stays zero.
+template <int kT>
+__device__ __forceinline__ void tile_mgs(const f32x4* W, float* VT, int wave, int lane) {
+    constexpr int kC = kT / 4;
+    if (wave == static_cast<int>(blockIdx.x & 3)) {
+        float a[kT], b[kT];
+#pragma unroll
+        for (int h = 0; h < kC; ++h) {
+            const f32x4 wa = W[(2 * lane) * kC + h], wb = W[(2 * lane + 1) * kC + h];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                a[4 * h + e] = wa[e];
+                b[4 * h + e] = wb[e];
+            }
+        }
+#pragma unroll
+        for (int t = 0; t < kT; ++t) {
+#pragma unroll
+            for (int g = 0; g < t; ++g) {
+                const float d = wave_sum(a[g] * a[t] + b[g] * b[t]);
+                a[t] -= d * a[g];
+                b[t] -= d * b[g];
+            }
+            const float n2 = wave_sum(a[t] * a[t] + b[t] * b[t]);
+            const float inv = n2 > 0.f ? 1.f / sqrtf(n2) : 0.f;
+            a[t] *= inv;
+            b[t] *= inv;
+        }
+#pragma unroll
+        for (int t = 0; t < kT; ++t) *reinterpret_cast<f32x2*>(VT + t * kD + 2 * lane) = f32x2{a[t], b[t]};
+    }
+    __syncthreads();
+}
+
+// Y = S V into Y [128][kT] (the caller adds the barrier before Y is read).
+template <int kT>
+__device__ __forceinline__ void tile_sv(const f32x4 (&s)[2][8], const float* VT, float* Y, int wave, int lane) {
+    const int lq = lane >> 4, j = lane & 3;
+#pragma unroll
+    for (int g = 0; g < kT / 4; ++g) {
+        f32x4 d[2][2];
+#pragma unroll
+        for (int a = 0; a < 2; ++a) d[a][0] = d[a][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const float* vrow = VT + (4 * g + j) * kD + 4 * lq;  // V of columns 16ct + 4lq + e, token 4g + j
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct) {
+            const f32x4 vb = *reinterpret_cast<const f32x4*>(vrow + 16 * ct);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                d[0][ct & 1] = __builtin_amdgcn_mfma_f32_4x4x1f32(s[0][ct][e], vb[e], d[0][ct & 1], 0, 0, 0);
+                d[1][ct & 1] = __builtin_amdgcn_mfma_f32_4x4x1f32(s[1][ct][e], vb[e], d[1][ct & 1], 0, 0, 0);
+            }
+        }
+        const f32x4 d0 = d[0][0] + d[0][1], d1 = d[1][0] + d[1][1];
+        // register i of lane l: row 16(2w + a) + 4((l & 15) >> 2) + i, token 4g + (l & 3), summed over the
+        // columns of lane group l >> 4; the swaps sum the 4 groups and leave each lane two of the 8 values
+        float u[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) u[i] = add_pair16(d0[i], d1[i]);   // bit 4 clear: band 0, set: band 1
+        const float w0 = add_pair32(u[0], u[2]), w1 = add_pair32(u[1], u[3]);  // bit 5 clear: i = 0, 1; set: 2, 3
+        const int row = 16 * (2 * wave + ((lane >> 4) & 1)) + 4 * ((lane & 15) >> 2) + 2 * (lane >> 5);
+        Y[row * kT + 4 * g + j] = w0;
+        Y[(row + 1) * kT + 4 * g + j] = w1;
+        // the next token group's operand loads stay behind this group's (registers)
+        if (kT == 8) __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// W = S^T Y: the tile state goes to LDS half by half (rows 0 .. 63 from waves 0 and 1, then
+// 64 .. 127), each half is read back as slices of 16 rows by 4 columns (lane l of wave w: columns
+// 4(8w + (l & 7)) .. +3, rows 8it + (l >> 3)) and multiplied by Y, and the partial sums reduce
+// over the 8 row lanes as in the plain-state layout (refit_sty). Ends with a barrier.
+template <int kT, int kBits>
+__device__ __forceinline__ void tile_sty(const TileRefitLds<kT, kBits>& L, const f32x4 (&s)[2][8], int wave, int lane) {
+    constexpr int kC = kT / 4, kJ = kT / 2;
+    const int uu = 8 * wave + (lane & 7), ro = lane >> 3;
+    const int b3 = ro & 1, b4 = (ro >> 1) & 1, b5 = ro >> 2;
+    f32x4 acc[4][kC];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int h = 0; h < kC; ++h) acc[e][h] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+        if ((wave >> 1) == hf) TileRows{s, lane}(L.half, 32 * (wave & 1));
+        __syncthreads();
+        // (with 8 tokens the slice is consumed two rows at a time: a fully unrolled loop loads
+        // all of it, and Y, ahead of the products and runs out of registers)
+#pragma unroll(kT == 8 ? 4 : 8)
+        for (int it = 0; it < 8; ++it) {
+            const f32x4 sv = state_unit(L.half, 8 * it + ro, uu);
+            const int row = 8 * (8 * hf + it) + ro;
+#pragma unroll
+            for (int h = 0; h < kC; ++h) {
+                f32x4 yv;
+                if constexpr (kT == 8) {
+                    yv = reinterpret_cast<const f32x4*>(L.Y)[row * kC + (h ^ b3)];
+                } else {
+                    const f32x2* Y2 = reinterpret_cast<const f32x2*>(L.Y);
+                    const f32x2 lo = Y2[row * 2 + b3], hi = Y2[row * 2 + (b3 ^ 1)];
+                    yv = f32x4{lo.x, lo.y, hi.x, hi.y};
+                }
+                acc[0][h] = axpy(sv.x, yv, acc[0][h]);
+                acc[1][h] = axpy(sv.y, yv, acc[1][h]);
+                acc[2][h] = axpy(sv.z, yv, acc[2][h]);
+                acc[3][h] = axpy(sv.w, yv, acc[3][h]);
+            }
+        }
+        __syncthreads();
+    }
+    float ra[4][kJ];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int j = 0; j < kJ; ++j)
+            ra[e][j] = acc[e][0][j] + dpp<kDppRor8>(kT == 8 ? acc[e][kC - 1][j] : acc[e][0][(j + 2) & 3]);
+    float rb[2][kJ];
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+#pragma unroll
+        for (int j = 0; j < kJ; ++j) rb[e][j] = add_pair16(ra[e][j], ra[e + 2][j]);
+    float* Wf = reinterpret_cast<float*>(L.W) + (4 * uu + 2 * b4 + b5) * kT + kJ * b3;
+    if constexpr (kT == 8) {
+        *reinterpret_cast<f32x4*>(Wf) = f32x4{add_pair32(rb[0][0], rb[1][0]), add_pair32(rb[0][1], rb[1][1]),
+                                               add_pair32(rb[0][2], rb[1][2]), add_pair32(rb[0][3], rb[1][3])};
+    } else {
+        *reinterpret_cast<f32x2*>(Wf) = f32x2{add_pair32(rb[0][0], rb[1][0]), add_pair32(rb[0][1], rb[1][1])};
+    }
+    __syncthreads();
+}
+
+// The refit of one head from the tile layout (s: the state, consumed). On entry W holds the start
+// vectors; every thread of the workgroup calls it. Writes the codes (Zh: the head's payload as
+// 32-bit words), B, c and the fp16 tokens [kT][128].
+template <int kT, int kBits>
+__device__ __forceinline__ void lq_refit_tiles(const TileRefitLds<kT, kBits>& L, f32x4 (&s)[2][8], int n_iter,
+                                               int tid, uint32_t* __restrict__ Zh, float* __restrict__ Bh,
+                                               float* __restrict__ Ch, half_t* __restrict__ Kh,
+                                               half_t* __restrict__ Uh) {
+    using Cfg = RefitCfg<kT, kBits>;
+    constexpr int kC = kT / 4;
+    const int wave = tid >> 6, lane = tid & 63;
+    const int lr = lane & 15, lq = lane >> 4;
+    tile_mgs<kT>(L.W, L.VT, wave, lane);
+    for (int it = 0; it < n_iter; ++it) {
+        tile_sv<kT>(s, L.VT, L.Y, wave, lane);
+        __syncthreads();
+        tile_sty(L, s, wave, lane);
+        tile_mgs<kT>(L.W, L.VT, wave, lane);
+    }
+    tile_sv<kT>(s, L.VT, L.Y, wave, lane);  // Kt = S V
+    __syncthreads();
+
+    // fp16 tokens (stored), and their exact fp32 values for the residual
+    if (tid < kD) {
+#pragma unroll
+        for (int h = 0; h < kC; ++h) {
+            const f32x4 kv = *reinterpret_cast<const f32x4*>(L.Y + tid * kT + 4 * h);
+            f32x4 kr, ur;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const half_t kh = static_cast<half_t>(kv[e]);
+                const half_t uh = static_cast<half_t>(L.VT[(4 * h + e) * kD + tid]);
+                kr[e] = static_cast<float>(kh);
+                ur[e] = static_cast<float>(uh);
+                Kh[(4 * h + e) * kD + tid] = kh;
+                Uh[(4 * h + e) * kD + tid] = uh;
+            }
+            *reinterpret_cast<f32x4*>(L.Kr + tid * kT + 4 * h) = kr;
+            *reinterpret_cast<f32x4*>(L.Ur + tid * kT + 4 * h) = ur;
+        }
+    }
+    __syncthreads();
+
+    // residual R = S - Kt Ut^T on the matrix cores: tile (a, ct) += (-Ut of columns 16ct + m) (Kt of
+    // rows 16(2w + a) + n)^T, 4 tokens per instruction
+#pragma unroll
+    for (int g = 0; g < kC; ++g) {
+        const float bk0 = L.Kr[(32 * wave + lr) * kT + 4 * g + lq];
+        const float bk1 = L.Kr[(32 * wave + 16 + lr) * kT + 4 * g + lq];
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct) {
+            const float au = -L.Ur[(16 * ct + lr) * kT + 4 * g + lq];
+            s[0][ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(au, bk0, s[0][ct], 0, 0, 0);
+            s[1][ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(au, bk1, s[1][ct], 0, 0, 0);
+        }
+    }
+
+    // smoothing: each row's sum of |R| over its 32 columns per lane and the 4 lanes that hold it
+    float ic[2];
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+        float t = 0.f;
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct)
+            t += (fabsf(s[a][ct].x) + fabsf(s[a][ct].y)) + (fabsf(s[a][ct].z) + fabsf(s[a][ct].w));
+        t = add_xor32(add_xor16(t));
+        const float cs = fmaxf(sqrtf(t * (1.f / kD)), kSmoothFloor);
+        ic[a] = 1.f / cs;
+        if (lq == 0) Ch[32 * wave + 16 * a + lr] = cs;
+    }
+
+    // X = R / c, the per-value-channel absmax B (the lane's two rows, its DPP row, then the 4
+    // waves) and the code scale qmax / B
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct) {
+        s[0][ct] = scale(ic[0], s[0][ct]);
+        s[1][ct] = scale(ic[1], s[1][ct]);
+        u32x4 m;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            m[e] = row16_max_bits(__float_as_uint(fmaxf(fabsf(s[0][ct][e]), fabsf(s[1][ct][e]))));
+        if (lr == 0) *reinterpret_cast<u32x4*>(L.cmax + wave * kD + 16 * ct + 4 * lq) = m;
+    }
+    __syncthreads();
+    if (tid < kD) {
+        const uint32_t* cm = reinterpret_cast<const uint32_t*>(L.cmax);
+        const float B = __uint_as_float(max(max(cm[tid], cm[kD + tid]), max(cm[2 * kD + tid], cm[3 * kD + tid])));
+        Bh[tid] = B;
+        L.sc[tid] = B > 0.f ? __fdiv_rn(static_cast<float>(Cfg::kQmax), B) : 0.f;
+    }
+    __syncthreads();
+
+    // codes of the lane's 4 columns in each of its two rows, staged so that whole rows leave together
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct) {
+        const f32x4 sc = *reinterpret_cast<const f32x4*>(L.sc + 16 * ct + 4 * lq);
+        const int u = 4 * ct + lq;  // the 4-column unit
+#pragma unroll
+        for (int a = 0; a < 2; ++a) {
+            const int row = 32 * wave + 16 * a + lr;
+            const f32x4 x = s[a][ct];
+            if constexpr (kBits == 8) {
+                L.codes[row * Cfg::kCodeStride + u] =
+                    pack_low_bytes(lq_code_t<8>(x.x * sc.x), lq_code_t<8>(x.y * sc.y), lq_code_t<8>(x.z * sc.z),
+                                   lq_code_t<8>(x.w * sc.w));
+            } else if constexpr (kBits == 4) {
+                reinterpret_cast<uint16_t*>(L.codes)[row * 2 * Cfg::kCodeStride + u] = static_cast<uint16_t>(
+                    (lq_code_t<4>(x.x * sc.x) & 0xfu) | ((lq_code_t<4>(x.y * sc.y) & 0xfu) << 4) |
+                    ((lq_code_t<4>(x.z * sc.z) & 0xfu) << 8) | ((lq_code_t<4>(x.w * sc.w) & 0xfu) << 12));
+            } else {
+                const uint32_t z0 = lq_code_t<6>(x.x * sc.x), z1 = lq_code_t<6>(x.y * sc.y);
+                const uint32_t z2 = lq_code_t<6>(x.z * sc.z), z3 = lq_code_t<6>(x.w * sc.w);
+                reinterpret_cast<uint16_t*>(L.codes)[row * 2 * Cfg::kCodeStride + u] = static_cast<uint16_t>(
+                    ((z0 >> 2) & 0xfu) | (((z1 >> 2) & 0xfu) << 4) | (((z2 >> 2) & 0xfu) << 8) | (((z3 >> 2) & 0xfu) << 12));
+                reinterpret_cast<uint8_t*>(L.codes)[row * 4 * Cfg::kCodeStride + 64 + u] =
+                    static_cast<uint8_t>((z0 & 3u) | ((z1 & 3u) << 2) | ((z2 & 3u) << 4) | ((z3 & 3u) << 6));
+            }
+        }
+    }
+    __syncthreads();
+    constexpr int kQuads = Cfg::kRowWords / 4;  // 16-byte pieces per row
+#pragma unroll
+    for (int mm = 0; mm < kD * kQuads / kThreads; ++mm) {
+        const int qd = tid + kThreads * mm;
+        const int row = qd / kQuads, d = 4 * (qd % kQuads);
+        const u32x4 w4 = *reinterpret_cast<const u32x4*>(L.codes + row * Cfg::kCodeStride + d);
+        __builtin_nontemporal_store(w4, reinterpret_cast<u32x4*>(Zh + row * Cfg::kRowWords + d));
+    }
+}
+
+// ---------------------------------------------------------------- conversion of a plain state
+// The state is loaded straight into the tile layout, the start is the first kT Walsh columns.
+template <int kT, int kBits>
+__global__ __launch_bounds__(kThreads) void lq_quantize_kernel(const float* __restrict__ S, int n_iter,
+                                                               uint32_t* __restrict__ Z, float* __restrict__ B,
+                                                               float* __restrict__ Cs, half_t* __restrict__ Kc,
+                                                               half_t* __restrict__ Uc) {
+    using L_t = TileRefitLds<kT, kBits>;
+    constexpr int kC = kT / 4;
+    extern __shared__ __align__(16) float lds[];
+    const L_t L(lds, lds + L_t::kRegionFloats);
+    const int h = head_of_block(blockIdx.x, gridDim.x), tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
+    const int lr = lane & 15, lq = lane >> 4;
+    const float* Sh = S + static_cast<size_t>(h) * kD * kD;
+    f32x4 s[2][8];
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct) s[a][ct] = stream_load(Sh + (32 * wave + 16 * a + lr) * kD + 16 * ct + 4 * lq);
+    if (tid < kD) {  // the first kT Walsh columns: (-1)^popcount(i & t) / sqrt(128)
+        constexpr float sq = 0.08838834764831845f;
+#pragma unroll
+        for (int hh = 0; hh < kC; ++hh) {
+            f32x4 w;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) w[e] = (__builtin_popcount(tid & (4 * hh + e)) & 1) ? -sq : sq;
+            L.W[tid * kC + hh] = w;
+        }
+    }
+    __syncthreads();
+    const size_t vo = static_cast<size_t>(h) * kD;
+    lq_refit_tiles(L, s, n_iter, tid, Z + static_cast<size_t>(h) * kD * RefitCfg<kT, kBits>::kRowWords, B + vo,
+                   Cs + vo, Kc + vo * kT, Uc + vo * kT);
+}
 
 __device__ __forceinline__ void split3_bf16(float x, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
     const __bf16 a = static_cast<__bf16>(x);
@@ -719,7 +694,9 @@ __global__ __launch_bounds__(kThreads) void lq_boundary_kernel(
     f32x2* red = reinterpret_cast<f32x2*>(Utok + kTok * kD);       // [4][128]
     f32x2* recp = red + 4 * kD;                                     // [128]
     // refit views (its region overlaps every step-phase array above; W and bscs do not)
-    const RefitLds<4, 8> L(dyn_lds, dyn_lds + kLqRegionFloats);
+    static_assert(TileRefitLds<4, 8>::kRegionFloats <= kLqRegionFloats, "the refit's region fits");
+    const TileRefitLds<4, 8> LT(dyn_lds, dyn_lds + kLqRegionFloats);
+    f32x4* const LW = LT.W;
     float* bscs = dyn_lds + kLqRegionFloats + 4 * kD;   // B / 127 of the old payload
 
     const int h = head_of_block(blockIdx.x, gridDim.x), tid = threadIdx.x;
@@ -826,8 +803,8 @@ __global__ __launch_bounds__(kThreads) void lq_boundary_kernel(
         if (first) Ktok[t * kD + cc] = x;
         else Utok[t * kD + cc] = x * gam_all;
     }
-    if (!first) L.W[cc] = f32x4{static_cast<float>(tokv[0]), static_cast<float>(tokv[1]),
-                                static_cast<float>(tokv[2]), static_cast<float>(tokv[3])};
+    if (!first) LW[cc] = f32x4{static_cast<float>(tokv[0]), static_cast<float>(tokv[1]),
+                               static_cast<float>(tokv[2]), static_cast<float>(tokv[3])};
     Kt[half * kD + cc] = u32x4{kcol[0], kcol[1], kcol[2], kcol[3]};
     __syncthreads();
 
@@ -874,7 +851,7 @@ __global__ __launch_bounds__(kThreads) void lq_boundary_kernel(
         const int c = cc;
         f32x2 acc = (red[c] + red[kD + c] + red[2 * kD + c] + red[3 * kD + c]) * bscs[c];
         acc += rp + recp[c];
-        const f32x4 ut = L.W[c];
+        const f32x4 ut = LW[c];
         acc += ctok[0] * ut.x + ctok[1] * ut.y + ctok[2] * ut.z + ctok[3] * ut.w;
         const float kq = kq_part[0] + kq_part[1];
         const float u = bt * (vr - acc.x);
@@ -912,10 +889,8 @@ __global__ __launch_bounds__(kThreads) void lq_boundary_kernel(
             acc[a][ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(Utok[lq * kD + col], bk, acc[a][ct], 0, 0, 0);
         }
     }
-    __syncthreads();  // every read of the step-phase arrays is done: the region holds S in halves
-    f32x4 s[16];
-    state_to_refit(dyn_lds, TileRows{acc, lane}, s, wave, lane);  // then the region is free for the refit
-    lq_refit(L, s, n_iter, tid, Zh, Bcol + vec_off, Csm + vec_off, Kc + tok0, Uc + tok0);
+    __syncthreads();  // every read of the step-phase arrays is done: the region is the refit's
+    lq_refit_tiles(LT, acc, n_iter, tid, Zh, Bcol + vec_off, Csm + vec_off, Kc + tok0, Uc + tok0);
 }
 
 // ---------------------------------------------------------------- the last step, per-key gates
@@ -926,9 +901,9 @@ __global__ __launch_bounds__(kThreads) void lq_boundary_kernel(
 // S_W = Gamma_{1:W} (C dequant(Z, B) + Kt Ut^T) + sum_j E_j u_j^T then forms on the
 // matrix cores in fp32 (the decayed keys are not bf16-exact): per 16 x 16 tile the
 // payload initialises the accumulator, four v_mfma_f32_16x16x4f32 add the 16 records and
-// one adds the 4 tokens, using the general boundary's operand layout (tile ct holds the
-// value columns 8m + ct; lane l ends with columns 32(l/16) + 8i + ct of its row). The
-// result passes through LDS into the refit's register layout.
+// one adds the 4 tokens, in the GDN boundaries' tile layout (lane l of wave w holds, in tile ct
+// of band a, row 16(2w + a) + (l & 15) and columns 16ct + 4(l >> 4) .. +3), which the refit
+// keeps.
 constexpr int kKdaRec = 16;
 // floats of the step-phase arrays: KE, Us, Gs [16][128], Zs, decayed token keys and
 // token values [4][128], red [4][128] x 2
@@ -936,9 +911,8 @@ constexpr int kKdaStepFloats = 3 * kKdaRec * kD + kD * kZsStride + 2 * kTok * kD
 // W (the refit's start) is written once the step arrays are dead, right after the refit's
 // region; B / 127 of the old payload follows the step arrays. 50 KB in all: three workgroups
 // per CU.
-constexpr int kKdaWOffset = RefitCfg<4, 8>::kRegionFloats;
-static_assert(kKdaWOffset >= kTransitFloats && kKdaWOffset + 4 * kD <= kKdaStepFloats,
-              "W must lie inside the step region, clear of the half state and the refit's arrays");
+constexpr int kKdaWOffset = TileRefitLds<4, 8>::kRegionFloats;
+static_assert(kKdaWOffset + 4 * kD <= kKdaStepFloats, "W must lie inside the step region, clear of the refit's arrays");
 constexpr int kLqKdaBoundaryFloats = kKdaStepFloats + kD;
 
 __global__ __launch_bounds__(kThreads) void lq_boundary_kda_kernel(
@@ -962,7 +936,7 @@ __global__ __launch_bounds__(kThreads) void lq_boundary_kda_kernel(
     float* Kt4 = reinterpret_cast<float*>(Zs + kD * kZsStride);    // [4][128] Gamma_{1:W} Kt
     float* Ut4 = Kt4 + kTok * kD;                                   // [4][128] Ut
     f32x2* red = reinterpret_cast<f32x2*>(Ut4 + kTok * kD);        // [4][128]
-    const RefitLds<4, 8> L(dyn_lds, dyn_lds + kKdaWOffset);
+    const TileRefitLds<4, 8> L(dyn_lds, dyn_lds + kKdaWOffset);
     float* bscs = dyn_lds + kKdaStepFloats;                         // B / 127 of the old payload
 
     const int h = head_of_block(blockIdx.x, gridDim.x), tid = threadIdx.x;
@@ -1099,62 +1073,44 @@ __global__ __launch_bounds__(kThreads) void lq_boundary_kda_kernel(
 
     // ---- S_W on the matrix cores, both 16-row bands of the wave held in registers
     const int lr = lane & 15, lq = lane >> 4;
-    f32x4 ua[kKdaRec / 4][2];
-#pragma unroll
-    for (int s4 = 0; s4 < kKdaRec / 4; ++s4) {
-        const float* src = Us + (4 * s4 + lq) * kD + 8 * lr;
-        ua[s4][0] = *reinterpret_cast<const f32x4*>(src);
-        ua[s4][1] = *reinterpret_cast<const f32x4*>(src + 4);
-    }
-    f32x4 utk[2];
-    utk[0] = *reinterpret_cast<const f32x4*>(Ut4 + lq * kD + 8 * lr);
-    utk[1] = *reinterpret_cast<const f32x4*>(Ut4 + lq * kD + 8 * lr + 4);
+    // (A: the records' and tokens' values of columns 16ct + m; B: their decayed keys of rows
+    // 16(2w + a) + n; the result layout is the tile layout)
     f32x4 acc[2][8];
 #pragma unroll
     for (int a = 0; a < 2; ++a) {
         const int row = 16 * (2 * wave + a) + lr;
-        float eb[kKdaRec / 4];
-#pragma unroll
-        for (int s4 = 0; s4 < kKdaRec / 4; ++s4) eb[s4] = KE[(4 * s4 + lq) * kD + row];
-        const float kb = Kt4[lq * kD + row];
         const float zc = zcoef[row];
 #pragma unroll
-        for (int d = 0; d < 8; ++d) {  // dword d: columns 32 lq + 4d .. +3
-            const uint32_t zd = Zs[row * kZsStride + 8 * lq + d];
-            const f32x4 bsd = *reinterpret_cast<const f32x4*>(bscs + 32 * lq + 4 * d);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {  // column 32 lq + 8 i + ct with i = d / 2, ct = 4 (d % 2) + e
-                const float zf = static_cast<float>(static_cast<int8_t>((zd >> (8 * e)) & 0xffu));
-                acc[a][4 * (d & 1) + e][d >> 1] = zf * (bsd[e] * zc);
-            }
+        for (int ct = 0; ct < 8; ++ct) {
+            const f32x4 bs = *reinterpret_cast<const f32x4*>(bscs + 16 * ct + 4 * lq);
+            acc[a][ct] = unpack_codes(Zs[row * kZsStride + 4 * ct + lq]) * (bs * zc);
         }
-#pragma unroll
-        for (int s4 = 0; s4 < kKdaRec / 4; ++s4)
-#pragma unroll
-            for (int ct = 0; ct < 8; ++ct)
-                acc[a][ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(ua[s4][ct / 4][ct % 4], eb[s4], acc[a][ct], 0, 0, 0);
-#pragma unroll
-        for (int ct = 0; ct < 8; ++ct)
-            acc[a][ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(utk[ct / 4][ct % 4], kb, acc[a][ct], 0, 0, 0);
     }
-    __syncthreads();  // every read of the step-phase arrays is done: the region holds S in halves, and W
+#pragma unroll
+    for (int s4 = 0; s4 < kKdaRec / 4; ++s4) {
+        const float eb0 = KE[(4 * s4 + lq) * kD + 32 * wave + lr], eb1 = KE[(4 * s4 + lq) * kD + 32 * wave + 16 + lr];
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct) {
+            const float ua = Us[(4 * s4 + lq) * kD + 16 * ct + lr];
+            acc[0][ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(ua, eb0, acc[0][ct], 0, 0, 0);
+            acc[1][ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(ua, eb1, acc[1][ct], 0, 0, 0);
+        }
+    }
+    {
+        const float kb0 = Kt4[lq * kD + 32 * wave + lr], kb1 = Kt4[lq * kD + 32 * wave + 16 + lr];
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct) {
+            const float ut = Ut4[lq * kD + 16 * ct + lr];
+            acc[0][ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(ut, kb0, acc[0][ct], 0, 0, 0);
+            acc[1][ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(ut, kb1, acc[1][ct], 0, 0, 0);
+        }
+    }
+    __syncthreads();  // every read of the step-phase arrays is done: the region is the refit's, and W
     if (!first)
         L.W[r] = f32x4{static_cast<float>(tokv[0]), static_cast<float>(tokv[1]), static_cast<float>(tokv[2]),
                        static_cast<float>(tokv[3])};
-    // this layout: acc[a][ct][i] is row 16(2w + a) + (l & 15), column 32(l >> 4) + 8i + ct
-    auto write = [&](float* base, int r0) {
-#pragma unroll
-        for (int a = 0; a < 2; ++a)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int hh = 0; hh < 2; ++hh)
-                    state_unit(base, r0 + 16 * a + lr, 8 * lq + 2 * i + hh) =
-                        f32x4{acc[a][4 * hh][i], acc[a][4 * hh + 1][i], acc[a][4 * hh + 2][i], acc[a][4 * hh + 3][i]};
-    };
-    f32x4 s[16];
-    state_to_refit(dyn_lds, write, s, wave, lane);  // then the region is free for the refit
-    lq_refit(L, s, n_iter, tid, Zh, Bcol + vec_off, Csm + vec_off, Kc + tok0, Uc + tok0);
+    __syncthreads();
+    lq_refit_tiles(L, acc, n_iter, tid, Zh, Bcol + vec_off, Csm + vec_off, Kc + tok0, Uc + tok0);
 }
 
 // ---------------------------------------------------------------- 4 and 6 bits
@@ -1416,7 +1372,8 @@ template <int kBits>
 struct LowBitsLds {
     using Cfg = LowBits<kBits>;
     static constexpr int kStep = 2 * kD * 4 + 3 * 2 * kD * 4 + kD * Cfg::kZsStride + 2 * Cfg::kT * kD + 4 * kD * 2 + kD * 2;
-    static constexpr int kRegion = cmax3(kStep, kTransitFloats, RefitCfg<Cfg::kT, kBits>::kRegionFloats);
+    static constexpr int kRefit = TileRefitLds<Cfg::kT, kBits>::kRegionFloats;
+    static constexpr int kRegion = kStep > kRefit ? kStep : kRefit;
     static constexpr int kBoundary = kRegion + Cfg::kT * kD + kD;
     static_assert(kRegion % 4 == 0, "W after the region must be 16-byte aligned");
 };
@@ -1447,7 +1404,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     float* Utok = Ktok + kT * kD;                                   // [kT][128], scaled by Gamma_{1:W}
     f32x2* red = reinterpret_cast<f32x2*>(Utok + kT * kD);         // [4][128]
     f32x2* recp = red + 4 * kD;                                     // [128]
-    const RefitLds<kT, kBits> L(dyn_lds, dyn_lds + kRegion);
+    const TileRefitLds<kT, kBits> L(dyn_lds, dyn_lds + kRegion);
     float* bscs = dyn_lds + kRegion + kT * kD;                      // B / qmax of the old payload
 
     const int h = head_of_block(blockIdx.x, gridDim.x), tid = threadIdx.x;
@@ -1656,10 +1613,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
                 acc[a][ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(Utok[(4 + lq) * kD + col], bk1, acc[a][ct], 0, 0, 0);
         }
     }
-    __syncthreads();  // every read of the step-phase arrays is done: the region holds S in halves
-    f32x4 s[16];
-    state_to_refit(dyn_lds, TileRows{acc, lane}, s, wave, lane);  // then the region is free for the refit
-    lq_refit(L, s, n_iter, tid, Zh, Bcol + vec_off, Csm + vec_off, Kc + tok0, Uc + tok0);
+    __syncthreads();  // every read of the step-phase arrays is done: the region is the refit's
+    lq_refit_tiles(L, acc, n_iter, tid, Zh, Bcol + vec_off, Csm + vec_off, Kc + tok0, Uc + tok0);
 }
 
 // ---------------------------------------------------------------- 4 and 6 bits, per-key gates
@@ -1676,8 +1631,7 @@ template <int kBits>
 struct LowKdaLds {
     using Cfg = LowBits<kBits>;
     static constexpr int kStep = 3 * kKdaRec * kD + kD * Cfg::kZsStride + 2 * Cfg::kT * kD + 4 * kD * 2;
-    static constexpr int kRefit = RefitCfg<Cfg::kT, kBits>::kRegionFloats;
-    static constexpr int kW = kRefit > kTransitFloats ? kRefit : kTransitFloats;
+    static constexpr int kW = TileRefitLds<Cfg::kT, kBits>::kRegionFloats;
     static constexpr int kBscs = kStep > kW + Cfg::kT * kD ? kStep : kW + Cfg::kT * kD;
     static constexpr int kTotal = kBscs + kD;
     static_assert(kW % 4 == 0 && (3 * kKdaRec * kD + kD * Cfg::kZsStride + 2 * Cfg::kT * kD) % 2 == 0,
@@ -1709,7 +1663,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     float* Ktk = reinterpret_cast<float*>(Zs + kD * kZsStride);    // [kT][128] Gamma_{1:W} Kt
     float* Utk = Ktk + kT * kD;                                     // [kT][128] Ut
     f32x2* red = reinterpret_cast<f32x2*>(Utk + kT * kD);          // [4][128]
-    const RefitLds<kT, kBits> L(dyn_lds, dyn_lds + Lds::kW);
+    const TileRefitLds<kT, kBits> L(dyn_lds, dyn_lds + Lds::kW);
     float* bscs = dyn_lds + Lds::kBscs;                             // B / qmax of the old payload
 
     const int h = head_of_block(blockIdx.x, gridDim.x), tid = threadIdx.x;
@@ -1826,76 +1780,64 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     }
     __syncthreads();
 
-    // ---- S_W on the matrix cores, both 16-row bands of the wave held in registers
+    // ---- S_W on the matrix cores in the tile layout (A: the records' and tokens' values of
+    // columns 16ct + m; B: their decayed keys of rows 16(2w + a) + n), both bands in registers
     const int lr = lane & 15, lq = lane >> 4;
-    f32x4 ua[kKdaRec / 4][2];
-#pragma unroll
-    for (int s4 = 0; s4 < kKdaRec / 4; ++s4) {
-        const float* src = Us + (4 * s4 + lq) * kD + 8 * lr;
-        ua[s4][0] = *reinterpret_cast<const f32x4*>(src);
-        ua[s4][1] = *reinterpret_cast<const f32x4*>(src + 4);
-    }
-    f32x4 utk[kC][2];
-#pragma unroll
-    for (int g = 0; g < kC; ++g) {
-        utk[g][0] = *reinterpret_cast<const f32x4*>(Utk + (4 * g + lq) * kD + 8 * lr);
-        utk[g][1] = *reinterpret_cast<const f32x4*>(Utk + (4 * g + lq) * kD + 8 * lr + 4);
-    }
     f32x4 acc[2][8];
 #pragma unroll
     for (int a = 0; a < 2; ++a) {
         const int row = 16 * (2 * wave + a) + lr;
-        float eb[kKdaRec / 4], kb[kC];
-#pragma unroll
-        for (int s4 = 0; s4 < kKdaRec / 4; ++s4) eb[s4] = KE[(4 * s4 + lq) * kD + row];
-#pragma unroll
-        for (int g = 0; g < kC; ++g) kb[g] = Ktk[(4 * g + lq) * kD + row];
         const float zc = zcoef[row];
-        const uint32_t* zs_row = Zs + row * kZsStride;
+        const uint16_t* z16 = reinterpret_cast<const uint16_t*>(Zs + row * kZsStride);
+        const uint8_t* z8lo = reinterpret_cast<const uint8_t*>(Zs + row * kZsStride + 16);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {  // columns 32 lq + 8 i + ct: nibble word 4 lq + i, nibble ct
-            const uint32_t zn = zs_row[4 * lq + i];
-            const uint32_t zlo = kBits == 6 ? reinterpret_cast<const uint16_t*>(zs_row + 16)[4 * lq + i] : 0u;
-            const f32x4 b0 = *reinterpret_cast<const f32x4*>(bscs + 32 * lq + 8 * i);
-            const f32x4 b1 = *reinterpret_cast<const f32x4*>(bscs + 32 * lq + 8 * i + 4);
-#pragma unroll
-            for (int ct = 0; ct < 8; ++ct) {
-                int z = static_cast<int>(zn << (28 - 4 * ct)) >> 28;
-                if constexpr (kBits == 6) z = 4 * z + static_cast<int>((zlo >> (2 * ct)) & 3u);
-                acc[a][ct][i] = static_cast<float>(z) * ((ct < 4 ? b0[ct] : b1[ct - 4]) * zc);
+        for (int ct = 0; ct < 8; ++ct) {  // the 4 codes of columns 16ct + 4lq .. +3
+            const f32x4 bs = *reinterpret_cast<const f32x4*>(bscs + 16 * ct + 4 * lq);
+            const uint32_t zz = z16[4 * ct + lq];
+            f32x4 zf;
+            if constexpr (kBits == 4) {
+                zf = f32x4{static_cast<float>(static_cast<int>(zz << 28) >> 28),
+                           static_cast<float>(static_cast<int>(zz << 24) >> 28),
+                           static_cast<float>(static_cast<int>(zz << 20) >> 28),
+                           static_cast<float>(static_cast<int>(zz << 16) >> 28)};
+            } else {
+                const uint32_t zb = z8lo[4 * ct + lq];
+                zf = f32x4{static_cast<float>(4 * (static_cast<int>(zz << 28) >> 28) + static_cast<int>(zb & 3u)),
+                           static_cast<float>(4 * (static_cast<int>(zz << 24) >> 28) + static_cast<int>((zb >> 2) & 3u)),
+                           static_cast<float>(4 * (static_cast<int>(zz << 20) >> 28) + static_cast<int>((zb >> 4) & 3u)),
+                           static_cast<float>(4 * (static_cast<int>(zz << 16) >> 28) + static_cast<int>(zb >> 6))};
             }
+            acc[a][ct] = zf * (bs * zc);
         }
-#pragma unroll
-        for (int s4 = 0; s4 < kKdaRec / 4; ++s4)
-#pragma unroll
-            for (int ct = 0; ct < 8; ++ct)
-                acc[a][ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(ua[s4][ct / 4][ct % 4], eb[s4], acc[a][ct], 0, 0, 0);
-#pragma unroll
-        for (int g = 0; g < kC; ++g)
-#pragma unroll
-            for (int ct = 0; ct < 8; ++ct)
-                acc[a][ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(utk[g][ct / 4][ct % 4], kb[g], acc[a][ct], 0, 0, 0);
     }
-    __syncthreads();  // every read of the step-phase arrays is done: the region holds S in halves, and W
+#pragma unroll
+    for (int s4 = 0; s4 < kKdaRec / 4; ++s4) {
+        const float eb0 = KE[(4 * s4 + lq) * kD + 32 * wave + lr], eb1 = KE[(4 * s4 + lq) * kD + 32 * wave + 16 + lr];
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct) {
+            const float ua = Us[(4 * s4 + lq) * kD + 16 * ct + lr];
+            acc[0][ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(ua, eb0, acc[0][ct], 0, 0, 0);
+            acc[1][ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(ua, eb1, acc[1][ct], 0, 0, 0);
+        }
+    }
+#pragma unroll
+    for (int g = 0; g < kC; ++g) {
+        const float kb0 = Ktk[(4 * g + lq) * kD + 32 * wave + lr], kb1 = Ktk[(4 * g + lq) * kD + 32 * wave + 16 + lr];
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct) {
+            const float ut = Utk[(4 * g + lq) * kD + 16 * ct + lr];
+            acc[0][ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(ut, kb0, acc[0][ct], 0, 0, 0);
+            acc[1][ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(ut, kb1, acc[1][ct], 0, 0, 0);
+        }
+    }
+    __syncthreads();  // every read of the step-phase arrays is done: the region is the refit's, and W
     if (!first)
 #pragma unroll
         for (int hh = 0; hh < kC; ++hh)
             L.W[r * kC + hh] = f32x4{static_cast<float>(tokv[4 * hh]), static_cast<float>(tokv[4 * hh + 1]),
                                      static_cast<float>(tokv[4 * hh + 2]), static_cast<float>(tokv[4 * hh + 3])};
-    // this layout: acc[a][ct][i] is row 16(2w + a) + (l & 15), column 32(l >> 4) + 8i + ct
-    auto write = [&](float* base, int r0) {
-#pragma unroll
-        for (int a = 0; a < 2; ++a)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int hh = 0; hh < 2; ++hh)
-                    state_unit(base, r0 + 16 * a + lr, 8 * lq + 2 * i + hh) =
-                        f32x4{acc[a][4 * hh][i], acc[a][4 * hh + 1][i], acc[a][4 * hh + 2][i], acc[a][4 * hh + 3][i]};
-    };
-    f32x4 s[16];
-    state_to_refit(dyn_lds, write, s, wave, lane);  // then the region is free for the refit
-    lq_refit(L, s, n_iter, tid, Zh, Bcol + vec_off, Csm + vec_off, Kc + tok0, Uc + tok0);
+    __syncthreads();
+    lq_refit_tiles(L, acc, n_iter, tid, Zh, Bcol + vec_off, Csm + vec_off, Kc + tok0, Uc + tok0);
 }
 
 // ---------------------------------------------------------------- launchers
@@ -1906,8 +1848,8 @@ static hipError_t set_lds(const void* fn, int floats) {
 
 hipError_t launch_lq_quantize(int heads, const float* S, int n_iter, int8_t* Z, float* B, float* C,
                               void* Kc, void* Uc, hipStream_t stream) {
-    using Cfg = RefitCfg<4, 8>;
-    constexpr int floats = Cfg::kRegionFloats + Cfg::kWFloats;
+    using L_t = TileRefitLds<4, 8>;
+    constexpr int floats = L_t::kRegionFloats + L_t::kWFloats;
     static const hipError_t attr = set_lds(reinterpret_cast<const void*>(lq_quantize_kernel<4, 8>), floats);
     if (attr != hipSuccess) return attr;
     hipLaunchKernelGGL((lq_quantize_kernel<4, 8>), dim3(heads), dim3(kThreads), sizeof(float) * floats, stream,
@@ -1953,8 +1895,8 @@ template <int kBits>
 static hipError_t launch_low_quantize(int heads, const float* S, int n_iter, void* Z, float* B, float* C, void* Kc,
                                       void* Uc, hipStream_t stream) {
     constexpr int kT = LowBits<kBits>::kT;
-    using Cfg = RefitCfg<kT, kBits>;
-    constexpr int floats = Cfg::kRegionFloats + Cfg::kWFloats;
+    using L_t = TileRefitLds<kT, kBits>;
+    constexpr int floats = L_t::kRegionFloats + L_t::kWFloats;
     static const hipError_t attr = set_lds(reinterpret_cast<const void*>(lq_quantize_kernel<kT, kBits>), floats);
     if (attr != hipSuccess) return attr;
     hipLaunchKernelGGL((lq_quantize_kernel<kT, kBits>), dim3(heads), dim3(kThreads), sizeof(float) * floats, stream,
