@@ -1229,6 +1229,125 @@ __global__ __launch_bounds__(kThreads) void q8_boundary_bf16_kernel(
     }
 }
 
+// ---- requantization from up to 32 records with scalar gates and bf16 keys (the DeltaProduct
+// window's end): as the GDN bf16 boundary, the decay after record j moves onto its correction,
+// S_W = Gamma_{1:W} S^_0 + sum_j k_j (Gamma_{j+1:W} u_j)^T, the keys are exact bf16 operands and
+// each scaled correction is split into three bf16 parts, so the record contraction is three
+// v_mfma_f32_16x16x32_bf16 per 16 x 16 tile (hi, mid, lo parts, the 32 records along the depth)
+// with exact products and fp32 sums, instead of eight fp32 MFMAs. Thread cc + 128 half stages
+// column / key row cc of records 16 half .. 16 half + 15.
+__global__ __launch_bounds__(kThreads) void q8_requant_bf16_kernel(int nrec, int rec_stride, int8_t* __restrict__ Z,
+                                                                   float* __restrict__ A,
+                                                                   const bf16_t* __restrict__ Kbuf,
+                                                                   const float* __restrict__ Ubuf,
+                                                                   const float* __restrict__ Gbuf) {
+    constexpr int kRec = 32;
+    __shared__ u32x4 Kt[kRec / 8][kD];        // keys of records 8b .. 8b+7 at each key row
+    __shared__ u32x4 Ut[3][kRec / 8][kD];     // scaled corrections, three bf16 parts, per column
+    __shared__ uint32_t Zs[kD * kZsStride];
+    __shared__ float zcoef[kD];
+
+    const int h = head_of_block(blockIdx.x, gridDim.x), tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
+    const int c4 = lane & 31, ro = lane >> 5;
+    const int cc = tid & (kD - 1), half = tid >> 7;
+    const size_t vec_off = static_cast<size_t>(h) * kD;
+    const size_t rec0 = static_cast<size_t>(h) * rec_stride * kD;
+    uint32_t* Zh = reinterpret_cast<uint32_t*>(Z + static_cast<size_t>(h) * kD * kD);
+
+    // ---- loads: the records of this thread's column / key row, the gates, then the codes
+    float ucol[16];
+    uint32_t kcol[8];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+        const int j = 16 * half + e;
+        const size_t at = rec0 + static_cast<size_t>(j < nrec ? j : 0) * kD + cc;  // slot clamped: in bounds
+        const float ul = Ubuf[at];
+        const uint32_t kl = static_cast<uint32_t>(Kbuf[at]);
+        ucol[e] = j < nrec ? ul : 0.f;
+        const uint32_t kb = j < nrec ? kl : 0u;
+        kcol[e >> 1] = (e & 1) ? (kcol[e >> 1] | (kb << 16)) : kb;
+    }
+    const float g_lane = lane < nrec ? Gbuf[static_cast<size_t>(h) * rec_stride + lane] : 1.f;
+    const float ar = A[vec_off + cc];
+    uint32_t zw[kRowsPerThread];
+#pragma unroll
+    for (int it = 0; it < kRowsPerThread; ++it)
+        zw[it] = __builtin_nontemporal_load(Zh + q8_row(it, wave, ro) * (kD / 4) + c4);
+
+    // ---- the decay after each record (suffix scan over the record lanes; g = 1 past nrec),
+    // the scaled corrections split into bf16 parts, the keys, and the codes staged
+    const float Sfx = suffix_prod<kRec>(g_lane, lane);
+    const float E = suffix_prod_excl<kRec>(Sfx, lane);
+    const float gall = lane_value(Sfx, 0);
+    float gam[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) gam[e] = lane_gather(E, 16 * half + e);
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+        u32x4 part[3];
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+            uint32_t hi, mid, lo;
+            split3_bf16x2(gam[8 * b + e] * ucol[8 * b + e], gam[8 * b + e + 1] * ucol[8 * b + e + 1], hi, mid, lo);
+            part[0][e >> 1] = hi;
+            part[1][e >> 1] = mid;
+            part[2][e >> 1] = lo;
+        }
+#pragma unroll
+        for (int pp = 0; pp < 3; ++pp) Ut[pp][2 * half + b][cc] = part[pp];
+        Kt[2 * half + b][cc] = u32x4{kcol[4 * b], kcol[4 * b + 1], kcol[4 * b + 2], kcol[4 * b + 3]};
+    }
+    if (half == 0) zcoef[cc] = ar * (1.f / 127.f) * gall;
+#pragma unroll
+    for (int it = 0; it < kRowsPerThread; ++it) Zs[q8_row(it, wave, ro) * kZsStride + c4] = zw[it];
+    __syncthreads();
+
+    // ---- S_W on the matrix cores (wave w: key rows 32w .. 32w+31 as two bands; B = the keys of
+    // the records 8(l/16) .. +7 at key row 16 band + l%16, A = their scaled corrections at column
+    // 16ct + l%16; result i of lane l is column 16ct + 4(l/16) + i), then the row absmax and codes
+    const int lr = lane & 15, lq = lane >> 4;
+    for (int a = 0; a < 2; ++a) {
+        const int row = 16 * (2 * wave + a) + lr;
+        const bf16x8 bv = __builtin_bit_cast(bf16x8, Kt[lq][row]);
+        const float zc = zcoef[row];
+        f32x4 acc[8];
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct) acc[ct] = unpack_i8x4(Zs[row * kZsStride + 4 * ct + lq]) * zc;
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct) {
+            const int col = 16 * ct + lr;
+#pragma unroll
+            for (int pp = 0; pp < 3; ++pp)
+                acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, Ut[pp][lq][col]), bv,
+                                                                  acc[ct], 0, 0, 0);
+        }
+        float m = 0.f;
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct)
+            m = fmaxf(m, fmaxf(fmaxf(fabsf(acc[ct].x), fabsf(acc[ct].y)),
+                               fmaxf(fabsf(acc[ct].z), fabsf(acc[ct].w))));
+        m = max_xor16(m);
+        float m0, m1;
+        swap32(m, m0, m1);
+        m = fmaxf(m0, m1);
+        const float sc = m > 0.f ? __fdiv_rn(127.f, m) : 0.f;
+        if (lq == 0) A[vec_off + row] = m;
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct)
+            Zs[row * kZsStride + 4 * ct + lq] = code_word_in_range(acc[ct].x * sc, acc[ct].y * sc,
+                                                                   acc[ct].z * sc, acc[ct].w * sc);
+    }
+    wave_lds_sync();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int row = 32 * wave + 8 * i + (lane >> 3), d0 = 4 * (lane & 7);
+        const uint32_t* src = Zs + row * kZsStride + d0;
+        const u32x4 w4 = {src[0], src[1], src[2], src[3]};
+        __builtin_nontemporal_store(w4, reinterpret_cast<u32x4*>(Zh + row * (kD / 4) + d0));
+    }
+}
+
 hipError_t launch_q8_quantize(int heads, const float* S, int8_t* Z, float* A, hipStream_t stream) {
     hipLaunchKernelGGL(q8_quantize_kernel, dim3(heads), dim3(kThreads), 0, stream, S, Z, A);
     return hipGetLastError();
@@ -1303,6 +1422,11 @@ static hipError_t launch_dp_window_t(const StepArgs& a, const WindowArgs& w, hip
                        static_cast<const T*>(a.k), static_cast<const T*>(a.v), a.gate, a.beta, a.y);
     if (hipError_t e = hipGetLastError()) return e;
     if (w.pos < w.W - 1) return hipSuccess;
+    if constexpr (sizeof(T) == 2) {  // bf16 keys: the bf16-split requantizer
+        hipLaunchKernelGGL(q8_requant_bf16_kernel, dim3(a.heads), dim3(kThreads), 0, stream, kN * w.W, kN * w.W,
+                           w.Z, w.A, static_cast<const bf16_t*>(w.Kbuf), w.Ubuf, w.Gbuf);
+        return hipGetLastError();
+    }
     const int floats = boundary_lds_floats(kRwkv7Rec);
     static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(q8_requant_kernel<false, T>),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize,
