@@ -1020,6 +1020,23 @@ __device__ __forceinline__ void split3_bf16x2(float x0, float x1, uint32_t& hi, 
     lo = pk_bf16(s0, s1);
 }
 
+// A raw buffer resource over n bytes at p (no stride, 32-bit data format word): loads through
+// it take a scalar and a lane byte offset, and an offset past n reads zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t head_buffer(const void* p, int n) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, n, 0x00020000);
+}
+// Word w of code row r in the LDS copy of a head's codes (32 words a row, no padding): the
+// 16-byte chunk index is XORed with (r / 2) % 8, so that 16 consecutive rows read at the
+// same chunk hit 16 different bank groups, and a row's 32 words stay in one bank sweep.
+__device__ __forceinline__ int zs_word(int r, int w) { return r * (kD / 4) + (w ^ (4 * ((r >> 1) & 7))); }
+// Slot of value column c in the staged corrections: column 32(m/4) + 4ct + m%4 at 16ct + m.
+__device__ __forceinline__ int ut_slot(int c) { return 16 * ((c >> 2) & 7) + 4 * (c >> 5) + (c & 3); }
+// max(m, |a|, |b|) with NaN-propagating maxima (v_maximum3_f32, whose inputs need no
+// canonicalizing; a NaN leaves the row's codes unspecified, as for any non-finite row).
+__device__ __forceinline__ float max3_abs(float m, float a, float b) {
+    return __builtin_elementwise_maximum(__builtin_elementwise_maximum(m, __builtin_fabsf(a)), __builtin_fabsf(b));
+}
+
 // ---- the last step of the window for scalar gates (GDN), bf16 keys and W <= 16.
 // The decay of record j is a scalar, so it moves onto the correction:
 // S_W = Gamma_{1:W} S^_0 + sum_j k_j (Gamma_{j+1:W} u_j)^T. The keys are exact in
@@ -1033,7 +1050,7 @@ __device__ __forceinline__ void split3_bf16x2(float x0, float x1, uint32_t& hi, 
 // second product, but chained onto the same accumulator after the x32 product it
 // gave wrong sums with this toolchain.)
 // Records are staged transposed, as 16-byte words of 8 consecutive records:
-// Kt[b][row] (keys of records 8b .. 8b+7 at a key row) and Ut[part][b][column].
+// Kt[b][row] (keys of records 8b .. 8b+7 at a key row) and Ut[part][b][ut_slot(column)].
 __global__ __launch_bounds__(kThreads) void q8_boundary_bf16_kernel(
     int W, int pos, int8_t* __restrict__ Z, float* __restrict__ A, const bf16_t* __restrict__ Kbuf,
     const float* __restrict__ Ubuf, const float* __restrict__ Gbuf, const bf16_t* __restrict__ q,
@@ -1049,7 +1066,7 @@ __global__ __launch_bounds__(kThreads) void q8_boundary_bf16_kernel(
     __shared__ float gam[kRec];           // Gamma_{j+1:W}; 1 for the current record
     __shared__ u32x4 Kt[2][kD];
     __shared__ u32x4 Ut[3][2][kD];
-    __shared__ uint32_t Zs[kD * kZsStride];
+    __shared__ __align__(16) uint32_t Zs[kD * kD / 4];  // codes, row-major, 16-byte chunks swizzled (zs_word)
 
     const int h = head_of_block(blockIdx.x, gridDim.x), tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
@@ -1065,12 +1082,19 @@ __global__ __launch_bounds__(kThreads) void q8_boundary_bf16_kernel(
     if (0 < pos) kc.load(Kbuf + rec0 + static_cast<size_t>(grp < pos ? grp : 0) * kD + 8 * ch);
     float ucol[8];
     uint32_t kcol[4];  // keys of records 8 half + e at key row cc, two bf16 per word
+    // the record slot of each load is the same in the whole wave: one buffer resource per
+    // record array of the head, the slot in the scalar offset, the column in the lane offset
+    const int half_w = __builtin_amdgcn_readfirstlane(half);
+    const auto urs = head_buffer(Ubuf + rec0, W * kD * sizeof(float));
+    const auto krs = head_buffer(Kbuf + rec0, W * kD * sizeof(bf16_t));
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-        const int j = 8 * half + e;
-        const size_t at = rec0 + static_cast<size_t>(j < pos ? j : 0) * kD + cc;
-        const float ul = Ubuf[at];  // unconditional: at is clamped to slot 0 (in bounds), the value dropped for j >= pos
-        const uint32_t kl = static_cast<uint32_t>(Kbuf[at]);
+        const int j = 8 * half_w + e;
+        const int slot = j < pos ? j : 0;  // clamped to slot 0 (in bounds), the value dropped for j >= pos
+        const float ul = __builtin_bit_cast(
+            float, __builtin_amdgcn_raw_buffer_load_b32(urs, cc * sizeof(float), slot * kD * sizeof(float), 0));
+        const uint32_t kl =
+            __builtin_amdgcn_raw_buffer_load_b16(krs, cc * sizeof(bf16_t), slot * kD * sizeof(bf16_t), 0);
         ucol[e] = j < pos ? ul : 0.f;
         const uint32_t kb = j < pos ? kl : 0u;
         kcol[e >> 1] = (e & 1) ? (kcol[e >> 1] | (kb << 16)) : kb;
@@ -1150,7 +1174,7 @@ __global__ __launch_bounds__(kThreads) void q8_boundary_bf16_kernel(
         part[2][e >> 1] = lo;
     }
 #pragma unroll
-    for (int pp = 0; pp < 3; ++pp) Ut[pp][half][cc] = part[pp];
+    for (int pp = 0; pp < 3; ++pp) Ut[pp][half][ut_slot(cc)] = part[pp];
     p1 = f32x4{add_xor32(p1.x), add_xor32(p1.y), add_xor32(p1.z), add_xor32(p1.w)};
     p2 = f32x4{add_xor32(p2.x), add_xor32(p2.y), add_xor32(p2.z), add_xor32(p2.w)};
     if (ro == 0) {
@@ -1160,8 +1184,12 @@ __global__ __launch_bounds__(kThreads) void q8_boundary_bf16_kernel(
         red[wave][4 * c4 + 3] = f32x2{p1.w, p2.w};
     }
     if (half == 1) recp[cc] = rp;
+    {  // zs_word of row 8 it + 2 wave + ro: the chunk swizzle is wave + 4 (it % 2)
+        const int w_even = (2 * wave + ro) * (kD / 4) + (c4 ^ (4 * wave));
+        const int w_odd = (2 * wave + ro) * (kD / 4) + (c4 ^ (4 * wave + 16));
 #pragma unroll
-    for (int it = 0; it < kRowsPerThread; ++it) Zs[q8_row(it, wave, ro) * kZsStride + c4] = zw[it];
+        for (int it = 0; it < kRowsPerThread; ++it) Zs[((it & 1) ? w_odd : w_even) + 8 * (kD / 4) * it] = zw[it];
+    }
     __syncthreads();
 
     // ---- correction and output; the current record (no decay after it) joins the operands
@@ -1173,17 +1201,20 @@ __global__ __launch_bounds__(kThreads) void q8_boundary_bf16_kernel(
         y[vec_off + c] = acc.y + u * kq;
         uint32_t uh, um, ul;
         split3_bf16(u, uh, um, ul);
-        reinterpret_cast<uint16_t*>(&Ut[0][pos >> 3][c])[pos & 7] = static_cast<uint16_t>(uh);
-        reinterpret_cast<uint16_t*>(&Ut[1][pos >> 3][c])[pos & 7] = static_cast<uint16_t>(um);
-        reinterpret_cast<uint16_t*>(&Ut[2][pos >> 3][c])[pos & 7] = static_cast<uint16_t>(ul);
+        const int cs = ut_slot(c);
+        reinterpret_cast<uint16_t*>(&Ut[0][pos >> 3][cs])[pos & 7] = static_cast<uint16_t>(uh);
+        reinterpret_cast<uint16_t*>(&Ut[1][pos >> 3][cs])[pos & 7] = static_cast<uint16_t>(um);
+        reinterpret_cast<uint16_t*>(&Ut[2][pos >> 3][cs])[pos & 7] = static_cast<uint16_t>(ul);
         reinterpret_cast<uint16_t*>(&Kt[pos >> 3][c])[pos & 7] = static_cast<uint16_t>(__float_as_uint(kr) >> 16);
     }
     __syncthreads();
 
     // ---- S_W on the matrix cores. Wave w owns key rows 32w .. 32w+31 as two bands of
-    // 16 (B = keys, key row 16 band + l%16); tile ct covers value columns 16ct .. +15
-    // (A = scaled corrections, column 16ct + l%16); result i of lane l is column
-    // 16ct + 4(l/16) + i: one 32-bit word of codes.
+    // 16 (B = keys, key row 16 band + l%16). Tile ct takes the value columns
+    // 32(m/4) + 4ct + m%4, m = 0..15 (A = scaled corrections, A row m from lane m of each
+    // lane group; ut_slot stores column 32(m/4) + 4ct + m%4 at 16ct + m): result i of lane l
+    // is then column 32(l/16) + 4ct + i, so lane l ends up holding code words 8(l/16) .. +7 of
+    // its row, two 16-byte chunks that go straight to memory.
     const int lr = lane & 15, lq = lane >> 4, blk = lq & 1;
     for (int a = 0; a < 2; ++a) {
         const int row = 16 * (2 * wave + a) + lr;
@@ -1192,40 +1223,41 @@ __global__ __launch_bounds__(kThreads) void q8_boundary_bf16_kernel(
         // half (lq >= 2) supply zero keys, so whatever they read as corrections drops out
         const bf16x8 bv_lo = lq < 2 ? bv : __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
         const float zc = zcoef[row];
+        const u32x4 zlo = *reinterpret_cast<const u32x4*>(&Zs[zs_word(row, 8 * lq)]);
+        const u32x4 zhi = *reinterpret_cast<const u32x4*>(&Zs[zs_word(row, 8 * lq + 4)]);
         f32x4 acc[8];
 #pragma unroll
-        for (int ct = 0; ct < 8; ++ct) acc[ct] = unpack_i8x4(Zs[row * kZsStride + 4 * ct + lq]) * zc;
+        for (int ct = 0; ct < 4; ++ct) {
+            acc[ct] = unpack_i8x4(zlo[ct]) * zc;
+            acc[ct + 4] = unpack_i8x4(zhi[ct]) * zc;
+        }
 #pragma unroll
         for (int ct = 0; ct < 8; ++ct) {
-            const int col = 16 * ct + lr;
-            const bf16x8 a1 = __builtin_bit_cast(bf16x8, Ut[lq < 2 ? 0 : 1][blk][col]);
-            const bf16x8 a2 = __builtin_bit_cast(bf16x8, Ut[2][blk][col]);
+            const bf16x8 a1 = __builtin_bit_cast(bf16x8, Ut[lq < 2 ? 0 : 1][blk][16 * ct + lr]);
+            const bf16x8 a2 = __builtin_bit_cast(bf16x8, Ut[2][blk][16 * ct + lr]);
             acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, bv, acc[ct], 0, 0, 0);
             acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a2, bv_lo, acc[ct], 0, 0, 0);
         }
-        float m = 0.f;
+        float m0 = 0.f, m1 = 0.f;
 #pragma unroll
-        for (int ct = 0; ct < 8; ++ct)
-            m = fmaxf(m, fmaxf(fmaxf(fabsf(acc[ct].x), fabsf(acc[ct].y)),
-                               fmaxf(fabsf(acc[ct].z), fabsf(acc[ct].w))));
-        m = max_xor16(m);
-        float m0, m1;
+        for (int ct = 0; ct < 8; ct += 2) {
+            m0 = max3_abs(m0, acc[ct].x, acc[ct].y);
+            m1 = max3_abs(m1, acc[ct].z, acc[ct].w);
+            m0 = max3_abs(m0, acc[ct + 1].x, acc[ct + 1].y);
+            m1 = max3_abs(m1, acc[ct + 1].z, acc[ct + 1].w);
+        }
+        float m = max_xor16(fmaxf(m0, m1));
         swap32(m, m0, m1);
         m = fmaxf(m0, m1);
         const float sc = m > 0.f ? __fdiv_rn(127.f, m) : 0.f;
         if (lq == 0) A[vec_off + row] = m;
+        uint32_t cw[8];
 #pragma unroll
         for (int ct = 0; ct < 8; ++ct)
-            Zs[row * kZsStride + 4 * ct + lq] = code_word_in_range(acc[ct].x * sc, acc[ct].y * sc,
-                                                                   acc[ct].z * sc, acc[ct].w * sc);
-    }
-    wave_lds_sync();
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int row = 32 * wave + 8 * i + (lane >> 3), d0 = 4 * (lane & 7);
-        const uint32_t* src = Zs + row * kZsStride + d0;
-        const u32x4 w4 = {src[0], src[1], src[2], src[3]};
-        __builtin_nontemporal_store(w4, reinterpret_cast<u32x4*>(Zh + row * (kD / 4) + d0));
+            cw[ct] = code_word_in_range(acc[ct].x * sc, acc[ct].y * sc, acc[ct].z * sc, acc[ct].w * sc);
+        u32x4* out = reinterpret_cast<u32x4*>(Zh + row * (kD / 4) + 8 * lq);
+        __builtin_nontemporal_store((u32x4{cw[0], cw[1], cw[2], cw[3]}), out);
+        __builtin_nontemporal_store((u32x4{cw[4], cw[5], cw[6], cw[7]}), out + 1);
     }
 }
 
