@@ -363,6 +363,17 @@ __device__ __forceinline__ uint32_t code_word_in_range(float a, float b, float c
                           code_bits_in_range(d));
 }
 
+// A raw buffer resource over n bytes at p (no stride, 32-bit data format word): loads through
+// it take a scalar and a lane byte offset, and an offset past n reads zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t head_buffer(const void* p, int n) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, n, 0x00020000);
+}
+// max(m, |a|, |b|) with NaN-propagating maxima (v_maximum3_f32, whose inputs need no
+// canonicalizing; a NaN leaves the row's codes unspecified, as for any non-finite row).
+__device__ __forceinline__ float max3_abs(float m, float a, float b) {
+    return __builtin_elementwise_maximum(__builtin_elementwise_maximum(m, __builtin_fabsf(a)), __builtin_fabsf(b));
+}
+
 // S_W of eq. 4 from the staged window, requantized in place: the record sum is a
 // [128 x kWmax] . [kWmax x 128] contraction per head, done on the matrix cores as its
 // transpose with v_mfma_f32_16x16x4f32 (A from lane l is A[l%16][l/16], B is B[l/16][l%16],
@@ -372,10 +383,10 @@ __device__ __forceinline__ uint32_t code_word_in_range(float a, float b, float c
 // 8(l%16) .. +7 with two 128-bit LDS loads and ends up holding the 32 consecutive columns
 // 32(l/16) .. +31 of its row: result i of tile ct is column 32(l/16) + 8i + ct. All operands
 // of a band are loaded before its MFMAs. Rows of KE / Us past the last record are zero;
-// zcoef[r] = a_r / 127 Gamma_{1:W, r}; Zs holds the old codes (row stride kZsStride) and
-// receives the new ones; the rows leave from there as whole 128-byte rows.
+// zcoef[r] = a_r / 127 Gamma_{1:W, r}; Zs holds the old codes (row stride kZsStride); the
+// new codes of a lane's 32 columns leave straight from its registers as two 16-byte stores.
 template <int kWmax>
-__device__ __forceinline__ void form_and_requantize(const float* KE, const float* Us, uint32_t* Zs,
+__device__ __forceinline__ void form_and_requantize(const float* KE, const float* Us, const uint32_t* Zs,
                                                     const float* zcoef, float* __restrict__ Ah,
                                                     uint32_t* __restrict__ Zh, int wave, int lane) {
     constexpr int kSteps = kWmax / 4;
@@ -409,34 +420,30 @@ __device__ __forceinline__ void form_and_requantize(const float* KE, const float
             if (s % 2 == 1) __builtin_amdgcn_sched_barrier(0);
         }
         // per-row absmax: 32 values in this lane, then the 4 lanes l, l^16, l^32, l^48
-        float m = 0.f;
+        float m0 = 0.f, m1 = 0.f;
 #pragma unroll
-        for (int ct = 0; ct < 8; ++ct)
-            m = fmaxf(m, fmaxf(fmaxf(fabsf(acc[ct].x), fabsf(acc[ct].y)),
-                               fmaxf(fabsf(acc[ct].z), fabsf(acc[ct].w))));
-        m = max_xor16(m);
-        float m0, m1;
+        for (int ct = 0; ct < 8; ct += 2) {
+            m0 = max3_abs(m0, acc[ct].x, acc[ct].y);
+            m1 = max3_abs(m1, acc[ct].z, acc[ct].w);
+            m0 = max3_abs(m0, acc[ct + 1].x, acc[ct + 1].y);
+            m1 = max3_abs(m1, acc[ct + 1].z, acc[ct + 1].w);
+        }
+        float m = max_xor16(fmaxf(m0, m1));
         swap32(m, m0, m1);
         m = fmaxf(m0, m1);
         const float sc = m > 0.f ? __fdiv_rn(127.f, m) : 0.f;
         if (lq == 0) Ah[row] = m;
-        // the new codes replace the old ones in Zs (this lane read exactly these words)
+        // word 2i + hh of the lane's 8 holds columns 32 lq + 8i + 4hh .. +3
+        uint32_t cw[8];
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh)
-                Zs[row * kZsStride + 8 * lq + 2 * i + hh] =
-                    code_word_in_range(acc[4 * hh + 0][i] * sc, acc[4 * hh + 1][i] * sc,
-                                       acc[4 * hh + 2][i] * sc, acc[4 * hh + 3][i] * sc);
-    }
-    // the wave's 32 rows (32w .. 32w+31, 4 KiB of codes) leave as whole 128-byte rows
-    wave_lds_sync();
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int row = 32 * wave + 8 * i + (lane >> 3), d0 = 4 * (lane & 7);
-        const uint32_t* src = Zs + row * kZsStride + d0;
-        const u32x4 w4 = {src[0], src[1], src[2], src[3]};
-        __builtin_nontemporal_store(w4, reinterpret_cast<u32x4*>(Zh + row * (kD / 4) + d0));
+                cw[2 * i + hh] = code_word_in_range(acc[4 * hh + 0][i] * sc, acc[4 * hh + 1][i] * sc,
+                                                    acc[4 * hh + 2][i] * sc, acc[4 * hh + 3][i] * sc);
+        u32x4* out = reinterpret_cast<u32x4*>(Zh + row * (kD / 4) + 8 * lq);
+        __builtin_nontemporal_store((u32x4{cw[0], cw[1], cw[2], cw[3]}), out);
+        __builtin_nontemporal_store((u32x4{cw[4], cw[5], cw[6], cw[7]}), out + 1);
     }
 }
 
@@ -1020,22 +1027,12 @@ __device__ __forceinline__ void split3_bf16x2(float x0, float x1, uint32_t& hi, 
     lo = pk_bf16(s0, s1);
 }
 
-// A raw buffer resource over n bytes at p (no stride, 32-bit data format word): loads through
-// it take a scalar and a lane byte offset, and an offset past n reads zero.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t head_buffer(const void* p, int n) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, n, 0x00020000);
-}
 // Word w of code row r in the LDS copy of a head's codes (32 words a row, no padding): the
 // 16-byte chunk index is XORed with (r / 2) % 8, so that 16 consecutive rows read at the
 // same chunk hit 16 different bank groups, and a row's 32 words stay in one bank sweep.
 __device__ __forceinline__ int zs_word(int r, int w) { return r * (kD / 4) + (w ^ (4 * ((r >> 1) & 7))); }
 // Slot of value column c in the staged corrections: column 32(m/4) + 4ct + m%4 at 16ct + m.
 __device__ __forceinline__ int ut_slot(int c) { return 16 * ((c >> 2) & 7) + 4 * (c >> 5) + (c & 3); }
-// max(m, |a|, |b|) with NaN-propagating maxima (v_maximum3_f32, whose inputs need no
-// canonicalizing; a NaN leaves the row's codes unspecified, as for any non-finite row).
-__device__ __forceinline__ float max3_abs(float m, float a, float b) {
-    return __builtin_elementwise_maximum(__builtin_elementwise_maximum(m, __builtin_fabsf(a)), __builtin_fabsf(b));
-}
 
 // ---- the last step of the window for scalar gates (GDN), bf16 keys and W <= 16.
 // The decay of record j is a scalar, so it moves onto the correction:
