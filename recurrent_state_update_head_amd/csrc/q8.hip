@@ -383,15 +383,16 @@ __device__ __forceinline__ float max3_abs(float m, float a, float b) {
 // 8(l%16) .. +7 with two 128-bit LDS loads and ends up holding the 32 consecutive columns
 // 32(l/16) .. +31 of its row: result i of tile ct is column 32(l/16) + 8i + ct. All operands
 // of a band are loaded before its MFMAs. Rows of KE / Us past the last record are zero;
-// zcoef[r] = a_r / 127 Gamma_{1:W, r}; Zs holds the old codes (row stride kZsStride); the
-// new codes of a lane's 32 columns leave straight from its registers as two 16-byte stores.
-template <int kWmax>
-__device__ __forceinline__ void form_and_requantize(const float* KE, const float* Us, const uint32_t* Zs,
+// zcoef[r] = a_r / 127 Gamma_{1:W, r}; old_codes(a, zo) gives the lane's 8 old code words of
+// band a (row 16 (2 wave + a) + l%16, words 8(l/16) .. +7); the new codes of those 32 columns
+// leave straight from the lane's registers as two 16-byte stores.
+template <int kWmax, typename OldCodes>
+__device__ __forceinline__ void form_and_requantize(const float* KE, const float* Us, OldCodes old_codes,
                                                     const float* zcoef, float* __restrict__ Ah,
                                                     uint32_t* __restrict__ Zh, int wave, int lane) {
     constexpr int kSteps = kWmax / 4;
     const int lr = lane & 15, lq = lane >> 4;
-    for (int a = 0; a < 2; ++a) {  // one 16-row band at a time: 8 accumulators live
+    auto band = [&](int a) {  // one 16-row band at a time: 8 accumulators live
         const int row = 16 * (2 * wave + a) + lr;
         float eb[kSteps];
 #pragma unroll
@@ -399,8 +400,7 @@ __device__ __forceinline__ void form_and_requantize(const float* KE, const float
             eb[s] = KE[(4 * s + lq) * kD + row];
         // old codes of columns 32 lq .. +31: dword d holds columns 32 lq + 4d .. +3
         uint32_t zo[8];
-#pragma unroll
-        for (int d = 0; d < 8; ++d) zo[d] = Zs[row * kZsStride + 8 * lq + d];
+        old_codes(a, zo);
         const float zc = zcoef[row];
         f32x4 acc[8];
 #pragma unroll
@@ -444,7 +444,9 @@ __device__ __forceinline__ void form_and_requantize(const float* KE, const float
         u32x4* out = reinterpret_cast<u32x4*>(Zh + row * (kD / 4) + 8 * lq);
         __builtin_nontemporal_store((u32x4{cw[0], cw[1], cw[2], cw[3]}), out);
         __builtin_nontemporal_store((u32x4{cw[4], cw[5], cw[6], cw[7]}), out + 1);
-    }
+    };
+    band(0);
+    band(1);
 }
 
 // ---- the last step of the window (pos = W - 1): the step itself, then S_W of eq. 4
@@ -603,7 +605,13 @@ __global__ __launch_bounds__(kThreads) void q8_boundary_kernel(
     __syncthreads();
 
     // ---- S_W = Gamma_{1:W} S^_0 + sum_j Gamma_{j+1:W} k_j u_j^T, requantized.
-    form_and_requantize<kWmax>(KE, Us, Zs, zcoef, A + vec_off, Zh, wave, lane);
+    const int lr = lane & 15, lq = lane >> 4;
+    auto old_codes = [&](int a, uint32_t(&zo)[8]) {
+        const uint32_t* src = Zs + (16 * (2 * wave + a) + lr) * kZsStride + 8 * lq;
+#pragma unroll
+        for (int d = 0; d < 8; ++d) zo[d] = src[d];
+    };
+    form_and_requantize<kWmax>(KE, Us, old_codes, zcoef, A + vec_off, Zh, wave, lane);
 }
 
 // ---- RWKV7 on the per-window int8 state, two records per token (LeapQuant, App. A: an
@@ -617,6 +625,8 @@ __global__ __launch_bounds__(kThreads) void q8_boundary_kernel(
 // Every token, the last one too, appends its two records; at the end of the window a
 // second launch requantizes S_W from all 2W records.
 constexpr int kRwkv7Rec = 32;  // records per window: two per token, W <= 16
+// Dynamic LDS of the requantizer: decayed keys and corrections of up to kRwkv7Rec records.
+__host__ __device__ constexpr int requant_lds_floats() { return 2 * kRwkv7Rec * kD; }
 
 template <typename T>
 __global__ __launch_bounds__(kThreads) void rwkv7_q8_step_kernel(
@@ -950,11 +960,10 @@ __global__ __launch_bounds__(kThreads) void q8_requant_kernel(int nrec, int rec_
     __shared__ float zcoef[kD];
     float* KE = dyn_lds;
     float* Us = KE + kRwkv7Rec * kD;
-    uint32_t* Zs = reinterpret_cast<uint32_t*>(Us + kRwkv7Rec * kD);
 
     const int h = head_of_block(blockIdx.x, gridDim.x), tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
-    const int c4 = lane & 31, ro = lane >> 5;
+    const int lr = lane & 15, lq = lane >> 4;
     const int r = tid & (kD - 1);
     const bool first = tid < kD;
     const size_t vec_off = static_cast<size_t>(h) * kD;
@@ -973,15 +982,23 @@ __global__ __launch_bounds__(kThreads) void q8_requant_kernel(int nrec, int rec_
     const float ar = A[vec_off + r];
     (void)ar_half_row;
     (void)ar;
-    uint32_t zw[kRowsPerThread];
+    // the old codes go straight into the layout of the MFMA results (no sweep needs them
+    // first): band a, row 16 (2 wave + a) + lr, words 8 lq .. +7, two 16-byte loads
+    uint32_t zr[2][8];
 #pragma unroll
-    for (int it = 0; it < kRowsPerThread; ++it)
-        zw[it] = __builtin_nontemporal_load(Zh + q8_row(it, wave, ro) * (kD / 4) + c4);
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            const u32x4 w = __builtin_nontemporal_load(
+                reinterpret_cast<const u32x4*>(Zh + (16 * (2 * wave + a) + lr) * (kD / 4) + 8 * lq) + hh);
+            zr[a][4 * hh + 0] = w.x;
+            zr[a][4 * hh + 1] = w.y;
+            zr[a][4 * hh + 2] = w.z;
+            zr[a][4 * hh + 3] = w.w;
+        }
     sk.store(KE, tid);
     su.store(Us, tid);
     for (int i = nrec * kD + tid; i < kRwkv7Rec * kD; i += kThreads) Us[i] = 0.f;
-#pragma unroll
-    for (int it = 0; it < kRowsPerThread; ++it) Zs[q8_row(it, wave, ro) * kZsStride + c4] = zw[it];
     __syncthreads();
     if constexpr (kPerKey) {  // both halves of each key row's records at once
         const float G = kdec.apply(KE, nrec, 1.f, tid);
@@ -995,7 +1012,11 @@ __global__ __launch_bounds__(kThreads) void q8_requant_kernel(int nrec, int rec_
     if (first)
         for (int j = nrec; j < kRwkv7Rec; ++j) KE[j * kD + r] = 0.f;
     __syncthreads();
-    form_and_requantize<kRwkv7Rec>(KE, Us, Zs, zcoef, A + vec_off, Zh, wave, lane);
+    auto old_codes = [&](int a, uint32_t(&zo)[8]) {
+#pragma unroll
+        for (int d = 0; d < 8; ++d) zo[d] = zr[a][d];
+    };
+    form_and_requantize<kRwkv7Rec>(KE, Us, old_codes, zcoef, A + vec_off, Zh, wave, lane);
 }
 
 // Three bf16 parts of an fp32 value: hi = bf16(x), mid = bf16(x - hi), lo = bf16(x - hi - mid).
@@ -1434,7 +1455,7 @@ static hipError_t launch_rwkv7_window_t(const StepArgs& a, const WindowArgs& w, 
                        static_cast<const T*>(kappa), a.gate, erase, a.y);
     if (hipError_t e = hipGetLastError()) return e;
     if (w.pos < w.W - 1) return hipSuccess;
-    const int floats = boundary_lds_floats(kRwkv7Rec);
+    const int floats = requant_lds_floats();
     static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(q8_requant_kernel<true, T>),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize,
                                                        static_cast<int>(sizeof(float) * floats));
@@ -1456,7 +1477,7 @@ static hipError_t launch_dp_window_t(const StepArgs& a, const WindowArgs& w, hip
                            w.Z, w.A, static_cast<const bf16_t*>(w.Kbuf), w.Ubuf, w.Gbuf);
         return hipGetLastError();
     }
-    const int floats = boundary_lds_floats(kRwkv7Rec);
+    const int floats = requant_lds_floats();
     static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(q8_requant_kernel<false, T>),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize,
                                                        static_cast<int>(sizeof(float) * floats));
