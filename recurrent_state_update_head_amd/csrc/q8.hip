@@ -379,13 +379,16 @@ __device__ __forceinline__ float max3_abs(float m, float a, float b) {
 // transpose with v_mfma_f32_16x16x4f32 (A from lane l is A[l%16][l/16], B is B[l/16][l%16],
 // result i of lane l is D[4(l/16)+i][l%16]). Wave w owns key rows 32w .. 32w+31 as two bands
 // of 16 (B = decayed keys KE, one row per lane l%16); value-column tile ct (A = corrections
-// Us) takes the columns 8m + ct, m = 0..15, so that lane l reads the corrections of columns
-// 8(l%16) .. +7 with two 128-bit LDS loads and ends up holding the 32 consecutive columns
-// 32(l/16) .. +31 of its row: result i of tile ct is column 32(l/16) + 8i + ct. All operands
+// Us) takes the columns col_base(m) + ct, m = 0..15, col_base(4g + i) = 64 (i / 2) + 16g +
+// 8 (i % 2), so that lane l reads the corrections of 8 consecutive columns with two 128-bit
+// LDS loads, and result i of tile ct is column col_base(4(l/16) + i) + ct: lane l ends up with
+// the code words 4(l/16) .. +3 and 16 + 4(l/16) .. +3 of its row, so that each of its two
+// 16-byte stores fills 64 contiguous bytes of the row with its 3 neighbours. All operands
 // of a band are loaded before its MFMAs. Rows of KE / Us past the last record are zero;
 // zcoef[r] = a_r / 127 Gamma_{1:W, r}; old_codes(a, zo) gives the lane's 8 old code words of
-// band a (row 16 (2 wave + a) + l%16, words 8(l/16) .. +7); the new codes of those 32 columns
-// leave straight from the lane's registers as two 16-byte stores.
+// band a (row 16 (2 wave + a) + l%16, words 4(l/16) .. +3 in zo[0..3] and 16 + 4(l/16) .. +3 in
+// zo[4..7]); the new codes of those 32 columns leave straight from the lane's registers.
+__device__ __forceinline__ int col_base(int m) { return 64 * ((m & 3) >> 1) + 16 * (m >> 2) + 8 * (m & 1); }
 template <int kWmax, typename OldCodes>
 __device__ __forceinline__ void form_and_requantize(const float* KE, const float* Us, OldCodes old_codes,
                                                     const float* zcoef, float* __restrict__ Ah,
@@ -398,7 +401,7 @@ __device__ __forceinline__ void form_and_requantize(const float* KE, const float
 #pragma unroll
         for (int s = 0; s < kSteps; ++s)
             eb[s] = KE[(4 * s + lq) * kD + row];
-        // old codes of columns 32 lq .. +31: dword d holds columns 32 lq + 4d .. +3
+        // old codes: word d (d = 2i + hh) holds columns col_base(4 lq + i) + 4hh .. +3
         uint32_t zo[8];
         old_codes(a, zo);
         const float zc = zcoef[row];
@@ -412,7 +415,7 @@ __device__ __forceinline__ void form_and_requantize(const float* KE, const float
         // them across both bands would take 16 kWmax registers)
 #pragma unroll
         for (int s = 0; s < kSteps; ++s) {
-            const float* src = Us + (4 * s + lq) * kD + 8 * lr;
+            const float* src = Us + (4 * s + lq) * kD + col_base(lr);
             const f32x4 ua[2] = {*reinterpret_cast<const f32x4*>(src), *reinterpret_cast<const f32x4*>(src + 4)};
 #pragma unroll
             for (int ct = 0; ct < 8; ++ct)
@@ -433,7 +436,7 @@ __device__ __forceinline__ void form_and_requantize(const float* KE, const float
         m = fmaxf(m0, m1);
         const float sc = m > 0.f ? __fdiv_rn(127.f, m) : 0.f;
         if (lq == 0) Ah[row] = m;
-        // word 2i + hh of the lane's 8 holds columns 32 lq + 8i + 4hh .. +3
+        // word 2i + hh of the lane's 8 holds columns col_base(4 lq + i) + 4hh .. +3
         uint32_t cw[8];
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -441,9 +444,9 @@ __device__ __forceinline__ void form_and_requantize(const float* KE, const float
             for (int hh = 0; hh < 2; ++hh)
                 cw[2 * i + hh] = code_word_in_range(acc[4 * hh + 0][i] * sc, acc[4 * hh + 1][i] * sc,
                                                     acc[4 * hh + 2][i] * sc, acc[4 * hh + 3][i] * sc);
-        u32x4* out = reinterpret_cast<u32x4*>(Zh + row * (kD / 4) + 8 * lq);
-        __builtin_nontemporal_store((u32x4{cw[0], cw[1], cw[2], cw[3]}), out);
-        __builtin_nontemporal_store((u32x4{cw[4], cw[5], cw[6], cw[7]}), out + 1);
+        uint32_t* out = Zh + row * (kD / 4) + 4 * lq;
+        __builtin_nontemporal_store((u32x4{cw[0], cw[1], cw[2], cw[3]}), reinterpret_cast<u32x4*>(out));
+        __builtin_nontemporal_store((u32x4{cw[4], cw[5], cw[6], cw[7]}), reinterpret_cast<u32x4*>(out + 16));
     };
     band(0);
     band(1);
@@ -607,9 +610,9 @@ __global__ __launch_bounds__(kThreads) void q8_boundary_kernel(
     // ---- S_W = Gamma_{1:W} S^_0 + sum_j Gamma_{j+1:W} k_j u_j^T, requantized.
     const int lr = lane & 15, lq = lane >> 4;
     auto old_codes = [&](int a, uint32_t(&zo)[8]) {
-        const uint32_t* src = Zs + (16 * (2 * wave + a) + lr) * kZsStride + 8 * lq;
+        const uint32_t* src = Zs + (16 * (2 * wave + a) + lr) * kZsStride + 4 * lq;
 #pragma unroll
-        for (int d = 0; d < 8; ++d) zo[d] = src[d];
+        for (int d = 0; d < 8; ++d) zo[d] = src[d < 4 ? d : 12 + d];
     };
     form_and_requantize<kWmax>(KE, Us, old_codes, zcoef, A + vec_off, Zh, wave, lane);
 }
@@ -983,14 +986,14 @@ __global__ __launch_bounds__(kThreads) void q8_requant_kernel(int nrec, int rec_
     (void)ar_half_row;
     (void)ar;
     // the old codes go straight into the layout of the MFMA results (no sweep needs them
-    // first): band a, row 16 (2 wave + a) + lr, words 8 lq .. +7, two 16-byte loads
+    // first): band a, row 16 (2 wave + a) + lr, words 4 lq .. +3 and 16 + 4 lq .. +3
     uint32_t zr[2][8];
 #pragma unroll
     for (int a = 0; a < 2; ++a)
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
             const u32x4 w = __builtin_nontemporal_load(
-                reinterpret_cast<const u32x4*>(Zh + (16 * (2 * wave + a) + lr) * (kD / 4) + 8 * lq) + hh);
+                reinterpret_cast<const u32x4*>(Zh + (16 * (2 * wave + a) + lr) * (kD / 4) + 4 * lq + 16 * hh));
             zr[a][4 * hh + 0] = w.x;
             zr[a][4 * hh + 1] = w.y;
             zr[a][4 * hh + 2] = w.z;
@@ -1052,8 +1055,12 @@ __device__ __forceinline__ void split3_bf16x2(float x0, float x1, uint32_t& hi, 
 // 16-byte chunk index is XORed with (r / 2) % 8, so that 16 consecutive rows read at the
 // same chunk hit 16 different bank groups, and a row's 32 words stay in one bank sweep.
 __device__ __forceinline__ int zs_word(int r, int w) { return r * (kD / 4) + (w ^ (4 * ((r >> 1) & 7))); }
-// Slot of value column c in the staged corrections: column 32(m/4) + 4ct + m%4 at 16ct + m.
-__device__ __forceinline__ int ut_slot(int c) { return 16 * ((c >> 2) & 7) + 4 * (c >> 5) + (c & 3); }
+// Slot of value column c in the staged corrections: tile ct, A row m = 4g + i takes the code
+// word 4g + ct (ct < 4) or 16 + 4g + ct - 4 (ct >= 4), column 4 word + i, stored at 16ct + m.
+__device__ __forceinline__ int ut_slot(int c) {
+    const int w = c >> 2;
+    return 16 * ((w & 3) + 4 * (w >> 4)) + 4 * ((w >> 2) & 3) + (c & 3);
+}
 
 // ---- the last step of the window for scalar gates (GDN), bf16 keys and W <= 16.
 // The decay of record j is a scalar, so it moves onto the correction:
@@ -1228,11 +1235,12 @@ __global__ __launch_bounds__(kThreads) void q8_boundary_bf16_kernel(
     __syncthreads();
 
     // ---- S_W on the matrix cores. Wave w owns key rows 32w .. 32w+31 as two bands of
-    // 16 (B = keys, key row 16 band + l%16). Tile ct takes the value columns
-    // 32(m/4) + 4ct + m%4, m = 0..15 (A = scaled corrections, A row m from lane m of each
-    // lane group; ut_slot stores column 32(m/4) + 4ct + m%4 at 16ct + m): result i of lane l
-    // is then column 32(l/16) + 4ct + i, so lane l ends up holding code words 8(l/16) .. +7 of
-    // its row, two 16-byte chunks that go straight to memory.
+    // 16 (B = keys, key row 16 band + l%16). Tile ct takes, for A row m = 4g + i (A = scaled
+    // corrections, row m from lane m of each lane group), the value column 4 word + i with
+    // word 4g + ct (ct < 4) or 16 + 4g + ct - 4 (ct >= 4); ut_slot stores it at 16ct + m.
+    // Result i of lane l is then in code word 4(l/16) + ct or 16 + 4(l/16) + ct - 4: lane l
+    // holds words 4(l/16) .. +3 and 16 + 4(l/16) .. +3 of its row, and each of its two 16-byte
+    // stores fills 64 contiguous bytes of the row with its 3 neighbours.
     const int lr = lane & 15, lq = lane >> 4, blk = lq & 1;
     for (int a = 0; a < 2; ++a) {
         const int row = 16 * (2 * wave + a) + lr;
@@ -1241,8 +1249,8 @@ __global__ __launch_bounds__(kThreads) void q8_boundary_bf16_kernel(
         // half (lq >= 2) supply zero keys, so whatever they read as corrections drops out
         const bf16x8 bv_lo = lq < 2 ? bv : __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
         const float zc = zcoef[row];
-        const u32x4 zlo = *reinterpret_cast<const u32x4*>(&Zs[zs_word(row, 8 * lq)]);
-        const u32x4 zhi = *reinterpret_cast<const u32x4*>(&Zs[zs_word(row, 8 * lq + 4)]);
+        const u32x4 zlo = *reinterpret_cast<const u32x4*>(&Zs[zs_word(row, 4 * lq)]);
+        const u32x4 zhi = *reinterpret_cast<const u32x4*>(&Zs[zs_word(row, 16 + 4 * lq)]);
         f32x4 acc[8];
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct) {
@@ -1273,9 +1281,9 @@ __global__ __launch_bounds__(kThreads) void q8_boundary_bf16_kernel(
 #pragma unroll
         for (int ct = 0; ct < 8; ++ct)
             cw[ct] = code_word_in_range(acc[ct].x * sc, acc[ct].y * sc, acc[ct].z * sc, acc[ct].w * sc);
-        u32x4* out = reinterpret_cast<u32x4*>(Zh + row * (kD / 4) + 8 * lq);
-        __builtin_nontemporal_store((u32x4{cw[0], cw[1], cw[2], cw[3]}), out);
-        __builtin_nontemporal_store((u32x4{cw[4], cw[5], cw[6], cw[7]}), out + 1);
+        uint32_t* out = Zh + row * (kD / 4) + 4 * lq;
+        __builtin_nontemporal_store((u32x4{cw[0], cw[1], cw[2], cw[3]}), reinterpret_cast<u32x4*>(out));
+        __builtin_nontemporal_store((u32x4{cw[4], cw[5], cw[6], cw[7]}), reinterpret_cast<u32x4*>(out + 16));
     }
 }
 
