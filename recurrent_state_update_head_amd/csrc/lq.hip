@@ -106,24 +106,24 @@ __global__ __launch_bounds__(kThreads) void lq_step_kernel(
     const bool first = tid < kD;
 
     // ---- loads: records, tokens, gates, inputs, then the codes
-    uint32_t kc[4] = {0u, 0u, 0u, 0u};
-    if (0 < pos) {
-        const uint4 x = *reinterpret_cast<const uint4*>(Kbuf + rec0 + static_cast<size_t>(grp < pos ? grp : 0) * kD + 8 * ch);
+    // (unconditional, so that no branch makes the compiler wait for them: slots and tokens
+    // are clamped in bounds; what a clamped lane loads is never used or meets a zero coefficient)
+    uint32_t kc[4];
+    {  // (at pos 0 the lane's own input keys, loaded anyway)
+        const uint4 x = *reinterpret_cast<const uint4*>(
+            0 < pos ? Kbuf + rec0 + static_cast<size_t>(grp < pos ? grp : 0) * kD + 8 * ch : k + vec_off + 8 * ch);
         kc[0] = x.x; kc[1] = x.y; kc[2] = x.z; kc[3] = x.w;
     }
     f32x4 ur[2];
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
         const int j = owner + 8 * m;
-        ur[m] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (8 * m < pos)
-            ur[m] = *reinterpret_cast<const f32x4*>(Ubuf + rec0 + static_cast<size_t>(j < pos ? j : 0) * kD + 4 * c4);
+        ur[m] = *reinterpret_cast<const f32x4*>(8 * m < pos ? Ubuf + rec0 + static_cast<size_t>(j < pos ? j : 0) * kD + 4 * c4
+                                                           : Bcol + vec_off + 4 * c4);  // (the lane's scales: loaded anyway)
     }
     // token keys (groups 0..3, 8 keys per lane) and token values (owners 0..3, 4 columns)
-    uint4 ktw = {0u, 0u, 0u, 0u};
-    if (grp < kTok) ktw = *reinterpret_cast<const uint4*>(Kc + tok0 + grp * kD + 8 * ch);
-    uint2 utw = {0u, 0u};
-    if (owner < kTok) utw = *reinterpret_cast<const uint2*>(Uc + tok0 + owner * kD + 4 * c4);
+    const uint4 ktw = *reinterpret_cast<const uint4*>(Kc + tok0 + (grp < kTok ? grp : 0) * kD + 8 * ch);
+    const uint2 utw = *reinterpret_cast<const uint2*>(Uc + tok0 + (owner < kTok ? owner : 0) * kD + 4 * c4);
     float g_lane = 1.f;  // GDN: lane i holds the gate of record i
     Stager<float, kPerKey ? 16 * kD : 8> sg;
     if constexpr (kPerKey) sg.load(Gbuf + rec0, pos * kD, tid);
@@ -1220,9 +1220,12 @@ __global__ __launch_bounds__(kThreads) void lq_low_step_kernel(
     const size_t tok0 = static_cast<size_t>(h) * kT * kD;
 
     // ---- loads: record keys (group grp) and values (column cc), tokens, inputs, codes
-    uint32_t kc[4] = {0u, 0u, 0u, 0u};
-    if (0 < pos) {
-        const uint4 x = *reinterpret_cast<const uint4*>(Kbuf + rec0 + static_cast<size_t>(grp < pos ? grp : 0) * kD + 8 * ch);
+    // (unconditional, so that no branch makes the compiler wait for them: slots and tokens
+    // are clamped in bounds; what a clamped lane loads is never used or meets a zero coefficient)
+    uint32_t kc[4];
+    {  // (at pos 0 the lane's own input keys, loaded anyway)
+        const uint4 x = *reinterpret_cast<const uint4*>(
+            0 < pos ? Kbuf + rec0 + static_cast<size_t>(grp < pos ? grp : 0) * kD + 8 * ch : k + vec_off + 8 * ch);
         kc[0] = x.x; kc[1] = x.y; kc[2] = x.z; kc[3] = x.w;
     }
     float ucol[8];
@@ -1232,8 +1235,7 @@ __global__ __launch_bounds__(kThreads) void lq_low_step_kernel(
         const float ul = Ubuf[rec0 + static_cast<size_t>(j < pos ? j : 0) * kD + cc];  // slot clamped to 0: in bounds, no branch
         ucol[e] = j < pos ? ul : 0.f;
     }
-    uint4 ktw = {0u, 0u, 0u, 0u};
-    if (first) ktw = *reinterpret_cast<const uint4*>(Kc + tok0 + (grp & (kT - 1)) * kD + 8 * ch);
+    const uint4 ktw = *reinterpret_cast<const uint4*>(Kc + tok0 + (grp & (kT - 1)) * kD + 8 * ch);
     half_t utv[kTh];
 #pragma unroll
     for (int e = 0; e < kTh; ++e) utv[e] = Uc[tok0 + (kTh * half + e) * kD + cc];
@@ -1436,8 +1438,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
         const uint32_t kb = j < pos ? kl : 0u;
         kcol[e >> 1] = (e & 1) ? (kcol[e >> 1] | (kb << 16)) : kb;
     }
-    uint4 ktw = {0u, 0u, 0u, 0u};
-    if (first) ktw = *reinterpret_cast<const uint4*>(Kc + tok0 + (grp & (kT - 1)) * kD + 8 * ch);
+    const uint4 ktw = *reinterpret_cast<const uint4*>(Kc + tok0 + (grp & (kT - 1)) * kD + 8 * ch);
     half_t tokv[kT];  // token t at row / column cc (threads < 128: keys; threads >= 128: values)
 #pragma unroll
     for (int t = 0; t < kT; ++t) tokv[t] = (first ? Kc : Uc)[tok0 + t * kD + cc];

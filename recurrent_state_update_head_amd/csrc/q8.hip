@@ -186,15 +186,20 @@ __global__ __launch_bounds__(kThreads) void q8_step_kernel(
 #pragma unroll
     for (int s = 0; s < kKSlots; ++s) {
         const int j = grp + 16 * s;
-        if (16 * s < pos) kc[s].load(Kbuf + rec0 + static_cast<size_t>(j < pos ? j : 0) * kD + 8 * ch);
+        // unconditional, so that no branch makes the compiler wait for it (a branch around a
+        // load ends in a wait for every load before it): a lane past the last record reads
+        // slot 0, a slot group with no record at all reads this lane's own input keys (loaded
+        // anyway, so no extra traffic); such keys are never used
+        kc[s].load(16 * s < pos ? Kbuf + rec0 + static_cast<size_t>(j < pos ? j : 0) * kD + 8 * ch : k + vec_off + 8 * ch);
     }
     f32x4 ur[kUSlots];
 #pragma unroll
     for (int m = 0; m < kUSlots; ++m) {
         const int j = owner + 8 * m;
-        ur[m] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (8 * m < pos)
-            ur[m] = *reinterpret_cast<const f32x4*>(Ubuf + rec0 + static_cast<size_t>(j < pos ? j : 0) * kD + 4 * c4);
+        // unconditional as the keys (a slot group with no record reads the lane's scales); a
+        // clamped slot's values meet a zero coefficient
+        ur[m] = *reinterpret_cast<const f32x4*>(8 * m < pos ? Ubuf + rec0 + static_cast<size_t>(j < pos ? j : 0) * kD + 4 * c4
+                                                           : A + vec_off + 4 * c4);
     }
     float g_lane = 1.f;  // GDN: lane i holds the gate of record i
     Stager<float, kPerKey ? kWmax * kD : 8> sg;
@@ -659,15 +664,20 @@ __global__ __launch_bounds__(kThreads) void rwkv7_q8_step_kernel(
 #pragma unroll
     for (int s = 0; s < kKSlots; ++s) {
         const int j = grp + 16 * s;
-        if (16 * s < nrec) kc[s].load(Kbuf + rec0 + static_cast<size_t>(j < nrec ? j : 0) * kD + 8 * ch);
+        // unconditional, so that no branch makes the compiler wait for it (a branch around a
+        // load ends in a wait for every load before it): a lane past the last record reads
+        // slot 0, a slot group with no record at all reads this lane's own input keys (loaded
+        // anyway, so no extra traffic); such keys are never used
+        kc[s].load(16 * s < nrec ? Kbuf + rec0 + static_cast<size_t>(j < nrec ? j : 0) * kD + 8 * ch : k + vec_off + 8 * ch);
     }
     f32x4 ur[kUSlots];
 #pragma unroll
     for (int m = 0; m < kUSlots; ++m) {
         const int j = owner + 8 * m;
-        ur[m] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (8 * m < nrec)
-            ur[m] = *reinterpret_cast<const f32x4*>(Ubuf + rec0 + static_cast<size_t>(j < nrec ? j : 0) * kD + 4 * c4);
+        // unconditional as the keys (a slot group with no record reads the lane's scales); a
+        // clamped slot's values meet a zero coefficient
+        ur[m] = *reinterpret_cast<const f32x4*>(8 * m < nrec ? Ubuf + rec0 + static_cast<size_t>(j < nrec ? j : 0) * kD + 4 * c4
+                                                              : A + vec_off + 4 * c4);
     }
     Stager<float, kRwkv7Rec * kD> sg;
     sg.load(Gbuf + rec0, nrec * kD, tid);
@@ -824,15 +834,20 @@ __global__ __launch_bounds__(kThreads) void dp_q8_step_kernel(
 #pragma unroll
     for (int s = 0; s < kKSlots; ++s) {
         const int j = grp + 16 * s;
-        if (16 * s < nrec) kc[s].load(Kbuf + rec0 + static_cast<size_t>(j < nrec ? j : 0) * kD + 8 * ch);
+        // unconditional, so that no branch makes the compiler wait for it (a branch around a
+        // load ends in a wait for every load before it): a lane past the last record reads
+        // slot 0, a slot group with no record at all reads this lane's own input keys (loaded
+        // anyway, so no extra traffic); such keys are never used
+        kc[s].load(16 * s < nrec ? Kbuf + rec0 + static_cast<size_t>(j < nrec ? j : 0) * kD + 8 * ch : k + key_off + 8 * ch);
     }
     f32x4 ur[kUSlots];
 #pragma unroll
     for (int m = 0; m < kUSlots; ++m) {
         const int j = owner + 8 * m;
-        ur[m] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (8 * m < nrec)
-            ur[m] = *reinterpret_cast<const f32x4*>(Ubuf + rec0 + static_cast<size_t>(j < nrec ? j : 0) * kD + 4 * c4);
+        // unconditional as the keys (a slot group with no record reads the lane's scales); a
+        // clamped slot's values meet a zero coefficient
+        ur[m] = *reinterpret_cast<const f32x4*>(8 * m < nrec ? Ubuf + rec0 + static_cast<size_t>(j < nrec ? j : 0) * kD + 4 * c4
+                                                              : A + vec_off + 4 * c4);
     }
     const float g_lane = lane < nrec ? Gbuf[static_cast<size_t>(h) * R + lane] : 1.f;
     Raw8<T> xch[kX];  // the lane's 8 key rows of every read vector
