@@ -448,7 +448,8 @@ __device__ __forceinline__ void tile_sty(const TileRefitLds<kT, kBits>& L, const
         __syncthreads();
         // (with 8 tokens the slice is consumed two rows at a time: a fully unrolled loop loads
         // all of it, and Y, ahead of the products and runs out of registers)
-#pragma unroll(kT == 8 ? 4 : 8)
+        constexpr int kSliceUnroll = kT == 8 ? 4 : 8;
+#pragma unroll kSliceUnroll
         for (int it = 0; it < 8; ++it) {
             const f32x4 sv = state_unit(L.half, 8 * it + ro, uu);
             const int row = 8 * (8 * hf + it) + ro;
