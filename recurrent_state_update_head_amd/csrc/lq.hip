@@ -16,6 +16,7 @@
 #include "kernels.hpp"
 #include "rsu_device.hpp"
 #include "codes.hpp"
+#include "decays.hpp"
 #include "swaps.hpp"
 
 namespace rsu {
@@ -92,6 +93,7 @@ __global__ __launch_bounds__(kThreads) void lq_step_kernel(
     __shared__ f32x2 rowv[kD];
     __shared__ f32x2 coef[16];
     __shared__ f32x2 ctok[kTok];
+    __shared__ __align__(16) float gtot[kPerKey ? kD : 4];  // KDA: the product of all record gates per key
     __shared__ f32x2 red[4][kD];
     __shared__ float kq_part[2];
 
@@ -159,23 +161,26 @@ __global__ __launch_bounds__(kThreads) void lq_step_kernel(
             Gall *= gi;
         }
     } else {
+        // the gates' suffix products per key column, in place; the column totals in gtot
         sg.store(gs_lds, tid);
         __syncthreads();
-#pragma unroll
-        for (int e = 0; e < 8; ++e) Ge[e] = Gt[e] = 1.f;
-        for (int i = pos - 1; i >= 0; --i) {
-            const f32x4 lo = *reinterpret_cast<const f32x4*>(gs_lds + i * kD + 8 * ch);
-            const f32x4 hi = *reinterpret_cast<const f32x4*>(gs_lds + i * kD + 8 * ch + 4);
-            const bool after = i > grp;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                Gt[e] *= lo[e];
-                Gt[e + 4] *= hi[e];
-                Ge[e] = after ? Ge[e] * lo[e] : Ge[e];
-                Ge[e + 4] = after ? Ge[e + 4] * hi[e] : Ge[e + 4];
-            }
+        if (first) {
+            Gall = column_suffix_products<16>(gs_lds, pos, r);
+            gtot[r] = Gall;
         }
-        for (int i = pos - 1; i >= 0; --i) Gall *= gs_lds[i * kD + r];
+        __syncthreads();
+        const bool rec = grp < pos;
+        const f32x4 lo = rec ? *reinterpret_cast<const f32x4*>(gs_lds + grp * kD + 8 * ch) : f32x4{1.f, 1.f, 1.f, 1.f};
+        const f32x4 hi = rec ? *reinterpret_cast<const f32x4*>(gs_lds + grp * kD + 8 * ch + 4) : f32x4{1.f, 1.f, 1.f, 1.f};
+        const f32x4 tlo = *reinterpret_cast<const f32x4*>(gtot + 8 * ch);
+        const f32x4 thi = *reinterpret_cast<const f32x4*>(gtot + 8 * ch + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            Ge[e] = lo[e];
+            Ge[e + 4] = hi[e];
+            Gt[e] = tlo[e];
+            Gt[e + 4] = thi[e];
+        }
     }
     auto gcur = [&](int e) { return e < 4 ? gch_lo[e] : gch_hi[e - 4]; };
     const uint32_t kcw[4] = {kchw.x, kchw.y, kchw.z, kchw.w};
@@ -1206,6 +1211,7 @@ __global__ __launch_bounds__(kThreads) void lq_low_step_kernel(
     using Cfg = LowBits<kBits>;
     constexpr int kT = Cfg::kT, kTh = Cfg::kTh;
     __shared__ f32x2 ctok[kT];
+    __shared__ __align__(16) float gtot[kPerKey ? kD : 4];  // KDA: the product of all record gates per key
     __shared__ f32x2 red[4][kD];
     __shared__ f32x2 recp[kD];
     __shared__ float kq_part[2];
@@ -1281,23 +1287,26 @@ __global__ __launch_bounds__(kThreads) void lq_low_step_kernel(
             Gall *= gi;
         }
     } else {
+        // the gates' suffix products per key column, in place; the column totals in gtot
         sg.store(gs_lds, tid);
         __syncthreads();
-#pragma unroll
-        for (int e = 0; e < 8; ++e) Ge[e] = Gt[e] = 1.f;
-        for (int i = pos - 1; i >= 0; --i) {
-            const f32x4 lo = *reinterpret_cast<const f32x4*>(gs_lds + i * kD + 8 * ch);
-            const f32x4 hi = *reinterpret_cast<const f32x4*>(gs_lds + i * kD + 8 * ch + 4);
-            const bool after = i > grp;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                Gt[e] *= lo[e];
-                Gt[e + 4] *= hi[e];
-                Ge[e] = after ? Ge[e] * lo[e] : Ge[e];
-                Ge[e + 4] = after ? Ge[e + 4] * hi[e] : Ge[e + 4];
-            }
+        if (first) {
+            Gall = column_suffix_products<16>(gs_lds, pos, cc);
+            gtot[cc] = Gall;
         }
-        for (int i = pos - 1; i >= 0; --i) Gall *= gs_lds[i * kD + cc];
+        __syncthreads();
+        const bool rec = grp < pos;
+        const f32x4 lo = rec ? *reinterpret_cast<const f32x4*>(gs_lds + grp * kD + 8 * ch) : f32x4{1.f, 1.f, 1.f, 1.f};
+        const f32x4 hi = rec ? *reinterpret_cast<const f32x4*>(gs_lds + grp * kD + 8 * ch + 4) : f32x4{1.f, 1.f, 1.f, 1.f};
+        const f32x4 tlo = *reinterpret_cast<const f32x4*>(gtot + 8 * ch);
+        const f32x4 thi = *reinterpret_cast<const f32x4*>(gtot + 8 * ch + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            Ge[e] = lo[e];
+            Ge[e + 4] = hi[e];
+            Gt[e] = tlo[e];
+            Gt[e + 4] = thi[e];
+        }
     }
     auto gcur = [&](int e) { return e < 4 ? gch_lo[e] : gch_hi[e - 4]; };
     const uint32_t kcw[4] = {kchw.x, kchw.y, kchw.z, kchw.w};

@@ -19,6 +19,7 @@
 #include "kernels.hpp"
 #include "rsu_device.hpp"
 #include "codes.hpp"
+#include "decays.hpp"
 
 namespace rsu {
 
@@ -157,7 +158,8 @@ struct KeyDecays {
 // corrections u_j are loaded straight into the registers of the row-owners that
 // add c_j u_j to their column partials. Scalar gates (GDN) are multiplied from
 // register copies (lane i of every wave holds g_i), so the step needs two
-// workgroup barriers; per-key gates (KDA) are staged in LDS first (one more).
+// workgroup barriers; per-key gates (KDA) are staged in LDS first and turned there into
+// their suffix products per key column (two more).
 template <bool kPerKey, int kWmax, typename T>
 __global__ __launch_bounds__(kThreads) void q8_step_kernel(
     int W, int pos, const int8_t* __restrict__ Z, const float* __restrict__ A, T* __restrict__ Kbuf,
@@ -224,15 +226,16 @@ __global__ __launch_bounds__(kThreads) void q8_step_kernel(
     for (int it = 0; it < kRowsPerThread; ++it)
         zw[it] = __builtin_nontemporal_load(Zh + q8_row(it, wave, ro) * (kD / 4) + c4);
 
-    if constexpr (kPerKey) {
-        sg.store(gs_lds, tid);
-        __syncthreads();
-    }
-
     // ---- decays: G_s = prod of the record gates after record grp + 16 s (from the
     // newest down), Gall = prod of all record gates; the current gate comes on top
     float Gs[kKSlots][kPerKey ? 8 : 1];
     float Gall = 1.f;
+    if constexpr (kPerKey) {  // the gates' suffix products per key column, in place
+        sg.store(gs_lds, tid);
+        __syncthreads();
+        if (first) Gall = column_suffix_products<kWmax>(gs_lds, pos, r);
+        __syncthreads();
+    }
     if constexpr (!kPerKey) {
         // suffix scan over the record lanes (g = 1 from record pos on): the product of the
         // gates after each record, gathered for the records of this lane's groups
@@ -244,20 +247,18 @@ __global__ __launch_bounds__(kThreads) void q8_step_kernel(
     } else {
 #pragma unroll
         for (int s = 0; s < kKSlots; ++s) {
+            const int j = grp + 16 * s;
 #pragma unroll
             for (int e = 0; e < 8; ++e) Gs[s][e] = 1.f;
-            if (16 * s >= pos) continue;
-            for (int i = pos - 1; i > grp + 16 * s; --i) {
-                const f32x4 lo = *reinterpret_cast<const f32x4*>(gs_lds + i * kD + 8 * ch);
-                const f32x4 hi = *reinterpret_cast<const f32x4*>(gs_lds + i * kD + 8 * ch + 4);
+            if (j >= pos) continue;
+            const f32x4 lo = *reinterpret_cast<const f32x4*>(gs_lds + j * kD + 8 * ch);
+            const f32x4 hi = *reinterpret_cast<const f32x4*>(gs_lds + j * kD + 8 * ch + 4);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    Gs[s][e] *= lo[e];
-                    Gs[s][e + 4] *= hi[e];
-                }
+            for (int e = 0; e < 4; ++e) {
+                Gs[s][e] = lo[e];
+                Gs[s][e + 4] = hi[e];
             }
         }
-        for (int i = pos - 1; i >= 0; --i) Gall *= gs_lds[i * kD + r];
     }
 
     // ---- record coefficients, reduced over the 16 lanes of each group
@@ -698,29 +699,29 @@ __global__ __launch_bounds__(kThreads) void rwkv7_q8_step_kernel(
     for (int it = 0; it < kRowsPerThread; ++it)
         zw[it] = __builtin_nontemporal_load(Zh + q8_row(it, wave, ro) * (kD / 4) + c4);
 
+    // ---- decays: Gs = product of the gates of the records after record grp + 16 s, per key of
+    // the lane's 8; Gall = product of all record gates at row r (suffix products per key
+    // column, in place)
     sg.store(gs_lds, tid);
     __syncthreads();
-
-    // ---- decays: Gs = product of the gates of the records after record grp + 16 s, per key of
-    // the lane's 8; Gall = product of all record gates at row r
+    float Gall = 1.f;
+    if (first) Gall = column_suffix_products<kRwkv7Rec>(gs_lds, nrec, r);
+    __syncthreads();
     float Gs[kKSlots][8];
 #pragma unroll
     for (int s = 0; s < kKSlots; ++s) {
+        const int j = grp + 16 * s;
 #pragma unroll
         for (int e = 0; e < 8; ++e) Gs[s][e] = 1.f;
-        if (16 * s >= nrec) continue;
-        for (int i = nrec - 1; i > grp + 16 * s; --i) {
-            const f32x4 lo = *reinterpret_cast<const f32x4*>(gs_lds + i * kD + 8 * ch);
-            const f32x4 hi = *reinterpret_cast<const f32x4*>(gs_lds + i * kD + 8 * ch + 4);
+        if (j >= nrec) continue;
+        const f32x4 lo = *reinterpret_cast<const f32x4*>(gs_lds + j * kD + 8 * ch);
+        const f32x4 hi = *reinterpret_cast<const f32x4*>(gs_lds + j * kD + 8 * ch + 4);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                Gs[s][e] *= lo[e];
-                Gs[s][e + 4] *= hi[e];
-            }
+        for (int e = 0; e < 4; ++e) {
+            Gs[s][e] = lo[e];
+            Gs[s][e + 4] = hi[e];
         }
     }
-    float Gall = 1.f;
-    for (int i = nrec - 1; i >= 0; --i) Gall *= gs_lds[i * kD + r];
 
     // ---- record coefficients against both read vectors, over the 16 lanes of each group
 #pragma unroll
