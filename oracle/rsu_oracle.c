@@ -206,6 +206,11 @@ void oracle_deltaproduct_step(int64_t nh, int dk, int dv, int n, double *S, cons
  * fp32 exactly as the device does it: the value is first rounded to fp32, the
  * reciprocal scale 127/a_i is one correctly rounded fp32 division, the product
  * one fp32 multiplication, the rounding to nearest with ties to even.
+ * A row whose maximum is below 2^-64 (where 127/a_i can overflow fp32: a
+ * subnormal or nearly subnormal row) is first scaled by 2^64, which is exact for
+ * its values and its maximum, and the same decision is taken on the scaled row;
+ * a_i is stored unscaled. (The pages are silent on such rows; this keeps the
+ * codes those of rne(S_ij * 127 / a_i) instead of saturating them.)
  * If w_out is not NULL it receives the exact pre-rounding code S_ij*127/a_i in
  * fp64 (used to find elements near a rounding tie).
  */
@@ -221,11 +226,13 @@ void oracle_q8_quantize(int64_t nrows, int ncols, const double *X, int8_t *Z, fl
             if (xf > amax)
                 amax = xf;
         }
+        const float f = amax < 0x1p-64f ? 0x1p64f : 1.0f;
         volatile float num = 127.0f;
-        float scale = amax > 0.0f ? num / amax : 0.0f;
+        float scale = amax > 0.0f ? num / (amax * f) : 0.0f;
         a[r] = amax;
         for (int j = 0; j < ncols; ++j) {
-            float w = (float)x[j] * scale;
+            volatile float xs = (float)x[j] * f; /* exact */
+            float w = xs * scale;
             float zr = rintf(w);
             if (zr > 127.0f)
                 zr = 127.0f;

@@ -180,6 +180,22 @@ def test_quantizer_round_half_even_ties():
     assert Z[0].tolist() == [127, 0, 2, 2, 0, -2, -2, 3, -4, 126, 0]
 
 
+@pytest.mark.parametrize("unit_exp", [-149, -130, -100, -71, -64, -40])
+def test_quantizer_tiny_rows_keep_exact_codes(unit_exp):
+    """Rows whose maximum is subnormal or tiny: values j * 2^e for every odd j in [-127, 127]
+    have the exact codes j (a = 127 * 2^e), however small 2^e is. Without the exact 2^64
+    rescaling of rows below 2^-64, 127 / a overflows fp32 and every code saturates."""
+    j = np.arange(-127, 128, 2).astype(np.float64)
+    row = j * 2.0 ** unit_exp
+    row[5] = 0.0
+    X = np.stack([row, np.linspace(-1.0, 1.0, 128)])
+    Z, a = oracle.q8_quantize(X)
+    want = j.astype(np.int64)
+    want[5] = 0
+    assert a[0] == np.float32(127 * 2.0 ** unit_exp)
+    assert Z[0].astype(np.int64).tolist() == want.tolist()
+
+
 def test_quantizer_absmax_zero_rows_and_bound():
     X = RNG.standard_normal((64, 128))
     X[3] = 0.0
