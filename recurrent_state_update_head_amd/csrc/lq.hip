@@ -581,13 +581,28 @@ __device__ __forceinline__ void lq_refit_tiles(const TileRefitLds<kT, kBits>& L,
         if (lr == 0) *reinterpret_cast<u32x4*>(L.cmax + wave * kD + 16 * ct + 4 * lq) = m;
     }
     __syncthreads();
+    uint32_t* cmw = reinterpret_cast<uint32_t*>(L.cmax);
     if (tid < kD) {
-        const uint32_t* cm = reinterpret_cast<const uint32_t*>(L.cmax);
-        const float B = __uint_as_float(max(max(cm[tid], cm[kD + tid]), max(cm[2 * kD + tid], cm[3 * kD + tid])));
+        const float B = __uint_as_float(max(max(cmw[tid], cmw[kD + tid]), max(cmw[2 * kD + tid], cmw[3 * kD + tid])));
         Bh[tid] = B;
-        L.sc[tid] = B > 0.f ? __fdiv_rn(static_cast<float>(Cfg::kQmax), B) : 0.f;
+        // a column maximum below 2^-64 scales the column by 2^64 first (exact). The factor goes
+        // to slot tid of cmax and the wave's "any such column" flag (lane 0) to slot kD + tid:
+        // slots only this thread has read.
+        const float f = tiny_factor(B);
+        L.sc[tid] = B > 0.f ? __fdiv_rn(static_cast<float>(Cfg::kQmax), B * f) : 0.f;
+        L.cmax[tid] = f;
+        const bool any_tiny = __ballot(f != 1.f) != 0;
+        if (lane == 0) cmw[kD + tid] = any_tiny;
     }
     __syncthreads();
+    if (__builtin_amdgcn_readfirstlane(cmw[kD] | cmw[kD + 64])) {  // rare
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct) {
+            const f32x4 f = *reinterpret_cast<const f32x4*>(L.cmax + 16 * ct + 4 * lq);
+            s[0][ct] *= f;
+            s[1][ct] *= f;
+        }
+    }
 
     // codes of the lane's 4 columns in each of its two rows, staged so that whole rows leave together
 #pragma unroll

@@ -39,11 +39,12 @@ __device__ __forceinline__ uint32_t quant_code(float x, float scale) {
 __device__ __forceinline__ int q8_row(int it, int wave, int ro) { return 8 * it + 2 * wave + ro; }
 
 // Requantize a head's fp32 tile held in registers (int8 layout) into Zh / Ah:
-// a_i = max_j |S_ij|, scale = 127 / a_i (one correctly rounded fp32 division),
-// z = clamp(rne(S * scale), -127, 127); a zero row gets a_i = 0 and z = 0.
-// Every thread of the workgroup must call it (it contains a barrier).
+// a_i = max_j |S_ij|, scale = 127 / (a_i f_i) (one correctly rounded fp32 division, f_i =
+// tiny_factor(a_i)), z = clamp(rne((S f_i) * scale), -127, 127); a zero row gets a_i = 0 and
+// z = 0. scale_s receives (scale, f_i) per row. Every thread of the workgroup must call it (it
+// contains a barrier).
 __device__ __forceinline__ void requantize_tile(const f32x4 (&s)[kRowsPerThread], uint32_t* Zh,
-                                                float* Ah, float* scale_s, int wave, int lane) {
+                                                float* Ah, f32x2* scale_s, int wave, int lane) {
     const int c4 = lane & 31, ro = lane >> 5;
     float amax[kRowsPerThread];
 #pragma unroll
@@ -57,16 +58,19 @@ __device__ __forceinline__ void requantize_tile(const f32x4 (&s)[kRowsPerThread]
     for (int it = 0; it < kRowsPerThread; ++it) mine = (c4 == it) ? amax[it] : mine;
     if (c4 < kRowsPerThread) {
         const int r = q8_row(c4, wave, ro);
-        scale_s[r] = mine > 0.f ? __fdiv_rn(127.f, mine) : 0.f;
+        const float f = tiny_factor(mine);
+        scale_s[r] = f32x2{mine > 0.f ? __fdiv_rn(127.f, mine * f) : 0.f, f};
         Ah[r] = mine;
     }
     __syncthreads();
 #pragma unroll
     for (int it = 0; it < kRowsPerThread; ++it) {
         const int r = q8_row(it, wave, ro);
-        const float sc = scale_s[r];
-        const uint32_t w = quant_code(s[it].x, sc) | (quant_code(s[it].y, sc) << 8) |
-                           (quant_code(s[it].z, sc) << 16) | (quant_code(s[it].w, sc) << 24);
+        const f32x2 sf = scale_s[r];
+        const float sc = sf.x;
+        const f32x4 x = s[it] * sf.y;  // exact
+        const uint32_t w = quant_code(x.x, sc) | (quant_code(x.y, sc) << 8) |
+                           (quant_code(x.z, sc) << 16) | (quant_code(x.w, sc) << 24);
         __builtin_nontemporal_store(w, Zh + r * (kD / 4) + c4);
     }
 }
@@ -74,7 +78,7 @@ __device__ __forceinline__ void requantize_tile(const f32x4 (&s)[kRowsPerThread]
 __global__ __launch_bounds__(kThreads) void q8_quantize_kernel(const float* __restrict__ S,
                                                                int8_t* __restrict__ Z,
                                                                float* __restrict__ A) {
-    __shared__ float scale_s[kD];
+    __shared__ f32x2 scale_s[kD];
     const int h = head_of_block(blockIdx.x, gridDim.x), tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
     const int c4 = lane & 31, ro = lane >> 5;
@@ -440,7 +444,13 @@ __device__ __forceinline__ void form_and_requantize(const float* KE, const float
         float m = max_xor16(fmaxf(m0, m1));
         swap32(m, m0, m1);
         m = fmaxf(m0, m1);
-        const float sc = m > 0.f ? __fdiv_rn(127.f, m) : 0.f;
+        // a row maximum below 2^-64 scales the row by 2^64 first (exact; rare, so it is a branch)
+        const float f = tiny_factor(m);
+        if (f != 1.f) {
+#pragma unroll
+            for (int ct = 0; ct < 8; ++ct) acc[ct] *= f;
+        }
+        const float sc = m > 0.f ? __fdiv_rn(127.f, m * f) : 0.f;
         if (lq == 0) Ah[row] = m;
         // word 2i + hh of the lane's 8 holds columns col_base(4 lq + i) + 4hh .. +3
         uint32_t cw[8];
@@ -1291,7 +1301,13 @@ __global__ __launch_bounds__(kThreads) void q8_boundary_bf16_kernel(
         float m = max_xor16(fmaxf(m0, m1));
         swap32(m, m0, m1);
         m = fmaxf(m0, m1);
-        const float sc = m > 0.f ? __fdiv_rn(127.f, m) : 0.f;
+        // a row maximum below 2^-64 scales the row by 2^64 first (exact; rare, so it is a branch)
+        const float f = tiny_factor(m);
+        if (f != 1.f) {
+#pragma unroll
+            for (int ct = 0; ct < 8; ++ct) acc[ct] *= f;
+        }
+        const float sc = m > 0.f ? __fdiv_rn(127.f, m * f) : 0.f;
         if (lq == 0) A[vec_off + row] = m;
         uint32_t cw[8];
 #pragma unroll
@@ -1405,7 +1421,13 @@ __global__ __launch_bounds__(kThreads) void q8_requant_bf16_kernel(int nrec, int
         float m0, m1;
         swap32(m, m0, m1);
         m = fmaxf(m0, m1);
-        const float sc = m > 0.f ? __fdiv_rn(127.f, m) : 0.f;
+        // a row maximum below 2^-64 scales the row by 2^64 first (exact; rare, so it is a branch)
+        const float f = tiny_factor(m);
+        if (f != 1.f) {
+#pragma unroll
+            for (int ct = 0; ct < 8; ++ct) acc[ct] *= f;
+        }
+        const float sc = m > 0.f ? __fdiv_rn(127.f, m * f) : 0.f;
         if (lq == 0) A[vec_off + row] = m;
 #pragma unroll
         for (int ct = 0; ct < 8; ++ct)

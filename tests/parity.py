@@ -406,12 +406,13 @@ def window_step(w: wl.Workload, pos: int, buf, d, y):
 
 
 def run_window(w: wl.Workload, sample: int | None = None, steps: int | None = None,
-               tie_band: float = 1e-3):
+               tie_band: float = 1e-3, a_abs: float = 0.0):
     """Int8 per-window path on the GPU against the oracle, teacher-forced per window:
     at every window start the oracle restarts from the GPU's (Z, a), so a 1-LSB
     rounding-tie flip at one boundary is not carried into later windows.
-    Returns a dict: max y error, max row-scale relative error, and code statistics
-    at the boundaries (max |dZ|, flips, flips outside the tie band)."""
+    Returns a dict: max y error, max row-scale relative error (beyond an absolute slack
+    a_abs), and code statistics at the boundaries (max |dZ|, flips, flips outside the tie
+    band)."""
     m = rsu()
     B, H, W = w.B, w.H, w.W
     steps = w.steps if steps is None else steps
@@ -449,7 +450,8 @@ def run_window(w: wl.Workload, sample: int | None = None, steps: int | None = No
             Zg = take(buf["Z"], hd, (128, 128)).astype(np.int32)
             ag = take(buf["A"], hd, (128,)).astype(np.float64)
             aref = ref.a.astype(np.float64)
-            st["a"] = max(st["a"], float(np.max(np.abs(ag - aref) / np.maximum(aref, 1e-30))))
+            st["a"] = max(st["a"], float(np.max(np.maximum(np.abs(ag - aref) - a_abs, 0.0) /
+                                                np.maximum(aref, 1e-300))))
             diff = Zg - ref.Z.astype(np.int32)
             flips = diff != 0
             near_tie = np.abs(np.abs(wcode - np.floor(wcode)) - 0.5) < tie_band
@@ -501,7 +503,10 @@ def check_stepq_pack(X, mag, omega, rep, err, tie_band=1e-4, mat_rel=1e-6, rel_b
     sqrt(m_i / w_i), except within a relative band of a rounding midpoint. Codes:
     recomputed from the GPU's own R; a code may differ by 1 only within tie_band (plus
     mat_rel * mag in code units) of a tie. Column factors: recomputed in fp64 from the
-    GPU's own R and codes; the GPU's C is their fp16 rounding up to a band at midpoints."""
+    GPU's own R and codes; the GPU's C is their fp16 rounding up to a band at midpoints.
+    A column whose range a_j is below 2^-64 has a column factor of about a_j / 7, which is
+    zero in fp16 on both sides (and checked as such), so it decodes to zero whatever its
+    codes: those codes are not compared (the GPU caps 7 / a_j where it overflows fp32)."""
     from oracle import stepq as sqo
     z, r, c = rep
     W = sqo.row_weights(omega)
@@ -522,6 +527,7 @@ def check_stepq_pack(X, mag, omega, rep, err, tie_band=1e-4, mat_rel=1e-6, rel_b
         code[:, cols] = U[:, cols] * (qmax / a[cols])[None, :]
         Zr = np.clip(np.rint(code), -qmax, qmax).astype(np.int64)
         dz = np.abs(z[i] - Zr)
+        dz[:, a < 2.0 ** -64] = 0
         err["z_maxdiff"] = max(err["z_maxdiff"], int(dz.max()))
         flips = dz > 0
         err["z_flips"] += int(flips.sum())
@@ -529,6 +535,9 @@ def check_stepq_pack(X, mag, omega, rep, err, tie_band=1e-4, mat_rel=1e-6, rel_b
         rr = np.where(live, r[i], np.inf)[:, None]
         band[:, cols] += mat_rel * qmax * (mag[i][:, cols] / rr) / a[cols][None, :]
         near = np.abs(np.abs(code - np.floor(code)) - 0.5) < band
+        tiny = a < 2.0 ** -64
+        flips[:, tiny] = False
+        err["tiny_cols"] = err.get("tiny_cols", 0) + int(tiny.sum())
         err["z_flips_outside_band"] += int((flips & ~near).sum())
         zf = z[i].astype(np.float64)
         cp = sqo.column_factors(X[i], r[i], zf, W[i])

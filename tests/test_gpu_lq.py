@@ -16,7 +16,7 @@ import pytest
 import torch
 
 import workloads as wl
-from parity import DEV, TOL_Q8, lq_host, new_lq_buffers, rsu, run_lq, say
+from parity import DEV, TOL_Q8, check_lq_refit, lq_host, new_lq_buffers, rsu, run_lq, say
 
 pytestmark = pytest.mark.gpu
 
@@ -172,6 +172,37 @@ def test_lq_low_bit_kda_b128_h32_full_size_sampled(cid):
 def test_lq_quantize_start_iterations(n_iter0):
     w = wl.custom(wl.WORKLOADS[6], B=2, H=3, W=16, steps=0)
     _check(run_lq(w, n_iter0=n_iter0, steps=0), f"quantize n_iter0={n_iter0}", boundaries=False)
+
+
+@pytest.mark.parametrize("cid,fn", [(6, "gdn_lq_quantize"), (16, "gdn_lq6_quantize"), (12, "gdn_lq4_quantize"),
+                                    (9, "kda_lq_quantize")])
+def test_lq_quantize_tiny_column(cid, fn):
+    """A value column whose smoothed maximum B lies near 2^-123, where qmax / B overflows fp32
+    (the column's state entries are at most 2^-126: subnormal or nearly; no outliers, so the
+    smoothing factors c lie in [0.11, 0.14]). The column is quantized after scaling by 2^64:
+    its codes follow the oracle's like any other column's, and its largest code is qmax."""
+    from oracle import lq as lqo
+    m = rsu()
+    w = wl.custom(wl.WORKLOADS[cid], B=1, H=3, W=16, steps=0, outliers=False)
+    S0 = wl.initial_state(w)
+    col = 9
+    e = np.ceil(np.log2(np.abs(S0[:, :, col]).max(axis=1).astype(np.float64))).astype(np.int32)
+    S0[:, :, col] = np.ldexp(S0[:, :, col], (-126 - e)[:, None])
+    say(f"[lq] {fn}: tiny column {col}")
+    buf = new_lq_buffers(w)
+    getattr(m, fn)(torch.from_numpy(S0).to(DEV).view(1, 3, 128, 128), 8, buf["Z"], buf["B"], buf["C"],
+                   buf["Kc"], buf["Uc"])
+    hd = torch.arange(w.heads, device=DEV)
+    rep = lq_host(buf, hd)
+    qmax = lqo.qmax_of(w.bits)
+    Bg = rep[1][:, col]
+    assert np.all(Bg > 0) and np.all(Bg < 2.0 ** -121.4), Bg
+    assert np.all(np.abs(rep[0][:, :, col]).max(axis=1) == qmax)
+    err = {"tok": 0.0, "tok_k": 0.0, "tok_u": 0.0, "c": 0.0, "B": 0.0, "z_maxdiff": 0, "z_flips": 0,
+           "z_flips_outside_band": 0}
+    walsh = np.broadcast_to(lqo.walsh_start(r=8 if w.bits == 4 else 4), (w.heads, 128, 8 if w.bits == 4 else 4))
+    check_lq_refit(S0.astype(np.float64), walsh, 8, rep, err, qmax=qmax)
+    _check(dict(err, y=0.0), f"{fn} tiny column", boundaries=False)
 
 
 def test_lq_zero_state_gives_zero_tokens_and_payload():

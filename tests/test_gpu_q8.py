@@ -45,6 +45,47 @@ def test_quantize_bit_exact_with_ties_and_zero_rows():
     assert not Z[0, 0, 3].any() and A[0, 0, 3] == 0
 
 
+def test_quantize_tiny_and_subnormal_rows_keep_their_codes():
+    """Rows whose maximum lies below 2^-64, down to the subnormal range, where 127 / max
+    overflows fp32: the row is quantized after scaling by 2^64, so a row j 2^e (e = -149 ..
+    -40) gets the codes of the row j, and the whole call is bit-exact against the oracle."""
+    m = rsu()
+    g = torch.Generator().manual_seed(11)
+    S = torch.randn(1, 2, 128, 128, generator=g) * 0.02
+    base = (torch.arange(128) - 64).float()                   # j = -64 .. 63, exact in fp32
+    exps = list(range(-149, -39))                              # 110 rows, both sides of 2^-64
+    for i, e in enumerate(exps):
+        S[0, 0, i] = torch.ldexp(base, torch.tensor(e))
+    S[0, 0, 120] = base                                        # the twin at scale 1
+    S[0, 1, :64] = torch.ldexp(S[0, 1, :64], torch.tensor(-100))   # normal-range rows below 2^-64
+    S[0, 1, 64:96] = torch.ldexp(S[0, 1, 64:96], torch.tensor(-118))  # rows near 2^-123
+    Sd = S.to(DEV)
+    Z = torch.empty(1, 2, 128, 128, dtype=torch.int8, device=DEV)
+    A = torch.empty(1, 2, 128, device=DEV)
+    m.q8_quantize(Sd, Z, A)
+    Zg, Ag = Z.cpu().numpy().reshape(-1, 128, 128), A.cpu().numpy().reshape(-1, 128)
+    Zr, ar = oracle.q8_quantize(S.double().numpy().reshape(-1, 128, 128))
+    np.testing.assert_array_equal(Zg, Zr)
+    np.testing.assert_array_equal(Ag, ar)
+    for i, e in enumerate(exps):
+        np.testing.assert_array_equal(Zg[0, i], Zg[0, 120], err_msg=f"row 64 * 2^{e}")
+        assert Ag[0, i] == np.ldexp(np.float32(64.0), e)
+
+
+@pytest.mark.parametrize("label,idx,over", [("gdn bf16", 4, {}), ("gdn f32", 4, {"qkv": "f32"}),
+                                            ("kda", 4, {"variant": "kda", "gate_lo": 0.8, "gate_hi": 1.0}),
+                                            ("rwkv7", 11, {}), ("deltaproduct", 15, {})])
+def test_window_tiny_row(label, idx, over):
+    """A key row with maximum in (2^-123, 2^-122] that no record writes to (every key is zero
+    there): each boundary re-forms it from its codes alone and requantizes it below 2^-121.4,
+    where 127 / max overflows fp32. Its codes must come back unchanged and its scale within
+    1e-5 relative of the oracle's beyond the absolute error of a subnormal coefficient: a_r / 127
+    Gamma_r is formed in fp32 by up to four multiplications, each off by at most 2^-150 once it
+    is subnormal, and the scale is 127 times it."""
+    w = wl.custom(wl.WORKLOADS[idx], B=2, H=3, steps=2 * wl.WORKLOADS[idx].W + 1, tiny_row=5, **over)
+    _check(run_window(w, a_abs=4 * 127 * 2.0 ** -150), f"{label} tiny row 5")
+
+
 @pytest.mark.parametrize("variant,W,B,H", [("gdn", 16, 3, 7), ("gdn", 5, 2, 3), ("gdn", 1, 2, 2),
                                            ("kda", 16, 2, 5), ("kda", 3, 1, 3),
                                            ("gdn", 16, 10, 10)])

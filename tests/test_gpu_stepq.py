@@ -112,6 +112,28 @@ def test_stepq_zero_rows_and_columns():
     _assert_ok(run_stepq(w, steps=2, S0=S0))
 
 
+def test_stepq_tiny_column():
+    """A column whose range a_j = max_i |x_ij| / r_i lies near 2^-128, where 7 / a_j overflows
+    fp32 (the column's state entries are at most 2^-130): its fp16 column factor, about
+    a_j / 7, is zero on both sides, so it decodes to zero whatever its codes; the rest of the
+    packing is checked as usual."""
+    w = wl.custom(BASE, B=2, H=3)
+    S0 = wl.initial_state(w)
+    col = 21
+    e = np.ceil(np.log2(np.abs(S0[:, :, col]).max(axis=1).astype(np.float64))).astype(np.int32)
+    S0[:, :, col] = np.ldexp(S0[:, :, col], (-130 - e)[:, None])
+    say("stepq tiny column")
+    m = rsu()
+    buf = new_stepq_buffers(w)
+    m.stepq_pack(torch.from_numpy(S0).to(DEV).view(w.B, w.H, 128, 128),
+                 torch.from_numpy(wl.row_influence(w)).to(DEV).view(w.B, w.H, 128), buf["Z"], buf["R"], buf["C"])
+    z, r, c = stepq_host(buf, torch.arange(w.heads, device=DEV))
+    assert not c[:, col].any()
+    err = run_stepq(w, steps=1, S0=S0)
+    assert err["tiny_cols"] == w.heads
+    _assert_ok(err)
+
+
 def test_stepq_empty_batch():
     m = rsu()
     w = wl.custom(BASE, B=0, H=4)

@@ -53,6 +53,9 @@ class Workload:
     outliers: bool = False
     bits: int = 8         # code width of the LeapQuant window format (8, 6, or 4 with 8 tokens)
     n: int = 1            # DeltaProduct: delta-rule sub-steps per token
+    tiny_row: int = -1    # >= 0: that key row of every S_0 is scaled by a power of two to a maximum
+                          # in (2^-123, 2^-122], where 127 / max overflows fp32, and every key (k,
+                          # kappa, the sub-step keys) is zero there, so no record writes to the row
 
     @property
     def heads(self) -> int:
@@ -180,7 +183,19 @@ def initial_state(wl: Workload) -> np.ndarray:
     nchunks = (n + _CHUNK - 1) // _CHUNK
     with concurrent.futures.ThreadPoolExecutor(_THREADS) as ex:
         list(ex.map(fill, range(nchunks)))
+    if wl.tiny_row >= 0:
+        row = S[:, wl.tiny_row, :]
+        e = np.ceil(np.log2(np.abs(row).max(axis=1).astype(np.float64))).astype(np.int32)
+        S[:, wl.tiny_row, :] = np.ldexp(row, (-122 - e)[:, None])
     return S
+
+
+def _keys(wl: Workload, x: np.ndarray) -> np.ndarray:
+    """Unit keys over d_k (fp64 normalisation, then the input dtype), zero at tiny_row."""
+    x = x.astype(np.float64)
+    if wl.tiny_row >= 0:
+        x[..., wl.tiny_row] = 0.0
+    return _cast(wl, _unit_rows(x))
 
 
 def step_inputs(wl: Workload, t: int) -> dict:
@@ -198,7 +213,7 @@ def step_inputs(wl: Workload, t: int) -> dict:
     n = wl.heads
     f32 = np.float32
     q = _cast(wl, _unit_rows(_rng(wl, _TAG_Q, t).standard_normal((n, DK), dtype=f32).astype(np.float64)))
-    k = _cast(wl, _unit_rows(_rng(wl, _TAG_K, t).standard_normal((n, DK), dtype=f32).astype(np.float64)))
+    k = _keys(wl, _rng(wl, _TAG_K, t).standard_normal((n, DK), dtype=f32))
     v = _cast(wl, _rng(wl, _TAG_V, t).standard_normal((n, DV), dtype=f32))
     gshape = (n, DK) if wl.per_key_gate else (n,)
     lo, hi = wl.gate_lo, wl.gate_hi
@@ -207,16 +222,14 @@ def step_inputs(wl: Workload, t: int) -> dict:
     beta = _rng(wl, _TAG_BETA, t).random((n,), dtype=f32)
     out = {"q": q, "k": k, "v": v, "gate": gate, "beta": beta}
     if wl.variant == "rwkv7":
-        out["kappa"] = _cast(wl, _unit_rows(_rng(wl, _TAG_KAPPA, t).standard_normal((n, DK), dtype=f32)
-                                            .astype(np.float64)))
+        out["kappa"] = _keys(wl, _rng(wl, _TAG_KAPPA, t).standard_normal((n, DK), dtype=f32))
         out["a"] = _rng(wl, _TAG_A, t).random((n, DK), dtype=f32)
     if wl.variant == "deltaproduct":
         # sub-step 0 takes the draws above; sub-steps 1 .. n-1 draw their own key, value and
         # strength the same way: k [heads, n, d_k], v [heads, n, d_v], beta [heads, n]
         ks, vs, bs = [k], [v], [beta]
         for i in range(1, wl.n):
-            ks.append(_cast(wl, _unit_rows(_rng(wl, _TAG_SUB_K, wl.n * t + i).standard_normal((n, DK), dtype=f32)
-                                           .astype(np.float64))))
+            ks.append(_keys(wl, _rng(wl, _TAG_SUB_K, wl.n * t + i).standard_normal((n, DK), dtype=f32)))
             vs.append(_cast(wl, _rng(wl, _TAG_SUB_V, wl.n * t + i).standard_normal((n, DV), dtype=f32)))
             bs.append(_rng(wl, _TAG_SUB_BETA, wl.n * t + i).random((n,), dtype=f32))
         out["k"] = np.ascontiguousarray(np.stack(ks, axis=1))
