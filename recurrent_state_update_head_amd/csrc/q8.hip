@@ -359,18 +359,20 @@ __device__ __forceinline__ uint32_t code_word(float a, float b, float c, float d
     return pack_low_bytes(code_bits(a), code_bits(b), code_bits(c), code_bits(d));
 }
 
-// The same without the clamp, for values w = x * fp32(127 / m) with |x| <= m, m the absmax
-// of the row the x belong to: |w| <= m fp32(127 / m) <= 127 (1 + 2^-24) rounds to at most
-// 127, so the integer is already a code (m = 0 gives w = 0). Non-finite rows give
+// The same without the clamp, for the products w = x * fp32(127 / (m f)) of a row whose absmax
+// is m, with f = tiny_factor(m) (1, or 2^64 for m below 2^-64): the code of w f, rounded once
+// by the magic add inside one fma. w f is exact wherever w is normal (f is a power of two) and
+// then equals fp32((x f) * fp32(127 / (m f))), the product for the scaled row; a subnormal w
+// gives |w f| < 2^-62, code 0 either way. |x| <= m bounds |w f| by 127 (1 + 2^-24), which rounds
+// to at most 127, so the integer is already a code (m = 0 gives w = 0). Non-finite rows give
 // unspecified codes.
-__device__ __forceinline__ uint32_t code_bits_in_range(float w) {
-#pragma clang fp contract(off)
+__device__ __forceinline__ uint32_t code_bits_in_range(float w, float f) {
     constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23
-    return static_cast<uint32_t>(__float_as_int(w + kMagic));
+    return static_cast<uint32_t>(__float_as_int(__builtin_fmaf(w, f, kMagic)));
 }
-__device__ __forceinline__ uint32_t code_word_in_range(float a, float b, float c, float d) {
-    return pack_low_bytes(code_bits_in_range(a), code_bits_in_range(b), code_bits_in_range(c),
-                          code_bits_in_range(d));
+__device__ __forceinline__ uint32_t code_word_in_range(f32x4 w, float f) {
+    return pack_low_bytes(code_bits_in_range(w.x, f), code_bits_in_range(w.y, f), code_bits_in_range(w.z, f),
+                          code_bits_in_range(w.w, f));
 }
 
 // A raw buffer resource over n bytes at p (no stride, 32-bit data format word): loads through
@@ -444,13 +446,11 @@ __device__ __forceinline__ void form_and_requantize(const float* KE, const float
         float m = max_xor16(fmaxf(m0, m1));
         swap32(m, m0, m1);
         m = fmaxf(m0, m1);
-        // a row maximum below 2^-64 scales the row by 2^64 first (exact; rare, so it is a branch)
+        // a row maximum below 2^-64 is decided as the row scaled by f = 2^64 (no branch: the
+        // factor enters the rounding fma)
         const float f = tiny_factor(m);
-        if (f != 1.f) {
-#pragma unroll
-            for (int ct = 0; ct < 8; ++ct) acc[ct] *= f;
-        }
-        const float sc = m > 0.f ? __fdiv_rn(127.f, m * f) : 0.f;
+        const float q = __fdiv_rn(127.f, m * f);  // (unconditional: a branch would split the block)
+        const float sc = m > 0.f ? q : 0.f;
         if (lq == 0) Ah[row] = m;
         // word 2i + hh of the lane's 8 holds columns col_base(4 lq + i) + 4hh .. +3
         uint32_t cw[8];
@@ -458,8 +458,8 @@ __device__ __forceinline__ void form_and_requantize(const float* KE, const float
         for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh)
-                cw[2 * i + hh] = code_word_in_range(acc[4 * hh + 0][i] * sc, acc[4 * hh + 1][i] * sc,
-                                                    acc[4 * hh + 2][i] * sc, acc[4 * hh + 3][i] * sc);
+                cw[2 * i + hh] = code_word_in_range(f32x4{acc[4 * hh + 0][i], acc[4 * hh + 1][i], acc[4 * hh + 2][i],
+                                                          acc[4 * hh + 3][i]} * sc, f);
         uint32_t* out = Zh + row * (kD / 4) + 4 * lq;
         __builtin_nontemporal_store((u32x4{cw[0], cw[1], cw[2], cw[3]}), reinterpret_cast<u32x4*>(out));
         __builtin_nontemporal_store((u32x4{cw[4], cw[5], cw[6], cw[7]}), reinterpret_cast<u32x4*>(out + 16));
@@ -1301,18 +1301,16 @@ __global__ __launch_bounds__(kThreads) void q8_boundary_bf16_kernel(
         float m = max_xor16(fmaxf(m0, m1));
         swap32(m, m0, m1);
         m = fmaxf(m0, m1);
-        // a row maximum below 2^-64 scales the row by 2^64 first (exact; rare, so it is a branch)
+        // a row maximum below 2^-64 is decided as the row scaled by f = 2^64 (no branch: the
+        // factor enters the rounding fma)
         const float f = tiny_factor(m);
-        if (f != 1.f) {
-#pragma unroll
-            for (int ct = 0; ct < 8; ++ct) acc[ct] *= f;
-        }
-        const float sc = m > 0.f ? __fdiv_rn(127.f, m * f) : 0.f;
+        const float q = __fdiv_rn(127.f, m * f);  // (unconditional: a branch would split the block)
+        const float sc = m > 0.f ? q : 0.f;
         if (lq == 0) A[vec_off + row] = m;
         uint32_t cw[8];
 #pragma unroll
         for (int ct = 0; ct < 8; ++ct)
-            cw[ct] = code_word_in_range(acc[ct].x * sc, acc[ct].y * sc, acc[ct].z * sc, acc[ct].w * sc);
+            cw[ct] = code_word_in_range(acc[ct] * sc, f);
         uint32_t* out = Zh + row * (kD / 4) + 4 * lq;
         __builtin_nontemporal_store((u32x4{cw[0], cw[1], cw[2], cw[3]}), reinterpret_cast<u32x4*>(out));
         __builtin_nontemporal_store((u32x4{cw[4], cw[5], cw[6], cw[7]}), reinterpret_cast<u32x4*>(out + 16));
@@ -1421,18 +1419,15 @@ __global__ __launch_bounds__(kThreads) void q8_requant_bf16_kernel(int nrec, int
         float m0, m1;
         swap32(m, m0, m1);
         m = fmaxf(m0, m1);
-        // a row maximum below 2^-64 scales the row by 2^64 first (exact; rare, so it is a branch)
+        // a row maximum below 2^-64 is decided as the row scaled by f = 2^64 (no branch: the
+        // factor enters the rounding fma)
         const float f = tiny_factor(m);
-        if (f != 1.f) {
-#pragma unroll
-            for (int ct = 0; ct < 8; ++ct) acc[ct] *= f;
-        }
-        const float sc = m > 0.f ? __fdiv_rn(127.f, m * f) : 0.f;
+        const float q = __fdiv_rn(127.f, m * f);  // (unconditional: a branch would split the block)
+        const float sc = m > 0.f ? q : 0.f;
         if (lq == 0) A[vec_off + row] = m;
 #pragma unroll
         for (int ct = 0; ct < 8; ++ct)
-            Zs[row * kZsStride + 4 * ct + lq] = code_word_in_range(acc[ct].x * sc, acc[ct].y * sc,
-                                                                   acc[ct].z * sc, acc[ct].w * sc);
+            Zs[row * kZsStride + 4 * ct + lq] = code_word_in_range(acc[ct] * sc, f);
     }
     wave_lds_sync();
 #pragma unroll
