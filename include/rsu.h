@@ -92,7 +92,10 @@ int kda_decode_step(const rsu_dims *dims, float *S, const void *q, const void *k
  *   a_i = max_j |S_ij| (fp32),  z_ij = clamp(rne(S_ij * (127 / a_i)), -127, 127),
  *   dequant = z_ij * a_i / 127;  a row of zeros gets a_i = 0 and z = 0.
  * The reciprocal 127/a_i is one correctly rounded fp32 division, the product
- * one fp32 multiplication, rounding is to nearest with ties to even.
+ * one fp32 multiplication, rounding is to nearest with ties to even. A row with
+ * a_i below 2^-64 (where 127/a_i can overflow fp32) is decided as that row and
+ * a_i multiplied by 2^64 (exact); a_i is stored unscaled. (The pages are silent
+ * on such rows; this keeps the codes of rne(S_ij * 127 / a_i).)
  *
  * q8_quantize: quantize S [B,H,d_k,d_v] fp32 into Z [B,H,d_k,d_v] int8 and
  * row_absmax [B,H,d_k] fp32 (the state at the start of the first window).
@@ -174,7 +177,8 @@ int kda_log_merge(const rsu_dims *dims, int C, int L, float *Sbase, float *lbar,
  * Kt = S V, Ut = V (MGS = modified Gram-Schmidt over the 4 columns in order), then
  * rounded to fp16; the residual R = S - Kt Ut^T (with the rounded tokens) gets
  * row_smooth_i = max(sqrt(mean_j |R_ij|), 1e-6) and the payload of R_ij / row_smooth_i,
- * rounded half to even into [-127, 127] per value column.
+ * rounded half to even into [-127, 127] per value column (a column whose absmax is
+ * below 2^-64 is decided scaled by 2^64, as for the per-row int8 state).
  *
  * gdn_lq_quantize: converts plain fp32 states S into the format; the fit starts
  *   from the first 4 Walsh columns ((-1)^popcount(i & t) / sqrt(d)). S is only read.
@@ -378,7 +382,10 @@ int deltaproduct_q8_window(const rsu_dims *dims, int n, int W, int pos, int8_t *
  * rounded half to even and clamped to [-7, 7] (0 where R_i or a_j is 0); C_j = fp16
  * of the weighted least squares sum_i w_i^2 R_i z_ij X_ij / sum_i w_i^2 R_i^2 z_ij^2
  * (0 for a column without nonzero codes). The row factor's formula is a reading
- * (the notes name SmoothQuant's fractional power; its square root is taken).
+ * (the notes name SmoothQuant's fractional power; its square root is taken). A column
+ * with a_j below 2^-64 has C_j (about a_j / 7) zero in fp16 and decodes to zero; its
+ * codes lie in [-7, 7] but are otherwise unspecified (7 / a_j is capped where it
+ * overflows fp32).
  *
  * stepq_pack: packs fp32 states S [B,H,d,d] (only read); dims->qkv_dtype is not used.
  * gdn_stepq_step / kda_stepq_step: one decode step on the packed state in place:
