@@ -297,6 +297,9 @@ def run_gpu(w: wl.Workload, steps: int, warmup: int, slots: bool = False, n_iter
     n_inputs = {"dense": w.steps, "stepq": w.steps, "q8_window": w.W, "lq_window": w.W, "log": w.M}[w.path]
     n_inputs = min(n_inputs, max(1, w.steps))
     x = _dev_inputs(w, n_inputs, torch, dev)
+    # the per-step views, made once: indexing five or six tensors in every step costs the host
+    # a few microseconds, which matters beside launches of 20-30 us
+    xv = [{name: t[i] for name, t in x.items()} for i in range(n_inputs)]
     y = torch.empty(B, H, 128, device=dev)
     S0 = torch.from_numpy(wl.initial_state(w)).to(dev).view(B, H, 128, 128)
     kda = w.per_key_gate
@@ -307,21 +310,21 @@ def run_gpu(w: wl.Workload, steps: int, warmup: int, slots: bool = False, n_iter
 
         def step():
             i = state["t"] % n_inputs
-            rsu.rwkv7_decode_step(S, x["q"][i], x["k"][i], x["v"][i], x["kappa"][i], x["gate"][i], x["a"][i], y)
+            rsu.rwkv7_decode_step(S, xv[i]["q"], xv[i]["k"], xv[i]["v"], xv[i]["kappa"], xv[i]["gate"], xv[i]["a"], y)
             state["t"] += 1
     elif w.path == "dense" and w.variant == "deltaproduct":
         S = S0
 
         def step():
             i = state["t"] % n_inputs
-            rsu.deltaproduct_decode_step(S, x["q"][i], x["k"][i], x["v"][i], x["gate"][i], x["beta"][i], y)
+            rsu.deltaproduct_decode_step(S, xv[i]["q"], xv[i]["k"], xv[i]["v"], xv[i]["gate"], xv[i]["beta"], y)
             state["t"] += 1
     elif w.path == "dense" and w.variant == "rwkv6":
         S = S0
 
         def step():
             i = state["t"] % n_inputs
-            rsu.rwkv6_decode_step(S, x["q"][i], x["k"][i], x["v"][i], x["gate"][i], y)
+            rsu.rwkv6_decode_step(S, xv[i]["q"], xv[i]["k"], xv[i]["v"], xv[i]["gate"], y)
             state["t"] += 1
     elif w.path == "dense":
         fn = rsu.kda_decode_step if kda else rsu.gdn_decode_step
@@ -329,7 +332,7 @@ def run_gpu(w: wl.Workload, steps: int, warmup: int, slots: bool = False, n_iter
 
         def step():
             i = state["t"] % n_inputs
-            fn(S, x["q"][i], x["k"][i], x["v"][i], x["gate"][i], x["beta"][i], y)
+            fn(S, xv[i]["q"], xv[i]["k"], xv[i]["v"], xv[i]["gate"], xv[i]["beta"], y)
             state["t"] += 1
     elif w.path == "stepq":
         Z = torch.empty(B, H, 128, 64, device=dev, dtype=torch.uint8)
@@ -350,12 +353,12 @@ def run_gpu(w: wl.Workload, steps: int, warmup: int, slots: bool = False, n_iter
 
             def step():
                 i = state["t"] % n_inputs
-                readout(Z, R, Cf, x["q"][i], x["k"][i], x["v"][i], x["gate"][i], x["beta"][i], u, y)
+                readout(Z, R, Cf, xv[i]["q"], xv[i]["k"], xv[i]["v"], xv[i]["gate"], xv[i]["beta"], u, y)
                 r1 = torch.cuda.Event()
                 r1.record(main)
                 with torch.cuda.stream(side):
                     side.wait_event(r1)
-                    repack(Z, R, Cf, om, x["k"][i], x["gate"][i], u)
+                    repack(Z, R, Cf, om, xv[i]["k"], xv[i]["gate"], u)
                     p1 = torch.cuda.Event()
                     p1.record(side)
                 main.wait_event(p1)
@@ -380,7 +383,7 @@ def run_gpu(w: wl.Workload, steps: int, warmup: int, slots: bool = False, n_iter
         else:
             def step():
                 i = state["t"] % n_inputs
-                fn(Z, R, Cf, om, x["q"][i], x["k"][i], x["v"][i], x["gate"][i], x["beta"][i], y)
+                fn(Z, R, Cf, om, xv[i]["q"], xv[i]["k"], xv[i]["v"], xv[i]["gate"], xv[i]["beta"], y)
                 state["t"] += 1
     elif w.path == "q8_window" and w.variant == "rwkv7":
         W = w.W
@@ -395,8 +398,8 @@ def run_gpu(w: wl.Workload, steps: int, warmup: int, slots: bool = False, n_iter
         def step():
             t = state["t"]
             i = t % n_inputs
-            rsu.rwkv7_q8_window(W, t % W, Z, A, Kb, Ub, Gb, x["q"][i], x["k"][i], x["v"][i], x["kappa"][i],
-                                x["gate"][i], x["a"][i], y)
+            rsu.rwkv7_q8_window(W, t % W, Z, A, Kb, Ub, Gb, xv[i]["q"], xv[i]["k"], xv[i]["v"], xv[i]["kappa"],
+                                xv[i]["gate"], xv[i]["a"], y)
             state["t"] += 1
     elif w.path == "q8_window" and w.variant == "deltaproduct":
         W, R = w.W, w.n * w.W
@@ -411,8 +414,8 @@ def run_gpu(w: wl.Workload, steps: int, warmup: int, slots: bool = False, n_iter
         def step():
             t = state["t"]
             i = t % n_inputs
-            rsu.deltaproduct_q8_window(W, t % W, Z, A, Kb, Ub, Gb, x["q"][i], x["k"][i], x["v"][i], x["gate"][i],
-                                       x["beta"][i], y)
+            rsu.deltaproduct_q8_window(W, t % W, Z, A, Kb, Ub, Gb, xv[i]["q"], xv[i]["k"], xv[i]["v"], xv[i]["gate"],
+                                       xv[i]["beta"], y)
             state["t"] += 1
     elif w.path == "q8_window":
         W = w.W
@@ -428,7 +431,7 @@ def run_gpu(w: wl.Workload, steps: int, warmup: int, slots: bool = False, n_iter
         def step():
             t = state["t"]
             i = t % n_inputs
-            fn(W, t % W, Z, A, Kb, Ub, Gb, x["q"][i], x["k"][i], x["v"][i], x["gate"][i], x["beta"][i], y)
+            fn(W, t % W, Z, A, Kb, Ub, Gb, xv[i]["q"], xv[i]["k"], xv[i]["v"], xv[i]["gate"], xv[i]["beta"], y)
             state["t"] += 1
     elif w.path == "lq_window":
         W = w.W
@@ -452,8 +455,8 @@ def run_gpu(w: wl.Workload, steps: int, warmup: int, slots: bool = False, n_iter
         def step():
             t = state["t"]
             i = t % n_inputs
-            win(W, t % W, n_iter, Z, Bc, Cs, Kc, Uc, Kb, Ub, Gb, x["q"][i], x["k"][i], x["v"][i],
-                x["gate"][i], x["beta"][i], y)
+            win(W, t % W, n_iter, Z, Bc, Cs, Kc, Uc, Kb, Ub, Gb, xv[i]["q"], xv[i]["k"], xv[i]["v"],
+                xv[i]["gate"], xv[i]["beta"], y)
             state["t"] += 1
     else:
         C = w.M - 1
@@ -478,8 +481,8 @@ def run_gpu(w: wl.Workload, steps: int, warmup: int, slots: bool = False, n_iter
 
             def step():
                 i = state["t"] % n_inputs
-                fs(C, Ld, Sb, lbar, Kl, Ul, Lm, x["q"][i], x["k"][i], x["v"][i], x["gate"][i],
-                   x["beta"][i], y)
+                fs(C, Ld, Sb, lbar, Kl, Ul, Lm, xv[i]["q"], xv[i]["k"], xv[i]["v"], xv[i]["gate"],
+                   xv[i]["beta"], y)
                 state["t"] += 1
         else:
             app = rsu.kda_log_append if kda else rsu.gdn_log_append
@@ -492,7 +495,7 @@ def run_gpu(w: wl.Workload, steps: int, warmup: int, slots: bool = False, n_iter
                 i = state["t"] % n_inputs
                 L = state["L"]
                 f = app if L < C else mrg
-                f(C, L, Sb, lbar, Kl, Ul, Lm, x["q"][i], x["k"][i], x["v"][i], x["gate"][i], x["beta"][i], y)
+                f(C, L, Sb, lbar, Kl, Ul, Lm, xv[i]["q"], xv[i]["k"], xv[i]["v"], xv[i]["gate"], xv[i]["beta"], y)
                 state["L"] = L + 1 if L < C else 0
                 state["t"] += 1
 

@@ -109,6 +109,11 @@ def _open(path: str) -> ctypes.CDLL:
 
 
 _lib = _open(LIB_PATH)
+_fns = {name: getattr(_lib, name) for name in _SIGS}
+
+# torch's current HIP stream as a raw handle; the private accessor skips building a Stream
+# object on every call (a few microseconds, which matter beside launches of 20-30 us)
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
 
 
 def abi_version() -> int:
@@ -116,20 +121,26 @@ def abi_version() -> int:
 
 
 def _stream():
-    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if _raw_stream is not None:
+        return _raw_stream(torch.cuda.current_device())
+    return torch.cuda.current_stream().cuda_stream
 
 
 def _ptr(t: torch.Tensor | None):
-    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+    return t.data_ptr() if t is not None else None
 
 
 def _call(name: str, *args):
-    rc = getattr(_lib, name)(*args)
+    rc = _fns[name](*args)
     if rc != 0:
         raise RsuError(f"{name} returned {rc}: {_lib.rsu_last_error().decode()}")
 
 
 def _need(t: torch.Tensor, name: str, dtype, shape):
+    # the common case in one expression; the checks below name what is wrong
+    if (isinstance(t, torch.Tensor) and t.is_cuda and (dtype is None or t.dtype == dtype) and t.shape == shape
+            and t.is_contiguous()):
+        return
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
     if t.device.type != "cuda":
@@ -648,3 +659,12 @@ def debug_metadata_counts(heads: int):
 def raw_library() -> ctypes.CDLL:
     """The loaded librsu.so (for ABI-level tests)."""
     return _lib
+
+
+def select_library(lib: ctypes.CDLL) -> ctypes.CDLL:
+    """Route every later call to lib, a build opened with _open (the checking build, for
+    tests); returns the library used until now."""
+    global _lib, _fns
+    prev = _lib
+    _lib, _fns = lib, {name: getattr(lib, name) for name in _SIGS}
+    return prev

@@ -26,7 +26,7 @@ def libs():
     m = rsu()
     from recurrent_state_update_head_amd._build import CHECK_LIB
     assert os.path.exists(CHECK_LIB), f"{CHECK_LIB} is not built (python -m recurrent_state_update_head_amd._build)"
-    plain, checked = m._lib, m._open(CHECK_LIB)
+    plain, checked = m.raw_library(), m._open(CHECK_LIB)
     with pytest.raises(m.RsuError, match="RSU_CHECK_METADATA"):
         m.debug_metadata_counts(1)  # the ordinary build keeps no counters
     return m, plain, checked
@@ -48,7 +48,7 @@ def _expected(L_before: np.ndarray, C: int, per_key: bool, slots: bool) -> np.nd
 def _run(m, lib, w, slots: bool, check: bool):
     """C + 2 steps (a full cycle, a merge and one more append) on one library build;
     returns the final buffers and the number of steps whose counts were checked."""
-    m._lib = lib
+    m.select_library(lib)
     B, H, C = w.B, w.H, w.M - 1
     Sbase = torch.from_numpy(wl.initial_state(w)).to(DEV).view(B, H, 128, 128)
     buf = new_log_buffers(w, C)
@@ -99,7 +99,7 @@ def test_log_metadata_written_once_per_head(libs, variant, qkv, slots):
         ref, _ = _run(m, plain, w, slots, check=False)
         got, n = _run(m, checked_lib, w, slots, check=True)
     finally:
-        m._lib = plain
+        m.select_library(plain)
     assert n == w.M + 1
     for name in ref:
         assert torch.equal(ref[name], got[name]), f"{name} differs between the checking and ordinary builds"
