@@ -342,30 +342,15 @@ __global__ __launch_bounds__(kThreads) void q8_step_kernel(
 constexpr int kZsStride = kD / 4 + 1;
 __host__ __device__ constexpr int boundary_lds_floats(int wmax) { return 2 * wmax * kD + kD * kZsStride; }
 
-// Round-half-to-even of |w| <= 2^22 to an integer with one fp32 add: the sum's
-// low mantissa bits are the integer. The code byte is the low byte of the sum's
-// bits after clamping those bits to the codes of -127 .. 127. The add is kept apart
-// from the product that forms w (no contraction into an FMA): the code is decided on
-// w rounded to fp32, as the quantizer of a plain state decides it.
-__device__ __forceinline__ uint32_t code_bits(float w) {
-#pragma clang fp contract(off)
-    constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23
-    const int bits = __float_as_int(w + kMagic);
-    const int lo = 0x4B400000 - 127, hi = 0x4B400000 + 127;
-    return static_cast<uint32_t>(min(max(bits, lo), hi));
-}
-// Codes of a, b, c, d (a in the low byte) as one word.
-__device__ __forceinline__ uint32_t code_word(float a, float b, float c, float d) {
-    return pack_low_bytes(code_bits(a), code_bits(b), code_bits(c), code_bits(d));
-}
-
-// The same without the clamp, for the products w = x * fp32(127 / (m f)) of a row whose absmax
-// is m, with f = tiny_factor(m) (1, or 2^64 for m below 2^-64): the code of w f, rounded once
-// by the magic add inside one fma. w f is exact wherever w is normal (f is a power of two) and
-// then equals fp32((x f) * fp32(127 / (m f))), the product for the scaled row; a subnormal w
-// gives |w f| < 2^-62, code 0 either way. |x| <= m bounds |w f| by 127 (1 + 2^-24), which rounds
-// to at most 127, so the integer is already a code (m = 0 gives w = 0). Non-finite rows give
-// unspecified codes.
+// Codes without a clamp, for the products w = x * fp32(127 / (m f)) of a row whose absmax is m,
+// with f = tiny_factor(m) (1, or 2^64 for m below 2^-64): the code of w f, rounded half to even
+// by the magic add inside one fma (|w f| <= 2^22: the sum's low mantissa bits are the integer,
+// its low byte the code's two's complement). The product w is rounded to fp32 first, as the
+// quantizer of a plain state decides it. w f is exact wherever w is normal (f is a power of
+// two) and then equals fp32((x f) * fp32(127 / (m f))), the product for the scaled row; a
+// subnormal w gives |w f| < 2^-62, code 0 either way. |x| <= m bounds |w f| by 127 (1 + 2^-24),
+// which rounds to at most 127, so the integer is already a code (m = 0 gives w = 0).
+// Non-finite rows give unspecified codes.
 __device__ __forceinline__ uint32_t code_bits_in_range(float w, float f) {
     constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23
     return static_cast<uint32_t>(__float_as_int(__builtin_fmaf(w, f, kMagic)));
