@@ -155,11 +155,11 @@ __global__ __launch_bounds__(kThreads) void lq_step_kernel(
     float Gg = 1.f, Gall = 1.f;
     float Ge[kPerKey ? 8 : 1], Gt[kPerKey ? 8 : 1];
     if constexpr (!kPerKey) {
-        for (int i = pos - 1; i >= 0; --i) {
-            const float gi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, g_lane), i));
-            Gg = i > grp ? Gg * gi : Gg;
-            Gall *= gi;
-        }
+        // suffix scan over the record lanes (g = 1 from record pos on): the product of the
+        // gates after each record, gathered for this lane's record group
+        const float Sfx = suffix_prod<16>(g_lane, lane);
+        Gg = lane_gather(suffix_prod_excl<16>(Sfx, lane), grp);
+        Gall = lane_value(Sfx, 0);
     } else {
         // the gates' suffix products per key column, in place; the column totals in gtot
         sg.store(gs_lds, tid);
@@ -770,13 +770,10 @@ __global__ __launch_bounds__(kThreads) void lq_boundary_kernel(
         zw[it] = __builtin_nontemporal_load(Zh + lq_row(it, wave, ro) * (kD / 4) + c4);
 
     // ---- gate products (newest first): after record grp, after record = lane, all
-    float Gg = 1.f, Gl = 1.f, Gall = 1.f;
-    for (int i = pos - 1; i >= 0; --i) {
-        const float gi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, g_lane), i));
-        Gg = i > grp ? Gg * gi : Gg;
-        Gl = i > lane ? Gl * gi : Gl;
-        Gall *= gi;
-    }
+    // (a suffix scan over the record lanes, g = 1 from record pos on)
+    const float Sfx = suffix_prod<16>(g_lane, lane);
+    const float Gl = suffix_prod_excl<16>(Sfx, lane);
+    const float Gg = lane_gather(Gl, grp), Gall = lane_value(Sfx, 0);
     const float gam_all = Gall * gr;  // Gamma_{1:W}
     if (wave == 0 && lane < kRec) gam[lane] = lane < pos ? Gl * gr : 1.f;
     const uint32_t kcw[4] = {kchw.x, kchw.y, kchw.z, kchw.w};
@@ -1296,11 +1293,11 @@ __global__ __launch_bounds__(kThreads) void lq_low_step_kernel(
     float Gg = 1.f, Gall = 1.f;
     float Ge[kPerKey ? 8 : 1], Gt[kPerKey ? 8 : 1];
     if constexpr (!kPerKey) {
-        for (int i = pos - 1; i >= 0; --i) {
-            const float gi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, g_lane), i));
-            Gg = i > grp ? Gg * gi : Gg;
-            Gall *= gi;
-        }
+        // suffix scan over the record lanes (g = 1 from record pos on): the product of the
+        // gates after each record, gathered for this lane's record group
+        const float Sfx = suffix_prod<16>(g_lane, lane);
+        Gg = lane_gather(suffix_prod_excl<16>(Sfx, lane), grp);
+        Gall = lane_value(Sfx, 0);
     } else {
         // the gates' suffix products per key column, in place; the column totals in gtot
         sg.store(gs_lds, tid);
@@ -1488,13 +1485,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     }
 
     // ---- gate products (newest first): after record grp, after record = lane, all
-    float Gg = 1.f, Gl = 1.f, Gall = 1.f;
-    for (int i = pos - 1; i >= 0; --i) {
-        const float gi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, g_lane), i));
-        Gg = i > grp ? Gg * gi : Gg;
-        Gl = i > lane ? Gl * gi : Gl;
-        Gall *= gi;
-    }
+    // (a suffix scan over the record lanes, g = 1 from record pos on)
+    const float Sfx = suffix_prod<16>(g_lane, lane);
+    const float Gl = suffix_prod_excl<16>(Sfx, lane);
+    const float Gg = lane_gather(Gl, grp), Gall = lane_value(Sfx, 0);
     const float gam_all = Gall * gr;  // Gamma_{1:W}
     if (wave == 0 && lane < kRec) gam[lane] = lane < pos ? Gl * gr : 1.f;
     const uint32_t kcw[4] = {kchw.x, kchw.y, kchw.z, kchw.w};

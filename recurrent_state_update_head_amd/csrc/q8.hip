@@ -116,10 +116,6 @@ struct Raw8<float> {
     __device__ __forceinline__ float operator[](int e) const { return e < 4 ? lo[e] : hi[e - 4]; }
 };
 
-__device__ __forceinline__ float lane_value(float x, int i) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), i));
-}
-
 // Per-key decays of a window's staged record keys, over all 256 threads of the workgroup:
 // thread t takes key row t >> 1 and the records of one half, j = (t & 1) kHalf + e, so the
 // two halves of a row sit in neighbouring lanes. load() issues the loads of the half's gates

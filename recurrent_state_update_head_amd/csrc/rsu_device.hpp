@@ -199,6 +199,11 @@ __device__ __forceinline__ float lane_gather(float x, int src) {
     return __int_as_float(__builtin_amdgcn_ds_bpermute(src << 2, __float_as_int(x)));
 }
 
+// Value of x in lane i (a wave-uniform index) of the same wave.
+__device__ __forceinline__ float lane_value(float x, int i) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), i));
+}
+
 // Suffix products over lanes 0..kN-1 of a wave (kN a power of two, at most 32): lane
 // l < kN gets x_l x_{l+1} ... x_{kN-1}; lanes past kN keep x. Every permute runs with the
 // whole wave; the range check selects the factor after it.
