@@ -289,7 +289,7 @@ def hbm_ceiling(torch, rsu, tiles: int, read_bytes: float, write_bytes: float, s
 
 
 def run_gpu(w: wl.Workload, steps: int, warmup: int, slots: bool = False, n_iter: int = 1, graph: bool = False,
-            split: bool = False, measure_ceiling: bool = True):
+            split: bool = False, measure_ceiling: bool = True, layers: int = 1):
     import torch
     import recurrent_state_update_head_amd as rsu
     dev = "cuda"
@@ -304,6 +304,7 @@ def run_gpu(w: wl.Workload, steps: int, warmup: int, slots: bool = False, n_iter
     S0 = torch.from_numpy(wl.initial_state(w)).to(dev).view(B, H, 128, 128)
     kda = w.per_key_gate
     state = {"t": 0}
+    drain = None  # set where launches can still run on another stream when a step returns
 
     if w.path == "dense" and w.variant == "rwkv7":
         S = S0
@@ -341,28 +342,42 @@ def run_gpu(w: wl.Workload, steps: int, warmup: int, slots: bool = False, n_iter
         om = torch.from_numpy(wl.row_influence(w)).to(dev).view(B, H, 128)
         rsu.stepq_pack(S0, om, Z, R, Cf)
         del S0
+        # `layers` independent packed states (a model's layers, the same inputs): a step runs
+        # each of them once
+        packs = [(Z, R, Cf)] + [(Z.clone(), R.clone(), Cf.clone()) for _ in range(layers - 1)]
         fn = rsu.kda_stepq_step if kda else rsu.gdn_stepq_step
         if split:
-            # the readout on this stream, the repack on a second one ordered by events (the
-            # next readout waits for it): nothing else runs here to hide the repack behind
+            # the readout on this stream, the repack on a second one ordered by events: a
+            # layer's next readout waits for its repack, which can run beside the readouts of
+            # the other layers (with one layer nothing else runs to hide the repack behind)
             readout = rsu.kda_stepq_readout if kda else rsu.gdn_stepq_readout
             repack = rsu.kda_stepq_repack if kda else rsu.gdn_stepq_repack
-            u = torch.empty(B, H, 128, device=dev)
+            us = [torch.empty(B, H, 128, device=dev) for _ in range(layers)]
+            ys = [y] + [torch.empty(B, H, 128, device=dev) for _ in range(layers - 1)]
+            u = us[0]
             side = torch.cuda.Stream()
             main = torch.cuda.current_stream()
+            done = [None] * layers  # each layer's last repack
 
             def step():
                 i = state["t"] % n_inputs
-                readout(Z, R, Cf, xv[i]["q"], xv[i]["k"], xv[i]["v"], xv[i]["gate"], xv[i]["beta"], u, y)
-                r1 = torch.cuda.Event()
-                r1.record(main)
-                with torch.cuda.stream(side):
-                    side.wait_event(r1)
-                    repack(Z, R, Cf, om, xv[i]["k"], xv[i]["gate"], u)
-                    p1 = torch.cuda.Event()
-                    p1.record(side)
-                main.wait_event(p1)
+                for l, (Zl, Rl, Cl) in enumerate(packs):
+                    if done[l] is not None:
+                        main.wait_event(done[l])
+                    readout(Zl, Rl, Cl, xv[i]["q"], xv[i]["k"], xv[i]["v"], xv[i]["gate"], xv[i]["beta"], us[l], ys[l])
+                    r1 = torch.cuda.Event()
+                    r1.record(main)
+                    with torch.cuda.stream(side):
+                        side.wait_event(r1)
+                        repack(Zl, Rl, Cl, om, xv[i]["k"], xv[i]["gate"], us[l])
+                        done[l] = torch.cuda.Event()
+                        done[l].record(side)
                 state["t"] += 1
+
+            def drain():
+                for e in done:
+                    if e is not None:
+                        main.wait_event(e)
 
             def split_phases(reps=32):
                 """Each half alone, launched back to back on one stream (the readout only reads the
@@ -383,7 +398,8 @@ def run_gpu(w: wl.Workload, steps: int, warmup: int, slots: bool = False, n_iter
         else:
             def step():
                 i = state["t"] % n_inputs
-                fn(Z, R, Cf, om, xv[i]["q"], xv[i]["k"], xv[i]["v"], xv[i]["gate"], xv[i]["beta"], y)
+                for Zl, Rl, Cl in packs:
+                    fn(Zl, Rl, Cl, om, xv[i]["q"], xv[i]["k"], xv[i]["v"], xv[i]["gate"], xv[i]["beta"], y)
                 state["t"] += 1
     elif w.path == "q8_window" and w.variant == "rwkv7":
         W = w.W
@@ -555,6 +571,8 @@ def run_gpu(w: wl.Workload, steps: int, warmup: int, slots: bool = False, n_iter
         e0.record(stream)
         for _ in range(steps):
             step()
+        if drain is not None:
+            drain()  # the timed region ends after the last launch on every stream
         e1.record(stream)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
@@ -750,6 +768,9 @@ def main():
                     help="lq path: subspace iterations per boundary refit (warm-started)")
     ap.add_argument("--split", action="store_true",
                     help="stepq path: the readout and the repack as two launches on two streams")
+    ap.add_argument("--layers", type=int, default=1,
+                    help="stepq path: independent packed states stepped in turn (a model's layers); with "
+                         "--split a layer's repack can run beside the next layer's readout")
     ap.add_argument("--slots", action="store_true",
                     help="log path: per-slot live lengths, every head at its own cycle point")
     ap.add_argument("--no-other-configs", action="store_true",
@@ -771,8 +792,11 @@ def main():
 
     if args.split and (w.path != "stepq" or args.graph):
         raise SystemExit("--split applies to the stepq workload, without --graph")
-    gpu_sec, wall, ceiling, phases, dist = run_gpu(w, steps, warmup, args.slots, args.n_iter, args.graph, args.split)
-    heads = w.heads
+    if args.layers < 1 or (args.layers > 1 and (w.path != "stepq" or args.graph)):
+        raise SystemExit("--layers N > 1 applies to the stepq workload, without --graph")
+    gpu_sec, wall, ceiling, phases, dist = run_gpu(w, steps, warmup, args.slots, args.n_iter, args.graph, args.split,
+                                                   layers=args.layers)
+    heads = w.heads * args.layers   # head-updates of one step (every layer once)
     per_head = slots_bytes_per_head(w) if args.slots else cycle_bytes_per_head(w)
     launch_sec = gpu_sec / steps
     achieved = per_head * heads / launch_sec / 1e9
@@ -802,7 +826,8 @@ def main():
                                              "lq_window": "int8+f32 scales+4 fp16 token pairs"}.get(w.path, "f32")),
                    "W": w.W or None, "M": w.M or None, "gates": w.variant,
                    "log_phases": ("per-slot (mixed)" if args.slots else "batch-uniform") if w.path == "log" else None,
-                   "refit_iterations": args.n_iter if w.path == "lq_window" else None},
+                   "refit_iterations": args.n_iter if w.path == "lq_window" else None,
+                   "layers": args.layers if w.path == "stepq" else None},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
                      "traffic_source": (f"{os.path.relpath(PROFILE_COUNTERS, ROOT)}: rocprofv3 FETCH_SIZE and "
@@ -812,7 +837,8 @@ def main():
         "hbm_ceiling": ceiling,
         "wall_s_timed_region": wall,
         "timing": ("the K steps captured as one HIP graph, replayed once" if args.graph else
-                   "eager launches, readout and repack on two streams" if args.split else "eager launches"),
+                   "eager launches, readout and repack on two streams" if args.split else "eager launches")
+                  + (f"; {args.layers} layers per step" if args.layers > 1 else ""),
     }
     out["step_time_distribution"] = dist
     if phases:
