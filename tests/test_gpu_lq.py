@@ -175,7 +175,7 @@ def test_lq_quantize_start_iterations(n_iter0):
 
 
 @pytest.mark.parametrize("cid,fn", [(6, "gdn_lq_quantize"), (16, "gdn_lq6_quantize"), (12, "gdn_lq4_quantize"),
-                                    (9, "kda_lq_quantize")])
+                                    (9, "kda_lq_quantize"), (18, "kda_lq6_quantize"), (17, "kda_lq4_quantize")])
 def test_lq_quantize_tiny_column(cid, fn):
     """A value column whose smoothed maximum B lies near 2^-123, where qmax / B overflows fp32
     (the column's state entries are at most 2^-126: subnormal or nearly; no outliers, so the

@@ -74,6 +74,9 @@ def test_quantize_tiny_and_subnormal_rows_keep_their_codes():
 
 @pytest.mark.parametrize("label,idx,over", [("gdn bf16", 4, {}), ("gdn f32", 4, {"qkv": "f32"}),
                                             ("kda", 4, {"variant": "kda", "gate_lo": 0.8, "gate_hi": 1.0}),
+                                            ("gdn bf16 W=32", 4, {"W": 32}),
+                                            ("kda f32 W=24", 4, {"W": 24, "qkv": "f32", "variant": "kda",
+                                                                 "gate_lo": 0.8, "gate_hi": 1.0}),
                                             ("rwkv7", 11, {}), ("deltaproduct", 15, {})])
 def test_window_tiny_row(label, idx, over):
     """A key row with maximum in (2^-123, 2^-122] that no record writes to (every key is zero
@@ -82,7 +85,8 @@ def test_window_tiny_row(label, idx, over):
     1e-5 relative of the oracle's beyond the absolute error of a subnormal coefficient: a_r / 127
     Gamma_r is formed in fp32 by up to four multiplications, each off by at most 2^-150 once it
     is subnormal, and the scale is 127 times it."""
-    w = wl.custom(wl.WORKLOADS[idx], B=2, H=3, steps=2 * wl.WORKLOADS[idx].W + 1, tiny_row=5, **over)
+    W = over.get("W", wl.WORKLOADS[idx].W)
+    w = wl.custom(wl.WORKLOADS[idx], B=2, H=3, steps=2 * W + 1, tiny_row=5, **over)
     _check(run_window(w, a_abs=4 * 127 * 2.0 ** -150), f"{label} tiny row 5")
 
 
